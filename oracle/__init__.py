@@ -1,0 +1,273 @@
+"""CPU float64 oracle for tile-based Gaussian-splat rasterization.
+
+TEST INFRASTRUCTURE. Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package. The product path (the
+HIP library and its Python binding) never touches it, and it shares no code,
+header, table or helper with that path. The seeded input generators in
+``scenes`` are the only module both sides use; they hold none of the method's
+arithmetic.
+
+Contents, each following the pages' problem statement (the pages print no
+formulas; see gs_oracle.c for the compositing reading):
+
+* :func:`bin_tiles` -- which 16x16 tiles each splat covers, and each tile's
+  list ordered by depth. The binning / radix-sort / tile-range stages appear
+  as ``emit_pairs``, ``radix_hist``, ``radix_scatter`` and ``extract_offsets``
+  in the timing table of page "Phase 5 step 30b — kernel-by-kernel timing"
+  (section 計測結果). Written out with a library sort (numpy.lexsort).
+* :func:`rasterize_fwd` / :func:`rasterize_bwd` -- per-pixel front-to-back
+  composite and the exact gradient of L = sum <dL/dImage, image> (C core,
+  float64, OpenMP over tiles).
+* :func:`composite_bruteforce` -- the same composite with no tiles at all:
+  every pixel walks every splat in (depth, id) order. Used to pin the tiled
+  oracle.
+
+Binning is the only integer decision driven by floating point here, and it is
+taken in float32 exactly like the kernels take it (the tile rectangle from
+mean +- radius, scaled by 1/16 and floored), so binning parity is bit-exact.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+TILE = 16
+ALPHA_MIN = 1.0 / 255.0
+ALPHA_MAX = 0.99
+T_MIN = 1e-4
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.OUT
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        lib.gso_forward.argtypes = [i32, i32, P, P, P, P, P, P, P, P, i32, P, P, P, P]
+        lib.gso_forward.restype = i32
+        lib.gso_backward.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, i32, P, P]
+        lib.gso_backward.restype = i32
+        lib.gso_threads.argtypes = []
+        lib.gso_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the C core runs on."""
+    return int(_load().gso_threads())
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def grid(width: int, height: int) -> tuple[int, int]:
+    return (width + TILE - 1) // TILE, (height + TILE - 1) // TILE
+
+
+# ----------------------------------------------------------------------------
+# Binning
+# ----------------------------------------------------------------------------
+
+def tile_rects(means2d: np.ndarray, radii: np.ndarray, depths: np.ndarray, width: int, height: int):
+    """Per-splat tile rectangle [tx0, tx1) x [ty0, ty1), float32 arithmetic.
+
+    A splat is culled (empty rectangle) if radius <= 0, depth is not > 0, or
+    its mean is not finite."""
+    GX, GY = grid(width, height)
+    f = np.float32
+    m = np.asarray(means2d, dtype=f)
+    r = np.asarray(radii, dtype=np.int32).astype(f)
+    inv = f(1.0 / TILE)
+    with np.errstate(invalid="ignore", over="ignore"):
+        x0 = np.floor((m[:, 0] - r) * inv)
+        x1 = np.floor((m[:, 0] + r) * inv) + f(1.0)
+        y0 = np.floor((m[:, 1] - r) * inv)
+        y1 = np.floor((m[:, 1] + r) * inv) + f(1.0)
+    tx0 = np.clip(x0, 0, GX).astype(np.int64)
+    tx1 = np.clip(x1, 0, GX).astype(np.int64)
+    ty0 = np.clip(y0, 0, GY).astype(np.int64)
+    ty1 = np.clip(y1, 0, GY).astype(np.int64)
+    d = np.asarray(depths, dtype=f)
+    live = (np.asarray(radii) > 0) & (d > 0) & np.isfinite(m[:, 0]) & np.isfinite(m[:, 1])
+    live &= (tx1 > tx0) & (ty1 > ty0)
+    tx1 = np.where(live, tx1, tx0)
+    ty1 = np.where(live, ty1, ty0)
+    return tx0, tx1, ty0, ty1
+
+
+def bin_tiles(means2d, radii, depths, width: int, height: int):
+    """Tile lists, as (sorted_ids int32 [I], tile_ranges int32 [GX*GY, 2]).
+
+    Each tile's list holds the splats whose rectangle covers it, ordered by
+    the float32 bit pattern of depth (positive floats order like their bit
+    patterns), ties broken by ascending splat id. Tile ids are row-major,
+    ``ty * GX + tx``; the lists are concatenated in tile-id order."""
+    GX, GY = grid(width, height)
+    tx0, tx1, ty0, ty1 = tile_rects(means2d, radii, depths, width, height)
+    nx = tx1 - tx0
+    ny = ty1 - ty0
+    cnt = nx * ny
+    total = int(cnt.sum())
+    ids = np.repeat(np.arange(len(cnt), dtype=np.int64), cnt)
+    # index of each intersection within its splat's rectangle, row-major
+    first = np.repeat(np.cumsum(cnt) - cnt, cnt)
+    local = np.arange(total, dtype=np.int64) - first
+    nxr = np.repeat(nx, cnt)
+    tx = np.repeat(tx0, cnt) + local % np.maximum(nxr, 1)
+    ty = np.repeat(ty0, cnt) + local // np.maximum(nxr, 1)
+    tile = ty * GX + tx
+    dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)[ids]
+    order = np.lexsort((ids, dbits, tile))
+    sorted_ids = ids[order].astype(np.int32)
+    counts = np.bincount(tile, minlength=GX * GY)
+    ends = np.cumsum(counts)
+    ranges = np.stack([ends - counts, ends], axis=1).astype(np.int32)
+    ranges[counts == 0] = 0
+    return sorted_ids, ranges
+
+
+# ----------------------------------------------------------------------------
+# Forward / backward (C core)
+# ----------------------------------------------------------------------------
+
+def _arrs(means2d, conics, colors, opacities):
+    # float64 copies of the (usually float32) inputs: the values are exact, and
+    # finite-difference pins can perturb them below float32 resolution.
+    return (np.ascontiguousarray(means2d, dtype=np.float64),
+            np.ascontiguousarray(conics, dtype=np.float64),
+            np.ascontiguousarray(colors, dtype=np.float64),
+            np.ascontiguousarray(opacities, dtype=np.float64))
+
+
+def rasterize_fwd(means2d, conics, colors, opacities, background, width: int, height: int,
+                  tile_ranges, sorted_ids, tiles=None):
+    """Forward composite. Returns dict with image [H,W,3] f64, final_T [H,W]
+    f64, n_contrib [H,W] i32 and ambiguous [H,W] bool. With ``tiles`` (a list
+    of tile ids) only those tiles' pixels are computed (others stay 0)."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    img = np.zeros((height, width, 3), dtype=np.float64)
+    T = np.zeros((height, width), dtype=np.float64)
+    nc = np.zeros((height, width), dtype=np.int32)
+    amb = np.zeros((height, width), dtype=np.uint8)
+    if tiles is None:
+        tl, ntl = None, 0
+    else:
+        tarr = np.ascontiguousarray(tiles, dtype=np.int32)
+        tl, ntl = _ptr(tarr), len(tarr)
+    lib.gso_forward(width, height, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
+                    _ptr(bg), tl, ntl, _ptr(img), _ptr(T), _ptr(nc), _ptr(amb))
+    return {"image": img, "final_T": T, "n_contrib": nc, "ambiguous": amb.astype(bool)}
+
+
+def rasterize_bwd(means2d, conics, colors, opacities, background, width: int, height: int,
+                  tile_ranges, sorted_ids, dL_dimage, tiles=None):
+    """Exact gradients of L = sum <dL_dimage, image>. Returns dict of float64
+    arrays: dmeans2d [n,2], dconics [n,3], dcolors [n,3], dopacities [n],
+    accum_weight [n]. With ``tiles`` only those tiles' pixels contribute."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    n = m.shape[0]
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    g = np.ascontiguousarray(dL_dimage, dtype=np.float64)
+    grads = np.zeros((n, 9), dtype=np.float64)
+    aw = np.zeros(n, dtype=np.float64)
+    if tiles is None:
+        tl, ntl = None, 0
+    else:
+        tarr = np.ascontiguousarray(tiles, dtype=np.int32)
+        tl, ntl = _ptr(tarr), len(tarr)
+    lib.gso_backward(width, height, n, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
+                     _ptr(bg), _ptr(g), tl, ntl, _ptr(grads), _ptr(aw))
+    return {"dmeans2d": grads[:, 0:2].copy(), "dconics": grads[:, 2:5].copy(),
+            "dcolors": grads[:, 5:8].copy(), "dopacities": grads[:, 8].copy(),
+            "accum_weight": aw}
+
+
+# ----------------------------------------------------------------------------
+# Brute force (no tiles), numpy
+# ----------------------------------------------------------------------------
+
+def composite_bruteforce(means2d, conics, colors, opacities, depths, radii, background,
+                         width: int, height: int, return_margin: bool = False):
+    """Every pixel walks every live splat in (float32 depth bits, id) order,
+    with the same skip / clamp / stop rules; no tiles and no radius test
+    beyond the per-splat cull (radius <= 0 or depth not > 0). Float64 numpy,
+    vectorised over pixels. Returns (image, final_T, n_steps) where n_steps
+    counts composited splats per pixel; with ``return_margin`` also the
+    smallest relative distance of any decision taken (skip, clamp, stop) to
+    its threshold."""
+    m = np.asarray(means2d, dtype=np.float64)
+    q = np.asarray(conics, dtype=np.float64)
+    col = np.asarray(colors, dtype=np.float64)
+    op = np.asarray(opacities, dtype=np.float64)
+    d32 = np.asarray(depths, dtype=np.float32)
+    live = (np.asarray(radii) > 0) & (d32 > 0) & np.isfinite(m).all(axis=1)
+    ids = np.nonzero(live)[0]
+    order = ids[np.lexsort((ids, d32.view(np.uint32)[ids]))]
+    ys, xs = np.mgrid[0:height, 0:width]
+    px = xs.ravel() + 0.5
+    py = ys.ravel() + 0.5
+    T = np.ones(px.shape)
+    C = np.zeros((px.size, 3))
+    done = np.zeros(px.shape, dtype=bool)
+    nstep = np.zeros(px.shape, dtype=np.int64)
+    margin = np.inf
+    for i in order:
+        dx = px - m[i, 0]
+        dy = py - m[i, 1]
+        power = -0.5 * (q[i, 0] * dx * dx + q[i, 2] * dy * dy) - q[i, 1] * dx * dy
+        raw = op[i] * np.exp(power)
+        alpha = np.minimum(ALPHA_MAX, raw)
+        use = (~done) & (alpha >= ALPHA_MIN)
+        nxt = T * (1.0 - alpha)
+        if return_margin:
+            live_px = ~done
+            if live_px.any():
+                margin = min(margin, float(np.min(np.abs(alpha[live_px] / ALPHA_MIN - 1.0))))
+            if use.any():
+                margin = min(margin, float(np.min(np.abs(raw[use] / ALPHA_MAX - 1.0))),
+                             float(np.min(np.abs(nxt[use] / T_MIN - 1.0))))
+        stop = use & (nxt < T_MIN)
+        done |= stop
+        use &= ~stop
+        C[use] += col[i] * (alpha[use] * T[use])[:, None]
+        T = np.where(use, nxt, T)
+        nstep += use
+    bg = np.zeros(3) if background is None else np.asarray(background, dtype=np.float64)
+    img = C + T[:, None] * bg[None, :]
+    res = (img.reshape(height, width, 3), T.reshape(height, width), nstep.reshape(height, width))
+    return res + (margin,) if return_margin else res
+
+
+# ----------------------------------------------------------------------------
+# Convenience over a scenes.Scene
+# ----------------------------------------------------------------------------
+
+def run_scene(sc, tiles=None, backward=True, dL_dimage=None):
+    """Bin, forward and (optionally) backward a scene. Returns a dict."""
+    ids, rng_ = bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    out = {"sorted_ids": ids, "tile_ranges": rng_}
+    out.update(rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                             sc.width, sc.height, rng_, ids, tiles=tiles))
+    if backward:
+        g = sc.dL_dimage if dL_dimage is None else dL_dimage
+        out.update(rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                                 sc.width, sc.height, rng_, ids, g, tiles=tiles))
+    return out

@@ -1,0 +1,280 @@
+/*
+ * gs_oracle.c -- CPU float64 oracle for tile-based Gaussian-splat rasterization.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the checker, not the product: it is
+ * built and called by the tests, by the package's smoke check and by the
+ * benchmark's CPU-baseline leg, never by the library itself. It shares no code
+ * with the HIP kernels.
+ *
+ * What it computes (a plain definition, written out per pixel):
+ *
+ *   The backward pass named on page "Phase 5 step 30b — kernel-by-kernel
+ *   timing" (section ホットスポット ranking, item 1: nine per-splat gradient
+ *   fields -- 2D mean, conic, RGB, opacity -- summed over all pixels) and on
+ *   the Spirula Studio page (从 8.6 KB 到 4.2 KB, section 机制拆解: the 2D
+ *   screen-space path rasterize_bwd_2d, with an optional accumulated-weight
+ *   output). Neither page prints the compositing formula; the reading used is
+ *   the standard tile-based 3D Gaussian splatting rule:
+ *
+ *     pixel centre p = (x + 0.5, y + 0.5), d = p - mean
+ *     sigma = -1/2 (a dx^2 + c dy^2) - b dx dy        (conic = (a, b, c))
+ *     G = exp(sigma),  alpha = min(0.99, opacity * G)
+ *     walk the tile's depth-sorted list front to back:
+ *       skip the splat if alpha < 1/255
+ *       stop (without compositing it) if T (1 - alpha) < 1e-4
+ *       else  C += colour alpha T,  T *= (1 - alpha)
+ *     image = C + T bg,  final_T = T,  n_contrib = list position of the last
+ *     composited splat + 1 (0 if none)
+ *
+ *   Backward: L = sum_p <g_p, image_p> with g = dL/dImage; the exact partial
+ *   derivatives of L with respect to each stored per-splat scalar, with the
+ *   discrete decisions (skip set, stop point, clamp state) held fixed:
+ *     dL/dcolour_i  = sum_p alpha_i T_i g_p
+ *     dL/dalpha_i   = sum_p <g_p, colour_i T_i - S_i / (1 - alpha_i)>,
+ *                     S_i = sum_{j>i} colour_j alpha_j T_j + T_final bg
+ *     if not clamped: dL/dsigma = alpha dL/dalpha, dL/dopacity = G dL/dalpha,
+ *       dL/da = -dx^2/2 dL/dsigma, dL/db = -dx dy dL/dsigma,
+ *       dL/dc = -dy^2/2 dL/dsigma,
+ *       dL/dmean = (a dx + b dy, b dx + c dy) dL/dsigma
+ *     accum_weight_i = sum_p alpha_i T_i over composited pairs
+ *
+ *   Unlike the kernels this evaluates T forwards (products) and S as a suffix
+ *   sum, in float64, with no division recurrence.
+ *
+ * Ambiguity flags: the kernels decide the three thresholds in float32. For
+ * each decision this file also computes a bound on how far a float32
+ * evaluation can be from the float64 value; a pixel is flagged when any of its
+ * decisions lies inside that band (several results are then correct).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define TILE 16
+#define ALPHA_MAX 0.99
+#define ALPHA_MIN (1.0 / 255.0)
+#define T_MIN 1e-4
+
+/* unit roundoff of float32, and the guard-band scale factors */
+static const double U32 = 5.9604644775390625e-08; /* 2^-24 */
+static const double K_ALPHA = 4.0;
+static const double K_T = 2.0;
+
+typedef struct {
+    const double* means;   /* [n][2] */
+    const double* conics;  /* [n][3] */
+    const double* colors;  /* [n][3] */
+    const double* opac;    /* [n]    */
+    double bg[3];
+} splats_t;
+
+/* One walked entry of a pixel: enough to form its gradient afterwards. */
+typedef struct {
+    int32_t k;       /* position in the tile list */
+    double alpha, T, G, dx, dy;
+    int clamped;
+} contrib_t;
+
+/* Relative error bound of a float32 evaluation of alpha at this pair. */
+static double alpha_rel_bound(double a, double b, double c, double dx, double dy, double sigma)
+{
+    double m = fabs(a) * dx * dx + fabs(c) * dy * dy + 2.0 * fabs(b * dx * dy);
+    return K_ALPHA * U32 * (4.0 + m + fabs(sigma));
+}
+
+/*
+ * Walk one pixel's list front to back. Fills `out` (capacity `cap`) with the
+ * composited entries, returns how many; writes T_final, n_contrib, colour sum
+ * and the ambiguity flag.
+ */
+static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int32_t end,
+                      double px, double py, contrib_t* out, int cap,
+                      double* T_out, int32_t* nc_out, double C[3], int* amb_out)
+{
+    double T = 1.0, errT = 0.0;
+    int cnt = 0, amb = 0;
+    int32_t last = 0;
+    C[0] = C[1] = C[2] = 0.0;
+    for (int32_t k = start; k < end; ++k) {
+        int32_t i = ids[k];
+        double mx = s->means[2 * i], my = s->means[2 * i + 1];
+        double a = s->conics[3 * i], b = s->conics[3 * i + 1], c = s->conics[3 * i + 2];
+        double o = s->opac[i];
+        double dx = px - mx, dy = py - my;
+        double sigma = -0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy;
+        double G = exp(sigma);
+        double ah = o * G;
+        double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;
+        double ea = alpha_rel_bound(a, b, c, dx, dy, sigma);
+        if (fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN) amb = 1;
+        if (alpha < ALPHA_MIN) continue;
+        if (fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32) amb = 1;
+        double test = T * (1.0 - alpha);
+        double et = errT + ea * alpha / (1.0 - alpha) + 4.0 * U32;
+        if (fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN) amb = 1;
+        if (test < T_MIN) break;
+        const double* col = s->colors + 3 * i;
+        C[0] += col[0] * alpha * T;
+        C[1] += col[1] * alpha * T;
+        C[2] += col[2] * alpha * T;
+        if (out && cnt < cap) {
+            contrib_t* e = &out[cnt];
+            e->k = k; e->alpha = alpha; e->T = T; e->G = G; e->dx = dx; e->dy = dy;
+            e->clamped = !(ah < ALPHA_MAX);
+        }
+        ++cnt;
+        T = test;
+        errT += ea * alpha / (1.0 - alpha) + 2.0 * U32;
+        last = k - start + 1;
+    }
+    *T_out = T;
+    *nc_out = last;
+    *amb_out = amb;
+    return cnt;
+}
+
+static int threads_used(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int gso_threads(void) { return threads_used(); }
+
+/*
+ * Forward over the tiles listed in `tiles` (or all tiles if tiles == NULL).
+ * image [H][W][3], final_T [H][W], n_contrib [H][W], amb [H][W]: only pixels
+ * of processed tiles are written.
+ */
+int gso_forward(int W, int H, const int32_t* ranges, const int32_t* ids,
+                const double* means, const double* conics, const double* colors, const double* opac,
+                const double* bg, const int32_t* tiles, int ntiles,
+                double* image, double* final_T, int32_t* n_contrib, uint8_t* amb)
+{
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE, GY = (H + TILE - 1) / TILE;
+    int nt = tiles ? ntiles : GX * GY;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ti = 0; ti < nt; ++ti) {
+        int t = tiles ? tiles[ti] : ti;
+        int tx = t % GX, ty = t / GX;
+        int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+        for (int ly = 0; ly < TILE; ++ly) {
+            int y = ty * TILE + ly;
+            if (y >= H) break;
+            for (int lx = 0; lx < TILE; ++lx) {
+                int x = tx * TILE + lx;
+                if (x >= W) break;
+                double T, C[3];
+                int32_t nc;
+                int a;
+                walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, NULL, 0, &T, &nc, C, &a);
+                size_t p = (size_t)y * W + x;
+                image[3 * p + 0] = C[0] + T * s.bg[0];
+                image[3 * p + 1] = C[1] + T * s.bg[1];
+                image[3 * p + 2] = C[2] + T * s.bg[2];
+                final_T[p] = T;
+                n_contrib[p] = nc;
+                amb[p] = (uint8_t)a;
+            }
+        }
+    }
+    return threads_used();
+}
+
+/*
+ * Backward over the listed tiles. grads [n][9] = (dmean x, dmean y, da, db, dc,
+ * dr, dg, db_colour, dopacity), accum_w [n]; both are ADDED to (caller zeroes).
+ * dimg [H][W][3] is the upstream gradient g.
+ */
+int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
+                 const double* means, const double* conics, const double* colors, const double* opac,
+                 const double* bg, const double* dimg, const int32_t* tiles, int ntiles,
+                 double* grads, double* accum_w)
+{
+    (void)n;
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE, GY = (H + TILE - 1) / TILE;
+    int nt = tiles ? ntiles : GX * GY;
+#pragma omp parallel
+    {
+        int cap = 0;
+        contrib_t* buf = NULL;
+        double* part = NULL;  /* per tile-list entry: 9 grads + accum weight */
+        int part_cap = 0;
+#pragma omp for schedule(dynamic, 1)
+        for (int ti = 0; ti < nt; ++ti) {
+            int t = tiles ? tiles[ti] : ti;
+            int tx = t % GX, ty = t / GX;
+            int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+            int L = end - start;
+            if (L <= 0) continue;
+            if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
+            if (L > part_cap) { free(part); part_cap = L; part = (double*)malloc(sizeof(double) * 10 * part_cap); }
+            memset(part, 0, sizeof(double) * 10 * L);
+            for (int ly = 0; ly < TILE; ++ly) {
+                int y = ty * TILE + ly;
+                if (y >= H) break;
+                for (int lx = 0; lx < TILE; ++lx) {
+                    int x = tx * TILE + lx;
+                    if (x >= W) break;
+                    double T, C[3];
+                    int32_t nc;
+                    int a;
+                    int cnt = walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, buf, cap, &T, &nc, C, &a);
+                    size_t p = (size_t)y * W + x;
+                    double g[3] = {dimg[3 * p], dimg[3 * p + 1], dimg[3 * p + 2]};
+                    /* S = sum over composited splats behind + T_final bg */
+                    double S[3] = {T * s.bg[0], T * s.bg[1], T * s.bg[2]};
+                    for (int e = cnt - 1; e >= 0; --e) {
+                        const contrib_t* q = &buf[e];
+                        int32_t i = ids[q->k];
+                        const double* col = s.colors + 3 * i;
+                        double al = q->alpha, Ti = q->T;
+                        double dal = 0.0;
+                        for (int ch = 0; ch < 3; ++ch)
+                            dal += g[ch] * (col[ch] * Ti - S[ch] / (1.0 - al));
+                        double* o = part + 10 * (q->k - start);
+                        double w = al * Ti;
+                        o[5] += w * g[0];
+                        o[6] += w * g[1];
+                        o[7] += w * g[2];
+                        if (!q->clamped) {
+                            double a_ = s.conics[3 * i], b_ = s.conics[3 * i + 1], c_ = s.conics[3 * i + 2];
+                            double ds = al * dal;
+                            o[0] += (a_ * q->dx + b_ * q->dy) * ds;
+                            o[1] += (b_ * q->dx + c_ * q->dy) * ds;
+                            o[2] += -0.5 * q->dx * q->dx * ds;
+                            o[3] += -q->dx * q->dy * ds;
+                            o[4] += -0.5 * q->dy * q->dy * ds;
+                            o[8] += q->G * dal;
+                        }
+                        o[9] += w;
+                        S[0] += col[0] * w;
+                        S[1] += col[1] * w;
+                        S[2] += col[2] * w;
+                    }
+                }
+            }
+#pragma omp critical(gso_merge)
+            {
+                for (int k = 0; k < L; ++k) {
+                    const double* o = part + 10 * k;
+                    int32_t i = ids[start + k];
+                    for (int f = 0; f < 9; ++f) grads[9 * (size_t)i + f] += o[f];
+                    accum_w[i] += o[9];
+                }
+            }
+        }
+        free(buf);
+        free(part);
+    }
+    return threads_used();
+}

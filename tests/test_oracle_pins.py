@@ -1,0 +1,332 @@
+"""Pins for the CPU oracle, against things other than itself.
+
+* a brute-force composite with no tiles (numpy, separate code);
+* hand-derived closed forms (tests/golden/closed_forms.json) and the
+  Gaussian density of scipy.stats.multivariate_normal (pins the conic
+  convention: conic = Sigma^-1 with b the off-diagonal entry);
+* central finite differences of the forward (pins every gradient field);
+* exact identities (colour-gradient sum, weight sum, linearity, tile
+  translation) and the compositing invariants;
+* a naive per-tile membership loop for binning and sort order.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.stats
+
+import oracle
+import scenes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _scene_from_case(case):
+    sp = case["splats"]
+    return scenes.custom_scene(
+        case["width"], case["height"],
+        means2d=[s["mean"] for s in sp], sigmas=[s["sigma"] for s in sp],
+        thetas=[s.get("theta", 0.0) for s in sp], opacities=[s["opacity"] for s in sp],
+        colors=[s["color"] for s in sp], depths=[s["depth"] for s in sp],
+        background=case.get("background"))
+
+
+def _tiled(sc, **kw):
+    return oracle.run_scene(sc, **kw)
+
+
+def _loss(sc, ids, rng_, means, conics, colors, opac, g):
+    out = oracle.rasterize_fwd(means, conics, colors, opac, sc.background, sc.width, sc.height, rng_, ids)
+    return float(np.sum(out["image"] * g))
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_closed_forms(case):
+    sc = _scene_from_case(case)
+    out = _tiled(sc, backward=False)
+    x, y = case["at"]
+    np.testing.assert_allclose(out["image"][y, x], case["image"], atol=case["tol"], rtol=0)
+    assert abs(out["final_T"][y, x] - case["final_T"]) <= case["tol"]
+    assert out["n_contrib"][y, x] == case["n_contrib"]
+
+
+def test_density_matches_scipy_mvn():
+    """One anisotropic splat: every pixel equals colour * min(0.99, o * G) with
+    G the unnormalised Gaussian density of covariance inv([[a, b], [b, c]])."""
+    sc = scenes.custom_scene(32, 32, means2d=[[13.3, 17.9]], sigmas=[[2.5, 5.0]], thetas=[0.6],
+                             opacities=[0.8], colors=[[0.3, 0.6, 0.9]], depths=[1.0])
+    out = _tiled(sc, backward=False)
+    a, b, c = sc.conics[0].astype(np.float64)
+    cov = np.linalg.inv(np.array([[a, b], [b, c]]))
+    mvn = scipy.stats.multivariate_normal(mean=sc.means2d[0].astype(np.float64), cov=cov)
+    ys, xs = np.mgrid[0:32, 0:32]
+    pts = np.stack([xs.ravel() + 0.5, ys.ravel() + 0.5], axis=1)
+    G = mvn.pdf(pts) * 2.0 * math.pi * math.sqrt(np.linalg.det(cov))
+    alpha = np.minimum(0.99, float(sc.opacities[0]) * G)
+    alpha = np.where(alpha >= 1.0 / 255.0, alpha, 0.0)
+    exp_img = alpha[:, None] * sc.colors[0].astype(np.float64)[None, :]
+    np.testing.assert_allclose(out["image"].reshape(-1, 3), exp_img, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(out["final_T"].ravel(), 1.0 - alpha, atol=1e-12)
+
+
+# ----------------------------------------------------------- brute force pins
+
+def _ragged_scene(seed, W=50, H=37, n=40):
+    rng = np.random.default_rng(seed)
+    return scenes.custom_scene(
+        W, H, means2d=np.stack([rng.uniform(-5, W + 5, n), rng.uniform(-5, H + 5, n)], 1),
+        sigmas=rng.uniform(0.7, 7.0, (n, 2)), thetas=rng.uniform(0, math.pi, n),
+        opacities=rng.uniform(0.05, 1.0, n), colors=rng.uniform(0, 1, (n, 3)),
+        depths=rng.uniform(0.1, 10, n), background=rng.uniform(0, 1, 3), seed=seed)
+
+
+@pytest.mark.parametrize("maker", [
+    lambda: scenes.make_scene("tiny", 0), lambda: scenes.make_scene("tiny", 1),
+    lambda: scenes.make_scene("tiny", 2), lambda: _ragged_scene(3), lambda: _ragged_scene(4),
+    lambda: scenes.make_scene("early", 0, n=800),
+], ids=["tiny0", "tiny1", "tiny2", "ragged3", "ragged4", "early-800"])
+def test_tiled_equals_bruteforce(maker):
+    sc = maker()
+    out = _tiled(sc, backward=False)
+    img, T, _ = oracle.composite_bruteforce(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.depths,
+                                            sc.radii, sc.background, sc.width, sc.height)
+    np.testing.assert_allclose(out["image"], img, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(out["final_T"], T, atol=1e-12, rtol=0)
+
+
+def test_compositing_invariants():
+    sc = scenes.make_scene("tiny", 0)
+    out = _tiled(sc, backward=False)
+    T = out["final_T"]
+    assert np.all(T <= 1.0) and np.all(T >= 1e-4)
+    lens = out["tile_ranges"][:, 1] - out["tile_ranges"][:, 0]
+    GX, _ = oracle.grid(sc.width, sc.height)
+    ys, xs = np.mgrid[0:sc.height, 0:sc.width]
+    tile_of_px = (ys // 16) * GX + xs // 16
+    assert np.all(out["n_contrib"] <= lens[tile_of_px])
+    assert np.all(out["n_contrib"] >= 0)
+    # a pixel with no composited splat has T = 1
+    assert np.all(T[out["n_contrib"] == 0] == 1.0)
+
+
+# ---------------------------------------------------------------- binning
+
+def _naive_bins(sc):
+    """Per tile, loop over every splat and apply the float32 rectangle test."""
+    GX, GY = oracle.grid(sc.width, sc.height)
+    f = np.float32
+    lists = []
+    for ty in range(GY):
+        for tx in range(GX):
+            mem = []
+            for i in range(sc.n):
+                if not (sc.radii[i] > 0 and sc.depths[i] > 0):
+                    continue
+                r = f(sc.radii[i])
+                lo_x = math.floor(f(sc.means2d[i, 0] - r) * f(0.0625))
+                hi_x = math.floor(f(sc.means2d[i, 0] + r) * f(0.0625))
+                lo_y = math.floor(f(sc.means2d[i, 1] - r) * f(0.0625))
+                hi_y = math.floor(f(sc.means2d[i, 1] + r) * f(0.0625))
+                if lo_x <= tx <= hi_x and lo_y <= ty <= hi_y:
+                    mem.append((int(sc.depths[i:i + 1].view(np.uint32)[0]), i))
+            lists.append([i for _, i in sorted(mem)])
+    return lists
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_binning_matches_naive_membership(seed):
+    sc = _ragged_scene(seed, n=60)
+    # force some equal depths so the id tie-break is exercised
+    sc.depths[::3] = sc.depths[0]
+    ids, rng_ = oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    naive = _naive_bins(sc)
+    for t, lst in enumerate(naive):
+        s, e = rng_[t]
+        assert list(ids[s:e]) == lst, t
+    assert sum(len(x) for x in naive) == len(ids)
+
+
+def test_binning_invariants_tiny():
+    sc = scenes.make_scene("tiny", 0)
+    ids, rng_ = oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    tx0, tx1, ty0, ty1 = oracle.tile_rects(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    assert int(((tx1 - tx0) * (ty1 - ty0)).sum()) == len(ids)
+    nonempty = rng_[rng_[:, 1] > rng_[:, 0]]
+    assert nonempty[0, 0] == 0 and nonempty[-1, 1] == len(ids)
+    assert np.all(nonempty[1:, 0] == nonempty[:-1, 1])       # contiguous, in tile order
+    db = sc.depths.view(np.uint32)
+    for s, e in nonempty:
+        key = db[ids[s:e]].astype(np.int64) * (1 << 32) + ids[s:e]
+        assert np.all(np.diff(key) > 0)
+
+
+def test_rect_is_conservative():
+    """Every pixel where a splat reaches alpha >= 1/255 lies in a tile of its rectangle."""
+    sc = scenes.make_scene("tiny", 1)
+    tx0, tx1, ty0, ty1 = oracle.tile_rects(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    ys, xs = np.mgrid[0:sc.height, 0:sc.width]
+    for i in range(sc.n):
+        dx = xs + 0.5 - float(sc.means2d[i, 0])
+        dy = ys + 0.5 - float(sc.means2d[i, 1])
+        a, b, c = sc.conics[i].astype(np.float64)
+        al = float(sc.opacities[i]) * np.exp(-0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy)
+        yy, xx = np.nonzero(al >= 1.0 / 255.0)
+        assert np.all((xx // 16 >= tx0[i]) & (xx // 16 < tx1[i]) & (yy // 16 >= ty0[i]) & (yy // 16 < ty1[i]))
+
+
+def test_culled_splats_never_binned():
+    sc = _ragged_scene(5, n=20)
+    sc.radii[0] = 0
+    sc.depths[1] = -1.0
+    sc.depths[2] = 0.0
+    ids, _ = oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    assert not np.isin([0, 1, 2], ids).any()
+
+
+# ---------------------------------------------------------------- gradients
+
+def _fd_scene(seed, n=6, bg=None, clamp=False):
+    rng = np.random.default_rng(100 + seed)
+    op = rng.uniform(0.3, 0.95, n)
+    means = rng.uniform(3, 13, (n, 2))
+    sig = rng.uniform(1.5, 4.0, (n, 2))
+    if clamp:
+        # two near-opaque splats centred close to a pixel centre: o G > 0.99 there
+        op[:2] = [1.0, 0.995]
+        means[:2] = [[8.6, 8.4], [4.55, 11.45]]
+        sig[:2] = [[4.0, 4.0], [3.5, 3.0]]
+    return scenes.custom_scene(
+        16, 16, means2d=means, sigmas=sig,
+        thetas=rng.uniform(0, math.pi, n), opacities=op, colors=rng.uniform(0, 1, (n, 3)),
+        depths=rng.uniform(0.1, 10, n), background=bg, seed=seed)
+
+
+def _margin(sc):
+    return oracle.composite_bruteforce(
+        sc.means2d, sc.conics, sc.colors, sc.opacities, sc.depths, sc.radii, sc.background,
+        sc.width, sc.height, return_margin=True)[3]
+
+
+def _first_clear(make, seeds):
+    """First scene whose decisions all sit > 1e-3 (relative) from a threshold,
+    so that a finite-difference step cannot cross one."""
+    for s in seeds:
+        sc = make(s)
+        if _margin(sc) > 1e-3:
+            return sc
+    raise AssertionError("no scene clear of the thresholds")
+
+
+def _fd_check(sc):
+    out = _tiled(sc)
+    ids, rng_ = out["sorted_ids"], out["tile_ranges"]
+    base = [sc.means2d.astype(np.float64), sc.conics.astype(np.float64),
+            sc.colors.astype(np.float64), sc.opacities.astype(np.float64)]
+    g = sc.dL_dimage.astype(np.float64)
+    fields = [("dmeans2d", 0, 2), ("dconics", 1, 3), ("dcolors", 2, 3), ("dopacities", 3, 1)]
+    for name, arg, width in fields:
+        an = out[name].reshape(sc.n, width)
+        fd = np.zeros_like(an)
+        for i in range(sc.n):
+            for k in range(width):
+                vals = []
+                for sgn in (+1, -1):
+                    p = [b.copy() for b in base]
+                    view = p[arg].reshape(sc.n, width)
+                    h = 1e-6 * max(1.0, abs(view[i, k]))
+                    view[i, k] += sgn * h
+                    vals.append(_loss(sc, ids, rng_, *p, g))
+                fd[i, k] = (vals[0] - vals[1]) / (2 * h)
+        scale = max(np.abs(an).max(), 1e-3)
+        np.testing.assert_allclose(an, fd, atol=1e-6 * scale, rtol=1e-6, err_msg=name)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_gradients_match_central_differences(seed):
+    _fd_check(_first_clear(_fd_scene, range(10 * seed, 10 * seed + 10)))
+
+
+def test_gradients_fd_with_background():
+    _fd_check(_first_clear(lambda s: _fd_scene(s, bg=[0.3, 0.5, 0.9]), range(50, 60)))
+
+
+def test_gradients_fd_with_clamped_splats():
+    sc = _first_clear(lambda s: _fd_scene(s, clamp=True), range(60, 90))
+    # the clamp is really hit: some pixel has opacity * G > 0.99
+    ys, xs = np.mgrid[0:16, 0:16]
+    a, b, c = sc.conics[0].astype(np.float64)
+    dx, dy = xs + 0.5 - float(sc.means2d[0, 0]), ys + 0.5 - float(sc.means2d[0, 1])
+    assert (float(sc.opacities[0]) * np.exp(-0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy) > 0.99).any()
+    _fd_check(sc)
+
+
+def _stacked(seed, n=6):
+    rng = np.random.default_rng(seed)
+    return scenes.custom_scene(16, 16, means2d=8.0 + rng.uniform(-1.5, 1.5, (n, 2)),
+                               sigmas=rng.uniform(6.0, 9.0, (n, 2)), thetas=rng.uniform(0, 3, n),
+                               opacities=rng.uniform(0.93, 0.97, n), colors=rng.uniform(0, 1, (n, 3)),
+                               depths=np.arange(1, n + 1, dtype=float), seed=seed)
+
+
+def test_gradients_fd_with_early_stop():
+    """Stacked dense splats so that most pixels stop early."""
+    sc = _first_clear(_stacked, range(5, 40))
+    out = _tiled(sc, backward=False)
+    assert (out["n_contrib"] < sc.n).mean() > 0.2      # the stop is actually exercised
+    _fd_check(sc)
+
+
+def test_colour_gradient_and_weight_identities():
+    sc = scenes.make_scene("tiny", 2)
+    out = _tiled(sc)
+    g = sc.dL_dimage.astype(np.float64)
+    one_minus_T = 1.0 - out["final_T"]
+    np.testing.assert_allclose(out["dcolors"].sum(axis=0), (g * one_minus_T[..., None]).sum(axis=(0, 1)),
+                               rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(out["accum_weight"].sum(), one_minus_T.sum(), rtol=1e-12)
+
+
+def test_gradients_linear_in_upstream():
+    sc = scenes.make_scene("tiny", 0)
+    rng = np.random.default_rng(9)
+    g1 = rng.normal(size=sc.dL_dimage.shape)
+    g2 = rng.normal(size=sc.dL_dimage.shape)
+    r1 = _tiled(sc, dL_dimage=g1)
+    r2 = _tiled(sc, dL_dimage=g2)
+    r3 = _tiled(sc, dL_dimage=2 * g1 - 3 * g2)
+    r0 = _tiled(sc, dL_dimage=np.zeros_like(g1))
+    for k in ["dmeans2d", "dconics", "dcolors", "dopacities"]:
+        np.testing.assert_allclose(r3[k], 2 * r1[k] - 3 * r2[k], atol=1e-10)
+        assert np.all(r0[k] == 0)
+
+
+def test_translation_by_one_tile():
+    """Moving every mean and the upstream gradient by (16, 16) on a larger image changes nothing."""
+    sc = _ragged_scene(8, W=40, H=40, n=30)
+    # means on a 1/1024 grid so that adding 16 is exact in float32
+    sc.means2d[:] = np.round(np.clip(sc.means2d, 2, 38) * 1024) / 1024
+    big = scenes.custom_scene(56, 56, means2d=sc.means2d + 16, sigmas=np.ones((sc.n, 2)),
+                              thetas=np.zeros(sc.n), opacities=sc.opacities, colors=sc.colors,
+                              depths=sc.depths, radii=sc.radii, background=sc.background)
+    big.conics[:] = sc.conics
+    g = np.zeros((56, 56, 3), dtype=np.float32)
+    g[16:, 16:] = sc.dL_dimage[:40, :40]
+    big.dL_dimage = g
+    a = _tiled(sc)
+    b = _tiled(big)
+    np.testing.assert_allclose(b["image"][16:, 16:], a["image"], atol=1e-13)
+    for k in ["dmeans2d", "dconics", "dcolors", "dopacities", "accum_weight"]:
+        if k == "accum_weight":
+            continue   # weight also collects from the border pixels outside the old image
+        np.testing.assert_allclose(b[k], a[k], atol=1e-11, rtol=1e-9, err_msg=k)
+
+
+def test_ambiguity_flags_only_near_thresholds():
+    sc = scenes.make_scene("early", 0)
+    out = _tiled(sc, backward=False)
+    frac = out["ambiguous"].mean()
+    assert frac < 1e-3, frac
