@@ -1,0 +1,162 @@
+"""libgsraster: tile-based Gaussian-splat rasterization (binning, forward,
+backward) as hand-written HIP kernels for the AMD Instinct MI355X (gfx950).
+
+This module is a thin binding over the C ABI of include/gsraster.h. The
+functions carry the C entry points' names; they check and marshal torch
+tensors (device memory, the current HIP stream) into the C call and allocate
+the outputs. Every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GS_FLAG_ACCUM_WEIGHT, GsError
+
+__all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_version", "GsError",
+           "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid"]
+
+TILE = 16
+
+
+def tile_grid(width: int, height: int) -> tuple[int, int]:
+    return (width + TILE - 1) // TILE, (height + TILE - 1) // TILE
+
+
+def gs_version() -> int:
+    return int(_lib.load().gs_version())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if t.numel() == 0:
+        # an empty view reports a NULL data pointer; pass its allocation instead
+        return ctypes.c_void_p(t.untyped_storage().data_ptr() or None)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class Bins:
+    """Result of gs_bin_tiles: sorted_ids [n_isect] int32, tile_ranges [GX*GY, 2] int32."""
+
+    def __init__(self, sorted_ids, tile_ranges, n_isect, width, height):
+        self.sorted_ids = sorted_ids
+        self.tile_ranges = tile_ranges
+        self.n_isect = n_isect
+        self.width = width
+        self.height = height
+
+
+def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int | None = None,
+                 stream=None) -> Bins:
+    """Bin splats into 16x16 tiles and sort each tile's list by depth.
+
+    Allocates sorted_ids with ``capacity`` slots (default: 4 per splat) and,
+    if the count read back exceeds it, reallocates and calls again."""
+    n = int(means2d.shape[0])
+    _need(means2d, "means2d", torch.float32, (n, 2))
+    _need(radii, "radii", torch.int32, (n,))
+    _need(depths, "depths", torch.float32, (n,))
+    lib = _lib.load()
+    dev = means2d.device
+    GX, GY = tile_grid(width, height)
+    cap = int(capacity) if capacity is not None else max(4 * n, 1)
+    ranges = torch.empty((GX * GY, 2), dtype=torch.int32, device=dev)
+    st = _stream(stream)
+    for _attempt in range(2):
+        ids = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+        ws_bytes = int(lib.gs_bin_tiles_workspace_size(n, cap, width, height))
+        ws = torch.empty((ws_bytes + 256,), dtype=torch.uint8, device=dev)
+        base = ws.data_ptr()
+        aligned = (base + 255) & ~255
+        n_isect = ctypes.c_int64(0)
+        status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(radii), _ptr(depths), width, height, cap,
+                                  _ptr(ids), _ptr(ranges), ctypes.byref(n_isect),
+                                  ctypes.c_void_p(aligned), ws_bytes, st)
+        if status == _lib.GS_ERR_CAPACITY:
+            cap = int(n_isect.value)
+            continue
+        _lib.check(status)
+        I = int(n_isect.value)
+        return Bins(ids[:I], ranges, I, width, height)
+    raise GsError(_lib.GS_ERR_CAPACITY, "binning capacity still too small after reallocation")
+
+
+def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int, height: int,
+                     tile_ranges, sorted_ids, stream=None):
+    """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W])."""
+    n = int(means2d.shape[0])
+    _need(means2d, "means2d", torch.float32, (n, 2))
+    _need(conics, "conics", torch.float32, (n, 3))
+    _need(colors, "colors", torch.float32, (n, 3))
+    _need(opacities, "opacities", torch.float32, (n,))
+    if background is not None:
+        _need(background, "background", torch.float32, (3,))
+    GX, GY = tile_grid(width, height)
+    _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
+    _need(sorted_ids, "sorted_ids", torch.int32)
+    dev = means2d.device
+    image = torch.empty((height, width, 3), dtype=torch.float32, device=dev)
+    final_T = torch.empty((height, width), dtype=torch.float32, device=dev)
+    n_contrib = torch.empty((height, width), dtype=torch.int32, device=dev)
+    _lib.check(_lib.load().gs_rasterize_fwd(
+        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
+        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _stream(stream)))
+    return image, final_T, n_contrib
+
+
+def gs_rasterize_bwd(means2d, conics, colors, opacities, background, width: int, height: int,
+                     tile_ranges, sorted_ids, final_T, n_contrib, dL_dimage, accum_weight: bool = False,
+                     out=None, stream=None):
+    """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
+    dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
+    per-splat accumulated weight [n]. ``out`` may pass preallocated outputs
+    (same dict keys) to keep allocation out of timed loops."""
+    n = int(means2d.shape[0])
+    _need(means2d, "means2d", torch.float32, (n, 2))
+    _need(conics, "conics", torch.float32, (n, 3))
+    _need(colors, "colors", torch.float32, (n, 3))
+    _need(opacities, "opacities", torch.float32, (n,))
+    if background is not None:
+        _need(background, "background", torch.float32, (3,))
+    GX, GY = tile_grid(width, height)
+    _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
+    _need(sorted_ids, "sorted_ids", torch.int32)
+    _need(final_T, "final_T", torch.float32, (height, width))
+    _need(n_contrib, "n_contrib", torch.int32, (height, width))
+    _need(dL_dimage, "dL_dimage", torch.float32, (height, width, 3))
+    dev = means2d.device
+    if out is None:
+        out = {"dL_dmeans2d": torch.empty((n, 2), dtype=torch.float32, device=dev),
+               "dL_dconics": torch.empty((n, 3), dtype=torch.float32, device=dev),
+               "dL_dcolors": torch.empty((n, 3), dtype=torch.float32, device=dev),
+               "dL_dopacities": torch.empty((n,), dtype=torch.float32, device=dev)}
+        if accum_weight:
+            out["accum_weight"] = torch.empty((n,), dtype=torch.float32, device=dev)
+    flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
+    _lib.check(_lib.load().gs_rasterize_bwd(
+        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
+        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
+        _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]), _ptr(out["dL_dcolors"]),
+        _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, _stream(stream)))
+    return out

@@ -1,0 +1,353 @@
+// gs_raster.hip -- gs_rasterize_fwd and gs_rasterize_bwd for gfx950.
+//
+// Both kernels run one 256-thread workgroup (4 wave64) per 16x16 tile; a
+// 16x16 tile of 256 pixels per workgroup is the decomposition on page
+// "Phase 5 step 30b — kernel-by-kernel timing" (section 結論と次着手). Each wave
+// owns one 8x8 quadrant of the tile (lane l -> pixel (l & 7, l >> 3) of the
+// quadrant), so a wave's pixels are as close together as possible: small
+// splats then touch fewer waves, which matters for the backward's per-wave
+// reductions.
+//
+// Splat parameters are staged through LDS in batches of 256 list entries:
+// each thread loads one entry (sorted id, then the splat's record) and writes
+// the per-splat alpha coefficients; the walk then reads them with broadcast
+// LDS loads. Optional outputs are template parameters, so a variant without
+// the accumulated weight carries no register, LDS slot or atomic for it (the
+// lesson of section 机制拆解 of the Spirula Studio page, where optional
+// feature arrays sized regardless of the switch halved occupancy).
+#include "gs_common.hpp"
+
+namespace gs {
+namespace {
+
+struct StageLds {
+    float4 a[kBlock];  // mean x, mean y, l11, l21
+    float4 b[kBlock];  // l22, log2(opacity), red, green
+    float c[kBlock];   // blue
+};
+
+__device__ __forceinline__ void quadrant_pixel(int tile, int GX, int& x, int& y)
+{
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    x = (tile % GX) * kTile + (w & 1) * 8 + (l & 7);
+    y = (tile / GX) * kTile + (w >> 1) * 8 + (l >> 3);
+}
+
+// Loads list entry `idx` into LDS slot `s`; returns the splat id.
+__device__ __forceinline__ int stage_entry(StageLds& S, int s, int id, const float2* __restrict__ means,
+                                           const float* __restrict__ conics,
+                                           const float* __restrict__ colors,
+                                           const float* __restrict__ opac, float& a, float& b, float& c,
+                                           float& o)
+{
+    const float2 m = means[id];
+    a = conics[3 * id + 0];
+    b = conics[3 * id + 1];
+    c = conics[3 * id + 2];
+    o = opac[id];
+    const AlphaCoef k = make_alpha_coef(m.x, m.y, a, b, c, o);
+    S.a[s] = make_float4(k.mx, k.my, k.l11, k.l21);
+    S.b[s] = make_float4(k.l22, k.lo, colors[3 * id + 0], colors[3 * id + 1]);
+    S.c[s] = colors[3 * id + 2];
+    return id;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int tiles,
+                                                     const int2* __restrict__ ranges,
+                                                     const int* __restrict__ ids,
+                                                     const float2* __restrict__ means,
+                                                     const float* __restrict__ conics,
+                                                     const float* __restrict__ colors,
+                                                     const float* __restrict__ opac,
+                                                     const float* __restrict__ bg, float* __restrict__ image,
+                                                     float* __restrict__ final_T, int* __restrict__ n_contrib)
+{
+    __shared__ StageLds S;
+    const int tile = xcd_tile(blockIdx.x, tiles);
+    if (tile >= tiles) return;
+    int x, y;
+    quadrant_pixel(tile, GX, x, y);
+    const bool inside = x < W && y < H;
+    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const int2 rg = ranges[tile];
+
+    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
+    int last = 0;
+    bool done = !inside;
+    for (int bs = rg.x; bs < rg.y; bs += kBlock) {
+        if (__syncthreads_count(done) == kBlock) break;  // every pixel of the tile has stopped
+        const int idx = bs + (int)threadIdx.x;
+        if (idx < rg.y) {
+            float a, b, c, o;
+            stage_entry(S, threadIdx.x, ids[idx], means, conics, colors, opac, a, b, c, o);
+        }
+        __syncthreads();
+        const int cnt = min(kBlock, rg.y - bs);
+        for (int j = 0; j < cnt; ++j) {
+            if (__ballot(!done) == 0) break;
+            if (done) continue;
+            const float4 A = S.a[j];
+            const float4 B = S.b[j];
+            const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
+            float dx, dy;
+            const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
+            if (al >= kAlphaMin) {
+                const float test = T * (1.0f - al);
+                if (test < kTMin) {
+                    done = true;
+                } else {
+                    const float wgt = al * T;
+                    C0 = __builtin_fmaf(B.z, wgt, C0);
+                    C1 = __builtin_fmaf(B.w, wgt, C1);
+                    C2 = __builtin_fmaf(S.c[j], wgt, C2);
+                    T = test;
+                    last = bs - rg.x + j + 1;
+                }
+            }
+        }
+    }
+    if (inside) {
+        const int p = y * W + x;
+        float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
+        if (bg) { b0 = bg[0]; b1 = bg[1]; b2 = bg[2]; }
+        image[3 * p + 0] = __builtin_fmaf(T, b0, C0);
+        image[3 * p + 1] = __builtin_fmaf(T, b1, C1);
+        image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
+        final_T[p] = T;
+        n_contrib[p] = last;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+//
+// Per (splat, pixel) pair the kernel forms the pixel's share of
+//   sum w g_r, sum w g_g, sum w g_b          (w = alpha T: colour gradient)
+//   sum s, sum s dx, sum s dy, sum s dx^2, sum s dx dy, sum s dy^2
+//                                          (s = dL/dsigma = alpha dL/dalpha)
+//   [sum w]                                (accumulated weight, optional)
+// and reduces them over the wave. The nine gradient fields are linear in
+// these sums (dmean = Q (sum s d), dconic = -(1/2 sum s dx^2, sum s dx dy,
+// 1/2 sum s dy^2), dopacity = sum s / opacity), so the per-splat constants are
+// applied once per (splat, tile) at the flush instead of once per pixel.
+//
+// Wave reduction of 9-10 values in 28 VALU ops instead of 54: one
+// v_permlane32_swap per pair of values folds the wave halves, one
+// v_permlane16_swap per pair of those folds rows, leaving 3 registers whose 4
+// rows each hold a different field; a 4-step DPP row scan finishes them. The
+// four row-leader lanes add their 3 values into the workgroup's LDS slot of
+// the splat, and after the batch one thread per splat sends the slot to the
+// global gradients with one float atomic per field.
+// ---------------------------------------------------------------------------
+constexpr int kSlot = 12;  // 3 registers x 4 rows
+
+template <bool AW>
+__global__ __launch_bounds__(kBlock) void bwd_kernel(
+    int W, int H, int GX, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
+    const float2* __restrict__ means, const float* __restrict__ conics, const float* __restrict__ colors,
+    const float* __restrict__ opac, const float* __restrict__ bg, const float* __restrict__ final_T,
+    const int* __restrict__ n_contrib, const float* __restrict__ dimg, float* __restrict__ d_means,
+    float* __restrict__ d_conics, float* __restrict__ d_colors, float* __restrict__ d_opac,
+    float* __restrict__ accum_w)
+{
+    __shared__ StageLds S;
+    __shared__ float part[kBlock][kSlot];
+    __shared__ int wave_max[4];
+
+    const int tile = xcd_tile(blockIdx.x, tiles);
+    if (tile >= tiles) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x, y;
+    quadrant_pixel(tile, GX, x, y);
+    const bool inside = x < W && y < H;
+    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const int2 rg = ranges[tile];
+
+    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    int nc = 0;
+    if (inside) {
+        const int p = y * W + x;
+        T = final_T[p];
+        // never walk past the tile's list, whatever n_contrib holds
+        nc = min(max(n_contrib[p], 0), rg.y - rg.x);
+        g0 = dimg[3 * p + 0];
+        g1 = dimg[3 * p + 1];
+        g2 = dimg[3 * p + 2];
+    }
+    // colour "behind" the current splat, normalised by the transmittance
+    // after it; starts as the background
+    float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;
+    if (bg) { B0 = bg[0]; B1 = bg[1]; B2 = bg[2]; }
+
+    const int wmax = wave_max_i32(nc);
+    if (lane == 0) wave_max[wv] = wmax;
+    __syncthreads();
+    const int tmax = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    if (tmax == 0) return;
+
+    const bool row_leader = (lane & 15) == 15;
+    const int row = lane >> 4;
+
+    for (int bs = ((tmax - 1) / kBlock) * kBlock; bs >= 0; bs -= kBlock) {
+        __syncthreads();  // previous batch fully flushed before LDS is reused
+        const int k = bs + (int)threadIdx.x;
+        int id = -1;
+        float ca = 0.0f, cb = 0.0f, cc = 0.0f, co = 1.0f;
+        if (k < tmax) {
+            id = stage_entry(S, threadIdx.x, ids[rg.x + k], means, conics, colors, opac, ca, cb, cc, co);
+#pragma unroll
+            for (int f = 0; f < kSlot; ++f) part[threadIdx.x][f] = 0.0f;
+        }
+        __syncthreads();
+
+        if (wmax > bs) {
+            for (int j = min(kBlock, wmax - bs) - 1; j >= 0; --j) {
+                const float4 A = S.a[j];
+                const float4 Bq = S.b[j];
+                const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
+                float dx, dy;
+                const float ar = alpha_raw(kf, px, py, dx, dy);
+                const float al = fminf(kAlphaMax, ar);
+                const bool contrib = (bs + j < nc) && (al >= kAlphaMin);
+                if (__ballot(contrib) == 0) continue;
+
+                const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
+                const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
+                const float cr = Bq.z, cg = Bq.w, cbl = S.c[j];
+                const float e0 = cr - B0, e1 = cg - B1, e2 = cbl - B2;
+                const float dal = Ti * __builtin_fmaf(e0, g0, __builtin_fmaf(e1, g1, e2 * g2));
+                B0 = __builtin_fmaf(ae, e0, B0);
+                B1 = __builtin_fmaf(ae, e1, B1);
+                B2 = __builtin_fmaf(ae, e2, B2);
+                T = Ti;
+                const float w = ae * Ti;
+                const float s = (ar < kAlphaMax) ? ae * dal : 0.0f;  // clamped alpha: no sigma path
+                const float sdx = s * dx, sdy = s * dy;
+
+                const float r0 = fold32(w * g0, w * g1);
+                const float r1 = fold32(w * g2, s);
+                const float r2 = fold32(sdx, sdy);
+                const float r3 = fold32(sdx * dx, sdx * dy);
+                const float r4 = fold32(sdy * dy, AW ? w : sdy * dy);
+                const float q0 = row_sum16(fold16(r0, r1));
+                const float q1 = row_sum16(fold16(r2, r3));
+                const float q2 = row_sum16(fold16(r4, r4));
+                if (row_leader) {
+                    atomicAdd(&part[j][row * 3 + 0], q0);
+                    atomicAdd(&part[j][row * 3 + 1], q1);
+                    atomicAdd(&part[j][row * 3 + 2], q2);
+                }
+            }
+        }
+        __syncthreads();
+
+        // Flush: thread t owns the entry it staged. Slot layout (row-major
+        // 4 x 3): row 0 = (w g_r, s dx, s dy^2), row 1 = (w g_b, s dx^2, s dy^2),
+        // row 2 = (w g_g, s dy, [w]), row 3 = (s, s dx dy, [w]).
+        if (id >= 0) {
+            const float* P = part[threadIdx.x];
+            const float Swr = P[0], Sdx = P[1], Sdyy = P[2];
+            const float Swb = P[3], Sdxx = P[4];
+            const float Swg = P[6], Sdy = P[7];
+            const float Ss = P[9], Sdxy = P[10];
+            const float Sw = AW ? P[8] : 0.0f;
+            const bool any = (Swr != 0.0f) | (Swg != 0.0f) | (Swb != 0.0f) | (Ss != 0.0f) |
+                             (Sdx != 0.0f) | (Sdy != 0.0f) | (Sdxx != 0.0f) | (Sdxy != 0.0f) |
+                             (Sdyy != 0.0f) | (Sw != 0.0f);
+            if (any) {
+                unsafeAtomicAdd(&d_means[2 * id + 0], __builtin_fmaf(ca, Sdx, cb * Sdy));
+                unsafeAtomicAdd(&d_means[2 * id + 1], __builtin_fmaf(cb, Sdx, cc * Sdy));
+                unsafeAtomicAdd(&d_conics[3 * id + 0], -0.5f * Sdxx);
+                unsafeAtomicAdd(&d_conics[3 * id + 1], -Sdxy);
+                unsafeAtomicAdd(&d_conics[3 * id + 2], -0.5f * Sdyy);
+                unsafeAtomicAdd(&d_colors[3 * id + 0], Swr);
+                unsafeAtomicAdd(&d_colors[3 * id + 1], Swg);
+                unsafeAtomicAdd(&d_colors[3 * id + 2], Swb);
+                unsafeAtomicAdd(&d_opac[id], Ss / co);
+                if (AW) unsafeAtomicAdd(&accum_w[id], Sw);
+            }
+        }
+    }
+}
+
+__global__ void zero_kernel(float* __restrict__ p, long long n)
+{
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+hipError_t zero_fill(float* p, long long n, hipStream_t st)
+{
+    if (n <= 0) return hipSuccess;
+    zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                      const float* opacities, const float* background, int32_t width,
+                                      int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                      float* image, float* final_T, int32_t* n_contrib, gs_stream_t stream_)
+{
+    hipStream_t st = (hipStream_t)stream_;
+    GS_CHECK_ARG(n >= 0, "gs_rasterize_fwd: n = %d < 0", n);
+    GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
+                 "gs_rasterize_fwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
+    GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
+    GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
+    GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
+    const int GX = grid_x(width), tiles = GX * grid_y(height);
+    fwd_kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, tiles, (const int2*)tile_ranges, sorted_ids,
+                                                   (const float2*)means2d, conics, colors, opacities, background,
+                                                   image, final_T, n_contrib);
+    GS_HIP(hipGetLastError());
+    return GS_OK;
+}
+
+extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                      const float* opacities, const float* background, int32_t width,
+                                      int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                      const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                                      float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                      float* dL_dopacities, float* accum_weight, uint32_t flags,
+                                      gs_stream_t stream_)
+{
+    hipStream_t st = (hipStream_t)stream_;
+    GS_CHECK_ARG(n >= 0, "gs_rasterize_bwd: n = %d < 0", n);
+    GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
+                 "gs_rasterize_bwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
+    GS_CHECK_ARG((flags & ~(uint32_t)GS_FLAG_ACCUM_WEIGHT) == 0, "gs_rasterize_bwd: unknown flags 0x%x", flags);
+    const bool aw = (flags & GS_FLAG_ACCUM_WEIGHT) != 0;
+    GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_bwd: NULL splat array");
+    GS_CHECK_ARG(n == 0 || (dL_dmeans2d && dL_dconics && dL_dcolors && dL_dopacities),
+                 "gs_rasterize_bwd: NULL gradient output");
+    GS_CHECK_ARG(!aw || n == 0 || accum_weight, "gs_rasterize_bwd: GS_FLAG_ACCUM_WEIGHT with accum_weight NULL");
+    GS_CHECK_ARG(tile_ranges && final_T && n_contrib && dL_dimage, "gs_rasterize_bwd: NULL image-side array");
+    GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_bwd: sorted_ids is NULL");
+    if (n == 0) return GS_OK;
+    GS_HIP(zero_fill(dL_dmeans2d, 2ll * n, st));
+    GS_HIP(zero_fill(dL_dconics, 3ll * n, st));
+    GS_HIP(zero_fill(dL_dcolors, 3ll * n, st));
+    GS_HIP(zero_fill(dL_dopacities, n, st));
+    if (aw) GS_HIP(zero_fill(accum_weight, n, st));
+    const int GX = grid_x(width), tiles = GX * grid_y(height);
+    if (aw)
+        bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
+            width, height, GX, tiles, (const int2*)tile_ranges, sorted_ids, (const float2*)means2d, conics, colors,
+            opacities, background, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics, dL_dcolors,
+            dL_dopacities, accum_weight);
+    else
+        bwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(
+            width, height, GX, tiles, (const int2*)tile_ranges, sorted_ids, (const float2*)means2d, conics, colors,
+            opacities, background, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics, dL_dcolors,
+            dL_dopacities, nullptr);
+    GS_HIP(hipGetLastError());
+    return GS_OK;
+}

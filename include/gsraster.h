@@ -1,0 +1,201 @@
+/*
+ * gsraster.h -- C ABI of libgsraster: tile-based Gaussian-splat rasterization
+ * (binning, forward, backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What the three calls compute
+ * ----------------------------
+ * The pages this library follows are the Spirula Studio article on the
+ * rasterize_bwd_2d kernel ("从 8.6 KB 到 4.2 KB ...", sections 机制拆解 and
+ * 亲手验证: the 2D screen-space backward pass, run once per training
+ * iteration, with an optional per-splat accumulated-weight output; a fixed
+ * benchmark load of 2,000,000 splats at 1237x822 with raster fwd / raster bwd
+ * / tile isect timings) and the 3dgs-rs log "Phase 5 step 30b — kernel-by-
+ * kernel timing" (section 計測結果: the per-iteration kernels emit_pairs,
+ * radix_hist / radix_scatter, extract_offsets, rasterize_f32 and
+ * rasterize_backwards; section ホットスポット ranking item 1: the backward
+ * accumulates nine per-splat gradient fields -- 2D mean, conic, RGB, opacity
+ * -- over all pixels; section 結論と次着手: a 16x16 tile of 256 pixels per
+ * workgroup). The pages give no formula. The compositing rule implemented is
+ * the standard one of tile-based 3D Gaussian splatting:
+ *
+ *   pixel (x, y) has centre p = (x + 0.5, y + 0.5); d = p - mean
+ *   sigma = -1/2 (a dx^2 + c dy^2) - b dx dy  with conic (a, b, c) the upper
+ *           triangle of the inverse 2D covariance (b is the off-diagonal entry)
+ *   alpha = min(0.99, opacity * exp(sigma))
+ *   each pixel walks its tile's list front to back:
+ *     alpha < 1/255              -> skip the splat
+ *     T * (1 - alpha) < 1e-4     -> stop; this splat is not composited
+ *     otherwise                  -> C += colour * alpha * T;  T *= 1 - alpha
+ *   image = C + T * background;  final_T = T;
+ *   n_contrib = 1 + list position of the last composited splat (0 if none)
+ *
+ * The backward returns dL/dparam for L = sum_p <dL_dimage_p, image_p>, with
+ * every skip / stop / clamp decision held as the forward took it (a clamped
+ * alpha passes no gradient to opacity, conic or mean).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers marked "device" are caller-owned device memory (hipMalloc or a
+ *    torch tensor), contiguous, float32 / int32 as stated. The library never
+ *    allocates or frees device memory; scratch comes in as `workspace`.
+ *  - All work is enqueued on `stream` (0 = the null stream) in stream order;
+ *    calls return before the work finishes, except gs_bin_tiles, which waits
+ *    once to read the intersection count back to the host.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Tiles are 16x16 pixels; tile ids are row-major: ty * GX + tx with
+ *    GX = ceil(width / 16), GY = ceil(height / 16).
+ *  - Images are HWC, row-major, y pointing down: image[(y * width + x) * 3 + ch].
+ *  - Errors: arguments the host can check (NULL where a pointer is required,
+ *    n < 0, width or height <= 0 or too large, unknown flags) return
+ *    GS_ERR_INVALID_ARG before any work is enqueued. A failing HIP call
+ *    returns GS_ERR_HIP. gs_last_error() then describes the failure (a
+ *    thread-local string, valid until the thread's next call). Faults inside
+ *    kernels surface at the caller's next synchronisation.
+ *  - Data preconditions (the caller's duty, not checked): finite values,
+ *    positive-definite conics, opacity in [0, 1], radii from a conservative
+ *    projection. Splats with radius <= 0, depth not > 0 or a non-finite mean
+ *    are culled by the binning.
+ *  - Calls are re-entrant; there is no global mutable state other than the
+ *    thread-local error string.
+ */
+#ifndef GSRASTER_H
+#define GSRASTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without pulling in the HIP headers: an opaque stream handle. */
+typedef struct ihipStream_t* gs_stream_t;
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARG = 1,
+    GS_ERR_CAPACITY = 2,
+    GS_ERR_HIP = 3,
+    GS_ERR_UNSUPPORTED = 4
+} gs_status;
+
+enum { GS_TILE = 16 };
+
+/* gs_rasterize_bwd flags */
+enum {
+    /* Also write accum_weight[i] = sum over composited (pixel, splat i) pairs of
+     * alpha * T: the "accum weight" optional feature of the Spirula Studio
+     * page (section 机制拆解). Without it no register, LDS or atomic is spent
+     * on the weight. */
+    GS_FLAG_ACCUM_WEIGHT = 1u << 0
+};
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* gs_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int gs_version(void);
+
+/*
+ * Binning: the per-iteration tile-binning, sort and tile-range stages
+ * (emit_pairs, radix_hist, radix_scatter, extract_offsets in the timing
+ * table of "Phase 5 step 30b — kernel-by-kernel timing", section 計測結果;
+ * the "tile isect" line of raster_bench on the Spirula Studio page, section
+ * 亲手验证).
+ *
+ * Each live splat covers the tile rectangle [tx0, tx1) x [ty0, ty1) computed
+ * in float32 as
+ *     tx0 = clamp(floor((mean_x - r) * 0.0625),       0, GX)
+ *     tx1 = clamp(floor((mean_x + r) * 0.0625) + 1,   0, GX)
+ * (and likewise in y), r = (float)radii[i]. Each tile's list holds the splats
+ * covering it, ordered by the float32 bit pattern of depth, ties broken by
+ * ascending splat id (so the result is unique). Lists are concatenated in
+ * tile-id order into sorted_ids; tile_ranges[t] = [start, end) into it
+ * ({0, 0} for an empty tile).
+ *
+ *   n            number of splats (>= 0)
+ *   means2d      device float [n][2], pixels
+ *   radii        device int32 [n], screen radius in pixels (<= 0: culled)
+ *   depths       device float [n] (not > 0: culled)
+ *   width,height image size in pixels, 1 .. 32768 each
+ *   capacity     number of int32 slots in sorted_ids
+ *   sorted_ids   device int32 [capacity] (out)
+ *   tile_ranges  device int32 [GX*GY][2] (out)
+ *   n_isect      host int64 (out): total number of (splat, tile) pairs
+ *   workspace    device scratch of at least gs_bin_tiles_workspace_size(...)
+ *                bytes, 256-byte aligned
+ *
+ * Synchronises `stream` once (to read the count). If capacity < *n_isect it
+ * returns GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges
+ * untouched: allocate *n_isect slots (and the matching workspace) and call
+ * again. Totals above 2^31 - 1 return GS_ERR_UNSUPPORTED.
+ */
+size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32_t width, int32_t height);
+
+gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
+                       int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
+                       int32_t* tile_ranges, int64_t* n_isect, void* workspace,
+                       size_t workspace_bytes, gs_stream_t stream);
+
+/*
+ * Forward composite (rasterize_f32 in the timing table of "Phase 5 step 30b —
+ * kernel-by-kernel timing", section 計測結果; the "raster fwd" line of
+ * raster_bench). One workgroup of 256 threads per 16x16 tile.
+ *
+ *   n                 number of splats
+ *   means2d           device float [n][2]
+ *   conics            device float [n][3] = (a, b, c) of the inverse covariance
+ *   colors            device float [n][3]
+ *   opacities         device float [n]
+ *   background        device float [3], or NULL for black
+ *   width, height     image size
+ *   tile_ranges       device int32 [GX*GY][2], from gs_bin_tiles
+ *   sorted_ids        device int32, from gs_bin_tiles
+ *   image             device float [height][width][3] (out)
+ *   final_T           device float [height][width]    (out)
+ *   n_contrib         device int32 [height][width]    (out)
+ */
+gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
+                           const float* opacities, const float* background, int32_t width,
+                           int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                           float* image, float* final_T, int32_t* n_contrib, gs_stream_t stream);
+
+/*
+ * Backward (rasterize_backwards in "Phase 5 step 30b — kernel-by-kernel
+ * timing", sections 計測結果 and ホットスポット ranking; rasterize_bwd_2d on the
+ * Spirula Studio page). One workgroup (4 wave64) per tile walks the tile's
+ * list in reverse from the largest n_contrib of its pixels, recovers T by
+ * division, and accumulates the nine gradient fields per splat; partial sums
+ * are reduced inside each wave and across the workgroup before one global
+ * float atomic per (splat, tile, field).
+ *
+ *   inputs as gs_rasterize_fwd, plus
+ *   final_T, n_contrib   device, as written by gs_rasterize_fwd for the same
+ *                        scene (the backward trusts them)
+ *   dL_dimage            device float [height][width][3]
+ *   dL_dmeans2d          device float [n][2] (out)
+ *   dL_dconics           device float [n][3] (out): partials w.r.t. the stored
+ *                        scalars a, b, c (b enters sigma as -b dx dy)
+ *   dL_dcolors           device float [n][3] (out)
+ *   dL_dopacities        device float [n]    (out)
+ *   accum_weight         device float [n] (out), required iff
+ *                        GS_FLAG_ACCUM_WEIGHT, else ignored (may be NULL)
+ *   flags                bitwise OR of GS_FLAG_*
+ *
+ * Outputs are zero-filled on `stream` first; splats in no list get exact
+ * zeros. Float atomics make the summation order, and so the last bits of the
+ * result, vary from run to run.
+ */
+gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
+                           const float* opacities, const float* background, int32_t width,
+                           int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                           const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                           float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                           float* dL_dopacities, float* accum_weight, uint32_t flags,
+                           gs_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSRASTER_H */

@@ -115,21 +115,29 @@ def bin_tiles(means2d, radii, depths, width: int, height: int):
     ``ty * GX + tx``; the lists are concatenated in tile-id order."""
     GX, GY = grid(width, height)
     tx0, tx1, ty0, ty1 = tile_rects(means2d, radii, depths, width, height)
-    nx = tx1 - tx0
-    ny = ty1 - ty0
+    # Splats in (depth bits, id) order: a stable sort of the depth bit patterns
+    # over ids listed in ascending order.
+    dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)
+    order = np.argsort(dbits, kind="stable")
+    nx = (tx1 - tx0)[order]
+    ny = (ty1 - ty0)[order]
     cnt = nx * ny
     total = int(cnt.sum())
-    ids = np.repeat(np.arange(len(cnt), dtype=np.int64), cnt)
-    # index of each intersection within its splat's rectangle, row-major
+    # every (splat, tile) pair, splat by splat in that order, tiles row-major
+    ids = np.repeat(order.astype(np.int32), cnt)
     first = np.repeat(np.cumsum(cnt) - cnt, cnt)
     local = np.arange(total, dtype=np.int64) - first
+    del first
     nxr = np.repeat(nx, cnt)
-    tx = np.repeat(tx0, cnt) + local % np.maximum(nxr, 1)
-    ty = np.repeat(ty0, cnt) + local // np.maximum(nxr, 1)
+    tx = np.repeat(tx0[order], cnt) + local % np.maximum(nxr, 1)
+    ty = np.repeat(ty0[order], cnt) + local // np.maximum(nxr, 1)
+    del local, nxr
     tile = ty * GX + tx
-    dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)[ids]
-    order = np.lexsort((ids, dbits, tile))
-    sorted_ids = ids[order].astype(np.int32)
+    del tx, ty
+    # A stable sort by tile keeps the (depth, id) order inside each tile.
+    tkey = tile.astype(np.int16) if GX * GY <= 32767 else tile
+    perm = np.argsort(tkey, kind="stable")
+    sorted_ids = ids[perm]
     counts = np.bincount(tile, minlength=GX * GY)
     ends = np.cumsum(counts)
     ranges = np.stack([ends - counts, ends], axis=1).astype(np.int32)

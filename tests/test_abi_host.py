@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any device work (these
+paths never touch a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from differentiable_tile_rasterization_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsraster.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\**(gs_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version():
+    assert _lib.load().gs_version() >= 100
+
+
+def test_workspace_size_grows_with_capacity():
+    lib = _lib.load()
+    a = lib.gs_bin_tiles_workspace_size(1000, 0, 64, 64)
+    b = lib.gs_bin_tiles_workspace_size(1000, 100000, 64, 64)
+    assert 0 < a < b
+    assert lib.gs_bin_tiles_workspace_size(-1, 0, 64, 64) == 0
+
+
+def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None):
+    p = ctypes.c_void_p(ptr)
+    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, None)
+
+
+def test_fwd_rejects_bad_arguments():
+    lib = _lib.load()
+    assert _fwd(lib, n=-1) == _lib.GS_ERR_INVALID_ARG
+    assert b"n = -1" in lib.gs_last_error()
+    assert _fwd(lib, w=0) == _lib.GS_ERR_INVALID_ARG
+    assert _fwd(lib, h=40000) == _lib.GS_ERR_INVALID_ARG
+    assert _fwd(lib, ptr=0) == _lib.GS_ERR_INVALID_ARG
+
+
+def test_bwd_rejects_bad_arguments():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+
+    def call(n=1, w=8, h=8, flags=0, aw=None, grad=p):
+        return lib.gs_rasterize_bwd(n, p, p, p, p, None, w, h, p, p, p, p, p, grad, grad, grad, grad, aw,
+                                    flags, None)
+    assert call(n=-5) == _lib.GS_ERR_INVALID_ARG
+    assert call(flags=0x80) == _lib.GS_ERR_INVALID_ARG
+    assert b"unknown flags" in lib.gs_last_error()
+    assert call(flags=_lib.GS_FLAG_ACCUM_WEIGHT, aw=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"accum_weight" in lib.gs_last_error()
+    assert call(grad=ctypes.c_void_p(0)) == _lib.GS_ERR_INVALID_ARG
+    assert call(w=-3) == _lib.GS_ERR_INVALID_ARG
+
+
+def test_bin_rejects_bad_arguments():
+    lib = _lib.load()
+    p = ctypes.c_void_p(256)
+    cnt = ctypes.c_int64(0)
+    def call(n=4, w=64, h=64, cap=16, ws=p, wsb=1 << 20, ncnt=True):
+        return lib.gs_bin_tiles(n, p, p, p, w, h, cap, p, p, ctypes.byref(cnt) if ncnt else None, ws, wsb, None)
+    assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
+    assert call(w=0) == _lib.GS_ERR_INVALID_ARG
+    assert call(cap=-1) == _lib.GS_ERR_INVALID_ARG
+    assert call(ncnt=False) == _lib.GS_ERR_INVALID_ARG
+    assert call(wsb=16) == _lib.GS_ERR_INVALID_ARG
+    assert b"workspace" in lib.gs_last_error()
+    assert call(ws=ctypes.c_void_p(257)) == _lib.GS_ERR_INVALID_ARG
+    assert b"aligned" in lib.gs_last_error()
+
+
+def test_error_string_is_thread_local():
+    import threading
+    lib = _lib.load()
+    assert _fwd(lib, n=-7) == _lib.GS_ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.gs_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert b"n = -7" in lib.gs_last_error()
+    assert b"n = -7" not in seen["msg"]
