@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import GS_FLAG_ACCUM_WEIGHT, GsError
 
-__all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_version", "GsError",
-           "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid"]
+__all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_rasterize_bwd_workspace_size",
+           "gs_version", "GsError", "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid", "Bins"]
 
 TILE = 16
 
@@ -57,14 +57,23 @@ def _need(t, name, dtype, shape=None):
 
 
 class Bins:
-    """Result of gs_bin_tiles: sorted_ids [n_isect] int32, tile_ranges [GX*GY, 2] int32."""
+    """Result of gs_bin_tiles: sorted_ids [n_isect] int32, tile_ranges
+    [GX*GY, 2] int32, splat_offsets [n+1] int32 (the numbering of each splat's
+    (splat, tile) pairs that the backward uses for its accumulation slots)."""
 
-    def __init__(self, sorted_ids, tile_ranges, n_isect, width, height):
+    def __init__(self, sorted_ids, tile_ranges, splat_offsets, n_isect, width, height):
         self.sorted_ids = sorted_ids
         self.tile_ranges = tile_ranges
+        self.splat_offsets = splat_offsets
         self.n_isect = n_isect
         self.width = width
         self.height = height
+
+
+def _aligned_workspace(nbytes, dev):
+    """A uint8 device buffer and a 256-byte aligned pointer into it."""
+    ws = torch.empty((nbytes + 256,), dtype=torch.uint8, device=dev)
+    return ws, ctypes.c_void_p((ws.data_ptr() + 255) & ~255)
 
 
 def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int | None = None,
@@ -82,23 +91,21 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
     GX, GY = tile_grid(width, height)
     cap = int(capacity) if capacity is not None else max(4 * n, 1)
     ranges = torch.empty((GX * GY, 2), dtype=torch.int32, device=dev)
+    offsets = torch.empty((n + 1,), dtype=torch.int32, device=dev)
     st = _stream(stream)
     for _attempt in range(2):
         ids = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
         ws_bytes = int(lib.gs_bin_tiles_workspace_size(n, cap, width, height))
-        ws = torch.empty((ws_bytes + 256,), dtype=torch.uint8, device=dev)
-        base = ws.data_ptr()
-        aligned = (base + 255) & ~255
+        ws, wsp = _aligned_workspace(ws_bytes, dev)
         n_isect = ctypes.c_int64(0)
         status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(radii), _ptr(depths), width, height, cap,
-                                  _ptr(ids), _ptr(ranges), ctypes.byref(n_isect),
-                                  ctypes.c_void_p(aligned), ws_bytes, st)
+                                  _ptr(ids), _ptr(ranges), _ptr(offsets), ctypes.byref(n_isect), wsp, ws_bytes, st)
         if status == _lib.GS_ERR_CAPACITY:
             cap = int(n_isect.value)
             continue
         _lib.check(status)
         I = int(n_isect.value)
-        return Bins(ids[:I], ranges, I, width, height)
+        return Bins(ids[:I], ranges, offsets, I, width, height)
     raise GsError(_lib.GS_ERR_CAPACITY, "binning capacity still too small after reallocation")
 
 
@@ -125,27 +132,32 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     return image, final_T, n_contrib
 
 
-def gs_rasterize_bwd(means2d, conics, colors, opacities, background, width: int, height: int,
-                     tile_ranges, sorted_ids, final_T, n_contrib, dL_dimage, accum_weight: bool = False,
-                     out=None, stream=None):
+def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, width: int, height: int, bins: Bins,
+                     final_T, n_contrib, dL_dimage, accum_weight: bool = False, out=None, workspace=None,
+                     stream=None):
     """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
     dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
     per-splat accumulated weight [n]. ``out`` may pass preallocated outputs
-    (same dict keys) to keep allocation out of timed loops."""
+    (same dict keys) and ``workspace`` a uint8 device buffer of at least
+    gs_rasterize_bwd_workspace_size(n, n_isect) + 256 bytes, to keep
+    allocation out of timed loops."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
     _need(conics, "conics", torch.float32, (n, 3))
     _need(colors, "colors", torch.float32, (n, 3))
     _need(opacities, "opacities", torch.float32, (n,))
+    _need(radii, "radii", torch.int32, (n,))
     if background is not None:
         _need(background, "background", torch.float32, (3,))
     GX, GY = tile_grid(width, height)
-    _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
-    _need(sorted_ids, "sorted_ids", torch.int32)
+    _need(bins.tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
+    _need(bins.sorted_ids, "sorted_ids", torch.int32)
+    _need(bins.splat_offsets, "splat_offsets", torch.int32, (n + 1,))
     _need(final_T, "final_T", torch.float32, (height, width))
     _need(n_contrib, "n_contrib", torch.int32, (height, width))
     _need(dL_dimage, "dL_dimage", torch.float32, (height, width, 3))
     dev = means2d.device
+    lib = _lib.load()
     if out is None:
         out = {"dL_dmeans2d": torch.empty((n, 2), dtype=torch.float32, device=dev),
                "dL_dconics": torch.empty((n, 3), dtype=torch.float32, device=dev),
@@ -153,10 +165,23 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, background, width: int,
                "dL_dopacities": torch.empty((n,), dtype=torch.float32, device=dev)}
         if accum_weight:
             out["accum_weight"] = torch.empty((n,), dtype=torch.float32, device=dev)
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect))
+    if workspace is None:
+        workspace, wsp = _aligned_workspace(ws_bytes, dev)
+    else:
+        _need(workspace, "workspace", torch.uint8)
+        if workspace.numel() < ws_bytes + 256:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {ws_bytes + 256}")
+        wsp = ctypes.c_void_p((workspace.data_ptr() + 255) & ~255)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
-    _lib.check(_lib.load().gs_rasterize_bwd(
-        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
-        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
-        _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]), _ptr(out["dL_dcolors"]),
-        _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, _stream(stream)))
+    _lib.check(lib.gs_rasterize_bwd(
+        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
+        height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
+        _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
+        _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, wsp,
+        ws_bytes, _stream(stream)))
     return out
+
+
+def gs_rasterize_bwd_workspace_size(n: int, n_isect: int) -> int:
+    return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_isect))

@@ -32,17 +32,7 @@ constexpr int kRadix = 1 << kRadixBits;
 __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float depth, int GX, int GY,
                                            int& tx0, int& tx1, int& ty0, int& ty1)
 {
-    // Float32 rectangle rule (see gsraster.h). Plain sub / mul by 1/16 / floor:
-    // no contraction is possible, so every compliant float32 evaluation agrees.
-    const float rf = (float)r;
-    const float x0 = floorf((mx - rf) * 0.0625f);
-    const float x1 = floorf((mx + rf) * 0.0625f) + 1.0f;
-    const float y0 = floorf((my - rf) * 0.0625f);
-    const float y1 = floorf((my + rf) * 0.0625f) + 1.0f;
-    tx0 = (int)fminf(fmaxf(x0, 0.0f), (float)GX);
-    tx1 = (int)fminf(fmaxf(x1, 0.0f), (float)GX);
-    ty0 = (int)fminf(fmaxf(y0, 0.0f), (float)GY);
-    ty1 = (int)fminf(fmaxf(y1, 0.0f), (float)GY);
+    tile_rect(mx, my, r, GX, GY, tx0, tx1, ty0, ty1);
     const bool live = r > 0 && depth > 0.0f && __builtin_isfinite(mx) && __builtin_isfinite(my);
     return live && tx1 > tx0 && ty1 > ty0;
 }
@@ -288,6 +278,16 @@ __global__ __launch_bounds__(256) void ranges_kernel(const unsigned long long* _
     if (i == n - 1 || (int)(keys[i + 1] >> 32) != t) ranges[t].y = (int)(i + 1);
 }
 
+// splat_offsets[i] = first slot of splat i's (splat, tile) pairs, [n] = total.
+__global__ __launch_bounds__(256) void offsets_kernel(int n, const unsigned long long* __restrict__ offsets,
+                                                      const unsigned long long* __restrict__ total,
+                                                      int* __restrict__ splat_offsets)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) splat_offsets[i] = (int)offsets[i];
+    if (i == n) splat_offsets[n] = (int)*total;
+}
+
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BinLayout {
@@ -335,8 +335,8 @@ extern "C" size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32
 
 extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
                                   int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
-                                  int32_t* tile_ranges, int64_t* n_isect, void* workspace,
-                                  size_t workspace_bytes, gs_stream_t stream_)
+                                  int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect,
+                                  void* workspace, size_t workspace_bytes, gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
     GS_CHECK_ARG(n >= 0, "gs_bin_tiles: n = %d < 0", n);
@@ -345,6 +345,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     GS_CHECK_ARG(capacity >= 0, "gs_bin_tiles: capacity %lld < 0", (long long)capacity);
     GS_CHECK_ARG(n_isect != nullptr, "gs_bin_tiles: n_isect is NULL");
     GS_CHECK_ARG(tile_ranges != nullptr, "gs_bin_tiles: tile_ranges is NULL");
+    GS_CHECK_ARG(splat_offsets != nullptr, "gs_bin_tiles: splat_offsets is NULL");
     GS_CHECK_ARG(n == 0 || (means2d && radii && depths), "gs_bin_tiles: NULL splat array");
     GS_CHECK_ARG(capacity == 0 || sorted_ids != nullptr, "gs_bin_tiles: sorted_ids is NULL");
     const BinLayout L = bin_layout(n, capacity);
@@ -379,6 +380,12 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     }
     const long long I = (long long)h_total;
     GS_HIP(hipMemsetAsync(tile_ranges, 0, sizeof(int) * 2 * (size_t)tiles, st));
+    if (n > 0) {
+        offsets_kernel<<<(n + 1 + 255) / 256, 256, 0, st>>>(n, offsets, total, splat_offsets);
+        GS_HIP(hipGetLastError());
+    } else {
+        GS_HIP(hipMemsetAsync(splat_offsets, 0, sizeof(int), st));
+    }
     if (I == 0) return GS_OK;
 
     auto* keys_a = (unsigned long long*)(ws + L.keys_a);

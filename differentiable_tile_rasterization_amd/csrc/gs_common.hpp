@@ -62,6 +62,27 @@ __device__ inline int xcd_tile(int wg, int tiles)
 }
 
 // ---------------------------------------------------------------------------
+// Tile rectangle [tx0, tx1) x [ty0, ty1) of a splat (the rule in gsraster.h):
+// plain float32 sub, multiply by 1/16 and floor, then clamp to the grid. No
+// contraction is possible in these expressions, so every evaluation -- the
+// binning's and the backward's, which recomputes it to find a (splat, tile)
+// pair's slot -- gets the same rectangle.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tile_rect(float mx, float my, int r, int GX, int GY, int& tx0, int& tx1, int& ty0,
+                                          int& ty1)
+{
+    const float rf = (float)r;
+    const float x0 = floorf((mx - rf) * 0.0625f);
+    const float x1 = floorf((mx + rf) * 0.0625f) + 1.0f;
+    const float y0 = floorf((my - rf) * 0.0625f);
+    const float y1 = floorf((my + rf) * 0.0625f) + 1.0f;
+    tx0 = (int)fminf(fmaxf(x0, 0.0f), (float)GX);
+    tx1 = (int)fminf(fmaxf(x1, 0.0f), (float)GX);
+    ty0 = (int)fminf(fmaxf(y0, 0.0f), (float)GY);
+    ty1 = (int)fminf(fmaxf(y1, 0.0f), (float)GY);
+}
+
+// ---------------------------------------------------------------------------
 // Per-splat alpha evaluation, shared by the forward and backward kernels so
 // that both take exactly the same float32 decisions.
 //
@@ -110,22 +131,62 @@ __device__ __forceinline__ float alpha_raw(const AlphaCoef& k, float px, float p
 }
 
 // ---------------------------------------------------------------------------
+// Culling test of a splat against a rectangle of pixel centres.
+//
+// A pixel can take the splat only if alpha >= 1/255, i.e. if the quadratic
+// form q(d) = d^T Q d stays within tau = 2 ln(255 opacity). Over a rectangle
+// dx in [x0, x1], dy in [y0, y1] (d = pixel - mean) the minimum of this convex
+// form is 0 if the rectangle holds the mean, and otherwise lies on an edge, at
+// the edge's stationary point clamped to the edge. The test adds a relative
+// and an absolute margin far above the float32 error of either evaluation, so
+// it never drops a pair whose alpha reaches 1/255.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float qform(float a, float b, float c, float dx, float dy)
+{
+    return __builtin_fmaf(dx, __builtin_fmaf(a, dx, 2.0f * b * dy), c * dy * dy);
+}
+
+__device__ __forceinline__ float rect_min_q(float a, float b, float c, float x0, float x1, float y0, float y1)
+{
+    if (x0 <= 0.0f && 0.0f <= x1 && y0 <= 0.0f && 0.0f <= y1) return 0.0f;
+    const float ia = 1.0f / a, ic = 1.0f / c;
+    float m = qform(a, b, c, x0, fminf(fmaxf(-b * x0 * ic, y0), y1));
+    m = fminf(m, qform(a, b, c, x1, fminf(fmaxf(-b * x1 * ic, y0), y1)));
+    m = fminf(m, qform(a, b, c, fminf(fmaxf(-b * y0 * ia, x0), x1), y0));
+    m = fminf(m, qform(a, b, c, fminf(fmaxf(-b * y1 * ia, x0), x1), y1));
+    return m;
+}
+
+// tau with its safety margin; negative when the splat can never reach 1/255
+// (opacity clearly below it), so that no pixel passes q <= tau.
+__device__ __forceinline__ float cull_tau(float o)
+{
+    const float t = 2.0f * logf(255.0f * o);
+    return __builtin_fmaf(t, 1.0f / 512.0f, t) + 1.0f / 512.0f;
+}
+
+// ---------------------------------------------------------------------------
 // Wave64 helpers.
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp0(float x)
 {
-    // DPP move with zero fill for lanes whose source is outside the row.
+    // DPP move; lanes whose source lies outside the row read zero.
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over each 16-lane row; the total lands in the row's last lane (15).
+// Sum over each 16-lane row, left in every lane of the row: four rotations
+// within the row (row_ror:8, 4, 2, 1), each fused into one v_add_f32_dpp.
 __device__ __forceinline__ float row_sum16(float x)
 {
-    x += dpp0<0x111>(x);   // row_shr:1
-    x += dpp0<0x112>(x);   // row_shr:2
-    x += dpp0<0x114>(x);   // row_shr:4
-    x += dpp0<0x118>(x);   // row_shr:8
+    x += dpp0<0x128>(x);   // row_ror:8
+    x += dpp0<0x124>(x);   // row_ror:4
+    x += dpp0<0x122>(x);   // row_ror:2
+    x += dpp0<0x121>(x);   // row_ror:1
+    // pin the total in a VGPR here: left alone, the compiler moves the last
+    // add under the caller's lane mask, where it costs a mov, a DPP mov and
+    // an add instead of one fused DPP add
+    asm volatile("" : "+v"(x));
     return x;
 }
 

@@ -85,8 +85,8 @@ enum { GS_TILE = 16 };
 enum {
     /* Also write accum_weight[i] = sum over composited (pixel, splat i) pairs of
      * alpha * T: the "accum weight" optional feature of the Spirula Studio
-     * page (section 机制拆解). Without it no register, LDS or atomic is spent
-     * on the weight. */
+     * page (section 机制拆解). Without it no register, LDS slot or store is
+     * spent on the weight. */
     GS_FLAG_ACCUM_WEIGHT = 1u << 0
 };
 
@@ -121,20 +121,25 @@ int gs_version(void);
  *   capacity     number of int32 slots in sorted_ids
  *   sorted_ids   device int32 [capacity] (out)
  *   tile_ranges  device int32 [GX*GY][2] (out)
+ *   splat_offsets device int32 [n + 1] (out): splat i's (splat, tile) pairs
+ *                are numbered splat_offsets[i] .. splat_offsets[i+1]-1, tiles
+ *                of its rectangle in row-major order; [n] = n_isect. The
+ *                backward uses this numbering to give each pair its own
+ *                accumulation slot.
  *   n_isect      host int64 (out): total number of (splat, tile) pairs
  *   workspace    device scratch of at least gs_bin_tiles_workspace_size(...)
  *                bytes, 256-byte aligned
  *
  * Synchronises `stream` once (to read the count). If capacity < *n_isect it
- * returns GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges
- * untouched: allocate *n_isect slots (and the matching workspace) and call
- * again. Totals above 2^31 - 1 return GS_ERR_UNSUPPORTED.
+ * returns GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges /
+ * splat_offsets untouched: allocate *n_isect slots (and the matching
+ * workspace) and call again. Totals above 2^31 - 1 return GS_ERR_UNSUPPORTED.
  */
 size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32_t width, int32_t height);
 
 gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
                        int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
-                       int32_t* tile_ranges, int64_t* n_isect, void* workspace,
+                       int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect, void* workspace,
                        size_t workspace_bytes, gs_stream_t stream);
 
 /*
@@ -165,13 +170,19 @@ gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics,
  * timing", sections 計測結果 and ホットスポット ranking; rasterize_bwd_2d on the
  * Spirula Studio page). One workgroup (4 wave64) per tile walks the tile's
  * list in reverse from the largest n_contrib of its pixels, recovers T by
- * division, and accumulates the nine gradient fields per splat; partial sums
- * are reduced inside each wave and across the workgroup before one global
- * float atomic per (splat, tile, field).
+ * division, and accumulates the nine gradient fields per splat. Partial sums
+ * are reduced inside each wave and across the workgroup, stored once per
+ * (splat, tile) pair into that pair's own workspace slot, and summed per
+ * splat by a second kernel in a fixed order: the result does not depend on
+ * scheduling (no floating-point atomics).
  *
- *   inputs as gs_rasterize_fwd, plus
+ *   n .. opacities       as gs_rasterize_fwd
+ *   radii                device int32 [n], the radii given to gs_bin_tiles
+ *   background           device float [3] or NULL (black)
+ *   tile_ranges, sorted_ids, splat_offsets, n_isect
+ *                        as returned by gs_bin_tiles for the same splats
  *   final_T, n_contrib   device, as written by gs_rasterize_fwd for the same
- *                        scene (the backward trusts them)
+ *                        scene; n_contrib is clamped to each tile's list length
  *   dL_dimage            device float [height][width][3]
  *   dL_dmeans2d          device float [n][2] (out)
  *   dL_dconics           device float [n][3] (out): partials w.r.t. the stored
@@ -181,18 +192,25 @@ gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics,
  *   accum_weight         device float [n] (out), required iff
  *                        GS_FLAG_ACCUM_WEIGHT, else ignored (may be NULL)
  *   flags                bitwise OR of GS_FLAG_*
+ *   workspace            device scratch of at least
+ *                        gs_rasterize_bwd_workspace_size(n, n_isect) bytes,
+ *                        256-byte aligned (may be NULL when n_isect == 0);
+ *                        contents on entry do not matter
  *
- * Outputs are zero-filled on `stream` first; splats in no list get exact
- * zeros. Float atomics make the summation order, and so the last bits of the
- * result, vary from run to run.
+ * Every output element is written; splats that no pixel takes get exact
+ * zeros. Inputs that do not come from one binning of the same splats are
+ * not detected; the kernels never write outside the outputs and workspace.
  */
+size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect);
+
 gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
-                           const float* opacities, const float* background, int32_t width,
-                           int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                           const float* opacities, const int32_t* radii, const float* background,
+                           int32_t width, int32_t height, const int32_t* tile_ranges,
+                           const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
                            const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
-                           float* dL_dopacities, float* accum_weight, uint32_t flags,
-                           gs_stream_t stream);
+                           float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, gs_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -63,9 +63,9 @@ def test_bwd_rejects_bad_arguments():
     lib = _lib.load()
     p = ctypes.c_void_p(1)
 
-    def call(n=1, w=8, h=8, flags=0, aw=None, grad=p):
-        return lib.gs_rasterize_bwd(n, p, p, p, p, None, w, h, p, p, p, p, p, grad, grad, grad, grad, aw,
-                                    flags, None)
+    def call(n=1, w=8, h=8, flags=0, aw=None, grad=p, n_isect=0, ws=None, wsb=0):
+        return lib.gs_rasterize_bwd(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, p, p, p, grad, grad, grad,
+                                    grad, aw, flags, ws, wsb, None)
     assert call(n=-5) == _lib.GS_ERR_INVALID_ARG
     assert call(flags=0x80) == _lib.GS_ERR_INVALID_ARG
     assert b"unknown flags" in lib.gs_last_error()
@@ -73,18 +73,30 @@ def test_bwd_rejects_bad_arguments():
     assert b"accum_weight" in lib.gs_last_error()
     assert call(grad=ctypes.c_void_p(0)) == _lib.GS_ERR_INVALID_ARG
     assert call(w=-3) == _lib.GS_ERR_INVALID_ARG
+    assert call(n_isect=-1) == _lib.GS_ERR_INVALID_ARG
+    assert call(n_isect=1 << 31) == _lib.GS_ERR_INVALID_ARG
+    need = lib.gs_rasterize_bwd_workspace_size(1, 100)
+    assert need >= 100 * 49
+    assert call(n_isect=100, ws=None, wsb=need) == _lib.GS_ERR_INVALID_ARG
+    assert b"workspace" in lib.gs_last_error()
+    assert call(n_isect=100, ws=ctypes.c_void_p(256), wsb=need - 1) == _lib.GS_ERR_INVALID_ARG
+    assert call(n_isect=100, ws=ctypes.c_void_p(300), wsb=need) == _lib.GS_ERR_INVALID_ARG
+    assert b"aligned" in lib.gs_last_error()
 
 
 def test_bin_rejects_bad_arguments():
     lib = _lib.load()
     p = ctypes.c_void_p(256)
     cnt = ctypes.c_int64(0)
-    def call(n=4, w=64, h=64, cap=16, ws=p, wsb=1 << 20, ncnt=True):
-        return lib.gs_bin_tiles(n, p, p, p, w, h, cap, p, p, ctypes.byref(cnt) if ncnt else None, ws, wsb, None)
+    def call(n=4, w=64, h=64, cap=16, ws=p, wsb=1 << 20, ncnt=True, offs=p):
+        return lib.gs_bin_tiles(n, p, p, p, w, h, cap, p, p, offs, ctypes.byref(cnt) if ncnt else None, ws, wsb,
+                                None)
     assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(w=0) == _lib.GS_ERR_INVALID_ARG
     assert call(cap=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(ncnt=False) == _lib.GS_ERR_INVALID_ARG
+    assert call(offs=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"splat_offsets" in lib.gs_last_error()
     assert call(wsb=16) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
     assert call(ws=ctypes.c_void_p(257)) == _lib.GS_ERR_INVALID_ARG
