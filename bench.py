@@ -151,7 +151,7 @@ def main():
 
     # ---- exact algorithmic counts
     probe = load_probe()
-    cnt = torch.zeros(8, dtype=torch.int64, device=dev)
+    cnt = torch.zeros(12, dtype=torch.int64, device=dev)
     flags = torch.zeros(max(bins.n_isect, 1), dtype=torch.uint8, device=dev)
     rc = probe.gsp_walk_stats(sc.n, m.data_ptr(), q.data_ptr(), o.data_ptr(), sc.width, sc.height,
                               bins.tile_ranges.data_ptr(), bins.sorted_ids.data_ptr(), nc.data_ptr(),
@@ -160,6 +160,7 @@ def main():
     torch.cuda.synchronize()
     cnt = [int(v) for v in cnt.cpu().tolist()]
     p_walk, p_contrib, entries, groups_tile, groups_wave, ew_walk, ew_kept = cnt[:7]
+    groups_half, groups_blk, iters_half, iters_blk = cnt[7:11]
     p_walk_check = int(nc.to(torch.int64).sum().item())
     assert p_walk == p_walk_check, (p_walk, p_walk_check)
 
@@ -268,7 +269,9 @@ def main():
                       "raster_bwd_median": float(np.median(t_calls)), "raster_bwd_min": float(np.min(t_calls))},
         "counts": {"p_walk": p_walk, "p_composited": p_contrib, "walked_entries": entries,
                    "splat_tile_groups": groups_tile, "splat_quadrant_groups": groups_wave,
-                   "entry_quadrant_walk": ew_walk, "entry_quadrant_kept": ew_kept, "n_isect": bins.n_isect},
+                   "entry_quadrant_walk": ew_walk, "entry_quadrant_kept": ew_kept, "n_isect": bins.n_isect,
+                   "splat_half_groups": groups_half, "splat_block4_groups": groups_blk,
+                   "lockstep_half_iters": iters_half, "lockstep_block4_iters": iters_blk},
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec))

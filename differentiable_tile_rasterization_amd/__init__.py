@@ -16,6 +16,7 @@ from . import _lib
 from ._lib import GS_FLAG_ACCUM_WEIGHT, GsError
 
 __all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_rasterize_bwd_workspace_size",
+           "gs_rasterize_fwd_workspace_size",
            "gs_version", "GsError", "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid", "Bins"]
 
 TILE = 16
@@ -76,6 +77,16 @@ def _aligned_workspace(nbytes, dev):
     return ws, ctypes.c_void_p((ws.data_ptr() + 255) & ~255)
 
 
+def _workspace(ws, nbytes, dev):
+    """Use the caller's uint8 buffer (checked) or allocate one."""
+    if ws is None:
+        return _aligned_workspace(nbytes, dev)
+    _need(ws, "workspace", torch.uint8)
+    if ws.numel() < nbytes + 256:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, need {nbytes + 256}")
+    return ws, ctypes.c_void_p((ws.data_ptr() + 255) & ~255)
+
+
 def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int | None = None,
                  stream=None) -> Bins:
     """Bin splats into 16x16 tiles and sort each tile's list by depth.
@@ -110,8 +121,10 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
 
 
 def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int, height: int,
-                     tile_ranges, sorted_ids, stream=None):
-    """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W])."""
+                     tile_ranges, sorted_ids, workspace=None, stream=None):
+    """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W]).
+    ``workspace`` may pass a uint8 device buffer of at least
+    gs_rasterize_fwd_workspace_size(n) + 256 bytes."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
     _need(conics, "conics", torch.float32, (n, 3))
@@ -126,9 +139,13 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     image = torch.empty((height, width, 3), dtype=torch.float32, device=dev)
     final_T = torch.empty((height, width), dtype=torch.float32, device=dev)
     n_contrib = torch.empty((height, width), dtype=torch.int32, device=dev)
-    _lib.check(_lib.load().gs_rasterize_fwd(
+    lib = _lib.load()
+    ws_bytes = int(lib.gs_rasterize_fwd_workspace_size(n))
+    workspace, wsp = _workspace(workspace, ws_bytes, dev)
+    _lib.check(lib.gs_rasterize_fwd(
         n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
-        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _stream(stream)))
+        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), wsp, ws_bytes,
+        _stream(stream)))
     return image, final_T, n_contrib
 
 
@@ -166,13 +183,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
         if accum_weight:
             out["accum_weight"] = torch.empty((n,), dtype=torch.float32, device=dev)
     ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect))
-    if workspace is None:
-        workspace, wsp = _aligned_workspace(ws_bytes, dev)
-    else:
-        _need(workspace, "workspace", torch.uint8)
-        if workspace.numel() < ws_bytes + 256:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {ws_bytes + 256}")
-        wsp = ctypes.c_void_p((workspace.data_ptr() + 255) & ~255)
+    workspace, wsp = _workspace(workspace, ws_bytes, dev)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
     _lib.check(lib.gs_rasterize_bwd(
         n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
@@ -185,3 +196,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
 
 def gs_rasterize_bwd_workspace_size(n: int, n_isect: int) -> int:
     return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_isect))
+
+
+def gs_rasterize_fwd_workspace_size(n: int) -> int:
+    return int(_lib.load().gs_rasterize_fwd_workspace_size(n))

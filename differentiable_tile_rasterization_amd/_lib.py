@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_CAPACITY", 3: "G
 
 # Every symbol include/gsraster.h declares.
 EXPORTS = ["gs_last_error", "gs_version", "gs_bin_tiles_workspace_size", "gs_bin_tiles",
-           "gs_rasterize_fwd", "gs_rasterize_bwd_workspace_size", "gs_rasterize_bwd"]
+           "gs_rasterize_fwd_workspace_size", "gs_rasterize_fwd", "gs_rasterize_bwd_workspace_size",
+           "gs_rasterize_bwd"]
 
 _lib = None
 
@@ -51,7 +52,9 @@ def load() -> ctypes.CDLL:
     lib.gs_bin_tiles_workspace_size.restype = sz
     lib.gs_bin_tiles.argtypes = [i32, P, P, P, i32, i32, i64, P, P, P, ctypes.POINTER(i64), P, sz, P]
     lib.gs_bin_tiles.restype = ctypes.c_int
-    lib.gs_rasterize_fwd.argtypes = [i32, P, P, P, P, P, i32, i32, P, P, P, P, P, P]
+    lib.gs_rasterize_fwd_workspace_size.argtypes = [i32]
+    lib.gs_rasterize_fwd_workspace_size.restype = sz
+    lib.gs_rasterize_fwd.argtypes = [i32, P, P, P, P, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.gs_rasterize_fwd.restype = ctypes.c_int
     lib.gs_rasterize_bwd_workspace_size.argtypes = [i32, i64]
     lib.gs_rasterize_bwd_workspace_size.restype = sz

@@ -46,6 +46,8 @@ __global__ __launch_bounds__(kBlock) void walk_stats_kernel(
     __syncthreads();
     const int tmax = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
     unsigned long long c_walk = nc, c_contrib = 0, c_swave = 0, c_keep = 0, c_stile = 0;
+    // finer groups inside the quadrant: 8x4 halves (lanes 0-31, 32-63) and 4x4 blocks
+    unsigned long long c_half = 0, c_blk = 0, c_half_max = 0, c_blk_max = 0;
     for (int bs = 0; bs < tmax; bs += kBlock) {
         __syncthreads();
         const int k = bs + (int)threadIdx.x;
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(kBlock) void walk_stats_kernel(
         }
         __syncthreads();
         const int jend = min(kBlock, wmax - bs);
+        unsigned h0 = 0, h1 = 0, b0 = 0, b1 = 0, b2 = 0, b3 = 0;
         for (int j = 0; j < jend; ++j) {
             const float4 A = S.a[j], B = S.b[j];
             const AlphaCoef kf{A.x, A.y, A.z, A.w, B.x, B.y};
@@ -73,12 +76,24 @@ __global__ __launch_bounds__(kBlock) void walk_stats_kernel(
             const bool contrib = (bs + j < nc) && (al >= kAlphaMin);
             const unsigned long long bal = __ballot(contrib);
             c_contrib += contrib ? 1 : 0;
+            h0 += (bal & 0xffffffffull) != 0;
+            h1 += (bal >> 32) != 0;
+            b0 += (bal & 0x0f0f0f0f0f0f0f0full & 0x00000000ffffffffull) != 0;  // x 0-3, y 0-3
+            b1 += (bal & 0xf0f0f0f0f0f0f0f0ull & 0x00000000ffffffffull) != 0;  // x 4-7, y 0-3
+            b2 += (bal & 0x0f0f0f0f0f0f0f0full & 0xffffffff00000000ull) != 0;  // x 0-3, y 4-7
+            b3 += (bal & 0xf0f0f0f0f0f0f0f0ull & 0xffffffff00000000ull) != 0;  // x 4-7, y 4-7
             if (bal != 0) {
                 if (lane == 0) {
                     ++c_swave;
                     entry_any[j] = 1;
                 }
             }
+        }
+        if (lane == 0) {
+            c_half += h0 + h1;
+            c_half_max += max(h0, h1);
+            c_blk += b0 + b1 + b2 + b3;
+            c_blk_max += max(max(b0, b1), max(b2, b3));
         }
         __syncthreads();
         if (k < tmax && entry_any[threadIdx.x]) {
@@ -93,6 +108,12 @@ __global__ __launch_bounds__(kBlock) void walk_stats_kernel(
         c_swave += __shfl_xor(c_swave, off, 64);
         c_keep += __shfl_xor(c_keep, off, 64);
         c_stile += __shfl_xor(c_stile, off, 64);
+    }
+    if (lane == 0) {
+        atomicAdd(&cnt[7], c_half);
+        atomicAdd(&cnt[8], c_blk);
+        atomicAdd(&cnt[9], c_half_max);
+        atomicAdd(&cnt[10], c_blk_max);
     }
     if (lane == 0) {
         atomicAdd(&cnt[0], c_walk);
@@ -227,11 +248,15 @@ __global__ void fold_selftest_kernel(const float* __restrict__ in, float* __rest
 
 using namespace gs;
 
-// counts[7] (uint64, zeroed by the caller): 0 walked pairs, 1 composited pairs,
+// counts[11] (uint64, zeroed by the caller): 0 walked pairs, 1 composited pairs,
 // 2 walked entries (sum over tiles of the tile's largest n_contrib),
 // 3 (splat, tile) groups with a composited pixel, 4 (splat, quadrant) groups
 // with a composited pixel, 5 (entry, quadrant) pairs walked without culling,
-// 6 (entry, quadrant) pairs the culling keeps. flags [n_isect] (optional,
+// 6 (entry, quadrant) pairs the culling keeps, 7 (splat, 8x4 half) and
+// 8 (splat, 4x4 block) groups with a composited pixel, 9 and 10 the same
+// counted as the largest of the halves (blocks) per wave and batch, i.e. the
+// wave iterations a lockstep walk over per-half (per-block) lists would need
+// at perfect culling. flags [n_isect] (optional,
 // zeroed by the caller) marks the (splat, tile) entries of count 3.
 extern "C" int gsp_walk_stats(int32_t n, const float* means2d, const float* conics, const float* opacities,
                               int32_t width, int32_t height, const int32_t* tile_ranges,

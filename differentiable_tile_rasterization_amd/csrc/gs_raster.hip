@@ -5,20 +5,57 @@
 // "Phase 5 step 30b — kernel-by-kernel timing" (section 結論と次着手). Each wave
 // owns one 8x8 quadrant of the tile (lane l -> pixel (l & 7, l >> 3) of the
 // quadrant), so a wave's pixels are as close together as possible: small
-// splats then touch fewer waves, which matters for the backward's per-wave
-// reductions.
+// splats then touch few waves.
 //
-// Splat parameters are staged through LDS in batches of 256 list entries:
-// each thread loads one entry (sorted id, then the splat's record) and writes
-// the per-splat alpha coefficients; the walk then reads them with broadcast
-// LDS loads. Optional outputs are template parameters, so a variant without
-// the accumulated weight carries no register, LDS slot or atomic for it (the
-// lesson of section 机制拆解 of the Spirula Studio page, where optional
-// feature arrays sized regardless of the switch halved occupancy).
+// Data path, per call:
+//   prep_kernel   one thread per splat packs a 64-byte record: mean, the
+//                 scaled Cholesky factor of the conic and log2(opacity) (the
+//                 alpha coefficients), colour, the conic itself and the
+//                 culling threshold. Tile lists reference splats in depth
+//                 order, i.e. at random ids; a record costs one 64-byte
+//                 segment per list entry where the caller's four separate
+//                 arrays cost about five cache lines.
+//   staging       per batch of 256 list entries, thread t loads entry t's
+//                 record, writes the alpha coefficients and colour to LDS and
+//                 tests the splat's alpha >= 1/255 ellipse against each
+//                 wave's quadrant; ballots build one compacted list per wave.
+//   walk          each wave walks only its own list, reading the coefficients
+//                 with broadcast LDS loads.
+// Optional outputs are template parameters, so a variant without the
+// accumulated weight carries no register, LDS slot or store for it (the lesson
+// of section 机制拆解 of the Spirula Studio page, where optional feature arrays
+// sized regardless of the switch halved occupancy).
 #include "gs_common.hpp"
 
 namespace gs {
 namespace {
+
+// Packed per-splat record (64 bytes).
+struct SplatRec {
+    float4 a;  // mean x, mean y, l11, l21
+    float4 b;  // l22, log2(opacity), red, green
+    float4 c;  // blue, conic a, conic b, conic c
+    float4 d;  // culling threshold tau, radius (int bits), 0, 0
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
+                                                   const float* __restrict__ conics, const float* __restrict__ colors,
+                                                   const float* __restrict__ opac, const int* __restrict__ radii,
+                                                   SplatRec* __restrict__ recs)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float2 m = means[i];
+    const float a = conics[3 * i + 0], b = conics[3 * i + 1], c = conics[3 * i + 2];
+    const float o = opac[i];
+    const AlphaCoef k = make_alpha_coef(m.x, m.y, a, b, c, o);
+    SplatRec r;
+    r.a = make_float4(k.mx, k.my, k.l11, k.l21);
+    r.b = make_float4(k.l22, k.lo, colors[3 * i + 0], colors[3 * i + 1]);
+    r.c = make_float4(colors[3 * i + 2], a, b, c);
+    r.d = make_float4(cull_tau(o), __int_as_float(radii ? radii[i] : 0), 0.0f, 0.0f);
+    recs[i] = r;
+}
 
 struct StageLds {
     float4 a[kBlock];  // mean x, mean y, l11, l21
@@ -33,23 +70,50 @@ __device__ __forceinline__ void quadrant_pixel(int tile, int GX, int& x, int& y)
     y = (tile / GX) * kTile + (w >> 1) * 8 + (l >> 3);
 }
 
-// Loads list entry `idx` into LDS slot `s`; returns the splat id.
-__device__ __forceinline__ int stage_entry(StageLds& S, int s, int id, const float2* __restrict__ means,
-                                           const float* __restrict__ conics,
-                                           const float* __restrict__ colors,
-                                           const float* __restrict__ opac, float& a, float& b, float& c,
-                                           float& o)
+// Stages record `r` into LDS slot threadIdx.x and returns the 4-bit mask of
+// quadrants (waves) whose pixel-centre rectangle the splat can reach;
+// `allowed` masks quadrants that do not walk this entry at all.
+__device__ __forceinline__ unsigned stage_record(StageLds& S, const SplatRec& r, float ox, float oy, unsigned allowed)
 {
-    const float2 m = means[id];
-    a = conics[3 * id + 0];
-    b = conics[3 * id + 1];
-    c = conics[3 * id + 2];
-    o = opac[id];
-    const AlphaCoef k = make_alpha_coef(m.x, m.y, a, b, c, o);
-    S.a[s] = make_float4(k.mx, k.my, k.l11, k.l21);
-    S.b[s] = make_float4(k.l22, k.lo, colors[3 * id + 0], colors[3 * id + 1]);
-    S.c[s] = colors[3 * id + 2];
-    return id;
+    S.a[threadIdx.x] = r.a;
+    S.b[threadIdx.x] = r.b;
+    S.c[threadIdx.x] = r.c.x;
+    unsigned mask = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float x0 = ox + (float)((q & 1) * 8) - r.a.x;
+        const float y0 = oy + (float)((q >> 1) * 8) - r.a.y;
+        if (((allowed >> q) & 1u) && rect_min_q(r.c.y, r.c.z, r.c.w, x0, x0 + 7.0f, y0, y0 + 7.0f) <= r.d.x)
+            mask |= 1u << q;
+    }
+    return mask;
+}
+
+// Builds the per-wave lists from every thread's quadrant mask; returns the
+// length of the calling wave's list. Ends with a workgroup barrier.
+__device__ __forceinline__ int build_lists(unsigned mask, unsigned char (*list)[kBlock], int (*list_cnt)[4])
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    unsigned long long bal[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bal[q] = __ballot((mask >> q) & 1u);
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) list_cnt[wv][q] = __popcll(bal[q]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if ((mask >> q) & 1u) {
+            int off = __popcll(bal[q] & lt_mask);
+            for (int w2 = 0; w2 < wv; ++w2) off += list_cnt[w2][q];
+            list[q][off] = (unsigned char)threadIdx.x;
+        }
+    }
+    const int len = list_cnt[0][wv] + list_cnt[1][wv] + list_cnt[2][wv] + list_cnt[3][wv];
+    __syncthreads();
+    return len;
 }
 
 // ---------------------------------------------------------------------------
@@ -58,37 +122,41 @@ __device__ __forceinline__ int stage_entry(StageLds& S, int s, int id, const flo
 __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int tiles,
                                                      const int2* __restrict__ ranges,
                                                      const int* __restrict__ ids,
-                                                     const float2* __restrict__ means,
-                                                     const float* __restrict__ conics,
-                                                     const float* __restrict__ colors,
-                                                     const float* __restrict__ opac,
+                                                     const SplatRec* __restrict__ recs,
                                                      const float* __restrict__ bg, float* __restrict__ image,
                                                      float* __restrict__ final_T, int* __restrict__ n_contrib)
 {
     __shared__ StageLds S;
+    __shared__ unsigned char list[4][kBlock];
+    __shared__ int list_cnt[4][4];
+    __shared__ int wave_live[4];
     const int tile = xcd_tile(blockIdx.x, tiles);
     if (tile >= tiles) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int x, y;
     quadrant_pixel(tile, GX, x, y);
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
     const int2 rg = ranges[tile];
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     int last = 0;
     bool done = !inside;
     for (int bs = rg.x; bs < rg.y; bs += kBlock) {
+        const bool wave_live_now = __ballot(!done) != 0;
+        if (lane == 0) wave_live[wv] = wave_live_now ? 1 : 0;
         if (__syncthreads_count(done) == kBlock) break;  // every pixel of the tile has stopped
+        const unsigned allowed = (unsigned)wave_live[0] | ((unsigned)wave_live[1] << 1) |
+                                 ((unsigned)wave_live[2] << 2) | ((unsigned)wave_live[3] << 3);
         const int idx = bs + (int)threadIdx.x;
-        if (idx < rg.y) {
-            float a, b, c, o;
-            stage_entry(S, threadIdx.x, ids[idx], means, conics, colors, opac, a, b, c, o);
-        }
-        __syncthreads();
-        const int cnt = min(kBlock, rg.y - bs);
-        for (int j = 0; j < cnt; ++j) {
+        unsigned mask = 0;
+        if (idx < rg.y) mask = stage_record(S, recs[ids[idx]], ox, oy, allowed);
+        const int len = build_lists(mask, list, list_cnt);
+        for (int li = 0; li < len; ++li) {
             if (__ballot(!done) == 0) break;
             if (done) continue;
+            const int j = list[wv][li];
             const float4 A = S.a[j];
             const float4 B = S.b[j];
             const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
@@ -137,9 +205,9 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
 // Wave reduction of 9-10 values in 28 VALU ops instead of 54: one
 // v_permlane32_swap per pair of values folds the wave halves, one
 // v_permlane16_swap per pair of those folds rows, leaving 3 registers whose 4
-// rows each hold a different field; a 4-step DPP row scan finishes them. The
-// four row-leader lanes add their 3 values into the workgroup's LDS slot of
-// the list entry.
+// rows each hold a different field; four row_ror DPP adds finish each row.
+// The four row-leader lanes add their 3 values into the workgroup's LDS slot
+// of the list entry.
 //
 // No global atomics: every (splat, tile) pair owns a fixed record slot, the
 // pair's index in the binning's enumeration (the splat's first slot plus the
@@ -148,19 +216,16 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
 // thread per entry stores the entry's sums there with plain vector stores and
 // marks the slot; gather_kernel then sums each splat's slots in a fixed order.
 // Scattered float atomics cost about 1 ms for the 2.1e7 field updates of the
-// 2M-splat scene on this part; the stores cost about 0.04 ms, and the result
-// is bitwise reproducible.
+// 2M-splat scene on this part; the stores cost about 0.04 ms.
 // ---------------------------------------------------------------------------
 constexpr int kSlot = 12;  // 3 registers x 4 rows
 
 template <bool AW>
 __global__ __launch_bounds__(kBlock) void bwd_kernel(
     int W, int H, int GX, int GY, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
-    const float2* __restrict__ means, const float* __restrict__ conics, const float* __restrict__ colors,
-    const float* __restrict__ opac, const int* __restrict__ radii, const int* __restrict__ splat_offsets,
-    long long n_slots, const float* __restrict__ bg, const float* __restrict__ final_T,
-    const int* __restrict__ n_contrib, const float* __restrict__ dimg, float4* __restrict__ rec,
-    unsigned char* __restrict__ slot_used)
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
+    const float* __restrict__ dimg, float4* __restrict__ rec_out, unsigned char* __restrict__ slot_used)
 {
     __shared__ StageLds S;
     __shared__ float part[kBlock][kSlot];
@@ -202,91 +267,65 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
 
     const bool row_leader = (lane & 15) == 15;
     const int row = lane >> 4;
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
 
     for (int bs = ((tmax - 1) / kBlock) * kBlock; bs >= 0; bs -= kBlock) {
         __syncthreads();  // previous batch fully flushed before LDS is reused
         const int k = bs + (int)threadIdx.x;
-        int id = -1;
-        float ca = 0.0f, cb = 0.0f, cc = 0.0f, co = 1.0f;
+        int id = -1, radius = 0;
         unsigned mask = 0;
         if (k < tmax) {
-            id = stage_entry(S, threadIdx.x, ids[rg.x + k], means, conics, colors, opac, ca, cb, cc, co);
+            id = ids[rg.x + k];
+            const SplatRec r = recs[id];
+            radius = __float_as_int(r.d.y);
+            const unsigned allowed = (unsigned)(k < wave_max[0]) | ((unsigned)(k < wave_max[1]) << 1) |
+                                     ((unsigned)(k < wave_max[2]) << 2) | ((unsigned)(k < wave_max[3]) << 3);
+            mask = stage_record(S, r, ox, oy, allowed);
 #pragma unroll
             for (int f = 0; f < kSlot; ++f) part[threadIdx.x][f] = 0.0f;
-            // Which quadrants (waves) can this splat reach at all?
-            const float4 A = S.a[threadIdx.x];
-            const float tau = cull_tau(co);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float x0 = ox + (float)((q & 1) * 8) - A.x;
-                const float y0 = oy + (float)((q >> 1) * 8) - A.y;
-                if (k < wave_max[q] && rect_min_q(ca, cb, cc, x0, x0 + 7.0f, y0, y0 + 7.0f) <= tau)
-                    mask |= 1u << q;
-            }
         }
-        unsigned long long bal[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bal[q] = __ballot((mask >> q) & 1u);
-        if (lane == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) list_cnt[wv][q] = __popcll(bal[q]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if ((mask >> q) & 1u) {
-                int off = __popcll(bal[q] & lt_mask);
-                for (int w2 = 0; w2 < wv; ++w2) off += list_cnt[w2][q];
-                list[q][off] = (unsigned char)threadIdx.x;
-            }
-        }
-        const int my_len = list_cnt[0][wv] + list_cnt[1][wv] + list_cnt[2][wv] + list_cnt[3][wv];
-        __syncthreads();
+        const int my_len = build_lists(mask, list, list_cnt);
 
-        {
-            for (int li = my_len - 1; li >= 0; --li) {
-                const int j = list[wv][li];
-                const float4 A = S.a[j];
-                const float4 Bq = S.b[j];
-                const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
-                float dx, dy;
-                const float ar = alpha_raw(kf, px, py, dx, dy);
-                const float al = fminf(kAlphaMax, ar);
-                const bool contrib = (bs + j < nc) && (al >= kAlphaMin);
-                if (__ballot(contrib) == 0) continue;
+        for (int li = my_len - 1; li >= 0; --li) {
+            const int j = list[wv][li];
+            const float4 A = S.a[j];
+            const float4 Bq = S.b[j];
+            const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
+            float dx, dy;
+            const float ar = alpha_raw(kf, px, py, dx, dy);
+            const float al = fminf(kAlphaMax, ar);
+            const bool contrib = (bs + j < nc) && (al >= kAlphaMin);
+            if (__ballot(contrib) == 0) continue;
 
-                const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
-                const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
-                const float cr = Bq.z, cg = Bq.w, cbl = S.c[j];
-                const float e0 = cr - B0, e1 = cg - B1, e2 = cbl - B2;
-                const float dal = Ti * __builtin_fmaf(e0, g0, __builtin_fmaf(e1, g1, e2 * g2));
-                B0 = __builtin_fmaf(ae, e0, B0);
-                B1 = __builtin_fmaf(ae, e1, B1);
-                B2 = __builtin_fmaf(ae, e2, B2);
-                T = Ti;
-                const float w = ae * Ti;
-                const float s = (ar < kAlphaMax) ? ae * dal : 0.0f;  // clamped alpha: no sigma path
-                // all ten values first, then the folds (no value is read after
-                // its register has been swapped)
-                const float sdx = s * dx, sdy = s * dy;
-                const float f0 = w * g0, f1 = w * g1, f2 = w * g2;
-                const float f6 = sdx * dx, f7 = sdx * dy, f8 = sdy * dy;
-                const float f9 = AW ? w : f8;
+            const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
+            const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
+            const float cr = Bq.z, cg = Bq.w, cbl = S.c[j];
+            const float e0 = cr - B0, e1 = cg - B1, e2 = cbl - B2;
+            const float dal = Ti * __builtin_fmaf(e0, g0, __builtin_fmaf(e1, g1, e2 * g2));
+            B0 = __builtin_fmaf(ae, e0, B0);
+            B1 = __builtin_fmaf(ae, e1, B1);
+            B2 = __builtin_fmaf(ae, e2, B2);
+            T = Ti;
+            const float w = ae * Ti;
+            const float s = (ar < kAlphaMax) ? ae * dal : 0.0f;  // clamped alpha: no sigma path
+            // all ten values first, then the folds (no value is read after its
+            // register has been swapped)
+            const float sdx = s * dx, sdy = s * dy;
+            const float f0 = w * g0, f1 = w * g1, f2 = w * g2;
+            const float f6 = sdx * dx, f7 = sdx * dy, f8 = sdy * dy;
+            const float f9 = AW ? w : f8;
 
-                const float r0 = fold32(f0, f1);
-                const float r1 = fold32(f2, s);
-                const float r2 = fold32(sdx, sdy);
-                const float r3 = fold32(f6, f7);
-                const float r4 = fold32(f8, f9);
-                const float q0 = row_sum16(fold16(r0, r1));
-                const float q1 = row_sum16(fold16(r2, r3));
-                const float q2 = row_sum16(fold16(r4, r4));
-                if (row_leader) {
-                    atomicAdd(&part[j][row * 3 + 0], q0);
-                    atomicAdd(&part[j][row * 3 + 1], q1);
-                    atomicAdd(&part[j][row * 3 + 2], q2);
-                }
+            const float r0 = fold32(f0, f1);
+            const float r1 = fold32(f2, s);
+            const float r2 = fold32(sdx, sdy);
+            const float r3 = fold32(f6, f7);
+            const float r4 = fold32(f8, f9);
+            const float q0 = row_sum16(fold16(r0, r1));
+            const float q1 = row_sum16(fold16(r2, r3));
+            const float q2 = row_sum16(fold16(r4, r4));
+            if (row_leader) {
+                atomicAdd(&part[j][row * 3 + 0], q0);
+                atomicAdd(&part[j][row * 3 + 1], q1);
+                atomicAdd(&part[j][row * 3 + 2], q2);
             }
         }
         __syncthreads();
@@ -307,15 +346,15 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             if (any) {
                 const float4 A = S.a[threadIdx.x];
                 int tx0, tx1, ty0, ty1;
-                tile_rect(A.x, A.y, radii[id], GX, GY, tx0, tx1, ty0, ty1);
+                tile_rect(A.x, A.y, radius, GX, GY, tx0, tx1, ty0, ty1);
                 const int tx = tile % GX, ty = tile / GX;
                 const long long slot = (long long)splat_offsets[id] + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
                 // the tile lies in the splat's rectangle whenever the inputs come
                 // from one binning; anything else is dropped, never written wild
                 if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && slot >= 0 && slot < n_slots) {
-                    rec[3 * slot + 0] = make_float4(Swr, Swg, Swb, Ss);
-                    rec[3 * slot + 1] = make_float4(Sdx, Sdy, Sdxx, Sdxy);
-                    rec[3 * slot + 2] = make_float4(Sdyy, Sw, 0.0f, 0.0f);
+                    rec_out[3 * slot + 0] = make_float4(Swr, Swg, Swb, Ss);
+                    rec_out[3 * slot + 1] = make_float4(Sdx, Sdy, Sdxx, Sdxy);
+                    rec_out[3 * slot + 2] = make_float4(Sdyy, Sw, 0.0f, 0.0f);
                     slot_used[slot] = 1;
                 }
             }
@@ -379,17 +418,19 @@ hipError_t clear_bytes(unsigned char* p, long long n, hipStream_t st)
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-struct BwdLayout {
-    size_t rec, used, bytes;
+// Workspace layouts. Forward: splat records. Backward: splat records, then the
+// per-(splat, tile) slots (3 float4 each) and their used-flags.
+struct Layout {
+    size_t recs, slots, used, bytes;
 };
 
-BwdLayout bwd_layout(long long n_slots)
+Layout layout(long long n, long long n_slots)
 {
-    BwdLayout L{};
-    const size_t m = (size_t)(n_slots > 0 ? n_slots : 1);
-    L.rec = 0;
-    L.used = align256(sizeof(float4) * 3 * m);
-    L.bytes = L.used + align256(m);
+    Layout L{};
+    L.recs = 0;
+    L.slots = align256(sizeof(SplatRec) * (size_t)(n > 0 ? n : 1));
+    L.used = L.slots + (n_slots > 0 ? align256(sizeof(float4) * 3 * (size_t)n_slots) : 0);
+    L.bytes = L.used + (n_slots > 0 ? align256((size_t)n_slots) : 0);
     return L;
 }
 
@@ -398,10 +439,17 @@ BwdLayout bwd_layout(long long n_slots)
 
 using namespace gs;
 
+extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
+{
+    if (n < 0) return 0;
+    return layout(n, 0).bytes;
+}
+
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                                       const float* opacities, const float* background, int32_t width,
                                       int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                      float* image, float* final_T, int32_t* n_contrib, gs_stream_t stream_)
+                                      float* image, float* final_T, int32_t* n_contrib, void* workspace,
+                                      size_t workspace_bytes, gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
     GS_CHECK_ARG(n >= 0, "gs_rasterize_fwd: n = %d < 0", n);
@@ -410,10 +458,19 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
     GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
     GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
+    const Layout L = layout(n, 0);
+    GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
+                 "gs_rasterize_fwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
+    GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_fwd: workspace not 256-byte aligned");
+    SplatRec* recs = n ? (SplatRec*)((char*)workspace + L.recs) : nullptr;
+    if (n > 0) {
+        prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, nullptr,
+                                                     recs);
+        GS_HIP(hipGetLastError());
+    }
     const int GX = grid_x(width), tiles = GX * grid_y(height);
     fwd_kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, tiles, (const int2*)tile_ranges, sorted_ids,
-                                                   (const float2*)means2d, conics, colors, opacities, background,
-                                                   image, final_T, n_contrib);
+                                                   recs, background, image, final_T, n_contrib);
     GS_HIP(hipGetLastError());
     return GS_OK;
 }
@@ -421,7 +478,7 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
 extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect)
 {
     if (n < 0 || n_isect < 0) return 0;
-    return bwd_layout(n_isect).bytes;
+    return layout(n, n_isect).bytes;
 }
 
 extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
@@ -448,36 +505,37 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(!aw || n == 0 || accum_weight, "gs_rasterize_bwd: GS_FLAG_ACCUM_WEIGHT with accum_weight NULL");
     GS_CHECK_ARG(tile_ranges && final_T && n_contrib && dL_dimage, "gs_rasterize_bwd: NULL image-side array");
     GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_bwd: sorted_ids is NULL");
-    const BwdLayout L = bwd_layout(n_isect);
-    GS_CHECK_ARG(n_isect == 0 || (workspace && workspace_bytes >= L.bytes),
+    const Layout L = layout(n, n_isect);
+    GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_bwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
-    GS_CHECK_ARG(n_isect == 0 || ((uintptr_t)workspace & 255) == 0,
-                 "gs_rasterize_bwd: workspace not 256-byte aligned");
+    GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_bwd: workspace not 256-byte aligned");
     if (n == 0) return GS_OK;
     const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
-    float4* rec = n_isect ? (float4*)((char*)workspace + L.rec) : nullptr;
+    SplatRec* recs = (SplatRec*)((char*)workspace + L.recs);
+    float4* slots = n_isect ? (float4*)((char*)workspace + L.slots) : nullptr;
     unsigned char* used = n_isect ? (unsigned char*)workspace + L.used : nullptr;
     if (n_isect > 0) {
         GS_HIP(clear_bytes(used, n_isect, st));
+        prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, radii,
+                                                     recs);
+        GS_HIP(hipGetLastError());
         if (aw)
             bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
-                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, (const float2*)means2d,
-                conics, colors, opacities, radii, splat_offsets, n_isect, background, final_T, n_contrib,
-                dL_dimage, rec, used);
+                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
+                background, final_T, n_contrib, dL_dimage, slots, used);
         else
             bwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(
-                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, (const float2*)means2d,
-                conics, colors, opacities, radii, splat_offsets, n_isect, background, final_T, n_contrib,
-                dL_dimage, rec, used);
+                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
+                background, final_T, n_contrib, dL_dimage, slots, used);
         GS_HIP(hipGetLastError());
     }
     const unsigned gb = (unsigned)((n + 255) / 256);
     if (aw)
-        gather_kernel<true><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, rec, used, conics, opacities,
+        gather_kernel<true><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, slots, used, conics, opacities,
                                                 (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities,
                                                 accum_weight);
     else
-        gather_kernel<false><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, rec, used, conics, opacities,
+        gather_kernel<false><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, slots, used, conics, opacities,
                                                  (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities,
                                                  nullptr);
     GS_HIP(hipGetLastError());

@@ -1,0 +1,93 @@
+"""Summarise rocprofv3 CSV output into the short text kept under profiles/.
+
+    python -m differentiable_tile_rasterization_amd.profsum stats <kernel_stats.csv> <out.md> "<command>"
+    python -m differentiable_tile_rasterization_amd.profsum pmc <fetch_dir> <write_dir> <out.json> <out.md> \\
+        "<fetch command>" "<write command>" [config]
+
+`stats` lists every kernel of a --kernel-trace --stats run (calls, average and
+total time). `pmc` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+dispatch) into bytes per launch, scaled by what the same counters read for the
+measurement library's 1 GiB float4 copy kernel (1 GiB read, 1 GiB written per
+launch), and writes the JSON the benchmark reads for its `traffic` field (it
+records the hash of the kernel sources it was taken on; the benchmark ignores
+it once the sources change).
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import json
+import os
+import sys
+
+COPY_BYTES = 1 << 30          # the copy kernel moves 1 GiB in and 1 GiB out per launch
+COPY_NAME = "copy_kernel"
+CALL_KERNELS = ["clear_bytes_kernel", "prep_kernel", "bwd_kernel", "gather_kernel"]
+
+
+def _short(name: str) -> str:
+    n = name.replace("gs::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0]
+
+
+def stats(csv_path: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel time: " + os.path.basename(out_md).rsplit(".", 1)[0], "",
+             "Command (repo root, on the GPU box):", "", "    " + command, "",
+             "| kernel | calls | avg us | min us | max us | total ms | % |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(dir_path: str) -> dict[str, list[float]]:
+    path = [os.path.join(dir_path, f) for f in os.listdir(dir_path) if f.endswith("counter_collection.csv")][0]
+    agg: dict[str, list[float]] = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: str, cmd_write: str,
+        config: str = "bench") -> None:
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from bench import kernel_source_hash  # the hash the benchmark compares against
+    fe, wr = _per_kernel(fetch_dir), _per_kernel(write_dir)
+    avg = lambda v: sum(v) / len(v)  # noqa: E731
+    f_scale = COPY_BYTES / (avg(fe[COPY_NAME]) * 1024.0)
+    w_scale = COPY_BYTES / (avg(wr[COPY_NAME]) * 1024.0)
+    per = {}
+    for k in sorted(set(fe) | set(wr)):
+        fb = avg(fe[k]) * 1024.0 * f_scale if k in fe else 0.0
+        wb = avg(wr[k]) * 1024.0 * w_scale if k in wr else 0.0
+        per[k] = {"fetch_bytes": fb, "write_bytes": wb}
+    call = [k for k in per if any(k.startswith(c) or c in k for c in CALL_KERNELS)]
+    total = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in call)
+    rec = {"config": config, "source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "call_kernels": call, "hbm_bytes_per_launch": total, "per_kernel": per,
+           "commands": [cmd_fetch, cmd_write]}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    lines = ["# HBM traffic (FETCH_SIZE / WRITE_SIZE), " + config, "",
+             "Commands (repo root, on the GPU box):", "", "    " + cmd_fetch, "    " + cmd_write, "",
+             f"Scale: the 1 GiB copy kernel reads {avg(fe[COPY_NAME]):.0f} KiB FETCH_SIZE and "
+             f"{avg(wr[COPY_NAME]):.0f} KiB WRITE_SIZE per launch, so FETCH_SIZE is multiplied by "
+             f"{f_scale:.3f} and WRITE_SIZE by {w_scale:.3f} to give bytes.", "",
+             "| kernel | fetched MB / launch | written MB / launch |", "|---|---:|---:|"]
+    for k, v in sorted(per.items(), key=lambda kv: -(kv[1]["fetch_bytes"] + kv[1]["write_bytes"])):
+        lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} |")
+    lines += ["", f"One gs_rasterize_bwd call ({', '.join(call)}): {total / 1e6:.1f} MB per launch "
+                  f"(source hash {rec['source_hash']})."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "pmc":
+        pmc(*sys.argv[2:])
+    else:
+        raise SystemExit(__doc__)

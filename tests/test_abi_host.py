@@ -45,9 +45,9 @@ def test_workspace_size_grows_with_capacity():
     assert lib.gs_bin_tiles_workspace_size(-1, 0, 64, 64) == 0
 
 
-def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None):
+def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None, ws=256, wsb=1 << 20):
     p = ctypes.c_void_p(ptr)
-    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, None)
+    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, ctypes.c_void_p(ws), wsb, None)
 
 
 def test_fwd_rejects_bad_arguments():
@@ -57,6 +57,10 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(lib, w=0) == _lib.GS_ERR_INVALID_ARG
     assert _fwd(lib, h=40000) == _lib.GS_ERR_INVALID_ARG
     assert _fwd(lib, ptr=0) == _lib.GS_ERR_INVALID_ARG
+    assert _fwd(lib, n=10, wsb=lib.gs_rasterize_fwd_workspace_size(10) - 1) == _lib.GS_ERR_INVALID_ARG
+    assert b"workspace" in lib.gs_last_error()
+    assert _fwd(lib, ws=128) == _lib.GS_ERR_INVALID_ARG
+    assert lib.gs_rasterize_fwd_workspace_size(1000) >= 64 * 1000
 
 
 def test_bwd_rejects_bad_arguments():
@@ -76,7 +80,7 @@ def test_bwd_rejects_bad_arguments():
     assert call(n_isect=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=1 << 31) == _lib.GS_ERR_INVALID_ARG
     need = lib.gs_rasterize_bwd_workspace_size(1, 100)
-    assert need >= 100 * 49
+    assert need >= 100 * 49 + 64
     assert call(n_isect=100, ws=None, wsb=need) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
     assert call(n_isect=100, ws=ctypes.c_void_p(256), wsb=need - 1) == _lib.GS_ERR_INVALID_ARG

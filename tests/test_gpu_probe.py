@@ -47,7 +47,7 @@ def test_walk_counts_match_oracle():
     bins = gsr.gs_bin_tiles(m, t(sc.radii), t(sc.depths), sc.width, sc.height)
     _, _, nc = gsr.gs_rasterize_fwd(m, q, c, o, t(sc.background), sc.width, sc.height, bins.tile_ranges,
                                     bins.sorted_ids)
-    cnt = torch.zeros(8, dtype=torch.int64, device=dev)
+    cnt = torch.zeros(12, dtype=torch.int64, device=dev)
     lib = _probe()
     P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
     assert lib.gsp_walk_stats(sc.n, P(m), P(q), P(o), sc.width, sc.height, P(bins.tile_ranges),
