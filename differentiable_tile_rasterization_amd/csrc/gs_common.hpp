@@ -210,6 +210,44 @@ __device__ __forceinline__ float fold16(float x, float y)
     return __uint_as_float(u0) + __uint_as_float(u1);
 }
 
+// ---------------------------------------------------------------------------
+// Register-merging row reductions. A DPP add with a bank mask writes only the
+// 4-lane banks it names and leaves the others as they were, so two registers
+// that each still need a pairwise step can be folded into one:
+//     z = y + perm(y)            on every lane
+//     z = x + perm(x)            on the masked banks only
+// The builtin DPP move has no way to keep the destination's old lanes while
+// fusing the add, so these two use inline assembly; the s_nop covers the
+// two wait states a DPP read needs after a VALU write of its source.
+// Permutations (all stay inside a 16-lane row):
+//   row_ror:8        lane i <-> i + 8      (pairs the two 8-lane halves)
+//   row_half_mirror  lane i <-> 7 - i      (inside each 8-lane half)
+//   quad_perm        inside each 4-lane group
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dpp_add_ror8(float x) { return x + dpp0<0x128>(x); }
+__device__ __forceinline__ float dpp_add_half_mirror(float x) { return x + dpp0<0x141>(x); }
+__device__ __forceinline__ float dpp_add_quad_xor2(float x) { return x + dpp0<0x4E>(x); }  // quad_perm [2,3,0,1]
+__device__ __forceinline__ float dpp_add_quad_xor1(float x) { return x + dpp0<0xB1>(x); }  // quad_perm [1,0,3,2]
+
+// lanes 0-7 of each row: x + ror8(x); lanes 8-15: y + ror8(y)
+__device__ __forceinline__ float merge_ror8(float x, float y)
+{
+    float z = dpp_add_ror8(y);
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3"
+                 : "+v"(z) : "v"(x));
+    return z;
+}
+
+// banks 0 and 2 (lanes 0-3, 8-11) of each row: x + half_mirror(x); banks 1
+// and 3: y + half_mirror(y)
+__device__ __forceinline__ float merge_half_mirror(float x, float y)
+{
+    float z = dpp_add_half_mirror(y);
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5"
+                 : "+v"(z) : "v"(x));
+    return z;
+}
+
 __device__ __forceinline__ int wave_max_i32(int v)
 {
     for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
