@@ -8,13 +8,13 @@
 // splats then touch few waves.
 //
 // Data path, per call:
-//   prep_kernel   one thread per splat packs a 64-byte record: mean, the
+//   prep_kernel   one thread per splat packs a 48-byte record: mean, the
 //                 scaled Cholesky factor of the conic and log2(opacity) (the
-//                 alpha coefficients), colour, the conic itself and the
-//                 culling threshold. Tile lists reference splats in depth
-//                 order, i.e. at random ids; a record costs one 64-byte
-//                 segment per list entry where the caller's four separate
-//                 arrays cost about five cache lines.
+//                 alpha coefficients), colour, the culling threshold and the
+//                 radius. Tile lists reference splats in depth order, i.e. at
+//                 random ids; a record costs one 48-byte read per list entry
+//                 where the caller's four separate arrays cost about five
+//                 cache lines.
 //   staging       per batch of 256 list entries, thread t loads entry t's
 //                 record, writes the alpha coefficients and colour to LDS and
 //                 tests the splat's alpha >= 1/255 ellipse against each
@@ -30,13 +30,16 @@
 namespace gs {
 namespace {
 
-// Packed per-splat record (64 bytes).
+// Packed per-splat record (48 bytes). The culling test runs on the scaled
+// form q' = (l11 dx + l21 dy)^2 + (l22 dy)^2 = q log2(e) / 2, whose
+// coefficients come from the factor itself, so the record needs no conic.
 struct SplatRec {
-    float4 a;  // mean x, mean y, l11, l21
+    float4 a;  // mean x, mean y, l11, l21 (scaled factor)
     float4 b;  // l22, log2(opacity), red, green
-    float4 c;  // blue, conic a, conic b, conic c
-    float4 d;  // culling threshold tau, radius (int bits), 0, 0
+    float4 c;  // blue, culling threshold on q', radius (int bits), 0
 };
+
+constexpr float kQScale = 0.72134752044448170f;  // log2(e) / 2: q' = kQScale q
 
 __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
                                                    const float* __restrict__ conics, const float* __restrict__ colors,
@@ -52,8 +55,7 @@ __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restri
     SplatRec r;
     r.a = make_float4(k.mx, k.my, k.l11, k.l21);
     r.b = make_float4(k.l22, k.lo, colors[3 * i + 0], colors[3 * i + 1]);
-    r.c = make_float4(colors[3 * i + 2], a, b, c);
-    r.d = make_float4(cull_tau(o), __int_as_float(radii ? radii[i] : 0), 0.0f, 0.0f);
+    r.c = make_float4(colors[3 * i + 2], kQScale * cull_tau(o), __int_as_float(radii ? radii[i] : 0), 0.0f);
     recs[i] = r;
 }
 
@@ -70,6 +72,15 @@ __device__ __forceinline__ void quadrant_pixel(int tile, int GX, int& x, int& y)
     y = (tile / GX) * kTile + (w >> 1) * 8 + (l >> 3);
 }
 
+// Coefficients (a', b', c') of q' = a' dx^2 + 2 b' dx dy + c' dy^2 from the
+// scaled factor in the record.
+__device__ __forceinline__ void qform_coef(const SplatRec& r, float& qa, float& qb, float& qc)
+{
+    qa = r.a.z * r.a.z;
+    qb = r.a.z * r.a.w;
+    qc = __builtin_fmaf(r.a.w, r.a.w, r.b.x * r.b.x);
+}
+
 // Stages record `r` into LDS slot threadIdx.x and returns the 4-bit mask of
 // quadrants (waves) whose pixel-centre rectangle the splat can reach;
 // `allowed` masks quadrants that do not walk this entry at all.
@@ -78,12 +89,14 @@ __device__ __forceinline__ unsigned stage_record(StageLds& S, const SplatRec& r,
     S.a[threadIdx.x] = r.a;
     S.b[threadIdx.x] = r.b;
     S.c[threadIdx.x] = r.c.x;
+    float qa, qb, qc;
+    qform_coef(r, qa, qb, qc);
     unsigned mask = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float x0 = ox + (float)((q & 1) * 8) - r.a.x;
         const float y0 = oy + (float)((q >> 1) * 8) - r.a.y;
-        if (((allowed >> q) & 1u) && rect_min_q(r.c.y, r.c.z, r.c.w, x0, x0 + 7.0f, y0, y0 + 7.0f) <= r.d.x)
+        if (((allowed >> q) & 1u) && rect_min_q(qa, qb, qc, x0, x0 + 7.0f, y0, y0 + 7.0f) <= r.c.y)
             mask |= 1u << q;
     }
     return mask;
@@ -233,13 +246,15 @@ __device__ __forceinline__ unsigned stage_record_halves(StageLds& S, const Splat
     S.a[threadIdx.x] = r.a;
     S.b[threadIdx.x] = r.b;
     S.c[threadIdx.x] = r.c.x;
+    float qa, qb, qc;
+    qform_coef(r, qa, qb, qc);
     unsigned mask = 0;
 #pragma unroll
     for (int hq = 0; hq < kHalves; ++hq) {
         const int q = hq >> 1, h = hq & 1;
         const float x0 = ox + (float)((q & 1) * 8) - r.a.x;
         const float y0 = oy + (float)((q >> 1) * 8 + h * 4) - r.a.y;
-        if (k < half_end[hq] && rect_min_q(r.c.y, r.c.z, r.c.w, x0, x0 + 7.0f, y0, y0 + 3.0f) <= r.d.x)
+        if (k < half_end[hq] && rect_min_q(qa, qb, qc, x0, x0 + 7.0f, y0, y0 + 3.0f) <= r.c.y)
             mask |= 1u << hq;
     }
     return mask;
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         if (k < tmax) {
             id = ids[rg.x + k];
             const SplatRec r = recs[id];
-            radius = __float_as_int(r.d.y);
+            radius = __float_as_int(r.c.z);
             mask = stage_record_halves(S, r, ox, oy, k, half_end);
 #pragma unroll
             for (int f = 0; f < kRaw; ++f) part[threadIdx.x][f] = 0.0f;
@@ -444,12 +459,21 @@ __global__ __launch_bounds__(256) void gather_kernel(int n, const int* __restric
     const long long s0 = max(0ll, (long long)splat_offsets[i]);
     const long long s1 = min(n_slots, (long long)splat_offsets[i + 1]);
     float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v = u, w = u;
-    for (long long sl = s0; sl < s1; ++sl) {
-        if (!slot_used[sl]) continue;
-        const float4 a = rec[3 * sl + 0], b = rec[3 * sl + 1], c = rec[3 * sl + 2];
-        u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
-        v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-        w.x += c.x; w.y += c.y;
+    // flags are read four at a time (the flag array is padded to 4 bytes)
+    const unsigned* words = reinterpret_cast<const unsigned*>(slot_used);
+    for (long long wi = s0 >> 2; wi < (s1 + 3) >> 2; ++wi) {
+        unsigned fl = words[wi];
+        if (fl == 0u) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const long long sl = 4 * wi + b;
+            if (((fl >> (8 * b)) & 0xffu) && sl >= s0 && sl < s1) {
+                const float4 a = rec[3 * sl + 0], bb = rec[3 * sl + 1], c = rec[3 * sl + 2];
+                u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
+                v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
+                w.x += c.x; w.y += c.y;
+            }
+        }
     }
     // u = (w g_r, w g_g, w g_b, s), v = (s dx, s dy, s dx^2, s dx dy), w = (s dy^2, w)
     const float ca = conics[3 * i + 0], cb = conics[3 * i + 1], cc = conics[3 * i + 2];
@@ -496,7 +520,7 @@ Layout layout(long long n, long long n_slots)
     L.recs = 0;
     L.slots = align256(sizeof(SplatRec) * (size_t)(n > 0 ? n : 1));
     L.used = L.slots + (n_slots > 0 ? align256(sizeof(float4) * 3 * (size_t)n_slots) : 0);
-    L.bytes = L.used + (n_slots > 0 ? align256((size_t)n_slots) : 0);
+    L.bytes = L.used + (n_slots > 0 ? align256((size_t)n_slots + 4) : 0);
     return L;
 }
 
@@ -571,17 +595,17 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(!aw || n == 0 || accum_weight, "gs_rasterize_bwd: GS_FLAG_ACCUM_WEIGHT with accum_weight NULL");
     GS_CHECK_ARG(tile_ranges && final_T && n_contrib && dL_dimage, "gs_rasterize_bwd: NULL image-side array");
     GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_bwd: sorted_ids is NULL");
+    const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
     const Layout L = layout(n, n_isect);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_bwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_bwd: workspace not 256-byte aligned");
     if (n == 0) return GS_OK;
-    const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
     SplatRec* recs = (SplatRec*)((char*)workspace + L.recs);
     float4* slots = n_isect ? (float4*)((char*)workspace + L.slots) : nullptr;
     unsigned char* used = n_isect ? (unsigned char*)workspace + L.used : nullptr;
     if (n_isect > 0) {
-        GS_HIP(clear_bytes(used, n_isect, st));
+        GS_HIP(clear_bytes(used, (n_isect + 3) & ~3ll, st));  // whole 4-byte flag words
         prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, radii,
                                                      recs);
         GS_HIP(hipGetLastError());

@@ -146,8 +146,8 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, co
  * Forward composite (rasterize_f32 in the timing table of "Phase 5 step 30b —
  * kernel-by-kernel timing", section 計測結果; the "raster fwd" line of
  * raster_bench). One workgroup of 256 threads per 16x16 tile. Each splat is
- * first packed into a 64-byte record in the workspace (alpha coefficients,
- * colour, conic, culling threshold); each wave then walks only the list
+ * first packed into a 48-byte record in the workspace (alpha coefficients,
+ * colour, culling threshold, radius); each wave then walks only the list
  * entries whose alpha >= 1/255 ellipse reaches its 8x8 quadrant.
  *
  *   n                 number of splats
@@ -163,7 +163,7 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, co
  *   final_T           device float [height][width]    (out)
  *   n_contrib         device int32 [height][width]    (out)
  *   workspace         device scratch of at least gs_rasterize_fwd_workspace_size(n)
- *                     bytes (64 per splat), 256-byte aligned; contents on entry do
+ *                     bytes (48 per splat), 256-byte aligned; contents on entry do
  *                     not matter
  */
 size_t gs_rasterize_fwd_workspace_size(int32_t n);
@@ -203,7 +203,7 @@ gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics,
  *   flags                bitwise OR of GS_FLAG_*
  *   workspace            device scratch of at least
  *                        gs_rasterize_bwd_workspace_size(n, n_isect) bytes
- *                        (64 per splat + 49 per pair), 256-byte aligned;
+ *                        (48 per splat + 49 per pair), 256-byte aligned;
  *                        contents on entry do not matter
  *
  * Every output element is written; splats that no pixel takes get exact

@@ -60,7 +60,7 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(lib, n=10, wsb=lib.gs_rasterize_fwd_workspace_size(10) - 1) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
     assert _fwd(lib, ws=128) == _lib.GS_ERR_INVALID_ARG
-    assert lib.gs_rasterize_fwd_workspace_size(1000) >= 64 * 1000
+    assert lib.gs_rasterize_fwd_workspace_size(1000) >= 48 * 1000
 
 
 def test_bwd_rejects_bad_arguments():
