@@ -237,48 +237,87 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
 constexpr int kRaw = 10;   // w g_r, w g_g, w g_b, s, s dx, s dy, s dx^2, s dx dy, s dy^2, w
 constexpr int kHalves = 8; // 4 waves x 2 halves
 
-// Staging for the half-wave walk: mask bit 2q + h = half h of quadrant q may
-// take the splat. `half_end` gives each half's walk length (its largest
-// n_contrib); entries at or past it are not listed for that half.
-__device__ __forceinline__ unsigned stage_record_halves(StageLds& S, const SplatRec& r, float ox, float oy, int k,
-                                                        const int* half_end)
+// Staging test of the half-wave walk: hit[hq] says whether the splat can
+// reach half h of quadrant q (hq = 2 q + h; the 8x4 pixels of rows 4 h ..
+// 4 h + 3 of the quadrant), i.e. column q & 1 of 8-pixel columns and row
+// 2 (q >> 1) + h of 4-pixel rows. Over a rectangle of pixel centres, the
+// minimum of the convex form q' is 0 if the mean lies inside; otherwise it
+// lies on the vertical edge facing the mean or on the horizontal edge facing
+// it, and along a line the minimiser has a closed form, clamped to the edge.
+// Clamping the mean's own coordinate into the column (row) range picks the
+// facing edge, or the line through the mean when the mean lies within that
+// range, where the candidate is 0 or a value at a point of the rectangle (an
+// upper bound on the minimum). So min(vertical candidate, horizontal
+// candidate) is the exact minimum, with no branch. Both candidates are
+// evaluated as the sum of squares (l11 u + l21 v)^2 + (l22 v)^2, which loses
+// nothing to cancellation for elongated splats. Halves whose walk ends at or
+// before entry k (`hend`, wave-uniform) drop the entry.
+__device__ __forceinline__ void half_hits(const SplatRec& r, float ox, float oy, int k, const int (&hend)[kHalves],
+                                          bool (&hit)[kHalves])
 {
-    S.a[threadIdx.x] = r.a;
-    S.b[threadIdx.x] = r.b;
-    S.c[threadIdx.x] = r.c.x;
-    float qa, qb, qc;
-    qform_coef(r, qa, qb, qc);
-    unsigned mask = 0;
+    const float l11 = r.a.z, l21 = r.a.w, l22 = r.b.x, tau = r.c.y;
+    // the minimiser along x = u is y = kv u; along y = v it is x = kh v
+    const float kv = -l11 * l21 * __builtin_amdgcn_rcpf(__builtin_fmaf(l21, l21, l22 * l22));
+    const float kh = -l21 * __builtin_amdgcn_rcpf(l11);
+    const float bu = ox - r.a.x, bv = oy - r.a.y;
+    float u0[2], u1[2], pu[2], yu[2], v0[4], v1[4], pv[4], sv[4], xv[4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u0[c] = bu + (float)(8 * c);
+        u1[c] = u0[c] + 7.0f;
+        const float u = __builtin_amdgcn_fmed3f(0.0f, u0[c], u1[c]);
+        pu[c] = l11 * u;
+        yu[c] = kv * u;
+    }
+#pragma unroll
+    for (int rw = 0; rw < 4; ++rw) {
+        v0[rw] = bv + (float)(4 * rw);
+        v1[rw] = v0[rw] + 3.0f;
+        const float v = __builtin_amdgcn_fmed3f(0.0f, v0[rw], v1[rw]);
+        pv[rw] = l21 * v;
+        const float t = l22 * v;
+        sv[rw] = t * t;
+        xv[rw] = kh * v;
+    }
 #pragma unroll
     for (int hq = 0; hq < kHalves; ++hq) {
-        const int q = hq >> 1, h = hq & 1;
-        const float x0 = ox + (float)((q & 1) * 8) - r.a.x;
-        const float y0 = oy + (float)((q >> 1) * 8 + h * 4) - r.a.y;
-        if (k < half_end[hq] && rect_min_q(qa, qb, qc, x0, x0 + 7.0f, y0, y0 + 3.0f) <= r.c.y)
-            mask |= 1u << hq;
+        const int q = hq >> 1, c = q & 1, rw = 2 * (q >> 1) + (hq & 1);
+        const float ys = __builtin_amdgcn_fmed3f(yu[c], v0[rw], v1[rw]);
+        const float a1 = __builtin_fmaf(l21, ys, pu[c]);
+        const float b1 = l22 * ys;
+        const float qv = __builtin_fmaf(a1, a1, b1 * b1);
+        const float xs = __builtin_amdgcn_fmed3f(xv[rw], u0[c], u1[c]);
+        const float a2 = __builtin_fmaf(l11, xs, pv[rw]);
+        const float qh = __builtin_fmaf(a2, a2, sv[rw]);
+        hit[hq] = (fminf(qv, qh) <= tau) & (k < hend[hq]);
     }
-    return mask;
 }
 
-// Per-half lists from every thread's 8-bit mask (list hq holds the batch
-// slots half hq may take, in list order); ends with a workgroup barrier.
-__device__ __forceinline__ void build_half_lists(unsigned mask, unsigned char (*list)[kBlock], int (*cnt)[kHalves])
+// Per-half lists of the batch slots whose hit bit is set, in slot order
+// (list hq holds the slots half hq may take); ends with a workgroup barrier.
+__device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], unsigned char (*list)[kBlock],
+                                                 int (*cnt)[kHalves])
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    unsigned long long bal[kHalves];
-#pragma unroll
-    for (int q = 0; q < kHalves; ++q) bal[q] = __ballot((mask >> q) & 1u);
-    if (lane == 0) {
-#pragma unroll
-        for (int q = 0; q < kHalves; ++q) cnt[wv][q] = __popcll(bal[q]);
-    }
-    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int mine = 0;
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
-        if ((mask >> q) & 1u) {
-            int off = __popcll(bal[q] & lt_mask);
-            for (int w2 = 0; w2 < wv; ++w2) off += cnt[w2][q];
+        const int c = __popcll(__ballot(hit[q]));  // whole-wave ballot, outside any lane branch
+        mine = lane == q ? c : mine;
+    }
+    if (lane < kHalves) cnt[wv][lane] = mine;
+    __syncthreads();
+    int base = 0;  // lane q: slots of half q staged by lower waves
+    if (lane < kHalves)
+        for (int w2 = 0; w2 < wv; ++w2) base += cnt[w2][lane];
+#pragma unroll
+    for (int q = 0; q < kHalves; ++q) {
+        const unsigned long long bal = __ballot(hit[q]);
+        if (hit[q]) {
+            const unsigned off = __builtin_amdgcn_mbcnt_hi(
+                (unsigned)(bal >> 32),
+                __builtin_amdgcn_mbcnt_lo((unsigned)bal, (unsigned)__builtin_amdgcn_readlane(base, q)));
             list[q][off] = (unsigned char)threadIdx.x;
         }
     }
@@ -320,18 +359,23 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         g1 = dimg[3 * p + 1];
         g2 = dimg[3 * p + 2];
     }
-    // colour "behind" the current splat, normalised by the transmittance
-    // after it; starts as the background
-    float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;
-    if (bg) { B0 = bg[0]; B1 = bg[1]; B2 = bg[2]; }
+    // Colour "behind" the current splat (normalised by the transmittance after
+    // it; the background at the start), carried only as its dot product with
+    // the pixel's colour gradient
+    float Bg = 0.0f;
+    if (bg) Bg = __builtin_fmaf(bg[0], g0, __builtin_fmaf(bg[1], g1, bg[2] * g2));
 
     int hmax = nc;  // largest n_contrib of this half (32 lanes)
     for (int off = 16; off > 0; off >>= 1) hmax = max(hmax, __shfl_xor(hmax, off, 64));
     if ((lane & 31) == 0) half_end[hq] = hmax;
     __syncthreads();
+    int hend[kHalves];  // walk end of every half, wave-uniform
     int tmax = 0;
 #pragma unroll
-    for (int q = 0; q < kHalves; ++q) tmax = max(tmax, half_end[q]);
+    for (int q = 0; q < kHalves; ++q) {
+        hend[q] = __builtin_amdgcn_readfirstlane(half_end[q]);
+        tmax = max(tmax, hend[q]);
+    }
     if (tmax == 0) return;
 
     // leaders of the merged reduction: one lane per 4-lane bank of W (bank b
@@ -345,73 +389,112 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         __syncthreads();  // previous batch fully flushed before LDS is reused
         const int k = bs + (int)threadIdx.x;
         int id = -1, radius = 0;
-        unsigned mask = 0;
+        SplatRec r;
+        r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
         if (k < tmax) {
             id = ids[rg.x + k];
-            const SplatRec r = recs[id];
+            r = recs[id];
             radius = __float_as_int(r.c.z);
-            mask = stage_record_halves(S, r, ox, oy, k, half_end);
+            S.a[threadIdx.x] = r.a;
+            S.b[threadIdx.x] = r.b;
+            S.c[threadIdx.x] = r.c.x;
 #pragma unroll
             for (int f = 0; f < kRaw; ++f) part[threadIdx.x][f] = 0.0f;
         }
-        build_half_lists(mask, list, list_cnt);
+        bool hit[kHalves];
+        half_hits(r, ox, oy, k, hend, hit);
+        build_half_lists(hit, list, list_cnt);
         // this lane's half list, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
         const int steps = max(my_len, len_other);
+        const int ncb = nc - bs;  // batch slots below this pixel's walk end
 
-        for (int it = 0; it < steps; ++it) {
-            const bool live = it < my_len;  // half-uniform
-            // each half walks its own list in reverse; a half whose list is
-            // exhausted reads the other half's entry (staged, finite) and takes
-            // no part: its alpha is masked, so T and the colour behind stay put
-            const int j = live ? list[hq][my_len - 1 - it] : list[other][len_other - 1 - it];
+        // One step of the reverse walk over batch slot j. `live` is
+        // half-uniform: a half whose list is exhausted follows the other
+        // half's entries (staged, finite) with its alpha masked, so T and the
+        // colour behind stay put and it adds nothing.
+        auto step = [&](int j, bool live) {
+            // the whole record at once: one LDS round trip per step
             const float4 A = S.a[j];
             const float4 Bq = S.b[j];
+            const float Cb = S.c[j];
             const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
             float dx, dy;
             const float ar = alpha_raw(kf, px, py, dx, dy);
             const float al = fminf(kAlphaMax, ar);
-            const bool contrib = live && (bs + j < nc) && (al >= kAlphaMin);
-            if (__ballot(contrib) == 0) continue;
+            const bool contrib = live && (j < ncb) && (al >= kAlphaMin);
+            // colour . gradient ahead of the test, so that the colour loads
+            // issue with the rest of the record (steps with no contribution
+            // are rare: the lists are culled per half)
+            float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
+            asm volatile("" : "+v"(cg));  // not sunk into the branch below
+            if (__ballot(contrib) == 0) return;
 
             const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
             const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
-            const float e0 = Bq.z - B0, e1 = Bq.w - B1, e2 = S.c[j] - B2;
-            const float dal = Ti * __builtin_fmaf(e0, g0, __builtin_fmaf(e1, g1, e2 * g2));
-            B0 = __builtin_fmaf(ae, e0, B0);
-            B1 = __builtin_fmaf(ae, e1, B1);
-            B2 = __builtin_fmaf(ae, e2, B2);
+            // dL/dalpha needs the colour behind only through its dot product
+            // with the pixel's colour gradient, which follows the same
+            // recurrence as the colour itself
+            const float eg = cg - Bg;
+            const float dal = Ti * eg;
+            Bg = __builtin_fmaf(ae, eg, Bg);
             T = Ti;
             const float w = ae * Ti;
             const float s = (ar < kAlphaMax) ? ae * dal : 0.0f;  // clamped alpha: no sigma path
-            // all ten values first, then the folds (no value is read after its
+            // all values first, then the folds (no value is read after its
             // register has been swapped)
             const float sdx = s * dx, sdy = s * dy;
             const float f0 = w * g0, f1 = w * g1, f2 = w * g2;
-            const float f6 = sdx * dx, f7 = sdx * dy, f8 = sdy * dy;
-            const float f9 = AW ? w : 0.0f;
+            const float f6 = sdx * dx, f7 = sdx * dy;
+            float f8 = sdy * dy;
+            // a plain product: left alone, the compiler fuses it into the first
+            // DPP add as mov + DPP mov + fma, and copies sdy around the swaps
+            asm volatile("" : "+v"(f8));
             // Fold rows (0, 1) and (2, 3): register R_k row r then holds field
             // 2k + (r & 1) of half r >> 1, summed over its two rows.
             const float r0 = fold16(f0, f1);
             const float r1 = fold16(f2, s);
             const float r2 = fold16(sdx, sdy);
             const float r3 = fold16(f6, f7);
-            const float r4 = fold16(f8, f9);
             // Inside each row: merge pairs of registers while halving the
             // lanes each partial covers (8 -> 4 -> 1 lanes): W's 4-lane bank b
-            // ends with the total of R_{0,2,1,3}[b]; r4 is reduced alone.
+            // ends with the total of R_{0,2,1,3}[b].
             const float wq = merge_half_mirror(merge_ror8(r0, r1), merge_ror8(r2, r3));
             float wt = dpp_add_quad_xor1(dpp_add_quad_xor2(wq));
-            float zt = dpp_add_quad_xor1(dpp_add_quad_xor2(dpp_add_half_mirror(dpp_add_ror8(r4))));
+            // field 8 (and the weight): folded with the weight when it is
+            // wanted, else summed per row and added by both row leaders
+            float zt = AW ? fold16(f8, w) : f8;
+            zt = dpp_add_quad_xor1(dpp_add_quad_xor2(dpp_add_half_mirror(dpp_add_ror8(zt))));
             // keep the last fused DPP adds here rather than under the leader masks
             asm volatile("" : "+v"(wt), "+v"(zt));
             if (live) {
                 float* P = part[j];
                 if (bank_lead) atomicAdd(&P[w_field], wt);
-                if (row_lead && (AW || !odd)) atomicAdd(&P[8 + odd], zt);
+                if (row_lead) atomicAdd(&P[AW ? 8 + odd : 8], zt);
             }
+        };
+        // both halves on their own lists, then the longer one alone
+        const int both = min(my_len, len_other);
+        // (the next list entry is read one step ahead, off the step's chain of
+        // dependent LDS reads)
+        int jn = list[hq][max(my_len - 1, 0)];
+        for (int it = 0; it < both; ++it) {
+            const int j = jn;
+            jn = list[hq][max(my_len - 2 - it, 0)];
+            step(j, true);
+        }
+        const int len0 = __builtin_amdgcn_readfirstlane(my_len);     // lane 0 is in half 0
+        const int len1 = __builtin_amdgcn_readfirstlane(len_other);
+        const int hl = 2 * wv + (len1 > len0 ? 1 : 0);  // the longer half
+        const bool live2 = hq == hl;
+        jn = list[hl][max(steps - 1 - both, 0)];
+        for (int it = both; it < steps; ++it) {
+            const int j = jn;
+            jn = list[hl][max(steps - 2 - it, 0)];
+            step(j, live2);
         }
         __syncthreads();
 
