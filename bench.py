@@ -100,7 +100,7 @@ def main():
     log(f"workload {args.config}: {sc.width}x{sc.height}, {sc.n} splats, accum_weight={aw}")
     bins = gsr.gs_bin_tiles(m, r, d, sc.width, sc.height)
     img, T, nc = gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
-    ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_isect) + 256, dtype=torch.uint8,
+    ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_isect, sc.width, sc.height) + 256, dtype=torch.uint8,
                      device=dev)
     out = gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw,
                                workspace=ws)

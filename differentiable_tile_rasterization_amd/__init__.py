@@ -156,7 +156,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
     per-splat accumulated weight [n]. ``out`` may pass preallocated outputs
     (same dict keys) and ``workspace`` a uint8 device buffer of at least
-    gs_rasterize_bwd_workspace_size(n, n_isect) + 256 bytes, to keep
+    gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
     allocation out of timed loops."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
@@ -182,7 +182,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
                "dL_dopacities": torch.empty((n,), dtype=torch.float32, device=dev)}
         if accum_weight:
             out["accum_weight"] = torch.empty((n,), dtype=torch.float32, device=dev)
-    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect))
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
     _lib.check(lib.gs_rasterize_bwd(
@@ -194,8 +194,8 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     return out
 
 
-def gs_rasterize_bwd_workspace_size(n: int, n_isect: int) -> int:
-    return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_isect))
+def gs_rasterize_bwd_workspace_size(n: int, n_isect: int, width: int, height: int) -> int:
+    return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_isect, width, height))
 
 
 def gs_rasterize_fwd_workspace_size(n: int) -> int:

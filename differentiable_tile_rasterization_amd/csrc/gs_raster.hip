@@ -15,16 +15,20 @@
 //                 random ids; a record costs one 48-byte read per list entry
 //                 where the caller's four separate arrays cost about five
 //                 cache lines.
-//   staging       per batch of 256 list entries, thread t loads entry t's
-//                 record, writes the alpha coefficients and colour to LDS and
-//                 tests the splat's alpha >= 1/255 ellipse against each
-//                 wave's quadrant; ballots build one compacted list per wave.
-//   walk          each wave walks only its own list, reading the coefficients
-//                 with broadcast LDS loads.
+//   staging       per batch of list entries (256 in the forward, 255 and a
+//                 dummy in the backward), thread t loads entry t's record,
+//                 writes the alpha coefficients and colour to LDS and tests
+//                 the splat's alpha >= 1/255 ellipse against each wave's
+//                 quadrant (forward) or each 8x4 half-quadrant (backward);
+//                 ballots build one compacted list per wave or half.
+//   walk          each wave (half) walks only its own list, reading the
+//                 coefficients with broadcast LDS loads.
 // Optional outputs are template parameters, so a variant without the
 // accumulated weight carries no register, LDS slot or store for it (the lesson
 // of section 机制拆解 of the Spirula Studio page, where optional feature arrays
 // sized regardless of the switch halved occupancy).
+#include <cstddef>
+
 #include "gs_common.hpp"
 
 namespace gs {
@@ -219,11 +223,18 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
 // 0-31 and 32-63), and each half has its own culled list. The wave steps both
 // lists in lockstep, each half on its own splat, so a small splat that reaches
 // only one half no longer costs the whole wave a step: on the 2M-splat scene
-// this cuts wave steps from 4.67M to about 3.3M. The per-step reduction stays
-// inside each half: five v_permlane16_swap + adds fold rows (0, 1) and (2, 3)
-// pairwise, leaving five registers whose four rows hold (field, half) pairs,
-// and four row_ror DPP adds finish each row; the four row-leader lanes then
-// add five values each into the workgroup's LDS partial of their half's entry.
+// this cuts wave steps from 4.67M to about 3.3M. Once the shorter list is
+// exhausted its half takes a dummy entry of opacity 0. The per-step reduction
+// stays inside each half: v_permlane16_swap + adds fold rows (0, 1) and
+// (2, 3) pairwise, leaving registers whose four rows hold (field, half) pairs,
+// and bank-masked DPP adds merge them while finishing each row; a few leader
+// lanes then add the totals into the workgroup's LDS partial of their half's
+// entry.
+//
+// Finer lists (one per 4x4 block, four per wave) take about 18% fewer steps
+// but were slower here: the workgroup meets at a barrier after every batch,
+// and the slowest of sixteen lists keeps the other waves waiting longer than
+// the slowest of eight.
 //
 // No global atomics: every (splat, tile) pair owns a fixed record slot, the
 // pair's index in the binning's enumeration (the splat's first slot plus the
@@ -293,9 +304,31 @@ __device__ __forceinline__ void half_hits(const SplatRec& r, float ox, float oy,
     }
 }
 
-// Per-half lists of the batch slots whose hit bit is set, in slot order
-// (list hq holds the slots half hq may take); ends with a workgroup barrier.
-__device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], unsigned char (*list)[kBlock],
+// LDS slot of one staged entry: its alpha coefficients and colour, and the
+// partial sums the walk adds into it. One base address serves every access of
+// a walk step (the lists hold slot byte offsets), so a step spends no VALU
+// instruction on addressing beyond the leaders' field offset.
+// The 80-byte stride is an odd multiple of 16 bytes, so the per-entry 16-byte
+// accesses of staging, zeroing and flushing hit distinct banks.
+struct BwdSlot {
+    float4 a;           // mean x, mean y, l11, l21 (scaled factor)
+    float4 b;           // l22, log2(opacity), red, green
+    float part[kRaw];   // w g_r, w g_g, w g_b, s, s dx, s dy, s dx^2, s dx dy, s dy^2, [w]
+    float c;            // blue
+    float pad;
+};
+static_assert(sizeof(BwdSlot) == 80 && offsetof(BwdSlot, part) == 32, "BwdSlot layout");
+
+__device__ __forceinline__ float4* part4(BwdSlot& e, int i) { return reinterpret_cast<float4*>(e.part) + i; }
+constexpr int kBatch = kBlock - 1;                                    // entries staged per batch
+constexpr int kDummy = kBlock - 1;                                    // slot of the dummy entry
+constexpr unsigned short kDummyOff = (unsigned short)(kDummy * sizeof(BwdSlot));
+constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummies read ahead of use
+
+// Per-half lists of the staged slots whose hit bit is set, as slot byte
+// offsets in descending slot order (the walk's order). Returns nothing; ends
+// with a workgroup barrier.
+__device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], unsigned short (*list)[kListLen],
                                                  int (*cnt)[kHalves])
 {
     const int lane = threadIdx.x & 63;
@@ -308,17 +341,26 @@ __device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], uns
     }
     if (lane < kHalves) cnt[wv][lane] = mine;
     __syncthreads();
-    int base = 0;  // lane q: slots of half q staged by lower waves
-    if (lane < kHalves)
-        for (int w2 = 0; w2 < wv; ++w2) base += cnt[w2][lane];
+    // lane q: list position of this wave's lowest hit of half q, counted from
+    // the front (slots of higher waves come first)
+    int top = 0;
+    if (lane < kHalves) {
+        int tot = 0, below = 0;
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const int c = cnt[w2][lane];
+            tot += c;
+            below += w2 < wv ? c : 0;
+        }
+        top = tot - 1 - below;
+    }
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
         const unsigned long long bal = __ballot(hit[q]);
         if (hit[q]) {
-            const unsigned off = __builtin_amdgcn_mbcnt_hi(
-                (unsigned)(bal >> 32),
-                __builtin_amdgcn_mbcnt_lo((unsigned)bal, (unsigned)__builtin_amdgcn_readlane(base, q)));
-            list[q][off] = (unsigned char)threadIdx.x;
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+            list[q][__builtin_amdgcn_readlane(top, q) - rank] =
+                (unsigned short)(threadIdx.x * sizeof(BwdSlot));
         }
     }
     __syncthreads();
@@ -329,16 +371,16 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     int W, int H, int GX, int GY, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
     const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
-    const float* __restrict__ dimg, float4* __restrict__ rec_out, unsigned char* __restrict__ slot_used)
+    const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
+    unsigned char* __restrict__ slot_used)
 {
-    __shared__ StageLds S;
-    __shared__ float part[kBlock][kRaw];
+    __shared__ BwdSlot S[kBlock];
     __shared__ int half_end[kHalves];
-    __shared__ unsigned char list[kHalves][kBlock];  // per half: batch slots that may touch it
-    __shared__ int list_cnt[4][kHalves];              // [staging wave][half]
+    __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
+    __shared__ int list_cnt[4][kHalves];               // [staging wave][half]
 
-    const int tile = xcd_tile(blockIdx.x, tiles);
-    if (tile >= tiles) return;
+    const int tile = order ? order[blockIdx.x] : xcd_tile(blockIdx.x, tiles);
+    if (tile < 0 || tile >= tiles) return;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int half = lane >> 5, hq = 2 * wv + half;
     int x, y;
@@ -368,6 +410,11 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     int hmax = nc;  // largest n_contrib of this half (32 lanes)
     for (int off = 16; off > 0; off >>= 1) hmax = max(hmax, __shfl_xor(hmax, off, 64));
     if ((lane & 31) == 0) half_end[hq] = hmax;
+    if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel, sums stay 0
+        S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
+        S[kDummy].c = 0.0f;
+    }
     __syncthreads();
     int hend[kHalves];  // walk end of every half, wave-uniform
     int tmax = 0;
@@ -384,66 +431,71 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const int odd = (lane >> 4) & 1;
     const bool bank_lead = (lane & 3) == 0, row_lead = (lane & 15) == 0;
     const int w_field = 2 * ((0x3120 >> (4 * ((lane >> 2) & 3))) & 3) + odd;
+    const int lead_off = (int)offsetof(BwdSlot, part) + 4 * w_field;  // byte offset of the bank leader's field
 
-    for (int bs = ((tmax - 1) / kBlock) * kBlock; bs >= 0; bs -= kBlock) {
+    for (int bs = ((tmax - 1) / kBatch) * kBatch; bs >= 0; bs -= kBatch) {
         __syncthreads();  // previous batch fully flushed before LDS is reused
         const int k = bs + (int)threadIdx.x;
         int id = -1, radius = 0;
         SplatRec r;
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
-        if (k < tmax) {
+        if (threadIdx.x < kBatch && k < tmax) {
             id = ids[rg.x + k];
             r = recs[id];
             radius = __float_as_int(r.c.z);
-            S.a[threadIdx.x] = r.a;
-            S.b[threadIdx.x] = r.b;
-            S.c[threadIdx.x] = r.c.x;
-#pragma unroll
-            for (int f = 0; f < kRaw; ++f) part[threadIdx.x][f] = 0.0f;
+            S[threadIdx.x].a = r.a;
+            S[threadIdx.x].b = r.b;
+            S[threadIdx.x].c = r.c.x;
         }
+        *part4(S[threadIdx.x], 0) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        *part4(S[threadIdx.x], 1) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        *reinterpret_cast<float2*>(S[threadIdx.x].part + 8) = make_float2(0.0f, 0.0f);
         bool hit[kHalves];
         half_hits(r, ox, oy, k, hend, hit);
         build_half_lists(hit, list, list_cnt);
-        // this lane's half list, and the wave's step count (longer half)
+        // this half's list length, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
         const int steps = max(my_len, len_other);
-        const int ncb = nc - bs;  // batch slots below this pixel's walk end
+        // the shorter half takes the dummy entry once its list is exhausted
+        // (and both read up to four entries past the end, ahead of use)
+        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDummyOff;
+        // batch slots below this pixel's walk end, as a byte offset bound
+        const int ncb_off = (nc - bs) * (int)sizeof(BwdSlot);
+        const unsigned short* L = list[hq];
+        const char* Sb = reinterpret_cast<const char*>(S);
 
-        // One step of the reverse walk over batch slot j. `live` is
-        // half-uniform: a half whose list is exhausted follows the other
-        // half's entries (staged, finite) with its alpha masked, so T and the
-        // colour behind stay put and it adds nothing.
-        auto step = [&](int j, bool live) {
-            // the whole record at once: one LDS round trip per step
-            const float4 A = S.a[j];
-            const float4 Bq = S.b[j];
-            const float Cb = S.c[j];
+        // A step's alpha does not depend on the previous step, so the next
+        // entry's record is read one step ahead and its list entry two steps
+        // ahead: their LDS reads leave the chain of dependent instructions.
+        // Two register sets take turns (the loop is unrolled by two), so the
+        // read-ahead costs no register copies.
+        auto rec_at = [&](int o) -> const BwdSlot& { return *reinterpret_cast<const BwdSlot*>(Sb + o); };
+        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur) {
             const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
             float dx, dy;
             const float ar = alpha_raw(kf, px, py, dx, dy);
             const float al = fminf(kAlphaMax, ar);
-            const bool contrib = live && (j < ncb) && (al >= kAlphaMin);
+            const bool contrib = (cur < ncb_off) && (al >= kAlphaMin);
             // colour . gradient ahead of the test, so that the colour loads
-            // issue with the rest of the record (steps with no contribution
-            // are rare: the lists are culled per half)
+            // issue with the rest of the record
             float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
             asm volatile("" : "+v"(cg));  // not sunk into the branch below
             if (__ballot(contrib) == 0) return;
 
             const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
             const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
-            // dL/dalpha needs the colour behind only through its dot product
-            // with the pixel's colour gradient, which follows the same
-            // recurrence as the colour itself
+            // dL/dalpha = T_i (c - colour behind) . g needs the colour behind
+            // only through its dot product with the pixel's colour gradient,
+            // which follows the same recurrence as the colour itself; then
+            // s = dL/dsigma = alpha dL/dalpha = w (c - behind) . g
             const float eg = cg - Bg;
-            const float dal = Ti * eg;
             Bg = __builtin_fmaf(ae, eg, Bg);
             T = Ti;
             const float w = ae * Ti;
-            const float s = (ar < kAlphaMax) ? ae * dal : 0.0f;  // clamped alpha: no sigma path
+            const float s = (ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
             // all values first, then the folds (no value is read after its
             // register has been swapped)
             const float sdx = s * dx, sdy = s * dy;
@@ -470,47 +522,44 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             zt = dpp_add_quad_xor1(dpp_add_quad_xor2(dpp_add_half_mirror(dpp_add_ror8(zt))));
             // keep the last fused DPP adds here rather than under the leader masks
             asm volatile("" : "+v"(wt), "+v"(zt));
-            if (live) {
-                float* P = part[j];
-                if (bank_lead) atomicAdd(&P[w_field], wt);
-                if (row_lead) atomicAdd(&P[AW ? 8 + odd : 8], zt);
-            }
+            char* P = const_cast<char*>(Sb) + cur;
+            if (bank_lead) atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
+            if (row_lead) atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
         };
-        // both halves on their own lists, then the longer one alone
-        const int both = min(my_len, len_other);
-        // (the next list entry is read one step ahead, off the step's chain of
-        // dependent LDS reads)
-        int jn = list[hq][max(my_len - 1, 0)];
-        for (int it = 0; it < both; ++it) {
-            const int j = jn;
-            jn = list[hq][max(my_len - 2 - it, 0)];
-            step(j, true);
-        }
-        const int len0 = __builtin_amdgcn_readfirstlane(my_len);     // lane 0 is in half 0
-        const int len1 = __builtin_amdgcn_readfirstlane(len_other);
-        const int hl = 2 * wv + (len1 > len0 ? 1 : 0);  // the longer half
-        const bool live2 = hq == hl;
-        jn = list[hl][max(steps - 1 - both, 0)];
-        for (int it = both; it < steps; ++it) {
-            const int j = jn;
-            jn = list[hl][max(steps - 2 - it, 0)];
-            step(j, live2);
+        int o0 = L[0], o1 = L[1], on0 = L[2];
+        float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+        float C0 = rec_at(o0).c;
+        for (int it = 0; it < steps; it += 2) {
+            // set 1 <- position it + 1; list position it + 3
+            const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+            const float C1 = rec_at(o1).c;
+            const int on1 = L[it + 3];
+            step(A0, B0, C0, o0);
+            if (it + 1 >= steps) break;
+            // set 0 <- position it + 2; list position it + 4
+            o0 = on0;
+            A0 = rec_at(o0).a;
+            B0 = rec_at(o0).b;
+            C0 = rec_at(o0).c;
+            on0 = L[it + 4];
+            step(A1, B1, C1, o1);
+            o1 = on1;
         }
         __syncthreads();
 
         // Flush: thread t owns the entry it staged.
         if (id >= 0) {
-            const float* P = part[threadIdx.x];
-            const float Swr = P[0], Swg = P[1], Swb = P[2], Ss = P[3], Sdx = P[4], Sdy = P[5];
-            const float Sdxx = P[6], Sdxy = P[7], Sdyy = P[8];
-            const float Sw = AW ? P[9] : 0.0f;
+            const float4 P0 = *part4(S[threadIdx.x], 0), P1 = *part4(S[threadIdx.x], 1);
+            const float2 P2 = *reinterpret_cast<const float2*>(S[threadIdx.x].part + 8);
+            const float Swr = P0.x, Swg = P0.y, Swb = P0.z, Ss = P0.w, Sdx = P1.x, Sdy = P1.y;
+            const float Sdxx = P1.z, Sdxy = P1.w, Sdyy = P2.x;
+            const float Sw = AW ? P2.y : 0.0f;
             const bool any = (Swr != 0.0f) | (Swg != 0.0f) | (Swb != 0.0f) | (Ss != 0.0f) |
                              (Sdx != 0.0f) | (Sdy != 0.0f) | (Sdxx != 0.0f) | (Sdxy != 0.0f) |
                              (Sdyy != 0.0f) | (Sw != 0.0f);
             if (any) {
-                const float4 A = S.a[threadIdx.x];
                 int tx0, tx1, ty0, ty1;
-                tile_rect(A.x, A.y, radius, GX, GY, tx0, tx1, ty0, ty1);
+                tile_rect(r.a.x, r.a.y, radius, GX, GY, tx0, tx1, ty0, ty1);
                 const int tx = tile % GX, ty = tile / GX;
                 const long long slot = (long long)splat_offsets[id] + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
                 // the tile lies in the splat's rectangle whenever the inputs come
@@ -524,6 +573,70 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Launch order of the backward's tiles: longest first inside each XCD's band.
+//
+// The backward runs about 2.6 rounds of resident workgroups per CU, and tile
+// costs vary (on the 2M-splat scene the costliest tile takes 1.5x the mean):
+// in plain tile order the last workgroups start late and leave CUs idle at
+// the end. Dispatching each band's tiles in decreasing order of their largest
+// n_contrib (the walk length; correlation 0.9 with the walk's cost) is the
+// longest-processing-time rule, which keeps that tail short. Workgroup w still
+// runs a tile of band w % 8 (the band of tile rows that XCD w % 8 works on),
+// as in the plain mapping.
+// ---------------------------------------------------------------------------
+constexpr int kMaxBand = 4096;  // tiles per band the ordering handles; larger grids keep plain order
+
+// one workgroup per tile: its largest n_contrib, clamped to its list length
+__global__ __launch_bounds__(256) void tile_cost_kernel(int W, int H, int GX, const int2* __restrict__ ranges,
+                                                         const int* __restrict__ n_contrib, int* __restrict__ cost)
+{
+    __shared__ int wave_max[4];
+    const int tile = blockIdx.x;
+    const int x = (tile % GX) * kTile + (threadIdx.x & 15), y = (tile / GX) * kTile + (threadIdx.x >> 4);
+    const int2 rg = ranges[tile];
+    int v = 0;
+    if (x < W && y < H) v = min(max(n_contrib[y * W + x], 0), rg.y - rg.x);
+    v = wave_max_i32(v);
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) cost[tile] = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+}
+
+// one workgroup per band: bitonic sort of (cost descending, tile ascending),
+// then order[r * 8 + band] = the band's r-th tile (-1 for padding)
+__global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* __restrict__ cost,
+                                                          int* __restrict__ order)
+{
+    __shared__ unsigned long long key[kMaxBand];
+    const int per = (tiles + kXcds - 1) / kXcds;
+    const int band = blockIdx.x, t0 = band * per;
+    const int n = max(0, min(per, tiles - t0));
+    int np = 1;
+    while (np < per) np <<= 1;
+    for (int i = threadIdx.x; i < np; i += blockDim.x)
+        key[i] = i < n ? ((unsigned long long)(0xffffffffu - (unsigned)cost[t0 + i]) << 32) | (unsigned)i
+                       : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= np; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < np; i += blockDim.x) {
+                const int ij = i ^ j;
+                if (ij > i) {
+                    const unsigned long long a = key[i], b = key[ij];
+                    if ((a > b) == ((i & k) == 0)) {
+                        key[i] = b;
+                        key[ij] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int r = threadIdx.x; r < per; r += blockDim.x)
+        order[r * kXcds + band] = r < n ? t0 + (int)(unsigned)(key[r] & 0xffffffffull) : -1;
 }
 
 // One thread per splat: sum its used slots in slot order, apply the splat's
@@ -592,18 +705,21 @@ hipError_t clear_bytes(unsigned char* p, long long n, hipStream_t st)
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace layouts. Forward: splat records. Backward: splat records, then the
-// per-(splat, tile) slots (3 float4 each) and their used-flags.
+// per-(splat, tile) slots (3 float4 each) and their used-flags, then the tile
+// costs and the launch order.
 struct Layout {
-    size_t recs, slots, used, bytes;
+    size_t recs, slots, used, cost, order, bytes;
 };
 
-Layout layout(long long n, long long n_slots)
+Layout layout(long long n, long long n_slots, long long tiles)
 {
     Layout L{};
     L.recs = 0;
     L.slots = align256(sizeof(SplatRec) * (size_t)(n > 0 ? n : 1));
     L.used = L.slots + (n_slots > 0 ? align256(sizeof(float4) * 3 * (size_t)n_slots) : 0);
-    L.bytes = L.used + (n_slots > 0 ? align256((size_t)n_slots + 4) : 0);
+    L.cost = L.used + (n_slots > 0 ? align256((size_t)n_slots + 4) : 0);
+    L.order = L.cost + (tiles > 0 ? align256(sizeof(int) * (size_t)tiles) : 0);
+    L.bytes = L.order + (tiles > 0 ? align256(sizeof(int) * (size_t)xcd_grid((int)tiles)) : 0);
     return L;
 }
 
@@ -615,7 +731,7 @@ using namespace gs;
 extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
 {
     if (n < 0) return 0;
-    return layout(n, 0).bytes;
+    return layout(n, 0, 0).bytes;
 }
 
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
@@ -631,7 +747,7 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
     GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
     GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
-    const Layout L = layout(n, 0);
+    const Layout L = layout(n, 0, 0);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_fwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_fwd: workspace not 256-byte aligned");
@@ -648,10 +764,10 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
     return GS_OK;
 }
 
-extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect)
+extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height)
 {
-    if (n < 0 || n_isect < 0) return 0;
-    return layout(n, n_isect).bytes;
+    if (n < 0 || n_isect < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
+    return layout(n, n_isect, (long long)grid_x(width) * grid_y(height)).bytes;
 }
 
 extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
@@ -679,7 +795,7 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(tile_ranges && final_T && n_contrib && dL_dimage, "gs_rasterize_bwd: NULL image-side array");
     GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_bwd: sorted_ids is NULL");
     const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
-    const Layout L = layout(n, n_isect);
+    const Layout L = layout(n, n_isect, tiles);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_bwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_bwd: workspace not 256-byte aligned");
@@ -687,19 +803,29 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     SplatRec* recs = (SplatRec*)((char*)workspace + L.recs);
     float4* slots = n_isect ? (float4*)((char*)workspace + L.slots) : nullptr;
     unsigned char* used = n_isect ? (unsigned char*)workspace + L.used : nullptr;
+    int* cost = (int*)((char*)workspace + L.cost);
+    int* order = (int*)((char*)workspace + L.order);
     if (n_isect > 0) {
         GS_HIP(clear_bytes(used, (n_isect + 3) & ~3ll, st));  // whole 4-byte flag words
         prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, radii,
                                                      recs);
         GS_HIP(hipGetLastError());
+        const int* ord = nullptr;
+        if ((tiles + kXcds - 1) / kXcds <= kMaxBand) {
+            tile_cost_kernel<<<tiles, 256, 0, st>>>(width, height, GX, (const int2*)tile_ranges, n_contrib, cost);
+            GS_HIP(hipGetLastError());
+            band_order_kernel<<<kXcds, 1024, 0, st>>>(tiles, cost, order);
+            GS_HIP(hipGetLastError());
+            ord = order;
+        }
         if (aw)
             bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
                 width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
-                background, final_T, n_contrib, dL_dimage, slots, used);
+                background, final_T, n_contrib, dL_dimage, ord, slots, used);
         else
             bwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(
                 width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
-                background, final_T, n_contrib, dL_dimage, slots, used);
+                background, final_T, n_contrib, dL_dimage, ord, slots, used);
         GS_HIP(hipGetLastError());
     }
     const unsigned gb = (unsigned)((n + 255) / 256);

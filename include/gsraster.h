@@ -202,15 +202,17 @@ gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics,
  *                        GS_FLAG_ACCUM_WEIGHT, else ignored (may be NULL)
  *   flags                bitwise OR of GS_FLAG_*
  *   workspace            device scratch of at least
- *                        gs_rasterize_bwd_workspace_size(n, n_isect) bytes
- *                        (48 per splat + 49 per pair), 256-byte aligned;
- *                        contents on entry do not matter
+ *                        gs_rasterize_bwd_workspace_size(n, n_isect, width,
+ *                        height) bytes (48 per splat + 49 per pair + 8 per
+ *                        tile), 256-byte aligned; contents on entry do not
+ *                        matter
  *
  * Every output element is written; splats that no pixel takes get exact
  * zeros. Inputs that do not come from one binning of the same splats are
  * not detected; the kernels never write outside the outputs and workspace.
  */
-size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect);
+/* 0 for n < 0, n_isect < 0 or a width / height outside 1..32768 */
+size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height);
 
 gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                            const float* opacities, const int32_t* radii, const float* background,

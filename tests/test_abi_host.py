@@ -79,7 +79,7 @@ def test_bwd_rejects_bad_arguments():
     assert call(w=-3) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=1 << 31) == _lib.GS_ERR_INVALID_ARG
-    need = lib.gs_rasterize_bwd_workspace_size(1, 100)
+    need = lib.gs_rasterize_bwd_workspace_size(1, 100, 8, 8)
     assert need >= 100 * 49 + 64
     assert call(n_isect=100, ws=None, wsb=need) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
