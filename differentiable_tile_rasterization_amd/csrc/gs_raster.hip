@@ -45,13 +45,11 @@ struct SplatRec {
 
 constexpr float kQScale = 0.72134752044448170f;  // log2(e) / 2: q' = kQScale q
 
-__global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
-                                                   const float* __restrict__ conics, const float* __restrict__ colors,
-                                                   const float* __restrict__ opac, const int* __restrict__ radii,
-                                                   SplatRec* __restrict__ recs)
+// The record of splat i, from the caller's arrays (radii may be NULL).
+__device__ __forceinline__ SplatRec make_rec(int i, const float2* __restrict__ means,
+                                             const float* __restrict__ conics, const float* __restrict__ colors,
+                                             const float* __restrict__ opac, const int* __restrict__ radii)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
     const float2 m = means[i];
     const float a = conics[3 * i + 0], b = conics[3 * i + 1], c = conics[3 * i + 2];
     const float o = opac[i];
@@ -60,6 +58,17 @@ __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restri
     r.a = make_float4(k.mx, k.my, k.l11, k.l21);
     r.b = make_float4(k.l22, k.lo, colors[3 * i + 0], colors[3 * i + 1]);
     r.c = make_float4(colors[3 * i + 2], kQScale * cull_tau(o), __int_as_float(radii ? radii[i] : 0), 0.0f);
+    return r;
+}
+
+__global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
+                                                   const float* __restrict__ conics, const float* __restrict__ colors,
+                                                   const float* __restrict__ opac, const int* __restrict__ radii,
+                                                   SplatRec* __restrict__ recs)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const SplatRec r = make_rec(i, means, conics, colors, opac, radii);
     recs[i] = r;
 }
 
@@ -587,56 +596,91 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
 // runs a tile of band w % 8 (the band of tile rows that XCD w % 8 works on),
 // as in the plain mapping.
 // ---------------------------------------------------------------------------
-constexpr int kMaxBand = 4096;  // tiles per band the ordering handles; larger grids keep plain order
 
-// one workgroup per tile: its largest n_contrib, clamped to its list length
-__global__ __launch_bounds__(256) void tile_cost_kernel(int W, int H, int GX, const int2* __restrict__ ranges,
-                                                         const int* __restrict__ n_contrib, int* __restrict__ cost)
+// Setup of a backward call, one launch. Blocks [0, cost_blocks) give one
+// wave per tile its largest n_contrib, clamped to its list length (the walk
+// length); the next rec_blocks pack one splat record per thread (as
+// prep_kernel); the rest clear the slot flags with 16-byte stores.
+__global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, int tiles, int cost_blocks,
+                                                        const int2* __restrict__ ranges,
+                                                        const int* __restrict__ n_contrib, int* __restrict__ cost,
+                                                        int n, int rec_blocks, const float2* __restrict__ means,
+                                                        const float* __restrict__ conics,
+                                                        const float* __restrict__ colors,
+                                                        const float* __restrict__ opac, const int* __restrict__ radii,
+                                                        SplatRec* __restrict__ recs, uint4* __restrict__ flags16,
+                                                        long long n16)
 {
-    __shared__ int wave_max[4];
-    const int tile = blockIdx.x;
-    const int x = (tile % GX) * kTile + (threadIdx.x & 15), y = (tile / GX) * kTile + (threadIdx.x >> 4);
-    const int2 rg = ranges[tile];
-    int v = 0;
-    if (x < W && y < H) v = min(max(n_contrib[y * W + x], 0), rg.y - rg.x);
-    v = wave_max_i32(v);
-    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) cost[tile] = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    const int b = blockIdx.x;
+    if (b < cost_blocks) {
+        const int tile = b * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+        if (tile >= tiles) return;
+        const int2 rg = ranges[tile];
+        const int y = (tile / GX) * kTile + (lane >> 2), x0 = (tile % GX) * kTile + 4 * (lane & 3);
+        int v = 0;
+        if (y < H) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (x0 + c < W) v = max(v, n_contrib[y * W + x0 + c]);
+        }
+        v = min(max(v, 0), rg.y - rg.x);
+        v = wave_max_i32(v);
+        if (lane == 0) cost[tile] = v;
+        return;
+    }
+    if (b < cost_blocks + rec_blocks) {
+        const int i = (b - cost_blocks) * 256 + threadIdx.x;
+        if (i < n) recs[i] = make_rec(i, means, conics, colors, opac, radii);
+        return;
+    }
+    const long long i = (long long)(b - cost_blocks - rec_blocks) * 256 + threadIdx.x;
+    if (i < n16) flags16[i] = make_uint4(0, 0, 0, 0);
 }
 
-// one workgroup per band: bitonic sort of (cost descending, tile ascending),
-// then order[r * 8 + band] = the band's r-th tile (-1 for padding)
+// One workgroup per band: counting sort of the band's tiles into 256 cost
+// buckets, costliest bucket first, then order[r * 8 + band] = the band's r-th
+// tile (-1 for padding). Ties within a bucket take any order; no result
+// depends on the launch order, only the time does.
 __global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* __restrict__ cost,
                                                           int* __restrict__ order)
 {
-    __shared__ unsigned long long key[kMaxBand];
+    __shared__ int hist[256];
+    __shared__ int cmax;
     const int per = (tiles + kXcds - 1) / kXcds;
     const int band = blockIdx.x, t0 = band * per;
     const int n = max(0, min(per, tiles - t0));
-    int np = 1;
-    while (np < per) np <<= 1;
-    for (int i = threadIdx.x; i < np; i += blockDim.x)
-        key[i] = i < n ? ((unsigned long long)(0xffffffffu - (unsigned)cost[t0 + i]) << 32) | (unsigned)i
-                       : ~0ull;
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+    if (threadIdx.x == 0) cmax = 0;
     __syncthreads();
-    for (int k = 2; k <= np; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < np; i += blockDim.x) {
-                const int ij = i ^ j;
-                if (ij > i) {
-                    const unsigned long long a = key[i], b = key[ij];
-                    if ((a > b) == ((i & k) == 0)) {
-                        key[i] = b;
-                        key[ij] = a;
-                    }
-                }
-            }
-            __syncthreads();
+    int m = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, cost[t0 + i]);
+    m = wave_max_i32(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(&cmax, m);
+    __syncthreads();
+    const int top = max(cmax, 1);
+    auto key = [&](int c) { return 255 - (int)(((long long)c * 255) / top); };  // 0 = costliest
+    for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[key(cost[t0 + i])], 1);
+    __syncthreads();
+    if (threadIdx.x < 64) {  // exclusive scan of the 256 buckets by one wave, 4 per lane
+        const int l = threadIdx.x;
+        const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+        int incl = h0 + h1 + h2 + h3;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d, 64);
+            if (l >= d) incl += u;
         }
+        const int ex = incl - (h0 + h1 + h2 + h3);
+        hist[4 * l] = ex;
+        hist[4 * l + 1] = ex + h0;
+        hist[4 * l + 2] = ex + h0 + h1;
+        hist[4 * l + 3] = ex + h0 + h1 + h2;
     }
-    for (int r = threadIdx.x; r < per; r += blockDim.x)
-        order[r * kXcds + band] = r < n ? t0 + (int)(unsigned)(key[r] & 0xffffffffull) : -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int r = atomicAdd(&hist[key(cost[t0 + i])], 1);
+        order[r * kXcds + band] = t0 + i;
+    }
+    for (int r = n + threadIdx.x; r < per; r += blockDim.x) order[r * kXcds + band] = -1;
 }
 
 // One thread per splat: sum its used slots in slot order, apply the splat's
@@ -684,24 +728,6 @@ __global__ __launch_bounds__(256) void gather_kernel(int n, const int* __restric
     if (AW) accum_w[i] = w.y;
 }
 
-// Byte fill with 16-byte stores where possible.
-__global__ void clear_bytes_kernel(unsigned char* __restrict__ p, long long n)
-{
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long n16 = n >> 4;
-    if (i < n16) reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
-    const long long t = (n16 << 4) + i;
-    if (i < 16 && t < n) p[t] = 0;
-}
-
-hipError_t clear_bytes(unsigned char* p, long long n, hipStream_t st)
-{
-    if (n <= 0) return hipSuccess;
-    const long long threads = max(n >> 4, 16ll);
-    clear_bytes_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(p, n);
-    return hipGetLastError();
-}
-
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace layouts. Forward: splat records. Backward: splat records, then the
@@ -711,13 +737,13 @@ struct Layout {
     size_t recs, slots, used, cost, order, bytes;
 };
 
-Layout layout(long long n, long long n_slots, long long tiles)
+Layout layout(long long n_recs, long long n_slots, long long tiles)
 {
     Layout L{};
     L.recs = 0;
-    L.slots = align256(sizeof(SplatRec) * (size_t)(n > 0 ? n : 1));
+    L.slots = n_recs > 0 ? align256(sizeof(SplatRec) * (size_t)n_recs) : 0;
     L.used = L.slots + (n_slots > 0 ? align256(sizeof(float4) * 3 * (size_t)n_slots) : 0);
-    L.cost = L.used + (n_slots > 0 ? align256((size_t)n_slots + 4) : 0);
+    L.cost = L.used + (n_slots > 0 ? align256((size_t)n_slots + 16) : 0);
     L.order = L.cost + (tiles > 0 ? align256(sizeof(int) * (size_t)tiles) : 0);
     L.bytes = L.order + (tiles > 0 ? align256(sizeof(int) * (size_t)xcd_grid((int)tiles)) : 0);
     return L;
@@ -731,7 +757,7 @@ using namespace gs;
 extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
 {
     if (n < 0) return 0;
-    return layout(n, 0, 0).bytes;
+    return layout(n > 0 ? n : 1, 0, 0).bytes;
 }
 
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
@@ -747,7 +773,7 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
     GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
     GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
-    const Layout L = layout(n, 0, 0);
+    const Layout L = layout(n > 0 ? n : 1, 0, 0);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_fwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_fwd: workspace not 256-byte aligned");
@@ -767,7 +793,7 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
 extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height)
 {
     if (n < 0 || n_isect < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
-    return layout(n, n_isect, (long long)grid_x(width) * grid_y(height)).bytes;
+    return layout(n > 0 ? n : 1, n_isect, (long long)grid_x(width) * grid_y(height)).bytes;
 }
 
 extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
@@ -806,18 +832,17 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     int* cost = (int*)((char*)workspace + L.cost);
     int* order = (int*)((char*)workspace + L.order);
     if (n_isect > 0) {
-        GS_HIP(clear_bytes(used, (n_isect + 3) & ~3ll, st));  // whole 4-byte flag words
-        prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, radii,
-                                                     recs);
+        // flags cleared in whole 16-byte units (the region is padded)
+        const long long n16 = (n_isect + 15) >> 4;
+        const int cost_blocks = (tiles + 3) / 4, rec_blocks = (n + 255) / 256;
+        const long long blocks = (long long)cost_blocks + rec_blocks + (n16 + 255) / 256;
+        bwd_setup_kernel<<<(unsigned)blocks, 256, 0, st>>>(
+            width, height, GX, tiles, cost_blocks, (const int2*)tile_ranges, n_contrib, cost, n, rec_blocks,
+            (const float2*)means2d, conics, colors, opacities, radii, recs, (uint4*)used, n16);
         GS_HIP(hipGetLastError());
-        const int* ord = nullptr;
-        if ((tiles + kXcds - 1) / kXcds <= kMaxBand) {
-            tile_cost_kernel<<<tiles, 256, 0, st>>>(width, height, GX, (const int2*)tile_ranges, n_contrib, cost);
-            GS_HIP(hipGetLastError());
-            band_order_kernel<<<kXcds, 1024, 0, st>>>(tiles, cost, order);
-            GS_HIP(hipGetLastError());
-            ord = order;
-        }
+        band_order_kernel<<<kXcds, 1024, 0, st>>>(tiles, cost, order);
+        GS_HIP(hipGetLastError());
+        const int* ord = order;
         if (aw)
             bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
                 width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
