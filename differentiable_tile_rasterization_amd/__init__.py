@@ -151,13 +151,15 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
 
 def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, width: int, height: int, bins: Bins,
                      final_T, n_contrib, dL_dimage, accum_weight: bool = False, out=None, workspace=None,
-                     stream=None):
+                     stream=None, events=None):
     """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
     dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
     per-splat accumulated weight [n]. ``out`` may pass preallocated outputs
     (same dict keys) and ``workspace`` a uint8 device buffer of at least
     gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
-    allocation out of timed loops."""
+    allocation out of timed loops. ``events``: four torch.cuda.Event objects
+    (timing enabled, already recorded once) to be recorded at the call's
+    stage boundaries (gs_rasterize_bwd_timed)."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
     _need(conics, "conics", torch.float32, (n, 3))
@@ -185,12 +187,18 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
-    _lib.check(lib.gs_rasterize_bwd(
-        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
-        height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
-        _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
-        _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, wsp,
-        ws_bytes, _stream(stream)))
+    args = (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
+            height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
+            _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
+            _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, wsp,
+            ws_bytes, _stream(stream))
+    if events is None:
+        _lib.check(lib.gs_rasterize_bwd(*args))
+    else:
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event objects")
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
+        _lib.check(lib.gs_rasterize_bwd_timed(*args, handles))
     return out
 
 

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_CAPACITY", 3: "G
 # Every symbol include/gsraster.h declares.
 EXPORTS = ["gs_last_error", "gs_version", "gs_bin_tiles_workspace_size", "gs_bin_tiles",
            "gs_rasterize_fwd_workspace_size", "gs_rasterize_fwd", "gs_rasterize_bwd_workspace_size",
-           "gs_rasterize_bwd"]
+           "gs_rasterize_bwd", "gs_rasterize_bwd_timed"]
 
 _lib = None
 
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.gs_rasterize_bwd.argtypes = [i32, P, P, P, P, P, P, i32, i32, P, P, P, i64, P, P, P,
                                      P, P, P, P, P, u32, P, sz, P]
     lib.gs_rasterize_bwd.restype = ctypes.c_int
+    lib.gs_rasterize_bwd_timed.argtypes = lib.gs_rasterize_bwd.argtypes + [ctypes.POINTER(P)]
+    lib.gs_rasterize_bwd_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -40,15 +40,17 @@ namespace {
 struct SplatRec {
     float4 a;  // mean x, mean y, l11, l21 (scaled factor)
     float4 b;  // l22, log2(opacity), red, green
-    float4 c;  // blue, culling threshold on q', radius (int bits), 0
+    float4 c;  // blue, culling threshold on q', radius (int bits), first pair slot (int bits; backward)
 };
 
 constexpr float kQScale = 0.72134752044448170f;  // log2(e) / 2: q' = kQScale q
 
-// The record of splat i, from the caller's arrays (radii may be NULL).
+// The record of splat i, from the caller's arrays (radii and first_slot may
+// be NULL: the forward needs neither).
 __device__ __forceinline__ SplatRec make_rec(int i, const float2* __restrict__ means,
                                              const float* __restrict__ conics, const float* __restrict__ colors,
-                                             const float* __restrict__ opac, const int* __restrict__ radii)
+                                             const float* __restrict__ opac, const int* __restrict__ radii,
+                                             const int* __restrict__ first_slot = nullptr)
 {
     const float2 m = means[i];
     const float a = conics[3 * i + 0], b = conics[3 * i + 1], c = conics[3 * i + 2];
@@ -57,7 +59,8 @@ __device__ __forceinline__ SplatRec make_rec(int i, const float2* __restrict__ m
     SplatRec r;
     r.a = make_float4(k.mx, k.my, k.l11, k.l21);
     r.b = make_float4(k.l22, k.lo, colors[3 * i + 0], colors[3 * i + 1]);
-    r.c = make_float4(colors[3 * i + 2], kQScale * cull_tau(o), __int_as_float(radii ? radii[i] : 0), 0.0f);
+    r.c = make_float4(colors[3 * i + 2], kQScale * cull_tau(o), __int_as_float(radii ? radii[i] : 0),
+                      __int_as_float(first_slot ? first_slot[i] : 0));
     return r;
 }
 
@@ -570,7 +573,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
                 int tx0, tx1, ty0, ty1;
                 tile_rect(r.a.x, r.a.y, radius, GX, GY, tx0, tx1, ty0, ty1);
                 const int tx = tile % GX, ty = tile / GX;
-                const long long slot = (long long)splat_offsets[id] + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
+                // the splat's first slot travels in its record
+                const long long slot =
+                    (long long)__float_as_int(r.c.w) + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
                 // the tile lies in the splat's rectangle whenever the inputs come
                 // from one binning; anything else is dropped, never written wild
                 if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && slot >= 0 && slot < n_slots) {
@@ -600,7 +605,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
 // Setup of a backward call, one launch. Blocks [0, cost_blocks) give one
 // wave per tile its largest n_contrib, clamped to its list length (the walk
 // length); the next rec_blocks pack one splat record per thread (as
-// prep_kernel); the rest clear the slot flags with 16-byte stores.
+// prep_kernel, and with each splat's first pair slot, so that the walk's
+// flush needs no scattered read of splat_offsets); the rest clear the slot
+// flags with 16-byte stores.
 __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, int tiles, int cost_blocks,
                                                         const int2* __restrict__ ranges,
                                                         const int* __restrict__ n_contrib, int* __restrict__ cost,
@@ -608,6 +615,7 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, in
                                                         const float* __restrict__ conics,
                                                         const float* __restrict__ colors,
                                                         const float* __restrict__ opac, const int* __restrict__ radii,
+                                                        const int* __restrict__ splat_offsets,
                                                         SplatRec* __restrict__ recs, uint4* __restrict__ flags16,
                                                         long long n16)
 {
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, in
     }
     if (b < cost_blocks + rec_blocks) {
         const int i = (b - cost_blocks) * 256 + threadIdx.x;
-        if (i < n) recs[i] = make_rec(i, means, conics, colors, opac, radii);
+        if (i < n) recs[i] = make_rec(i, means, conics, colors, opac, radii, splat_offsets);
         return;
     }
     const long long i = (long long)(b - cost_blocks - rec_blocks) * 256 + threadIdx.x;
@@ -907,16 +915,20 @@ extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, in
     return layout(n > 0 ? n : 1, n_isect, (long long)grid_x(width) * grid_y(height)).bytes;
 }
 
-extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
-                                      const float* opacities, const int32_t* radii, const float* background,
-                                      int32_t width, int32_t height, const int32_t* tile_ranges,
-                                      const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
-                                      const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
-                                      float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
-                                      float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
-                                      size_t workspace_bytes, gs_stream_t stream_)
+namespace {
+gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const float* colors,
+                   const float* opacities, const int32_t* radii, const float* background, int32_t width,
+                   int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                   const int32_t* splat_offsets, int64_t n_isect, const float* final_T, const int32_t* n_contrib,
+                   const float* dL_dimage, float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                   float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
+                   size_t workspace_bytes, gs_stream_t stream_, const gs_event_t* events)
 {
     hipStream_t st = (hipStream_t)stream_;
+    // stage-boundary events of gs_rasterize_bwd_timed (none for gs_rasterize_bwd)
+    auto mark = [&](int k) -> hipError_t {
+        return (events && events[k]) ? hipEventRecord((hipEvent_t)events[k], st) : hipSuccess;
+    };
     GS_CHECK_ARG(n >= 0, "gs_rasterize_bwd: n = %d < 0", n);
     GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "gs_rasterize_bwd: n_isect = %lld out of range",
                  (long long)n_isect);
@@ -936,7 +948,13 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_bwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_bwd: workspace not 256-byte aligned");
-    if (n == 0) return GS_OK;
+    GS_HIP(mark(0));
+    if (n == 0) {
+        GS_HIP(mark(1));
+        GS_HIP(mark(2));
+        GS_HIP(mark(3));
+        return GS_OK;
+    }
     SplatRec* recs = (SplatRec*)((char*)workspace + L.recs);
     float4* slots = n_isect ? (float4*)((char*)workspace + L.slots) : nullptr;
     unsigned char* used = n_isect ? (unsigned char*)workspace + L.used : nullptr;
@@ -949,10 +967,11 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
         const long long blocks = (long long)cost_blocks + rec_blocks + (n16 + 255) / 256;
         bwd_setup_kernel<<<(unsigned)blocks, 256, 0, st>>>(
             width, height, GX, tiles, cost_blocks, (const int2*)tile_ranges, n_contrib, cost, n, rec_blocks,
-            (const float2*)means2d, conics, colors, opacities, radii, recs, (uint4*)used, n16);
+            (const float2*)means2d, conics, colors, opacities, radii, splat_offsets, recs, (uint4*)used, n16);
         GS_HIP(hipGetLastError());
         band_order_kernel<<<kXcds, 1024, 0, st>>>(tiles, cost, order);
         GS_HIP(hipGetLastError());
+        GS_HIP(mark(1));
         const int* ord = order;
         if (aw)
             bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
@@ -963,6 +982,10 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
                 width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
                 background, final_T, n_contrib, dL_dimage, ord, slots, used);
         GS_HIP(hipGetLastError());
+        GS_HIP(mark(2));
+    } else {
+        GS_HIP(mark(1));
+        GS_HIP(mark(2));
     }
     const uint4* flags16 = reinterpret_cast<const uint4*>(used);  // padded to whole 16-byte units
     const unsigned* words = reinterpret_cast<const unsigned*>(used);
@@ -990,5 +1013,37 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
                                                        nullptr);
     }
     GS_HIP(hipGetLastError());
+    GS_HIP(mark(3));
     return GS_OK;
+}
+}  // namespace
+
+extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                      const float* opacities, const int32_t* radii, const float* background,
+                                      int32_t width, int32_t height, const int32_t* tile_ranges,
+                                      const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
+                                      const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                                      float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                      float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, gs_stream_t stream)
+{
+    return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
+                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* conics,
+                                            const float* colors, const float* opacities, const int32_t* radii,
+                                            const float* background, int32_t width, int32_t height,
+                                            const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                            const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                            const int32_t* n_contrib, const float* dL_dimage, float* dL_dmeans2d,
+                                            float* dL_dconics, float* dL_dcolors, float* dL_dopacities,
+                                            float* accum_weight, uint32_t flags, void* workspace,
+                                            size_t workspace_bytes, gs_stream_t stream, const gs_event_t events[4])
+{
+    GS_CHECK_ARG(events, "gs_rasterize_bwd_timed: events is NULL");
+    return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
+                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, events);
 }

@@ -8,9 +8,10 @@
 total time). `pmc` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) into bytes per launch, scaled by what the same counters read for the
 measurement library's 1 GiB float4 copy kernel (1 GiB read, 1 GiB written per
-launch), and writes the JSON the benchmark reads for its `traffic` field (it
-records the hash of the kernel sources it was taken on; the benchmark ignores
-it once the sources change).
+launch), and writes the JSON the benchmark reads for its `traffic` field: the
+bytes of the reverse-walk kernel per launch (it records the hash of the
+kernel sources it was taken on; the benchmark ignores it once the sources
+change).
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ import sys
 
 COPY_BYTES = 1 << 30          # the copy kernel moves 1 GiB in and 1 GiB out per launch
 COPY_NAME = "copy_kernel"
-CALL_KERNELS = ["clear_bytes_kernel", "prep_kernel", "bwd_kernel", "gather_kernel"]
+CALL_KERNELS = ["bwd_setup_kernel", "band_order_kernel", "bwd_kernel", "gather_kernel", "gather_splat_kernel"]
+DOMINANT = "bwd_kernel<"      # the reverse walk: the kernel the roofline is taken on
 
 
 def _short(name: str) -> str:
@@ -65,11 +67,13 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
         fb = avg(fe[k]) * 1024.0 * f_scale if k in fe else 0.0
         wb = avg(wr[k]) * 1024.0 * w_scale if k in wr else 0.0
         per[k] = {"fetch_bytes": fb, "write_bytes": wb}
-    call = [k for k in per if any(k.startswith(c) or c in k for c in CALL_KERNELS)]
+    call = [k for k in per if any(k.startswith(c) for c in CALL_KERNELS)]
     total = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in call)
+    dom = [k for k in per if k.startswith(DOMINANT)]
+    dom_bytes = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in dom)
     rec = {"config": config, "source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
-           "call_kernels": call, "hbm_bytes_per_launch": total, "per_kernel": per,
-           "commands": [cmd_fetch, cmd_write]}
+           "dominant_kernel": dom, "hbm_bytes_per_launch": dom_bytes, "call_kernels": call,
+           "call_bytes_per_launch": total, "per_kernel": per, "commands": [cmd_fetch, cmd_write]}
     json.dump(rec, open(out_json, "w"), indent=1)
     lines = ["# HBM traffic (FETCH_SIZE / WRITE_SIZE), " + config, "",
              "Commands (repo root, on the GPU box):", "", "    " + cmd_fetch, "    " + cmd_write, "",
@@ -79,7 +83,8 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
              "| kernel | fetched MB / launch | written MB / launch |", "|---|---:|---:|"]
     for k, v in sorted(per.items(), key=lambda kv: -(kv[1]["fetch_bytes"] + kv[1]["write_bytes"])):
         lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.1f} |")
-    lines += ["", f"One gs_rasterize_bwd call ({', '.join(call)}): {total / 1e6:.1f} MB per launch "
+    lines += ["", f"The reverse walk ({', '.join(dom)}): {dom_bytes / 1e6:.1f} MB per launch. "
+                  f"One gs_rasterize_bwd call ({', '.join(call)}): {total / 1e6:.1f} MB "
                   f"(source hash {rec['source_hash']})."]
     open(out_md, "w").write("\n".join(lines) + "\n")
 

@@ -70,6 +70,7 @@ extern "C" {
 
 /* hipStream_t without pulling in the HIP headers: an opaque stream handle. */
 typedef struct ihipStream_t* gs_stream_t;
+typedef struct ihipEvent_t* gs_event_t;
 
 typedef enum {
     GS_OK = 0,
@@ -222,6 +223,27 @@ gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                            float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                            size_t workspace_bytes, gs_stream_t stream);
+
+/*
+ * gs_rasterize_bwd with its stages timed: the same work, arguments and errors,
+ * and in addition a HIP event (created by the caller) recorded on `stream`
+ * at each stage boundary, for measurement tools:
+ *   events[0]  before the setup (splat records, per-tile walk lengths and the
+ *              tiles' launch order, cleared slot flags)
+ *   events[1]  before the reverse walk (the per-tile backward kernel)
+ *   events[2]  after the reverse walk, before the per-splat gather
+ *   events[3]  after the gather
+ * NULL entries are skipped. With n == 0 or n_isect == 0 the walk is not
+ * launched and events[1] and events[2] are recorded back to back.
+ */
+gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                 const float* opacities, const int32_t* radii, const float* background,
+                                 int32_t width, int32_t height, const int32_t* tile_ranges,
+                                 const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
+                                 const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                                 float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                 float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
+                                 size_t workspace_bytes, gs_stream_t stream, const gs_event_t events[4]);
 
 #ifdef __cplusplus
 }

@@ -88,6 +88,20 @@ def test_bwd_rejects_bad_arguments():
     assert b"aligned" in lib.gs_last_error()
 
 
+def test_bwd_timed_rejects_bad_arguments():
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+
+    def call(events, n=-5):
+        return lib.gs_rasterize_bwd_timed(n, p, p, p, p, p, None, 8, 8, p, p, p, 0, p, p, p, p, p, p, p, None, 0,
+                                          None, 0, None, events)
+    assert call(None) == _lib.GS_ERR_INVALID_ARG
+    assert b"events" in lib.gs_last_error()
+    # the plain argument checks come first, before any event is recorded
+    assert call((ctypes.c_void_p * 4)(1, 1, 1, 1)) == _lib.GS_ERR_INVALID_ARG
+    assert b"n = -5" in lib.gs_last_error()
+
+
 def test_bin_rejects_bad_arguments():
     lib = _lib.load()
     p = ctypes.c_void_p(256)

@@ -240,3 +240,26 @@ def test_bench_sampled_tiles_at_full_size():
     sel = np.isin((ys // 16) * GX + xs // 16, tiles) & ~fo["ambiguous"]
     np.testing.assert_allclose(img.cpu().numpy()[sel], fo["image"][sel], atol=IMG_TOL, rtol=0)
     np.testing.assert_array_equal(nc.cpu().numpy()[sel], fo["n_contrib"][sel])
+
+
+def test_timed_entry_point_matches_and_orders_its_events():
+    sc = scenes.make_scene("early", 0)
+    bins = gpu_bins(sc)
+    _, T, nc = gpu_fwd(sc, bins)
+    plain = gpu_bwd(sc, bins, T, nc, sc.dL_dimage)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record(stream)   # creates the underlying HIP events
+    timed = gsr.gs_rasterize_bwd(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                 _dev(sc.radii), _dev(sc.background), sc.width, sc.height, bins, T, nc,
+                                 _dev(sc.dL_dimage), events=evs)
+    torch.cuda.synchronize()
+    for k in plain:
+        # same kernels, same inputs: the same result up to the order of the
+        # few workgroup-local float additions
+        ref = plain[k].cpu().numpy()
+        np.testing.assert_allclose(timed[k].cpu().numpy(), ref, rtol=0, atol=1e-6 * max(1e-30, np.abs(ref).max()))
+    spans = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    _say("stage ms", spans)
+    assert all(x >= 0 for x in spans) and spans[1] > 0
