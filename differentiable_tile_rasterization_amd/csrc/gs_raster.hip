@@ -28,6 +28,7 @@
 // of section 机制拆解 of the Spirula Studio page, where optional feature arrays
 // sized regardless of the switch halved occupancy).
 #include <cstddef>
+#include <type_traits>
 
 #include "gs_common.hpp"
 
@@ -465,6 +466,13 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         *reinterpret_cast<float2*>(S[threadIdx.x].part + 8) = make_float2(0.0f, 0.0f);
         bool hit[kHalves];
         half_hits(r, ox, oy, k, hend, hit);
+        // Can any entry of the batch reach the 0.99 clamp? alpha_raw =
+        // exp2(log2 o - q) with q >= 0 never exceeds exp2(log2 o) (the same
+        // monotone v_exp_f32), so an entry with exp2(log2 o) clearly below
+        // 0.99 never clamps. Most batches have none, and their walk skips the
+        // clamp's three instructions per step.
+        const bool may_clamp = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
+        const bool clamp_batch = __syncthreads_or(may_clamp) != 0;
         build_half_lists(hit, list, list_cnt);
         // this half's list length, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
@@ -485,11 +493,12 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         // Two register sets take turns (the loop is unrolled by two), so the
         // read-ahead costs no register copies.
         auto rec_at = [&](int o) -> const BwdSlot& { return *reinterpret_cast<const BwdSlot*>(Sb + o); };
-        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur) {
+        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur, auto clamp_tag) {
+            constexpr bool kClamp = decltype(clamp_tag)::value;
             const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
             float dx, dy;
             const float ar = alpha_raw(kf, px, py, dx, dy);
-            const float al = fminf(kAlphaMax, ar);
+            const float al = kClamp ? fminf(kAlphaMax, ar) : ar;
             const bool contrib = (cur < ncb_off) && (al >= kAlphaMin);
             // colour . gradient ahead of the test, so that the colour loads
             // issue with the rest of the record
@@ -507,7 +516,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             Bg = __builtin_fmaf(ae, eg, Bg);
             T = Ti;
             const float w = ae * Ti;
-            const float s = (ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
+            const float s = (!kClamp || ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
             // all values first, then the folds (no value is read after its
             // register has been swapped)
             const float sdx = s * dx, sdy = s * dy;
@@ -538,25 +547,31 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             if (bank_lead) atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
             if (row_lead) atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
         };
-        int o0 = L[0], o1 = L[1], on0 = L[2];
-        float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
-        float C0 = rec_at(o0).c;
-        for (int it = 0; it < steps; it += 2) {
-            // set 1 <- position it + 1; list position it + 3
-            const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
-            const float C1 = rec_at(o1).c;
-            const int on1 = L[it + 3];
-            step(A0, B0, C0, o0);
-            if (it + 1 >= steps) break;
-            // set 0 <- position it + 2; list position it + 4
-            o0 = on0;
-            A0 = rec_at(o0).a;
-            B0 = rec_at(o0).b;
-            C0 = rec_at(o0).c;
-            on0 = L[it + 4];
-            step(A1, B1, C1, o1);
-            o1 = on1;
-        }
+        auto walk = [&](auto clamp_tag) {
+            int o0 = L[0], o1 = L[1], on0 = L[2];
+            float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+            float C0 = rec_at(o0).c;
+            for (int it = 0; it < steps; it += 2) {
+                // set 1 <- position it + 1; list position it + 3
+                const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+                const float C1 = rec_at(o1).c;
+                const int on1 = L[it + 3];
+                step(A0, B0, C0, o0, clamp_tag);
+                if (it + 1 >= steps) break;
+                // set 0 <- position it + 2; list position it + 4
+                o0 = on0;
+                A0 = rec_at(o0).a;
+                B0 = rec_at(o0).b;
+                C0 = rec_at(o0).c;
+                on0 = L[it + 4];
+                step(A1, B1, C1, o1, clamp_tag);
+                o1 = on1;
+            }
+        };
+        if (clamp_batch)
+            walk(std::true_type{});
+        else
+            walk(std::false_type{});
         __syncthreads();
 
         // Flush: thread t owns the entry it staged.
