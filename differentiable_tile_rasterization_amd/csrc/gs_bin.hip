@@ -1,19 +1,26 @@
-// gs_bin.hip -- gs_bin_tiles: tile binning, stable radix sort, tile ranges.
+// gs_bin.hip -- gs_bin_tiles: tile binning, stable radix sorts, tile ranges.
 //
 // Stages (the binning / sort / range kernels of the 3dgs-rs pipeline listed in
 // the timing table of "Phase 5 step 30b — kernel-by-kernel timing", section
 // 計測結果: emit_pairs, radix_hist, radix_scatter, extract_offsets):
 //   1. count   one thread per splat: float32 tile rectangle, number of tiles
-//   2. scan    exclusive prefix sum of the counts (device-wide, 64-bit)
+//   2. scan    exclusive prefix sum of the counts in splat order (device-wide,
+//              64-bit): each splat's first pair slot, splat_offsets
 //   3. host    read the total back (the call's only synchronisation)
-//   4. emit    one thread per splat writes (tile << 32 | depth bits, id) for its
-//              tiles, row-major, at its scan offset: the pair order is
-//              deterministic (no atomic counter)
-//   5. sort    stable LSD radix sort, 8-bit digits, over only the key bits that
-//              can be non-zero: 31 depth bits (depth > 0, so the sign bit is 0)
-//              and ceil(log2(tiles)) tile bits. Stability plus emission in
-//              splat order makes equal depths come out by ascending splat id.
-//   6. ranges  [start, end) per tile from the boundaries of the sorted keys
+//   4. depth   stable LSD radix sort of the splats by the bit pattern of their
+//              depth (32 bits, 8-bit digits), splat ids starting in id order
+//   5. emit    the splats' tile rectangles (stored by the count pass) and
+//              counts gathered into depth order and scanned; the splat of
+//              depth rank k writes its tiles, row-major, at that offset, as
+//              (32-bit tile id, splat id)
+//   6. tiles   stable LSD radix sort of the pairs by tile id over only the
+//              ceil(log2(tiles)) bits it can have (2 passes of 8-bit digits up
+//              to 65536 tiles). Stability keeps each tile's pairs in depth
+//              order, equal depths by ascending splat id.
+//   7. ranges  [start, end) per tile from the boundaries of the sorted keys
+// Sorting the splats by depth first moves the 32 depth bits off the pairs:
+// the passes over all pairs fall from six (tile and depth bits together) to
+// two, over 8-byte instead of 12-byte elements.
 #include "gs_common.hpp"
 
 namespace gs {
@@ -37,10 +44,14 @@ __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float dept
     return live && tx1 > tx0 && ty1 > ty0;
 }
 
+// counts[i] = number of tiles of splat i; rects[i] = its tile rectangle
+// (tx0, ty0, tx1, ty1), empty for a culled splat. A grid has at most 2048
+// tiles per side, so 16 bits per bound suffice.
 __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
                                                     const int* __restrict__ radii,
                                                     const float* __restrict__ depths, int GX, int GY,
-                                                    unsigned long long* __restrict__ counts)
+                                                    unsigned long long* __restrict__ counts,
+                                                    ushort4* __restrict__ rects)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -48,6 +59,9 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
     counts[i] = live ? (unsigned long long)(tx1 - tx0) * (unsigned long long)(ty1 - ty0) : 0ull;
+    rects[i] = live ? make_ushort4((unsigned short)tx0, (unsigned short)ty0, (unsigned short)tx1,
+                                   (unsigned short)ty1)
+                    : make_ushort4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -156,29 +170,64 @@ hipError_t exclusive_scan(const TI* in, TO* out, long long n, unsigned long long
 }
 
 // ---------------------------------------------------------------------------
-// Emit: splat i writes its tiles, row-major, at offsets[i].
+// Depth order and emission.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void emit_kernel(int n, const float2* __restrict__ means,
-                                                   const int* __restrict__ radii,
-                                                   const float* __restrict__ depths, int GX, int GY,
-                                                   const unsigned long long* __restrict__ offsets,
-                                                   unsigned long long* __restrict__ keys,
-                                                   int* __restrict__ vals)
+// keys = depth bit patterns, vals = splat ids (the depth sort's input).
+__global__ __launch_bounds__(256) void depth_keys_kernel(int n, const float* __restrict__ depths,
+                                                         unsigned* __restrict__ keys, int* __restrict__ vals)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const float2 m = means[i];
-    const float d = depths[i];
-    int tx0, tx1, ty0, ty1;
-    if (!splat_rect(m.x, m.y, radii[i], d, GX, GY, tx0, tx1, ty0, ty1)) return;
-    const unsigned long long dbits = (unsigned long long)__float_as_uint(d);
-    unsigned long long o = offsets[i];
-    for (int ty = ty0; ty < ty1; ++ty)
-        for (int tx = tx0; tx < tx1; ++tx) {
-            keys[o] = ((unsigned long long)(ty * GX + tx) << 32) | dbits;
-            vals[o] = i;
-            ++o;
+    keys[i] = __float_as_uint(depths[i]);
+    vals[i] = i;
+}
+
+// Depth rank k: the rectangle and tile count of its splat.
+__global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __restrict__ by_depth,
+                                                           const ushort4* __restrict__ rects,
+                                                           ushort4* __restrict__ rect_sorted,
+                                                           unsigned long long* __restrict__ cnt_sorted)
+{
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const ushort4 rc = rects[by_depth[k]];
+    rect_sorted[k] = rc;
+    cnt_sorted[k] = (unsigned long long)(rc.z - rc.x) * (unsigned long long)(rc.w - rc.y);
+}
+
+// Emission: one wave per 64 consecutive depth ranks. Their pairs are
+// contiguous, [emit_off[k0], emit_off[k0 + 64]), and the wave writes them
+// together, one pair per lane per step (coalesced), the pair's splat found by
+// binary search in the wave's copy of the offsets: the splat of depth rank k
+// writes its tiles, row-major, from emit_off[k], as (tile id, splat id).
+__global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, const int* __restrict__ by_depth,
+                                                     const ushort4* __restrict__ rect_sorted,
+                                                     const unsigned long long* __restrict__ emit_off, int GX,
+                                                     unsigned* __restrict__ keys, int* __restrict__ vals)
+{
+    __shared__ unsigned long long off[kWave + 1];
+    __shared__ ushort4 rc[kWave];
+    __shared__ int sid[kWave];
+    const int lane = threadIdx.x;
+    const int k0 = blockIdx.x * kWave, k = k0 + lane;
+    off[lane] = k < n ? emit_off[k] : (unsigned long long)n_pairs;
+    if (lane == 0) off[kWave] = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned long long)n_pairs;
+    rc[lane] = k < n ? rect_sorted[k] : make_ushort4(0, 0, 0, 0);
+    sid[lane] = k < n ? by_depth[k] : 0;
+    __syncthreads();
+    const unsigned long long p0 = off[0], p1 = off[kWave];
+    for (unsigned long long p = p0 + lane; p < p1; p += kWave) {
+        int lo = 0, hi = kWave - 1;  // the last local rank s with off[s] <= p
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= p) lo = mid; else hi = mid - 1;
         }
+        const ushort4 b = rc[lo];
+        const unsigned rel = (unsigned)(p - off[lo]), wdt = (unsigned)(b.z - b.x);
+        const unsigned row = rel / wdt;
+        keys[p] = (unsigned)((b.y + row) * GX + b.x + (rel - row * wdt));
+        vals[p] = sid[lo];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -186,9 +235,9 @@ __global__ __launch_bounds__(256) void emit_kernel(int n, const float2* __restri
 // hist: per workgroup digit counts, stored digit-major (digit * nwg + wg) so
 // that one exclusive scan yields every workgroup's output offset per digit.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const unsigned long long* __restrict__ keys,
-                                                                  long long n, int shift, int nwg,
-                                                                  unsigned* __restrict__ hist)
+template <typename K>
+__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __restrict__ keys, long long n,
+                                                                  int shift, int nwg, unsigned* __restrict__ hist)
 {
     __shared__ unsigned h[4][kRadix];
     for (int k = threadIdx.x; k < 4 * kRadix; k += kSortThreads) (&h[0][0])[k] = 0;
@@ -207,36 +256,73 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const unsigned
     hist[(long long)d * nwg + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
 }
 
-__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
-    const unsigned long long* __restrict__ keys_in, const int* __restrict__ vals_in, long long n, int shift,
-    int nwg, const unsigned* __restrict__ offs, unsigned long long* __restrict__ keys_out,
-    int* __restrict__ vals_out)
+// Scatter of one pass. The workgroup's keys are first ranked stably by digit
+// (per round: 8 ballots give each lane its rank among the wave's lanes with
+// the same digit; waves and rounds are ordered by running counts) and placed
+// in LDS in digit order; the tile is then written out from LDS, so that
+// consecutive threads store consecutive addresses inside each digit's run
+// instead of one key at a time into up to 256 different runs.
+template <typename K>
+__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __restrict__ keys_in,
+                                                                     const int* __restrict__ vals_in, long long n,
+                                                                     int shift, int nwg,
+                                                                     const unsigned* __restrict__ offs,
+                                                                     K* __restrict__ keys_out,
+                                                                     int* __restrict__ vals_out)
 {
     __shared__ unsigned wave_cnt[4][kRadix];  // keys of digit d in wave w, this round
-    __shared__ unsigned wave_off[4][kRadix];  // where wave w's keys of digit d start
-    __shared__ unsigned running[kRadix];      // keys of digit d placed by earlier rounds
+    __shared__ unsigned wave_off[4][kRadix];  // where wave w's keys of digit d go (block-local)
+    __shared__ unsigned running[kRadix];      // block-local position of digit d's next key
+    __shared__ unsigned local_start[kRadix];  // block-local start of digit d
     __shared__ unsigned global_off[kRadix];
+    __shared__ K lkey[kSortTile];
+    __shared__ int lval[kSortTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    {
-        const int d = threadIdx.x;
-        running[d] = 0;
-        global_off[d] = offs[(long long)d * nwg + blockIdx.x];
-        for (int k = 0; k < 4; ++k) wave_cnt[k][d] = 0;
+    const long long base = (long long)blockIdx.x * kSortTile;
+    const int cnt = (int)(n - base < (long long)kSortTile ? n - base : (long long)kSortTile);
+    const int td = threadIdx.x;  // kSortThreads == kRadix: thread td looks after digit td
+    K key[kSortRounds];
+    int val[kSortRounds];
+    local_start[td] = 0;
+    for (int k = 0; k < 4; ++k) wave_cnt[k][td] = 0;
+    global_off[td] = offs[(long long)td * nwg + blockIdx.x];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int li = r * kSortThreads + threadIdx.x;
+        key[r] = 0;
+        val[r] = 0;
+        if (li < cnt) {
+            key[r] = keys_in[base + li];
+            val[r] = vals_in[base + li];
+            atomicAdd(&local_start[(unsigned)(key[r] >> shift) & (kRadix - 1)], 1u);
+        }
     }
     __syncthreads();
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    const long long base = (long long)blockIdx.x * kSortTile;
-    for (int r = 0; r < kSortRounds; ++r) {
-        const long long idx = base + (long long)r * kSortThreads + threadIdx.x;
-        const bool valid = idx < n;
-        unsigned long long key = 0;
-        int val = 0;
-        unsigned d = 0;
-        if (valid) {
-            key = keys_in[idx];
-            val = vals_in[idx];
-            d = (unsigned)(key >> shift) & (kRadix - 1);
+    if (threadIdx.x < kWave) {  // exclusive scan of the 256 digit counts, 4 per lane
+        const int l = threadIdx.x;
+        const unsigned h0 = local_start[4 * l], h1 = local_start[4 * l + 1], h2 = local_start[4 * l + 2],
+                       h3 = local_start[4 * l + 3];
+        unsigned incl = h0 + h1 + h2 + h3;
+        for (int dl = 1; dl < kWave; dl <<= 1) {
+            const unsigned u = __shfl_up(incl, dl, kWave);
+            if (l >= dl) incl += u;
         }
+        const unsigned ex = incl - (h0 + h1 + h2 + h3);
+        local_start[4 * l] = ex;
+        local_start[4 * l + 1] = ex + h0;
+        local_start[4 * l + 2] = ex + h0 + h1;
+        local_start[4 * l + 3] = ex + h0 + h1 + h2;
+    }
+    __syncthreads();
+    running[td] = local_start[td];
+    __syncthreads();
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int li = r * kSortThreads + threadIdx.x;
+        const bool valid = li < cnt;
+        const unsigned d = valid ? (unsigned)(key[r] >> shift) & (kRadix - 1) : 0u;
         // lanes of this wave holding the same digit (8 ballots)
         unsigned long long peers = __ballot(valid);
 #pragma unroll
@@ -249,33 +335,44 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
         if (valid && rank == 0) wave_cnt[w][d] = (unsigned)__popcll(peers);
         __syncthreads();
         {
-            const int dd = threadIdx.x;
-            unsigned run = running[dd];
+            unsigned run = running[td];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                wave_off[k][dd] = run;
-                run += wave_cnt[k][dd];
-                wave_cnt[k][dd] = 0;
+                wave_off[k][td] = run;
+                run += wave_cnt[k][td];
+                wave_cnt[k][td] = 0;
             }
-            running[dd] = run;
+            running[td] = run;
         }
         __syncthreads();
         if (valid) {
-            const unsigned pos = global_off[d] + wave_off[w][d] + rank;
-            keys_out[pos] = key;
-            vals_out[pos] = val;
+            const unsigned lp = wave_off[w][d] + rank;
+            lkey[lp] = key[r];
+            lval[lp] = val[r];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int lp = r * kSortThreads + threadIdx.x;
+        if (lp < cnt) {
+            const K k = lkey[lp];
+            const unsigned d = (unsigned)(k >> shift) & (kRadix - 1);
+            const unsigned pos = global_off[d] + ((unsigned)lp - local_start[d]);
+            keys_out[pos] = k;
+            vals_out[pos] = lval[lp];
         }
     }
 }
 
-__global__ __launch_bounds__(256) void ranges_kernel(const unsigned long long* __restrict__ keys, long long n,
+__global__ __launch_bounds__(256) void ranges_kernel(const unsigned* __restrict__ keys, long long n,
                                                      int2* __restrict__ ranges)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const int t = (int)(keys[i] >> 32);
-    if (i == 0 || (int)(keys[i - 1] >> 32) != t) ranges[t].x = (int)i;
-    if (i == n - 1 || (int)(keys[i + 1] >> 32) != t) ranges[t].y = (int)(i + 1);
+    const int t = (int)keys[i];
+    if (i == 0 || (int)keys[i - 1] != t) ranges[t].x = (int)i;
+    if (i == n - 1 || (int)keys[i + 1] != t) ranges[t].y = (int)(i + 1);
 }
 
 // splat_offsets[i] = first slot of splat i's (splat, tile) pairs, [n] = total.
@@ -291,26 +388,52 @@ __global__ __launch_bounds__(256) void offsets_kernel(int n, const unsigned long
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BinLayout {
-    size_t counts, offsets, part, total, keys_a, keys_b, vals_tmp, hist, bytes;
+    size_t counts, rects, offsets, part, total, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted, cnt_sorted,
+        emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
 };
 
 BinLayout bin_layout(long long n, long long cap)
 {
     BinLayout L{};
     size_t o = 0;
-    const long long nwg_sort = (cap + kSortTile - 1) / kSortTile;
+    const long long nmax = n > cap ? n : cap;
+    const long long nwg_sort = (nmax + kSortTile - 1) / kSortTile;
     const long long scan_items = n > (long long)kRadix * nwg_sort ? n : (long long)kRadix * nwg_sort;
     const long long nparts = (scan_items + kScanTile - 1) / kScanTile + 1;
-    L.counts = o;   o += align256(sizeof(unsigned long long) * (size_t)(n > 0 ? n : 1));
-    L.offsets = o;  o += align256(sizeof(unsigned long long) * (size_t)(n > 0 ? n : 1));
-    L.part = o;     o += align256(sizeof(unsigned long long) * (size_t)nparts);
-    L.total = o;    o += align256(sizeof(unsigned long long));
-    L.keys_a = o;   o += align256(sizeof(unsigned long long) * (size_t)(cap > 0 ? cap : 1));
-    L.keys_b = o;   o += align256(sizeof(unsigned long long) * (size_t)(cap > 0 ? cap : 1));
-    L.vals_tmp = o; o += align256(sizeof(int) * (size_t)(cap > 0 ? cap : 1));
-    L.hist = o;     o += align256(sizeof(unsigned) * (size_t)kRadix * (size_t)(nwg_sort > 0 ? nwg_sort : 1));
+    const size_t n1 = (size_t)(n > 0 ? n : 1), c1 = (size_t)(cap > 0 ? cap : 1);
+    L.counts = o;     o += align256(sizeof(unsigned long long) * n1);
+    L.rects = o;      o += align256(sizeof(ushort4) * n1);
+    L.offsets = o;    o += align256(sizeof(unsigned long long) * n1);
+    L.part = o;       o += align256(sizeof(unsigned long long) * (size_t)nparts);
+    L.total = o;      o += align256(sizeof(unsigned long long));
+    L.dkeys_a = o;    o += align256(sizeof(unsigned) * n1);
+    L.dkeys_b = o;    o += align256(sizeof(unsigned) * n1);
+    L.dvals_a = o;    o += align256(sizeof(int) * n1);
+    L.dvals_b = o;    o += align256(sizeof(int) * n1);
+    L.rect_sorted = o; o += align256(sizeof(ushort4) * n1);
+    L.cnt_sorted = o; o += align256(sizeof(unsigned long long) * n1);
+    L.emit_off = o;   o += align256(sizeof(unsigned long long) * n1);
+    L.keys_a = o;     o += align256(sizeof(unsigned) * c1);
+    L.keys_b = o;     o += align256(sizeof(unsigned) * c1);
+    L.vals_tmp = o;   o += align256(sizeof(int) * c1);
+    L.hist = o;       o += align256(sizeof(unsigned) * (size_t)kRadix * (size_t)(nwg_sort > 0 ? nwg_sort : 1));
     L.bytes = o;
     return L;
+}
+
+// One stable LSD pass over 8-bit digit `shift` of keys_in -> keys_out.
+template <typename K>
+hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, unsigned* hist,
+                      unsigned long long* part, unsigned long long* total, hipStream_t st)
+{
+    const int nwg = (int)((cnt + kSortTile - 1) / kSortTile);
+    radix_hist_kernel<K><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = exclusive_scan<unsigned, unsigned>(hist, hist, (long long)kRadix * nwg, part, total, st);
+    if (e != hipSuccess) return e;
+    radix_scatter_kernel<K><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
+    return hipGetLastError();
 }
 
 int bits_for(long long v)  // smallest b with (1 << b) > v - 1, i.e. enough bits for values 0..v-1
@@ -360,10 +483,12 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     auto* offsets = (unsigned long long*)(ws + L.offsets);
     auto* part = (unsigned long long*)(ws + L.part);
     auto* total = (unsigned long long*)(ws + L.total);
+    auto* rects = (ushort4*)(ws + L.rects);
 
     unsigned long long h_total = 0;
     if (n > 0) {
-        count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, counts);
+        count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, counts,
+                                                      rects);
         GS_HIP(hipGetLastError());
         GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(counts, offsets, n, part, total, st)));
         GS_HIP(hipMemcpyAsync(&h_total, total, sizeof(h_total), hipMemcpyDeviceToHost, st));
@@ -388,36 +513,44 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     }
     if (I == 0) return GS_OK;
 
-    auto* keys_a = (unsigned long long*)(ws + L.keys_a);
-    auto* keys_b = (unsigned long long*)(ws + L.keys_b);
-    auto* vals_t = (int*)(ws + L.vals_tmp);
+    // Splats in depth order: stable sort of (depth bits, id), ids starting in id order.
+    auto* dka = (unsigned*)(ws + L.dkeys_a);
+    auto* dkb = (unsigned*)(ws + L.dkeys_b);
+    auto* dva = (int*)(ws + L.dvals_a);
+    auto* dvb = (int*)(ws + L.dvals_b);
     auto* hist = (unsigned*)(ws + L.hist);
+    depth_keys_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, depths, dka, dva);
+    GS_HIP(hipGetLastError());
+    for (int shift = 0; shift < 32; shift += kRadixBits) {
+        GS_HIP(radix_pass<unsigned>(dka, dva, dkb, dvb, n, shift, hist, part, total, st));
+        unsigned* tk = dka; dka = dkb; dkb = tk;
+        int* tv = dva; dva = dvb; dvb = tv;
+    }
+    const int* by_depth = dva;  // four passes: back in the first buffers
 
-    // Digit passes: depth bits 0..30, then tile bits 32..32+tb-1.
+    // Emission offsets in depth order.
+    auto* rect_sorted = (ushort4*)(ws + L.rect_sorted);
+    auto* cnt_sorted = (unsigned long long*)(ws + L.cnt_sorted);
+    auto* emit_off = (unsigned long long*)(ws + L.emit_off);
+    gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
+    GS_HIP(hipGetLastError());
+    GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(cnt_sorted, emit_off, n, part, total, st)));
+
+    // Tile passes, ping-ponged so that the last one writes its values into sorted_ids.
     const int tb = bits_for(tiles);
-    int shifts[8];
-    int np = 0;
-    for (int s = 0; s < 31; s += kRadixBits) shifts[np++] = s;
-    for (int s = 32; s < 32 + tb; s += kRadixBits) shifts[np++] = s;
-
-    // Ping-pong so that the last pass writes its values into sorted_ids.
-    unsigned long long* kin = keys_a;
-    unsigned long long* kout = keys_b;
+    const int np = (tb + kRadixBits - 1) / kRadixBits;
+    auto* keys_a = (unsigned*)(ws + L.keys_a);
+    auto* keys_b = (unsigned*)(ws + L.keys_b);
+    auto* vals_t = (int*)(ws + L.vals_tmp);
+    unsigned* kin = keys_a;
+    unsigned* kout = keys_b;
     int* vin = (np % 2 == 0) ? sorted_ids : vals_t;
     int* vout = (np % 2 == 0) ? vals_t : sorted_ids;
-
-    emit_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, offsets, kin,
-                                                 vin);
+    emit_kernel<<<(n + kWave - 1) / kWave, kWave, 0, st>>>(n, I, by_depth, rect_sorted, emit_off, GX, kin, vin);
     GS_HIP(hipGetLastError());
-
-    const int nwg = (int)((I + kSortTile - 1) / kSortTile);
     for (int p = 0; p < np; ++p) {
-        radix_hist_kernel<<<nwg, kSortThreads, 0, st>>>(kin, I, shifts[p], nwg, hist);
-        GS_HIP(hipGetLastError());
-        GS_HIP((exclusive_scan<unsigned, unsigned>(hist, hist, (long long)kRadix * nwg, part, total, st)));
-        radix_scatter_kernel<<<nwg, kSortThreads, 0, st>>>(kin, vin, I, shifts[p], nwg, hist, kout, vout);
-        GS_HIP(hipGetLastError());
-        unsigned long long* tk = kin; kin = kout; kout = tk;
+        GS_HIP(radix_pass<unsigned>(kin, vin, kout, vout, I, kRadixBits * p, hist, part, total, st));
+        unsigned* tk = kin; kin = kout; kout = tk;
         int* tv = vin; vin = vout; vout = tv;
     }
     ranges_kernel<<<(unsigned)((I + 255) / 256), 256, 0, st>>>(kin, I, (int2*)tile_ranges);
