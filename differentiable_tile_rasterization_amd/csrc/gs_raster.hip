@@ -339,21 +339,23 @@ constexpr unsigned short kDummyOff = (unsigned short)(kDummy * sizeof(BwdSlot));
 constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummies read ahead of use
 
 // Per-half lists of the staged slots whose hit bit is set, as slot byte
-// offsets in descending slot order (the walk's order). Returns nothing; ends
-// with a workgroup barrier.
-__device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], unsigned short (*list)[kListLen],
-                                                 int (*cnt)[kHalves])
+// offsets in descending slot order (the walk's order). The same exchange of
+// per-wave counts also ORs `flag` over the workgroup, which is returned.
+// Ends with a workgroup barrier.
+__device__ __forceinline__ bool build_half_lists(const bool (&hit)[kHalves], bool flag,
+                                                 unsigned short (*list)[kListLen], int (*cnt)[kHalves + 1])
 {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int mine = 0;
+    int mine = __ballot(flag) != 0 ? 1 : 0;  // lane kHalves: the wave's flag
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
         const int c = __popcll(__ballot(hit[q]));  // whole-wave ballot, outside any lane branch
         mine = lane == q ? c : mine;
     }
-    if (lane < kHalves) cnt[wv][lane] = mine;
+    if (lane <= kHalves) cnt[wv][lane] = mine;
     __syncthreads();
+    const bool any_flag = (cnt[0][kHalves] | cnt[1][kHalves] | cnt[2][kHalves] | cnt[3][kHalves]) != 0;
     // lane q: list position of this wave's lowest hit of half q, counted from
     // the front (slots of higher waves come first)
     int top = 0;
@@ -377,6 +379,7 @@ __device__ __forceinline__ void build_half_lists(const bool (&hit)[kHalves], uns
         }
     }
     __syncthreads();
+    return any_flag;
 }
 
 template <bool AW>
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     __shared__ BwdSlot S[kBlock];
     __shared__ int half_end[kHalves];
     __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
-    __shared__ int list_cnt[4][kHalves];               // [staging wave][half]
+    __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
 
     const int tile = order ? order[blockIdx.x] : xcd_tile(blockIdx.x, tiles);
     if (tile < 0 || tile >= tiles) return;
@@ -446,8 +449,10 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const int w_field = 2 * ((0x3120 >> (4 * ((lane >> 2) & 3))) & 3) + odd;
     const int lead_off = (int)offsetof(BwdSlot, part) + 4 * w_field;  // byte offset of the bank leader's field
 
+    // No barrier at the top of a batch: thread t flushes slot t and then stages
+    // slot t itself, and the barrier after the walk already separates the
+    // walk's reads of the slots and lists from their rewriting.
     for (int bs = ((tmax - 1) / kBatch) * kBatch; bs >= 0; bs -= kBatch) {
-        __syncthreads();  // previous batch fully flushed before LDS is reused
         const int k = bs + (int)threadIdx.x;
         int id = -1, radius = 0;
         SplatRec r;
@@ -472,8 +477,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
         const bool may_clamp = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
-        const bool clamp_batch = __syncthreads_or(may_clamp) != 0;
-        build_half_lists(hit, list, list_cnt);
+        const bool clamp_batch = build_half_lists(hit, may_clamp, list, list_cnt);
         // this half's list length, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
