@@ -76,147 +76,13 @@ __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restri
     recs[i] = r;
 }
 
-struct StageLds {
-    float4 a[kBlock];  // mean x, mean y, l11, l21
-    float4 b[kBlock];  // l22, log2(opacity), red, green
-    float c[kBlock];   // blue
-};
-
+// Pixel of thread threadIdx.x in the walks: wave w owns the 8x8 quadrant
+// (w & 1, w >> 1) of the tile, lane l its pixel (l & 7, l >> 3).
 __device__ __forceinline__ void quadrant_pixel(int tile, int GX, int& x, int& y)
 {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     x = (tile % GX) * kTile + (w & 1) * 8 + (l & 7);
     y = (tile / GX) * kTile + (w >> 1) * 8 + (l >> 3);
-}
-
-// Coefficients (a', b', c') of q' = a' dx^2 + 2 b' dx dy + c' dy^2 from the
-// scaled factor in the record.
-__device__ __forceinline__ void qform_coef(const SplatRec& r, float& qa, float& qb, float& qc)
-{
-    qa = r.a.z * r.a.z;
-    qb = r.a.z * r.a.w;
-    qc = __builtin_fmaf(r.a.w, r.a.w, r.b.x * r.b.x);
-}
-
-// Stages record `r` into LDS slot threadIdx.x and returns the 4-bit mask of
-// quadrants (waves) whose pixel-centre rectangle the splat can reach;
-// `allowed` masks quadrants that do not walk this entry at all.
-__device__ __forceinline__ unsigned stage_record(StageLds& S, const SplatRec& r, float ox, float oy, unsigned allowed)
-{
-    S.a[threadIdx.x] = r.a;
-    S.b[threadIdx.x] = r.b;
-    S.c[threadIdx.x] = r.c.x;
-    float qa, qb, qc;
-    qform_coef(r, qa, qb, qc);
-    unsigned mask = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float x0 = ox + (float)((q & 1) * 8) - r.a.x;
-        const float y0 = oy + (float)((q >> 1) * 8) - r.a.y;
-        if (((allowed >> q) & 1u) && rect_min_q(qa, qb, qc, x0, x0 + 7.0f, y0, y0 + 7.0f) <= r.c.y)
-            mask |= 1u << q;
-    }
-    return mask;
-}
-
-// Builds the per-wave lists from every thread's quadrant mask; returns the
-// length of the calling wave's list. Ends with a workgroup barrier.
-__device__ __forceinline__ int build_lists(unsigned mask, unsigned char (*list)[kBlock], int (*list_cnt)[4])
-{
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    unsigned long long bal[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) bal[q] = __ballot((mask >> q) & 1u);
-    if (lane == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) list_cnt[wv][q] = __popcll(bal[q]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if ((mask >> q) & 1u) {
-            int off = __popcll(bal[q] & lt_mask);
-            for (int w2 = 0; w2 < wv; ++w2) off += list_cnt[w2][q];
-            list[q][off] = (unsigned char)threadIdx.x;
-        }
-    }
-    const int len = list_cnt[0][wv] + list_cnt[1][wv] + list_cnt[2][wv] + list_cnt[3][wv];
-    __syncthreads();
-    return len;
-}
-
-// ---------------------------------------------------------------------------
-// Forward
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int tiles,
-                                                     const int2* __restrict__ ranges,
-                                                     const int* __restrict__ ids,
-                                                     const SplatRec* __restrict__ recs,
-                                                     const float* __restrict__ bg, float* __restrict__ image,
-                                                     float* __restrict__ final_T, int* __restrict__ n_contrib)
-{
-    __shared__ StageLds S;
-    __shared__ unsigned char list[4][kBlock];
-    __shared__ int list_cnt[4][4];
-    __shared__ int wave_live[4];
-    const int tile = xcd_tile(blockIdx.x, tiles);
-    if (tile >= tiles) return;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int x, y;
-    quadrant_pixel(tile, GX, x, y);
-    const bool inside = x < W && y < H;
-    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
-    const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = ranges[tile];
-
-    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-    int last = 0;
-    bool done = !inside;
-    for (int bs = rg.x; bs < rg.y; bs += kBlock) {
-        const bool wave_live_now = __ballot(!done) != 0;
-        if (lane == 0) wave_live[wv] = wave_live_now ? 1 : 0;
-        if (__syncthreads_count(done) == kBlock) break;  // every pixel of the tile has stopped
-        const unsigned allowed = (unsigned)wave_live[0] | ((unsigned)wave_live[1] << 1) |
-                                 ((unsigned)wave_live[2] << 2) | ((unsigned)wave_live[3] << 3);
-        const int idx = bs + (int)threadIdx.x;
-        unsigned mask = 0;
-        if (idx < rg.y) mask = stage_record(S, recs[ids[idx]], ox, oy, allowed);
-        const int len = build_lists(mask, list, list_cnt);
-        for (int li = 0; li < len; ++li) {
-            if (__ballot(!done) == 0) break;
-            if (done) continue;
-            const int j = list[wv][li];
-            const float4 A = S.a[j];
-            const float4 B = S.b[j];
-            const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
-            float dx, dy;
-            const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
-            if (al >= kAlphaMin) {
-                const float test = T * (1.0f - al);
-                if (test < kTMin) {
-                    done = true;
-                } else {
-                    const float wgt = al * T;
-                    C0 = __builtin_fmaf(B.z, wgt, C0);
-                    C1 = __builtin_fmaf(B.w, wgt, C1);
-                    C2 = __builtin_fmaf(S.c[j], wgt, C2);
-                    T = test;
-                    last = bs - rg.x + j + 1;
-                }
-            }
-        }
-    }
-    if (inside) {
-        const int p = y * W + x;
-        float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
-        if (bg) { b0 = bg[0]; b1 = bg[1]; b2 = bg[2]; }
-        image[3 * p + 0] = __builtin_fmaf(T, b0, C0);
-        image[3 * p + 1] = __builtin_fmaf(T, b1, C1);
-        image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
-        final_T[p] = T;
-        n_contrib[p] = last;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -605,6 +471,153 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
                 }
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+//
+// The same half-wave walk as the backward, front to back: per batch of 255
+// list entries, thread t stages entry t's record in a 48-byte LDS slot and
+// tests it against the 8x4 halves whose pixels have not all stopped; ballots
+// build one list per half (slot byte offsets, ascending: the walk's order),
+// the shorter list of a wave padded with a dummy entry of opacity 0. A wave
+// walks both of its lists in lockstep, the next record read one step ahead,
+// and leaves the batch once its 64 pixels have stopped; the workgroup stops
+// when all 256 have.
+// ---------------------------------------------------------------------------
+struct FwdSlot {
+    float4 a;   // mean x, mean y, l11, l21 (scaled factor)
+    float4 b;   // l22, log2(opacity), red, green
+    float c;    // blue
+    float pad[3];
+};
+static_assert(sizeof(FwdSlot) == 48, "FwdSlot layout");
+
+__global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int tiles,
+                                                     const int2* __restrict__ ranges,
+                                                     const int* __restrict__ ids,
+                                                     const SplatRec* __restrict__ recs,
+                                                     const float* __restrict__ bg, float* __restrict__ image,
+                                                     float* __restrict__ final_T, int* __restrict__ n_contrib)
+{
+    __shared__ FwdSlot S[kBlock];
+    __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
+    __shared__ int list_cnt[4][kHalves + 1];
+    __shared__ int half_live[kHalves];
+    const int tile = xcd_tile(blockIdx.x, tiles);
+    if (tile >= tiles) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int half = lane >> 5, hq = 2 * wv + half;
+    int x, y;
+    quadrant_pixel(tile, GX, x, y);
+    const bool inside = x < W && y < H;
+    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
+    const int2 rg = ranges[tile];
+    if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel
+        S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
+        S[kDummy].c = 0.0f;
+    }
+    constexpr unsigned short kDummyFwd = (unsigned short)(kDummy * sizeof(FwdSlot));
+    const char* Sb = reinterpret_cast<const char*>(S);
+    auto rec_at = [&](int o) -> const FwdSlot& { return *reinterpret_cast<const FwdSlot*>(Sb + o); };
+
+    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
+    int last_bs = -1, last_cur = 0;  // batch start and slot offset of the last composited entry
+    bool done = !inside;
+    for (int bs = rg.x; bs < rg.y; bs += kBatch) {
+        // halves with a pixel still compositing; the tile stops when none is left
+        const bool half_alive = __ballot(!done) & (half ? 0xffffffff00000000ull : 0xffffffffull);
+        if ((lane & 31) == 0) half_live[hq] = half_alive ? 1 : 0;
+        if (__syncthreads_count(done) == kBlock) break;  // every pixel of the tile has stopped
+        int hend[kHalves];  // halves with no live pixel take no entries
+#pragma unroll
+        for (int q = 0; q < kHalves; ++q) hend[q] = half_live[q] ? 0x7fffffff : 0;
+        const int idx = bs + (int)threadIdx.x;
+        SplatRec r;
+        r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
+        if (threadIdx.x < kBatch && idx < rg.y) {
+            r = recs[ids[idx]];
+            S[threadIdx.x].a = r.a;
+            S[threadIdx.x].b = r.b;
+            S[threadIdx.x].c = r.c.x;
+        }
+        bool hit[kHalves];
+        half_hits(r, ox, oy, 0, hend, hit);
+        // ascending slot order: list position = (hits in lower waves and lanes)
+        int mine = 0;
+#pragma unroll
+        for (int q = 0; q < kHalves; ++q) {
+            const int c = __popcll(__ballot(hit[q]));
+            mine = lane == q ? c : mine;
+        }
+        if (lane < kHalves) list_cnt[wv][lane] = mine;
+        __syncthreads();
+        int below = 0;
+        if (lane < kHalves)
+            for (int w2 = 0; w2 < wv; ++w2) below += list_cnt[w2][lane];
+#pragma unroll
+        for (int q = 0; q < kHalves; ++q) {
+            const unsigned long long bal = __ballot(hit[q]);
+            if (hit[q]) {
+                const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+                list[q][__builtin_amdgcn_readlane(below, q) + rank] = (unsigned short)(threadIdx.x * sizeof(FwdSlot));
+            }
+        }
+        __syncthreads();
+        const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
+        const int other = hq ^ 1;
+        const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
+        const int steps = max(my_len, len_other);
+        for (int p = my_len + (lane & 31); p < steps + 2; p += 32) list[hq][p] = kDummyFwd;
+        const unsigned short* L = list[hq];
+
+        int off = L[0], offn = L[1];
+        float4 An = rec_at(off).a, Bn = rec_at(off).b;
+        float Cn = rec_at(off).c;
+        for (int it = 0; it < steps; ++it) {
+            const float4 A = An, B = Bn;
+            const float Cb = Cn;
+            const int cur = off;
+            off = offn;
+            offn = L[it + 2];
+            An = rec_at(off).a;
+            Bn = rec_at(off).b;
+            Cn = rec_at(off).c;
+            if (__ballot(!done) == 0) break;  // the wave's 64 pixels have stopped
+            const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
+            float dx, dy;
+            const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
+            if (!done && al >= kAlphaMin) {
+                const float test = T * (1.0f - al);
+                if (test < kTMin) {
+                    done = true;
+                } else {
+                    const float wgt = al * T;
+                    C0 = __builtin_fmaf(B.z, wgt, C0);
+                    C1 = __builtin_fmaf(B.w, wgt, C1);
+                    C2 = __builtin_fmaf(Cb, wgt, C2);
+                    T = test;
+                    last_bs = bs;
+                    last_cur = cur;
+                }
+            }
+        }
+        __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
+    }
+    if (inside) {
+        const int p = y * W + x;
+        float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
+        if (bg) { b0 = bg[0]; b1 = bg[1]; b2 = bg[2]; }
+        image[3 * p + 0] = __builtin_fmaf(T, b0, C0);
+        image[3 * p + 1] = __builtin_fmaf(T, b1, C1);
+        image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
+        final_T[p] = T;
+        n_contrib[p] = last_bs < 0 ? 0 : last_bs - rg.x + last_cur / (int)sizeof(FwdSlot) + 1;
     }
 }
 
