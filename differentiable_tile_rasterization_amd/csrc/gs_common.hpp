@@ -229,6 +229,15 @@ __device__ __forceinline__ float dpp_add_half_mirror(float x) { return x + dpp0<
 __device__ __forceinline__ float dpp_add_quad_xor2(float x) { return x + dpp0<0x4E>(x); }  // quad_perm [2,3,0,1]
 __device__ __forceinline__ float dpp_add_quad_xor1(float x) { return x + dpp0<0xB1>(x); }  // quad_perm [1,0,3,2]
 
+// rows 1 and 3: x + (lane 15 of the row before); rows 0 and 2 keep x. With a
+// row total in every lane, rows 1 and 3 then hold the total of rows (0, 1)
+// and (2, 3).
+__device__ __forceinline__ float dpp_add_prev_row_odd(float x)
+{
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(x));
+    return x;
+}
+
 // lanes 0-7 of each row: x + ror8(x); lanes 8-15: y + ror8(y)
 __device__ __forceinline__ float merge_ror8(float x, float y)
 {

@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
-        const int steps = max(my_len, len_other);
+        // the same for both halves: wave-uniform, so the loop runs on scalar control
+        const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
         // the shorter half takes the dummy entry once its list is exhausted
         // (and both read up to four entries past the end, ahead of use)
         for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDummyOff;
@@ -363,6 +364,14 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         // Two register sets take turns (the loop is unrolled by two), so the
         // read-ahead costs no register copies.
         auto rec_at = [&](int o) -> const BwdSlot& { return *reinterpret_cast<const BwdSlot*>(Sb + o); };
+        // list entries as 32-bit values: the 16-bit load zero-extends, and
+        // holding the widened value keeps the compiler from masking it again
+        // at every use
+        auto list_at = [&](int i) -> int {
+            int o = L[i];
+            asm("" : "+v"(o));
+            return o;
+        };
         auto step = [&](const float4& A, const float4& Bq, float Cb, int cur, auto clamp_tag) {
             constexpr bool kClamp = decltype(clamp_tag)::value;
             const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
@@ -404,28 +413,35 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             const float r3 = fold16(f6, f7);
             // Inside each row: merge pairs of registers while halving the
             // lanes each partial covers (8 -> 4 -> 1 lanes): W's 4-lane bank b
-            // ends with the total of R_{0,2,1,3}[b].
+            // ends with the total of R_{0,2,1,3}[b]. (Leaving the last two
+            // levels to the LDS, with four lanes adding into one address, is
+            // far slower: same-address LDS float adds serialize.)
             const float wq = merge_half_mirror(merge_ror8(r0, r1), merge_ror8(r2, r3));
             float wt = dpp_add_quad_xor1(dpp_add_quad_xor2(wq));
             // field 8 (and the weight): folded with the weight when it is
-            // wanted, else summed per row and added by both row leaders
+            // wanted (rows 0 and 2 then hold field 8, rows 1 and 3 the
+            // weight), else summed per row and the two rows of each half
+            // added in registers (so that no two lanes add into one address:
+            // same-address LDS adds serialize)
             float zt = AW ? fold16(f8, w) : f8;
             zt = dpp_add_quad_xor1(dpp_add_quad_xor2(dpp_add_half_mirror(dpp_add_ror8(zt))));
+            if (!AW) zt = dpp_add_prev_row_odd(zt);
             // keep the last fused DPP adds here rather than under the leader masks
             asm volatile("" : "+v"(wt), "+v"(zt));
             char* P = const_cast<char*>(Sb) + cur;
             if (bank_lead) atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
-            if (row_lead) atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
+            if (AW ? row_lead : (lane & 31) == 16)
+                atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
         };
         auto walk = [&](auto clamp_tag) {
-            int o0 = L[0], o1 = L[1], on0 = L[2];
+            int o0 = list_at(0), o1 = list_at(1), on0 = list_at(2);
             float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
             float C0 = rec_at(o0).c;
             for (int it = 0; it < steps; it += 2) {
                 // set 1 <- position it + 1; list position it + 3
                 const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
                 const float C1 = rec_at(o1).c;
-                const int on1 = L[it + 3];
+                const int on1 = list_at(it + 3);
                 step(A0, B0, C0, o0, clamp_tag);
                 if (it + 1 >= steps) break;
                 // set 0 <- position it + 2; list position it + 4
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
                 A0 = rec_at(o0).a;
                 B0 = rec_at(o0).b;
                 C0 = rec_at(o0).c;
-                on0 = L[it + 4];
+                on0 = list_at(it + 4);
                 step(A1, B1, C1, o1, clamp_tag);
                 o1 = on1;
             }
@@ -572,7 +588,8 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
-        const int steps = max(my_len, len_other);
+        // the same for both halves: wave-uniform, so the loop runs on scalar control
+        const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
         for (int p = my_len + (lane & 31); p < steps + 2; p += 32) list[hq][p] = kDummyFwd;
         const unsigned short* L = list[hq];
 
