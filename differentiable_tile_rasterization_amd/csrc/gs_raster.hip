@@ -314,6 +314,12 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const bool bank_lead = (lane & 3) == 0, row_lead = (lane & 15) == 0;
     const int w_field = 2 * ((0x3120 >> (4 * ((lane >> 2) & 3))) & 3) + odd;
     const int lead_off = (int)offsetof(BwdSlot, part) + 4 * w_field;  // byte offset of the bank leader's field
+    // the same as wave masks, so that a step can switch off the leaders of a
+    // half with no contributing lane (an exhausted list's dummy entry, or an
+    // entry that reaches none of the half's walked pixels) on scalar
+    // registers: each LDS add lane costs the LDS several cycles
+    const unsigned long long bank_mask = __ballot(bank_lead);
+    const unsigned long long row_mask = __ballot(AW ? row_lead : (lane & 31) == 16);
 
     // No barrier at the top of a batch: thread t flushes slot t and then stages
     // slot t itself, and the barrier after the walk already separates the
@@ -378,12 +384,21 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             float dx, dy;
             const float ar = alpha_raw(kf, px, py, dx, dy);
             const float al = kClamp ? fminf(kAlphaMax, ar) : ar;
-            const bool contrib = (cur < ncb_off) && (al >= kAlphaMin);
+            // contributing lanes (position below n_contrib, alpha >= 1/255) as
+            // a wave mask built from the two compares, which keeps the
+            // per-half tests below on scalar registers
+            const unsigned long long bal = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) &
+                                           __builtin_amdgcn_sicmp(cur, ncb_off, 40 /* signed < */);
+            const bool contrib = __builtin_amdgcn_inverse_ballot_w64(bal);
             // colour . gradient ahead of the test, so that the colour loads
             // issue with the rest of the record
             float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
             asm volatile("" : "+v"(cg));  // not sunk into the branch below
-            if (__ballot(contrib) == 0) return;
+            if (bal == 0) return;
+            unsigned bal_hi = (unsigned)(bal >> 32);
+            asm("" : "+s"(bal_hi));  // a 32-bit test (a 64-bit unsigned compare has no scalar form)
+            const unsigned long long live = ((unsigned)bal != 0u ? 0x00000000ffffffffull : 0ull) |
+                                            (bal_hi != 0u ? 0xffffffff00000000ull : 0ull);
 
             const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
             const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
@@ -429,8 +444,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             // keep the last fused DPP adds here rather than under the leader masks
             asm volatile("" : "+v"(wt), "+v"(zt));
             char* P = const_cast<char*>(Sb) + cur;
-            if (bank_lead) atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
-            if (AW ? row_lead : (lane & 31) == 16)
+            if (__builtin_amdgcn_inverse_ballot_w64(bank_mask & live))
+                atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
+            if (__builtin_amdgcn_inverse_ballot_w64(row_mask & live))
                 atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
         };
         auto walk = [&](auto clamp_tag) {
