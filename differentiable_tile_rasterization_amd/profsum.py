@@ -3,8 +3,12 @@
     python -m differentiable_tile_rasterization_amd.profsum stats <kernel_stats.csv> <out.md> "<command>"
     python -m differentiable_tile_rasterization_amd.profsum pmc <fetch_dir> <write_dir> <out.json> <out.md> \\
         "<fetch command>" "<write command>" [config]
+    python -m differentiable_tile_rasterization_amd.profsum counters <out.md> <kernel prefix> \\
+        <dir> "<command>" [<dir> "<command>" ...]
 
-`stats` lists every kernel of a --kernel-trace --stats run (calls, average and
+`counters` lists, for the last dispatch of the named kernel in each --pmc run
+directory, every counter summed over the device, with the LDS and VALU
+utilisations they give. `stats` lists every kernel of a --kernel-trace --stats run (calls, average and
 total time). `pmc` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) into bytes per launch, scaled by what the same counters read for the
 measurement library's 1 GiB float4 copy kernel (1 GiB read, 1 GiB written per
@@ -89,10 +93,45 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def counters(out_md: str, prefix: str, *runs: str) -> None:
+    vals: dict[str, float] = {}
+    cmds = []
+    for d, cmd in zip(runs[0::2], runs[1::2]):
+        path = [os.path.join(d, f) for f in os.listdir(d) if f.endswith("counter_collection.csv")][0]
+        per: dict[int, dict[str, float]] = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in csv.DictReader(open(path)):
+            if _short(r["Kernel_Name"]).startswith(prefix):
+                per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        last = per[max(per)]
+        for k, v in last.items():
+            vals[k if k != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE ({os.path.basename(d)})"] = v
+        cmds.append(cmd)
+    lines = [f"# Counters of {prefix} (last dispatch of each run, summed over the device)", "",
+             "Commands (repo root, on the GPU box):", ""] + ["    " + c for c in cmds] + [
+             "", "| counter | value |", "|---|---:|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in sorted(vals.items())]
+    grbm = [v for k, v in vals.items() if k.startswith("GRBM_GUI_ACTIVE")]
+    if grbm:
+        cyc = max(grbm) / 8.0  # GRBM_GUI_ACTIVE counts per XCD; 8 XCDs
+        lines += ["", f"Kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs): {cyc:.4g} = {cyc / 2.4e3:.1f} us at 2.4 GHz."]
+        if "SQ_LDS_IDX_ACTIVE" in vals:
+            lines.append(f"LDS index unit busy: SQ_LDS_IDX_ACTIVE / (256 CUs x cycles) = "
+                         f"{vals['SQ_LDS_IDX_ACTIVE'] / (256 * cyc):.2f}.")
+        if "SQ_ACTIVE_INST_VALU" in vals:
+            lines.append(f"VALU busy: SQ_ACTIVE_INST_VALU x 4 / (1024 SIMDs x cycles) = "
+                         f"{vals['SQ_ACTIVE_INST_VALU'] * 4 / (1024 * cyc):.2f}.")
+        if "SQ_INSTS_VALU" in vals:
+            lines.append(f"VALU issue: SQ_INSTS_VALU x 4 / (1024 SIMDs x cycles) = "
+                         f"{vals['SQ_INSTS_VALU'] * 4 / (1024 * cyc):.2f} of one wave instruction per 4 cycles.")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "pmc":
         pmc(*sys.argv[2:])
+    elif sys.argv[1] == "counters":
+        counters(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
