@@ -56,6 +56,8 @@ def _load():
         lib.gso_forward.restype = i32
         lib.gso_backward.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, i32, P, P]
         lib.gso_backward.restype = i32
+        lib.gso_max_weight.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, i32, P, P]
+        lib.gso_max_weight.restype = i32
         lib.gso_threads.argtypes = []
         lib.gso_threads.restype = i32
         _lib = lib
@@ -208,19 +210,47 @@ def rasterize_bwd(means2d, conics, colors, opacities, background, width: int, he
             "accum_weight": aw}
 
 
+def max_weight(means2d, conics, colors, opacities, background, width: int, height: int,
+               tile_ranges, sorted_ids, tiles=None):
+    """Per-splat maximum compositing weight alpha T over composited pairs (0
+    for a splat no pixel composites): the "max wt" statistic that the Spirula
+    Studio page's raster_bench times (section 亲手验证) without defining it.
+    Returns (max_weight float64 [n], uncertain bool [n]); ``uncertain`` marks
+    the splats that a pixel with an ambiguous float32 decision could
+    composite (several results are then correct for them)."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    n = m.shape[0]
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    mw = np.zeros(n, dtype=np.float64)
+    unc = np.zeros(n, dtype=np.uint8)
+    if tiles is None:
+        tl, ntl = None, 0
+    else:
+        tarr = np.ascontiguousarray(tiles, dtype=np.int32)
+        tl, ntl = _ptr(tarr), len(tarr)
+    lib.gso_max_weight(width, height, n, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
+                       _ptr(bg), tl, ntl, _ptr(mw), _ptr(unc))
+    return mw, unc.astype(bool)
+
+
 # ----------------------------------------------------------------------------
 # Brute force (no tiles), numpy
 # ----------------------------------------------------------------------------
 
 def composite_bruteforce(means2d, conics, colors, opacities, depths, radii, background,
-                         width: int, height: int, return_margin: bool = False):
+                         width: int, height: int, return_margin: bool = False,
+                         return_max_weight: bool = False):
     """Every pixel walks every live splat in (float32 depth bits, id) order,
     with the same skip / clamp / stop rules; no tiles and no radius test
     beyond the per-splat cull (radius <= 0 or depth not > 0). Float64 numpy,
     vectorised over pixels. Returns (image, final_T, n_steps) where n_steps
     counts composited splats per pixel; with ``return_margin`` also the
     smallest relative distance of any decision taken (skip, clamp, stop) to
-    its threshold."""
+    its threshold, and with ``return_max_weight`` (last) each splat's largest
+    alpha T over the pixels that composite it."""
     m = np.asarray(means2d, dtype=np.float64)
     q = np.asarray(conics, dtype=np.float64)
     col = np.asarray(colors, dtype=np.float64)
@@ -236,6 +266,7 @@ def composite_bruteforce(means2d, conics, colors, opacities, depths, radii, back
     C = np.zeros((px.size, 3))
     done = np.zeros(px.shape, dtype=bool)
     nstep = np.zeros(px.shape, dtype=np.int64)
+    maxw = np.zeros(m.shape[0])
     margin = np.inf
     for i in order:
         dx = px - m[i, 0]
@@ -256,12 +287,18 @@ def composite_bruteforce(means2d, conics, colors, opacities, depths, radii, back
         done |= stop
         use &= ~stop
         C[use] += col[i] * (alpha[use] * T[use])[:, None]
+        if use.any():
+            maxw[i] = float(np.max(alpha[use] * T[use]))
         T = np.where(use, nxt, T)
         nstep += use
     bg = np.zeros(3) if background is None else np.asarray(background, dtype=np.float64)
     img = C + T[:, None] * bg[None, :]
     res = (img.reshape(height, width, 3), T.reshape(height, width), nstep.reshape(height, width))
-    return res + (margin,) if return_margin else res
+    if return_margin:
+        res = res + (margin,)
+    if return_max_weight:
+        res = res + (maxw,)
+    return res
 
 
 # ----------------------------------------------------------------------------

@@ -38,6 +38,11 @@
  *       dL/dmean = (a dx + b dy, b dx + c dy) dL/dsigma
  *     accum_weight_i = sum_p alpha_i T_i over composited pairs
  *
+ *   Max weight (the "max wt" line of the Spirula Studio page's raster_bench,
+ *   section 亲手验证, which names it without a formula; read as the largest
+ *   compositing weight a splat receives):
+ *     max_weight_i = max_p alpha_i T_i over composited pairs (0 if none)
+ *
  *   Unlike the kernels this evaluates T forwards (products) and S as a suffix
  *   sum, in float64, with no division recurrence.
  *
@@ -275,6 +280,88 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
         }
         free(buf);
         free(part);
+    }
+    return threads_used();
+}
+
+/*
+ * Max weight over the listed tiles: max_w [n] = max over composited pairs of
+ * alpha T (MAXED into; caller zeroes). uncertain [n] is set for every splat
+ * that a pixel with an ambiguous decision could composite: from that pixel's
+ * first ambiguous decision on, the float32 walk may take other skip / clamp /
+ * stop decisions, so every splat of its list whose alpha there reaches the
+ * skip threshold (within the float32 error band) is marked.
+ */
+int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
+                   const double* means, const double* conics, const double* colors, const double* opac,
+                   const double* bg, const int32_t* tiles, int ntiles, double* max_w, uint8_t* uncertain)
+{
+    (void)n;
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE, GY = (H + TILE - 1) / TILE;
+    int nt = tiles ? ntiles : GX * GY;
+#pragma omp parallel
+    {
+        int cap = 0;
+        contrib_t* buf = NULL;
+        double* part = NULL;   /* per tile-list entry: max weight */
+        uint8_t* unc = NULL;   /* per tile-list entry: uncertain */
+        int part_cap = 0;
+#pragma omp for schedule(dynamic, 1)
+        for (int ti = 0; ti < nt; ++ti) {
+            int t = tiles ? tiles[ti] : ti;
+            int tx = t % GX, ty = t / GX;
+            int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+            int L = end - start;
+            if (L <= 0) continue;
+            if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
+            if (L > part_cap) {
+                free(part); free(unc); part_cap = L;
+                part = (double*)malloc(sizeof(double) * part_cap);
+                unc = (uint8_t*)malloc(part_cap);
+            }
+            memset(part, 0, sizeof(double) * L);
+            memset(unc, 0, L);
+            for (int ly = 0; ly < TILE; ++ly) {
+                int y = ty * TILE + ly;
+                if (y >= H) break;
+                for (int lx = 0; lx < TILE; ++lx) {
+                    int x = tx * TILE + lx;
+                    if (x >= W) break;
+                    double T, C[3];
+                    int32_t nc;
+                    int a;
+                    double px = x + 0.5, py = y + 0.5;
+                    int cnt = walk_pixel(&s, ids, start, end, px, py, buf, cap, &T, &nc, C, &a);
+                    for (int e = 0; e < cnt; ++e) {
+                        double w = buf[e].alpha * buf[e].T;
+                        double* o = part + (buf[e].k - start);
+                        if (w > *o) *o = w;
+                    }
+                    if (!a) continue;
+                    for (int32_t k = start; k < end; ++k) {
+                        int32_t i = ids[k];
+                        double dx = px - s.means[2 * i], dy = py - s.means[2 * i + 1];
+                        double ca = s.conics[3 * i], cb = s.conics[3 * i + 1], cc = s.conics[3 * i + 2];
+                        double sigma = -0.5 * (ca * dx * dx + cc * dy * dy) - cb * dx * dy;
+                        double ah = s.opac[i] * exp(sigma);
+                        double ea = alpha_rel_bound(ca, cb, cc, dx, dy, sigma);
+                        if (ah >= ALPHA_MIN * (1.0 - ea) - 2.0 * U32 * ALPHA_MIN) unc[k - start] = 1;
+                    }
+                }
+            }
+#pragma omp critical(gso_merge_max)
+            {
+                for (int k = 0; k < L; ++k) {
+                    int32_t i = ids[start + k];
+                    if (part[k] > max_w[i]) max_w[i] = part[k];
+                    if (unc[k]) uncertain[i] = 1;
+                }
+            }
+        }
+        free(buf);
+        free(part);
+        free(unc);
     }
     return threads_used();
 }

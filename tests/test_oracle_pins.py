@@ -330,3 +330,76 @@ def test_ambiguity_flags_only_near_thresholds():
     out = _tiled(sc, backward=False)
     frac = out["ambiguous"].mean()
     assert frac < 1e-3, frac
+
+
+# ------------------------------------------------------------------ max weight
+# The per-splat "max wt" statistic: the largest alpha T a splat receives over
+# the pixels that composite it (the raster_bench line of the Spirula Studio
+# page, section 亲手验证, named there without a formula).
+
+def _max_weight(sc, out):
+    return oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                             sc.width, sc.height, out["tile_ranges"], out["sorted_ids"])
+
+
+@pytest.mark.parametrize("maker", [
+    lambda: scenes.make_scene("tiny", 0), lambda: scenes.make_scene("tiny", 1),
+    lambda: _ragged_scene(3), lambda: scenes.make_scene("early", 0, n=800),
+], ids=["tiny0", "tiny1", "ragged3", "early-800"])
+def test_max_weight_equals_bruteforce(maker):
+    sc = maker()
+    out = _tiled(sc, backward=False)
+    mw, _ = _max_weight(sc, out)
+    *_, bmw = oracle.composite_bruteforce(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.depths,
+                                          sc.radii, sc.background, sc.width, sc.height,
+                                          return_max_weight=True)
+    np.testing.assert_allclose(mw, bmw, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("o", [0.3, 0.7, 0.995])
+def test_max_weight_single_splat(o):
+    """Alone, a splat centred on a pixel centre takes its largest weight there,
+    with T = 1 and G = 1: min(0.99, o)."""
+    sc = scenes.custom_scene(16, 16, means2d=[[8.5, 7.5]], sigmas=[[1.5, 2.5]], thetas=[0.4],
+                             opacities=[o], colors=[[0.5, 0.5, 0.5]], depths=[1.0])
+    mw, unc = _max_weight(sc, _tiled(sc, backward=False))
+    assert not unc.any()
+    assert abs(mw[0] - min(0.99, o)) <= 1e-7   # float32 storage of the opacity
+
+
+def test_max_weight_behind_a_weak_splat():
+    """Two concentric isotropic splats, front opacity o1 <= 1/2: the back one's
+    weight o2 G (1 - o1 G) grows with G up to G = 1, so its maximum is at the
+    centre pixel: o2 (1 - o1); the front one's is o1."""
+    o1, o2 = 0.375, 0.8125   # exact in float32
+    sc = scenes.custom_scene(32, 32, means2d=[[16.5, 16.5]] * 2, sigmas=[[3.0, 3.0]] * 2,
+                             thetas=[0.0, 0.0], opacities=[o1, o2], colors=[[1, 0, 0], [0, 1, 0]],
+                             depths=[1.0, 2.0])
+    mw, _ = _max_weight(sc, _tiled(sc, backward=False))
+    np.testing.assert_allclose(mw, [o1, o2 * (1 - o1)], atol=1e-12, rtol=0)
+
+
+def test_max_weight_off_centre():
+    """Front opacity o1 > 1/2: the back splat's weight o2 G (1 - o1 G) peaks on
+    the ring G = 1 / (2 o1) at o2 / (4 o1), not at the centre. Wide splats make
+    the pixel grid sample G finely near the ring: the maximum over pixels lies
+    just below the continuous one and never above it."""
+    o1, o2 = 0.875, 0.75
+    sc = scenes.custom_scene(96, 96, means2d=[[48.5, 48.5]] * 2, sigmas=[[20.0, 20.0]] * 2,
+                             thetas=[0.0, 0.0], opacities=[o1, o2], colors=[[1, 0, 0], [0, 1, 0]],
+                             depths=[1.0, 2.0])
+    mw, _ = _max_weight(sc, _tiled(sc, backward=False))
+    peak = o2 / (4 * o1)
+    assert mw[1] <= peak + 1e-12
+    assert mw[1] >= peak - 2e-4
+    assert mw[1] > o2 * (1 - o1) + 0.05   # well above the value at the centre
+
+
+def test_max_weight_invariants():
+    for sc in [scenes.make_scene("tiny", 2), scenes.make_scene("early", 1, n=600)]:
+        out = _tiled(sc)
+        mw, _ = _max_weight(sc, out)
+        aw = out["accum_weight"]
+        assert np.all(mw >= 0) and np.all(mw <= 0.99)
+        assert np.all(mw <= aw + 1e-12)                 # the largest term of a sum of positives
+        np.testing.assert_array_equal(mw > 0, aw > 0)   # composited somewhere, or nowhere
