@@ -117,6 +117,10 @@ def main():
     def fwd():
         gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
 
+    def fwd_max_weight():
+        gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids,
+                             max_weight=True)
+
     def per_call(fn, steps, warmup):
         for _ in range(warmup):
             fn()
@@ -159,6 +163,7 @@ def main():
     stage_mean = {k: float(np.mean(v)) for k, v in stage_ms.items()}
     log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
     t_fwd = per_call(fwd, 10, 2)
+    t_mw = per_call(fwd_max_weight, 10, 2)
     t0 = time.perf_counter()
     for _ in range(3):
         gsr.gs_bin_tiles(m, r, d, sc.width, sc.height, capacity=bins.n_isect)
@@ -285,7 +290,8 @@ def main():
                    "width": sc.width, "height": sc.height, "splats": sc.n},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "stages_ms": {"tile_isect": t_bin, "raster_fwd": float(np.median(t_fwd)), "raster_bwd": ms,
+        "stages_ms": {"tile_isect": t_bin, "raster_fwd": float(np.median(t_fwd)),
+                      "raster_fwd_max_wt": float(np.median(t_mw)), "raster_bwd": ms,
                       "raster_bwd_median": float(np.median(t_calls)), "raster_bwd_min": float(np.min(t_calls))},
         "counts": {"p_walk": p_walk, "p_composited": p_contrib, "walked_entries": entries,
                    "splat_tile_groups": groups_tile, "splat_quadrant_groups": groups_wave,

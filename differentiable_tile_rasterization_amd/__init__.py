@@ -121,8 +121,10 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
 
 
 def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int, height: int,
-                     tile_ranges, sorted_ids, workspace=None, stream=None):
-    """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W]).
+                     tile_ranges, sorted_ids, max_weight: bool = False, workspace=None, stream=None):
+    """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W]),
+    and with ``max_weight`` also each splat's largest compositing weight
+    alpha T over the pixels that composite it ([n], 0 if none).
     ``workspace`` may pass a uint8 device buffer of at least
     gs_rasterize_fwd_workspace_size(n) + 256 bytes."""
     n = int(means2d.shape[0])
@@ -139,13 +141,16 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     image = torch.empty((height, width, 3), dtype=torch.float32, device=dev)
     final_T = torch.empty((height, width), dtype=torch.float32, device=dev)
     n_contrib = torch.empty((height, width), dtype=torch.int32, device=dev)
+    mw = torch.empty((n,), dtype=torch.float32, device=dev) if max_weight else None
     lib = _lib.load()
     ws_bytes = int(lib.gs_rasterize_fwd_workspace_size(n))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     _lib.check(lib.gs_rasterize_fwd(
         n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
-        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), wsp, ws_bytes,
-        _stream(stream)))
+        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _ptr(mw), wsp,
+        ws_bytes, _stream(stream)))
+    if max_weight:
+        return image, final_T, n_contrib, mw
     return image, final_T, n_contrib
 
 

@@ -238,6 +238,28 @@ __device__ __forceinline__ float dpp_add_prev_row_odd(float x)
     return x;
 }
 
+// Unsigned max with a DPP-permuted copy of itself, one fused instruction per
+// level (for non-negative floats, the max of their bit patterns is the bit
+// pattern of their max). row_umax32 leaves in rows 1 and 3 the max over the
+// two rows of each 32-lane half (rows 0 and 2 hold their own row's max).
+#define GS_DPP_UMAX(name, ctrl)                                                          \
+    __device__ __forceinline__ unsigned name(unsigned x)                                 \
+    {                                                                                    \
+        asm volatile("s_nop 1\n\tv_max_u32_dpp %0, %0, %0 " ctrl : "+v"(x));           \
+        return x;                                                                        \
+    }
+GS_DPP_UMAX(dpp_umax_ror8, "row_ror:8 row_mask:0xf bank_mask:0xf")
+GS_DPP_UMAX(dpp_umax_half_mirror, "row_half_mirror row_mask:0xf bank_mask:0xf")
+GS_DPP_UMAX(dpp_umax_quad_xor2, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
+GS_DPP_UMAX(dpp_umax_quad_xor1, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
+GS_DPP_UMAX(dpp_umax_prev_row_odd, "row_bcast:15 row_mask:0xa bank_mask:0xf")
+#undef GS_DPP_UMAX
+
+__device__ __forceinline__ unsigned row_umax32(unsigned x)
+{
+    return dpp_umax_prev_row_odd(dpp_umax_quad_xor1(dpp_umax_quad_xor2(dpp_umax_half_mirror(dpp_umax_ror8(x)))));
+}
+
 // lanes 0-7 of each row: x + ror8(x); lanes 8-15: y + ror8(y)
 __device__ __forceinline__ float merge_ror8(float x, float y)
 {

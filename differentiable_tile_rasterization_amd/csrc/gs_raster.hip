@@ -506,6 +506,13 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     }
 }
 
+// Zero fill (the max-weight output, raised by atomic max from 0).
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* __restrict__ p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Forward
 //
@@ -517,21 +524,32 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
 // walks both of its lists in lockstep, the next record read one step ahead,
 // and leaves the batch once its 64 pixels have stopped; the workgroup stops
 // when all 256 have.
+//
+// Optional per-splat max weight (MW): the largest alpha T a splat receives
+// over the pixels that composite it. Per step, each half's largest weight
+// (DPP max over its 32 lanes) goes into the entry's slot with one LDS max;
+// after each batch, thread t raises the splat's global maximum with one
+// integer atomic max. Weights are >= 0, so the order of their float32 bit
+// patterns is the order of their values, and a max is the same in any order:
+// the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
 struct FwdSlot {
-    float4 a;   // mean x, mean y, l11, l21 (scaled factor)
-    float4 b;   // l22, log2(opacity), red, green
-    float c;    // blue
-    float pad[3];
+    float4 a;       // mean x, mean y, l11, l21 (scaled factor)
+    float4 b;       // l22, log2(opacity), red, green
+    float c;        // blue
+    unsigned maxw;  // largest weight of the batch's walk (float bits), MW only
+    float pad[2];
 };
 static_assert(sizeof(FwdSlot) == 48, "FwdSlot layout");
 
-__global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int tiles,
+template <bool MW>
+__global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX, int tiles,
                                                      const int2* __restrict__ ranges,
                                                      const int* __restrict__ ids,
                                                      const SplatRec* __restrict__ recs,
                                                      const float* __restrict__ bg, float* __restrict__ image,
-                                                     float* __restrict__ final_T, int* __restrict__ n_contrib)
+                                                     float* __restrict__ final_T, int* __restrict__ n_contrib,
+                                                     unsigned* __restrict__ max_weight)
 {
     __shared__ FwdSlot S[kBlock];
     __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
@@ -558,12 +576,15 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     int last_bs = -1, last_cur = 0;  // batch start and slot offset of the last composited entry
-    bool done = !inside;
+    // the wave's stopped pixels (and those outside the image), as a lane mask:
+    // the walk's tests then build their masks with compare instructions alone
+    unsigned long long done_m = __ballot(!inside);
     for (int bs = rg.x; bs < rg.y; bs += kBatch) {
         // halves with a pixel still compositing; the tile stops when none is left
-        const bool half_alive = __ballot(!done) & (half ? 0xffffffff00000000ull : 0xffffffffull);
+        const bool half_alive = ~done_m & (half ? 0xffffffff00000000ull : 0xffffffffull);
         if ((lane & 31) == 0) half_live[hq] = half_alive ? 1 : 0;
-        if (__syncthreads_count(done) == kBlock) break;  // every pixel of the tile has stopped
+        if (__syncthreads_count(__builtin_amdgcn_inverse_ballot_w64(done_m)) == kBlock)
+            break;  // every pixel of the tile has stopped
         int hend[kHalves];  // halves with no live pixel take no entries
 #pragma unroll
         for (int q = 0; q < kHalves; ++q) hend[q] = half_live[q] ? 0x7fffffff : 0;
@@ -571,11 +592,14 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
         SplatRec r;
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
+        int id = -1;
         if (threadIdx.x < kBatch && idx < rg.y) {
-            r = recs[ids[idx]];
+            id = ids[idx];
+            r = recs[id];
             S[threadIdx.x].a = r.a;
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
+            if (MW) S[threadIdx.x].maxw = 0u;
         }
         bool hit[kHalves];
         half_hits(r, ox, oy, 0, hend, hit);
@@ -621,26 +645,41 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int W, int H, int GX, int t
             An = rec_at(off).a;
             Bn = rec_at(off).b;
             Cn = rec_at(off).c;
-            if (__ballot(!done) == 0) break;  // the wave's 64 pixels have stopped
+            if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
             const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
             float dx, dy;
             const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
-            if (!done && al >= kAlphaMin) {
-                const float test = T * (1.0f - al);
-                if (test < kTMin) {
-                    done = true;
-                } else {
-                    const float wgt = al * T;
-                    C0 = __builtin_fmaf(B.z, wgt, C0);
-                    C1 = __builtin_fmaf(B.w, wgt, C1);
-                    C2 = __builtin_fmaf(Cb, wgt, C2);
-                    T = test;
-                    last_bs = bs;
-                    last_cur = cur;
-                }
+            const float test = T * (1.0f - al);
+            // walked pixels whose alpha reaches 1/255; of those, the ones that
+            // composite (T stays >= 1e-4) and the ones that stop here
+            const unsigned long long a_m = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) & ~done_m;
+            const unsigned long long c_m = a_m & __builtin_amdgcn_fcmpf(test, kTMin, 3 /* ordered >= */);
+            done_m |= a_m & ~c_m;
+            if (c_m == 0) continue;
+            const bool comp = __builtin_amdgcn_inverse_ballot_w64(c_m);
+            const float wgt = comp ? al * T : 0.0f;  // other lanes add exact zeros
+            C0 = __builtin_fmaf(B.z, wgt, C0);
+            C1 = __builtin_fmaf(B.w, wgt, C1);
+            C2 = __builtin_fmaf(Cb, wgt, C2);
+            T = comp ? test : T;
+            last_bs = comp ? bs : last_bs;
+            last_cur = comp ? cur : last_cur;
+            if (MW) {
+                // each half's largest weight, in every lane of rows 1 and 3
+                const unsigned m = row_umax32(__float_as_uint(wgt));
+                unsigned hi = (unsigned)(c_m >> 32);
+                asm("" : "+s"(hi));  // a 32-bit test (a 64-bit unsigned compare has no scalar form)
+                const unsigned long long lead = ((unsigned)c_m != 0u ? (1ull << 16) : 0ull) |
+                                                (hi != 0u ? (1ull << 48) : 0ull);
+                if (__builtin_amdgcn_inverse_ballot_w64(lead))  // lane 16 or 48 of a half that composited
+                    atomicMax(reinterpret_cast<unsigned*>(const_cast<char*>(Sb) + cur + offsetof(FwdSlot, maxw)), m);
             }
         }
         __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
+        if (MW && id >= 0 && id < n) {  // thread t owns slot t until it restages it
+            const unsigned v = S[threadIdx.x].maxw;
+            if (v != 0u) atomicMax(max_weight + id, v);
+        }
     }
     if (inside) {
         const int p = y * W + x;
@@ -947,8 +986,8 @@ extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                                       const float* opacities, const float* background, int32_t width,
                                       int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                      float* image, float* final_T, int32_t* n_contrib, void* workspace,
-                                      size_t workspace_bytes, gs_stream_t stream_)
+                                      float* image, float* final_T, int32_t* n_contrib, float* max_weight,
+                                      void* workspace, size_t workspace_bytes, gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
     GS_CHECK_ARG(n >= 0, "gs_rasterize_fwd: n = %d < 0", n);
@@ -968,8 +1007,19 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
         GS_HIP(hipGetLastError());
     }
     const int GX = grid_x(width), tiles = GX * grid_y(height);
-    fwd_kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, tiles, (const int2*)tile_ranges, sorted_ids,
-                                                   recs, background, image, final_T, n_contrib);
+    if (max_weight) {
+        if (n > 0) {
+            zero_u32_kernel<<<(n + 255) / 256, 256, 0, st>>>((unsigned*)max_weight, n);
+            GS_HIP(hipGetLastError());
+        }
+        fwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
+                                                             sorted_ids, recs, background, image, final_T,
+                                                             n_contrib, (unsigned*)max_weight);
+    } else {
+        fwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
+                                                              sorted_ids, recs, background, image, final_T,
+                                                              n_contrib, nullptr);
+    }
     GS_HIP(hipGetLastError());
     return GS_OK;
 }

@@ -148,8 +148,15 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, co
  * kernel-by-kernel timing", section 計測結果; the "raster fwd" line of
  * raster_bench). One workgroup of 256 threads per 16x16 tile. Each splat is
  * first packed into a 48-byte record in the workspace (alpha coefficients,
- * colour, culling threshold, radius); each wave then walks only the list
- * entries whose alpha >= 1/255 ellipse reaches its 8x8 quadrant.
+ * colour, culling threshold, radius); each half of a wave (an 8x4 block of
+ * pixels) then walks only the list entries whose alpha >= 1/255 ellipse
+ * reaches it.
+ *
+ * Optionally also the per-splat max weight (the "max wt" line of raster_bench
+ * on the Spirula Studio page, section 亲手验证, which names the statistic
+ * without a formula; read here as the largest compositing weight alpha T the
+ * splat receives over the pixels that composite it, 0 if none). The result
+ * does not depend on scheduling.
  *
  *   n                 number of splats
  *   means2d           device float [n][2]
@@ -163,6 +170,8 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, co
  *   image             device float [height][width][3] (out)
  *   final_T           device float [height][width]    (out)
  *   n_contrib         device int32 [height][width]    (out)
+ *   max_weight        device float [n] (out), or NULL to skip it; every entry is
+ *                     written (0 for a splat no pixel composites)
  *   workspace         device scratch of at least gs_rasterize_fwd_workspace_size(n)
  *                     bytes (48 per splat), 256-byte aligned; contents on entry do
  *                     not matter
@@ -172,8 +181,8 @@ size_t gs_rasterize_fwd_workspace_size(int32_t n);
 gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                            const float* opacities, const float* background, int32_t width,
                            int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                           float* image, float* final_T, int32_t* n_contrib, void* workspace,
-                           size_t workspace_bytes, gs_stream_t stream);
+                           float* image, float* final_T, int32_t* n_contrib, float* max_weight,
+                           void* workspace, size_t workspace_bytes, gs_stream_t stream);
 
 /*
  * Backward (rasterize_backwards in "Phase 5 step 30b — kernel-by-kernel

@@ -211,13 +211,14 @@ def rasterize_bwd(means2d, conics, colors, opacities, background, width: int, he
 
 
 def max_weight(means2d, conics, colors, opacities, background, width: int, height: int,
-               tile_ranges, sorted_ids, tiles=None):
+               tile_ranges, sorted_ids, tiles=None, tol: float = 1e-5):
     """Per-splat maximum compositing weight alpha T over composited pairs (0
     for a splat no pixel composites): the "max wt" statistic that the Spirula
     Studio page's raster_bench times (section 亲手验证) without defining it.
     Returns (max_weight float64 [n], uncertain bool [n]); ``uncertain`` marks
-    the splats that a pixel with an ambiguous float32 decision could
-    composite (several results are then correct for them)."""
+    the splats whose maximum a float32 walk may legitimately change by more
+    than ``tol``: a pixel with an ambiguous decision may give them a weight
+    that reaches their maximum less ``tol``."""
     lib = _load()
     m, q, c, o = _arrs(means2d, conics, colors, opacities)
     n = m.shape[0]
@@ -225,15 +226,17 @@ def max_weight(means2d, conics, colors, opacities, background, width: int, heigh
     rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
     ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
     mw = np.zeros(n, dtype=np.float64)
-    unc = np.zeros(n, dtype=np.uint8)
+    amb = np.zeros(n, dtype=np.float64)
     if tiles is None:
         tl, ntl = None, 0
     else:
         tarr = np.ascontiguousarray(tiles, dtype=np.int32)
         tl, ntl = _ptr(tarr), len(tarr)
     lib.gso_max_weight(width, height, n, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
-                       _ptr(bg), tl, ntl, _ptr(mw), _ptr(unc))
-    return mw, unc.astype(bool)
+                       _ptr(bg), tl, ntl, _ptr(mw), _ptr(amb))
+    # a splat is certain when every weight an ambiguous pixel may give it is
+    # within tol of zero, or stays below its maximum less tol
+    return mw, (amb > tol) & (amb >= mw - tol)
 
 
 # ----------------------------------------------------------------------------

@@ -98,11 +98,11 @@ static double alpha_rel_bound(double a, double b, double c, double dx, double dy
  */
 static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int32_t end,
                       double px, double py, contrib_t* out, int cap,
-                      double* T_out, int32_t* nc_out, double C[3], int* amb_out)
+                      double* T_out, int32_t* nc_out, double C[3], int* amb_out, int32_t* kamb_out)
 {
     double T = 1.0, errT = 0.0;
     int cnt = 0, amb = 0;
-    int32_t last = 0;
+    int32_t last = 0, kamb = end;
     C[0] = C[1] = C[2] = 0.0;
     for (int32_t k = start; k < end; ++k) {
         int32_t i = ids[k];
@@ -116,11 +116,13 @@ static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int3
         double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;
         double ea = alpha_rel_bound(a, b, c, dx, dy, sigma);
         if (fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN) amb = 1;
+        if (amb && kamb == end) kamb = k;
         if (alpha < ALPHA_MIN) continue;
         if (fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32) amb = 1;
         double test = T * (1.0 - alpha);
         double et = errT + ea * alpha / (1.0 - alpha) + 4.0 * U32;
         if (fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN) amb = 1;
+        if (amb && kamb == end) kamb = k;
         if (test < T_MIN) break;
         const double* col = s->colors + 3 * i;
         C[0] += col[0] * alpha * T;
@@ -139,6 +141,7 @@ static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int3
     *T_out = T;
     *nc_out = last;
     *amb_out = amb;
+    if (kamb_out) *kamb_out = kamb;
     return cnt;
 }
 
@@ -180,7 +183,7 @@ int gso_forward(int W, int H, const int32_t* ranges, const int32_t* ids,
                 double T, C[3];
                 int32_t nc;
                 int a;
-                walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, NULL, 0, &T, &nc, C, &a);
+                walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, NULL, 0, &T, &nc, C, &a, NULL);
                 size_t p = (size_t)y * W + x;
                 image[3 * p + 0] = C[0] + T * s.bg[0];
                 image[3 * p + 1] = C[1] + T * s.bg[1];
@@ -233,7 +236,7 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
                     double T, C[3];
                     int32_t nc;
                     int a;
-                    int cnt = walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, buf, cap, &T, &nc, C, &a);
+                    int cnt = walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, buf, cap, &T, &nc, C, &a, NULL);
                     size_t p = (size_t)y * W + x;
                     double g[3] = {dimg[3 * p], dimg[3 * p + 1], dimg[3 * p + 2]};
                     /* S = sum over composited splats behind + T_final bg */
@@ -286,15 +289,20 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
 
 /*
  * Max weight over the listed tiles: max_w [n] = max over composited pairs of
- * alpha T (MAXED into; caller zeroes). uncertain [n] is set for every splat
- * that a pixel with an ambiguous decision could composite: from that pixel's
- * first ambiguous decision on, the float32 walk may take other skip / clamp /
- * stop decisions, so every splat of its list whose alpha there reaches the
- * skip threshold (within the float32 error band) is marked.
+ * alpha T (MAXED into; caller zeroes). max_w_amb [n] (MAXED into) bounds what
+ * a float32 walk may give a splat at pixels with an ambiguous decision: up to
+ * such a pixel's first ambiguous decision the float32 walk takes the same
+ * decisions; from there on, every splat of its list whose alpha reaches the
+ * skip threshold (within the error band) may be composited with a weight of
+ * at most 1.01 alpha T, T being this walk's transmittance before it, the walk
+ * continued past its stop (each flipped skip changes T by a factor within
+ * (1 - 1/255)^-1; a flipped clamp changes alpha by a few ulp). A splat whose
+ * max_w_amb stays below its max_w less the comparison tolerance has the same
+ * maximum in any correct float32 walk.
  */
 int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
                    const double* means, const double* conics, const double* colors, const double* opac,
-                   const double* bg, const int32_t* tiles, int ntiles, double* max_w, uint8_t* uncertain)
+                   const double* bg, const int32_t* tiles, int ntiles, double* max_w, double* max_w_amb)
 {
     (void)n;
     splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
@@ -305,7 +313,7 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
         int cap = 0;
         contrib_t* buf = NULL;
         double* part = NULL;   /* per tile-list entry: max weight */
-        uint8_t* unc = NULL;   /* per tile-list entry: uncertain */
+        double* pamb = NULL;   /* per tile-list entry: bound at ambiguous pixels */
         int part_cap = 0;
 #pragma omp for schedule(dynamic, 1)
         for (int ti = 0; ti < nt; ++ti) {
@@ -316,12 +324,12 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
             if (L <= 0) continue;
             if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
             if (L > part_cap) {
-                free(part); free(unc); part_cap = L;
+                free(part); free(pamb); part_cap = L;
                 part = (double*)malloc(sizeof(double) * part_cap);
-                unc = (uint8_t*)malloc(part_cap);
+                pamb = (double*)malloc(sizeof(double) * part_cap);
             }
             memset(part, 0, sizeof(double) * L);
-            memset(unc, 0, L);
+            memset(pamb, 0, sizeof(double) * L);
             for (int ly = 0; ly < TILE; ++ly) {
                 int y = ty * TILE + ly;
                 if (y >= H) break;
@@ -329,24 +337,31 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
                     int x = tx * TILE + lx;
                     if (x >= W) break;
                     double T, C[3];
-                    int32_t nc;
+                    int32_t nc, kamb;
                     int a;
                     double px = x + 0.5, py = y + 0.5;
-                    int cnt = walk_pixel(&s, ids, start, end, px, py, buf, cap, &T, &nc, C, &a);
+                    int cnt = walk_pixel(&s, ids, start, end, px, py, buf, cap, &T, &nc, C, &a, &kamb);
                     for (int e = 0; e < cnt; ++e) {
                         double w = buf[e].alpha * buf[e].T;
                         double* o = part + (buf[e].k - start);
                         if (w > *o) *o = w;
                     }
                     if (!a) continue;
+                    double Tw = 1.0;  /* this walk's T, continued past its stop */
                     for (int32_t k = start; k < end; ++k) {
                         int32_t i = ids[k];
                         double dx = px - s.means[2 * i], dy = py - s.means[2 * i + 1];
                         double ca = s.conics[3 * i], cb = s.conics[3 * i + 1], cc = s.conics[3 * i + 2];
                         double sigma = -0.5 * (ca * dx * dx + cc * dy * dy) - cb * dx * dy;
                         double ah = s.opac[i] * exp(sigma);
+                        double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;
                         double ea = alpha_rel_bound(ca, cb, cc, dx, dy, sigma);
-                        if (ah >= ALPHA_MIN * (1.0 - ea) - 2.0 * U32 * ALPHA_MIN) unc[k - start] = 1;
+                        if (k >= kamb && ah >= ALPHA_MIN * (1.0 - ea) - 2.0 * U32 * ALPHA_MIN) {
+                            double wb = 1.01 * alpha * Tw;
+                            double* o = pamb + (k - start);
+                            if (wb > *o) *o = wb;
+                        }
+                        if (alpha >= ALPHA_MIN) Tw *= 1.0 - alpha;
                     }
                 }
             }
@@ -355,13 +370,13 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
                 for (int k = 0; k < L; ++k) {
                     int32_t i = ids[start + k];
                     if (part[k] > max_w[i]) max_w[i] = part[k];
-                    if (unc[k]) uncertain[i] = 1;
+                    if (pamb[k] > max_w_amb[i]) max_w_amb[i] = pamb[k];
                 }
             }
         }
         free(buf);
         free(part);
-        free(unc);
+        free(pamb);
     }
     return threads_used();
 }

@@ -47,7 +47,7 @@ def test_workspace_size_grows_with_capacity():
 
 def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None, ws=256, wsb=1 << 20):
     p = ctypes.c_void_p(ptr)
-    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, ctypes.c_void_p(ws), wsb, None)
+    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, nul, ctypes.c_void_p(ws), wsb, None)
 
 
 def test_fwd_rejects_bad_arguments():

@@ -8,7 +8,11 @@ Bars:
     of its threshold, so that both outcomes are correct);
   * backward: each gradient field within 1e-4 * max|oracle field|, with
     dL/dImage zeroed at the flagged pixels in both inputs, so that no gradient
-    depends on a decision that may legitimately flip.
+    depends on a decision that may legitimately flip;
+  * max weight (the forward's optional per-splat max of alpha T): within
+    1e-5 absolute for every splat that no flagged pixel could composite (the
+    others: in [0, 0.99]); the forward's other outputs bit-identical with
+    and without it.
 """
 import math
 
@@ -24,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 IMG_TOL = 1e-5
 T_TOL = 1e-5
+MAXW_TOL = 1e-5
 GRAD_REL = 1e-4
 MAX_AMBIG = 5e-3   # fraction of pixels the oracle may flag
 
@@ -43,10 +48,26 @@ def gpu_bins(sc):
     return gsr.gs_bin_tiles(_dev(sc.means2d), _dev(sc.radii), _dev(sc.depths), sc.width, sc.height)
 
 
-def gpu_fwd(sc, bins, bg=True):
+def gpu_fwd(sc, bins, bg=True, max_weight=False):
     return gsr.gs_rasterize_fwd(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
                                 _dev(sc.background) if bg else None, sc.width, sc.height,
-                                bins.tile_ranges, bins.sorted_ids)
+                                bins.tile_ranges, bins.sorted_ids, max_weight=max_weight)
+
+
+def check_max_weight(sc, bins, ids_o, rng_o, img, T, nc):
+    """The forward with the max-weight output: the same image, final_T and
+    n_contrib as without it, and the per-splat max against the oracle."""
+    img2, T2, nc2, mw = gpu_fwd(sc, bins, max_weight=True)
+    torch.cuda.synchronize()
+    assert torch.equal(img2, img) and torch.equal(T2, T) and torch.equal(nc2, nc)
+    mw_o, unc = oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                                  sc.width, sc.height, rng_o, ids_o)
+    mw = mw.cpu().numpy().astype(np.float64)
+    err = np.abs(mw - mw_o)[~unc].max(initial=0.0)
+    assert err <= MAXW_TOL, err
+    assert np.all(mw >= 0.0) and np.all(mw <= 0.99 + 1e-6)
+    assert unc.mean() <= 0.01, unc.mean()
+    return err, int(unc.sum())
 
 
 def gpu_bwd(sc, bins, final_T, n_contrib, g, accum_weight=False):
@@ -77,6 +98,8 @@ def check_scene(sc, accum_weight=None, runs=1):
     _say("forward")
     img, T, nc = gpu_fwd(sc, bins)
     torch.cuda.synchronize()
+    _say("max weight")
+    err_mw, n_unc = check_max_weight(sc, bins, ids_o, rng_o, img, T, nc)
     fo = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
                               sc.width, sc.height, rng_o, ids_o)
     amb = fo["ambiguous"]
@@ -119,7 +142,8 @@ def check_scene(sc, accum_weight=None, runs=1):
             err = np.abs(res[gk] - ref).max(initial=0.0)
             errs[gk] = err / scale if scale > 0 else err
             assert err <= GRAD_REL * max(scale, 1e-30), (gk, err, scale)
-    _say("max rel err", {k: f"{v:.2e}" for k, v in errs.items()}, f"img {err_img:.2e} T {err_T:.2e}")
+    _say("max rel err", {k: f"{v:.2e}" for k, v in errs.items()}, f"img {err_img:.2e} T {err_T:.2e}",
+         f"max weight {err_mw:.2e} ({n_unc} uncertain splats)")
     return bins, results
 
 
