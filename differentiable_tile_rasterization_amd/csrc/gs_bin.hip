@@ -35,6 +35,8 @@ constexpr int kSortRounds = 16;                       // rounds of 256 keys per 
 constexpr int kSortTile = kSortThreads * kSortRounds; // 4096 keys per workgroup
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
+static_assert(kSortThreads == kRadix && kSortThreads == 4 * kWave && kSortTile == 4 * kSortRounds * kWave,
+              "radix sort tiling: one thread per digit, four waves each holding a quarter of the tile");
 
 __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float depth, int GX, int GY,
                                            int& tx0, int& tx1, int& ty0, int& ty1)
@@ -257,11 +259,18 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __res
 }
 
 // Scatter of one pass. The workgroup's keys are first ranked stably by digit
-// (per round: 8 ballots give each lane its rank among the wave's lanes with
-// the same digit; waves and rounds are ordered by running counts) and placed
-// in LDS in digit order; the tile is then written out from LDS, so that
-// consecutive threads store consecutive addresses inside each digit's run
-// instead of one key at a time into up to 256 different runs.
+// and placed in LDS in digit order; the tile is then written out from LDS, so
+// that consecutive threads store consecutive addresses inside each digit's
+// run instead of one key at a time into up to 256 different runs.
+// Ranking: wave w holds the tile's keys 1024 w .. 1024 w + 1023, 64 per round
+// (round r: keys 1024 w + 64 r + lane). Within a round, 8 ballots give each
+// lane its rank among the wave's lanes with the same digit; a per-wave running
+// count per digit (read by those lanes, then advanced by the first of them:
+// LDS operations of one wave take effect in order) carries the rank across
+// the wave's rounds, with no workgroup barrier. After the rounds, each digit's
+// block-local start and each wave's offset inside it come from one scan; as
+// the waves hold consecutive quarters of the tile, wave order then round
+// order is the tile's order: the placement is stable.
 template <typename K>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __restrict__ keys_in,
                                                                      const int* __restrict__ vals_in, long long n,
@@ -270,11 +279,10 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
                                                                      K* __restrict__ keys_out,
                                                                      int* __restrict__ vals_out)
 {
-    __shared__ unsigned wave_cnt[4][kRadix];  // keys of digit d in wave w, this round
-    __shared__ unsigned wave_off[4][kRadix];  // where wave w's keys of digit d go (block-local)
-    __shared__ unsigned running[kRadix];      // block-local position of digit d's next key
+    __shared__ unsigned wave_run[4][kRadix];  // per wave: keys of digit d ranked so far, then its offset
     __shared__ unsigned local_start[kRadix];  // block-local start of digit d
     __shared__ unsigned global_off[kRadix];
+    __shared__ unsigned scan_part[4];
     __shared__ K lkey[kSortTile];
     __shared__ int lval[kSortTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -283,47 +291,26 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     const int td = threadIdx.x;  // kSortThreads == kRadix: thread td looks after digit td
     K key[kSortRounds];
     int val[kSortRounds];
-    local_start[td] = 0;
-    for (int k = 0; k < 4; ++k) wave_cnt[k][td] = 0;
+    unsigned rk[kSortRounds];  // rank among the wave's keys of the same digit
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wave_run[w][64 * k + lane] = 0u;  // each wave clears its own row
     global_off[td] = offs[(long long)td * nwg + blockIdx.x];
-    __syncthreads();
+    const int wbase = w * (kSortTile / 4);  // this wave's quarter of the tile
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
-        const int li = r * kSortThreads + threadIdx.x;
+        const int li = wbase + r * kWave + lane;
         key[r] = 0;
         val[r] = 0;
         if (li < cnt) {
             key[r] = keys_in[base + li];
             val[r] = vals_in[base + li];
-            atomicAdd(&local_start[(unsigned)(key[r] >> shift) & (kRadix - 1)], 1u);
         }
     }
-    __syncthreads();
-    if (threadIdx.x < kWave) {  // exclusive scan of the 256 digit counts, 4 per lane
-        const int l = threadIdx.x;
-        const unsigned h0 = local_start[4 * l], h1 = local_start[4 * l + 1], h2 = local_start[4 * l + 2],
-                       h3 = local_start[4 * l + 3];
-        unsigned incl = h0 + h1 + h2 + h3;
-        for (int dl = 1; dl < kWave; dl <<= 1) {
-            const unsigned u = __shfl_up(incl, dl, kWave);
-            if (l >= dl) incl += u;
-        }
-        const unsigned ex = incl - (h0 + h1 + h2 + h3);
-        local_start[4 * l] = ex;
-        local_start[4 * l + 1] = ex + h0;
-        local_start[4 * l + 2] = ex + h0 + h1;
-        local_start[4 * l + 3] = ex + h0 + h1 + h2;
-    }
-    __syncthreads();
-    running[td] = local_start[td];
-    __syncthreads();
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
-        const int li = r * kSortThreads + threadIdx.x;
-        const bool valid = li < cnt;
+        const bool valid = wbase + r * kWave + lane < cnt;
         const unsigned d = valid ? (unsigned)(key[r] >> shift) & (kRadix - 1) : 0u;
-        // lanes of this wave holding the same digit (8 ballots)
         unsigned long long peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
@@ -332,21 +319,36 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
             peers &= bit ? bal : ~bal;
         }
         const unsigned rank = (unsigned)__popcll(peers & lt_mask);
-        if (valid && rank == 0) wave_cnt[w][d] = (unsigned)__popcll(peers);
-        __syncthreads();
-        {
-            unsigned run = running[td];
+        const unsigned before = valid ? wave_run[w][d] : 0u;
+        rk[r] = before + rank;
+        if (valid && rank == 0) wave_run[w][d] = before + (unsigned)__popcll(peers);
+    }
+    __syncthreads();
+    // digit td: its count over the tile, the exclusive scan of the counts over
+    // the digits, and each wave's offset inside the digit's run
+    const unsigned c0 = wave_run[0][td], c1 = wave_run[1][td], c2 = wave_run[2][td], c3 = wave_run[3][td];
+    const unsigned tot = c0 + c1 + c2 + c3;
+    unsigned incl = tot;
+    for (int dl = 1; dl < kWave; dl <<= 1) {
+        const unsigned u = __shfl_up(incl, dl, kWave);
+        if (lane >= dl) incl += u;
+    }
+    if (lane == kWave - 1) scan_part[w] = incl;
+    __syncthreads();
+    unsigned before_w = 0;
+    for (int k = 0; k < w; ++k) before_w += scan_part[k];
+    const unsigned start = before_w + incl - tot;
+    local_start[td] = start;
+    wave_run[0][td] = start;
+    wave_run[1][td] = start + c0;
+    wave_run[2][td] = start + c0 + c1;
+    wave_run[3][td] = start + c0 + c1 + c2;
+    __syncthreads();
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                wave_off[k][td] = run;
-                run += wave_cnt[k][td];
-                wave_cnt[k][td] = 0;
-            }
-            running[td] = run;
-        }
-        __syncthreads();
-        if (valid) {
-            const unsigned lp = wave_off[w][d] + rank;
+    for (int r = 0; r < kSortRounds; ++r) {
+        if (wbase + r * kWave + lane < cnt) {
+            const unsigned d = (unsigned)(key[r] >> shift) & (kRadix - 1);
+            const unsigned lp = wave_run[w][d] + rk[r];
             lkey[lp] = key[r];
             lval[lp] = val[r];
         }
@@ -365,14 +367,33 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     }
 }
 
+// Tile ranges from the boundaries of the sorted tile keys. Thread i takes keys
+// 4 i .. 4 i + 3 (one 16-byte load) and their two neighbours.
 __global__ __launch_bounds__(256) void ranges_kernel(const unsigned* __restrict__ keys, long long n,
                                                      int2* __restrict__ ranges)
 {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int t = (int)keys[i];
-    if (i == 0 || (int)keys[i - 1] != t) ranges[t].x = (int)i;
-    if (i == n - 1 || (int)keys[i + 1] != t) ranges[t].y = (int)(i + 1);
+    const long long i0 = 4 * ((long long)blockIdx.x * blockDim.x + threadIdx.x);
+    if (i0 >= n) return;
+    int k[4];
+    if (i0 + 4 <= n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + i0);  // keys are 256-byte aligned
+        k[0] = (int)v.x; k[1] = (int)v.y; k[2] = (int)v.z; k[3] = (int)v.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) k[j] = i0 + j < n ? (int)keys[i0 + j] : -1;
+    }
+    int prev = i0 > 0 ? (int)keys[i0 - 1] : -1;
+    const int next = i0 + 4 < n ? (int)keys[i0 + 4] : -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const long long i = i0 + j;
+        if (i >= n) break;
+        const int t = k[j];
+        if (t != prev) ranges[t].x = (int)i;
+        const int nx = j < 3 && i + 1 < n ? k[j + 1] : (j < 3 ? -1 : next);
+        if (nx != t) ranges[t].y = (int)(i + 1);
+        prev = t;
+    }
 }
 
 // splat_offsets[i] = first slot of splat i's (splat, tile) pairs, [n] = total.
@@ -388,8 +409,8 @@ __global__ __launch_bounds__(256) void offsets_kernel(int n, const unsigned long
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BinLayout {
-    size_t counts, rects, offsets, part, total, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted, cnt_sorted,
-        emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
+    size_t counts, rects, offsets, part, total, pairs, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted,
+        cnt_sorted, emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
 };
 
 BinLayout bin_layout(long long n, long long cap)
@@ -406,6 +427,7 @@ BinLayout bin_layout(long long n, long long cap)
     L.offsets = o;    o += align256(sizeof(unsigned long long) * n1);
     L.part = o;       o += align256(sizeof(unsigned long long) * (size_t)nparts);
     L.total = o;      o += align256(sizeof(unsigned long long));
+    L.pairs = o;      o += align256(sizeof(unsigned long long));  // the pair count, kept apart from the scans' totals
     L.dkeys_a = o;    o += align256(sizeof(unsigned) * n1);
     L.dkeys_b = o;    o += align256(sizeof(unsigned) * n1);
     L.dvals_a = o;    o += align256(sizeof(int) * n1);
@@ -456,6 +478,39 @@ extern "C" size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32
     return bin_layout(n, capacity).bytes;
 }
 
+namespace gs {
+namespace {
+
+// One small pinned host buffer per calling thread, for the pair count's
+// readback (allocated on the thread's first call, kept until the process ends;
+// pinned, so that the copy is asynchronous). nullptr if it cannot be had.
+unsigned long long* pinned_count()
+{
+    thread_local unsigned long long* p = nullptr;
+    if (!p) {
+        void* q = nullptr;
+        if (hipHostMalloc(&q, 64, hipHostMallocPortable) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        p = static_cast<unsigned long long*>(q);
+    }
+    return p;
+}
+
+struct CountEvent {  // destroyed on every return path
+    hipEvent_t e = nullptr;
+    ~CountEvent()
+    {
+        if (e) (void)hipEventDestroy(e);
+    }
+};
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
 extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
                                   int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
                                   int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect,
@@ -485,14 +540,55 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     auto* total = (unsigned long long*)(ws + L.total);
     auto* rects = (ushort4*)(ws + L.rects);
 
+    auto* pairs = (unsigned long long*)(ws + L.pairs);
+    auto* dka = (unsigned*)(ws + L.dkeys_a);
+    auto* dkb = (unsigned*)(ws + L.dkeys_b);
+    auto* dva = (int*)(ws + L.dvals_a);
+    auto* dvb = (int*)(ws + L.dvals_b);
+    auto* hist = (unsigned*)(ws + L.hist);
+    auto* rect_sorted = (ushort4*)(ws + L.rect_sorted);
+    auto* cnt_sorted = (unsigned long long*)(ws + L.cnt_sorted);
+    auto* emit_off = (unsigned long long*)(ws + L.emit_off);
+    const int* by_depth = dva;
+
+    // The pair count is read back with an asynchronous copy into pinned host
+    // memory, and everything that does not need it (the splats' depth sort
+    // and their rectangles in depth order; workspace only) is enqueued before
+    // the host waits for that copy: the GPU stays busy while the host waits
+    // and then enqueues the pair stages behind the depth sort.
     unsigned long long h_total = 0;
     if (n > 0) {
         count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, counts,
                                                       rects);
         GS_HIP(hipGetLastError());
-        GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(counts, offsets, n, part, total, st)));
-        GS_HIP(hipMemcpyAsync(&h_total, total, sizeof(h_total), hipMemcpyDeviceToHost, st));
-        GS_HIP(hipStreamSynchronize(st));
+        GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(counts, offsets, n, part, pairs, st)));
+        unsigned long long* pin = pinned_count();
+        CountEvent ev;
+        if (pin) {
+            GS_HIP(hipMemcpyAsync(pin, pairs, sizeof(*pin), hipMemcpyDeviceToHost, st));
+            GS_HIP(hipEventCreateWithFlags(&ev.e, hipEventDisableTiming));
+            GS_HIP(hipEventRecord(ev.e, st));
+        } else {  // no pinned buffer: a plain synchronous read
+            GS_HIP(hipMemcpyAsync(&h_total, pairs, sizeof(h_total), hipMemcpyDeviceToHost, st));
+            GS_HIP(hipStreamSynchronize(st));
+        }
+        // Splats in depth order: stable sort of (depth bits, id), ids starting in id order.
+        depth_keys_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, depths, dka, dva);
+        GS_HIP(hipGetLastError());
+        for (int shift = 0; shift < 32; shift += kRadixBits) {
+            GS_HIP(radix_pass<unsigned>(dka, dva, dkb, dvb, n, shift, hist, part, total, st));
+            unsigned* tk = dka; dka = dkb; dkb = tk;
+            int* tv = dva; dva = dvb; dvb = tv;
+        }
+        by_depth = dva;  // four passes: back in the first buffers
+        // Emission offsets in depth order.
+        gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
+        GS_HIP(hipGetLastError());
+        GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(cnt_sorted, emit_off, n, part, total, st)));
+        if (pin) {
+            GS_HIP(hipEventSynchronize(ev.e));
+            h_total = *pin;
+        }
     }
     *n_isect = (int64_t)h_total;
     if (h_total > 0x7fffffffull) {
@@ -506,35 +602,12 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     const long long I = (long long)h_total;
     GS_HIP(hipMemsetAsync(tile_ranges, 0, sizeof(int) * 2 * (size_t)tiles, st));
     if (n > 0) {
-        offsets_kernel<<<(n + 1 + 255) / 256, 256, 0, st>>>(n, offsets, total, splat_offsets);
+        offsets_kernel<<<(n + 1 + 255) / 256, 256, 0, st>>>(n, offsets, pairs, splat_offsets);
         GS_HIP(hipGetLastError());
     } else {
         GS_HIP(hipMemsetAsync(splat_offsets, 0, sizeof(int), st));
     }
     if (I == 0) return GS_OK;
-
-    // Splats in depth order: stable sort of (depth bits, id), ids starting in id order.
-    auto* dka = (unsigned*)(ws + L.dkeys_a);
-    auto* dkb = (unsigned*)(ws + L.dkeys_b);
-    auto* dva = (int*)(ws + L.dvals_a);
-    auto* dvb = (int*)(ws + L.dvals_b);
-    auto* hist = (unsigned*)(ws + L.hist);
-    depth_keys_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, depths, dka, dva);
-    GS_HIP(hipGetLastError());
-    for (int shift = 0; shift < 32; shift += kRadixBits) {
-        GS_HIP(radix_pass<unsigned>(dka, dva, dkb, dvb, n, shift, hist, part, total, st));
-        unsigned* tk = dka; dka = dkb; dkb = tk;
-        int* tv = dva; dva = dvb; dvb = tv;
-    }
-    const int* by_depth = dva;  // four passes: back in the first buffers
-
-    // Emission offsets in depth order.
-    auto* rect_sorted = (ushort4*)(ws + L.rect_sorted);
-    auto* cnt_sorted = (unsigned long long*)(ws + L.cnt_sorted);
-    auto* emit_off = (unsigned long long*)(ws + L.emit_off);
-    gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
-    GS_HIP(hipGetLastError());
-    GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(cnt_sorted, emit_off, n, part, total, st)));
 
     // Tile passes, ping-ponged so that the last one writes its values into sorted_ids.
     const int tb = bits_for(tiles);
@@ -553,7 +626,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         unsigned* tk = kin; kin = kout; kout = tk;
         int* tv = vin; vin = vout; vout = tv;
     }
-    ranges_kernel<<<(unsigned)((I + 255) / 256), 256, 0, st>>>(kin, I, (int2*)tile_ranges);
+    ranges_kernel<<<(unsigned)((I + 1023) / 1024), 256, 0, st>>>(kin, I, (int2*)tile_ranges);
     GS_HIP(hipGetLastError());
     return GS_OK;
 }

@@ -131,8 +131,11 @@ int gs_version(void);
  *   workspace    device scratch of at least gs_bin_tiles_workspace_size(...)
  *                bytes, 256-byte aligned
  *
- * Synchronises `stream` once (to read the count). If capacity < *n_isect it
- * returns GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges /
+ * Waits once on the host for the pair count (an asynchronous copy into a
+ * small pinned host buffer that each calling thread keeps from its first
+ * call; the stages that do not need the count are enqueued before the wait,
+ * so the GPU does not idle meanwhile). If capacity < *n_isect it returns
+ * GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges /
  * splat_offsets untouched: allocate *n_isect slots (and the matching
  * workspace) and call again. Totals above 2^31 - 1 return GS_ERR_UNSUPPORTED.
  */
