@@ -89,35 +89,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const T* __re
     if (threadIdx.x == 0) part[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-// One workgroup: exclusive scan of part[0..m) in place; grand total to *total.
-__global__ __launch_bounds__(kScanThreads) void scan_parts_kernel(unsigned long long* __restrict__ part, int m,
-                                                                  unsigned long long* __restrict__ total)
-{
-    __shared__ unsigned long long buf[kScanThreads];
-    __shared__ unsigned long long carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < m; base += kScanThreads) {
-        const int i = base + threadIdx.x;
-        const unsigned long long v = i < m ? part[i] : 0ull;
-        buf[threadIdx.x] = v;
-        __syncthreads();
-        for (int off = 1; off < kScanThreads; off <<= 1) {
-            const unsigned long long t = threadIdx.x >= off ? buf[threadIdx.x - off] : 0ull;
-            __syncthreads();
-            buf[threadIdx.x] += t;
-            __syncthreads();
-        }
-        const unsigned long long incl = buf[threadIdx.x];
-        const unsigned long long c = carry;
-        if (i < m) part[i] = c + incl - v;
-        __syncthreads();
-        if (threadIdx.x == kScanThreads - 1) carry = c + incl;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0 && total) *total = carry;
-}
-
 // Workgroup-wide inclusive scan of one value per thread (256 threads).
 __device__ __forceinline__ unsigned long long block_incl_scan(unsigned long long v, unsigned long long* wsum)
 {
@@ -133,12 +104,25 @@ __device__ __forceinline__ unsigned long long block_incl_scan(unsigned long long
     return v + pre;
 }
 
+// Second kernel of the scan: workgroup b first sums the per-workgroup totals
+// part[0..b) itself (a few thousand at most, so this costs less than a
+// separate scan of them would cost in launch latency), then scans its tile;
+// the last workgroup also writes the grand total to *total (if not null).
 template <typename TI, typename TO>
 __global__ __launch_bounds__(kScanThreads) void scan_down_kernel(const TI* __restrict__ in, TO* __restrict__ out,
                                                                  long long n,
-                                                                 const unsigned long long* __restrict__ part)
+                                                                 const unsigned long long* __restrict__ part,
+                                                                 int m, unsigned long long* __restrict__ total)
 {
     __shared__ unsigned long long wsum[kScanThreads / kWave];
+    __shared__ unsigned long long red[kScanThreads / kWave];
+    unsigned long long pre = 0;
+    for (int k = threadIdx.x; k < (int)blockIdx.x; k += kScanThreads) pre += part[k];
+    for (int off = 32; off > 0; off >>= 1) pre += __shfl_xor(pre, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = pre;
+    __syncthreads();
+    pre = red[0] + red[1] + red[2] + red[3];
+    if (total && threadIdx.x == 0 && (int)blockIdx.x == m - 1) *total = pre + part[blockIdx.x];
     // Blocked arrangement: thread t owns items [t*16, t*16+16) of the tile.
     const long long base = (long long)blockIdx.x * kScanTile + (long long)threadIdx.x * kScanItems;
     unsigned long long v[kScanItems];
@@ -150,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_down_kernel(const TI* __res
         s += v[k];
     }
     const unsigned long long incl = block_incl_scan(s, wsum);
-    unsigned long long run = part[blockIdx.x] + incl - s;
+    unsigned long long run = pre + incl - s;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const long long idx = base + k;
@@ -166,25 +150,13 @@ hipError_t exclusive_scan(const TI* in, TO* out, long long n, unsigned long long
     const int m = (int)((n + kScanTile - 1) / kScanTile);
     if (m == 0) return hipMemsetAsync(total, 0, sizeof(unsigned long long), st);
     scan_reduce_kernel<TI><<<m, kScanThreads, 0, st>>>(in, n, part);
-    scan_parts_kernel<<<1, kScanThreads, 0, st>>>(part, m, total);
-    scan_down_kernel<TI, TO><<<m, kScanThreads, 0, st>>>(in, out, n, part);
+    scan_down_kernel<TI, TO><<<m, kScanThreads, 0, st>>>(in, out, n, part, m, total);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Depth order and emission.
 // ---------------------------------------------------------------------------
-// keys = depth bit patterns, vals = splat ids (the depth sort's input).
-__global__ __launch_bounds__(256) void depth_keys_kernel(int n, const float* __restrict__ depths,
-                                                         unsigned* __restrict__ keys, int* __restrict__ vals)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    keys[i] = __float_as_uint(depths[i]);
-    vals[i] = i;
-}
-
-// Depth rank k: the rectangle and tile count of its splat.
 __global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __restrict__ by_depth,
                                                            const ushort4* __restrict__ rects,
                                                            ushort4* __restrict__ rect_sorted,
@@ -303,7 +275,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
         val[r] = 0;
         if (li < cnt) {
             key[r] = keys_in[base + li];
-            val[r] = vals_in[base + li];
+            val[r] = vals_in ? vals_in[base + li] : (int)(base + li);  // no values: the index
         }
     }
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
@@ -396,14 +368,17 @@ __global__ __launch_bounds__(256) void ranges_kernel(const unsigned* __restrict_
     }
 }
 
-// splat_offsets[i] = first slot of splat i's (splat, tile) pairs, [n] = total.
-__global__ __launch_bounds__(256) void offsets_kernel(int n, const unsigned long long* __restrict__ offsets,
-                                                      const unsigned long long* __restrict__ total,
-                                                      int* __restrict__ splat_offsets)
+// After the count check: splat_offsets[i] = first slot of splat i's (splat,
+// tile) pairs, [n] = the pair count (0 without splats); tile_ranges cleared
+// (the ranges pass fills the non-empty tiles).
+__global__ __launch_bounds__(256) void outputs_kernel(int n, int tiles, const unsigned long long* __restrict__ offsets,
+                                                      const unsigned long long* __restrict__ pairs,
+                                                      int* __restrict__ splat_offsets, int* __restrict__ tile_ranges)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) splat_offsets[i] = (int)offsets[i];
-    if (i == n) splat_offsets[n] = (int)*total;
+    if (i == n) splat_offsets[n] = pairs ? (int)*pairs : 0;
+    if (i < 2ll * tiles) tile_ranges[i] = 0;
 }
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -572,15 +547,20 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
             GS_HIP(hipMemcpyAsync(&h_total, pairs, sizeof(h_total), hipMemcpyDeviceToHost, st));
             GS_HIP(hipStreamSynchronize(st));
         }
-        // Splats in depth order: stable sort of (depth bits, id), ids starting in id order.
-        depth_keys_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, depths, dka, dva);
-        GS_HIP(hipGetLastError());
+        // Splats in depth order: stable sort of (depth bits, id). The first
+        // pass reads the depths' bit patterns in place, with the index as id.
+        const unsigned* dk_in = reinterpret_cast<const unsigned*>(depths);
+        const int* dv_in = nullptr;
+        unsigned* dk_out = dkb;
+        int* dv_out = dvb;
         for (int shift = 0; shift < 32; shift += kRadixBits) {
-            GS_HIP(radix_pass<unsigned>(dka, dva, dkb, dvb, n, shift, hist, part, total, st));
-            unsigned* tk = dka; dka = dkb; dkb = tk;
-            int* tv = dva; dva = dvb; dvb = tv;
+            GS_HIP(radix_pass<unsigned>(dk_in, dv_in, dk_out, dv_out, n, shift, hist, part, total, st));
+            dk_in = dk_out;
+            dv_in = dv_out;
+            dk_out = dk_out == dkb ? dka : dkb;
+            dv_out = dv_out == dvb ? dva : dvb;
         }
-        by_depth = dva;  // four passes: back in the first buffers
+        by_depth = dv_in;
         // Emission offsets in depth order.
         gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
         GS_HIP(hipGetLastError());
@@ -600,12 +580,11 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         return GS_ERR_CAPACITY;
     }
     const long long I = (long long)h_total;
-    GS_HIP(hipMemsetAsync(tile_ranges, 0, sizeof(int) * 2 * (size_t)tiles, st));
-    if (n > 0) {
-        offsets_kernel<<<(n + 1 + 255) / 256, 256, 0, st>>>(n, offsets, pairs, splat_offsets);
+    {
+        const long long cover = (long long)n + 1 > 2ll * tiles ? (long long)n + 1 : 2ll * tiles;
+        outputs_kernel<<<(unsigned)((cover + 255) / 256), 256, 0, st>>>(n, tiles, offsets, n > 0 ? pairs : nullptr,
+                                                                        splat_offsets, tile_ranges);
         GS_HIP(hipGetLastError());
-    } else {
-        GS_HIP(hipMemsetAsync(splat_offsets, 0, sizeof(int), st));
     }
     if (I == 0) return GS_OK;
 
