@@ -242,7 +242,9 @@ def main():
         roof = {"bound": "hbm", "achieved": hbm_bytes / t_walk / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
-    roof["kernel"] = "bwd_kernel (reverse walk)"
+    # the library's choice of reverse walk (more than 16 tiles per splat: stored partials)
+    roof["kernel"] = ("bwd_store_kernel (reverse walk, stored partials)" if bins.n_isect > 16 * sc.n
+                      else "bwd_kernel (reverse walk, LDS adds)")
     roof["kernel_ms"] = stage_mean["walk"]
     roof["terms_ms"] = terms
     roof["call_frac"] = terms[bound + "_ms"] / ms  # the same work against the whole call's time

@@ -156,10 +156,12 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
 
 def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, width: int, height: int, bins: Bins,
                      final_T, n_contrib, dL_dimage, accum_weight: bool = False, out=None, workspace=None,
-                     stream=None, events=None):
+                     stream=None, events=None, walk=None):
     """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
     dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
-    per-splat accumulated weight [n]. ``out`` may pass preallocated outputs
+    per-splat accumulated weight [n]. ``walk``: None (the library chooses by
+    the mean tiles per splat), "add" or "store" (GS_FLAG_WALK_ADD /
+    GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
     (same dict keys) and ``workspace`` a uint8 device buffer of at least
     gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
     allocation out of timed loops. ``events``: four torch.cuda.Event objects
@@ -192,6 +194,10 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
+    if walk is not None:
+        if walk not in ("add", "store"):
+            raise ValueError(f"walk: None, 'add' or 'store', not {walk!r}")
+        flags |= _lib.GS_FLAG_WALK_ADD if walk == "add" else _lib.GS_FLAG_WALK_STORE
     args = (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
             height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
             _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),

@@ -183,32 +183,430 @@ __device__ __forceinline__ void half_hits(const SplatRec& r, float ox, float oy,
     }
 }
 
+// LDS slot of one staged entry: its alpha coefficients and colour, and its
+// position in each half's list. One base address serves every record read of
+// a walk step (the lists hold slot byte offsets).
+struct StoreSlot {
+    float4 a;                      // mean x, mean y, l11, l21 (scaled factor)
+    float4 b;                      // l22, log2(opacity), red, green
+    float c;                       // blue
+    unsigned char pos[kHalves];    // list position in each half, 0xff: not in that list
+    int slot;                      // the entry's (splat, tile) pair slot, -1: nothing to flush
+};
+static_assert(sizeof(StoreSlot) == 48 && offsetof(StoreSlot, pos) == 36, "StoreSlot layout");
+
+constexpr int kBatch = kBlock - 1;                                    // entries staged per batch, at most
+constexpr int kDummy = kBlock - 1;                                    // slot of the dummy entry
+constexpr unsigned short kDummyOff = (unsigned short)(kDummy * sizeof(StoreSlot));
+constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummies read ahead of use
+
+// Partial sums: one record of kRaw (or kRaw - 1 without the weight) floats per
+// (half, list position) walked in a batch, written once with plain stores.
+// Half q's records start at the sum of the lengths of the lists before it. A
+// batch keeps as many of its candidate entries (from the top: the walk runs
+// backwards) as fit: on the 2M-splat scene a 255-entry batch holds a median
+// of about 340 half-list entries.
+template <bool AW> struct BwdParts {
+    static constexpr int kF = AW ? kRaw : kRaw - 1;  // floats per record
+    static constexpr int kCap = AW ? 248 : 276;      // records per batch (at most 26 KB of LDS in all: six workgroups per CU)
+};
+
+// Per-half lists of the staged slots whose hit bit is set, as slot byte
+// offsets in descending slot order (the walk's order); each listed entry's
+// position is also written into its own slot's pos bytes. The same exchange of
+// per-wave counts also ORs `flag` over the workgroup, which is returned, and
+// gives every half's list length (len, wave-uniform). Ends with a barrier.
+__device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bool flag, StoreSlot* S,
+                                                 unsigned short (*list)[kListLen], int (*cnt)[kHalves + 1],
+                                                 int (&len)[kHalves])
+{
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int mine = __ballot(flag) != 0 ? 1 : 0;  // lane kHalves: the wave's flag
+#pragma unroll
+    for (int q = 0; q < kHalves; ++q) {
+        const int c = __popcll(__ballot(hit[q]));  // whole-wave ballot, outside any lane branch
+        mine = lane == q ? c : mine;
+    }
+    if (lane <= kHalves) cnt[wv][lane] = mine;
+    __syncthreads();
+    const bool any_flag = (cnt[0][kHalves] | cnt[1][kHalves] | cnt[2][kHalves] | cnt[3][kHalves]) != 0;
+    // lane q: list position of this wave's lowest hit of half q, counted from
+    // the front (slots of higher waves come first)
+    int top = 0, tot = 0;
+    if (lane < kHalves) {
+        int below = 0;
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const int c = cnt[w2][lane];
+            tot += c;
+            below += w2 < wv ? c : 0;
+        }
+        top = tot - 1 - below;
+    }
+    *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(0xffffffffu, 0xffffffffu);
+#pragma unroll
+    for (int q = 0; q < kHalves; ++q) {
+        len[q] = __builtin_amdgcn_readlane(tot, q);
+        const unsigned long long bal = __ballot(hit[q]);
+        if (hit[q]) {
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+            const int at = __builtin_amdgcn_readlane(top, q) - rank;
+            list[q][at] = (unsigned short)(threadIdx.x * sizeof(StoreSlot));
+            S[threadIdx.x].pos[q] = (unsigned char)at;  // after the 0xff fill: the same thread, in order
+        }
+    }
+    __syncthreads();
+    return any_flag;
+}
+
+// Six waves per SIMD: the LDS allows six workgroups per CU, and the walk's
+// registers fit 80 VGPRs.
+template <bool AW>
+__global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
+    int W, int H, int GX, int GY, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
+    const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
+    unsigned char* __restrict__ slot_used)
+{
+    using PP = BwdParts<AW>;
+    constexpr int kF = PP::kF, kCap = PP::kCap;
+    __shared__ StoreSlot S[kBlock];
+    __shared__ float parts[kCap * kF];
+    __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
+    __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
+    __shared__ int half_end[kHalves];
+    __shared__ int half_base[kHalves];                 // first partial record of each half, for the flush
+    __shared__ int wave_hits[4];                       // half-list entries of each wave's candidates
+    __shared__ int cut;                                // lowest kept candidate of the batch
+
+    const int tile = order ? order[blockIdx.x] : xcd_tile(blockIdx.x, tiles);
+    if (tile < 0 || tile >= tiles) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int half = lane >> 5, hq = 2 * wv + half;
+    int x, y;
+    quadrant_pixel(tile, GX, x, y);
+    const bool inside = x < W && y < H;
+    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
+    const int2 rg = ranges[tile];
+
+    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    int nc = 0;
+    if (inside) {
+        const int p = y * W + x;
+        T = final_T[p];
+        // never walk past the tile's list, whatever n_contrib holds
+        nc = min(max(n_contrib[p], 0), rg.y - rg.x);
+        g0 = dimg[3 * p + 0];
+        g1 = dimg[3 * p + 1];
+        g2 = dimg[3 * p + 2];
+    }
+    // Colour "behind" the current splat (normalised by the transmittance after
+    // it; the background at the start), carried only as its dot product with
+    // the pixel's colour gradient
+    float Bg = 0.0f;
+    if (bg) Bg = __builtin_fmaf(bg[0], g0, __builtin_fmaf(bg[1], g1, bg[2] * g2));
+
+    int hmax = nc;  // largest n_contrib of this half (32 lanes)
+    for (int off = 16; off > 0; off >>= 1) hmax = max(hmax, __shfl_xor(hmax, off, 64));
+    if ((lane & 31) == 0) half_end[hq] = hmax;
+    if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel
+        S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
+        S[kDummy].c = 0.0f;
+    }
+    __syncthreads();
+    int hend[kHalves];  // walk end of every half, wave-uniform
+    int tmax = 0;
+#pragma unroll
+    for (int q = 0; q < kHalves; ++q) {
+        hend[q] = __builtin_amdgcn_readfirstlane(half_end[q]);
+        tmax = max(tmax, hend[q]);
+    }
+    if (tmax == 0) return;
+
+    // Leaders of the merged reduction, which store the totals: one lane per
+    // 4-lane bank of W (bank b of row r holds field 2 k + (r & 1),
+    // k = 0, 2, 1, 3 for b = 0..3) and, for the fields 8, 9, one lane per
+    // half (lane 16; its row holds the half's field 8 once the two rows are
+    // added) or, with the weight, one per row.
+    const int odd = (lane >> 4) & 1;
+    const bool bank_lead = (lane & 3) == 0, row_lead = (lane & 15) == 0;
+    const int w_field = 2 * ((0x3120 >> (4 * ((lane >> 2) & 3))) & 3) + odd;  // a bank leader's field
+    const int z_field = AW ? 8 + odd : 8;                                     // a row leader's field
+    // wave masks of the leaders, so that a step can switch off those of a half
+    // whose list is exhausted on scalar registers
+    const unsigned long long bank_mask = __ballot(bank_lead);
+    const unsigned long long row_mask = __ballot(AW ? row_lead : (lane & 31) == 16);
+
+    // No barrier at the top of a batch: thread t flushes slot t and then stages
+    // slot t itself, and the barrier after the walk already separates the
+    // walk's reads of the slots and lists from their rewriting; the partial
+    // records are cleared only after the next barrier.
+    int hi = tmax;  // the batches cover [0, tmax) from the top down
+    while (hi > 0) {
+        const int lo = max(0, hi - kBatch);  // candidates [lo, hi): entry lo + t in slot t
+        const int k = lo + (int)threadIdx.x;
+        const bool cand = (int)threadIdx.x < kBatch && k < hi;
+        int id = -1, radius = 0;
+        SplatRec r;
+        r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
+        if (cand) {
+            id = ids[rg.x + k];
+            r = recs[id];
+            radius = __float_as_int(r.c.z);
+            S[threadIdx.x].a = r.a;
+            S[threadIdx.x].b = r.b;
+            S[threadIdx.x].c = r.c.x;
+        }
+        bool hit[kHalves];
+        half_hits(r, ox, oy, k, hend, hit);
+        // Keep the top candidates whose half-list entries fit the partial
+        // records: suffix sums of the hit counts over the slots, from the top.
+        int hc = 0;
+#pragma unroll
+        for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
+        int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_down(suf, off, kWave);
+            if (lane + off < kWave) suf += u;
+        }
+        if (lane == 0) wave_hits[wv] = suf;
+        if (threadIdx.x == 0) cut = kBatch;
+        __syncthreads();
+        for (int w2 = wv + 1; w2 < 4; ++w2) suf += wave_hits[w2];
+        const bool keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
+        const unsigned long long kb = __ballot(keep);
+        if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));
+        if (!keep) {
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) hit[q] = false;
+        }
+        // The entry's pair slot: the splat's first slot (from its record) plus
+        // the tile's row-major index inside the splat's tile rectangle
+        // (recomputed from mean and radius with the binning's float32 rule).
+        // The tile lies in the rectangle whenever the inputs come from one
+        // binning; anything else gets no slot and is never written wild.
+        {
+            int slot = -1;
+            if (keep) {
+                int tx0, tx1, ty0, ty1;
+                tile_rect(r.a.x, r.a.y, radius, GX, GY, tx0, tx1, ty0, ty1);
+                const int tx = tile % GX, ty = tile / GX;
+                const long long sl =
+                    (long long)__float_as_int(r.c.w) + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
+                if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && sl >= 0 && sl < n_slots) slot = (int)sl;
+            }
+            S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
+        }
+        // Can any entry of the batch reach the 0.99 clamp? alpha_raw =
+        // exp2(log2 o - q) with q >= 0 never exceeds exp2(log2 o) (the same
+        // monotone v_exp_f32), so an entry with exp2(log2 o) clearly below
+        // 0.99 never clamps. Most batches have none, and their walk skips the
+        // clamp's three instructions per step.
+        const bool may_clamp = keep && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
+        int len[kHalves];
+        const bool clamp_batch = build_store_lists(hit, may_clamp, S, list, list_cnt, len);
+        int base[kHalves];  // first partial record of each half
+        base[0] = 0;
+#pragma unroll
+        for (int q = 1; q < kHalves; ++q) base[q] = base[q - 1] + len[q - 1];
+        const int next_hi = lo + cut;
+        // the wave's two list lengths and first records (wave-uniform selects
+        // over the unrolled halves: no indexing of the register arrays by the
+        // wave number), then this lane's half
+        const int wvu = __builtin_amdgcn_readfirstlane(wv);
+        int len_a = 0, len_b = 0, base_a = 0, base_b = 0;
+#pragma unroll
+        for (int q = 0; q < kHalves; q += 2) {
+            len_a = q == 2 * wvu ? len[q] : len_a;
+            len_b = q == 2 * wvu ? len[q + 1] : len_b;
+            base_a = q == 2 * wvu ? base[q] : base_a;
+            base_b = q == 2 * wvu ? base[q + 1] : base_b;
+        }
+        const int my_len = half ? len_b : len_a, len_other = half ? len_a : len_b;
+        const int my_base = half ? base_b : base_a;
+        // the bases wait in LDS for the flush (past the barrier after the walk)
+        // rather than in registers through the walk
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) half_base[q] = base[q];
+        }
+        // the same for both halves: wave-uniform, so the loop runs on scalar control
+        const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
+        // the shorter half takes the dummy entry once its list is exhausted
+        // (and both read up to four entries past the end, ahead of use)
+        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDummyOff;
+        // batch slots below this pixel's walk end, as a byte offset bound
+        const int ncb_off = (nc - lo) * (int)sizeof(StoreSlot);
+        const unsigned short* L = list[hq];
+        const char* Sb = reinterpret_cast<const char*>(S);
+        // a leader's partial record fields for step 0 of its half; step j adds j records
+        // (lanes 0 and 16 of a half lead both a bank and a row: two fields)
+        float* const rec0 = parts + my_base * kF;
+
+        // A step's alpha does not depend on the previous step, so the next
+        // entry's record is read one step ahead and its list entry two steps
+        // ahead: their LDS reads leave the chain of dependent instructions.
+        // Two register sets take turns (the loop is unrolled by two), so the
+        // read-ahead costs no register copies.
+        auto rec_at = [&](int o) -> const StoreSlot& { return *reinterpret_cast<const StoreSlot*>(Sb + o); };
+        auto list_at = [&](int i) -> int { return L[i]; };
+        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur, int j, auto clamp_tag) {
+            constexpr bool kClamp = decltype(clamp_tag)::value;
+            const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
+            float dx, dy;
+            const float ar = alpha_raw(kf, px, py, dx, dy);
+            const float al = kClamp ? fminf(kAlphaMax, ar) : ar;
+            // contributing lanes (position below n_contrib, alpha >= 1/255) as
+            // a wave mask built from the two compares, which keeps the
+            // per-half tests below on scalar registers
+            const unsigned long long bal = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) &
+                                           __builtin_amdgcn_sicmp(cur, ncb_off, 40 /* signed < */);
+            const bool contrib = __builtin_amdgcn_inverse_ballot_w64(bal);
+            // colour . gradient ahead of the test, so that the colour loads
+            // issue with the rest of the record
+            float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
+            asm volatile("" : "+v"(cg));  // not sunk into the branch below
+            // Every listed (half, position) record is written, zeros included:
+            // the records need no clearing. The dummy positions past a
+            // half's list write nothing.
+            const unsigned long long valid = (j < len_a ? 0x00000000ffffffffull : 0ull) |
+                                             (j < len_b ? 0xffffffff00000000ull : 0ull);
+            float* const rec = rec0 + j * kF;
+            if (bal == 0) {
+                if (__builtin_amdgcn_inverse_ballot_w64(bank_mask & valid)) rec[w_field] = 0.0f;
+                if (__builtin_amdgcn_inverse_ballot_w64(row_mask & valid)) rec[z_field] = 0.0f;
+                return;
+            }
+
+            const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
+            const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
+            // dL/dalpha = T_i (c - colour behind) . g needs the colour behind
+            // only through its dot product with the pixel's colour gradient,
+            // which follows the same recurrence as the colour itself; then
+            // s = dL/dsigma = alpha dL/dalpha = w (c - behind) . g
+            const float eg = cg - Bg;
+            Bg = __builtin_fmaf(ae, eg, Bg);
+            T = Ti;
+            const float w = ae * Ti;
+            const float s = (!kClamp || ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
+            // all values first, then the folds (no value is read after its
+            // register has been swapped)
+            const float sdx = s * dx, sdy = s * dy;
+            const float f0 = w * g0, f1 = w * g1, f2 = w * g2;
+            const float f6 = sdx * dx, f7 = sdx * dy;
+            float f8 = sdy * dy;
+            // a plain product: left alone, the compiler fuses it into the first
+            // DPP add as mov + DPP mov + fma, and copies sdy around the swaps
+            asm volatile("" : "+v"(f8));
+            // Fold rows (0, 1) and (2, 3): register R_k row r then holds field
+            // 2k + (r & 1) of half r >> 1, summed over its two rows.
+            const float r0 = fold16(f0, f1);
+            const float r1 = fold16(f2, s);
+            const float r2 = fold16(sdx, sdy);
+            const float r3 = fold16(f6, f7);
+            // Inside each row: merge pairs of registers while halving the
+            // lanes each partial covers (8 -> 4 -> 1 lanes): W's 4-lane bank b
+            // ends with the total of R_{0,2,1,3}[b].
+            const float wq = merge_half_mirror(merge_ror8(r0, r1), merge_ror8(r2, r3));
+            float wt = dpp_add_quad_xor1(dpp_add_quad_xor2(wq));
+            // field 8 (and the weight): folded with the weight when it is
+            // wanted (rows 0 and 2 then hold field 8, rows 1 and 3 the
+            // weight), else summed per row and the two rows of each half
+            // added in registers
+            float zt = AW ? fold16(f8, w) : f8;
+            zt = dpp_add_quad_xor1(dpp_add_quad_xor2(dpp_add_half_mirror(dpp_add_ror8(zt))));
+            if (!AW) zt = dpp_add_prev_row_odd(zt);
+            // keep the last fused DPP adds here rather than under the leader masks
+            asm volatile("" : "+v"(wt), "+v"(zt));
+            // The (half, position) record is this step's alone: plain stores
+            // (a half with no contributing lane stores its exact zeros).
+            if (__builtin_amdgcn_inverse_ballot_w64(bank_mask & valid)) rec[w_field] = wt;
+            if (__builtin_amdgcn_inverse_ballot_w64(row_mask & valid)) rec[z_field] = zt;
+        };
+        auto walk = [&](auto clamp_tag) {
+            int o0 = list_at(0), o1 = list_at(1), on0 = list_at(2);
+            float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+            float C0 = rec_at(o0).c;
+            for (int it = 0; it < steps; it += 2) {
+                // set 1 <- position it + 1; list position it + 3
+                const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+                const float C1 = rec_at(o1).c;
+                const int on1 = list_at(it + 3);
+                step(A0, B0, C0, o0, it, clamp_tag);
+                if (it + 1 >= steps) break;
+                // set 0 <- position it + 2; list position it + 4
+                o0 = on0;
+                A0 = rec_at(o0).a;
+                B0 = rec_at(o0).b;
+                C0 = rec_at(o0).c;
+                on0 = list_at(it + 4);
+                step(A1, B1, C1, o1, it + 1, clamp_tag);
+                o1 = on1;
+            }
+        };
+        if (clamp_batch)
+            walk(std::true_type{});
+        else
+            walk(std::false_type{});
+        __syncthreads();
+
+        // Flush: thread t owns the entry it staged; its sums are those of the
+        // records of the halves that listed it.
+        const int slot = S[threadIdx.x].slot;
+        if (slot >= 0) {
+            const uint2 pw = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
+            float u[kRaw] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) {
+                const unsigned at = ((q < 4 ? pw.x : pw.y) >> (8 * (q & 3))) & 0xffu;
+                if (at != 0xffu) {
+                    const float* pr = parts + (half_base[q] + (int)at) * kF;
+#pragma unroll
+                    for (int f = 0; f < kF; ++f) u[f] += pr[f];
+                }
+            }
+            const bool any = (u[0] != 0.0f) | (u[1] != 0.0f) | (u[2] != 0.0f) | (u[3] != 0.0f) |
+                             (u[4] != 0.0f) | (u[5] != 0.0f) | (u[6] != 0.0f) | (u[7] != 0.0f) |
+                             (u[8] != 0.0f) | (AW && u[9] != 0.0f);
+            if (any) {
+                rec_out[3 * (long long)slot + 0] = make_float4(u[0], u[1], u[2], u[3]);
+                rec_out[3 * (long long)slot + 1] = make_float4(u[4], u[5], u[6], u[7]);
+                rec_out[3 * (long long)slot + 2] = make_float4(u[8], AW ? u[9] : 0.0f, 0.0f, 0.0f);
+                slot_used[slot] = 1;
+            }
+        }
+        hi = next_hi;
+    }
+}
+
 // LDS slot of one staged entry: its alpha coefficients and colour, and the
 // partial sums the walk adds into it. One base address serves every access of
 // a walk step (the lists hold slot byte offsets), so a step spends no VALU
 // instruction on addressing beyond the leaders' field offset.
 // The 80-byte stride is an odd multiple of 16 bytes, so the per-entry 16-byte
 // accesses of staging, zeroing and flushing hit distinct banks.
-struct BwdSlot {
+struct AddSlot {
     float4 a;           // mean x, mean y, l11, l21 (scaled factor)
     float4 b;           // l22, log2(opacity), red, green
     float part[kRaw];   // w g_r, w g_g, w g_b, s, s dx, s dy, s dx^2, s dx dy, s dy^2, [w]
     float c;            // blue
     float pad;
 };
-static_assert(sizeof(BwdSlot) == 80 && offsetof(BwdSlot, part) == 32, "BwdSlot layout");
+static_assert(sizeof(AddSlot) == 80 && offsetof(AddSlot, part) == 32, "AddSlot layout");
 
-__device__ __forceinline__ float4* part4(BwdSlot& e, int i) { return reinterpret_cast<float4*>(e.part) + i; }
-constexpr int kBatch = kBlock - 1;                                    // entries staged per batch
-constexpr int kDummy = kBlock - 1;                                    // slot of the dummy entry
-constexpr unsigned short kDummyOff = (unsigned short)(kDummy * sizeof(BwdSlot));
-constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummies read ahead of use
+__device__ __forceinline__ float4* add_part4(AddSlot& e, int i) { return reinterpret_cast<float4*>(e.part) + i; }
+constexpr unsigned short kAddDummyOff = (unsigned short)(kDummy * sizeof(AddSlot));
 
 // Per-half lists of the staged slots whose hit bit is set, as slot byte
 // offsets in descending slot order (the walk's order). The same exchange of
 // per-wave counts also ORs `flag` over the workgroup, which is returned.
 // Ends with a workgroup barrier.
-__device__ __forceinline__ bool build_half_lists(const bool (&hit)[kHalves], bool flag,
+__device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool flag,
                                                  unsigned short (*list)[kListLen], int (*cnt)[kHalves + 1])
 {
     const int lane = threadIdx.x & 63;
@@ -241,7 +639,7 @@ __device__ __forceinline__ bool build_half_lists(const bool (&hit)[kHalves], boo
             const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
             list[q][__builtin_amdgcn_readlane(top, q) - rank] =
-                (unsigned short)(threadIdx.x * sizeof(BwdSlot));
+                (unsigned short)(threadIdx.x * sizeof(AddSlot));
         }
     }
     __syncthreads();
@@ -256,7 +654,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
     unsigned char* __restrict__ slot_used)
 {
-    __shared__ BwdSlot S[kBlock];
+    __shared__ AddSlot S[kBlock];
     __shared__ int half_end[kHalves];
     __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
     __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
@@ -313,7 +711,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const int odd = (lane >> 4) & 1;
     const bool bank_lead = (lane & 3) == 0, row_lead = (lane & 15) == 0;
     const int w_field = 2 * ((0x3120 >> (4 * ((lane >> 2) & 3))) & 3) + odd;
-    const int lead_off = (int)offsetof(BwdSlot, part) + 4 * w_field;  // byte offset of the bank leader's field
+    const int lead_off = (int)offsetof(AddSlot, part) + 4 * w_field;  // byte offset of the bank leader's field
     // the same as wave masks, so that a step can switch off the leaders of a
     // half with no contributing lane (an exhausted list's dummy entry, or an
     // entry that reaches none of the half's walked pixels) on scalar
@@ -338,8 +736,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
         }
-        *part4(S[threadIdx.x], 0) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        *part4(S[threadIdx.x], 1) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        *add_part4(S[threadIdx.x], 0) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        *add_part4(S[threadIdx.x], 1) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         *reinterpret_cast<float2*>(S[threadIdx.x].part + 8) = make_float2(0.0f, 0.0f);
         bool hit[kHalves];
         half_hits(r, ox, oy, k, hend, hit);
@@ -349,7 +747,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
         const bool may_clamp = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
-        const bool clamp_batch = build_half_lists(hit, may_clamp, list, list_cnt);
+        const bool clamp_batch = build_add_lists(hit, may_clamp, list, list_cnt);
         // this half's list length, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
@@ -358,9 +756,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
         // the shorter half takes the dummy entry once its list is exhausted
         // (and both read up to four entries past the end, ahead of use)
-        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDummyOff;
+        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kAddDummyOff;
         // batch slots below this pixel's walk end, as a byte offset bound
-        const int ncb_off = (nc - bs) * (int)sizeof(BwdSlot);
+        const int ncb_off = (nc - bs) * (int)sizeof(AddSlot);
         const unsigned short* L = list[hq];
         const char* Sb = reinterpret_cast<const char*>(S);
 
@@ -369,7 +767,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         // ahead: their LDS reads leave the chain of dependent instructions.
         // Two register sets take turns (the loop is unrolled by two), so the
         // read-ahead costs no register copies.
-        auto rec_at = [&](int o) -> const BwdSlot& { return *reinterpret_cast<const BwdSlot*>(Sb + o); };
+        auto rec_at = [&](int o) -> const AddSlot& { return *reinterpret_cast<const AddSlot*>(Sb + o); };
         // list entries as 32-bit values: the 16-bit load zero-extends, and
         // holding the widened value keeps the compiler from masking it again
         // at every use
@@ -447,7 +845,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
             if (__builtin_amdgcn_inverse_ballot_w64(bank_mask & live))
                 atomicAdd(reinterpret_cast<float*>(P + lead_off), wt);
             if (__builtin_amdgcn_inverse_ballot_w64(row_mask & live))
-                atomicAdd(reinterpret_cast<float*>(P + offsetof(BwdSlot, part)) + (AW ? 8 + odd : 8), zt);
+                atomicAdd(reinterpret_cast<float*>(P + offsetof(AddSlot, part)) + (AW ? 8 + odd : 8), zt);
         };
         auto walk = [&](auto clamp_tag) {
             int o0 = list_at(0), o1 = list_at(1), on0 = list_at(2);
@@ -478,7 +876,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
 
         // Flush: thread t owns the entry it staged.
         if (id >= 0) {
-            const float4 P0 = *part4(S[threadIdx.x], 0), P1 = *part4(S[threadIdx.x], 1);
+            const float4 P0 = *add_part4(S[threadIdx.x], 0), P1 = *add_part4(S[threadIdx.x], 1);
             const float2 P2 = *reinterpret_cast<const float2*>(S[threadIdx.x].part + 8);
             const float Swr = P0.x, Swg = P0.y, Swb = P0.z, Ss = P0.w, Sdx = P1.x, Sdy = P1.y;
             const float Sdxx = P1.z, Sdxy = P1.w, Sdyy = P2.x;
@@ -866,6 +1264,7 @@ __global__ __launch_bounds__(256) void gather_splat_kernel(int n, const int* __r
 // output (zeros for a splat no pixel took).
 constexpr int kGatherWin = 16 * kWave;  // flag bytes scanned per step
 constexpr int kGatherSplatMaxPairs = 16;  // mean pairs per splat up to which one thread takes a splat
+constexpr int kWalkStoreMinPairs = 16;    // mean pairs per splat above which the stored-partials walk runs
 
 template <bool AW>
 __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
@@ -1049,8 +1448,15 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
                  (long long)n_isect);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
                  "gs_rasterize_bwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
-    GS_CHECK_ARG((flags & ~(uint32_t)GS_FLAG_ACCUM_WEIGHT) == 0, "gs_rasterize_bwd: unknown flags 0x%x", flags);
+    GS_CHECK_ARG((flags & ~(uint32_t)(GS_FLAG_ACCUM_WEIGHT | GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE)) == 0,
+                 "gs_rasterize_bwd: unknown flags 0x%x", flags);
+    GS_CHECK_ARG((flags & (GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE)) != (GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE),
+                 "gs_rasterize_bwd: GS_FLAG_WALK_ADD and GS_FLAG_WALK_STORE both set");
     const bool aw = (flags & GS_FLAG_ACCUM_WEIGHT) != 0;
+    // the stored-partials walk pays off where splats cover many tiles (more
+    // contributing lanes per step, more LDS adds per entry)
+    const bool store_walk = (flags & GS_FLAG_WALK_STORE) != 0 ||
+                            ((flags & GS_FLAG_WALK_ADD) == 0 && n_isect > (long long)kWalkStoreMinPairs * n);
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities && radii && splat_offsets),
                  "gs_rasterize_bwd: NULL splat array");
     GS_CHECK_ARG(n == 0 || (dL_dmeans2d && dL_dconics && dL_dcolors && dL_dopacities),
@@ -1088,14 +1494,15 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         GS_HIP(hipGetLastError());
         GS_HIP(mark(1));
         const int* ord = order;
-        if (aw)
-            bwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(
-                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
-                background, final_T, n_contrib, dL_dimage, ord, slots, used);
+        auto launch = [&](auto kernel) {
+            kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, GY, tiles, (const int2*)tile_ranges,
+                                                       sorted_ids, recs, splat_offsets, n_isect, background,
+                                                       final_T, n_contrib, dL_dimage, ord, slots, used);
+        };
+        if (store_walk)
+            aw ? launch(bwd_store_kernel<true>) : launch(bwd_store_kernel<false>);
         else
-            bwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(
-                width, height, GX, GY, tiles, (const int2*)tile_ranges, sorted_ids, recs, splat_offsets, n_isect,
-                background, final_T, n_contrib, dL_dimage, ord, slots, used);
+            aw ? launch(bwd_kernel<true>) : launch(bwd_kernel<false>);
         GS_HIP(hipGetLastError());
         GS_HIP(mark(2));
     } else {

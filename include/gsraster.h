@@ -88,7 +88,18 @@ enum {
      * alpha * T: the "accum weight" optional feature of the Spirula Studio
      * page (section 机制拆解). Without it no register, LDS slot or store is
      * spent on the weight. */
-    GS_FLAG_ACCUM_WEIGHT = 1u << 0
+    GS_FLAG_ACCUM_WEIGHT = 1u << 0,
+    /* Force one of the two reverse walks (same results up to the order of
+     * float additions). Without either, the call takes the stored-partials
+     * walk when the splats average more than 16 tiles each, else the LDS-add
+     * walk. Setting both is an invalid argument.
+     *   WALK_ADD:   each wave adds its per-step totals into the entry's LDS
+     *               partial sums (float LDS adds; 255-entry batches);
+     *   WALK_STORE: each (half-list, position) step stores its totals into a
+     *               record of its own (no adds; batches as large as the
+     *               records' LDS allows). */
+    GS_FLAG_WALK_ADD = 1u << 1,
+    GS_FLAG_WALK_STORE = 1u << 2
 };
 
 /* Thread-local description of the last non-OK status returned on this thread. */

@@ -70,10 +70,10 @@ def check_max_weight(sc, bins, ids_o, rng_o, img, T, nc):
     return err, int(unc.sum())
 
 
-def gpu_bwd(sc, bins, final_T, n_contrib, g, accum_weight=False):
+def gpu_bwd(sc, bins, final_T, n_contrib, g, accum_weight=False, walk=None):
     return gsr.gs_rasterize_bwd(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
                                 _dev(sc.radii), _dev(sc.background), sc.width, sc.height, bins, final_T, n_contrib,
-                                _dev(g), accum_weight=accum_weight)
+                                _dev(g), accum_weight=accum_weight, walk=walk)
 
 
 def check_bins(sc, bins):
@@ -87,8 +87,9 @@ def check_bins(sc, bins):
     return ids_o, rng_o
 
 
-def check_scene(sc, accum_weight=None, runs=1):
-    """Full parity of one scene: bins, forward, backward."""
+def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store")):
+    """Full parity of one scene: bins, forward, backward (with each of the
+    two reverse walks by default)."""
     if accum_weight is None:
         accum_weight = sc.accum_weight
     _say(f"scene {sc.name} seed {sc.seed} {sc.width}x{sc.height} n={sc.n}: binning")
@@ -119,32 +120,35 @@ def check_scene(sc, accum_weight=None, runs=1):
     g[amb] = 0.0
     bo = oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
                               sc.width, sc.height, rng_o, ids_o, g)
-    results = []
-    for r in range(runs):
-        out = gpu_bwd(sc, bins, torch.from_numpy(T.astype(np.float32)).cuda(), nc, g, accum_weight)
-        torch.cuda.synchronize()
-        results.append({k: v.cpu().numpy().astype(np.float64) for k, v in out.items()})
     pairs = [("dL_dmeans2d", "dmeans2d"), ("dL_dconics", "dconics"), ("dL_dcolors", "dcolors"),
              ("dL_dopacities", "dopacities")]
     if accum_weight:
         pairs.append(("accum_weight", "accum_weight"))
-    # no global atomics: runs differ only by the order in which a tile's four
-    # waves add into a splat's workgroup-local partial (a few ulp)
-    for res in results[1:]:
-        for k in res:
-            np.testing.assert_allclose(res[k], results[0][k], rtol=1e-5,
-                                       atol=1e-6 * max(np.abs(results[0][k]).max(), 1e-30), err_msg=k)
-    errs = {}
-    for res in results:
-        for gk, ok_ in pairs:
-            ref = bo[ok_]
-            scale = np.abs(ref).max(initial=0.0)
-            err = np.abs(res[gk] - ref).max(initial=0.0)
-            errs[gk] = err / scale if scale > 0 else err
-            assert err <= GRAD_REL * max(scale, 1e-30), (gk, err, scale)
-    _say("max rel err", {k: f"{v:.2e}" for k, v in errs.items()}, f"img {err_img:.2e} T {err_T:.2e}",
-         f"max weight {err_mw:.2e} ({n_unc} uncertain splats)")
-    return bins, results
+    all_results = []
+    for walk in walks:
+        results = []
+        for r in range(runs):
+            out = gpu_bwd(sc, bins, torch.from_numpy(T.astype(np.float32)).cuda(), nc, g, accum_weight, walk)
+            torch.cuda.synchronize()
+            results.append({k: v.cpu().numpy().astype(np.float64) for k, v in out.items()})
+        # no global atomics: runs differ at most by the order of a few float
+        # additions inside a workgroup (a few ulp)
+        for res in results[1:]:
+            for k in res:
+                np.testing.assert_allclose(res[k], results[0][k], rtol=1e-5,
+                                           atol=1e-6 * max(np.abs(results[0][k]).max(), 1e-30), err_msg=k)
+        errs = {}
+        for res in results:
+            for gk, ok_ in pairs:
+                ref = bo[ok_]
+                scale = np.abs(ref).max(initial=0.0)
+                err = np.abs(res[gk] - ref).max(initial=0.0)
+                errs[gk] = err / scale if scale > 0 else err
+                assert err <= GRAD_REL * max(scale, 1e-30), (walk, gk, err, scale)
+        _say(f"walk {walk}: max rel err", {k: f"{v:.2e}" for k, v in errs.items()},
+             f"img {err_img:.2e} T {err_T:.2e}", f"max weight {err_mw:.2e} ({n_unc} uncertain splats)")
+        all_results += results
+    return bins, all_results
 
 
 # ----------------------------------------------------------------- configs
@@ -222,8 +226,9 @@ def test_culled_and_offscreen_splats():
     sc.depths[10:15] = -1.0
     sc.depths[15:18] = np.nan
     bins, res = check_scene(sc)
-    for k in ["dL_dmeans2d", "dL_dconics", "dL_dcolors", "dL_dopacities"]:
-        assert np.all(res[0][k][:18] == 0.0)
+    for r in res:  # both walks
+        for k in ["dL_dmeans2d", "dL_dconics", "dL_dcolors", "dL_dopacities"]:
+            assert np.all(r[k][:18] == 0.0)
 
 
 def test_no_splats_and_no_intersections():
@@ -234,9 +239,10 @@ def test_no_splats_and_no_intersections():
     assert np.all(bins.tile_ranges.cpu().numpy() == 0)
     img, T, nc = gpu_fwd(sc, bins)
     assert np.all(T.cpu().numpy() == 1.0) and np.all(nc.cpu().numpy() == 0)
-    out = gpu_bwd(sc, bins, T, nc, sc.dL_dimage)
-    for v in out.values():
-        assert torch.all(v == 0)
+    for walk in ("add", "store"):
+        out = gpu_bwd(sc, bins, T, nc, sc.dL_dimage, walk=walk)
+        for v in out.values():
+            assert torch.all(v == 0)
     empty = scenes.custom_scene(8, 8, np.zeros((0, 2)), np.zeros((0, 2)), np.zeros(0), np.zeros(0),
                                 np.zeros((0, 3)), np.zeros(0))
     b0 = gpu_bins(empty)
