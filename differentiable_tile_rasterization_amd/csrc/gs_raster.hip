@@ -973,7 +973,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
     auto rec_at = [&](int o) -> const FwdSlot& { return *reinterpret_cast<const FwdSlot*>(Sb + o); };
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
-    int last_bs = -1, last_cur = 0;  // batch start and slot offset of the last composited entry
+    int last_n = 0;  // list position of the last composited entry, plus one
     // the wave's stopped pixels (and those outside the image), as a lane mask:
     // the walk's tests then build their masks with compare instructions alone
     unsigned long long done_m = __ballot(!inside);
@@ -1028,40 +1028,29 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
         // the same for both halves: wave-uniform, so the loop runs on scalar control
         const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
-        for (int p = my_len + (lane & 31); p < steps + 2; p += 32) list[hq][p] = kDummyFwd;
+        for (int p = my_len + (lane & 31); p < steps + 3; p += 32) list[hq][p] = kDummyFwd;
         const unsigned short* L = list[hq];
 
-        int off = L[0], offn = L[1];
-        float4 An = rec_at(off).a, Bn = rec_at(off).b;
-        float Cn = rec_at(off).c;
-        for (int it = 0; it < steps; ++it) {
-            const float4 A = An, B = Bn;
-            const float Cb = Cn;
-            const int cur = off;
-            off = offn;
-            offn = L[it + 2];
-            An = rec_at(off).a;
-            Bn = rec_at(off).b;
-            Cn = rec_at(off).c;
-            if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
+        int bl_cur = -1;  // slot offset of this batch's last composited entry (-1: none)
+        // One entry against the lane's pixel. Lanes whose alpha reaches 1/255
+        // are walked; of those, the ones whose T stays >= 1e-4 composite and
+        // the others stop here.
+        auto step = [&](const float4& A, const float4& B, float Cb, int cur) {
             const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
             float dx, dy;
             const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
-            const float test = T * (1.0f - al);
-            // walked pixels whose alpha reaches 1/255; of those, the ones that
-            // composite (T stays >= 1e-4) and the ones that stop here
+            const float test = __builtin_fmaf(-al, T, T);  // T (1 - alpha), rounded once
             const unsigned long long a_m = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) & ~done_m;
             const unsigned long long c_m = a_m & __builtin_amdgcn_fcmpf(test, kTMin, 3 /* ordered >= */);
             done_m |= a_m & ~c_m;
-            if (c_m == 0) continue;
+            if (c_m == 0) return;
             const bool comp = __builtin_amdgcn_inverse_ballot_w64(c_m);
             const float wgt = comp ? al * T : 0.0f;  // other lanes add exact zeros
             C0 = __builtin_fmaf(B.z, wgt, C0);
             C1 = __builtin_fmaf(B.w, wgt, C1);
             C2 = __builtin_fmaf(Cb, wgt, C2);
             T = comp ? test : T;
-            last_bs = comp ? bs : last_bs;
-            last_cur = comp ? cur : last_cur;
+            bl_cur = comp ? cur : bl_cur;
             if (MW) {
                 // each half's largest weight, in every lane of rows 1 and 3
                 const unsigned m = row_umax32(__float_as_uint(wgt));
@@ -1072,7 +1061,28 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
                 if (__builtin_amdgcn_inverse_ballot_w64(lead))  // lane 16 or 48 of a half that composited
                     atomicMax(reinterpret_cast<unsigned*>(const_cast<char*>(Sb) + cur + offsetof(FwdSlot, maxw)), m);
             }
+        };
+        // Two entries per iteration with two record buffers, each refilled
+        // one entry ahead of its use (the lists hold dummies past their end).
+        int o0 = L[0], o1 = L[1];
+        float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+        float K0 = rec_at(o0).c;
+        for (int it = 0; it < steps; it += 2) {
+            if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
+            const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+            const float K1 = rec_at(o1).c;
+            const int n0 = L[it + 2];
+            step(A0, B0, K0, o0);
+            if (it + 1 >= steps) break;
+            A0 = rec_at(n0).a;
+            B0 = rec_at(n0).b;
+            K0 = rec_at(n0).c;
+            const int n1 = L[it + 3];
+            step(A1, B1, K1, o1);
+            o0 = n0;
+            o1 = n1;
         }
+        if (bl_cur >= 0) last_n = bs - rg.x + bl_cur / (int)sizeof(FwdSlot) + 1;
         __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
         if (MW && id >= 0 && id < n) {  // thread t owns slot t until it restages it
             const unsigned v = S[threadIdx.x].maxw;
@@ -1087,7 +1097,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         image[3 * p + 1] = __builtin_fmaf(T, b1, C1);
         image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
         final_T[p] = T;
-        n_contrib[p] = last_bs < 0 ? 0 : last_bs - rg.x + last_cur / (int)sizeof(FwdSlot) + 1;
+        n_contrib[p] = last_n;
     }
 }
 
