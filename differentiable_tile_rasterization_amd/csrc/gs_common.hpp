@@ -238,26 +238,29 @@ __device__ __forceinline__ float dpp_add_prev_row_odd(float x)
     return x;
 }
 
-// Unsigned max with a DPP-permuted copy of itself, one fused instruction per
-// level (for non-negative floats, the max of their bit patterns is the bit
-// pattern of their max). row_umax32 leaves in rows 1 and 3 the max over the
-// two rows of each 32-lane half (rows 0 and 2 hold their own row's max).
-#define GS_DPP_UMAX(name, ctrl)                                                          \
-    __device__ __forceinline__ unsigned name(unsigned x)                                 \
-    {                                                                                    \
-        asm volatile("s_nop 1\n\tv_max_u32_dpp %0, %0, %0 " ctrl : "+v"(x));           \
-        return x;                                                                        \
-    }
-GS_DPP_UMAX(dpp_umax_ror8, "row_ror:8 row_mask:0xf bank_mask:0xf")
-GS_DPP_UMAX(dpp_umax_half_mirror, "row_half_mirror row_mask:0xf bank_mask:0xf")
-GS_DPP_UMAX(dpp_umax_quad_xor2, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
-GS_DPP_UMAX(dpp_umax_quad_xor1, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
-GS_DPP_UMAX(dpp_umax_prev_row_odd, "row_bcast:15 row_mask:0xa bank_mask:0xf")
-#undef GS_DPP_UMAX
-
-__device__ __forceinline__ unsigned row_umax32(unsigned x)
+// Maxima of two values over each 32-lane half, for non-negative floats as
+// their bit patterns (whose unsigned order is the order of the values).
+// v_permlane16_swap folds the two rows of each half lane-wise, x's into rows 0
+// and 2 and y's into rows 1 and 3; four DPP rotations (each fused into one
+// v_max_u32_dpp) finish each row. Row 0 holds half 0's max of x, row 1 half
+// 0's max of y, rows 2 and 3 the same for half 1, in every lane of the row.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp0u(unsigned x)
 {
-    return dpp_umax_prev_row_odd(dpp_umax_quad_xor1(dpp_umax_quad_xor2(dpp_umax_half_mirror(dpp_umax_ror8(x)))));
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ unsigned half_umax_pair(unsigned x, unsigned y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    const unsigned u0 = r[0], u1 = r[1];
+    unsigned m = max(u0, u1);
+    m = max(m, dpp0u<0x128>(m));  // row_ror:8
+    m = max(m, dpp0u<0x124>(m));  // row_ror:4
+    m = max(m, dpp0u<0x122>(m));  // row_ror:2
+    m = max(m, dpp0u<0x121>(m));  // row_ror:1
+    asm volatile("" : "+v"(m));   // keep the last level fused, outside the caller's lane mask
+    return m;
 }
 
 // lanes 0-7 of each row: x + ror8(x); lanes 8-15: y + ror8(y)

@@ -924,9 +924,12 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* __restrict__ p,
 // when all 256 have.
 //
 // Optional per-splat max weight (MW): the largest alpha T a splat receives
-// over the pixels that composite it. Per step, each half's largest weight
-// (DPP max over its 32 lanes) goes into the entry's slot with one LDS max;
-// after each batch, thread t raises the splat's global maximum with one
+// over the pixels that composite it. After each pair of steps, each half's
+// largest weight of either step (DPP max over its 32 lanes, the two steps'
+// chains interleaved) is stored by one lane per half into a record of its own
+// per (half, list position), cleared at every batch; after the batch, thread
+// t takes the max over the records of the halves that listed its entry (the
+// positions kept in its slot) and raises the splat's global maximum with one
 // integer atomic max. Weights are >= 0, so the order of their float32 bit
 // patterns is the order of their values, and a max is the same in any order:
 // the result does not depend on scheduling.
@@ -935,8 +938,8 @@ struct FwdSlot {
     float4 a;       // mean x, mean y, l11, l21 (scaled factor)
     float4 b;       // l22, log2(opacity), red, green
     float c;        // blue
-    unsigned maxw;  // largest weight of the batch's walk (float bits), MW only
-    float pad[2];
+    unsigned char pos[kHalves];  // list position in each half, 0xff: not listed (MW only)
+    float pad;
 };
 static_assert(sizeof(FwdSlot) == 48, "FwdSlot layout");
 
@@ -953,6 +956,8 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
     __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
     __shared__ int list_cnt[4][kHalves + 1];
     __shared__ int half_live[kHalves];
+    // MW: largest weight per (half, list position), float bits; 0: none
+    __shared__ __align__(16) unsigned mw_rec[MW ? kHalves : 1][MW ? kBlock : 4];
     const int tile = xcd_tile(blockIdx.x, tiles);
     if (tile >= tiles) return;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -997,7 +1002,10 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             S[threadIdx.x].a = r.a;
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
-            if (MW) S[threadIdx.x].maxw = 0u;
+        }
+        if (MW) {  // this batch's records start cleared
+            uint4* z = reinterpret_cast<uint4*>(&mw_rec[0][0]) + 2 * threadIdx.x;
+            z[0] = z[1] = make_uint4(0u, 0u, 0u, 0u);
         }
         bool hit[kHalves];
         half_hits(r, ox, oy, 0, hend, hit);
@@ -1013,15 +1021,22 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         int below = 0;
         if (lane < kHalves)
             for (int w2 = 0; w2 < wv; ++w2) below += list_cnt[w2][lane];
+        unsigned pos_lo = ~0u, pos_hi = ~0u;  // MW: the entry's list positions, a byte per half
 #pragma unroll
         for (int q = 0; q < kHalves; ++q) {
             const unsigned long long bal = __ballot(hit[q]);
             if (hit[q]) {
                 const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-                list[q][__builtin_amdgcn_readlane(below, q) + rank] = (unsigned short)(threadIdx.x * sizeof(FwdSlot));
+                const int at = __builtin_amdgcn_readlane(below, q) + rank;
+                list[q][at] = (unsigned short)(threadIdx.x * sizeof(FwdSlot));
+                if (MW) {
+                    if (q < 4) pos_lo = (pos_lo & ~(0xffu << (8 * q))) | ((unsigned)at << (8 * q));
+                    else pos_hi = (pos_hi & ~(0xffu << (8 * (q - 4)))) | ((unsigned)at << (8 * (q - 4)));
+                }
             }
         }
+        if (MW) *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(pos_lo, pos_hi);
         __syncthreads();
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
@@ -1035,7 +1050,8 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         // One entry against the lane's pixel. Lanes whose alpha reaches 1/255
         // are walked; of those, the ones whose T stays >= 1e-4 composite and
         // the others stop here.
-        auto step = [&](const float4& A, const float4& B, float Cb, int cur) {
+        unsigned long long any_c = 0;  // MW: lanes that composited in the current pair of steps
+        auto step = [&](const float4& A, const float4& B, float Cb, int cur) -> float {
             const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
             float dx, dy;
             const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
@@ -1043,7 +1059,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             const unsigned long long a_m = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) & ~done_m;
             const unsigned long long c_m = a_m & __builtin_amdgcn_fcmpf(test, kTMin, 3 /* ordered >= */);
             done_m |= a_m & ~c_m;
-            if (c_m == 0) return;
+            if (c_m == 0) return 0.0f;
             const bool comp = __builtin_amdgcn_inverse_ballot_w64(c_m);
             const float wgt = comp ? al * T : 0.0f;  // other lanes add exact zeros
             C0 = __builtin_fmaf(B.z, wgt, C0);
@@ -1051,41 +1067,55 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             C2 = __builtin_fmaf(Cb, wgt, C2);
             T = comp ? test : T;
             bl_cur = comp ? cur : bl_cur;
-            if (MW) {
-                // each half's largest weight, in every lane of rows 1 and 3
-                const unsigned m = row_umax32(__float_as_uint(wgt));
-                unsigned hi = (unsigned)(c_m >> 32);
-                asm("" : "+s"(hi));  // a 32-bit test (a 64-bit unsigned compare has no scalar form)
-                const unsigned long long lead = ((unsigned)c_m != 0u ? (1ull << 16) : 0ull) |
-                                                (hi != 0u ? (1ull << 48) : 0ull);
-                if (__builtin_amdgcn_inverse_ballot_w64(lead))  // lane 16 or 48 of a half that composited
-                    atomicMax(reinterpret_cast<unsigned*>(const_cast<char*>(Sb) + cur + offsetof(FwdSlot, maxw)), m);
-            }
+            if (MW) any_c |= c_m;
+            return wgt;
+        };
+        // MW: the pair's largest weights per half go to positions it, it + 1:
+        // row 0 (2) of the wave holds half 0's (1's) for the first step, row 1
+        // (3) for the second, and the first lane of each row stores its own
+        auto store_max = [&](float w0, float w1, int it) {
+            if (any_c == 0) return;  // the records stay 0
+            any_c = 0;
+            const unsigned m = half_umax_pair(__float_as_uint(w0), __float_as_uint(w1));
+            if (__builtin_amdgcn_inverse_ballot_w64(0x0001000100010001ull))
+                mw_rec[hq][it + ((lane >> 4) & 1)] = m;
         };
         // Two entries per iteration with two record buffers, each refilled
         // one entry ahead of its use (the lists hold dummies past their end).
         int o0 = L[0], o1 = L[1];
         float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
         float K0 = rec_at(o0).c;
+        float w_tail = 0.0f;  // MW: the weights of an odd count's last step, stored after the loop
         for (int it = 0; it < steps; it += 2) {
             if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
             const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
             const float K1 = rec_at(o1).c;
             const int n0 = L[it + 2];
-            step(A0, B0, K0, o0);
-            if (it + 1 >= steps) break;
+            const float w0 = step(A0, B0, K0, o0);
+            if (it + 1 >= steps) {
+                w_tail = w0;
+                break;
+            }
             A0 = rec_at(n0).a;
             B0 = rec_at(n0).b;
             K0 = rec_at(n0).c;
             const int n1 = L[it + 3];
-            step(A1, B1, K1, o1);
+            const float w1 = step(A1, B1, K1, o1);
+            if (MW) store_max(w0, w1, it);
             o0 = n0;
             o1 = n1;
         }
+        if (MW && (steps & 1)) store_max(w_tail, 0.0f, steps - 1);  // any_c is 0 if it was not walked
         if (bl_cur >= 0) last_n = bs - rg.x + bl_cur / (int)sizeof(FwdSlot) + 1;
         __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
         if (MW && id >= 0 && id < n) {  // thread t owns slot t until it restages it
-            const unsigned v = S[threadIdx.x].maxw;
+            const uint2 pp = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
+            unsigned v = 0u;
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) {
+                const unsigned p = ((q < 4 ? pp.x : pp.y) >> (8 * (q & 3))) & 0xffu;
+                if (p != 0xffu) v = max(v, mw_rec[q][p]);
+            }
             if (v != 0u) atomicMax(max_weight + id, v);
         }
     }
