@@ -33,10 +33,10 @@ constexpr int kScanTile = kScanThreads * kScanItems;  // 4096 items per workgrou
 constexpr int kSortThreads = 256;
 constexpr int kSortRounds = 16;                       // rounds of 256 keys per workgroup
 constexpr int kSortTile = kSortThreads * kSortRounds; // 4096 keys per workgroup
-constexpr int kRadixBits = 8;
+constexpr int kRadixBits = 8;                         // widest digit
 constexpr int kRadix = 1 << kRadixBits;
 static_assert(kSortThreads == kRadix && kSortThreads == 4 * kWave && kSortTile == 4 * kSortRounds * kWave,
-              "radix sort tiling: one thread per digit, four waves each holding a quarter of the tile");
+              "radix sort tiling: at most one digit per thread, four waves each holding a quarter of the tile");
 
 __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float depth, int GX, int GY,
                                            int& tx0, int& tx1, int& ty0, int& ty1)
@@ -205,29 +205,30 @@ __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, c
 }
 
 // ---------------------------------------------------------------------------
-// Stable LSD radix sort pass over digit [shift, shift + 8).
+// Stable LSD radix sort pass over digit [shift, shift + BITS), BITS <= 8.
 // hist: per workgroup digit counts, stored digit-major (digit * nwg + wg) so
 // that one exclusive scan yields every workgroup's output offset per digit.
 // ---------------------------------------------------------------------------
-template <typename K>
+template <typename K, int BITS>
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __restrict__ keys, long long n,
                                                                   int shift, int nwg, unsigned* __restrict__ hist)
 {
-    __shared__ unsigned h[4][kRadix];
-    for (int k = threadIdx.x; k < 4 * kRadix; k += kSortThreads) (&h[0][0])[k] = 0;
+    constexpr int R = 1 << BITS;
+    __shared__ unsigned h[4][R];
+    for (int k = threadIdx.x; k < 4 * R; k += kSortThreads) (&h[0][0])[k] = 0;
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const long long base = (long long)blockIdx.x * kSortTile;
     for (int r = 0; r < kSortRounds; ++r) {
         const long long idx = base + (long long)r * kSortThreads + threadIdx.x;
         if (idx < n) {
-            const unsigned d = (unsigned)(keys[idx] >> shift) & (kRadix - 1);
+            const unsigned d = (unsigned)(keys[idx] >> shift) & (R - 1);
             atomicAdd(&h[w][d], 1u);
         }
     }
     __syncthreads();
-    const int d = threadIdx.x;  // kSortThreads == kRadix
-    hist[(long long)d * nwg + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+    const int d = threadIdx.x;
+    if (d < R) hist[(long long)d * nwg + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
 }
 
 // Scatter of one pass. The workgroup's keys are first ranked stably by digit
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __res
 // block-local start and each wave's offset inside it come from one scan; as
 // the waves hold consecutive quarters of the tile, wave order then round
 // order is the tile's order: the placement is stable.
-template <typename K>
+template <typename K, int BITS>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __restrict__ keys_in,
                                                                      const int* __restrict__ vals_in, long long n,
                                                                      int shift, int nwg,
@@ -251,22 +252,23 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
                                                                      K* __restrict__ keys_out,
                                                                      int* __restrict__ vals_out)
 {
-    __shared__ unsigned wave_run[4][kRadix];  // per wave: keys of digit d ranked so far, then its offset
-    __shared__ unsigned local_start[kRadix];  // block-local start of digit d
-    __shared__ unsigned global_off[kRadix];
+    constexpr int R = 1 << BITS;
+    __shared__ unsigned wave_run[4][R];  // per wave: keys of digit d ranked so far, then its offset
+    __shared__ unsigned local_start[R];  // block-local start of digit d
+    __shared__ unsigned global_off[R];
     __shared__ unsigned scan_part[4];
     __shared__ K lkey[kSortTile];
     __shared__ int lval[kSortTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const long long base = (long long)blockIdx.x * kSortTile;
     const int cnt = (int)(n - base < (long long)kSortTile ? n - base : (long long)kSortTile);
-    const int td = threadIdx.x;  // kSortThreads == kRadix: thread td looks after digit td
+    const int td = threadIdx.x;  // thread td < R looks after digit td
+    const bool has_digit = td < R;
     K key[kSortRounds];
     int val[kSortRounds];
     unsigned rk[kSortRounds];  // rank among the wave's keys of the same digit
-#pragma unroll
-    for (int k = 0; k < 4; ++k) wave_run[w][64 * k + lane] = 0u;  // each wave clears its own row
-    global_off[td] = offs[(long long)td * nwg + blockIdx.x];
+    for (int k = lane; k < R; k += kWave) wave_run[w][k] = 0u;  // each wave clears its own row
+    if (has_digit) global_off[td] = offs[(long long)td * nwg + blockIdx.x];
     const int wbase = w * (kSortTile / 4);  // this wave's quarter of the tile
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
@@ -282,10 +284,10 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
         const bool valid = wbase + r * kWave + lane < cnt;
-        const unsigned d = valid ? (unsigned)(key[r] >> shift) & (kRadix - 1) : 0u;
+        const unsigned d = valid ? (unsigned)(key[r] >> shift) & (R - 1) : 0u;
         unsigned long long peers = __ballot(valid);
 #pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
+        for (int b = 0; b < BITS; ++b) {
             const bool bit = (d >> b) & 1u;
             const unsigned long long bal = __ballot(bit);
             peers &= bit ? bal : ~bal;
@@ -298,7 +300,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     __syncthreads();
     // digit td: its count over the tile, the exclusive scan of the counts over
     // the digits, and each wave's offset inside the digit's run
-    const unsigned c0 = wave_run[0][td], c1 = wave_run[1][td], c2 = wave_run[2][td], c3 = wave_run[3][td];
+    const unsigned c0 = has_digit ? wave_run[0][td] : 0u, c1 = has_digit ? wave_run[1][td] : 0u;
+    const unsigned c2 = has_digit ? wave_run[2][td] : 0u, c3 = has_digit ? wave_run[3][td] : 0u;
     const unsigned tot = c0 + c1 + c2 + c3;
     unsigned incl = tot;
     for (int dl = 1; dl < kWave; dl <<= 1) {
@@ -310,16 +313,18 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     unsigned before_w = 0;
     for (int k = 0; k < w; ++k) before_w += scan_part[k];
     const unsigned start = before_w + incl - tot;
-    local_start[td] = start;
-    wave_run[0][td] = start;
-    wave_run[1][td] = start + c0;
-    wave_run[2][td] = start + c0 + c1;
-    wave_run[3][td] = start + c0 + c1 + c2;
+    if (has_digit) {
+        local_start[td] = start;
+        wave_run[0][td] = start;
+        wave_run[1][td] = start + c0;
+        wave_run[2][td] = start + c0 + c1;
+        wave_run[3][td] = start + c0 + c1 + c2;
+    }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
         if (wbase + r * kWave + lane < cnt) {
-            const unsigned d = (unsigned)(key[r] >> shift) & (kRadix - 1);
+            const unsigned d = (unsigned)(key[r] >> shift) & (R - 1);
             const unsigned lp = wave_run[w][d] + rk[r];
             lkey[lp] = key[r];
             lval[lp] = val[r];
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
         const int lp = r * kSortThreads + threadIdx.x;
         if (lp < cnt) {
             const K k = lkey[lp];
-            const unsigned d = (unsigned)(k >> shift) & (kRadix - 1);
+            const unsigned d = (unsigned)(k >> shift) & (R - 1);
             const unsigned pos = global_off[d] + ((unsigned)lp - local_start[d]);
             keys_out[pos] = k;
             vals_out[pos] = lval[lp];
@@ -418,19 +423,32 @@ BinLayout bin_layout(long long n, long long cap)
     return L;
 }
 
-// One stable LSD pass over 8-bit digit `shift` of keys_in -> keys_out.
-template <typename K>
-hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, unsigned* hist,
-                      unsigned long long* part, unsigned long long* total, hipStream_t st)
+// One stable LSD pass over the BITS-bit digit at `shift` of keys_in -> keys_out.
+template <typename K, int BITS>
+hipError_t radix_pass_b(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, unsigned* hist,
+                        unsigned long long* part, unsigned long long* total, hipStream_t st)
 {
     const int nwg = (int)((cnt + kSortTile - 1) / kSortTile);
-    radix_hist_kernel<K><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
+    radix_hist_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = exclusive_scan<unsigned, unsigned>(hist, hist, (long long)kRadix * nwg, part, total, st);
+    e = exclusive_scan<unsigned, unsigned>(hist, hist, (long long)(1 << BITS) * nwg, part, total, st);
     if (e != hipSuccess) return e;
-    radix_scatter_kernel<K><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
+    radix_scatter_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
     return hipGetLastError();
+}
+
+template <typename K>
+hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, int bits,
+                      unsigned* hist, unsigned long long* part, unsigned long long* total, hipStream_t st)
+{
+    switch (bits) {
+    case 4: return radix_pass_b<K, 4>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 5: return radix_pass_b<K, 5>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 6: return radix_pass_b<K, 6>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 7: return radix_pass_b<K, 7>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    default: return radix_pass_b<K, 8>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    }
 }
 
 int bits_for(long long v)  // smallest b with (1 << b) > v - 1, i.e. enough bits for values 0..v-1
@@ -554,7 +572,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         unsigned* dk_out = dkb;
         int* dv_out = dvb;
         for (int shift = 0; shift < 32; shift += kRadixBits) {
-            GS_HIP(radix_pass<unsigned>(dk_in, dv_in, dk_out, dv_out, n, shift, hist, part, total, st));
+            GS_HIP(radix_pass<unsigned>(dk_in, dv_in, dk_out, dv_out, n, shift, kRadixBits, hist, part, total, st));
             dk_in = dk_out;
             dv_in = dv_out;
             dk_out = dk_out == dkb ? dka : dkb;
@@ -588,9 +606,13 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     }
     if (I == 0) return GS_OK;
 
-    // Tile passes, ping-ponged so that the last one writes its values into sorted_ids.
+    // Tile passes, ping-ponged so that the last one writes its values into
+    // sorted_ids: as few passes as 8-bit digits allow, the tile id's bits
+    // split evenly over them (narrower digits make longer runs per digit in
+    // each workgroup's output, i.e. fuller cache lines), at least 4 bits each.
     const int tb = bits_for(tiles);
     const int np = (tb + kRadixBits - 1) / kRadixBits;
+    const int pb = np > 0 ? max(4, (tb + np - 1) / np) : kRadixBits;
     auto* keys_a = (unsigned*)(ws + L.keys_a);
     auto* keys_b = (unsigned*)(ws + L.keys_b);
     auto* vals_t = (int*)(ws + L.vals_tmp);
@@ -601,7 +623,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     emit_kernel<<<(n + kWave - 1) / kWave, kWave, 0, st>>>(n, I, by_depth, rect_sorted, emit_off, GX, kin, vin);
     GS_HIP(hipGetLastError());
     for (int p = 0; p < np; ++p) {
-        GS_HIP(radix_pass<unsigned>(kin, vin, kout, vout, I, kRadixBits * p, hist, part, total, st));
+        GS_HIP(radix_pass<unsigned>(kin, vin, kout, vout, I, pb * p, pb, hist, part, total, st));
         unsigned* tk = kin; kin = kout; kout = tk;
         int* tv = vin; vin = vout; vout = tv;
     }
