@@ -219,12 +219,18 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __res
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const long long base = (long long)blockIdx.x * kSortTile;
+    // every key of the thread requested before the first count (one wait)
+    K key[kSortRounds];
+    const bool full = base + kSortTile <= n;
+#pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
         const long long idx = base + (long long)r * kSortThreads + threadIdx.x;
-        if (idx < n) {
-            const unsigned d = (unsigned)(keys[idx] >> shift) & (R - 1);
-            atomicAdd(&h[w][d], 1u);
-        }
+        key[r] = full || idx < n ? keys[idx] : K(0);
+    }
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const long long idx = base + (long long)r * kSortThreads + threadIdx.x;
+        if (full || idx < n) atomicAdd(&h[w][(unsigned)(key[r] >> shift) & (R - 1)], 1u);
     }
     __syncthreads();
     const int d = threadIdx.x;
@@ -268,17 +274,24 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     int val[kSortRounds];
     unsigned rk[kSortRounds];  // rank among the wave's keys of the same digit
     for (int k = lane; k < R; k += kWave) wave_run[w][k] = 0u;  // each wave clears its own row
-    if (has_digit) global_off[td] = offs[(long long)td * nwg + blockIdx.x];
+    const unsigned goff = has_digit ? offs[(long long)td * nwg + blockIdx.x] : 0u;  // stored after the ranking
     const int wbase = w * (kSortTile / 4);  // this wave's quarter of the tile
+    // all loads issued before the first use (the branches are uniform)
+    const bool full = cnt == kSortTile;
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
         const int li = wbase + r * kWave + lane;
-        key[r] = 0;
-        val[r] = 0;
-        if (li < cnt) {
-            key[r] = keys_in[base + li];
-            val[r] = vals_in ? vals_in[base + li] : (int)(base + li);  // no values: the index
+        key[r] = full || li < cnt ? keys_in[base + li] : K(0);
+    }
+    if (vals_in) {
+#pragma unroll
+        for (int r = 0; r < kSortRounds; ++r) {
+            const int li = wbase + r * kWave + lane;
+            val[r] = full || li < cnt ? vals_in[base + li] : 0;
         }
+    } else {  // no values: the index
+#pragma unroll
+        for (int r = 0; r < kSortRounds; ++r) val[r] = (int)(base + wbase + r * kWave + lane);
     }
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
 #pragma unroll
@@ -297,6 +310,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
         rk[r] = before + rank;
         if (valid && rank == 0) wave_run[w][d] = before + (unsigned)__popcll(peers);
     }
+    if (has_digit) global_off[td] = goff;
     __syncthreads();
     // digit td: its count over the tile, the exclusive scan of the counts over
     // the digits, and each wave's offset inside the digit's run
