@@ -171,36 +171,72 @@ __global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __r
 
 // Emission: one wave per 64 consecutive depth ranks. Their pairs are
 // contiguous, [emit_off[k0], emit_off[k0 + 64]), and the wave writes them
-// together, one pair per lane per step (coalesced), the pair's splat found by
-// binary search in the wave's copy of the offsets: the splat of depth rank k
-// writes its tiles, row-major, from emit_off[k], as (tile id, splat id).
+// together, one pair per lane per step (coalesced): the splat of depth rank k
+// writes its tiles, row-major, from emit_off[k], as (tile id, splat id). At
+// each step of 64 pairs, every splat whose first pair falls in the step marks
+// that position with its lane (non-empty splats start at distinct positions),
+// and an inclusive max-scan over the lanes, seeded with the previous step's
+// last owner, gives each position its splat. The row inside the splat's
+// rectangle comes from a float quotient corrected by one (rel < 2^22 and the
+// width <= 2048, so the estimate is within one of the quotient).
+__device__ __forceinline__ int wave_max_scan(int x)  // inclusive, ascending lanes, x >= 0
+{
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15 into rows 1, 3
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, const int* __restrict__ by_depth,
                                                      const ushort4* __restrict__ rect_sorted,
                                                      const unsigned long long* __restrict__ emit_off, int GX,
                                                      unsigned* __restrict__ keys, int* __restrict__ vals)
 {
-    __shared__ unsigned long long off[kWave + 1];
     __shared__ ushort4 rc[kWave];
+    __shared__ unsigned rstart[kWave];  // first pair of the lane's splat, relative to the wave's first
     __shared__ int sid[kWave];
+    __shared__ int mark[kWave];         // per step: 1 + lane of the splat starting at the position, or 0
     const int lane = threadIdx.x;
     const int k0 = blockIdx.x * kWave, k = k0 + lane;
-    off[lane] = k < n ? emit_off[k] : (unsigned long long)n_pairs;
-    if (lane == 0) off[kWave] = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned long long)n_pairs;
-    rc[lane] = k < n ? rect_sorted[k] : make_ushort4(0, 0, 0, 0);
+    const unsigned long long my_off = k < n ? emit_off[k] : (unsigned long long)n_pairs;
+    const unsigned long long p0 = emit_off[k0];
+    const unsigned long long p1 = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned long long)n_pairs;
+    const ushort4 b = k < n ? rect_sorted[k] : make_ushort4(0, 0, 0, 0);
+    const unsigned my_cnt = (unsigned)(b.z - b.x) * (unsigned)(b.w - b.y);
+    const unsigned my_rel = (unsigned)(my_off - p0);  // the wave's pairs number below 2^31
+    rc[lane] = b;
+    rstart[lane] = my_rel;
     sid[lane] = k < n ? by_depth[k] : 0;
-    __syncthreads();
-    const unsigned long long p0 = off[0], p1 = off[kWave];
-    for (unsigned long long p = p0 + lane; p < p1; p += kWave) {
-        int lo = 0, hi = kWave - 1;  // the last local rank s with off[s] <= p
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    const unsigned total = (unsigned)(p1 - p0);
+    int carry = 0;
+    for (unsigned q = 0; q < total; q += kWave) {
+        mark[lane] = 0;
+        __syncthreads();
+        if (my_cnt > 0 && my_rel >= q && my_rel - q < (unsigned)kWave) mark[my_rel - q] = lane + 1;
+        __syncthreads();
+        const int o = max(wave_max_scan(mark[lane]), carry);
+        carry = __builtin_amdgcn_readlane(o, kWave - 1);
+        const unsigned rel_p = q + (unsigned)lane;
+        if (rel_p < total) {
+            const int s = o - 1;
+            const ushort4 bs = rc[s];
+            const unsigned rel = rel_p - rstart[s], wdt = (unsigned)(bs.z - bs.x);
+            int row = (int)((float)rel * __builtin_amdgcn_rcpf((float)wdt));
+            int col = (int)rel - row * (int)wdt;
+            if (col < 0) {
+                --row;
+                col += (int)wdt;
+            } else if (col >= (int)wdt) {
+                ++row;
+                col -= (int)wdt;
+            }
+            const unsigned long long p = p0 + rel_p;
+            keys[p] = (unsigned)((bs.y + row) * GX + bs.x + col);
+            vals[p] = sid[s];
         }
-        const ushort4 b = rc[lo];
-        const unsigned rel = (unsigned)(p - off[lo]), wdt = (unsigned)(b.z - b.x);
-        const unsigned row = rel / wdt;
-        keys[p] = (unsigned)((b.y + row) * GX + b.x + (rel - row * wdt));
-        vals[p] = sid[lo];
     }
 }
 
