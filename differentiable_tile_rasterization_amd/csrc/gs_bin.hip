@@ -27,8 +27,8 @@ namespace gs {
 namespace {
 
 constexpr int kScanThreads = 256;
-constexpr int kScanItems = 16;                        // per thread
-constexpr int kScanTile = kScanThreads * kScanItems;  // 4096 items per workgroup
+constexpr int kScanItems = 4;                         // per thread: one 16-byte load
+constexpr int kScanTile = kScanThreads * kScanItems;  // 1024 items per workgroup
 
 constexpr int kSortThreads = 256;
 constexpr int kSortRounds = 16;                       // rounds of 256 keys per workgroup
@@ -52,7 +52,7 @@ __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float dept
 __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
                                                     const int* __restrict__ radii,
                                                     const float* __restrict__ depths, int GX, int GY,
-                                                    unsigned long long* __restrict__ counts,
+                                                    unsigned* __restrict__ counts,
                                                     ushort4* __restrict__ rects)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -60,29 +60,36 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
     const float2 m = means[i];
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
-    counts[i] = live ? (unsigned long long)(tx1 - tx0) * (unsigned long long)(ty1 - ty0) : 0ull;
+    counts[i] = live ? (unsigned)((tx1 - tx0) * (ty1 - ty0)) : 0u;  // at most 2048 x 2048
     rects[i] = live ? make_ushort4((unsigned short)tx0, (unsigned short)ty0, (unsigned short)tx1,
                                    (unsigned short)ty1)
                     : make_ushort4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Device-wide exclusive scan (3 kernels): per-workgroup totals, a one-workgroup
-// scan of those totals, then a per-workgroup scan seeded with its offset.
-// T is the element type (uint32 or uint64); sums are carried in uint64.
+// Device-wide exclusive scan of 32-bit items (2 kernels): per-workgroup totals,
+// then a per-workgroup scan seeded with the sum of the earlier totals. Thread
+// t of workgroup b holds items 1024 b + 4 t .. + 3 (one 16-byte load and
+// store: consecutive threads, consecutive addresses). Sums are carried in
+// 64 bits; the outputs are their low 32 bits (exact whenever the total fits,
+// which the callers check before using them).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const T* __restrict__ in, long long n,
+__device__ __forceinline__ uint4 load_items4(const unsigned* __restrict__ in, long long idx, long long n)
+{
+    if (idx + 4 <= n) return *reinterpret_cast<const uint4*>(in + idx);  // arrays are 256-byte aligned
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < n) v.x = in[idx];
+    if (idx + 1 < n) v.y = in[idx + 1];
+    if (idx + 2 < n) v.z = in[idx + 2];
+    return v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const unsigned* __restrict__ in, long long n,
                                                                    unsigned long long* __restrict__ part)
 {
     __shared__ unsigned long long red[kScanThreads / kWave];
-    const long long base = (long long)blockIdx.x * kScanTile;
-    unsigned long long s = 0;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-        const long long idx = base + (long long)k * kScanThreads + threadIdx.x;
-        if (idx < n) s += (unsigned long long)in[idx];
-    }
+    const uint4 v = load_items4(in, (long long)blockIdx.x * kScanTile + kScanItems * threadIdx.x, n);
+    unsigned long long s = (unsigned long long)v.x + v.y + v.z + v.w;
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
@@ -108,14 +115,15 @@ __device__ __forceinline__ unsigned long long block_incl_scan(unsigned long long
 // part[0..b) itself (a few thousand at most, so this costs less than a
 // separate scan of them would cost in launch latency), then scans its tile;
 // the last workgroup also writes the grand total to *total (if not null).
-template <typename TI, typename TO>
-__global__ __launch_bounds__(kScanThreads) void scan_down_kernel(const TI* __restrict__ in, TO* __restrict__ out,
-                                                                 long long n,
+// in == out is allowed (each workgroup reads its items before writing them).
+__global__ __launch_bounds__(kScanThreads) void scan_down_kernel(const unsigned* in, unsigned* out, long long n,
                                                                  const unsigned long long* __restrict__ part,
                                                                  int m, unsigned long long* __restrict__ total)
 {
     __shared__ unsigned long long wsum[kScanThreads / kWave];
     __shared__ unsigned long long red[kScanThreads / kWave];
+    const long long idx = (long long)blockIdx.x * kScanTile + kScanItems * threadIdx.x;
+    const uint4 v = load_items4(in, idx, n);
     unsigned long long pre = 0;
     for (int k = threadIdx.x; k < (int)blockIdx.x; k += kScanThreads) pre += part[k];
     for (int off = 32; off > 0; off >>= 1) pre += __shfl_xor(pre, off, 64);
@@ -123,34 +131,29 @@ __global__ __launch_bounds__(kScanThreads) void scan_down_kernel(const TI* __res
     __syncthreads();
     pre = red[0] + red[1] + red[2] + red[3];
     if (total && threadIdx.x == 0 && (int)blockIdx.x == m - 1) *total = pre + part[blockIdx.x];
-    // Blocked arrangement: thread t owns items [t*16, t*16+16) of the tile.
-    const long long base = (long long)blockIdx.x * kScanTile + (long long)threadIdx.x * kScanItems;
-    unsigned long long v[kScanItems];
-    unsigned long long s = 0;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-        const long long idx = base + k;
-        v[k] = idx < n ? (unsigned long long)in[idx] : 0ull;
-        s += v[k];
-    }
+    const unsigned long long s = (unsigned long long)v.x + v.y + v.z + v.w;
     const unsigned long long incl = block_incl_scan(s, wsum);
-    unsigned long long run = pre + incl - s;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-        const long long idx = base + k;
-        if (idx < n) out[idx] = (TO)run;
-        run += v[k];
+    uint4 o;
+    o.x = (unsigned)(pre + incl - s);
+    o.y = o.x + v.x;
+    o.z = o.y + v.y;
+    o.w = o.z + v.z;
+    if (idx + 4 <= n) {
+        *reinterpret_cast<uint4*>(out + idx) = o;
+    } else {
+        if (idx < n) out[idx] = o.x;
+        if (idx + 1 < n) out[idx + 1] = o.y;
+        if (idx + 2 < n) out[idx + 2] = o.z;
     }
 }
 
-template <typename TI, typename TO>
-hipError_t exclusive_scan(const TI* in, TO* out, long long n, unsigned long long* part,
+hipError_t exclusive_scan(const unsigned* in, unsigned* out, long long n, unsigned long long* part,
                           unsigned long long* total, hipStream_t st)
 {
     const int m = (int)((n + kScanTile - 1) / kScanTile);
     if (m == 0) return hipMemsetAsync(total, 0, sizeof(unsigned long long), st);
-    scan_reduce_kernel<TI><<<m, kScanThreads, 0, st>>>(in, n, part);
-    scan_down_kernel<TI, TO><<<m, kScanThreads, 0, st>>>(in, out, n, part, m, total);
+    scan_reduce_kernel<<<m, kScanThreads, 0, st>>>(in, n, part);
+    scan_down_kernel<<<m, kScanThreads, 0, st>>>(in, out, n, part, m, total);
     return hipGetLastError();
 }
 
@@ -160,13 +163,13 @@ hipError_t exclusive_scan(const TI* in, TO* out, long long n, unsigned long long
 __global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __restrict__ by_depth,
                                                            const ushort4* __restrict__ rects,
                                                            ushort4* __restrict__ rect_sorted,
-                                                           unsigned long long* __restrict__ cnt_sorted)
+                                                           unsigned* __restrict__ cnt_sorted)
 {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
     const ushort4 rc = rects[by_depth[k]];
     rect_sorted[k] = rc;
-    cnt_sorted[k] = (unsigned long long)(rc.z - rc.x) * (unsigned long long)(rc.w - rc.y);
+    cnt_sorted[k] = (unsigned)(rc.z - rc.x) * (unsigned)(rc.w - rc.y);
 }
 
 // Emission: one wave per 64 consecutive depth ranks. Their pairs are
@@ -193,7 +196,7 @@ __device__ __forceinline__ int wave_max_scan(int x)  // inclusive, ascending lan
 template <typename K>
 __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, const int* __restrict__ by_depth,
                                                      const ushort4* __restrict__ rect_sorted,
-                                                     const unsigned long long* __restrict__ emit_off, int GX,
+                                                     const unsigned* __restrict__ emit_off, int GX,
                                                      K* __restrict__ keys, int* __restrict__ vals)
 {
     __shared__ ushort4 rc[kWave];
@@ -202,16 +205,17 @@ __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, c
     __shared__ int mark[kWave];         // per step: 1 + lane of the splat starting at the position, or 0
     const int lane = threadIdx.x;
     const int k0 = blockIdx.x * kWave, k = k0 + lane;
-    const unsigned long long my_off = k < n ? emit_off[k] : (unsigned long long)n_pairs;
-    const unsigned long long p0 = emit_off[k0];
-    const unsigned long long p1 = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned long long)n_pairs;
+    // the pair count is below 2^31 here (checked before emission)
+    const unsigned my_off = k < n ? emit_off[k] : (unsigned)n_pairs;
+    const unsigned p0 = emit_off[k0];
+    const unsigned p1 = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned)n_pairs;
     const ushort4 b = k < n ? rect_sorted[k] : make_ushort4(0, 0, 0, 0);
     const unsigned my_cnt = (unsigned)(b.z - b.x) * (unsigned)(b.w - b.y);
-    const unsigned my_rel = (unsigned)(my_off - p0);  // the wave's pairs number below 2^31
+    const unsigned my_rel = my_off - p0;
     rc[lane] = b;
     rstart[lane] = my_rel;
     sid[lane] = k < n ? by_depth[k] : 0;
-    const unsigned total = (unsigned)(p1 - p0);
+    const unsigned total = p1 - p0;
     int carry = 0;
     for (unsigned q = 0; q < total; q += kWave) {
         mark[lane] = 0;
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, c
                 ++row;
                 col -= (int)wdt;
             }
-            const unsigned long long p = p0 + rel_p;
+            const unsigned p = p0 + rel_p;
             keys[p] = (K)((bs.y + row) * GX + bs.x + col);
             vals[p] = sid[s];
         }
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(256) void ranges_kernel(const K* __restrict__ keys,
 // After the count check: splat_offsets[i] = first slot of splat i's (splat,
 // tile) pairs, [n] = the pair count (0 without splats); tile_ranges cleared
 // (the ranges pass fills the non-empty tiles).
-__global__ __launch_bounds__(256) void outputs_kernel(int n, int tiles, const unsigned long long* __restrict__ offsets,
+__global__ __launch_bounds__(256) void outputs_kernel(int n, int tiles, const unsigned* __restrict__ offsets,
                                                       const unsigned long long* __restrict__ pairs,
                                                       int* __restrict__ splat_offsets, int* __restrict__ tile_ranges)
 {
@@ -460,9 +464,9 @@ BinLayout bin_layout(long long n, long long cap)
     const long long scan_items = n > (long long)kRadix * nwg_sort ? n : (long long)kRadix * nwg_sort;
     const long long nparts = (scan_items + kScanTile - 1) / kScanTile + 1;
     const size_t n1 = (size_t)(n > 0 ? n : 1), c1 = (size_t)(cap > 0 ? cap : 1);
-    L.counts = o;     o += align256(sizeof(unsigned long long) * n1);
+    L.counts = o;     o += align256(sizeof(unsigned) * n1);
     L.rects = o;      o += align256(sizeof(ushort4) * n1);
-    L.offsets = o;    o += align256(sizeof(unsigned long long) * n1);
+    L.offsets = o;    o += align256(sizeof(unsigned) * n1);
     L.part = o;       o += align256(sizeof(unsigned long long) * (size_t)nparts);
     L.total = o;      o += align256(sizeof(unsigned long long));
     L.pairs = o;      o += align256(sizeof(unsigned long long));  // the pair count, kept apart from the scans' totals
@@ -471,8 +475,8 @@ BinLayout bin_layout(long long n, long long cap)
     L.dvals_a = o;    o += align256(sizeof(int) * n1);
     L.dvals_b = o;    o += align256(sizeof(int) * n1);
     L.rect_sorted = o; o += align256(sizeof(ushort4) * n1);
-    L.cnt_sorted = o; o += align256(sizeof(unsigned long long) * n1);
-    L.emit_off = o;   o += align256(sizeof(unsigned long long) * n1);
+    L.cnt_sorted = o; o += align256(sizeof(unsigned) * n1);
+    L.emit_off = o;   o += align256(sizeof(unsigned) * n1);
     L.keys_a = o;     o += align256(sizeof(unsigned) * c1);
     L.keys_b = o;     o += align256(sizeof(unsigned) * c1);
     L.vals_tmp = o;   o += align256(sizeof(int) * c1);
@@ -490,7 +494,7 @@ hipError_t radix_pass_b(const K* kin, const int* vin, K* kout, int* vout, long l
     radix_hist_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = exclusive_scan<unsigned, unsigned>(hist, hist, (long long)(1 << BITS) * nwg, part, total, st);
+    e = exclusive_scan(hist, hist, (long long)(1 << BITS) * nwg, part, total, st);
     if (e != hipSuccess) return e;
     radix_scatter_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
     return hipGetLastError();
@@ -513,7 +517,7 @@ hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long lon
 // values into sorted_ids) and the ranges, with keys of type K.
 template <typename K>
 hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rect_sorted,
-                     const unsigned long long* emit_off, int GX, int np, int pb, K* keys_a, K* keys_b, int* vals_t,
+                     const unsigned* emit_off, int GX, int np, int pb, K* keys_a, K* keys_b, int* vals_t,
                      int* sorted_ids, unsigned* hist, unsigned long long* part, unsigned long long* total,
                      int2* tile_ranges, hipStream_t st)
 {
@@ -610,8 +614,8 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     const int GX = grid_x(width), GY = grid_y(height);
     const int tiles = GX * GY;
     char* ws = (char*)workspace;
-    auto* counts = (unsigned long long*)(ws + L.counts);
-    auto* offsets = (unsigned long long*)(ws + L.offsets);
+    auto* counts = (unsigned*)(ws + L.counts);
+    auto* offsets = (unsigned*)(ws + L.offsets);
     auto* part = (unsigned long long*)(ws + L.part);
     auto* total = (unsigned long long*)(ws + L.total);
     auto* rects = (ushort4*)(ws + L.rects);
@@ -623,8 +627,8 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     auto* dvb = (int*)(ws + L.dvals_b);
     auto* hist = (unsigned*)(ws + L.hist);
     auto* rect_sorted = (ushort4*)(ws + L.rect_sorted);
-    auto* cnt_sorted = (unsigned long long*)(ws + L.cnt_sorted);
-    auto* emit_off = (unsigned long long*)(ws + L.emit_off);
+    auto* cnt_sorted = (unsigned*)(ws + L.cnt_sorted);
+    auto* emit_off = (unsigned*)(ws + L.emit_off);
     const int* by_depth = dva;
 
     // The pair count is read back with an asynchronous copy into pinned host
@@ -637,7 +641,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, counts,
                                                       rects);
         GS_HIP(hipGetLastError());
-        GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(counts, offsets, n, part, pairs, st)));
+        GS_HIP(exclusive_scan(counts, offsets, n, part, pairs, st));
         unsigned long long* pin = pinned_count();
         CountEvent ev;
         if (pin) {
@@ -665,7 +669,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         // Emission offsets in depth order.
         gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
         GS_HIP(hipGetLastError());
-        GS_HIP((exclusive_scan<unsigned long long, unsigned long long>(cnt_sorted, emit_off, n, part, total, st)));
+        GS_HIP(exclusive_scan(cnt_sorted, emit_off, n, part, total, st));
         if (pin) {
             GS_HIP(hipEventSynchronize(ev.e));
             h_total = *pin;
