@@ -249,6 +249,17 @@ def test_no_splats_and_no_intersections():
     assert b0.n_isect == 0
 
 
+@pytest.mark.parametrize("W,H", [(4096, 4096), (4112, 4112)])
+def test_binning_large_grids(W, H):
+    """65536 tiles (the largest grid sorted with 16-bit tile keys, tile ids up to
+    0xffff) and 66049 tiles (32-bit keys, three 6-bit tile passes)."""
+    sc = _custom(11, W, H, 3000, sig=(2.0, 40.0), pad=50)
+    _say(f"large grid {W}x{H}: binning")
+    bins = gpu_bins(sc)
+    check_bins(sc, bins)
+    assert bins.n_isect > 10000
+
+
 def test_binning_capacity_retry():
     sc = scenes.make_scene("tiny", 0)
     bins = gsr.gs_bin_tiles(_dev(sc.means2d), _dev(sc.radii), _dev(sc.depths), sc.width, sc.height,
