@@ -5,22 +5,25 @@
 // 計測結果: emit_pairs, radix_hist, radix_scatter, extract_offsets):
 //   1. count   one thread per splat: float32 tile rectangle, number of tiles
 //   2. scan    exclusive prefix sum of the counts in splat order (device-wide,
-//              64-bit): each splat's first pair slot, splat_offsets
-//   3. host    read the total back (the call's only synchronisation)
+//              32-bit items and offsets, sums and the total in 64 bits): each
+//              splat's first pair slot, splat_offsets
+//   3. host    read the total back (the call's only synchronisation; the
+//              depth sort is already queued behind the copy)
 //   4. depth   stable LSD radix sort of the splats by the bit pattern of their
 //              depth (32 bits, 8-bit digits), splat ids starting in id order
 //   5. emit    the splats' tile rectangles (stored by the count pass) and
 //              counts gathered into depth order and scanned; the splat of
 //              depth rank k writes its tiles, row-major, at that offset, as
-//              (32-bit tile id, splat id)
+//              (tile id, splat id), tile ids 16-bit up to 65536 tiles
 //   6. tiles   stable LSD radix sort of the pairs by tile id over only the
-//              ceil(log2(tiles)) bits it can have (2 passes of 8-bit digits up
-//              to 65536 tiles). Stability keeps each tile's pairs in depth
-//              order, equal depths by ascending splat id.
+//              ceil(log2(tiles)) bits it can have, split evenly over as few
+//              passes as 8-bit digits allow (two 6-bit passes at 4056 tiles).
+//              Stability keeps each tile's pairs in depth order, equal depths
+//              by ascending splat id.
 //   7. ranges  [start, end) per tile from the boundaries of the sorted keys
 // Sorting the splats by depth first moves the 32 depth bits off the pairs:
 // the passes over all pairs fall from six (tile and depth bits together) to
-// two, over 8-byte instead of 12-byte elements.
+// two, over 6-byte instead of 12-byte elements.
 #include "gs_common.hpp"
 
 namespace gs {
