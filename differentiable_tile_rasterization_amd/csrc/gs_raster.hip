@@ -1254,60 +1254,117 @@ __device__ __forceinline__ void gather_write(int i, const float (&u)[10], const 
     if (AW) accum_w[i] = u[9];
 }
 
-// Gather for short pair ranges (a few tiles per splat): one thread per
-// splat sums its used slots in slot order, reading the flags four at a time.
-// (Batching the record requests of several slots costs registers, and with
-// them occupancy, for no gain at a few pairs per splat.)
-template <bool AW>
-__global__ __launch_bounds__(256) void gather_splat_kernel(int n, const int* __restrict__ splat_offsets,
-                                                           long long n_slots, const float4* __restrict__ rec,
-                                                           const unsigned* __restrict__ words,
-                                                           const float* __restrict__ conics,
-                                                           const float* __restrict__ opac,
-                                                           float2* __restrict__ d_means, float* __restrict__ d_conics,
-                                                           float* __restrict__ d_colors, float* __restrict__ d_opac,
-                                                           float* __restrict__ accum_w)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const long long s0 = min(max(0ll, (long long)splat_offsets[i]), n_slots);
-    const long long s1 = min(max(s0, (long long)splat_offsets[i + 1]), n_slots);
-    float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (long long wi = s0 >> 2; wi < (s1 + 3) >> 2; ++wi) {
-        const unsigned fl = words[wi];
-        if (fl == 0u) continue;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const long long sl = 4 * wi + b;
-            if (((fl >> (8 * b)) & 0xffu) && sl >= s0 && sl < s1) {
-                const float4 ra = rec[3 * sl + 0], rb = rec[3 * sl + 1], rc = rec[3 * sl + 2];
-                u[0] += ra.x; u[1] += ra.y; u[2] += ra.z; u[3] += ra.w;
-                u[4] += rb.x; u[5] += rb.y; u[6] += rb.z; u[7] += rb.w;
-                u[8] += rc.x; u[9] += rc.y;
-            }
-        }
-    }
-    gather_write<AW>(i, u, conics, opac, d_means, d_conics, d_colors, d_opac, accum_w);
-}
-
-// Gather for long pair ranges: one wave per 64 consecutive splats. Their
-// pairs are contiguous,
+// Gathers: one wave per 64 consecutive splats. Their pairs are contiguous,
 // [offsets[i0], offsets[i0 + 64]), and most pair slots are unused (78% on the
 // 2M-splat scene, 98% on the 1M-splat high-overlap scene, where early stop
-// leaves most of each tile list unwalked), so the wave first scans the flag
-// bytes together, 16 per lane (1 KB per step, coalesced, the next kilobyte
-// requested before the current one is used), and compacts the used pair
-// indices into an LDS list in pair order. It then takes the listed pairs 64
-// at a time, one per lane: the slot's record, the pair's splat (binary search
-// in the wave's copy of the offsets), and an LDS add into that splat's sums.
-// Finally lane l applies splat i0 + l's conic and opacity and writes every
-// output (zeros for a splat no pixel took).
+// leaves most of each tile list unwalked), so the wave scans the flag bytes
+// together, 16 per lane (1 KB per step, coalesced, the next kilobyte requested
+// before the current one is used), and compacts the used pair positions into
+// an LDS list in pair order. Then, for a few pairs per splat (gather_kernel),
+// lane l finds the part of the list that belongs to splat i0 + l (a binary
+// search for its first pair; the next lane's start ends it) and adds those
+// records in registers, two at a time, in slot order. For many (large splats:
+// a kilobyte of flags then holds only a few splats' pairs, and few lanes
+// would have work), gather_lds_kernel takes the listed pairs 64 at a time,
+// one per lane: the slot's record, the pair's splat (binary search in the
+// wave's copy of the offsets), and LDS adds into that splat's sums. Finally
+// lane l applies its splat's conic and opacity and writes every output (zeros
+// for a splat no pixel took).
 constexpr int kGatherWin = 16 * kWave;  // flag bytes scanned per step
-constexpr int kGatherSplatMaxPairs = 16;  // mean pairs per splat up to which one thread takes a splat
-constexpr int kWalkStoreMinPairs = 16;    // mean pairs per splat above which the stored-partials walk runs
+constexpr int kGatherRegMaxPairs = 32;  // mean pairs per splat up to which gather_kernel runs
+constexpr int kWalkStoreMinPairs = 16;  // mean pairs per splat above which the stored-partials walk runs
 
 template <bool AW>
 __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
+                                                       const float4* __restrict__ rec,
+                                                       const uint4* __restrict__ flags16,
+                                                       const float* __restrict__ conics, const float* __restrict__ opac,
+                                                       float2* __restrict__ d_means, float* __restrict__ d_conics,
+                                                       float* __restrict__ d_colors, float* __restrict__ d_opac,
+                                                       float* __restrict__ accum_w)
+{
+    __shared__ int used_list[kGatherWin];  // used pairs of the current window, relative to its start
+    const int lane = threadIdx.x;
+    const int i0 = blockIdx.x * kWave;
+    const int i = i0 + lane;
+    const long long my_off = min(max((long long)splat_offsets[min(i, n)], 0ll), n_slots);
+    const long long p0 = __shfl(my_off, 0, kWave);
+    const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
+    float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    auto add_rec = [&](long long P) {
+        const float4 a = rec[3 * P + 0], b = rec[3 * P + 1];
+        const float2 c = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
+        u[0] += a.x; u[1] += a.y; u[2] += a.z; u[3] += a.w;
+        u[4] += b.x; u[5] += b.y; u[6] += b.z; u[7] += b.w;
+        u[8] += c.x;
+        if (AW) u[9] += c.y;
+    };
+    const long long w0 = p0 & ~15ll;  // windows start on 16-byte flag boundaries
+    auto window = [&](long long wb) -> uint4 {
+        const long long q = wb + 16 * lane;
+        return q < p1 ? flags16[q >> 4] : make_uint4(0, 0, 0, 0);
+    };
+    uint4 fl_next = w0 < p1 ? window(w0) : make_uint4(0, 0, 0, 0);
+    for (long long wb = w0; wb < p1; wb += kGatherWin) {
+        const uint4 fl = fl_next;
+        if (wb + kGatherWin < p1) fl_next = window(wb + kGatherWin);
+        // this lane's 16 flag bytes -> used pair positions, kept in [p0, p1)
+        const long long q = wb + 16 * lane;
+        const unsigned wd[4] = {fl.x, fl.y, fl.z, fl.w};
+        unsigned mask = 0;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const long long pb = q + b;
+            if (((wd[b >> 2] >> (8 * (b & 3))) & 0xffu) && pb >= p0 && pb < p1) mask |= 1u << b;
+        }
+        // compaction: exclusive prefix of the per-lane counts over the wave
+        const int cnt = __popc(mask);
+        int incl = cnt;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += v;
+        }
+        const int total = __shfl(incl, kWave - 1, kWave);
+        if (total == 0) continue;  // wave-uniform
+        int pos = incl - cnt;
+        while (mask) {
+            const int b = __builtin_ctz(mask);
+            mask &= mask - 1;
+            used_list[pos++] = 16 * lane + b;
+        }
+        __syncthreads();
+        // this splat's part of the list: from the first listed pair at or
+        // after its first slot to the next splat's start
+        const long long rel = my_off - wb;
+        int beg = 0;
+        if (i >= n || rel >= (long long)kGatherWin) {
+            beg = total;
+        } else if (rel > 0) {
+            int lo = 0, hi = total;  // first r with used_list[r] >= rel
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (used_list[mid] < (int)rel) lo = mid + 1; else hi = mid;
+            }
+            beg = lo;
+        }
+        int end = __shfl_down(beg, 1, kWave);
+        if (lane == kWave - 1) end = total;
+        end = max(end, beg);
+        int r = beg;
+        for (; r + 1 < end; r += 2) {
+            add_rec(wb + used_list[r]);
+            add_rec(wb + used_list[r + 1]);
+        }
+        if (r < end) add_rec(wb + used_list[r]);
+        __syncthreads();  // used_list is rewritten by the next window
+    }
+    if (i >= n) return;
+    if (!AW) u[9] = 0.0f;
+    gather_write<AW>(i, u, conics, opac, d_means, d_conics, d_colors, d_opac, accum_w);
+}
+
+template <bool AW>
+__global__ __launch_bounds__(kWave) void gather_lds_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
                                                        const float4* __restrict__ rec,
                                                        const uint4* __restrict__ flags16,
                                                        const float* __restrict__ conics, const float* __restrict__ opac,
@@ -1550,30 +1607,18 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         GS_HIP(mark(2));
     }
     const uint4* flags16 = reinterpret_cast<const uint4*>(used);  // padded to whole 16-byte units
-    const unsigned* words = reinterpret_cast<const unsigned*>(used);
-    // A few pairs per splat: one thread per splat. Many (large splats): one
-    // wave per 64 splats scanning their flags together.
-    if (n_isect <= (long long)kGatherSplatMaxPairs * n) {
-        const unsigned gb = (unsigned)((n + 255) / 256);
-        if (aw)
-            gather_splat_kernel<true><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, slots, words, conics,
-                                                          opacities, (float2*)dL_dmeans2d, dL_dconics, dL_dcolors,
-                                                          dL_dopacities, accum_weight);
-        else
-            gather_splat_kernel<false><<<gb, 256, 0, st>>>(n, splat_offsets, n_isect, slots, words, conics,
-                                                           opacities, (float2*)dL_dmeans2d, dL_dconics, dL_dcolors,
-                                                           dL_dopacities, nullptr);
+    const unsigned gb = (unsigned)((n + kWave - 1) / kWave);
+#define GS_GATHER(K, AWV, ACC)                                                                                    \
+    K<AWV><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities, (float2*)dL_dmeans2d, \
+                                 dL_dconics, dL_dcolors, dL_dopacities, ACC)
+    if (n_isect <= (long long)kGatherRegMaxPairs * n) {
+        if (aw) GS_GATHER(gather_kernel, true, accum_weight);
+        else GS_GATHER(gather_kernel, false, nullptr);
     } else {
-        const unsigned gb = (unsigned)((n + kWave - 1) / kWave);
-        if (aw)
-            gather_kernel<true><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities,
-                                                      (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities,
-                                                      accum_weight);
-        else
-            gather_kernel<false><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities,
-                                                       (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities,
-                                                       nullptr);
+        if (aw) GS_GATHER(gather_lds_kernel, true, accum_weight);
+        else GS_GATHER(gather_lds_kernel, false, nullptr);
     }
+#undef GS_GATHER
     GS_HIP(hipGetLastError());
     GS_HIP(mark(3));
     return GS_OK;
