@@ -1260,16 +1260,15 @@ __device__ __forceinline__ void gather_write(int i, const float (&u)[10], const 
 // leaves most of each tile list unwalked), so the wave scans the flag bytes
 // together, 16 per lane (1 KB per step, coalesced, the next kilobyte requested
 // before the current one is used), and compacts the used pair positions into
-// an LDS list in pair order. Then, for a few pairs per splat (gather_kernel),
-// lane l finds the part of the list that belongs to splat i0 + l (a binary
-// search for its first pair; the next lane's start ends it) and adds those
-// records in registers, two at a time, in slot order. For many (large splats:
-// a kilobyte of flags then holds only a few splats' pairs, and few lanes
-// would have work), gather_lds_kernel takes the listed pairs 64 at a time,
-// one per lane: the slot's record, the pair's splat (binary search in the
-// wave's copy of the offsets), and LDS adds into that splat's sums. Finally
-// lane l applies its splat's conic and opacity and writes every output (zeros
-// for a splat no pixel took).
+// an LDS list in pair order. Lane l finds the part of the list that belongs
+// to splat i0 + l (a binary search for its first pair; the next lane's start
+// ends it) and sums it in registers, in slot order. For a few pairs per splat
+// (gather_kernel) each lane loads its own records, two at a time. For many
+// (large splats: a kilobyte of flags then holds only a dozen splats' pairs,
+// and few lanes would load), gather_staged_kernel loads the listed records one
+// per lane, every lane busy, stages them in LDS, and each lane then adds its
+// splat's part from there. Finally lane l applies its splat's conic and
+// opacity and writes every output (zeros for a splat no pixel took).
 constexpr int kGatherWin = 16 * kWave;  // flag bytes scanned per step
 constexpr int kGatherRegMaxPairs = 32;  // mean pairs per splat up to which gather_kernel runs
 constexpr int kWalkStoreMinPairs = 16;  // mean pairs per splat above which the stored-partials walk runs
@@ -1364,27 +1363,25 @@ __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restr
 }
 
 template <bool AW>
-__global__ __launch_bounds__(kWave) void gather_lds_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
-                                                       const float4* __restrict__ rec,
-                                                       const uint4* __restrict__ flags16,
-                                                       const float* __restrict__ conics, const float* __restrict__ opac,
-                                                       float2* __restrict__ d_means, float* __restrict__ d_conics,
-                                                       float* __restrict__ d_colors, float* __restrict__ d_opac,
-                                                       float* __restrict__ accum_w)
+__global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* __restrict__ splat_offsets,
+                                                              long long n_slots, const float4* __restrict__ rec,
+                                                              const uint4* __restrict__ flags16,
+                                                              const float* __restrict__ conics,
+                                                              const float* __restrict__ opac,
+                                                              float2* __restrict__ d_means,
+                                                              float* __restrict__ d_conics,
+                                                              float* __restrict__ d_colors,
+                                                              float* __restrict__ d_opac, float* __restrict__ accum_w)
 {
-    constexpr int kF = AW ? 10 : 9;
-    __shared__ long long offs[kWave + 1];
-    __shared__ float acc[kWave][kF];
     __shared__ int used_list[kGatherWin];  // used pairs of the current window, relative to its start
+    __shared__ float4 stage[kWave][3];     // records of up to 64 listed pairs
     const int lane = threadIdx.x;
     const int i0 = blockIdx.x * kWave;
     const int i = i0 + lane;
-    offs[lane] = min(max((long long)splat_offsets[min(i, n)], 0ll), n_slots);
-    if (lane == 0) offs[kWave] = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
-#pragma unroll
-    for (int f = 0; f < kF; ++f) acc[lane][f] = 0.0f;
-    __syncthreads();
-    const long long p0 = offs[0], p1 = offs[kWave];
+    const long long my_off = min(max((long long)splat_offsets[min(i, n)], 0ll), n_slots);
+    const long long p0 = __shfl(my_off, 0, kWave);
+    const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
+    float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     const long long w0 = p0 & ~15ll;  // windows start on 16-byte flag boundaries
     auto window = [&](long long wb) -> uint4 {
         const long long q = wb + 16 * lane;
@@ -1407,10 +1404,11 @@ __global__ __launch_bounds__(kWave) void gather_lds_kernel(int n, const int* __r
         const int cnt = __popc(mask);
         int incl = cnt;
         for (int d = 1; d < kWave; d <<= 1) {
-            const int u = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += u;
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += v;
         }
         const int total = __shfl(incl, kWave - 1, kWave);
+        if (total == 0) continue;  // wave-uniform
         int pos = incl - cnt;
         while (mask) {
             const int b = __builtin_ctz(mask);
@@ -1418,32 +1416,48 @@ __global__ __launch_bounds__(kWave) void gather_lds_kernel(int n, const int* __r
             used_list[pos++] = 16 * lane + b;
         }
         __syncthreads();
+        // this splat's part of the list: from the first listed pair at or
+        // after its first slot to the next splat's start
+        const long long rel = my_off - wb;
+        int beg = 0;
+        if (i >= n || rel >= (long long)kGatherWin) {
+            beg = total;
+        } else if (rel > 0) {
+            int lo = 0, hi = total;  // first r with used_list[r] >= rel
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (used_list[mid] < (int)rel) lo = mid + 1; else hi = mid;
+            }
+            beg = lo;
+        }
+        int end = __shfl_down(beg, 1, kWave);
+        if (lane == kWave - 1) end = total;
+        end = max(end, beg);
+        // the listed records, 64 at a time: loaded one per lane (every lane
+        // busy), staged in LDS, and summed by their splats' lanes in order
         for (int r0 = 0; r0 < total; r0 += kWave) {
             const int r = r0 + lane;
             if (r < total) {
                 const long long P = wb + used_list[r];
-                const float4 a = rec[3 * P + 0], b = rec[3 * P + 1], c = rec[3 * P + 2];
-                // the pair's splat: the last local index s with offs[s] <= P
-                int lo = 0, hi = kWave - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (offs[mid] <= P) lo = mid; else hi = mid - 1;
-                }
-                float* A = acc[lo];
-                atomicAdd(&A[0], a.x); atomicAdd(&A[1], a.y); atomicAdd(&A[2], a.z); atomicAdd(&A[3], a.w);
-                atomicAdd(&A[4], b.x); atomicAdd(&A[5], b.y); atomicAdd(&A[6], b.z); atomicAdd(&A[7], b.w);
-                atomicAdd(&A[8], c.x);
-                if (AW) atomicAdd(&A[kF - 1], c.y);
+                stage[lane][0] = rec[3 * P + 0];
+                stage[lane][1] = rec[3 * P + 1];
+                stage[lane][2] = rec[3 * P + 2];
             }
+            __syncthreads();
+            const int k1 = min(end, r0 + kWave);
+            for (int k = max(beg, r0); k < k1; ++k) {
+                const float4 a = stage[k - r0][0], b = stage[k - r0][1], c = stage[k - r0][2];
+                u[0] += a.x; u[1] += a.y; u[2] += a.z; u[3] += a.w;
+                u[4] += b.x; u[5] += b.y; u[6] += b.z; u[7] += b.w;
+                u[8] += c.x;
+                if (AW) u[9] += c.y;
+            }
+            __syncthreads();  // stage is rewritten by the next round
         }
         __syncthreads();  // used_list is rewritten by the next window
     }
-    __syncthreads();
     if (i >= n) return;
-    float u[10];
-#pragma unroll
-    for (int f = 0; f < 9; ++f) u[f] = acc[lane][f];
-    u[9] = AW ? acc[lane][kF - 1] : 0.0f;
+    if (!AW) u[9] = 0.0f;
     gather_write<AW>(i, u, conics, opac, d_means, d_conics, d_colors, d_opac, accum_w);
 }
 
@@ -1615,8 +1629,8 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         if (aw) GS_GATHER(gather_kernel, true, accum_weight);
         else GS_GATHER(gather_kernel, false, nullptr);
     } else {
-        if (aw) GS_GATHER(gather_lds_kernel, true, accum_weight);
-        else GS_GATHER(gather_lds_kernel, false, nullptr);
+        if (aw) GS_GATHER(gather_staged_kernel, true, accum_weight);
+        else GS_GATHER(gather_staged_kernel, false, nullptr);
     }
 #undef GS_GATHER
     GS_HIP(hipGetLastError());
