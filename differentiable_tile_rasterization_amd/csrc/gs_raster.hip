@@ -197,7 +197,6 @@ static_assert(sizeof(StoreSlot) == 48 && offsetof(StoreSlot, pos) == 36, "StoreS
 
 constexpr int kBatch = kBlock - 1;                                    // entries staged per batch, at most
 constexpr int kDummy = kBlock - 1;                                    // slot of the dummy entry
-constexpr unsigned short kDummyOff = (unsigned short)(kDummy * sizeof(StoreSlot));
 constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummies read ahead of use
 
 // Partial sums: one record of kRaw (or kRaw - 1 without the weight) floats per
@@ -208,8 +207,17 @@ constexpr int kListLen = kBlock + 4;  // list row: up to 255 entries, then dummi
 // of about 340 half-list entries.
 template <bool AW> struct BwdParts {
     static constexpr int kF = AW ? kRaw : kRaw - 1;  // floats per record
-    static constexpr int kCap = AW ? 248 : 276;      // records per batch (at most 26 KB of LDS in all: six workgroups per CU)
+    static constexpr int kCap = AW ? 453 : 503;      // records per batch (at most 26 KB of LDS in all: six workgroups per CU)
 };
+
+// The stored-partials walk stages at most 127 entries per batch (waves 0 and
+// 1; slot 127 is the dummy): the records, not the slots, bound its batches
+// (a 255-entry batch holds a median of ~590 half-list entries on the
+// high-overlap scene), and the LDS the smaller slots free holds more records.
+constexpr int kSBatch = 127;
+constexpr int kSSlots = kSBatch + 1;
+constexpr int kSListLen = kSBatch + 5;  // list row: up to 127 entries, then dummies read ahead of use
+constexpr unsigned short kSDummyOff = (unsigned short)(kSBatch * sizeof(StoreSlot));
 
 // Per-half lists of the staged slots whose hit bit is set, as slot byte
 // offsets in descending slot order (the walk's order); each listed entry's
@@ -217,7 +225,7 @@ template <bool AW> struct BwdParts {
 // per-wave counts also ORs `flag` over the workgroup, which is returned, and
 // gives every half's list length (len, wave-uniform). Ends with a barrier.
 __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bool flag, StoreSlot* S,
-                                                 unsigned short (*list)[kListLen], int (*cnt)[kHalves + 1],
+                                                 unsigned short (*list)[kSListLen], int (*cnt)[kHalves + 1],
                                                  int (&len)[kHalves])
 {
     const int lane = threadIdx.x & 63;
@@ -243,7 +251,7 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
         }
         top = tot - 1 - below;
     }
-    *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(0xffffffffu, 0xffffffffu);
+    if (threadIdx.x < kSSlots) *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(0xffffffffu, 0xffffffffu);
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
         len[q] = __builtin_amdgcn_readlane(tot, q);
@@ -272,9 +280,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 {
     using PP = BwdParts<AW>;
     constexpr int kF = PP::kF, kCap = PP::kCap;
-    __shared__ StoreSlot S[kBlock];
+    __shared__ StoreSlot S[kSSlots];
     __shared__ float parts[kCap * kF];
-    __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
+    __shared__ unsigned short list[kHalves][kSListLen];  // per half: slots that may touch it, then dummies
     __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
     __shared__ int half_end[kHalves];
     __shared__ int half_base[kHalves];                 // first partial record of each half, for the flush
@@ -313,9 +321,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     for (int off = 16; off > 0; off >>= 1) hmax = max(hmax, __shfl_xor(hmax, off, 64));
     if ((lane & 31) == 0) half_end[hq] = hmax;
     if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel
-        S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
-        S[kDummy].c = 0.0f;
+        S[kSBatch].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        S[kSBatch].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
+        S[kSBatch].c = 0.0f;
     }
     __syncthreads();
     int hend[kHalves];  // walk end of every half, wave-uniform
@@ -347,9 +355,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     // records are cleared only after the next barrier.
     int hi = tmax;  // the batches cover [0, tmax) from the top down
     while (hi > 0) {
-        const int lo = max(0, hi - kBatch);  // candidates [lo, hi): entry lo + t in slot t
+        const int lo = max(0, hi - kSBatch);  // candidates [lo, hi): entry lo + t in slot t
         const int k = lo + (int)threadIdx.x;
-        const bool cand = (int)threadIdx.x < kBatch && k < hi;
+        const bool cand = (int)threadIdx.x < kSBatch && k < hi;
         int id = -1, radius = 0;
         SplatRec r;
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -362,8 +370,8 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
         }
-        bool hit[kHalves];
-        half_hits(r, ox, oy, k, hend, hit);
+        bool hit[kHalves] = {false, false, false, false, false, false, false, false};
+        if (threadIdx.x < kSSlots) half_hits(r, ox, oy, k, hend, hit);  // waves 0, 1: the candidates' waves
         // Keep the top candidates whose half-list entries fit the partial
         // records: suffix sums of the hit counts over the slots, from the top.
         int hc = 0;
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             if (lane + off < kWave) suf += u;
         }
         if (lane == 0) wave_hits[wv] = suf;
-        if (threadIdx.x == 0) cut = kBatch;
+        if (threadIdx.x == 0) cut = kSBatch;
         __syncthreads();
         for (int w2 = wv + 1; w2 < 4; ++w2) suf += wave_hits[w2];
         const bool keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
                     (long long)__float_as_int(r.c.w) + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
                 if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && sl >= 0 && sl < n_slots) slot = (int)sl;
             }
-            S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
+            if (threadIdx.x < kSSlots) S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
         }
         // Can any entry of the batch reach the 0.99 clamp? alpha_raw =
         // exp2(log2 o - q) with q >= 0 never exceeds exp2(log2 o) (the same
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
         // the shorter half takes the dummy entry once its list is exhausted
         // (and both read up to four entries past the end, ahead of use)
-        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDummyOff;
+        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kSDummyOff;
         // batch slots below this pixel's walk end, as a byte offset bound
         const int ncb_off = (nc - lo) * (int)sizeof(StoreSlot);
         const unsigned short* L = list[hq];
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 
         // Flush: thread t owns the entry it staged; its sums are those of the
         // records of the halves that listed it.
-        const int slot = S[threadIdx.x].slot;
+        const int slot = threadIdx.x < kSSlots ? S[threadIdx.x].slot : -1;
         if (slot >= 0) {
             const uint2 pw = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
             float u[kRaw] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
