@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 #   accumulated weight (optional):     +1 per composited pair
 FLOP_WALK = 13
 FLOP_CONTRIB = 45
-# fp32 VALU peak without packed FP32 forms (which this build must not use):
+# fp32 VALU peak without packed FP32 forms (the library is compiled without them):
 # 256 CUs x 4 SIMD x 16 lanes x 2 flops (FMA) x 2.4 GHz.
 PEAK_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
@@ -80,8 +80,8 @@ def main():
     ap.add_argument("--cpu-sample", type=float, default=1.0, help="fraction of tiles the oracle baseline runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the kernel has no multi-GPU "
-              "path in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
+              "path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -41,7 +41,7 @@ def stats(csv_path: str, out_md: str, command: str) -> None:
     rows = list(csv.DictReader(open(csv_path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["# Kernel time: " + os.path.basename(out_md).rsplit(".", 1)[0], "",
-             "Command (repo root, on the GPU box):", "", "    " + command, "",
+             "Command (repo root, on the MI355X host):", "", "    " + command, "",
              "| kernel | calls | avg us | min us | max us | total ms | % |",
              "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
@@ -81,7 +81,7 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
            "call_bytes_per_launch": total, "per_kernel": per, "commands": [cmd_fetch, cmd_write]}
     json.dump(rec, open(out_json, "w"), indent=1)
     lines = ["# HBM traffic (FETCH_SIZE / WRITE_SIZE), " + config, "",
-             "Commands (repo root, on the GPU box):", "", "    " + cmd_fetch, "    " + cmd_write, "",
+             "Commands (repo root, on the MI355X host):", "", "    " + cmd_fetch, "    " + cmd_write, "",
              f"Scale: the 1 GiB copy kernel reads {avg(fe[COPY_NAME]):.0f} KiB FETCH_SIZE and "
              f"{avg(wr[COPY_NAME]):.0f} KiB WRITE_SIZE per launch, so FETCH_SIZE is multiplied by "
              f"{f_scale:.3f} and WRITE_SIZE by {w_scale:.3f} to give bytes.", "",
@@ -108,7 +108,7 @@ def counters(out_md: str, prefix: str, *runs: str) -> None:
             vals[k if k != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE ({os.path.basename(d)})"] = v
         cmds.append(cmd)
     lines = [f"# Counters of {prefix} (last dispatch of each run, summed over the device)", "",
-             "Commands (repo root, on the GPU box):", ""] + ["    " + c for c in cmds] + [
+             "Commands (repo root, on the MI355X host):", ""] + ["    " + c for c in cmds] + [
              "", "| counter | value |", "|---|---:|"]
     lines += [f"| {k} | {v:.4g} |" for k, v in sorted(vals.items())]
     grbm = [v for k, v in vals.items() if k.startswith("GRBM_GUI_ACTIVE")]
