@@ -584,7 +584,8 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             if (any) {
                 rec_out[3 * (long long)slot + 0] = make_float4(u[0], u[1], u[2], u[3]);
                 rec_out[3 * (long long)slot + 1] = make_float4(u[4], u[5], u[6], u[7]);
-                rec_out[3 * (long long)slot + 2] = make_float4(u[8], AW ? u[9] : 0.0f, 0.0f, 0.0f);
+                // the third part's last 8 bytes are padding, never read
+                *reinterpret_cast<float2*>(rec_out + 3 * (long long)slot + 2) = make_float2(u[8], AW ? u[9] : 0.0f);
                 slot_used[slot] = 1;
             }
         }
@@ -904,7 +905,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
                 if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && slot >= 0 && slot < n_slots) {
                     rec_out[3 * slot + 0] = make_float4(Swr, Swg, Swb, Ss);
                     rec_out[3 * slot + 1] = make_float4(Sdx, Sdy, Sdxx, Sdxy);
-                    rec_out[3 * slot + 2] = make_float4(Sdyy, Sw, 0.0f, 0.0f);
+                    // the third part's last 8 bytes are padding, never read
+                    *reinterpret_cast<float2*>(rec_out + 3 * slot + 2) = make_float2(Sdyy, Sw);
                     slot_used[slot] = 1;
                 }
             }
@@ -1449,7 +1451,8 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
                 const long long P = wb + used_list[r];
                 stage[lane][0] = rec[3 * P + 0];
                 stage[lane][1] = rec[3 * P + 1];
-                stage[lane][2] = rec[3 * P + 2];
+                const float2 c2 = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
+                stage[lane][2] = make_float4(c2.x, c2.y, 0.0f, 0.0f);
             }
             __syncthreads();
             const int k1 = min(end, r0 + kWave);
