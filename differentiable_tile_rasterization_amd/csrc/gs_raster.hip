@@ -15,14 +15,15 @@
 //                 random ids; a record costs one 48-byte read per list entry
 //                 where the caller's four separate arrays cost about five
 //                 cache lines.
-//   staging       per batch of list entries (256 in the forward, 255 and a
-//                 dummy in the backward), thread t loads entry t's record,
-//                 writes the alpha coefficients and colour to LDS and tests
-//                 the splat's alpha >= 1/255 ellipse against each wave's
-//                 quadrant (forward) or each 8x4 half-quadrant (backward);
-//                 ballots build one compacted list per wave or half.
-//   walk          each wave (half) walks only its own list, reading the
-//                 coefficients with broadcast LDS loads.
+//   staging       per batch of list entries (255 and a dummy; 127 and a
+//                 dummy in the stored-partials reverse walk), thread t loads
+//                 entry t's record, writes the alpha coefficients and colour
+//                 to LDS and tests the splat's alpha >= 1/255 ellipse against
+//                 each 8x4 half-quadrant; ballots build one compacted list per
+//                 half.
+//   walk          each wave walks its two halves' lists in lockstep, each
+//                 half reading its entry's coefficients with broadcast LDS
+//                 loads.
 // Optional outputs are template parameters, so a variant without the
 // accumulated weight carries no register, LDS slot or store for it (the lesson
 // of section 机制拆解 of the Spirula Studio page, where optional feature arrays

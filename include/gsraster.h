@@ -96,8 +96,8 @@ enum {
      *   WALK_ADD:   each wave adds its per-step totals into the entry's LDS
      *               partial sums (float LDS adds; 255-entry batches);
      *   WALK_STORE: each (half-list, position) step stores its totals into a
-     *               record of its own (no adds; batches as large as the
-     *               records' LDS allows). */
+     *               record of its own (no adds; batches of at most 127
+     *               entries, cut further if their records would not fit). */
     GS_FLAG_WALK_ADD = 1u << 1,
     GS_FLAG_WALK_STORE = 1u << 2
 };
