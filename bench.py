@@ -46,10 +46,16 @@ KERNEL_SOURCES = ["differentiable_tile_rasterization_amd/csrc/gs_raster.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so that editing a comment does not retire the traffic counters."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
