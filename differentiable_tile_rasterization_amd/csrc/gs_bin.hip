@@ -16,8 +16,9 @@
 //              depth rank k writes its tiles, row-major, at that offset, as
 //              (tile id, splat id), tile ids 16-bit up to 65536 tiles
 //   6. tiles   stable LSD radix sort of the pairs by tile id over only the
-//              ceil(log2(tiles)) bits it can have, split evenly over as few
-//              passes as 8-bit digits allow (two 6-bit passes at 4056 tiles).
+//              ceil(log2(tiles)) bits it can have, split as evenly as possible
+//              over as few passes as 8-bit digits allow, narrower digits first
+//              (6 + 6 bits at 4056 tiles, 6 + 7 at 8160).
 //              Stability keeps each tile's pairs in depth order, equal depths
 //              by ascending splat id.
 //   7. ranges  [start, end) per tile from the boundaries of the sorted keys
@@ -520,7 +521,7 @@ hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long lon
 // values into sorted_ids) and the ranges, with keys of type K.
 template <typename K>
 hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rect_sorted,
-                     const unsigned* emit_off, int GX, int np, int pb, K* keys_a, K* keys_b, int* vals_t,
+                     const unsigned* emit_off, int GX, int np, int tb, K* keys_a, K* keys_b, int* vals_t,
                      int* sorted_ids, unsigned* hist, unsigned long long* part, unsigned long long* total,
                      int2* tile_ranges, hipStream_t st)
 {
@@ -531,8 +532,13 @@ hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rec
     emit_kernel<K><<<(n + kWave - 1) / kWave, kWave, 0, st>>>(n, I, by_depth, rect_sorted, emit_off, GX, kin, vin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    int shift = 0;
     for (int p = 0; p < np; ++p) {
-        e = radix_pass<K>(kin, vin, kout, vout, I, pb * p, pb, hist, part, total, st);
+        // tb bits over np passes, the narrower digits first (the first pass,
+        // reading the pairs in emission order, writes the most scattered runs)
+        const int bits = max(4, tb / np + (p >= np - tb % np ? 1 : 0));
+        e = radix_pass<K>(kin, vin, kout, vout, I, shift, bits, hist, part, total, st);
+        shift += bits;
         if (e != hipSuccess) return e;
         K* tk = kin; kin = kout; kout = tk;
         int* tv = vin; vin = vout; vout = tv;
@@ -698,19 +704,20 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
 
     // Tile passes, ping-ponged so that the last one writes its values into
     // sorted_ids: as few passes as 8-bit digits allow, the tile id's bits
-    // split evenly over them (narrower digits make longer runs per digit in
-    // each workgroup's output, i.e. fuller cache lines), at least 4 bits each.
+    // split as evenly as possible over them, the narrower digits first
+    // (narrower digits make longer runs per digit in each workgroup's output,
+    // i.e. fuller cache lines), at least 4 bits each.
     const int tb = bits_for(tiles);
     const int np = (tb + kRadixBits - 1) / kRadixBits;
-    const int pb = np > 0 ? max(4, (tb + np - 1) / np) : kRadixBits;
+
     int* vals_t = (int*)(ws + L.vals_tmp);
     // 16-bit tile keys up to 65536 tiles (a quarter less traffic per pass)
     if (tiles <= 65536)
-        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, rect_sorted, emit_off, GX, np, pb,
+        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, rect_sorted, emit_off, GX, np, tb,
                                          (unsigned short*)(ws + L.keys_a), (unsigned short*)(ws + L.keys_b), vals_t,
                                          sorted_ids, hist, part, total, (int2*)tile_ranges, st));
     else
-        GS_HIP(tile_sort<unsigned>(n, I, by_depth, rect_sorted, emit_off, GX, np, pb, (unsigned*)(ws + L.keys_a),
+        GS_HIP(tile_sort<unsigned>(n, I, by_depth, rect_sorted, emit_off, GX, np, tb, (unsigned*)(ws + L.keys_a),
                                    (unsigned*)(ws + L.keys_b), vals_t, sorted_ids, hist, part, total,
                                    (int2*)tile_ranges, st));
     return GS_OK;
