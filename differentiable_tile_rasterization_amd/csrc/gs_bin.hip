@@ -34,13 +34,21 @@ constexpr int kScanThreads = 256;
 constexpr int kScanItems = 4;                         // per thread: one 16-byte load
 constexpr int kScanTile = kScanThreads * kScanItems;  // 1024 items per workgroup
 
-constexpr int kSortThreads = 256;
-constexpr int kSortRounds = 16;                       // rounds of 256 keys per workgroup
-constexpr int kSortTile = kSortThreads * kSortRounds; // 4096 keys per workgroup
+// Radix sort tiling: a workgroup of W waves sorts W * 1024 keys, 16 per
+// thread. The pair passes use 8 waves (8192 keys: longer runs per digit in
+// each workgroup's output, so fewer partly written cache lines); the splats'
+// depth sort 4 (4096 keys: its 1-2M keys then still make enough workgroups to
+// fill the chip).
+constexpr int kSortRounds = 16;                       // rounds of W * 64 keys per workgroup
 constexpr int kRadixBits = 8;                         // widest digit
 constexpr int kRadix = 1 << kRadixBits;
-static_assert(kSortThreads == kRadix && kSortThreads == 4 * kWave && kSortTile == 4 * kSortRounds * kWave,
-              "radix sort tiling: at most one digit per thread, four waves each holding a quarter of the tile");
+constexpr int kDepthWaves = 4, kPairWaves = 8;
+constexpr int kSortTileMin = kDepthWaves * kWave * kSortRounds;  // the smaller tile: workspace sizing
+template <int W> struct SortTiling {
+    static constexpr int kThreads = W * kWave;
+    static constexpr int kTile = kThreads * kSortRounds;
+    static_assert(kThreads >= kRadix, "at most one digit per thread");
+};
 
 __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float depth, int GX, int GY,
                                            int& tx0, int& tx1, int& ty0, int& ty1)
@@ -254,13 +262,15 @@ __global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, c
 // hist: per workgroup digit counts, stored digit-major (digit * nwg + wg) so
 // that one exclusive scan yields every workgroup's output offset per digit.
 // ---------------------------------------------------------------------------
-template <typename K, int BITS>
-__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __restrict__ keys, long long n,
-                                                                  int shift, int nwg, unsigned* __restrict__ hist)
+template <typename K, int BITS, int W>
+__global__ __launch_bounds__(SortTiling<W>::kThreads) void radix_hist_kernel(const K* __restrict__ keys, long long n,
+                                                                             int shift, int nwg,
+                                                                             unsigned* __restrict__ hist)
 {
     constexpr int R = 1 << BITS;
-    __shared__ unsigned h[4][R];
-    for (int k = threadIdx.x; k < 4 * R; k += kSortThreads) (&h[0][0])[k] = 0;
+    constexpr int kSortWaves = W, kSortThreads = SortTiling<W>::kThreads, kSortTile = SortTiling<W>::kTile;
+    __shared__ unsigned h[kSortWaves][R];  // one copy per wave: fewer lanes per address
+    for (int k = threadIdx.x; k < kSortWaves * R; k += kSortThreads) (&h[0][0])[k] = 0;
     __syncthreads();
     const int w = threadIdx.x >> 6;
     const long long base = (long long)blockIdx.x * kSortTile;
@@ -279,7 +289,12 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __res
     }
     __syncthreads();
     const int d = threadIdx.x;
-    if (d < R) hist[(long long)d * nwg + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+    if (d < R) {
+        unsigned c = 0;
+#pragma unroll
+        for (int k = 0; k < kSortWaves; ++k) c += h[k][d];
+        hist[(long long)d * nwg + blockIdx.x] = c;
+    }
 }
 
 // Scatter of one pass. The workgroup's keys are first ranked stably by digit
@@ -287,27 +302,28 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(const K* __res
 // that consecutive threads store consecutive addresses inside each digit's
 // run instead of one key at a time into up to 256 different runs.
 // Ranking: wave w holds the tile's keys 1024 w .. 1024 w + 1023, 64 per round
-// (round r: keys 1024 w + 64 r + lane). Within a round, 8 ballots give each
+// (round r: keys 1024 w + 64 r + lane). Within a round, BITS ballots give each
 // lane its rank among the wave's lanes with the same digit; a per-wave running
 // count per digit (read by those lanes, then advanced by the first of them:
 // LDS operations of one wave take effect in order) carries the rank across
 // the wave's rounds, with no workgroup barrier. After the rounds, each digit's
 // block-local start and each wave's offset inside it come from one scan; as
-// the waves hold consecutive quarters of the tile, wave order then round
-// order is the tile's order: the placement is stable.
-template <typename K, int BITS>
-__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __restrict__ keys_in,
-                                                                     const int* __restrict__ vals_in, long long n,
-                                                                     int shift, int nwg,
-                                                                     const unsigned* __restrict__ offs,
-                                                                     K* __restrict__ keys_out,
-                                                                     int* __restrict__ vals_out)
+// the waves hold consecutive parts of the tile, wave order then round order
+// is the tile's order: the placement is stable.
+template <typename K, int BITS, int W>
+__global__ __launch_bounds__(SortTiling<W>::kThreads) void radix_scatter_kernel(const K* __restrict__ keys_in,
+                                                                                const int* __restrict__ vals_in,
+                                                                                long long n, int shift, int nwg,
+                                                                                const unsigned* __restrict__ offs,
+                                                                                K* __restrict__ keys_out,
+                                                                                int* __restrict__ vals_out)
 {
     constexpr int R = 1 << BITS;
-    __shared__ unsigned wave_run[4][R];  // per wave: keys of digit d ranked so far, then its offset
-    __shared__ unsigned local_start[R];  // block-local start of digit d
+    constexpr int kSortWaves = W, kSortThreads = SortTiling<W>::kThreads, kSortTile = SortTiling<W>::kTile;
+    __shared__ unsigned wave_run[kSortWaves][R];  // per wave: keys of digit d ranked so far, then its offset
+    __shared__ unsigned local_start[R];           // block-local start of digit d
     __shared__ unsigned global_off[R];
-    __shared__ unsigned scan_part[4];
+    __shared__ unsigned scan_part[kSortWaves];
     __shared__ K lkey[kSortTile];
     __shared__ int lval[kSortTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     unsigned rk[kSortRounds];  // rank among the wave's keys of the same digit
     for (int k = lane; k < R; k += kWave) wave_run[w][k] = 0u;  // each wave clears its own row
     const unsigned goff = has_digit ? offs[(long long)td * nwg + blockIdx.x] : 0u;  // stored after the ranking
-    const int wbase = w * (kSortTile / 4);  // this wave's quarter of the tile
+    const int wbase = w * (kSortTile / kSortWaves);  // this wave's part of the tile
     // all loads issued before the first use (the branches are uniform)
     const bool full = cnt == kSortTile;
 #pragma unroll
@@ -359,9 +375,13 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     __syncthreads();
     // digit td: its count over the tile, the exclusive scan of the counts over
     // the digits, and each wave's offset inside the digit's run
-    const unsigned c0 = has_digit ? wave_run[0][td] : 0u, c1 = has_digit ? wave_run[1][td] : 0u;
-    const unsigned c2 = has_digit ? wave_run[2][td] : 0u, c3 = has_digit ? wave_run[3][td] : 0u;
-    const unsigned tot = c0 + c1 + c2 + c3;
+    unsigned c[kSortWaves];
+    unsigned tot = 0;
+#pragma unroll
+    for (int k = 0; k < kSortWaves; ++k) {
+        c[k] = has_digit ? wave_run[k][td] : 0u;
+        tot += c[k];
+    }
     unsigned incl = tot;
     for (int dl = 1; dl < kWave; dl <<= 1) {
         const unsigned u = __shfl_up(incl, dl, kWave);
@@ -374,10 +394,12 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const K* __
     const unsigned start = before_w + incl - tot;
     if (has_digit) {
         local_start[td] = start;
-        wave_run[0][td] = start;
-        wave_run[1][td] = start + c0;
-        wave_run[2][td] = start + c0 + c1;
-        wave_run[3][td] = start + c0 + c1 + c2;
+        unsigned run = start;
+#pragma unroll
+        for (int k = 0; k < kSortWaves; ++k) {
+            wave_run[k][td] = run;
+            run += c[k];
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -464,7 +486,7 @@ BinLayout bin_layout(long long n, long long cap)
     BinLayout L{};
     size_t o = 0;
     const long long nmax = n > cap ? n : cap;
-    const long long nwg_sort = (nmax + kSortTile - 1) / kSortTile;
+    const long long nwg_sort = (nmax + kSortTileMin - 1) / kSortTileMin;  // the most workgroups a sort uses
     const long long scan_items = n > (long long)kRadix * nwg_sort ? n : (long long)kRadix * nwg_sort;
     const long long nparts = (scan_items + kScanTile - 1) / kScanTile + 1;
     const size_t n1 = (size_t)(n > 0 ? n : 1), c1 = (size_t)(cap > 0 ? cap : 1);
@@ -490,17 +512,18 @@ BinLayout bin_layout(long long n, long long cap)
 }
 
 // One stable LSD pass over the BITS-bit digit at `shift` of keys_in -> keys_out.
-template <typename K, int BITS>
+template <typename K, int BITS, int W>
 hipError_t radix_pass_b(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, unsigned* hist,
                         unsigned long long* part, unsigned long long* total, hipStream_t st)
 {
+    constexpr int kSortThreads = SortTiling<W>::kThreads, kSortTile = SortTiling<W>::kTile;
     const int nwg = (int)((cnt + kSortTile - 1) / kSortTile);
-    radix_hist_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
+    radix_hist_kernel<K, BITS, W><<<nwg, kSortThreads, 0, st>>>(kin, cnt, shift, nwg, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = exclusive_scan(hist, hist, (long long)(1 << BITS) * nwg, part, total, st);
     if (e != hipSuccess) return e;
-    radix_scatter_kernel<K, BITS><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
+    radix_scatter_kernel<K, BITS, W><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
     return hipGetLastError();
 }
 
@@ -508,12 +531,13 @@ template <typename K>
 hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, int bits,
                       unsigned* hist, unsigned long long* part, unsigned long long* total, hipStream_t st)
 {
+    constexpr int W = kPairWaves;  // the pair passes
     switch (bits) {
-    case 4: return radix_pass_b<K, 4>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
-    case 5: return radix_pass_b<K, 5>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
-    case 6: return radix_pass_b<K, 6>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
-    case 7: return radix_pass_b<K, 7>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
-    default: return radix_pass_b<K, 8>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 4: return radix_pass_b<K, 4, W>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 5: return radix_pass_b<K, 5, W>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 6: return radix_pass_b<K, 6, W>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    case 7: return radix_pass_b<K, 7, W>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
+    default: return radix_pass_b<K, 8, W>(kin, vin, kout, vout, cnt, shift, hist, part, total, st);
     }
 }
 
@@ -668,7 +692,8 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         unsigned* dk_out = dkb;
         int* dv_out = dvb;
         for (int shift = 0; shift < 32; shift += kRadixBits) {
-            GS_HIP(radix_pass<unsigned>(dk_in, dv_in, dk_out, dv_out, n, shift, kRadixBits, hist, part, total, st));
+            GS_HIP((radix_pass_b<unsigned, kRadixBits, kDepthWaves>(dk_in, dv_in, dk_out, dv_out, n, shift, hist, part,
+                                                                     total, st)));
             dk_in = dk_out;
             dv_in = dv_out;
             dk_out = dk_out == dkb ? dka : dkb;
