@@ -1247,21 +1247,32 @@ __global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* 
 // Output stage of both gathers: u = (w g_r, w g_g, w g_b, s, s dx, s dy,
 // s dx^2, s dx dy, s dy^2, [w]) summed over the splat's pairs; applies the
 // splat's conic and opacity and writes every output.
-template <bool AW>
-__device__ __forceinline__ void gather_write(int i, const float (&u)[10], const float* __restrict__ conics,
-                                             const float* __restrict__ opac, float2* __restrict__ d_means,
-                                             float* __restrict__ d_conics, float* __restrict__ d_colors,
-                                             float* __restrict__ d_opac, float* __restrict__ accum_w)
+// The splat's conic and opacity, requested when the gather starts (they do
+// not depend on the pairs), so that their latency overlaps the pair scan.
+struct SplatConsts {
+    float a, b, c, o;
+};
+__device__ __forceinline__ SplatConsts load_consts(int i, int n, const float* __restrict__ conics,
+                                                   const float* __restrict__ opac)
 {
-    const float ca = conics[3 * i + 0], cb = conics[3 * i + 1], cc = conics[3 * i + 2];
-    d_means[i] = make_float2(__builtin_fmaf(ca, u[4], cb * u[5]), __builtin_fmaf(cb, u[4], cc * u[5]));
+    if (i >= n) return SplatConsts{0.0f, 0.0f, 0.0f, 1.0f};
+    return SplatConsts{conics[3 * i + 0], conics[3 * i + 1], conics[3 * i + 2], opac[i]};
+}
+
+template <bool AW>
+__device__ __forceinline__ void gather_write(int i, const float (&u)[10], const SplatConsts& k,
+                                             float2* __restrict__ d_means, float* __restrict__ d_conics,
+                                             float* __restrict__ d_colors, float* __restrict__ d_opac,
+                                             float* __restrict__ accum_w)
+{
+    d_means[i] = make_float2(__builtin_fmaf(k.a, u[4], k.b * u[5]), __builtin_fmaf(k.b, u[4], k.c * u[5]));
     d_conics[3 * i + 0] = -0.5f * u[6];
     d_conics[3 * i + 1] = -u[7];
     d_conics[3 * i + 2] = -0.5f * u[8];
     d_colors[3 * i + 0] = u[0];
     d_colors[3 * i + 1] = u[1];
     d_colors[3 * i + 2] = u[2];
-    d_opac[i] = u[3] != 0.0f ? u[3] / opac[i] : 0.0f;
+    d_opac[i] = u[3] != 0.0f ? u[3] / k.o : 0.0f;
     if (AW) accum_w[i] = u[9];
 }
 
@@ -1298,6 +1309,7 @@ __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restr
     const int i0 = blockIdx.x * kWave;
     const int i = i0 + lane;
     const long long my_off = min(max((long long)splat_offsets[min(i, n)], 0ll), n_slots);
+    const SplatConsts sc = load_consts(i, n, conics, opac);
     const long long p0 = __shfl(my_off, 0, kWave);
     const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
     float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -1370,7 +1382,7 @@ __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restr
     }
     if (i >= n) return;
     if (!AW) u[9] = 0.0f;
-    gather_write<AW>(i, u, conics, opac, d_means, d_conics, d_colors, d_opac, accum_w);
+    gather_write<AW>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w);
 }
 
 template <bool AW>
@@ -1390,6 +1402,7 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
     const int i0 = blockIdx.x * kWave;
     const int i = i0 + lane;
     const long long my_off = min(max((long long)splat_offsets[min(i, n)], 0ll), n_slots);
+    const SplatConsts sc = load_consts(i, n, conics, opac);
     const long long p0 = __shfl(my_off, 0, kWave);
     const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
     float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -1470,7 +1483,7 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
     }
     if (i >= n) return;
     if (!AW) u[9] = 0.0f;
-    gather_write<AW>(i, u, conics, opac, d_means, d_conics, d_colors, d_opac, accum_w);
+    gather_write<AW>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w);
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
