@@ -213,6 +213,15 @@ def test_long_lists_many_batches():
     assert bins.n_isect > 512
 
 
+def test_image_covering_splats():
+    """A few splats each covering most of a 300x200 image: hundreds of tiles per
+    splat (the stored-partials walk and the staged gather), several gather
+    windows per splat."""
+    sc = _custom(12, 300, 200, 6, sig=(40.0, 90.0), op=(0.2, 0.6), pad=0)
+    bins, _ = check_scene(sc)
+    assert bins.n_isect > 32 * sc.n
+
+
 def test_equal_depths_tie_break():
     sc = _custom(7, 64, 64, 300)
     sc.depths[:] = np.float32(3.0)
