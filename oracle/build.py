@@ -1,8 +1,8 @@
 """Build the oracle's C core (``oracle/_gs_oracle.so``) with gcc.
 
-Test infrastructure: the library built here is the checker, never part of the
-product path. Plain IEEE float64 (no fast-math, no contraction) so the
-arithmetic is exactly what the source says.
+Test infrastructure: the library built here is what the tests compare the
+product against, never part of the product path. Plain IEEE float64 (no
+fast-math, no contraction) so the arithmetic is exactly what the source says.
 """
 from __future__ import annotations
 

@@ -1,7 +1,7 @@
 /*
  * gs_oracle.c -- CPU float64 oracle for tile-based Gaussian-splat rasterization.
  *
- * TEST INFRASTRUCTURE ONLY. This file is the checker, not the product: it is
+ * TEST INFRASTRUCTURE ONLY. This file is the test oracle, not the product: it is
  * built and called by the tests, by the package's smoke check and by the
  * benchmark's CPU-baseline leg, never by the library itself. It shares no code
  * with the HIP kernels.
