@@ -119,15 +119,18 @@ __device__ inline AlphaCoef make_alpha_coef(float mx, float my, float a, float b
     return k;
 }
 
-// Returns alpha_raw = opacity * exp(sigma) (unclamped) and dx, dy.
+// Returns alpha_raw = opacity * exp(sigma) (unclamped) and dx, dy. The
+// exponent log2(opacity) - v2^2 - v1^2 is two FMAs (two roundings): each
+// subtracts a non-negative square from a value that is at most log2(opacity),
+// so the exponent never exceeds log2(opacity) and alpha_raw never exceeds
+// exp2(log2(opacity)) (v_exp_f32 is monotone).
 __device__ __forceinline__ float alpha_raw(const AlphaCoef& k, float px, float py, float& dx, float& dy)
 {
     dx = px - k.mx;
     dy = py - k.my;
     const float v1 = __builtin_fmaf(k.l11, dx, k.l21 * dy);
     const float v2 = k.l22 * dy;
-    const float q = __builtin_fmaf(v1, v1, v2 * v2);
-    return __builtin_amdgcn_exp2f(k.lo - q);
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(-v1, v1, __builtin_fmaf(-v2, v2, k.lo)));
 }
 
 // ---------------------------------------------------------------------------

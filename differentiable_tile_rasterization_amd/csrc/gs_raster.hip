@@ -411,9 +411,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             }
             if (threadIdx.x < kSSlots) S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
         }
-        // Can any entry of the batch reach the 0.99 clamp? alpha_raw =
-        // exp2(log2 o - q) with q >= 0 never exceeds exp2(log2 o) (the same
-        // monotone v_exp_f32), so an entry with exp2(log2 o) clearly below
+        // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
+        // exponent never exceeds log2 o, so alpha_raw never exceeds
+        // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
         const bool may_clamp = keep && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
@@ -751,9 +751,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         *reinterpret_cast<float2*>(S[threadIdx.x].part + 8) = make_float2(0.0f, 0.0f);
         bool hit[kHalves];
         half_hits(r, ox, oy, k, hend, hit);
-        // Can any entry of the batch reach the 0.99 clamp? alpha_raw =
-        // exp2(log2 o - q) with q >= 0 never exceeds exp2(log2 o) (the same
-        // monotone v_exp_f32), so an entry with exp2(log2 o) clearly below
+        // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
+        // exponent never exceeds log2 o, so alpha_raw never exceeds
+        // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
         const bool may_clamp = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
