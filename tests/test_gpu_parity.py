@@ -181,13 +181,16 @@ def test_tiny_with_accum_weight():
 
 # ----------------------------------------------------------------- edge cases
 
-def _custom(seed, W, H, n, sig=(0.7, 7.0), op=(0.05, 1.0), bg=None, pad=5):
+def _custom(seed, W, H, n, sig=(0.7, 7.0), op=(0.05, 1.0), bg=None, pad=5, grad32=False):
+    """``grad32``: draw dL/dImage as float32 normals from the same generator
+    (much faster for images of tens of megapixels)."""
     rng = np.random.default_rng(seed)
-    return scenes.custom_scene(
-        W, H, means2d=np.stack([rng.uniform(-pad, W + pad, n), rng.uniform(-pad, H + pad, n)], 1),
-        sigmas=rng.uniform(sig[0], sig[1], (n, 2)), thetas=rng.uniform(0, math.pi, n),
-        opacities=rng.uniform(op[0], op[1], n), colors=rng.uniform(0, 1, (n, 3)),
-        depths=rng.uniform(0.1, 10, n), background=bg, seed=seed)
+    means = np.stack([rng.uniform(-pad, W + pad, n), rng.uniform(-pad, H + pad, n)], 1)
+    sigmas, thetas = rng.uniform(sig[0], sig[1], (n, 2)), rng.uniform(0, math.pi, n)
+    opac, cols, depths = rng.uniform(op[0], op[1], n), rng.uniform(0, 1, (n, 3)), rng.uniform(0.1, 10, n)
+    g = rng.standard_normal((H, W, 3), dtype=np.float32) if grad32 else None
+    return scenes.custom_scene(W, H, means2d=means, sigmas=sigmas, thetas=thetas, opacities=opac, colors=cols,
+                               depths=depths, dL_dimage=g, background=bg, seed=seed)
 
 
 def test_ragged_image_with_background():
@@ -267,6 +270,16 @@ def test_binning_large_grids(W, H):
     bins = gpu_bins(sc)
     check_bins(sc, bins)
     assert bins.n_isect > 10000
+
+
+def test_large_grid_forward_backward():
+    """66049 tiles (4112 x 4112, tile ids beyond 16 bits): the backward's tile
+    order and XCD band mapping, both reverse walks and the forward over the
+    whole grid. A sparse scene (3000 splats), so that the oracle covers every
+    pixel."""
+    sc = _custom(13, 4112, 4112, 3000, sig=(2.0, 40.0), pad=50, grad32=True)
+    bins, _ = check_scene(sc)
+    assert bins.tile_ranges.shape[0] == 66049 and bins.n_isect > 100000
 
 
 def test_binning_capacity_retry():
