@@ -37,17 +37,46 @@ def _short(name: str) -> str:
     return n.split("(")[0]
 
 
+LDS_PER_CU = 160 * 1024   # gfx950
+WAVES_PER_CU = 32         # 8 per SIMD
+
+
+def _launch_shapes(csv_path: str) -> dict[str, tuple[int, int]]:
+    """(LDS bytes per workgroup, workgroup size) of each kernel, from the
+    kernel-trace CSV written beside the stats CSV (first dispatch)."""
+    trace = os.path.join(os.path.dirname(csv_path), os.path.basename(csv_path).replace("kernel_stats", "kernel_trace"))
+    shapes: dict[str, tuple[int, int]] = {}
+    if os.path.exists(trace):
+        for r in csv.DictReader(open(trace)):
+            k = _short(r["Kernel_Name"])
+            if k not in shapes:
+                shapes[k] = (int(r["LDS_Block_Size"]), int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"])
+                             * int(r["Workgroup_Size_Z"]))
+    return shapes
+
+
 def stats(csv_path: str, out_md: str, command: str) -> None:
     rows = list(csv.DictReader(open(csv_path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    shapes = _launch_shapes(csv_path)
     lines = ["# Kernel time: " + os.path.basename(out_md).rsplit(".", 1)[0], "",
              "Command (repo root, on the MI355X host):", "", "    " + command, "",
-             "| kernel | calls | avg us | min us | max us | total ms | % |",
-             "|---|---:|---:|---:|---:|---:|---:|"]
+             "LDS B/WG and WG size are the kernel trace's; \"waves/CU by LDS\" is the resident-wave",
+             "limit that LDS alone sets (160 KB per CU, at most 32 waves per CU).", "",
+             "| kernel | calls | avg us | min us | max us | total ms | % | LDS B/WG | WG size | waves/CU by LDS |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
-        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        k = _short(r["Name"])
+        lds, wg = shapes.get(k, (0, 0))
+        if wg:
+            waves = -(-wg // 64)
+            lim = WAVES_PER_CU if lds == 0 else min(WAVES_PER_CU, (LDS_PER_CU // lds) * waves)
+            extra = f"{lds} | {wg} | {lim}"
+        else:
+            extra = "| |"
+        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} | {extra} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -121,6 +150,9 @@ def counters(out_md: str, prefix: str, *runs: str) -> None:
         if "SQ_ACTIVE_INST_VALU" in vals:
             lines.append(f"VALU busy: SQ_ACTIVE_INST_VALU x 4 / (1024 SIMDs x cycles) = "
                          f"{vals['SQ_ACTIVE_INST_VALU'] * 4 / (1024 * cyc):.2f}.")
+        if "SQ_WAVE_CYCLES" in vals:  # counted in units of 4 cycles
+            lines.append(f"Mean resident waves per CU: SQ_WAVE_CYCLES x 4 / (256 CUs x cycles) = "
+                         f"{vals['SQ_WAVE_CYCLES'] * 4 / (256 * cyc):.1f}.")
         if "SQ_INSTS_VALU" in vals:
             lines.append(f"VALU issue: SQ_INSTS_VALU x 4 / (1024 SIMDs x cycles) = "
                          f"{vals['SQ_INSTS_VALU'] * 4 / (1024 * cyc):.2f} of one wave instruction per 4 cycles.")
