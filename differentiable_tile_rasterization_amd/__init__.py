@@ -39,9 +39,20 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, dev):
+    """The caller's stream, or the current stream of the tensors' device; a
+    stream of another device is refused (its kernels would address memory of
+    the wrong GPU)."""
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if s.device != dev:
+        raise ValueError(f"stream is on {s.device}, the tensors on {dev}")
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, means2d on {dev}: all tensors must share one device")
 
 
 def _need(t, name, dtype, shape=None):
@@ -99,18 +110,21 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
     _need(depths, "depths", torch.float32, (n,))
     lib = _lib.load()
     dev = means2d.device
+    _same_device(dev, radii=radii, depths=depths)
     GX, GY = tile_grid(width, height)
     cap = int(capacity) if capacity is not None else max(4 * n, 1)
     ranges = torch.empty((GX * GY, 2), dtype=torch.int32, device=dev)
     offsets = torch.empty((n + 1,), dtype=torch.int32, device=dev)
-    st = _stream(stream)
+    st = _stream(stream, dev)
     for _attempt in range(2):
         ids = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
         ws_bytes = int(lib.gs_bin_tiles_workspace_size(n, cap, width, height))
         ws, wsp = _aligned_workspace(ws_bytes, dev)
         n_isect = ctypes.c_int64(0)
-        status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(radii), _ptr(depths), width, height, cap,
-                                  _ptr(ids), _ptr(ranges), _ptr(offsets), ctypes.byref(n_isect), wsp, ws_bytes, st)
+        with torch.cuda.device(dev):
+            status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(radii), _ptr(depths), width, height, cap,
+                                      _ptr(ids), _ptr(ranges), _ptr(offsets), ctypes.byref(n_isect), wsp, ws_bytes,
+                                      st)
         if status == _lib.GS_ERR_CAPACITY:
             cap = int(n_isect.value)
             continue
@@ -138,6 +152,8 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
     _need(sorted_ids, "sorted_ids", torch.int32)
     dev = means2d.device
+    _same_device(dev, conics=conics, colors=colors, opacities=opacities, background=background,
+                 tile_ranges=tile_ranges, sorted_ids=sorted_ids, workspace=workspace)
     image = torch.empty((height, width, 3), dtype=torch.float32, device=dev)
     final_T = torch.empty((height, width), dtype=torch.float32, device=dev)
     n_contrib = torch.empty((height, width), dtype=torch.int32, device=dev)
@@ -145,10 +161,12 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     lib = _lib.load()
     ws_bytes = int(lib.gs_rasterize_fwd_workspace_size(n))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
-    _lib.check(lib.gs_rasterize_fwd(
-        n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
-        _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _ptr(mw), wsp,
-        ws_bytes, _stream(stream)))
+    st = _stream(stream, dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.gs_rasterize_fwd(
+            n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
+            _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _ptr(mw), wsp,
+            ws_bytes, st))
     if max_weight:
         return image, final_T, n_contrib, mw
     return image, final_T, n_contrib
@@ -183,14 +201,21 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     _need(n_contrib, "n_contrib", torch.int32, (height, width))
     _need(dL_dimage, "dL_dimage", torch.float32, (height, width, 3))
     dev = means2d.device
+    _same_device(dev, conics=conics, colors=colors, opacities=opacities, radii=radii, background=background,
+                 tile_ranges=bins.tile_ranges, sorted_ids=bins.sorted_ids, splat_offsets=bins.splat_offsets,
+                 final_T=final_T, n_contrib=n_contrib, dL_dimage=dL_dimage, workspace=workspace)
     lib = _lib.load()
+    shapes = {"dL_dmeans2d": (n, 2), "dL_dconics": (n, 3), "dL_dcolors": (n, 3), "dL_dopacities": (n,)}
+    if accum_weight:
+        shapes["accum_weight"] = (n,)
     if out is None:
-        out = {"dL_dmeans2d": torch.empty((n, 2), dtype=torch.float32, device=dev),
-               "dL_dconics": torch.empty((n, 3), dtype=torch.float32, device=dev),
-               "dL_dcolors": torch.empty((n, 3), dtype=torch.float32, device=dev),
-               "dL_dopacities": torch.empty((n,), dtype=torch.float32, device=dev)}
-        if accum_weight:
-            out["accum_weight"] = torch.empty((n,), dtype=torch.float32, device=dev)
+        out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+    else:  # the kernels write every element: shapes, dtype and device are checked like the inputs
+        for k, v in shapes.items():
+            if k not in out:
+                raise ValueError(f"out lacks {k!r}")
+            _need(out[k], k, torch.float32, v)
+            _same_device(dev, **{k: out[k]})
     ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
@@ -201,15 +226,16 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     args = (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
             height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
             _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
-            _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight")), flags, wsp,
-            ws_bytes, _stream(stream))
-    if events is None:
-        _lib.check(lib.gs_rasterize_bwd(*args))
-    else:
-        if len(events) != 4:
-            raise ValueError("events: four torch.cuda.Event objects")
-        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
-        _lib.check(lib.gs_rasterize_bwd_timed(*args, handles))
+            _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight") if accum_weight else None),
+            flags, wsp, ws_bytes, _stream(stream, dev))
+    if events is not None and len(events) != 4:
+        raise ValueError("events: four torch.cuda.Event objects")
+    with torch.cuda.device(dev):
+        if events is None:
+            _lib.check(lib.gs_rasterize_bwd(*args))
+        else:
+            handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
+            _lib.check(lib.gs_rasterize_bwd_timed(*args, handles))
     return out
 
 

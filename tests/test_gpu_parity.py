@@ -326,3 +326,27 @@ def test_timed_entry_point_matches_and_orders_its_events():
     spans = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
     _say("stage ms", spans)
     assert all(x >= 0 for x in spans) and spans[1] > 0
+
+
+def test_binding_rejects_bad_outputs_before_launch():
+    """Caller-supplied outputs are checked like inputs (the kernels write every
+    element): a wrong shape, dtype or a missing entry raises, nothing runs."""
+    sc = scenes.make_scene("tiny", 0)
+    bins = gpu_bins(sc)
+    _, T, nc = gpu_fwd(sc, bins)
+    n = sc.n
+    good = {"dL_dmeans2d": torch.zeros((n, 2), device="cuda"), "dL_dconics": torch.zeros((n, 3), device="cuda"),
+            "dL_dcolors": torch.zeros((n, 3), device="cuda"), "dL_dopacities": torch.zeros((n,), device="cuda")}
+    args = (_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.radii),
+            _dev(sc.background), sc.width, sc.height, bins, T, nc, _dev(sc.dL_dimage))
+    bad_shape = dict(good, dL_dconics=torch.zeros((n - 1, 3), device="cuda"))
+    bad_dtype = dict(good, dL_dopacities=torch.zeros((n,), dtype=torch.float64, device="cuda"))
+    missing = {k: v for k, v in good.items() if k != "dL_dcolors"}
+    for out, exc in [(bad_shape, ValueError), (bad_dtype, TypeError), (missing, ValueError)]:
+        with pytest.raises(exc):
+            gsr.gs_rasterize_bwd(*args, out=out)
+    with pytest.raises(ValueError):  # the weight output is required with the flag
+        gsr.gs_rasterize_bwd(*args, accum_weight=True, out=good)
+    res = gsr.gs_rasterize_bwd(*args, out=good)
+    torch.cuda.synchronize()
+    assert res is good and float(good["dL_dcolors"].abs().sum()) > 0
