@@ -61,6 +61,16 @@ __device__ inline int xcd_tile(int wg, int tiles)
     return (wg % kXcds) * per + wg / kXcds;
 }
 
+// A tile's [start, end) range of the sorted pair list, clamped to
+// 0 <= start <= end <= n_pairs, so that ranges that did not come from one
+// binning of these splats never index outside the list.
+__device__ __forceinline__ int2 clamp_range(int2 rg, long long n_pairs)
+{
+    const long long x = min(max((long long)rg.x, 0ll), n_pairs);
+    const long long y = min(max((long long)rg.y, x), n_pairs);
+    return make_int2((int)x, (int)y);
+}
+
 // ---------------------------------------------------------------------------
 // Tile rectangle [tx0, tx1) x [ty0, ty1) of a splat (the rule in gsraster.h):
 // plain float32 sub, multiply by 1/16 and floor, then clamp to the grid. No

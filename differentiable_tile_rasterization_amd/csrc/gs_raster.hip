@@ -273,7 +273,7 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
 // registers fit 80 VGPRs.
 template <bool AW>
 __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
-    int W, int H, int GX, int GY, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
+    int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
     const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = ranges[tile];
+    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
@@ -363,8 +363,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         SplatRec r;
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
-        if (cand) {
-            id = ids[rg.x + k];
+        if (cand) id = ids[rg.x + k];
+        if ((unsigned)id >= (unsigned)n) id = -1;  // an id outside [0, n) is no entry
+        if (id >= 0) {
             r = recs[id];
             radius = __float_as_int(r.c.z);
             S[threadIdx.x].a = r.a;
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         // binning; anything else gets no slot and is never written wild.
         {
             int slot = -1;
-            if (keep) {
+            if (keep && id >= 0) {
                 int tx0, tx1, ty0, ty1;
                 tile_rect(r.a.x, r.a.y, radius, GX, GY, tx0, tx1, ty0, ty1);
                 const int tx = tile % GX, ty = tile / GX;
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
-        const bool may_clamp = keep && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
+        const bool may_clamp = keep && id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
         int len[kHalves];
         const bool clamp_batch = build_store_lists(hit, may_clamp, S, list, list_cnt, len);
         int base[kHalves];  // first partial record of each half
@@ -658,7 +659,7 @@ __device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool
 
 template <bool AW>
 __global__ __launch_bounds__(kBlock) void bwd_kernel(
-    int W, int H, int GX, int GY, int tiles, const int2* __restrict__ ranges, const int* __restrict__ ids,
+    int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
     const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = ranges[tile];
+    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
@@ -738,8 +739,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         SplatRec r;
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
-        if (threadIdx.x < kBatch && k < tmax) {
-            id = ids[rg.x + k];
+        if (threadIdx.x < kBatch && k < tmax) id = ids[rg.x + k];
+        if ((unsigned)id >= (unsigned)n) id = -1;  // an id outside [0, n) is no entry
+        if (id >= 0) {
             r = recs[id];
             radius = __float_as_int(r.c.z);
             S[threadIdx.x].a = r.a;
@@ -1007,8 +1009,9 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
         int id = -1;
-        if (threadIdx.x < kBatch && idx < rg.y) {
-            id = ids[idx];
+        if (threadIdx.x < kBatch && idx < rg.y) id = ids[idx];
+        if ((unsigned)id >= (unsigned)n) id = -1;  // an id outside [0, n) is no entry
+        if (id >= 0) {
             r = recs[id];
             S[threadIdx.x].a = r.a;
             S[threadIdx.x].b = r.b;
@@ -1184,7 +1187,7 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, in
             for (int c = 0; c < 4; ++c)
                 if (x0 + c < W) v = max(v, n_contrib[y * W + x0 + c]);
         }
-        v = min(max(v, 0), rg.y - rg.x);
+        v = max(min(v, rg.y - rg.x), 0);  // an inverted range costs nothing
         v = wave_max_i32(v);
         if (lane == 0) cost[tile] = v;
         return;
@@ -1219,7 +1222,7 @@ __global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* 
     if ((threadIdx.x & 63) == 0) atomicMax(&cmax, m);
     __syncthreads();
     const int top = max(cmax, 1);
-    auto key = [&](int c) { return 255 - (int)(((long long)c * 255) / top); };  // 0 = costliest
+    auto key = [&](int c) { return 255 - (int)(((long long)max(c, 0) * 255) / top); };  // 0 = costliest, in [0, 255]
     for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[key(cost[t0 + i])], 1);
     __syncthreads();
     if (threadIdx.x < 64) {  // exclusive scan of the 256 buckets by one wave, 4 per lane
@@ -1631,7 +1634,7 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         GS_HIP(mark(1));
         const int* ord = order;
         auto launch = [&](auto kernel) {
-            kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, GY, tiles, (const int2*)tile_ranges,
+            kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, GY, tiles, n, (const int2*)tile_ranges,
                                                        sorted_ids, recs, splat_offsets, n_isect, background,
                                                        final_T, n_contrib, dL_dimage, ord, slots, used);
         };

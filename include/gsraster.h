@@ -55,6 +55,13 @@
  *    positive-definite conics, opacity in [0, 1], radii from a conservative
  *    projection. Splats with radius <= 0, depth not > 0 or a non-finite mean
  *    are culled by the binning.
+ *  - Binning outputs passed on: tile_ranges, sorted_ids and splat_offsets
+ *    should come from one gs_bin_tiles call on the same splats and image
+ *    size. The kernels still bound what they read: a sorted_ids entry
+ *    outside [0, n) is no entry (both rasterizers), and gs_rasterize_bwd
+ *    clamps every tile range and splat offset to [0, n_isect].
+ *    gs_rasterize_fwd, which is not given n_isect, reads sorted_ids over the
+ *    tile ranges as passed.
  *  - Calls are re-entrant; there is no global mutable state other than the
  *    thread-local error string.
  */

@@ -350,3 +350,55 @@ def test_binding_rejects_bad_outputs_before_launch():
     res = gsr.gs_rasterize_bwd(*args, out=good)
     torch.cuda.synchronize()
     assert res is good and float(good["dL_dcolors"].abs().sum()) > 0
+
+
+def test_out_of_range_ids_and_ranges():
+    """sorted_ids outside [0, n) are no entries (forward and both reverse
+    walks give the oracle's result on the lists without them), and tile ranges
+    that are inverted or reach past the pair list are clamped to it: the
+    backward reads nothing outside its inputs."""
+    sc = scenes.make_scene("tiny", 0)
+    bins = gpu_bins(sc)
+    ids = bins.sorted_ids.cpu().numpy().copy()
+    rng = bins.tile_ranges.cpu().numpy().copy()
+    bad = np.random.default_rng(5).choice(len(ids), 40, replace=False)
+    ids_bad = ids.copy()
+    ids_bad[bad[:20]] = sc.n + 7
+    ids_bad[bad[20:]] = -3
+    keep = np.ones(len(ids), bool)
+    keep[bad] = False
+    new_pos = np.concatenate([[0], np.cumsum(keep)])  # position in the filtered list of each old position
+    rng_o = np.stack([new_pos[rng[:, 0]], new_pos[rng[:, 1]]], 1).astype(np.int32)
+    ids_o = ids[keep].astype(np.int32)
+    gb = gsr.Bins(torch.from_numpy(ids_bad).cuda(), bins.tile_ranges, bins.splat_offsets, bins.n_isect,
+                  sc.width, sc.height)
+    img, T, nc = gpu_fwd(sc, gb)
+    fo = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
+                              rng_o, ids_o)
+    ok = ~fo["ambiguous"]
+    assert np.abs(img.cpu().numpy() - fo["image"])[ok].max() <= IMG_TOL
+    assert np.abs(T.cpu().numpy() - fo["final_T"])[ok].max() <= T_TOL
+    g = sc.dL_dimage.copy()
+    g[fo["ambiguous"]] = 0.0
+    bo = oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
+                              rng_o, ids_o, g)
+    for walk in ("add", "store"):
+        out = gpu_bwd(sc, gb, T, nc, g, walk=walk)
+        for gk, ok_ in [("dL_dmeans2d", "dmeans2d"), ("dL_dconics", "dconics"), ("dL_dcolors", "dcolors"),
+                        ("dL_dopacities", "dopacities")]:
+            ref = bo[ok_]
+            err = np.abs(out[gk].cpu().numpy() - ref).max()
+            assert err <= GRAD_REL * np.abs(ref).max(), (walk, gk, err)
+    # ranges: one past the end of the pair list, one inverted, one starting below 0
+    _, T0, nc0 = gpu_fwd(sc, bins)
+    r2 = rng.copy()
+    r2[0] = [rng[0, 0], len(ids) + 1000]
+    r2[1] = [rng[1, 1], rng[1, 0]]
+    r2[2] = [-50, rng[2, 1]]
+    gb2 = gsr.Bins(bins.sorted_ids, torch.from_numpy(r2).cuda(), bins.splat_offsets, bins.n_isect, sc.width,
+                   sc.height)
+    for walk in ("add", "store"):
+        out = gpu_bwd(sc, gb2, T0, nc0, sc.dL_dimage, walk=walk)
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            assert torch.isfinite(v).all(), (walk, k)
