@@ -1,0 +1,77 @@
+"""The oracle's pins catch plausible mistakes in it.
+
+Each case below plants one mistake in a copy of the oracle's C core (a sign,
+a factor, an index, a threshold or a dropped term that a careful reader could
+still miss), builds it with the same flags as the real one into a temporary
+directory and runs the pins (`test_oracle_pins.py`) against it in a fresh
+process: every mutant must fail at least one pin. An unmutated copy built the
+same way must pass them all. Everything runs on the CPU.
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "csrc", "gs_oracle.c")
+
+# (name, text in the source, replacement); each text occurs exactly once
+MUTANTS = [
+    ("sigma_cross_term_sign", "- b * dx * dy;\n        double G", "+ b * dx * dy;\n        double G"),
+    ("sigma_missing_half", "-0.5 * (a * dx * dx + c * dy * dy)", "-(a * dx * dx + c * dy * dy)"),
+    ("no_alpha_clamp", "double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;\n        double ea", "double alpha = ah;\n        double ea"),
+    ("no_skip_below_1_255", "if (alpha < ALPHA_MIN) continue;", "if (alpha < 0.0) continue;"),
+    ("stop_tested_on_previous_T", "if (test < T_MIN) break;", "if (T < T_MIN) break;"),
+    ("T_with_unclamped_alpha", "double test = T * (1.0 - alpha);", "double test = T * (1.0 - ah);"),
+    ("behind_not_divided", "S[ch] / (1.0 - al)", "S[ch]"),
+    ("dmean_index", "(a_ * q->dx + b_ * q->dy) * ds", "(a_ * q->dx + b_ * q->dx) * ds"),
+    ("dconic_b_halved", "o[3] += -q->dx * q->dy * ds;", "o[3] += -0.5 * q->dx * q->dy * ds;"),
+    ("dopacity_alpha_for_G", "o[8] += q->G * dal;", "o[8] += al * dal;"),
+    ("dcolour_channel", "o[6] += w * g[1];", "o[6] += w * g[0];"),
+    ("behind_accumulates_alpha", "S[1] += col[1] * w;", "S[1] += col[1] * al;"),
+    ("clamped_alpha_keeps_sigma_path", "if (!q->clamped) {", "if (1) {"),
+    ("n_contrib_off_by_one", "last = k - start + 1;", "last = k - start;"),
+    ("image_without_background", "image[3 * p + 0] = C[0] + T * s.bg[0];", "image[3 * p + 0] = C[0];"),
+    ("accum_weight_alpha", "o[9] += w;", "o[9] += al;"),
+]
+
+
+def _run(name, text, repl, tmp):
+    src = open(SRC).read()
+    if text is not None:
+        assert src.count(text) == 1, (name, src.count(text))
+        src = src.replace(text, repl)
+    d = os.path.join(tmp, name)
+    os.makedirs(d, exist_ok=True)
+    c = os.path.join(d, "gs_oracle.c")
+    so = os.path.join(d, "gs_oracle.so")
+    open(c, "w").write(src)
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+                    "-o", so, c, "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, GS_ORACLE_LIB=so, OMP_NUM_THREADS="2")
+    p = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-x", "-q",
+                        "-p", "no:cacheprovider", "-m", "not gpu"], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    return p.returncode, p.stdout[-400:]
+
+
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    tmp = str(tmp_path_factory.mktemp("oracle_mutants"))
+    cases = [("unmutated", None, None)] + MUTANTS
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        futs = {name: ex.submit(_run, name, t, r, tmp) for name, t, r in cases}
+        return {name: f.result() for name, f in futs.items()}
+
+
+def test_unmutated_copy_passes(outcomes):
+    rc, tail = outcomes["unmutated"]
+    assert rc == 0, tail
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_pins_catch_mutant(outcomes, name):
+    rc, tail = outcomes[name]
+    assert rc == 1, f"pins did not fail on mutant {name} (exit {rc}): {tail}"  # 1: tests ran and failed
