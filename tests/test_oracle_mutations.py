@@ -5,10 +5,13 @@ a factor, an index, a threshold or a dropped term that a careful reader could
 still miss), builds it with the same flags as the real one into a temporary
 directory and runs the pins (`test_oracle_pins.py`) against it in a fresh
 process: every mutant must fail at least one pin. An unmutated copy built the
-same way must pass them all. Everything runs on the CPU.
+same way must pass them all. The binning, which the oracle writes in numpy,
+gets the same treatment: a mutated copy of the oracle package is imported in
+place of the real one. Everything runs on the CPU.
 """
 import concurrent.futures
 import os
+import shutil
 import subprocess
 import sys
 
@@ -16,6 +19,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "csrc", "gs_oracle.c")
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
 
 # (name, text in the source, replacement); each text occurs exactly once
 MUTANTS = [
@@ -57,21 +61,60 @@ def _run(name, text, repl, tmp):
     return p.returncode, p.stdout[-400:]
 
 
+# mistakes in the numpy binning (oracle/__init__.py)
+PY_MUTANTS = [
+    ("rect_round_for_floor", "x0 = np.floor((m[:, 0] - r) * inv)", "x0 = np.round((m[:, 0] - r) * inv)"),
+    ("rect_end_exclusive_lost", "y1 = np.floor((m[:, 1] + r) * inv) + f(1.0)", "y1 = np.floor((m[:, 1] + r) * inv)"),
+    ("depth_ties_by_descending_id", 'order = np.argsort(dbits, kind="stable")',
+     "order = np.lexsort((-np.arange(len(dbits)), dbits))"),
+    ("negative_depth_not_culled", "live = (np.asarray(radii) > 0) & (d > 0) &", "live = (np.asarray(radii) > 0) &"),
+    ("tile_ids_column_major", "tile = ty * GX + tx", "tile = tx * GY + ty"),
+]
+
+
+def _run_py(name, text, repl, tmp, lib):
+    """The pins against a copy of the oracle package whose binning carries one
+    mistake (its C core: the real build)."""
+    d = os.path.join(tmp, "py_" + name)
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so"))
+    shutil.copytree(os.path.join(ROOT, "scenes"), os.path.join(d, "scenes"), ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(d, "tests", "golden"))
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(d, "tests", f))
+    src = open(PY_SRC).read()
+    if text is not None:
+        assert src.count(text) == 1, (name, src.count(text))
+        src = src.replace(text, repl)
+    open(os.path.join(d, "oracle", "__init__.py"), "w").write(src)
+    env = dict(os.environ, GS_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    p = subprocess.run([sys.executable, "-m", "pytest", os.path.join(d, "tests", "test_oracle_pins.py"), "-x", "-q",
+                        "-p", "no:cacheprovider", "-m", "not gpu"], cwd=d, env=env, capture_output=True, text=True,
+                       timeout=600)
+    return p.returncode, p.stdout[-400:]
+
+
 @pytest.fixture(scope="module")
 def outcomes(tmp_path_factory):
+    import oracle
+
+    lib = oracle.build.build(force=False)  # the real C core, for the binning mutants
     tmp = str(tmp_path_factory.mktemp("oracle_mutants"))
     cases = [("unmutated", None, None)] + MUTANTS
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         futs = {name: ex.submit(_run, name, t, r, tmp) for name, t, r in cases}
+        futs.update({name: ex.submit(_run_py, name, t, r, tmp, lib)
+                     for name, t, r in [("py_unmutated", None, None)] + PY_MUTANTS})
         return {name: f.result() for name, f in futs.items()}
 
 
-def test_unmutated_copy_passes(outcomes):
-    rc, tail = outcomes["unmutated"]
+@pytest.mark.parametrize("name", ["unmutated", "py_unmutated"])
+def test_unmutated_copy_passes(outcomes, name):
+    rc, tail = outcomes[name]
     assert rc == 0, tail
 
 
-@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS + PY_MUTANTS])
 def test_pins_catch_mutant(outcomes, name):
     rc, tail = outcomes[name]
     assert rc == 1, f"pins did not fail on mutant {name} (exit {rc}): {tail}"  # 1: tests ran and failed
