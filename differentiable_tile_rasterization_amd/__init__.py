@@ -68,6 +68,20 @@ def _need(t, name, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _pair_count(sorted_ids, n_isect) -> int:
+    """The pair count the kernels clamp tile ranges to: every entry of
+    sorted_ids by default, never more than it holds."""
+    if sorted_ids.dim() != 1:
+        raise ValueError(f"sorted_ids must be one-dimensional, got shape {tuple(sorted_ids.shape)}")
+    held = int(sorted_ids.numel())
+    if n_isect is None:
+        return held
+    n_isect = int(n_isect)
+    if n_isect < 0 or n_isect > held:
+        raise ValueError(f"n_isect = {n_isect}, but sorted_ids holds {held} entries")
+    return n_isect
+
+
 class Bins:
     """Result of gs_bin_tiles: sorted_ids [n_isect] int32, tile_ranges
     [GX*GY, 2] int32, splat_offsets [n+1] int32 (the numbering of each splat's
@@ -135,12 +149,15 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
 
 
 def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int, height: int,
-                     tile_ranges, sorted_ids, max_weight: bool = False, workspace=None, stream=None):
+                     tile_ranges, sorted_ids, max_weight: bool = False, workspace=None, stream=None,
+                     n_isect: int | None = None):
     """Forward composite. Returns (image [H,W,3], final_T [H,W], n_contrib [H,W]),
     and with ``max_weight`` also each splat's largest compositing weight
     alpha T over the pixels that composite it ([n], 0 if none).
     ``workspace`` may pass a uint8 device buffer of at least
-    gs_rasterize_fwd_workspace_size(n) + 256 bytes."""
+    gs_rasterize_fwd_workspace_size(n) + 256 bytes. ``n_isect`` (default:
+    every entry of ``sorted_ids``) is the pair count the tile ranges are
+    clamped to; it may not exceed the entries sorted_ids holds."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
     _need(conics, "conics", torch.float32, (n, 3))
@@ -151,6 +168,7 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     GX, GY = tile_grid(width, height)
     _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
     _need(sorted_ids, "sorted_ids", torch.int32)
+    n_pairs = _pair_count(sorted_ids, n_isect)
     dev = means2d.device
     _same_device(dev, conics=conics, colors=colors, opacities=opacities, background=background,
                  tile_ranges=tile_ranges, sorted_ids=sorted_ids, workspace=workspace)
@@ -165,7 +183,7 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     with torch.cuda.device(dev):
         _lib.check(lib.gs_rasterize_fwd(
             n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(background), width, height,
-            _ptr(tile_ranges), _ptr(sorted_ids), _ptr(image), _ptr(final_T), _ptr(n_contrib), _ptr(mw), wsp,
+            _ptr(tile_ranges), _ptr(sorted_ids), n_pairs, _ptr(image), _ptr(final_T), _ptr(n_contrib), _ptr(mw), wsp,
             ws_bytes, st))
     if max_weight:
         return image, final_T, n_contrib, mw
@@ -197,6 +215,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     _need(bins.tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
     _need(bins.sorted_ids, "sorted_ids", torch.int32)
     _need(bins.splat_offsets, "splat_offsets", torch.int32, (n + 1,))
+    _pair_count(bins.sorted_ids, bins.n_isect)
     _need(final_T, "final_T", torch.float32, (height, width))
     _need(n_contrib, "n_contrib", torch.int32, (height, width))
     _need(dL_dimage, "dL_dimage", torch.float32, (height, width, 3))

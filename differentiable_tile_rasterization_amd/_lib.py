@@ -56,7 +56,7 @@ def load() -> ctypes.CDLL:
     lib.gs_bin_tiles.restype = ctypes.c_int
     lib.gs_rasterize_fwd_workspace_size.argtypes = [i32]
     lib.gs_rasterize_fwd_workspace_size.restype = sz
-    lib.gs_rasterize_fwd.argtypes = [i32, P, P, P, P, P, i32, i32, P, P, P, P, P, P, P, sz, P]
+    lib.gs_rasterize_fwd.argtypes = [i32, P, P, P, P, P, i32, i32, P, P, i64, P, P, P, P, P, sz, P]
     lib.gs_rasterize_fwd.restype = ctypes.c_int
     lib.gs_rasterize_bwd_workspace_size.argtypes = [i32, i64, i32, i32]
     lib.gs_rasterize_bwd_workspace_size.restype = sz

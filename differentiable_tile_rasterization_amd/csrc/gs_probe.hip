@@ -156,45 +156,6 @@ __global__ __launch_bounds__(256) void atomic_replay_kernel(const unsigned char*
     if (NF == 10) unsafeAtomicAdd(&aw[id], 1.0f);
 }
 
-// Variants of the flush stream, over the same flagged (splat, tile) groups:
-//  1: packed 16-float record per splat, one thread issues the 10 field atomics
-//  2: packed record, 16 lanes per group (lane f adds field f, 10 lanes active)
-//  3: one int32 swap per group into a per-splat list head (linked-list gather)
-//  4: plain stores of a 10-float record per group (no atomics), as traffic floor
-//  5: coalesced atomics, group g adds to rec[g * 16 + f] (no address reuse)
-__global__ __launch_bounds__(256) void atomic_variant_kernel(int mode, const unsigned char* __restrict__ flags,
-                                                             const int* __restrict__ ids, long long n,
-                                                             float* __restrict__ rec, int* __restrict__ head,
-                                                             int* __restrict__ next)
-{
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (mode == 2) {
-        const long long i = t >> 4;
-        const int f = (int)(t & 15);
-        if (i >= n || !flags[i] || f >= 10) return;
-        unsafeAtomicAdd(&rec[(long long)ids[i] * 16 + f], 1.0f);
-        return;
-    }
-    const long long i = t;
-    if (i >= n || !flags[i]) return;
-    const int id = ids[i];
-    if (mode == 1) {
-        float* r = rec + (long long)id * 16;
-#pragma unroll
-        for (int f = 0; f < 10; ++f) unsafeAtomicAdd(&r[f], 1.0f);
-    } else if (mode == 3) {
-        next[i] = atomicExch(&head[id], (int)i);
-    } else if (mode == 4) {
-        float* r = rec + i * 10;
-#pragma unroll
-        for (int f = 0; f < 10; ++f) r[f] = 1.0f;
-    } else if (mode == 5) {
-        float* r = rec + i * 16;
-#pragma unroll
-        for (int f = 0; f < 10; ++f) unsafeAtomicAdd(&r[f], 1.0f);
-    }
-}
-
 // 8 independent FMA chains per lane; iters * 8 FMAs per lane.
 __global__ __launch_bounds__(256) void valu_peak_kernel(float* out, int iters, float s)
 {
@@ -290,17 +251,6 @@ extern "C" int gsp_atomic_replay(const unsigned char* flags, const int32_t* sort
     else
         atomic_replay_kernel<9><<<blocks, 256, 0, (hipStream_t)stream>>>(flags, sorted_ids, n_isect, d_means,
                                                                          d_conics, d_colors, d_opac, aw);
-    return hipGetLastError() == hipSuccess ? 0 : 3;
-}
-
-extern "C" int gsp_atomic_variant(int mode, const unsigned char* flags, const int32_t* sorted_ids,
-                                  long long n_isect, float* rec, int* head, int* next, gs_stream_t stream)
-{
-    const long long threads = mode == 2 ? n_isect * 16 : n_isect;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    if (blocks == 0) return 0;
-    atomic_variant_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(mode, flags, sorted_ids, n_isect, rec, head,
-                                                                     next);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

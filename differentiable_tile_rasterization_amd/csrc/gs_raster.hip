@@ -25,9 +25,14 @@
 //                 half reading its entry's coefficients with broadcast LDS
 //                 loads.
 // Optional outputs are template parameters, so a variant without the
-// accumulated weight carries no register, LDS slot or store for it (the lesson
-// of section 机制拆解 of the Spirula Studio page, where optional feature arrays
-// sized regardless of the switch halved occupancy).
+// accumulated weight spends no instruction, register or global store on it,
+// and its stored-partials records are a float shorter (the lesson of section
+// 机制拆解 of the Spirula Studio page, where optional feature arrays sized
+// regardless of the switch cut occupancy). The LDS-add walk keeps the same
+// 80-byte slot in both instances: its records must stay 16-byte aligned, the
+// next smaller aligned stride (64 bytes) cannot hold the nine sums beside the
+// coefficients, and at 72 bytes (unaligned, seven workgroups per CU instead of
+// six) the walk ran slower (0.500 against 0.464 ms on the 2M-splat scene).
 #include <cstddef>
 #include <type_traits>
 
@@ -600,7 +605,9 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 // a walk step (the lists hold slot byte offsets), so a step spends no VALU
 // instruction on addressing beyond the leaders' field offset.
 // The 80-byte stride is an odd multiple of 16 bytes, so the per-entry 16-byte
-// accesses of staging, zeroing and flushing hit distinct banks.
+// accesses of staging, zeroing and flushing hit distinct banks. The weight's
+// word (part[9]) is in the slot of both instances: without it the slot would
+// still be 80 bytes (see the note on optional outputs at the top).
 struct AddSlot {
     float4 a;           // mean x, mean y, l11, l21 (scaled factor)
     float4 b;           // l22, log2(opacity), red, green
@@ -958,7 +965,7 @@ static_assert(sizeof(FwdSlot) == 48, "FwdSlot layout");
 
 template <bool MW>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX, int tiles,
-                                                     const int2* __restrict__ ranges,
+                                                     const int2* __restrict__ ranges, long long n_pairs,
                                                      const int* __restrict__ ids,
                                                      const SplatRec* __restrict__ recs,
                                                      const float* __restrict__ bg, float* __restrict__ image,
@@ -980,7 +987,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = ranges[tile];
+    const int2 rg = clamp_range(ranges[tile], n_pairs);  // a range past the pair list reads nothing wild
     if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel
         S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
@@ -1524,16 +1531,19 @@ extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                                       const float* opacities, const float* background, int32_t width,
                                       int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                      float* image, float* final_T, int32_t* n_contrib, float* max_weight,
-                                      void* workspace, size_t workspace_bytes, gs_stream_t stream_)
+                                      int64_t n_isect, float* image, float* final_T, int32_t* n_contrib,
+                                      float* max_weight, void* workspace, size_t workspace_bytes,
+                                      gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
     GS_CHECK_ARG(n >= 0, "gs_rasterize_fwd: n = %d < 0", n);
+    GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "gs_rasterize_fwd: n_isect = %lld out of range",
+                 (long long)n_isect);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
                  "gs_rasterize_fwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
     GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
-    GS_CHECK_ARG(n == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
+    GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
     const Layout L = layout(n > 0 ? n : 1, 0, 0);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_fwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
@@ -1551,11 +1561,11 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const flo
             GS_HIP(hipGetLastError());
         }
         fwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
-                                                             sorted_ids, recs, background, image, final_T,
+                                                             n_isect, sorted_ids, recs, background, image, final_T,
                                                              n_contrib, (unsigned*)max_weight);
     } else {
         fwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
-                                                              sorted_ids, recs, background, image, final_T,
+                                                              n_isect, sorted_ids, recs, background, image, final_T,
                                                               n_contrib, nullptr);
     }
     GS_HIP(hipGetLastError());

@@ -58,10 +58,10 @@
  *  - Binning outputs passed on: tile_ranges, sorted_ids and splat_offsets
  *    should come from one gs_bin_tiles call on the same splats and image
  *    size. The kernels still bound what they read: a sorted_ids entry
- *    outside [0, n) is no entry (both rasterizers), and gs_rasterize_bwd
- *    clamps every tile range and splat offset to [0, n_isect].
- *    gs_rasterize_fwd, which is not given n_isect, reads sorted_ids over the
- *    tile ranges as passed.
+ *    outside [0, n) is no entry, and both rasterizers clamp every tile
+ *    range (the backward also every splat offset) to [0, n_isect], the pair
+ *    count the caller passes with sorted_ids (which must hold at least
+ *    n_isect entries).
  *  - Calls are re-entrant; there is no global mutable state other than the
  *    thread-local error string.
  */
@@ -93,8 +93,12 @@ enum { GS_TILE = 16 };
 enum {
     /* Also write accum_weight[i] = sum over composited (pixel, splat i) pairs of
      * alpha * T: the "accum weight" optional feature of the Spirula Studio
-     * page (section 机制拆解). Without it no register, LDS slot or store is
-     * spent on the weight. */
+     * page (section 机制拆解). The weight is a template parameter of the
+     * kernels: without the flag no instruction, register or global store is
+     * spent on it. The LDS-add walk keeps an 80-byte LDS slot per staged
+     * entry in both instances (16-byte aligned records at an odd multiple of
+     * 16 bytes); the stored-partials walk's records are 36 bytes without the
+     * weight and 40 with it. */
     GS_FLAG_ACCUM_WEIGHT = 1u << 0,
     /* Force one of the two reverse walks (same results up to the order of
      * float additions). Without either, the call takes the stored-partials
@@ -186,8 +190,11 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, co
  *   opacities         device float [n]
  *   background        device float [3], or NULL for black
  *   width, height     image size
- *   tile_ranges       device int32 [GX*GY][2], from gs_bin_tiles
- *   sorted_ids        device int32, from gs_bin_tiles
+ *   tile_ranges       device int32 [GX*GY][2], from gs_bin_tiles; each range is
+ *                     clamped to [0, n_isect] before use
+ *   sorted_ids        device int32 [n_isect], from gs_bin_tiles
+ *   n_isect           number of entries of sorted_ids (the binning's pair
+ *                     count); 0 .. 2^31 - 1, else GS_ERR_INVALID_ARG
  *   image             device float [height][width][3] (out)
  *   final_T           device float [height][width]    (out)
  *   n_contrib         device int32 [height][width]    (out)
@@ -202,7 +209,7 @@ size_t gs_rasterize_fwd_workspace_size(int32_t n);
 gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                            const float* opacities, const float* background, int32_t width,
                            int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                           float* image, float* final_T, int32_t* n_contrib, float* max_weight,
+                           int64_t n_isect, float* image, float* final_T, int32_t* n_contrib, float* max_weight,
                            void* workspace, size_t workspace_bytes, gs_stream_t stream);
 
 /*

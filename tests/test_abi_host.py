@@ -45,9 +45,9 @@ def test_workspace_size_grows_with_capacity():
     assert lib.gs_bin_tiles_workspace_size(-1, 0, 64, 64) == 0
 
 
-def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None, ws=256, wsb=1 << 20):
+def _fwd(lib, n=1, w=64, h=64, ptr=1, nul=None, ws=256, wsb=1 << 20, n_isect=0):
     p = ctypes.c_void_p(ptr)
-    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, p, p, p, nul, ctypes.c_void_p(ws), wsb, None)
+    return lib.gs_rasterize_fwd(n, p, p, p, p, nul, w, h, p, p, n_isect, p, p, p, nul, ctypes.c_void_p(ws), wsb, None)
 
 
 def test_fwd_rejects_bad_arguments():
@@ -60,6 +60,14 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(lib, n=10, wsb=lib.gs_rasterize_fwd_workspace_size(10) - 1) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
     assert _fwd(lib, ws=128) == _lib.GS_ERR_INVALID_ARG
+    assert _fwd(lib, n_isect=-1) == _lib.GS_ERR_INVALID_ARG
+    assert b"n_isect" in lib.gs_last_error()
+    assert _fwd(lib, n_isect=1 << 31) == _lib.GS_ERR_INVALID_ARG
+    p = ctypes.c_void_p(1)
+    # a pair count with no pair list
+    assert lib.gs_rasterize_fwd(1, p, p, p, p, None, 8, 8, p, None, 5, p, p, p, None, ctypes.c_void_p(256),
+                                1 << 20, None) == _lib.GS_ERR_INVALID_ARG
+    assert b"sorted_ids" in lib.gs_last_error()
     assert lib.gs_rasterize_fwd_workspace_size(1000) >= 48 * 1000
 
 
@@ -136,3 +144,18 @@ def test_error_string_is_thread_local():
     t.join()
     assert b"n = -7" in lib.gs_last_error()
     assert b"n = -7" not in seen["msg"]
+
+
+def test_binding_pair_count_never_exceeds_the_list():
+    """The binding hands the kernels a pair count no larger than the entries
+    sorted_ids holds (the forward and backward clamp tile ranges to it)."""
+    import torch
+    import differentiable_tile_rasterization_amd as gsr
+    ids = torch.zeros(10, dtype=torch.int32)
+    assert gsr._pair_count(ids, None) == 10
+    assert gsr._pair_count(ids, 7) == 7
+    for bad in (11, -1):
+        with pytest.raises(ValueError):
+            gsr._pair_count(ids, bad)
+    with pytest.raises(ValueError):
+        gsr._pair_count(torch.zeros((2, 5), dtype=torch.int32), None)

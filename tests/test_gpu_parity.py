@@ -397,6 +397,17 @@ def test_out_of_range_ids_and_ranges():
     r2[2] = [-50, rng[2, 1]]
     gb2 = gsr.Bins(bins.sorted_ids, torch.from_numpy(r2).cuda(), bins.splat_offsets, bins.n_isect, sc.width,
                    sc.height)
+    # the forward walks each range clamped to [0, n_isect] (an inverted one is
+    # empty): the oracle on the clamped ranges gives the same image
+    r2c = np.clip(r2, 0, len(ids))
+    r2c[:, 1] = np.maximum(r2c[:, 1], r2c[:, 0])
+    img2, T2, nc2 = gpu_fwd(sc, gb2)
+    fo2 = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
+                               sc.height, r2c.astype(np.int32), ids)
+    ok2 = ~fo2["ambiguous"]
+    assert np.abs(img2.cpu().numpy() - fo2["image"])[ok2].max() <= IMG_TOL
+    assert np.abs(T2.cpu().numpy() - fo2["final_T"])[ok2].max() <= T_TOL
+    np.testing.assert_array_equal(nc2.cpu().numpy()[ok2], fo2["n_contrib"][ok2])
     for walk in ("add", "store"):
         out = gpu_bwd(sc, gb2, T0, nc0, sc.dL_dimage, walk=walk)
         torch.cuda.synchronize()
