@@ -14,7 +14,8 @@ formulas; see gs_oracle.c for the compositing reading):
   list ordered by depth. The binning / radix-sort / tile-range stages appear
   as ``emit_pairs``, ``radix_hist``, ``radix_scatter`` and ``extract_offsets``
   in the timing table of page "Phase 5 step 30b — kernel-by-kernel timing"
-  (section 計測結果). Written out with a library sort (numpy.lexsort).
+  (section 計測結果). Written out as one library sort (numpy.lexsort) of all
+  (splat, tile) pairs by (tile, depth bits, id).
 * :func:`rasterize_fwd` / :func:`rasterize_bwd` -- per-pixel front-to-back
   composite and the exact gradient of L = sum <dL/dImage, image> (C core,
   float64, OpenMP over tiles).
@@ -116,31 +117,27 @@ def bin_tiles(means2d, radii, depths, width: int, height: int):
     Each tile's list holds the splats whose rectangle covers it, ordered by
     the float32 bit pattern of depth (positive floats order like their bit
     patterns), ties broken by ascending splat id. Tile ids are row-major,
-    ``ty * GX + tx``; the lists are concatenated in tile-id order."""
+    ``ty * GX + tx``; the lists are concatenated in tile-id order.
+
+    Written as the definition: every (splat, tile) pair is listed, then one
+    library sort orders the pairs by (tile id, depth bits, splat id)."""
     GX, GY = grid(width, height)
     tx0, tx1, ty0, ty1 = tile_rects(means2d, radii, depths, width, height)
-    # Splats in (depth bits, id) order: a stable sort of the depth bit patterns
-    # over ids listed in ascending order.
-    dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)
-    order = np.argsort(dbits, kind="stable")
-    nx = (tx1 - tx0)[order]
-    ny = (ty1 - ty0)[order]
-    cnt = nx * ny
+    nx = tx1 - tx0
+    cnt = nx * (ty1 - ty0)
     total = int(cnt.sum())
-    # every (splat, tile) pair, splat by splat in that order, tiles row-major
-    ids = np.repeat(order.astype(np.int32), cnt)
-    first = np.repeat(np.cumsum(cnt) - cnt, cnt)
-    local = np.arange(total, dtype=np.int64) - first
-    del first
-    nxr = np.repeat(nx, cnt)
-    tx = np.repeat(tx0[order], cnt) + local % np.maximum(nxr, 1)
-    ty = np.repeat(ty0[order], cnt) + local // np.maximum(nxr, 1)
+    # every (splat, tile) pair: splat by splat, each splat's tiles row-major
+    ids = np.repeat(np.arange(len(cnt), dtype=np.int32), cnt)
+    local = np.arange(total, dtype=np.int64) - np.repeat(np.cumsum(cnt) - cnt, cnt)
+    nxr = np.maximum(np.repeat(nx, cnt), 1)
+    tx = np.repeat(tx0, cnt) + local % nxr
+    ty = np.repeat(ty0, cnt) + local // nxr
     del local, nxr
     tile = ty * GX + tx
     del tx, ty
-    # A stable sort by tile keeps the (depth, id) order inside each tile.
-    tkey = tile.astype(np.int16) if GX * GY <= 32767 else tile
-    perm = np.argsort(tkey, kind="stable")
+    dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)
+    # np.lexsort sorts by its last key first: tile, then depth bits, then id
+    perm = np.lexsort((ids, dbits[ids], tile))
     sorted_ids = ids[perm]
     counts = np.bincount(tile, minlength=GX * GY)
     ends = np.cumsum(counts)

@@ -39,6 +39,12 @@ MUTANTS = [
     ("n_contrib_off_by_one", "last = k - start + 1;", "last = k - start;"),
     ("image_without_background", "image[3 * p + 0] = C[0] + T * s.bg[0];", "image[3 * p + 0] = C[0];"),
     ("accum_weight_alpha", "o[9] += w;", "o[9] += al;"),
+    # the ambiguity bands and the max-weight continuation bound
+    ("alpha_band_ten_times_wider", "static const double K_ALPHA = 4.0;", "static const double K_ALPHA = 40.0;"),
+    ("skip_band_dropped", "if (fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN) amb = 1;", ""),
+    ("clamp_band_dropped", "if (fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32) amb = 1;", ""),
+    ("stop_band_dropped", "if (fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN) amb = 1;", ""),
+    ("max_weight_bound_dropped", "double wb = 1.01 * alpha * Tw;", "double wb = 0.0;"),
 ]
 
 
@@ -65,8 +71,10 @@ def _run(name, text, repl, tmp):
 PY_MUTANTS = [
     ("rect_round_for_floor", "x0 = np.floor((m[:, 0] - r) * inv)", "x0 = np.round((m[:, 0] - r) * inv)"),
     ("rect_end_exclusive_lost", "y1 = np.floor((m[:, 1] + r) * inv) + f(1.0)", "y1 = np.floor((m[:, 1] + r) * inv)"),
-    ("depth_ties_by_descending_id", 'order = np.argsort(dbits, kind="stable")',
-     "order = np.lexsort((-np.arange(len(dbits)), dbits))"),
+    ("depth_ties_by_descending_id", "perm = np.lexsort((ids, dbits[ids], tile))",
+     "perm = np.lexsort((-ids, dbits[ids], tile))"),
+    ("depth_before_tile", "perm = np.lexsort((ids, dbits[ids], tile))",
+     "perm = np.lexsort((ids, tile, dbits[ids]))"),
     ("negative_depth_not_culled", "live = (np.asarray(radii) > 0) & (d > 0) &", "live = (np.asarray(radii) > 0) &"),
     ("tile_ids_column_major", "tile = ty * GX + tx", "tile = tx * GY + ty"),
 ]
