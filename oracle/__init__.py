@@ -59,10 +59,14 @@ def _load():
         lib.gso_forward.restype = i32
         lib.gso_backward.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, i32, P, P]
         lib.gso_backward.restype = i32
-        lib.gso_max_weight.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, i32, P, P]
+        lib.gso_max_weight.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, i32, P, P, P]
         lib.gso_max_weight.restype = i32
+        lib.gso_pixel_outcomes.argtypes = [i32, i32, P, P, P, P, P, P, P, i32, P, P, i32, P, P, P, P]
+        lib.gso_pixel_outcomes.restype = i32
         lib.gso_threads.argtypes = []
         lib.gso_threads.restype = i32
+        lib.gso_set_threads.argtypes = [i32]
+        lib.gso_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -70,6 +74,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the C core runs on."""
     return int(_load().gso_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run the C core's parallel loops on ``n`` threads from now on."""
+    _load().gso_set_threads(int(n))
 
 
 def _ptr(a: np.ndarray):
@@ -210,14 +219,17 @@ def rasterize_bwd(means2d, conics, colors, opacities, background, width: int, he
 
 
 def max_weight(means2d, conics, colors, opacities, background, width: int, height: int,
-               tile_ranges, sorted_ids, tiles=None, tol: float = 1e-5):
+               tile_ranges, sorted_ids, tiles=None, tol: float = 1e-5, bounds: bool = False):
     """Per-splat maximum compositing weight alpha T over composited pairs (0
     for a splat no pixel composites): the "max wt" statistic that the Spirula
     Studio page's raster_bench times (section 亲手验证) without defining it.
     Returns (max_weight float64 [n], uncertain bool [n]); ``uncertain`` marks
     the splats whose maximum a float32 walk may legitimately change by more
     than ``tol``: a pixel with an ambiguous decision may give them a weight
-    that reaches their maximum less ``tol``."""
+    that reaches their maximum less ``tol``. With ``bounds`` also (lo, hi)
+    [n]: every admissible maximum lies in [lo, hi] (lo from the pairs
+    composited before their pixel's first ambiguous decision, hi the larger
+    of the maximum and the bound at ambiguous pixels)."""
     lib = _load()
     m, q, c, o = _arrs(means2d, conics, colors, opacities)
     n = m.shape[0]
@@ -226,16 +238,59 @@ def max_weight(means2d, conics, colors, opacities, background, width: int, heigh
     ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
     mw = np.zeros(n, dtype=np.float64)
     amb = np.zeros(n, dtype=np.float64)
+    cert = np.zeros(n, dtype=np.float64)
     if tiles is None:
         tl, ntl = None, 0
     else:
         tarr = np.ascontiguousarray(tiles, dtype=np.int32)
         tl, ntl = _ptr(tarr), len(tarr)
     lib.gso_max_weight(width, height, n, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
-                       _ptr(bg), tl, ntl, _ptr(mw), _ptr(amb))
+                       _ptr(bg), tl, ntl, _ptr(mw), _ptr(amb), _ptr(cert))
     # a splat is certain when every weight an ambiguous pixel may give it is
     # within tol of zero, or stays below its maximum less tol
-    return mw, (amb > tol) & (amb >= mw - tol)
+    unc = (amb > tol) & (amb >= mw - tol)
+    if bounds:
+        return mw, unc, cert, np.maximum(mw, amb)
+    return mw, unc
+
+
+def pixel_outcomes(means2d, conics, colors, opacities, background, width: int, height: int,
+                   tile_ranges, sorted_ids, xs, ys, cap: int = 64):
+    """Every admissible (image, final_T, n_contrib) of the pixels (xs, ys):
+    at each decision that lies inside its float32 error band both outcomes are
+    followed. Returns image [P, cap, 3], final_T [P, cap], n_contrib [P, cap]
+    and count [P] (the outcomes filled in; -1 when there were more than
+    ``cap``). An unflagged pixel has exactly one outcome, the forward's."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    xs = np.ascontiguousarray(xs, dtype=np.int32)
+    ys = np.ascontiguousarray(ys, dtype=np.int32)
+    P = len(xs)
+    img = np.zeros((P, cap, 3), dtype=np.float64)
+    T = np.zeros((P, cap), dtype=np.float64)
+    nc = np.zeros((P, cap), dtype=np.int32)
+    cnt = np.zeros(P, dtype=np.int32)
+    if P:
+        lib.gso_pixel_outcomes(width, height, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
+                               _ptr(bg), P, _ptr(xs), _ptr(ys), cap, _ptr(img), _ptr(T), _ptr(nc), _ptr(cnt))
+    return img, T, nc, cnt
+
+
+def matches_an_outcome(img, T, nc, outcomes, img_tol: float, T_tol: float):
+    """Per pixel: whether (img [P, 3], T [P], nc [P]) equals one of the
+    pixel's admissible outcomes (from :func:`pixel_outcomes`) within the
+    tolerances (n_contrib exactly). Pixels with too many outcomes count as
+    not matched."""
+    oi, oT, onc, cnt = outcomes
+    cap = oT.shape[1]
+    valid = np.arange(cap)[None, :] < cnt[:, None]
+    ok = (np.abs(oi - np.asarray(img, dtype=np.float64)[:, None, :]).max(axis=2) <= img_tol) & \
+         (np.abs(oT - np.asarray(T, dtype=np.float64)[:, None]) <= T_tol) & \
+         (onc == np.asarray(nc)[:, None]) & valid
+    return ok.any(axis=1)
 
 
 # ----------------------------------------------------------------------------

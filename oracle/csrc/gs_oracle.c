@@ -91,6 +91,44 @@ static double alpha_rel_bound(double a, double b, double c, double dx, double dy
     return K_ALPHA * U32 * (4.0 + m + fabs(sigma));
 }
 
+/* The three decision bands: 1 when a float32 evaluation (alpha within relative
+ * error ea, T(1 - alpha) within relative error et) may take the decision the
+ * other way. */
+static int in_skip_band(double alpha, double ea)
+{
+    return fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN;
+}
+
+static int in_clamp_band(double ah, double ea)
+{
+    return fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32;
+}
+
+static int in_stop_band(double test, double et)
+{
+    return fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN;
+}
+
+/* Splat i at pixel centre (px, py): offset, sigma, G, unclamped and clamped
+ * alpha, and the float32 error bound of alpha. */
+typedef struct {
+    double dx, dy, sigma, G, ah, alpha, ea;
+} pair_t;
+
+static pair_t eval_pair(const splats_t* s, int32_t i, double px, double py)
+{
+    pair_t q;
+    double a = s->conics[3 * i], b = s->conics[3 * i + 1], c = s->conics[3 * i + 2];
+    q.dx = px - s->means[2 * i];
+    q.dy = py - s->means[2 * i + 1];
+    q.sigma = -0.5 * (a * q.dx * q.dx + c * q.dy * q.dy) - b * q.dx * q.dy;
+    q.G = exp(q.sigma);
+    q.ah = s->opac[i] * q.G;
+    q.alpha = q.ah < ALPHA_MAX ? q.ah : ALPHA_MAX;
+    q.ea = alpha_rel_bound(a, b, c, q.dx, q.dy, q.sigma);
+    return q;
+}
+
 /*
  * Walk one pixel's list front to back. Fills `out` (capacity `cap`) with the
  * composited entries, returns how many; writes T_final, n_contrib, colour sum
@@ -106,22 +144,15 @@ static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int3
     C[0] = C[1] = C[2] = 0.0;
     for (int32_t k = start; k < end; ++k) {
         int32_t i = ids[k];
-        double mx = s->means[2 * i], my = s->means[2 * i + 1];
-        double a = s->conics[3 * i], b = s->conics[3 * i + 1], c = s->conics[3 * i + 2];
-        double o = s->opac[i];
-        double dx = px - mx, dy = py - my;
-        double sigma = -0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy;
-        double G = exp(sigma);
-        double ah = o * G;
-        double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;
-        double ea = alpha_rel_bound(a, b, c, dx, dy, sigma);
-        if (fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN) amb = 1;
+        const pair_t q = eval_pair(s, i, px, py);
+        double ah = q.ah, alpha = q.alpha, ea = q.ea;
+        if (in_skip_band(alpha, ea)) amb = 1;
         if (amb && kamb == end) kamb = k;
         if (alpha < ALPHA_MIN) continue;
-        if (fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32) amb = 1;
+        if (in_clamp_band(ah, ea)) amb = 1;
         double test = T * (1.0 - alpha);
         double et = errT + ea * alpha / (1.0 - alpha) + 4.0 * U32;
-        if (fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN) amb = 1;
+        if (in_stop_band(test, et)) amb = 1;
         if (amb && kamb == end) kamb = k;
         if (test < T_MIN) break;
         const double* col = s->colors + 3 * i;
@@ -130,7 +161,7 @@ static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int3
         C[2] += col[2] * alpha * T;
         if (out && cnt < cap) {
             contrib_t* e = &out[cnt];
-            e->k = k; e->alpha = alpha; e->T = T; e->G = G; e->dx = dx; e->dy = dy;
+            e->k = k; e->alpha = alpha; e->T = T; e->G = q.G; e->dx = q.dx; e->dy = q.dy;
             e->clamped = !(ah < ALPHA_MAX);
         }
         ++cnt;
@@ -155,6 +186,16 @@ static int threads_used(void)
 }
 
 int gso_threads(void) { return threads_used(); }
+
+/* Threads of the parallel loops from now on (n >= 1). */
+void gso_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
 
 /*
  * Forward over the tiles listed in `tiles` (or all tiles if tiles == NULL).
@@ -288,6 +329,98 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
 }
 
 /*
+ * Admissible outcomes of one pixel. Where a decision lies inside its band,
+ * a float32 walk may take it either way, and both results are correct. This
+ * walks the pixel's list front to back like walk_pixel and, at every skip or
+ * stop decision inside its band, follows both outcomes (each branch then
+ * continues with its own T and its own later decisions and bands). Every leaf is one admissible
+ * (image, final_T, n_contrib); at most `cap` are kept, and *overflow is set if
+ * there were more.
+ */
+typedef struct {
+    const splats_t* s;
+    const int32_t* ids;
+    int32_t start, end;
+    double px, py;
+    double* img;      /* [cap][3] */
+    double* T;        /* [cap] */
+    int32_t* nc;      /* [cap] */
+    int cap, count, overflow;
+} explore_t;
+
+/* Walk from list position k0 with the state (T, errT, C, last) reached
+ * before it; fs / fc / ft force the skip / clamp / stop decision of entry k0
+ * (-1: the float64 decision, with its band followed). */
+static void explore(explore_t* e, int32_t k0, int fs, int fc, int ft, double T, double errT, const double C0[3],
+                    int32_t last)
+{
+    const splats_t* s = e->s;
+    double C[3] = {C0[0], C0[1], C0[2]};
+    for (int32_t k = k0; k < e->end; ++k) {
+        if (e->count >= e->cap) { e->overflow = 1; return; }
+        int32_t i = e->ids[k];
+        const pair_t q = eval_pair(s, i, e->px, e->py);
+        double ah = q.ah, alpha = q.alpha, ea = q.ea;
+        int first = k == k0;
+        int skip = alpha < ALPHA_MIN;
+        if (first && fs >= 0) skip = fs;
+        else if (in_skip_band(alpha, ea)) explore(e, k, !skip, -1, -1, T, errT, C, last);
+        if (skip) continue;
+        /* a clamp decided the other way moves alpha by no more than its band
+         * (a few ulp), far below the image tolerance, and its effect on the
+         * stop decision lies inside the stop band: it is not branched on */
+        int clamp = !(ah < ALPHA_MAX);
+        if (first && fc >= 0) clamp = fc;
+        double al = clamp ? ALPHA_MAX : ah;
+        double test = T * (1.0 - al);
+        double et = errT + ea * al / (1.0 - al) + 4.0 * U32;
+        int stop = test < T_MIN;
+        if (first && ft >= 0) stop = ft;
+        else if (in_stop_band(test, et)) explore(e, k, 0, clamp, !stop, T, errT, C, last);
+        if (stop) break;
+        const double* col = s->colors + 3 * i;
+        C[0] += col[0] * al * T;
+        C[1] += col[1] * al * T;
+        C[2] += col[2] * al * T;
+        T = test;
+        errT += ea * al / (1.0 - al) + 2.0 * U32;
+        last = k - e->start + 1;
+    }
+    if (e->count >= e->cap) { e->overflow = 1; return; }
+    double* im = e->img + 3 * (size_t)e->count;
+    im[0] = C[0] + T * s->bg[0];
+    im[1] = C[1] + T * s->bg[1];
+    im[2] = C[2] + T * s->bg[2];
+    e->T[e->count] = T;
+    e->nc[e->count] = last;
+    e->count++;
+}
+
+/*
+ * Admissible outcomes of the listed pixels (xs[p], ys[p]): img [np][cap][3],
+ * T [np][cap], nc [np][cap], count [np] (-1: more than cap outcomes).
+ */
+int gso_pixel_outcomes(int W, int H, const int32_t* ranges, const int32_t* ids,
+                       const double* means, const double* conics, const double* colors, const double* opac,
+                       const double* bg, int npix, const int32_t* xs, const int32_t* ys, int cap,
+                       double* img, double* T, int32_t* nc, int32_t* count)
+{
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE;
+    (void)H;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int p = 0; p < npix; ++p) {
+        int t = (ys[p] / TILE) * GX + xs[p] / TILE;
+        explore_t e = {&s, ids, ranges[2 * t], ranges[2 * t + 1], xs[p] + 0.5, ys[p] + 0.5,
+                       img + 3 * (size_t)cap * p, T + (size_t)cap * p, nc + (size_t)cap * p, cap, 0, 0};
+        double C[3] = {0.0, 0.0, 0.0};
+        explore(&e, e.start, -1, -1, -1, 1.0, 0.0, C, 0);
+        count[p] = e.overflow ? -1 : e.count;
+    }
+    return threads_used();
+}
+
+/*
  * Max weight over the listed tiles: max_w [n] = max over composited pairs of
  * alpha T (MAXED into; caller zeroes). max_w_amb [n] (MAXED into) bounds what
  * a float32 walk may give a splat at pixels with an ambiguous decision: up to
@@ -298,11 +431,16 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
  * continued past its stop (each flipped skip changes T by a factor within
  * (1 - 1/255)^-1; a flipped clamp changes alpha by a few ulp). A splat whose
  * max_w_amb stays below its max_w less the comparison tolerance has the same
- * maximum in any correct float32 walk.
+ * maximum in any correct float32 walk. max_w_cert [n] (MAXED into; may be
+ * NULL) is the maximum over the pairs composited before their pixel's first
+ * ambiguous decision, which every correct float32 walk composites too: a
+ * lower bound of any admissible maximum, as max(max_w, max_w_amb) is an upper
+ * bound.
  */
 int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
                    const double* means, const double* conics, const double* colors, const double* opac,
-                   const double* bg, const int32_t* tiles, int ntiles, double* max_w, double* max_w_amb)
+                   const double* bg, const int32_t* tiles, int ntiles, double* max_w, double* max_w_amb,
+                   double* max_w_cert)
 {
     (void)n;
     splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
@@ -314,6 +452,7 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
         contrib_t* buf = NULL;
         double* part = NULL;   /* per tile-list entry: max weight */
         double* pamb = NULL;   /* per tile-list entry: bound at ambiguous pixels */
+        double* pcert = NULL;  /* per tile-list entry: max over pairs before their pixel's first ambiguity */
         int part_cap = 0;
 #pragma omp for schedule(dynamic, 1)
         for (int ti = 0; ti < nt; ++ti) {
@@ -324,12 +463,14 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
             if (L <= 0) continue;
             if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
             if (L > part_cap) {
-                free(part); free(pamb); part_cap = L;
+                free(part); free(pamb); free(pcert); part_cap = L;
                 part = (double*)malloc(sizeof(double) * part_cap);
                 pamb = (double*)malloc(sizeof(double) * part_cap);
+                pcert = (double*)malloc(sizeof(double) * part_cap);
             }
             memset(part, 0, sizeof(double) * L);
             memset(pamb, 0, sizeof(double) * L);
+            memset(pcert, 0, sizeof(double) * L);
             for (int ly = 0; ly < TILE; ++ly) {
                 int y = ty * TILE + ly;
                 if (y >= H) break;
@@ -345,17 +486,14 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
                         double w = buf[e].alpha * buf[e].T;
                         double* o = part + (buf[e].k - start);
                         if (w > *o) *o = w;
+                        double* oc = pcert + (buf[e].k - start);
+                        if (buf[e].k < kamb && w > *oc) *oc = w;
                     }
                     if (!a) continue;
                     double Tw = 1.0;  /* this walk's T, continued past its stop */
                     for (int32_t k = start; k < end; ++k) {
-                        int32_t i = ids[k];
-                        double dx = px - s.means[2 * i], dy = py - s.means[2 * i + 1];
-                        double ca = s.conics[3 * i], cb = s.conics[3 * i + 1], cc = s.conics[3 * i + 2];
-                        double sigma = -0.5 * (ca * dx * dx + cc * dy * dy) - cb * dx * dy;
-                        double ah = s.opac[i] * exp(sigma);
-                        double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;
-                        double ea = alpha_rel_bound(ca, cb, cc, dx, dy, sigma);
+                        const pair_t q = eval_pair(&s, ids[k], px, py);
+                        double ah = q.ah, alpha = q.alpha, ea = q.ea;
                         if (k >= kamb && ah >= ALPHA_MIN * (1.0 - ea) - 2.0 * U32 * ALPHA_MIN) {
                             double wb = 1.01 * alpha * Tw;
                             double* o = pamb + (k - start);
@@ -371,12 +509,14 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
                     int32_t i = ids[start + k];
                     if (part[k] > max_w[i]) max_w[i] = part[k];
                     if (pamb[k] > max_w_amb[i]) max_w_amb[i] = pamb[k];
+                    if (max_w_cert && pcert[k] > max_w_cert[i]) max_w_cert[i] = pcert[k];
                 }
             }
         }
         free(buf);
         free(part);
         free(pamb);
+        free(pcert);
     }
     return threads_used();
 }

@@ -23,9 +23,9 @@ PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
 
 # (name, text in the source, replacement); each text occurs exactly once
 MUTANTS = [
-    ("sigma_cross_term_sign", "- b * dx * dy;\n        double G", "+ b * dx * dy;\n        double G"),
-    ("sigma_missing_half", "-0.5 * (a * dx * dx + c * dy * dy)", "-(a * dx * dx + c * dy * dy)"),
-    ("no_alpha_clamp", "double alpha = ah < ALPHA_MAX ? ah : ALPHA_MAX;\n        double ea", "double alpha = ah;\n        double ea"),
+    ("sigma_cross_term_sign", "- b * q.dx * q.dy;", "+ b * q.dx * q.dy;"),
+    ("sigma_missing_half", "-0.5 * (a * q.dx * q.dx + c * q.dy * q.dy)", "-(a * q.dx * q.dx + c * q.dy * q.dy)"),
+    ("no_alpha_clamp", "q.alpha = q.ah < ALPHA_MAX ? q.ah : ALPHA_MAX;", "q.alpha = q.ah;"),
     ("no_skip_below_1_255", "if (alpha < ALPHA_MIN) continue;", "if (alpha < 0.0) continue;"),
     ("stop_tested_on_previous_T", "if (test < T_MIN) break;", "if (T < T_MIN) break;"),
     ("T_with_unclamped_alpha", "double test = T * (1.0 - alpha);", "double test = T * (1.0 - ah);"),
@@ -41,10 +41,16 @@ MUTANTS = [
     ("accum_weight_alpha", "o[9] += w;", "o[9] += al;"),
     # the ambiguity bands and the max-weight continuation bound
     ("alpha_band_ten_times_wider", "static const double K_ALPHA = 4.0;", "static const double K_ALPHA = 40.0;"),
-    ("skip_band_dropped", "if (fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN) amb = 1;", ""),
-    ("clamp_band_dropped", "if (fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32) amb = 1;", ""),
-    ("stop_band_dropped", "if (fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN) amb = 1;", ""),
+    ("skip_band_dropped", "return fabs(alpha - ALPHA_MIN) <= ea * alpha + 2.0 * U32 * ALPHA_MIN;", "return 0;"),
+    ("clamp_band_dropped", "return fabs(ah - ALPHA_MAX) <= ea * ah + 2.0 * U32;", "return 0;"),
+    ("stop_band_dropped", "return fabs(test - T_MIN) <= K_T * et * T_MIN + 1e-6 * T_MIN;", "return 0;"),
     ("max_weight_bound_dropped", "double wb = 1.01 * alpha * Tw;", "double wb = 0.0;"),
+    ("max_weight_lower_bound_past_ambiguity", "if (buf[e].k < kamb && w > *oc) *oc = w;", "if (w > *oc) *oc = w;"),
+    # the admissible-outcome enumeration
+    ("outcomes_skip_branch_dropped", "else if (in_skip_band(alpha, ea)) explore(e, k, !skip, -1, -1, T, errT, C, last);",
+     ""),
+    ("outcomes_stop_branch_dropped", "else if (in_stop_band(test, et)) explore(e, k, 0, clamp, !stop, T, errT, C, last);",
+     ""),
 ]
 
 

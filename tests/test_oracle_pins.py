@@ -421,10 +421,11 @@ F32 = np.float32
 
 
 def _dual_walk(sc, ids, rng_, tiles):
-    """Each pixel of ``tiles`` walked twice by the plain definition: in
-    float64 and in float32 (means, conic, opacity as stored; sigma, exp, the
-    clamp, the thresholds and T all in the walk's precision). Tracks each
-    pixel until its two walks first decide differently (skip, stop or clamp)."""
+    """Each pixel of ``tiles`` walked twice, each walk to its end, by the
+    plain definition: in float64 and in float32 (means, conic, opacity and
+    colour as stored; sigma, exp, the clamp, the thresholds, T and the colour
+    sums all in the walk's precision). ``differs`` marks the pixels whose two
+    walks decide differently somewhere (skip, stop or clamp)."""
     GX, _ = oracle.grid(sc.width, sc.height)
     tiles = np.asarray(tiles)
     ly, lx = np.mgrid[0:16, 0:16]
@@ -435,46 +436,52 @@ def _dual_walk(sc, ids, rng_, tiles):
     xs, ys, tl = xs[keep], ys[keep], tl[keep]
     start = rng_[tl, 0].astype(np.int64)
     L = (rng_[tl, 1] - rng_[tl, 0]).astype(np.int64)
-    m32, q32, o32 = sc.means2d.astype(F32), sc.conics.astype(F32), sc.opacities.astype(F32)
-    m64, q64, o64 = m32.astype(np.float64), q32.astype(np.float64), o32.astype(np.float64)
-    px64, py64 = xs + 0.5, ys + 0.5
-    px32, py32 = px64.astype(F32), py64.astype(F32)
     P = len(xs)
-    T64, T32 = np.ones(P), np.ones(P, F32)
-    nc = np.zeros(P, np.int64)
-    done = np.zeros(P, bool)
+    bg = np.zeros(3) if sc.background is None else np.asarray(sc.background, dtype=np.float64)
+    walks = {}
+    for dt in (np.float64, F32):
+        m, q, o = sc.means2d.astype(F32).astype(dt), sc.conics.astype(F32).astype(dt), \
+            sc.opacities.astype(F32).astype(dt)
+        col = sc.colors.astype(F32).astype(dt)
+        px, py = (xs + 0.5).astype(dt), (ys + 0.5).astype(dt)
+        w = {"T": np.ones(P, dt), "C": np.zeros((P, 3), dt), "nc": np.zeros(P, np.int64),
+             "done": np.zeros(P, bool), "mw": np.zeros(sc.n, dt), "dec": {}}
+        for j in range(int(L.max(initial=0))):
+            act = np.nonzero((j < L) & ~w["done"])[0]
+            if act.size == 0:
+                break
+            i = ids[start[act] + j]
+            dx, dy = px[act] - m[i, 0], py[act] - m[i, 1]
+            ah = o[i] * np.exp(dt(-0.5) * (q[i, 0] * dx * dx + q[i, 2] * dy * dy) - q[i, 1] * dx * dy)
+            a = np.minimum(dt(0.99), ah)
+            use = a >= dt(1.0 / 255.0)
+            t = w["T"][act] * (dt(1.0) - a)
+            stop = use & (t < dt(1e-4))
+            comp = use & ~stop
+            # decision code per (pixel, step): 0 skip, 1 stop, 2 composite, 3 composite clamped
+            w["dec"][j] = (act, np.where(~use, 0, np.where(stop, 1, np.where(ah < dt(0.99), 2, 3))))
+            ac = act[comp]
+            wt = a[comp] * w["T"][ac]
+            np.maximum.at(w["mw"], i[comp], wt)
+            w["C"][ac] += col[i[comp]] * wt[:, None]
+            w["T"][ac] = t[comp]
+            w["nc"][ac] = j + 1
+            w["done"][act[stop]] = True
+        walks[dt] = w
+    w64, w32 = walks[np.float64], walks[F32]
     differs = np.zeros(P, bool)
-    mw64, mw32 = np.zeros(sc.n), np.zeros(sc.n, F32)
-    for j in range(int(L.max(initial=0))):
-        act = np.nonzero((j < L) & ~done)[0]
-        if act.size == 0:
-            break
-        i = ids[start[act] + j]
-        dx, dy = px64[act] - m64[i, 0], py64[act] - m64[i, 1]
-        ah64 = o64[i] * np.exp(-0.5 * (q64[i, 0] * dx * dx + q64[i, 2] * dy * dy) - q64[i, 1] * dx * dy)
-        a64 = np.minimum(0.99, ah64)
-        use64 = a64 >= 1.0 / 255.0
-        t64 = T64[act] * (1.0 - a64)
-        stop64 = use64 & (t64 < 1e-4)
-        dx, dy = px32[act] - m32[i, 0], py32[act] - m32[i, 1]
-        ah32 = o32[i] * np.exp(F32(-0.5) * (q32[i, 0] * dx * dx + q32[i, 2] * dy * dy) - q32[i, 1] * dx * dy)
-        a32 = np.minimum(F32(0.99), ah32)
-        use32 = a32 >= F32(1.0 / 255.0)
-        t32 = T32[act] * (F32(1.0) - a32)
-        stop32 = use32 & (t32 < F32(1e-4))
-        mis = (use64 != use32) | (use64 & (stop64 != stop32)) | \
-            (use64 & ~stop64 & ((ah64 < 0.99) != (ah32 < F32(0.99))))
-        differs[act[mis]] = True
-        done[act[mis]] = True
-        comp = ~mis & use64 & ~stop64
-        ac = act[comp]
-        np.maximum.at(mw64, i[comp], a64[comp] * T64[ac])
-        np.maximum.at(mw32, i[comp], a32[comp] * T32[ac])
-        T64[ac], T32[ac] = t64[comp], t32[comp]
-        nc[ac] = j + 1
-        done[act[~mis & stop64]] = True
-    return {"x": xs, "y": ys, "differs": differs, "T64": T64, "T32": T32, "n_contrib": nc,
-            "mw64": mw64, "mw32": mw32}
+    for j, (act64, d64) in w64["dec"].items():
+        act32, d32 = w32["dec"].get(j, (np.zeros(0, np.int64), np.zeros(0, np.int64)))
+        a = np.full(P, -1)
+        a[act64] = d64
+        b = np.full(P, -1)
+        b[act32] = d32
+        differs |= a != b
+    img = {k: w["C"].astype(np.float64) + w["T"].astype(np.float64)[:, None] * bg[None, :]
+           for k, w in (("64", w64), ("32", w32))}
+    return {"x": xs, "y": ys, "differs": differs, "T64": w64["T"], "T32": w32["T"].astype(np.float64),
+            "nc64": w64["nc"], "nc32": w32["nc"], "img64": img["64"], "img32": img["32"],
+            "mw64": w64["mw"], "mw32": w32["mw"].astype(np.float64)}
 
 
 def _threshold_scene(seed, W=256, H=256):
@@ -554,25 +561,41 @@ def _rewalk_check(sc, tiles=None, need_flips=False):
     GX, GY = oracle.grid(sc.width, sc.height)
     tiles = np.arange(GX * GY) if tiles is None else tiles
     r = _dual_walk(sc, out["sorted_ids"], out["tile_ranges"], tiles)
-    amb = out["ambiguous"][r["y"], r["x"]]
+    at = (r["y"], r["x"])
+    amb = out["ambiguous"][at]
+    # the float64 re-walk is the oracle's walk
+    np.testing.assert_array_equal(r["nc64"], out["n_contrib"][at])
+    np.testing.assert_allclose(r["T64"], out["final_T"][at], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(r["img64"], out["image"][at], atol=1e-12, rtol=0)
+    # float32 decides differently only on flagged pixels, and agrees with the
+    # float64 walk to the forward's tolerance where it decides the same
     assert not (r["differs"] & ~amb).any(), "a float32 decision flip on an unflagged pixel"
-    ok = ~r["differs"]   # pixels walked to their end (a differing one is left at its first difference)
-    # the float64 re-walk is the oracle's walk; the float32 one agrees with it
-    # to the forward's tolerance wherever it took the same decisions
-    np.testing.assert_array_equal(r["n_contrib"][ok], out["n_contrib"][r["y"], r["x"]][ok])
-    np.testing.assert_allclose(r["T64"][ok], out["final_T"][r["y"], r["x"]][ok], atol=1e-12, rtol=0)
-    assert np.abs(r["T32"][ok] - r["T64"][ok]).max(initial=0.0) <= 1e-5
-    # max weight: a float32 maximum moves by more than 1e-5 only for splats the
-    # oracle marks uncertain
-    mw, unc = oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
-                                sc.height, out["tile_ranges"], out["sorted_ids"], tiles=tiles)
-    # (the re-walk's maxima miss only what differing pixels composite after
-    # their first difference: such splats are marked)
-    np.testing.assert_allclose(r["mw64"][~unc], mw[~unc], atol=1e-12, rtol=0)
-    moved = np.abs(r["mw32"].astype(np.float64) - mw) > 1e-5
+    ok = ~r["differs"]
+    np.testing.assert_array_equal(r["nc32"][ok], r["nc64"][ok])
+    assert np.abs(r["T32"] - r["T64"])[ok].max(initial=0.0) <= 1e-5
+    assert np.abs(r["img32"] - r["img64"])[ok].max(initial=0.0) <= 1e-5
+    # everywhere, the float32 result is one of the pixel's admissible outcomes
+    # (an unflagged pixel has one: the forward's)
+    outc = oracle.pixel_outcomes(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
+                                 sc.height, out["tile_ranges"], out["sorted_ids"], r["x"], r["y"])
+    assert np.all(outc[3][~amb] == 1)
+    np.testing.assert_allclose(outc[0][~amb, 0], out["image"][at][~amb], atol=1e-12, rtol=0)
+    assert np.all(outc[3][amb] >= 1)
+    match = oracle.matches_an_outcome(r["img32"], r["T32"], r["nc32"], outc, 1e-5, 1e-5)
+    assert match.all(), np.nonzero(~match)[0][:10]
+    # max weight: every splat's float32 maximum lies in the oracle's bounds,
+    # and moves by more than 1e-5 only for splats the oracle marks uncertain
+    mw, unc, lo, hi = oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                                        sc.width, sc.height, out["tile_ranges"], out["sorted_ids"], tiles=tiles,
+                                        bounds=True)
+    np.testing.assert_allclose(r["mw64"], mw, atol=1e-12, rtol=0)
+    moved = np.abs(r["mw32"] - mw) > 1e-5
     assert not (moved & ~unc).any(), np.nonzero(moved & ~unc)[0][:10]
+    assert np.all(r["mw32"] >= lo - 1e-5) and np.all(r["mw32"] <= hi + 1e-5)
+    assert np.all(lo <= mw) and np.all(mw <= hi)
     if need_flips:  # the constructed scenes really make float32 decide differently
         assert r["differs"].sum() >= 10 and moved.sum() >= 1, (int(r["differs"].sum()), int(moved.sum()))
+        assert (outc[3][amb] >= 2).mean() > 0.5
     return r, amb
 
 
