@@ -8,11 +8,18 @@ workload: the fixed raster_bench load of the Spirula Studio page (section
 
 Prints one JSON line with the metric (pairs/s; pairs = sum over pixels of
 n_contrib, the list entries the backward must revisit), ms/call, a roofline
-object for the call's dominant kernel, the reverse walk (algorithmic work /
-its mean launch time, from HIP events the library records around it on the
-call's stream, against the bound that dominates, with every term listed) and
-a CPU baseline (the float64 oracle on a bounded sample of the same scene, on
-the host's cores).
+object for the call's dominant kernel, the reverse walk, and a CPU baseline
+(the float64 oracle on the same scene, on the host's threads, plus one-thread
+times of the three small workloads).
+
+Roofline: T_roof = max(T_VALU,min, T_LDS, T_HBM), each an algorithmic count
+over a ceiling measured in the same run (FMA and exp issue, LDS broadcast
+reads and writes, streaming HBM copy); there is no atomic term, the path
+issues no global atomics. ``frac`` is the walk's min-model VALU rate against
+the part's VALU issue rate from its unit counts; ``frac_measured_roof`` is
+T_roof over the walk's time (its mean launch time from HIP events the library
+records around it on the call's stream); ``call_frac`` the same over the
+whole call.
 """
 from __future__ import annotations
 
@@ -27,17 +34,27 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# Algorithmic floating-point work per pair, counted from the formulas as
-# written (an FMA counts 2, a division, exp or compare-free min counts 1):
-#   per walked (pixel, entry) pair:    alpha evaluation                 13
-#   per composited pair, in addition:  T recovery, dL/dalpha, colour
-#                                      behind, 9 gradient terms + sums  45
-#   accumulated weight (optional):     +1 per composited pair
-FLOP_WALK = 13
-FLOP_CONTRIB = 45
-# fp32 VALU peak without packed FP32 forms (the library is compiled without them):
-# 256 CUs x 4 SIMD x 16 lanes x 2 flops (FMA) x 2.4 GHz.
-PEAK_ALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# Algorithmic work of the reverse walk, per composited (pixel, splat) pair, in
+# VALU lane-operations: the minimum model (every evaluated lane composites):
+# alpha recomputation and the skip test (14), T recovery, dL/dalpha, the colour
+# behind and the nine gradient terms with their sums (46); plus 2
+# transcendentals (exp, reciprocal). The walk model, a diagnostic of a kernel
+# that evaluates every walked pair in lockstep, adds 14 lane-ops and one
+# transcendental per walked pair on top of the 46 + 1 per composited pair.
+VALU_MIN_PER_PAIR = 60
+TRANS_PER_PAIR = 2
+VALU_WALK_PER_WALKED = 14
+VALU_WALK_PER_PAIR = 46
+# LDS traffic of the walk per walked list entry: a 40-byte record written
+# once and read (broadcast) by each of the four waves.
+LDS_RECORD_BYTES = 40
+LDS_READS_PER_ENTRY = 4
+# VALU issue of the part, from its unit counts: 256 CUs x 4 SIMDs, one wave64
+# instruction per SIMD every 4 cycles (16 lanes per cycle), 2.4 GHz. The
+# published 157.3 TFLOP/s counts packed FP32 FMAs (two lanes' worth per
+# instruction slot and 2 flops each); the library is compiled without packed
+# forms, so one lane-operation per lane-slot is the ceiling.
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 
 PROFILE_PMC = os.path.join(ROOT, "profiles", "bwd_bench_pmc.json")
@@ -67,10 +84,13 @@ def load_probe():
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_longlong
     lib.gsp_walk_stats.argtypes = [i32, P, P, P, i32, i32, P, P, P, P, P, P]
     lib.gsp_copy.argtypes = [P, P, i64, ctypes.c_int, P]
+    lib.gsp_copy_stream.argtypes = [P, P, i64, ctypes.c_int, P]
+    lib.gsp_lds_peak.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
     lib.gsp_atomic_replay.argtypes = [P, P, i64, P, P, P, P, P, P]
     lib.gsp_valu_peak.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
     lib.gsp_exp_peak.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
-    for f in ["gsp_walk_stats", "gsp_copy", "gsp_atomic_replay", "gsp_valu_peak", "gsp_exp_peak"]:
+    for f in ["gsp_walk_stats", "gsp_copy", "gsp_copy_stream", "gsp_lds_peak", "gsp_atomic_replay",
+              "gsp_valu_peak", "gsp_exp_peak"]:
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -172,8 +192,12 @@ def main():
     n4 = 64 * 1024 * 1024  # 1 GiB per buffer
     src = torch.empty(n4 * 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    t_copy = gpu_time(lambda: probe.gsp_copy(src.data_ptr(), dst.data_ptr(), n4, 256 * 8 * 4, st))
-    hbm_gbs = 2 * n4 * 16 / t_copy / 1e9
+    hbm_sweep = {}
+    for blocks in (2048, 4096, 8192, 16384):
+        t_c = gpu_time(lambda: probe.gsp_copy_stream(src.data_ptr(), dst.data_ptr(), n4, blocks, st))
+        hbm_sweep[blocks] = 2 * n4 * 16 / t_c / 1e9
+    t_copy_plain = gpu_time(lambda: probe.gsp_copy(src.data_ptr(), dst.data_ptr(), n4, 256 * 8 * 4, st))
+    hbm_gbs = max(hbm_sweep.values())
     del src, dst
     scratch = {k: torch.zeros_like(v) for k, v in out.items()}
     t_atomic = gpu_time(lambda: probe.gsp_atomic_replay(
@@ -182,13 +206,36 @@ def main():
         scratch["accum_weight"].data_ptr() if aw else None, st))
     nfields = 10 if aw else 9
     n_atomics = groups_tile * nfields
-    atomic_rate = n_atomics / t_atomic
     pk = torch.zeros(4096, dtype=torch.float32, device=dev)
     iters = 512
     t_valu = gpu_time(lambda: probe.gsp_valu_peak(pk.data_ptr(), 256 * 32, iters, st))
-    valu_tflops = 256 * 32 * 256 * iters * 8 * 2 / t_valu / 1e12
+    fma_lane_ops = 256 * 32 * 256 * iters * 8 / t_valu      # FMA lane-operations per second
     t_exp = gpu_time(lambda: probe.gsp_exp_peak(pk.data_ptr(), 256 * 32, iters, st))
     exp_rate = 256 * 32 * 256 * iters * 4 / t_exp
+    lds_blocks, lds_iters = 256 * 4, 2048
+    t_lds_rd = gpu_time(lambda: probe.gsp_lds_peak(pk.data_ptr(), lds_blocks, lds_iters, 0, st))
+    lds_bcast_Bps = lds_blocks * 4 * lds_iters * 8 * 16 / t_lds_rd      # 16 B per wave instruction
+    t_lds_wr = gpu_time(lambda: probe.gsp_lds_peak(pk.data_ptr(), lds_blocks, lds_iters, 1, st))
+    lds_write_Bps = lds_blocks * 256 * lds_iters * 8 * 16 / t_lds_wr   # 16 B per lane
+    log(f"ceilings: HBM copy {hbm_gbs:.0f} GB/s (blocks sweep {({k: round(v) for k, v in hbm_sweep.items()})}), "
+        f"FMA {fma_lane_ops / 1e12:.1f} T lane-op/s, exp {exp_rate / 1e12:.2f} T/s, LDS broadcast read "
+        f"{lds_bcast_Bps / 1e12:.2f} TB/s, LDS write {lds_write_Bps / 1e12:.1f} TB/s")
+
+    # ---- per-stage times, from HIP events the library records on this stream
+    # at its stage boundaries (gs_rasterize_bwd_timed); run before the timed
+    # region, whose calls then see the clocks at their sustained level
+    stage_ms = {"setup": [], "walk": [], "gather": []}
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in evs:
+            e.record(stream)
+        gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw, out=out,
+                             workspace=ws, events=evs)
+        torch.cuda.synchronize()
+        for k, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
+            stage_ms[k].append(evs[a].elapsed_time(evs[b]))
+    stage_mean = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
 
     # ---- timed region: exactly K backward calls, synchronised on both sides
     for _ in range(args.warmup):
@@ -205,20 +252,6 @@ def main():
     ms_region = e0.elapsed_time(e1) / args.steps
     log(f"timed region: {args.steps} calls, {ms_region:.4f} ms/call (events), wall {wall * 1e3 / args.steps:.4f}")
     t_calls = per_call(bwd, args.steps, 1)
-    # per-stage times of the same calls, from HIP events the library records
-    # on this stream at its stage boundaries (gs_rasterize_bwd_timed)
-    stage_ms = {"setup": [], "walk": [], "gather": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for e in evs:
-            e.record(stream)
-        gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw, out=out,
-                             workspace=ws, events=evs)
-        torch.cuda.synchronize()
-        for k, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
-            stage_ms[k].append(evs[a].elapsed_time(evs[b]))
-    stage_mean = {k: float(np.mean(v)) for k, v in stage_ms.items()}
-    log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
     t_fwd = per_call(fwd, 10, 2)
     t_mw = per_call(fwd_max_weight, 10, 2)
     t0 = time.perf_counter()
@@ -227,69 +260,75 @@ def main():
     torch.cuda.synchronize()
     t_bin = (time.perf_counter() - t0) / 3 * 1e3
 
-    # ---- roofline of the reverse-walk kernel (the call's dominant kernel)
+    # ---- roofline of the reverse walk (the call's dominant kernel)
     ms = float(ms_region)
     t_s = ms * 1e-3
     t_walk = stage_mean["walk"] * 1e-3
-    flops = FLOP_WALK * p_walk + (FLOP_CONTRIB + (1 if aw else 0)) * p_contrib
+    valu_min = VALU_MIN_PER_PAIR * p_contrib
+    trans_min = TRANS_PER_PAIR * p_contrib
+    valu_walk = VALU_WALK_PER_WALKED * p_walk + VALU_WALK_PER_PAIR * p_contrib
+    trans_walk = p_walk + p_contrib
+    lds_write_bytes = entries * LDS_RECORD_BYTES
+    lds_read_bytes = entries * LDS_RECORD_BYTES * LDS_READS_PER_ENTRY
     hbm_bytes = sc.n * 36 + entries * 4 + len(bins.tile_ranges) * 8 + sc.width * sc.height * 20 \
         + sc.n * 4 * nfields
+    # each term: an algorithmic count over a ceiling measured above
     terms = {
-        "alu_ms": flops / (PEAK_ALU_TFLOPS * 1e12) * 1e3,
-        "hbm_ms": hbm_bytes / (PEAK_HBM_GBS * 1e9) * 1e3,
+        "valu_min_ms": (valu_min / fma_lane_ops + trans_min / exp_rate) * 1e3,
+        "lds_ms": (lds_write_bytes / lds_write_Bps + lds_read_bytes / lds_bcast_Bps) * 1e3,
+        "hbm_ms": hbm_bytes / (hbm_gbs * 1e9) * 1e3,
+        "atomic_ms": None,  # not applicable: the path issues no global atomics (each pair's sums are stored)
     }
-    bound = max(terms, key=terms.get).split("_")[0]
-    traffic = None
+    bound_term = max((k for k in terms if terms[k] is not None), key=lambda k: terms[k])
+    t_roof = terms[bound_term] * 1e-3
+    traffic, traffic_src = None, None
     if os.path.exists(PROFILE_PMC):
         with open(PROFILE_PMC) as f:
             pmc = json.load(f)
         if pmc.get("source_hash") == kernel_source_hash() and pmc.get("config") == args.config:
             traffic = pmc.get("hbm_bytes_per_launch")
-    if bound == "alu":
-        roof = {"bound": "alu", "achieved": flops / t_walk / 1e12, "peak": PEAK_ALU_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": hbm_bytes / t_walk / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+            traffic_src = ("stored: rocprofv3 FETCH_SIZE / WRITE_SIZE of this kernel source (hash "
+                           f"{pmc.get('source_hash')}), profiles/bwd_bench_pmc.json; not measured in this run")
+    roof = {
+        "bound": "alu",
+        # min-model VALU lane-operations (transcendentals counted as one) per
+        # second of the walk, against the part's VALU issue rate
+        "achieved": (valu_min + trans_min) / t_walk / 1e12,
+        "peak": PEAK_VALU_TOPS,
+        "unit": "T VALU lane-op/s",
+    }
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
+    roof["traffic_source"] = traffic_src
     # the library's choice of reverse walk (more than 16 tiles per splat: stored partials)
     roof["kernel"] = ("bwd_store_kernel (reverse walk, stored partials)" if bins.n_isect > 16 * sc.n
                       else "bwd_kernel (reverse walk, LDS adds)")
     roof["kernel_ms"] = stage_mean["walk"]
     roof["terms_ms"] = terms
-    roof["call_frac"] = terms[bound + "_ms"] / ms  # the same work against the whole call's time
+    roof["binding_term"] = bound_term
+    roof["t_roof_ms"] = t_roof * 1e3
+    roof["frac_measured_roof"] = t_roof / t_walk     # T_roof / walk time, every term on a measured ceiling
+    roof["call_frac"] = t_roof / t_s                 # the same against the whole call
     roof["stages_ms"] = stage_mean
-    roof["algorithmic"] = {"flops": flops, "hbm_bytes": hbm_bytes, "atomics": n_atomics,
-                           "flop_per_walked_pair": FLOP_WALK, "flop_per_composited_pair": FLOP_CONTRIB}
+    roof["walk_model_ms"] = (valu_walk / fma_lane_ops + trans_walk / exp_rate) * 1e3   # diagnostic
+    roof["algorithmic"] = {
+        "composited_pairs": p_contrib, "walked_pairs": p_walk, "walked_entries": entries,
+        "valu_min_lane_ops": valu_min, "transcendentals_min": trans_min,
+        "valu_walk_lane_ops": valu_walk, "lds_bytes": lds_write_bytes + lds_read_bytes, "hbm_bytes": hbm_bytes,
+        "per_composited_pair": {"valu": VALU_MIN_PER_PAIR, "transcendental": TRANS_PER_PAIR}}
     # the flush as 9-10 scattered float atomics per (splat, tile) group, timed
     # alone: what an atomic-accumulating design would pay (this one stores)
     roof["atomic_flush_replay_ms"] = t_atomic * 1e3
-    roof["ceilings_measured"] = {"hbm_copy_GBs": hbm_gbs, "atomic_replay_per_s": atomic_rate,
-                                 "valu_fma_TFLOPs": valu_tflops, "exp_per_s": exp_rate}
+    roof["ceilings_measured"] = {"hbm_copy_GBs": hbm_gbs, "hbm_copy_plain_GBs": 2 * n4 * 16 / t_copy_plain / 1e9,
+                                 "fma_lane_ops_per_s": fma_lane_ops, "exp_per_s": exp_rate,
+                                 "lds_broadcast_read_Bps": lds_bcast_Bps, "lds_write_Bps": lds_write_Bps,
+                                 "atomic_replay_per_s": n_atomics / t_atomic}
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    # ---- CPU baseline: the oracle beside the GPU, on the host's cores
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        GX, GY = gsr.tile_grid(sc.width, sc.height)
-        ntiles = GX * GY
-        k = max(1, int(round(args.cpu_sample * ntiles)))
-        tiles = np.sort(np.random.default_rng(0).choice(ntiles, k, replace=False)).astype(np.int32)
-        ids_h = bins.sorted_ids.cpu().numpy()
-        rng_h = bins.tile_ranges.cpu().numpy()
-        nc_h = nc.cpu().numpy()
-        ys, xs = np.mgrid[0:sc.height, 0:sc.width]
-        sel = np.isin((ys // 16) * GX + xs // 16, tiles)
-        pw_sample = int(nc_h[sel].astype(np.int64).sum())
-        oracle.threads()
-        c0 = time.perf_counter()
-        oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
-                             rng_h, ids_h, sc.dL_dimage, tiles=tiles)
-        c_s = time.perf_counter() - c0
-        cpu = {"value": pw_sample / c_s, "unit": "pairs/s", "cores": oracle.threads(), "kind": "oracle",
-               "seconds": c_s,
-               "sample": f"float64 oracle rasterize_bwd over {k} of {ntiles} tiles (random, seed 0) of the same "
-                         f"scene, {pw_sample} walked pairs; binning excluded"}
-        log(f"cpu oracle: {c_s:.2f} s on {cpu['cores']} threads, {cpu['value']:.3e} pairs/s")
+        cpu = cpu_baseline(oracle, sc, bins, nc, args, log)
 
     value = p_walk / t_s
     rec = {
@@ -312,6 +351,65 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec))
+
+
+def cpu_baseline(oracle, sc, bins, nc, args, log):
+    """The float64 oracle on the host: forward and backward of the timed
+    scene over a sample of its tiles (all tiles by default) on every host
+    thread, and both on one thread for the three small workloads (tiny, early,
+    mid; their own binning, by the oracle). Binning is excluded from the
+    times."""
+    import numpy as np
+    import scenes
+
+    GX, GY = oracle.grid(sc.width, sc.height)
+    ntiles = GX * GY
+    k = max(1, int(round(args.cpu_sample * ntiles)))
+    tiles = np.sort(np.random.default_rng(0).choice(ntiles, k, replace=False)).astype(np.int32)
+    ids_h = bins.sorted_ids.cpu().numpy()
+    rng_h = bins.tile_ranges.cpu().numpy()
+    nc_h = nc.cpu().numpy()
+    ys, xs = np.mgrid[0:sc.height, 0:sc.width]
+    sel = np.isin((ys // 16) * GX + xs // 16, tiles)
+    pw_sample = int(nc_h[sel].astype(np.int64).sum())
+    # the host threads OpenMP is given (OMP_NUM_THREADS: the CPU share of this
+    # job, which may be fewer than the host's cores)
+    threads = oracle.threads()
+    used = threads
+    c0 = time.perf_counter()
+    oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
+                         rng_h, ids_h, tiles=tiles)
+    f_s = time.perf_counter() - c0
+    c0 = time.perf_counter()
+    oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
+                         rng_h, ids_h, sc.dL_dimage, tiles=tiles)
+    b_s = time.perf_counter() - c0
+    log(f"cpu oracle ({used} threads): forward {f_s:.2f} s, backward {b_s:.2f} s, "
+        f"{pw_sample / b_s:.3e} pairs/s")
+    single = {}
+    oracle.set_threads(1)
+    for name in ("tiny", "early", "mid"):
+        s2 = scenes.make_scene(name, 0)
+        ids2, rng2 = oracle.bin_tiles(s2.means2d, s2.radii, s2.depths, s2.width, s2.height)
+        c0 = time.perf_counter()
+        fo = oracle.rasterize_fwd(s2.means2d, s2.conics, s2.colors, s2.opacities, s2.background, s2.width,
+                                  s2.height, rng2, ids2)
+        f2 = time.perf_counter() - c0
+        c0 = time.perf_counter()
+        oracle.rasterize_bwd(s2.means2d, s2.conics, s2.colors, s2.opacities, s2.background, s2.width, s2.height,
+                             rng2, ids2, s2.dL_dimage)
+        b2 = time.perf_counter() - c0
+        pw = int(fo["n_contrib"].astype(np.int64).sum())
+        single[name] = {"forward_s": f2, "backward_s": b2, "walked_pairs": pw, "backward_pairs_per_s": pw / b2}
+        log(f"cpu oracle, 1 thread, {name}: forward {f2:.3f} s, backward {b2:.3f} s")
+    oracle.set_threads(threads)
+    return {"value": pw_sample / b_s, "unit": "pairs/s", "cores": used, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "forward_s": f_s, "backward_s": b_s,
+            "forward_pairs_per_s": pw_sample / f_s,
+            "sample": f"float64 oracle rasterize_fwd and rasterize_bwd over {k} of {ntiles} tiles (random, "
+                      f"seed 0) of the same scene, {pw_sample} walked pairs, on {used} threads; binning excluded; "
+                      "value = walked pairs / backward seconds",
+            "single_thread": single}
 
 
 if __name__ == "__main__":

@@ -5,8 +5,11 @@
 //                    (splat, 8x8 quadrant) groups with a composited pixel, and
 //                    how many (entry, quadrant) pairs the culling keeps. Uses
 //                    the library's own alpha evaluation and culling test.
-// * gsp_copy         plain float4 copy: HBM ceiling and the reference kernel
-//                    for scaling hardware byte counters.
+// * gsp_copy         plain float4 copy: the reference kernel for scaling
+//                    hardware byte counters.
+// * gsp_copy_stream  unrolled non-temporal float4 copy: the HBM ceiling.
+// * gsp_lds_peak     LDS ceilings: wave-uniform (broadcast) 16-byte reads and
+//                    per-lane 16-byte writes.
 // * gsp_atomic_replay the backward's flush stream replayed alone: one thread
 //                    per (splat, tile) group that receives gradient, one float
 //                    atomic per field, same addresses and order of issue.
@@ -133,6 +136,69 @@ __global__ __launch_bounds__(256) void copy_kernel(const float4* __restrict__ in
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = in[i];
 }
 
+// Streaming copy for the HBM ceiling: each thread moves four float4 per
+// iteration (all four loads issued before the stores), non-temporal loads and
+// stores (the data is touched once), grid-stride over the buffer.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void copy_stream_kernel(const v4f* __restrict__ in, v4f* __restrict__ out,
+                                                          long long n)
+{
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const v4f a = __builtin_nontemporal_load(in + i);
+        const v4f b = __builtin_nontemporal_load(in + i + stride);
+        const v4f c = __builtin_nontemporal_load(in + i + 2 * stride);
+        const v4f d = __builtin_nontemporal_load(in + i + 3 * stride);
+        __builtin_nontemporal_store(a, out + i);
+        __builtin_nontemporal_store(b, out + i + stride);
+        __builtin_nontemporal_store(c, out + i + 2 * stride);
+        __builtin_nontemporal_store(d, out + i + 3 * stride);
+    }
+    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(in + i), out + i);
+}
+
+// LDS ceilings, one 256-thread workgroup per CU slot, 32 KB of LDS each.
+//  mode 0 (broadcast read): every lane of a wave reads the same 16 bytes
+//         (wave-uniform address), eight independent reads in flight; counts
+//         16 bytes per wave instruction, the way the walk's record reads are
+//         counted.
+//  mode 1 (write): every lane writes 16 bytes to its own address (1 KB per
+//         wave instruction, no bank conflicts).
+// iters * 8 instructions per wave; the result is kept live through out.
+__global__ __launch_bounds__(256) void lds_peak_kernel(float* out, int iters, int mode)
+{
+    __shared__ float4 buf[2048];
+    const int t = threadIdx.x, wv = t >> 6;
+    for (int k = t; k < 2048; k += 256) buf[k] = make_float4((float)k, 1.0f, 2.0f, 3.0f);
+    __syncthreads();
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (mode == 0) {
+        int base = __builtin_amdgcn_readfirstlane(wv * 64);
+        for (int i = 0; i < iters; ++i) {
+            float4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = buf[(base + 8 * j + (i & 7)) & 2047];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                acc.x += v[j].x;
+                acc.y += v[j].y;
+            }
+            base = __builtin_amdgcn_readfirstlane((base + 97) & 1023);
+        }
+    } else {
+        for (int i = 0; i < iters; ++i) {
+            const float f = (float)i;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) buf[(j * 256 + t) & 2047] = make_float4(f, f, f, f);
+        }
+        __syncthreads();
+        acc = buf[t];
+    }
+    if (acc.x == 123.456f) out[blockIdx.x] = acc.y;  // keeps the reads live
+}
+
 template <int NF>
 __global__ __launch_bounds__(256) void atomic_replay_kernel(const unsigned char* __restrict__ flags,
                                                             const int* __restrict__ ids, long long n,
@@ -236,6 +302,18 @@ extern "C" int gsp_walk_stats(int32_t n, const float* means2d, const float* coni
 extern "C" int gsp_copy(const void* in, void* out, long long n_float4, int blocks, gs_stream_t stream)
 {
     copy_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const float4*)in, (float4*)out, n_float4);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+extern "C" int gsp_copy_stream(const void* in, void* out, long long n_float4, int blocks, gs_stream_t stream)
+{
+    copy_stream_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const v4f*)in, (v4f*)out, n_float4);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+extern "C" int gsp_lds_peak(float* out, int blocks, int iters, int mode, gs_stream_t stream)
+{
+    lds_peak_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(out, iters, mode);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -5,14 +5,17 @@ Bars:
   * forward: image within 1e-5 absolute, final_T within 1e-5 absolute,
     n_contrib exact, on every pixel the oracle does not flag as ambiguous
     (a pixel where some float32 decision sits within the float32 error bound
-    of its threshold, so that both outcomes are correct);
-  * backward: each gradient field within 1e-4 * max|oracle field|, with
-    dL/dImage zeroed at the flagged pixels in both inputs, so that no gradient
-    depends on a decision that may legitimately flip;
+    of its threshold, so that both outcomes are correct); on a flagged pixel
+    the same bars against one of the pixel's admissible outcomes (the oracle
+    walk with every in-band decision taken either way);
+  * backward: each of the nine scalar gradient fields (and the accumulated
+    weight) within 1e-4 * max|oracle field| of that field, with dL/dImage
+    zeroed at the flagged pixels in both inputs, so that no gradient depends
+    on a decision that may legitimately flip;
   * max weight (the forward's optional per-splat max of alpha T): within
-    1e-5 absolute for every splat that no flagged pixel could composite (the
-    others: in [0, 0.99]); the forward's other outputs bit-identical with
-    and without it.
+    1e-5 absolute for every splat that no flagged pixel could move (the
+    others: within the oracle's bounds on any admissible maximum); the
+    forward's other outputs bit-identical with and without it.
 """
 import math
 
@@ -30,7 +33,51 @@ IMG_TOL = 1e-5
 T_TOL = 1e-5
 MAXW_TOL = 1e-5
 GRAD_REL = 1e-4
-MAX_AMBIG = 5e-3   # fraction of pixels the oracle may flag
+MAX_AMBIG = 5e-3   # fraction of pixels the oracle may flag (scenes without a measured value)
+# flagged fractions measured on seed 0 (tiny 0, early 1.37e-4, mid 1.97e-4,
+# bench 1.50e-3, stress 2.54e-3); the bound is twice that
+AMBIG_BOUND = {"early": 2.8e-4, "mid": 4e-4, "bench": 3e-3, "stress": 5.1e-3}
+# scalar gradient fields: (output, column) and their names
+FIELDS = [("dL_dmeans2d", "dmeans2d", 0, "dmean_x"), ("dL_dmeans2d", "dmeans2d", 1, "dmean_y"),
+          ("dL_dconics", "dconics", 0, "dconic_a"), ("dL_dconics", "dconics", 1, "dconic_b"),
+          ("dL_dconics", "dconics", 2, "dconic_c"), ("dL_dcolors", "dcolors", 0, "dcolor_r"),
+          ("dL_dcolors", "dcolors", 1, "dcolor_g"), ("dL_dcolors", "dcolors", 2, "dcolor_b"),
+          ("dL_dopacities", "dopacities", None, "dopacity")]
+WEIGHT_FIELD = ("accum_weight", "accum_weight", None, "accum_weight")
+
+
+def field_errors(res, bo, accum_weight=False):
+    """Per scalar field: (max abs error, max |oracle field|)."""
+    out = {}
+    for gk, ok_, col, name in FIELDS + ([WEIGHT_FIELD] if accum_weight else []):
+        ref = bo[ok_] if col is None else bo[ok_][:, col]
+        got = res[gk] if col is None else res[gk][:, col]
+        out[name] = (float(np.abs(got - ref).max(initial=0.0)), float(np.abs(ref).max(initial=0.0)))
+    return out
+
+
+def check_fields(res, bo, accum_weight=False, label=""):
+    errs = field_errors(res, bo, accum_weight)
+    for name, (err, scale) in errs.items():
+        assert err <= GRAD_REL * max(scale, 1e-30), (label, name, err, scale)
+    return {k: (e / s if s > 0 else e) for k, (e, s) in errs.items()}
+
+
+def check_flagged_pixels(sc, rng_o, ids_o, amb, img, T, nc):
+    """Every flagged pixel's image, final_T and n_contrib equal one of its
+    admissible outcomes. Returns (flagged, outcomes per pixel: mean, max)."""
+    ys, xs = np.nonzero(amb)
+    if len(xs) == 0:
+        return 0, 0.0, 0
+    outc = oracle.pixel_outcomes(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
+                                 sc.height, rng_o, ids_o, xs, ys)
+    cnt = outc[3]
+    assert np.all(cnt != -1), f"{int((cnt == -1).sum())} flagged pixels with more than 64 outcomes"
+    match = oracle.matches_an_outcome(img[ys, xs], T[ys, xs], nc[ys, xs], outc, IMG_TOL, T_TOL)
+    bad = np.nonzero(~match)[0]
+    assert bad.size == 0, [(int(xs[i]), int(ys[i]), img[ys[i], xs[i]].tolist(), float(T[ys[i], xs[i]]),
+                            int(nc[ys[i], xs[i]])) for i in bad[:5]]
+    return len(xs), float(cnt.mean()), int(cnt.max())
 
 
 def _say(*a):
@@ -60,12 +107,15 @@ def check_max_weight(sc, bins, ids_o, rng_o, img, T, nc):
     img2, T2, nc2, mw = gpu_fwd(sc, bins, max_weight=True)
     torch.cuda.synchronize()
     assert torch.equal(img2, img) and torch.equal(T2, T) and torch.equal(nc2, nc)
-    mw_o, unc = oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
-                                  sc.width, sc.height, rng_o, ids_o)
+    mw_o, unc, lo, hi = oracle.max_weight(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                                          sc.width, sc.height, rng_o, ids_o, bounds=True)
     mw = mw.cpu().numpy().astype(np.float64)
     err = np.abs(mw - mw_o)[~unc].max(initial=0.0)
     assert err <= MAXW_TOL, err
     assert np.all(mw >= 0.0) and np.all(mw <= 0.99 + 1e-6)
+    # an uncertain splat's maximum: within the bounds of every admissible one
+    out_of_bounds = (mw < lo - MAXW_TOL) | (mw > hi + MAXW_TOL)
+    assert not out_of_bounds.any(), np.nonzero(out_of_bounds)[0][:10]
     assert unc.mean() <= 0.01, unc.mean()
     return err, int(unc.sum())
 
@@ -105,7 +155,8 @@ def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store")):
                               sc.width, sc.height, rng_o, ids_o)
     amb = fo["ambiguous"]
     ok = ~amb
-    assert amb.sum() <= max(MAX_AMBIG * amb.size, 8), amb.mean()
+    bound = AMBIG_BOUND.get(sc.name, MAX_AMBIG) if sc.seed == 0 else MAX_AMBIG
+    assert amb.sum() <= max(bound * amb.size, 8), amb.mean()
     img = img.cpu().numpy().astype(np.float64)
     T = T.cpu().numpy().astype(np.float64)
     nc_h = nc.cpu().numpy()
@@ -114,16 +165,15 @@ def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store")):
     assert err_img <= IMG_TOL, err_img
     assert err_T <= T_TOL, err_T
     np.testing.assert_array_equal(nc_h[ok], fo["n_contrib"][ok])
+    n_flag, mean_out, max_out = check_flagged_pixels(sc, rng_o, ids_o, amb, img, T, nc_h)
+    _say(f"flagged pixels {n_flag} ({n_flag / amb.size:.2e}), each equal to one of its admissible outcomes "
+         f"(mean {mean_out:.2f}, max {max_out} per pixel); uncertain max-weight splats {n_unc}")
 
     _say(f"backward (ambiguous px {int(amb.sum())})")
     g = sc.dL_dimage.copy()
     g[amb] = 0.0
     bo = oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
                               sc.width, sc.height, rng_o, ids_o, g)
-    pairs = [("dL_dmeans2d", "dmeans2d"), ("dL_dconics", "dconics"), ("dL_dcolors", "dcolors"),
-             ("dL_dopacities", "dopacities")]
-    if accum_weight:
-        pairs.append(("accum_weight", "accum_weight"))
     all_results = []
     for walk in walks:
         results = []
@@ -137,15 +187,9 @@ def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store")):
             for k in res:
                 np.testing.assert_allclose(res[k], results[0][k], rtol=1e-5,
                                            atol=1e-6 * max(np.abs(results[0][k]).max(), 1e-30), err_msg=k)
-        errs = {}
         for res in results:
-            for gk, ok_ in pairs:
-                ref = bo[ok_]
-                scale = np.abs(ref).max(initial=0.0)
-                err = np.abs(res[gk] - ref).max(initial=0.0)
-                errs[gk] = err / scale if scale > 0 else err
-                assert err <= GRAD_REL * max(scale, 1e-30), (walk, gk, err, scale)
-        _say(f"walk {walk}: max rel err", {k: f"{v:.2e}" for k, v in errs.items()},
+            errs = check_fields(res, bo, accum_weight, label=walk)
+        _say(f"walk {walk}: per-field err / max|field|", {k: f"{v:.2e}" for k, v in errs.items()},
              f"img {err_img:.2e} T {err_T:.2e}", f"max weight {err_mw:.2e} ({n_unc} uncertain splats)")
         all_results += results
     return bins, all_results
@@ -300,9 +344,14 @@ def test_bench_sampled_tiles_at_full_size():
     fo = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
                               sc.height, rng_o, ids_o, tiles=tiles)
     ys, xs = np.mgrid[0:sc.height, 0:sc.width]
-    sel = np.isin((ys // 16) * GX + xs // 16, tiles) & ~fo["ambiguous"]
-    np.testing.assert_allclose(img.cpu().numpy()[sel], fo["image"][sel], atol=IMG_TOL, rtol=0)
-    np.testing.assert_array_equal(nc.cpu().numpy()[sel], fo["n_contrib"][sel])
+    in_tiles = np.isin((ys // 16) * GX + xs // 16, tiles)
+    sel = in_tiles & ~fo["ambiguous"]
+    img_h, T_h, nc_h = img.cpu().numpy(), T.cpu().numpy(), nc.cpu().numpy()
+    np.testing.assert_allclose(img_h[sel], fo["image"][sel], atol=IMG_TOL, rtol=0)
+    np.testing.assert_allclose(T_h[sel], fo["final_T"][sel], atol=T_TOL, rtol=0)
+    np.testing.assert_array_equal(nc_h[sel], fo["n_contrib"][sel])
+    n_flag, _, _ = check_flagged_pixels(sc, rng_o, ids_o, in_tiles & fo["ambiguous"], img_h, T_h, nc_h)
+    _say(f"sampled bench tiles: {int(sel.sum())} pixels, {n_flag} flagged ones on an admissible outcome")
 
 
 def test_timed_entry_point_matches_and_orders_its_events():
@@ -384,11 +433,7 @@ def test_out_of_range_ids_and_ranges():
                               rng_o, ids_o, g)
     for walk in ("add", "store"):
         out = gpu_bwd(sc, gb, T, nc, g, walk=walk)
-        for gk, ok_ in [("dL_dmeans2d", "dmeans2d"), ("dL_dconics", "dconics"), ("dL_dcolors", "dcolors"),
-                        ("dL_dopacities", "dopacities")]:
-            ref = bo[ok_]
-            err = np.abs(out[gk].cpu().numpy() - ref).max()
-            assert err <= GRAD_REL * np.abs(ref).max(), (walk, gk, err)
+        check_fields({k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}, bo, label=walk)
     # ranges: one past the end of the pair list, one inverted, one starting below 0
     _, T0, nc0 = gpu_fwd(sc, bins)
     r2 = rng.copy()
