@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import GS_FLAG_ACCUM_WEIGHT, GsError
 
 __all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_rasterize_bwd_workspace_size",
-           "gs_rasterize_fwd_workspace_size",
+           "gs_rasterize_fwd_workspace_size", "gs_rasterize_bwd_noalloc", "gs_rasterize_bwd_noalloc_capacity",
            "gs_version", "GsError", "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid", "Bins"]
 
 TILE = 16
@@ -190,19 +190,8 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     return image, final_T, n_contrib
 
 
-def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, width: int, height: int, bins: Bins,
-                     final_T, n_contrib, dL_dimage, accum_weight: bool = False, out=None, workspace=None,
-                     stream=None, events=None, walk=None):
-    """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
-    dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
-    per-splat accumulated weight [n]. ``walk``: None (the library chooses by
-    the mean tiles per splat), "add" or "store" (GS_FLAG_WALK_ADD /
-    GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
-    (same dict keys) and ``workspace`` a uint8 device buffer of at least
-    gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
-    allocation out of timed loops. ``events``: four torch.cuda.Event objects
-    (timing enabled, already recorded once) to be recorded at the call's
-    stage boundaries (gs_rasterize_bwd_timed)."""
+def _check_bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                    n_contrib, dL_dimage, workspace):
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
     _need(conics, "conics", torch.float32, (n, 3))
@@ -219,34 +208,72 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     _need(final_T, "final_T", torch.float32, (height, width))
     _need(n_contrib, "n_contrib", torch.int32, (height, width))
     _need(dL_dimage, "dL_dimage", torch.float32, (height, width, 3))
-    dev = means2d.device
-    _same_device(dev, conics=conics, colors=colors, opacities=opacities, radii=radii, background=background,
-                 tile_ranges=bins.tile_ranges, sorted_ids=bins.sorted_ids, splat_offsets=bins.splat_offsets,
-                 final_T=final_T, n_contrib=n_contrib, dL_dimage=dL_dimage, workspace=workspace)
-    lib = _lib.load()
+    _same_device(means2d.device, conics=conics, colors=colors, opacities=opacities, radii=radii,
+                 background=background, tile_ranges=bins.tile_ranges, sorted_ids=bins.sorted_ids,
+                 splat_offsets=bins.splat_offsets, final_T=final_T, n_contrib=n_contrib, dL_dimage=dL_dimage,
+                 workspace=workspace)
+
+
+def _output_shapes(n, accum_weight):
     shapes = {"dL_dmeans2d": (n, 2), "dL_dconics": (n, 3), "dL_dcolors": (n, 3), "dL_dopacities": (n,)}
     if accum_weight:
         shapes["accum_weight"] = (n,)
+    return shapes
+
+
+def _check_outputs(out, n, accum_weight, dev):
+    """The kernels write every element: shapes, dtype and device are checked like the inputs."""
     if out is None:
-        out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
-    else:  # the kernels write every element: shapes, dtype and device are checked like the inputs
-        for k, v in shapes.items():
-            if k not in out:
-                raise ValueError(f"out lacks {k!r}")
-            _need(out[k], k, torch.float32, v)
-            _same_device(dev, **{k: out[k]})
-    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
-    workspace, wsp = _workspace(workspace, ws_bytes, dev)
+        raise ValueError("out: a dict of preallocated outputs is required")
+    for k, v in _output_shapes(n, accum_weight).items():
+        if k not in out:
+            raise ValueError(f"out lacks {k!r}")
+        _need(out[k], k, torch.float32, v)
+        _same_device(dev, **{k: out[k]})
+
+
+def _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T, n_contrib,
+              dL_dimage, out, accum_weight, walk):
+    """The C arguments up to and including flags."""
+    n = int(means2d.shape[0])
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
     if walk is not None:
         if walk not in ("add", "store"):
             raise ValueError(f"walk: None, 'add' or 'store', not {walk!r}")
         flags |= _lib.GS_FLAG_WALK_ADD if walk == "add" else _lib.GS_FLAG_WALK_STORE
-    args = (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
+    return (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
             height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
             _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
-            _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]), _ptr(out.get("accum_weight") if accum_weight else None),
-            flags, wsp, ws_bytes, _stream(stream, dev))
+            _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]),
+            _ptr(out.get("accum_weight") if accum_weight else None), flags)
+
+
+def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, width: int, height: int, bins: Bins,
+                     final_T, n_contrib, dL_dimage, accum_weight: bool = False, out=None, workspace=None,
+                     stream=None, events=None, walk=None):
+    """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
+    dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
+    per-splat accumulated weight [n]. ``walk``: None (the library chooses by
+    the mean tiles per splat), "add" or "store" (GS_FLAG_WALK_ADD /
+    GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
+    (same dict keys) and ``workspace`` a uint8 device buffer of at least
+    gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
+    allocation out of timed loops. ``events``: four torch.cuda.Event objects
+    (timing enabled, already recorded once) to be recorded at the call's
+    stage boundaries (gs_rasterize_bwd_timed)."""
+    n = int(means2d.shape[0])
+    dev = means2d.device
+    _check_bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                    n_contrib, dL_dimage, workspace)
+    lib = _lib.load()
+    if out is None:
+        out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in _output_shapes(n, accum_weight).items()}
+    else:
+        _check_outputs(out, n, accum_weight, dev)
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
+    workspace, wsp = _workspace(workspace, ws_bytes, dev)
+    args = _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                     n_contrib, dL_dimage, out, accum_weight, walk) + (wsp, ws_bytes, _stream(stream, dev))
     if events is not None and len(events) != 4:
         raise ValueError("events: four torch.cuda.Event objects")
     with torch.cuda.device(dev):
@@ -256,6 +283,32 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
             handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
             _lib.check(lib.gs_rasterize_bwd_timed(*args, handles))
     return out
+
+
+def gs_rasterize_bwd_noalloc(means2d, conics, colors, opacities, radii, background, width: int, height: int,
+                             bins: Bins, final_T, n_contrib, dL_dimage, out, accum_weight: bool = False,
+                             stream=None, walk=None):
+    """gs_rasterize_bwd with its workspace in the library's fixed device
+    array (no allocation by the library; ``out`` holds the caller's
+    preallocated outputs, the keys of gs_rasterize_bwd's result). Raises
+    GsError (GS_ERR_CAPACITY) when the scene needs more than
+    gs_rasterize_bwd_noalloc_capacity() bytes. Calls that overlap on one GPU
+    share that array and race."""
+    n = int(means2d.shape[0])
+    dev = means2d.device
+    _check_bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                    n_contrib, dL_dimage, None)
+    _check_outputs(out, n, accum_weight, dev)
+    lib = _lib.load()
+    args = _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                     n_contrib, dL_dimage, out, accum_weight, walk)
+    with torch.cuda.device(dev):
+        _lib.check(lib.gs_rasterize_bwd_noalloc(*args, _stream(stream, dev)))
+    return out
+
+
+def gs_rasterize_bwd_noalloc_capacity() -> int:
+    return int(_lib.load().gs_rasterize_bwd_noalloc_capacity())
 
 
 def gs_rasterize_bwd_workspace_size(n: int, n_isect: int, width: int, height: int) -> int:

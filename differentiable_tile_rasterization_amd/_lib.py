@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_CAPACITY", 3: "G
 # Every symbol include/gsraster.h declares.
 EXPORTS = ["gs_last_error", "gs_version", "gs_bin_tiles_workspace_size", "gs_bin_tiles",
            "gs_rasterize_fwd_workspace_size", "gs_rasterize_fwd", "gs_rasterize_bwd_workspace_size",
-           "gs_rasterize_bwd", "gs_rasterize_bwd_timed"]
+           "gs_rasterize_bwd", "gs_rasterize_bwd_timed", "gs_rasterize_bwd_noalloc_capacity",
+           "gs_rasterize_bwd_noalloc"]
 
 _lib = None
 
@@ -65,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.gs_rasterize_bwd.restype = ctypes.c_int
     lib.gs_rasterize_bwd_timed.argtypes = lib.gs_rasterize_bwd.argtypes + [ctypes.POINTER(P)]
     lib.gs_rasterize_bwd_timed.restype = ctypes.c_int
+    lib.gs_rasterize_bwd_noalloc_capacity.argtypes = []
+    lib.gs_rasterize_bwd_noalloc_capacity.restype = sz
+    lib.gs_rasterize_bwd_noalloc.argtypes = lib.gs_rasterize_bwd.argtypes[:22] + [P]
+    lib.gs_rasterize_bwd_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 

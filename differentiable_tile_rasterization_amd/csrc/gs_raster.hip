@@ -34,6 +34,7 @@
 // coefficients, and at 72 bytes (unaligned, seven workgroups per CU instead of
 // six) the walk ran slower (0.500 against 0.464 ms on the 2M-splat scene).
 #include <cstddef>
+#include <mutex>
 #include <type_traits>
 
 #include "gs_common.hpp"
@@ -1705,4 +1706,76 @@ extern "C" gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, con
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
                     sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, events);
+}
+
+// ---------------------------------------------------------------------------
+// gs_rasterize_bwd_noalloc: the backward with its workspace in a fixed device
+// array, for callers that cannot allocate (graph capture, tight serving
+// loops). The array is a file-scope device variable: every GPU the library
+// runs on holds its own copy, at its own address, until the process ends. Host
+// code never passes the array's name to a kernel (on the host it only stands
+// for the symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept per device.
+// ---------------------------------------------------------------------------
+namespace gs {
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;   // 64 MiB per device
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+}  // namespace gs
+
+static __device__ __align__(256) unsigned char scratch[gs::kScratchBytes];
+
+namespace {
+// The current device's address of the scratch array (looked up on the first
+// call on that device).
+gs_status scratch_address(void** out)
+{
+    int dev = -1;
+    GS_HIP(hipGetDevice(&dev));
+    GS_CHECK_ARG(dev >= 0 && dev < kMaxDevices, "gs_rasterize_bwd_noalloc: device %d beyond %d devices", dev,
+                 kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        GS_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        GS_CHECK_ARG(p != nullptr && ((uintptr_t)p & 255) == 0, "gs_rasterize_bwd_noalloc: scratch address %p",
+                     p);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GS_OK;
+}
+}  // namespace
+
+extern "C" size_t gs_rasterize_bwd_noalloc_capacity(void) { return kScratchBytes; }
+
+extern "C" gs_status gs_rasterize_bwd_noalloc(int32_t n, const float* means2d, const float* conics,
+                                              const float* colors, const float* opacities, const int32_t* radii,
+                                              const float* background, int32_t width, int32_t height,
+                                              const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                              const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                              const int32_t* n_contrib, const float* dL_dimage,
+                                              float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                              float* dL_dopacities, float* accum_weight, uint32_t flags,
+                                              gs_stream_t stream)
+{
+    // sizes first, on the host: a call that would not fit touches no device
+    const size_t need = gs_rasterize_bwd_workspace_size(n, n_isect, width, height);
+    GS_CHECK_ARG(need > 0, "gs_rasterize_bwd_noalloc: n = %d, n_isect = %lld or image %d x %d out of range", n,
+                 (long long)n_isect, width, height);
+    if (need > kScratchBytes) {
+        set_error("gs_rasterize_bwd_noalloc: %d splats, %lld pairs and %d x %d pixels need %zu bytes of scratch; "
+                  "the fixed scratch holds %zu (use gs_rasterize_bwd with a workspace)",
+                  n, (long long)n_isect, width, height, need, kScratchBytes);
+        return GS_ERR_CAPACITY;
+    }
+    void* ws = nullptr;
+    const gs_status st = scratch_address(&ws);
+    if (st != GS_OK) return st;
+    return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
+                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    dL_dcolors, dL_dopacities, accum_weight, flags, ws, kScratchBytes, stream, nullptr);
 }

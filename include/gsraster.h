@@ -282,6 +282,37 @@ gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* c
                                  float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                                  size_t workspace_bytes, gs_stream_t stream, const gs_event_t events[4]);
 
+/*
+ * gs_rasterize_bwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * gs_rasterize_bwd, less workspace / workspace_bytes; the caller still passes
+ * every input and output.
+ *
+ * The workspace gs_rasterize_bwd would take lives in a fixed device array of
+ * the library, gs_rasterize_bwd_noalloc_capacity() bytes (64 MiB), which each
+ * GPU the library runs on holds from its first call until the process ends
+ * (enough for about a million (splat, tile) pairs: gs_rasterize_bwd_workspace_size
+ * tells what a scene needs). A scene that needs more returns GS_ERR_CAPACITY
+ * before anything is enqueued. The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine; its first call on a device looks up
+ * that device's address of the array (hipGetSymbolAddress) and keeps it.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race and
+ * give wrong results. The kernels clear what must start at zero on every
+ * call, so nothing carries over from the previous call.
+ */
+size_t gs_rasterize_bwd_noalloc_capacity(void);
+
+gs_status gs_rasterize_bwd_noalloc(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                   const float* opacities, const int32_t* radii, const float* background,
+                                   int32_t width, int32_t height, const int32_t* tile_ranges,
+                                   const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
+                                   const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                                   float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                   float* dL_dopacities, float* accum_weight, uint32_t flags,
+                                   gs_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

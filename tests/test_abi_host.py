@@ -159,3 +159,22 @@ def test_binding_pair_count_never_exceeds_the_list():
             gsr._pair_count(ids, bad)
     with pytest.raises(ValueError):
         gsr._pair_count(torch.zeros((2, 5), dtype=torch.int32), None)
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_call():
+    """The allocation-free backward checks the scene's size against its fixed
+    scratch on the host first: an oversized call returns GS_ERR_CAPACITY (and
+    bad sizes GS_ERR_INVALID_ARG) without touching a device."""
+    lib = _lib.load()
+    cap = lib.gs_rasterize_bwd_noalloc_capacity()
+    assert cap == 64 << 20
+    p = ctypes.c_void_p(1)
+
+    def call(n=1000, n_isect=0, w=64, h=64):
+        return lib.gs_rasterize_bwd_noalloc(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, p, p, p, p, p, p, p,
+                                            None, 0, None)
+    assert call(n_isect=2_000_000) == _lib.GS_ERR_CAPACITY
+    assert b"scratch" in lib.gs_last_error()
+    assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
+    assert call(w=0) == _lib.GS_ERR_INVALID_ARG
+    assert lib.gs_rasterize_bwd_workspace_size(1000, 1_000_000, 64, 64) <= cap

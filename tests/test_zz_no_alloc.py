@@ -1,0 +1,68 @@
+"""gs_rasterize_bwd_noalloc (the backward with its workspace in the library's
+fixed device array) through the C ABI: two calls in a row, the second on a
+smaller scene, each against gs_rasterize_bwd on the same inputs (each scalar
+gradient field within 1e-4 of its largest magnitude; the two share their
+kernels, so the results agree to a few ulp)."""
+import numpy as np
+import pytest
+import torch
+
+import scenes
+import differentiable_tile_rasterization_amd as gsr
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _inputs(sc):
+    m, q, c, o, r = _dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.radii)
+    bg = _dev(sc.background)
+    bins = gsr.gs_bin_tiles(m, r, _dev(sc.depths), sc.width, sc.height)
+    _, T, nc = gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
+    return (m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, _dev(sc.dL_dimage))
+
+
+def _compare(sc, accum_weight, walk=None):
+    args = _inputs(sc)
+    need = gsr.gs_rasterize_bwd_workspace_size(sc.n, args[8].n_isect, sc.width, sc.height)
+    assert need <= gsr.gs_rasterize_bwd_noalloc_capacity()
+    ref = gsr.gs_rasterize_bwd(*args, accum_weight=accum_weight, walk=walk)
+    out = {k: torch.full_like(v, float("nan")) for k, v in ref.items()}   # every element must be written
+    res = gsr.gs_rasterize_bwd_noalloc(*args, out=out, accum_weight=accum_weight, walk=walk)
+    torch.cuda.synchronize()
+    assert res is out
+    for k, v in ref.items():
+        a = out[k].cpu().numpy().astype(np.float64).reshape(sc.n, -1)
+        b = v.cpu().numpy().astype(np.float64).reshape(sc.n, -1)
+        assert np.isfinite(a).all(), k
+        for j in range(b.shape[1]):
+            scale = np.abs(b[:, j]).max(initial=0.0)
+            assert np.abs(a[:, j] - b[:, j]).max(initial=0.0) <= 1e-4 * max(scale, 1e-30), (k, j)
+            assert np.abs(a[:, j] - b[:, j]).max(initial=0.0) <= 1e-6 * max(scale, 1e-30), (k, j)
+    print(f"[no-alloc] {sc.name} n={sc.n} pairs={args[8].n_isect}: matches gs_rasterize_bwd "
+          f"(scratch {need} of {gsr.gs_rasterize_bwd_noalloc_capacity()} bytes)", flush=True)
+
+
+def test_noalloc_two_calls_second_smaller():
+    _compare(scenes.make_scene("early", 0), accum_weight=False)
+    _compare(scenes.make_scene("tiny", 1), accum_weight=True)
+    _compare(scenes.make_scene("tiny", 2), accum_weight=False, walk="store")
+
+
+def test_noalloc_rejects_a_scene_beyond_its_scratch():
+    sc = scenes.make_scene("mid", 0)
+    args = _inputs(sc)
+    bins = args[8]
+    n = sc.n
+    out = {k: torch.zeros(s, device="cuda:0") for k, s in
+           {"dL_dmeans2d": (n, 2), "dL_dconics": (n, 3), "dL_dcolors": (n, 3), "dL_dopacities": (n,)}.items()}
+    # the same splats with a pair count whose slots would not fit the scratch
+    big = gsr.Bins(torch.zeros(4_000_000, dtype=torch.int32, device="cuda:0"), bins.tile_ranges,
+                   bins.splat_offsets, 4_000_000, sc.width, sc.height)
+    with pytest.raises(gsr.GsError) as e:
+        gsr.gs_rasterize_bwd_noalloc(*args[:8], big, *args[9:], out=out)
+    assert "GS_ERR_CAPACITY" in str(e.value) and "scratch" in str(e.value)
+    assert float(out["dL_dcolors"].abs().sum()) == 0.0   # nothing ran
