@@ -15,7 +15,8 @@ times of the three small workloads).
 Roofline: T_roof = max(T_VALU,min, T_LDS, T_HBM), each an algorithmic count
 over a ceiling measured in the same run (FMA and exp issue, LDS broadcast
 reads and writes, streaming HBM copy); there is no atomic term, the path
-issues no global atomics. ``frac`` is the walk's min-model VALU rate against
+issues no global atomics. T_LDS counts one record write per walked entry and
+one wave-broadcast read per (splat, half-wave) group with a composited pixel. ``frac`` is the walk's min-model VALU rate against
 the part's VALU issue rate from its unit counts; ``frac_measured_roof`` is
 T_roof over the walk's time (its mean launch time from HIP events the library
 records around it on the call's stream); ``call_frac`` the same over the
@@ -45,8 +46,11 @@ VALU_MIN_PER_PAIR = 60
 TRANS_PER_PAIR = 2
 VALU_WALK_PER_WALKED = 14
 VALU_WALK_PER_PAIR = 46
-# LDS traffic of the walk per walked list entry: a 40-byte record written
-# once and read (broadcast) by each of the four waves.
+# LDS traffic of a walk that stages its records in LDS: a 40-byte record
+# written once per walked list entry, and read (wave-broadcast) once per
+# (splat, 8x4 half-wave) group with a composited pixel -- the reads no
+# culling can avoid. The unculled model (every entry read by each of the four
+# waves) is reported beside it as a diagnostic.
 LDS_RECORD_BYTES = 40
 LDS_READS_PER_ENTRY = 4
 # VALU issue of the part, from its unit counts: 256 CUs x 4 SIMDs, one wave64
@@ -103,6 +107,8 @@ def main():
     ap.add_argument("--config", default="bench")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--walk", default=None, choices=["add", "store", "defer"],
+                    help="force one reverse walk (default: the library's choice)")
     ap.add_argument("--cpu-sample", type=float, default=1.0, help="fraction of tiles the oracle baseline runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,14 +137,14 @@ def main():
     ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_isect, sc.width, sc.height) + 256, dtype=torch.uint8,
                      device=dev)
     out = gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw,
-                               workspace=ws)
+                               workspace=ws, walk=args.walk)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     st = ctypes.c_void_p(stream.cuda_stream)
 
     def bwd():
         gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw, out=out,
-                             workspace=ws)
+                             workspace=ws, walk=args.walk)
 
     def fwd():
         gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
@@ -222,20 +228,25 @@ def main():
         f"{lds_bcast_Bps / 1e12:.2f} TB/s, LDS write {lds_write_Bps / 1e12:.1f} TB/s")
 
     # ---- per-stage times, from HIP events the library records on this stream
-    # at its stage boundaries (gs_rasterize_bwd_timed); run before the timed
-    # region, whose calls then see the clocks at their sustained level
-    stage_ms = {"setup": [], "walk": [], "gather": []}
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for e in evs:
-            e.record(stream)
-        gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw, out=out,
-                             workspace=ws, events=evs)
-        torch.cuda.synchronize()
-        for k, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
-            stage_ms[k].append(evs[a].elapsed_time(evs[b]))
-    stage_mean = {k: float(np.mean(v)) for k, v in stage_ms.items()}
-    log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
+    # at its stage boundaries (gs_rasterize_bwd_timed); measured once before
+    # the timed region (the clocks then settle under sustained load) and once
+    # after it, whose means the roofline uses
+    def stage_times():
+        stage_ms = {"setup": [], "walk": [], "gather": []}
+        for _ in range(args.steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for e in evs:
+                e.record(stream)
+            gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw, out=out,
+                                 workspace=ws, events=evs, walk=args.walk)
+            torch.cuda.synchronize()
+            for k, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
+                stage_ms[k].append(evs[a].elapsed_time(evs[b]))
+        return {k: float(np.mean(v)) for k, v in stage_ms.items()}
+
+    stage_pre = stage_times()
+    log("stages before the timed region (ms, mean of %d calls): " % args.steps
+        + ", ".join(f"{k} {v:.4f}" for k, v in stage_pre.items()))
 
     # ---- timed region: exactly K backward calls, synchronised on both sides
     for _ in range(args.warmup):
@@ -252,6 +263,8 @@ def main():
     ms_region = e0.elapsed_time(e1) / args.steps
     log(f"timed region: {args.steps} calls, {ms_region:.4f} ms/call (events), wall {wall * 1e3 / args.steps:.4f}")
     t_calls = per_call(bwd, args.steps, 1)
+    stage_mean = stage_times()
+    log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
     t_fwd = per_call(fwd, 10, 2)
     t_mw = per_call(fwd_max_weight, 10, 2)
     t0 = time.perf_counter()
@@ -269,7 +282,8 @@ def main():
     valu_walk = VALU_WALK_PER_WALKED * p_walk + VALU_WALK_PER_PAIR * p_contrib
     trans_walk = p_walk + p_contrib
     lds_write_bytes = entries * LDS_RECORD_BYTES
-    lds_read_bytes = entries * LDS_RECORD_BYTES * LDS_READS_PER_ENTRY
+    lds_read_bytes = groups_half * LDS_RECORD_BYTES
+    lds_read_bytes_unculled = entries * LDS_RECORD_BYTES * LDS_READS_PER_ENTRY
     hbm_bytes = sc.n * 36 + entries * 4 + len(bins.tile_ranges) * 8 + sc.width * sc.height * 20 \
         + sc.n * 4 * nfields
     # each term: an algorithmic count over a ceiling measured above
@@ -300,9 +314,11 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["traffic_source"] = traffic_src
-    # the library's choice of reverse walk (more than 16 tiles per splat: stored partials)
-    roof["kernel"] = ("bwd_store_kernel (reverse walk, stored partials)" if bins.n_isect > 16 * sc.n
-                      else "bwd_kernel (reverse walk, LDS adds)")
+    # the reverse walk that ran (the library's default: the deferred walk)
+    walk_used = args.walk or "defer"
+    roof["kernel"] = {"add": "bwd_kernel (reverse walk, LDS adds)",
+                      "store": "bwd_store_kernel (reverse walk, stored partials)",
+                      "defer": "bwd_defer_kernel (reverse walk, deferred reduction)"}[walk_used]
     roof["kernel_ms"] = stage_mean["walk"]
     roof["terms_ms"] = terms
     roof["binding_term"] = bound_term
@@ -310,7 +326,9 @@ def main():
     roof["frac_measured_roof"] = t_roof / t_walk     # T_roof / walk time, every term on a measured ceiling
     roof["call_frac"] = t_roof / t_s                 # the same against the whole call
     roof["stages_ms"] = stage_mean
+    roof["stages_ms_before_timed_region"] = stage_pre
     roof["walk_model_ms"] = (valu_walk / fma_lane_ops + trans_walk / exp_rate) * 1e3   # diagnostic
+    roof["lds_unculled_model_ms"] = (lds_write_bytes / lds_write_Bps + lds_read_bytes_unculled / lds_bcast_Bps) * 1e3
     roof["algorithmic"] = {
         "composited_pairs": p_contrib, "walked_pairs": p_walk, "walked_entries": entries,
         "valu_min_lane_ops": valu_min, "transcendentals_min": trans_min,

@@ -238,9 +238,10 @@ def _bwd_args(means2d, conics, colors, opacities, radii, background, width, heig
     n = int(means2d.shape[0])
     flags = GS_FLAG_ACCUM_WEIGHT if accum_weight else 0
     if walk is not None:
-        if walk not in ("add", "store"):
-            raise ValueError(f"walk: None, 'add' or 'store', not {walk!r}")
-        flags |= _lib.GS_FLAG_WALK_ADD if walk == "add" else _lib.GS_FLAG_WALK_STORE
+        walks = {"add": _lib.GS_FLAG_WALK_ADD, "store": _lib.GS_FLAG_WALK_STORE, "defer": _lib.GS_FLAG_WALK_DEFER}
+        if walk not in walks:
+            raise ValueError(f"walk: None, 'add', 'store' or 'defer', not {walk!r}")
+        flags |= walks[walk]
     return (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
             height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
             _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
@@ -253,9 +254,9 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
                      stream=None, events=None, walk=None):
     """Backward. Returns dict with dL_dmeans2d [n,2], dL_dconics [n,3],
     dL_dcolors [n,3], dL_dopacities [n] and, with ``accum_weight``, the
-    per-splat accumulated weight [n]. ``walk``: None (the library chooses by
-    the mean tiles per splat), "add" or "store" (GS_FLAG_WALK_ADD /
-    GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
+    per-splat accumulated weight [n]. ``walk``: None (the library's default,
+    the deferred walk), "defer", "add" or "store" (GS_FLAG_WALK_DEFER /
+    GS_FLAG_WALK_ADD / GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
     (same dict keys) and ``workspace`` a uint8 device buffer of at least
     gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
     allocation out of timed loops. ``events``: four torch.cuda.Event objects

@@ -20,6 +20,7 @@ GS_ERR_UNSUPPORTED = 4
 GS_FLAG_ACCUM_WEIGHT = 1
 GS_FLAG_WALK_ADD = 2
 GS_FLAG_WALK_STORE = 4
+GS_FLAG_WALK_DEFER = 8
 
 STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_CAPACITY", 3: "GS_ERR_HIP",
                 4: "GS_ERR_UNSUPPORTED"}

@@ -15,8 +15,8 @@
 //                 random ids; a record costs one 48-byte read per list entry
 //                 where the caller's four separate arrays cost about five
 //                 cache lines.
-//   staging       per batch of list entries (255 and a dummy; 127 and a
-//                 dummy in the stored-partials reverse walk), thread t loads
+//   staging       per batch of list entries (255 and a dummy; 191 or 127
+//                 and a dummy in some reverse walks), thread t loads
 //                 entry t's record, writes the alpha coefficients and colour
 //                 to LDS and tests the splat's alpha >= 1/255 ellipse against
 //                 each 8x4 half-quadrant; ballots build one compacted list per
@@ -217,6 +217,24 @@ template <bool AW> struct BwdParts {
     static constexpr int kCap = AW ? 453 : 503;      // records per batch (at most 26 KB of LDS in all: six workgroups per CU)
 };
 
+// The deferred walk: per (half list, position) records like the stored-partials
+// walk, of the same batch size, at four workgroups per CU (its per-wave pads
+// take 16 KB): 40 KB of LDS in all.
+// NB: entries staged per batch (NB + 1 slots, the last the dummy); KC: lockstep
+// steps between two deferred reductions; WG: workgroups per CU the LDS is
+// sized for. The partial records take what the slots, lists and per-wave
+// pads leave of 160 KB / WG.
+template <bool AW, int NB, int KC, int WG> struct DeferShape {
+    static constexpr int kF = AW ? kRaw : kRaw - 1;
+    static constexpr int kSlots = NB + 1;
+    static constexpr int kListLen = NB + 5;  // up to NB entries, then dummies read ahead of use
+    static constexpr unsigned short kDummyOff = (unsigned short)(NB * sizeof(StoreSlot));
+    static constexpr int kFixed = kSlots * (int)sizeof(StoreSlot) + kHalves * kListLen * 2 + 4 * KC * 64 * 8 +
+                                  4 * (kHalves + 1) * 4 + 2 * kHalves * 4 + 4 * 4 + 4;
+    static constexpr int kCap = ((160 * 1024) / WG - kFixed - 256) / (kF * 4);
+    static_assert(kCap >= 2 * kHalves * KC, "the partial records must hold at least one chunk");
+};
+
 // The stored-partials walk stages at most 127 entries per batch (waves 0 and
 // 1; slot 127 is the dummy): the records, not the slots, bound its batches
 // (a 255-entry batch holds a median of ~590 half-list entries on the
@@ -231,8 +249,9 @@ constexpr unsigned short kSDummyOff = (unsigned short)(kSBatch * sizeof(StoreSlo
 // position is also written into its own slot's pos bytes. The same exchange of
 // per-wave counts also ORs `flag` over the workgroup, which is returned, and
 // gives every half's list length (len, wave-uniform). Ends with a barrier.
+template <int NSlots = kSSlots, int ListLen = kSListLen>
 __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bool flag, StoreSlot* S,
-                                                 unsigned short (*list)[kSListLen], int (*cnt)[kHalves + 1],
+                                                 unsigned short (*list)[ListLen], int (*cnt)[kHalves + 1],
                                                  int (&len)[kHalves])
 {
     const int lane = threadIdx.x & 63;
@@ -258,7 +277,7 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
         }
         top = tot - 1 - below;
     }
-    if (threadIdx.x < kSSlots) *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(0xffffffffu, 0xffffffffu);
+    if (threadIdx.x < NSlots) *reinterpret_cast<uint2*>(S[threadIdx.x].pos) = make_uint2(0xffffffffu, 0xffffffffu);
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
         len[q] = __builtin_amdgcn_readlane(tot, q);
@@ -574,6 +593,390 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         // Flush: thread t owns the entry it staged; its sums are those of the
         // records of the halves that listed it.
         const int slot = threadIdx.x < kSSlots ? S[threadIdx.x].slot : -1;
+        if (slot >= 0) {
+            const uint2 pw = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
+            float u[kRaw] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) {
+                const unsigned at = ((q < 4 ? pw.x : pw.y) >> (8 * (q & 3))) & 0xffu;
+                if (at != 0xffu) {
+                    const float* pr = parts + (half_base[q] + (int)at) * kF;
+#pragma unroll
+                    for (int f = 0; f < kF; ++f) u[f] += pr[f];
+                }
+            }
+            const bool any = (u[0] != 0.0f) | (u[1] != 0.0f) | (u[2] != 0.0f) | (u[3] != 0.0f) |
+                             (u[4] != 0.0f) | (u[5] != 0.0f) | (u[6] != 0.0f) | (u[7] != 0.0f) |
+                             (u[8] != 0.0f) | (AW && u[9] != 0.0f);
+            if (any) {
+                rec_out[3 * (long long)slot + 0] = make_float4(u[0], u[1], u[2], u[3]);
+                rec_out[3 * (long long)slot + 1] = make_float4(u[4], u[5], u[6], u[7]);
+                // the third part's last 8 bytes are padding, never read
+                *reinterpret_cast<float2*>(rec_out + 3 * (long long)slot + 2) = make_float2(u[8], AW ? u[9] : 0.0f);
+                slot_used[slot] = 1;
+            }
+        }
+        hi = next_hi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The deferred walk (the default). The same batches, half lists, (half list,
+// position) records and flush as the stored-partials walk, with the per-step
+// reduction taken out of the lockstep loop:
+//   phase 1, every step: alpha, the contributing lanes, T and the colour
+//     behind, and each lane's w = alpha T and s = dL/dsigma (zeros where it
+//     does not contribute), written to the wave's pad (one float2 per lane);
+//   phase 2, every KC steps: the 2 KC records of those steps (KC steps x two
+//     halves) are split over the 64 lanes, 32 / KC lanes per record, each
+//     lane summing KC pixels of one row of its record's half in registers
+//     (sum w g_r, w g_g, w g_b, s, s k, s k^2 over its column offsets k;
+//     dx = dx0 + k and dy is constant along the row), turning them into the
+//     record's ten sums about the entry's mean, and the record's lanes add
+//     theirs with fused DPP adds; the first lane stores the record.
+// A step then costs about 21 VALU instructions instead of about 50 (the
+// cross-lane tree of the other walks: ~21 per step, and the LDS float adds
+// of the first walk, ~25 LDS cycles each), and phase 2 about 15 per step.
+// The pads (KC x 64 float2 per wave) are written and read by the same wave,
+// whose LDS accesses are served in order: no barrier is needed around them.
+// ---------------------------------------------------------------------------
+template <bool AW, int NB, int KC, int WG>
+__global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
+    int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
+    const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
+    unsigned char* __restrict__ slot_used)
+{
+    using PP = DeferShape<AW, NB, KC, WG>;
+    constexpr int kF = PP::kF, kCap = PP::kCap, kDSlots = PP::kSlots, kDListLen = PP::kListLen;
+    constexpr unsigned short kDDummyOff = PP::kDummyOff;
+    constexpr int kLPR = 32 / KC;   // phase 2: lanes per (half, position) record
+    constexpr int kPPL = KC;        // phase 2: pixels per lane (a row or part of one)
+    __shared__ StoreSlot S[kDSlots];
+    __shared__ float parts[kCap * kF];
+    __shared__ unsigned short list[kHalves][kDListLen];  // per half: slots that may touch it, then dummies
+    __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
+    __shared__ int half_end[kHalves];
+    __shared__ int half_base[kHalves];                 // first partial record of each half, for the flush
+    __shared__ int wave_hits[4];                       // half-list entries of each wave's candidates
+    __shared__ int cut;                                // lowest kept candidate of the batch
+    // per wave: each lane's (w, s) at each step of the current chunk
+    __shared__ __align__(16) float2 pad[4][KC][kWave];
+
+    const int tile = order ? order[blockIdx.x] : xcd_tile(blockIdx.x, tiles);
+    if (tile < 0 || tile >= tiles) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int half = lane >> 5, hq = 2 * wv + half;
+    int x, y;
+    quadrant_pixel(tile, GX, x, y);
+    const bool inside = x < W && y < H;
+    const float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
+    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
+
+    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    int nc = 0;
+    if (inside) {
+        const int p = y * W + x;
+        T = final_T[p];
+        // never walk past the tile's list, whatever n_contrib holds
+        nc = min(max(n_contrib[p], 0), rg.y - rg.x);
+        g0 = dimg[3 * p + 0];
+        g1 = dimg[3 * p + 1];
+        g2 = dimg[3 * p + 2];
+    }
+    // Colour "behind" the current splat (normalised by the transmittance after
+    // it; the background at the start), carried only as its dot product with
+    // the pixel's colour gradient
+    float Bg = 0.0f;
+    if (bg) Bg = __builtin_fmaf(bg[0], g0, __builtin_fmaf(bg[1], g1, bg[2] * g2));
+
+    int hmax = nc;  // largest n_contrib of this half (32 lanes)
+    for (int off = 16; off > 0; off >>= 1) hmax = max(hmax, __shfl_xor(hmax, off, 64));
+    if ((lane & 31) == 0) half_end[hq] = hmax;
+    if (threadIdx.x == 0) {  // the dummy entry: opacity 0, reaches no pixel
+        S[NB].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        S[NB].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
+        S[NB].c = 0.0f;
+    }
+    __syncthreads();
+    int hend[kHalves];  // walk end of every half, wave-uniform
+    int tmax = 0;
+#pragma unroll
+    for (int q = 0; q < kHalves; ++q) {
+        hend[q] = __builtin_amdgcn_readfirstlane(half_end[q]);
+        tmax = max(tmax, hend[q]);
+    }
+    if (tmax == 0) return;
+
+    // Phase-2 role of this lane (fixed for the whole walk): for the record of
+    // step lane / (2 kLPR) of each chunk, it sums kPPL consecutive pixels of
+    // half h of its wave's quadrant (8 x 4 pixels, row-major: pixel u * 8 + kx
+    // is lane 32 h + 8 u + kx), all in one row u, from column kx0. Their colour
+    // gradients come over once through the pad.
+    const int ph = (lane / kLPR) & 1, pv = lane % kLPR;
+    const int pu = (pv * kPPL) >> 3, pkx0 = (pv * kPPL) & 7;
+    float gr[kPPL], gg[kPPL], gb[kPPL];
+    {
+        float* gt = reinterpret_cast<float*>(&pad[wv][0][0]);
+        gt[3 * lane + 0] = g0;
+        gt[3 * lane + 1] = g1;
+        gt[3 * lane + 2] = g2;
+        // the LDS serves one wave's accesses in order, so the reads below see
+        // the other lanes' writes; the compiler must not move them across
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int kx = 0; kx < kPPL; ++kx) {
+            const int src = 32 * ph + 8 * pu + pkx0 + kx;
+            gr[kx] = gt[3 * src + 0];
+            gg[kx] = gt[3 * src + 1];
+            gb[kx] = gt[3 * src + 2];
+        }
+        asm volatile("" ::: "memory");
+    }
+    // centre of this lane's first pixel (pkx0, 4 h + u) of the quadrant
+    const float row_x0 = ox + (float)((wv & 1) * 8 + pkx0);
+    const float row_y = oy + (float)((wv >> 1) * 8 + 4 * ph + pu);
+
+    // No barrier at the top of a batch: thread t flushes slot t and then stages
+    // slot t itself, and the barrier after the walk already separates the
+    // walk's reads of the slots and lists from their rewriting; the partial
+    // records are cleared only after the next barrier.
+    int hi = tmax;  // the batches cover [0, tmax) from the top down
+    while (hi > 0) {
+        const int lo = max(0, hi - NB);  // candidates [lo, hi): entry lo + t in slot t
+        const int k = lo + (int)threadIdx.x;
+        const bool cand = (int)threadIdx.x < NB && k < hi;
+        int id = -1, radius = 0;
+        SplatRec r;
+        r.a = r.b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
+        if (cand) id = ids[rg.x + k];
+        if ((unsigned)id >= (unsigned)n) id = -1;  // an id outside [0, n) is no entry
+        if (id >= 0) {
+            r = recs[id];
+            radius = __float_as_int(r.c.z);
+            S[threadIdx.x].a = r.a;
+            S[threadIdx.x].b = r.b;
+            S[threadIdx.x].c = r.c.x;
+        }
+        bool hit[kHalves] = {false, false, false, false, false, false, false, false};
+        if (threadIdx.x < kDSlots) half_hits(r, ox, oy, k, hend, hit);  // the candidates' waves
+        // Keep the top candidates whose half-list entries fit the partial
+        // records: suffix sums of the hit counts over the slots, from the top.
+        int hc = 0;
+#pragma unroll
+        for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
+        int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_down(suf, off, kWave);
+            if (lane + off < kWave) suf += u;
+        }
+        if (lane == 0) wave_hits[wv] = suf;
+        if (threadIdx.x == 0) cut = NB;
+        __syncthreads();
+        for (int w2 = wv + 1; w2 < 4; ++w2) suf += wave_hits[w2];
+        const bool keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
+        const unsigned long long kb = __ballot(keep);
+        if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));
+        if (!keep) {
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) hit[q] = false;
+        }
+        // The entry's pair slot: the splat's first slot (from its record) plus
+        // the tile's row-major index inside the splat's tile rectangle
+        // (recomputed from mean and radius with the binning's float32 rule).
+        // The tile lies in the rectangle whenever the inputs come from one
+        // binning; anything else gets no slot and is never written wild.
+        {
+            int slot = -1;
+            if (keep && id >= 0) {
+                int tx0, tx1, ty0, ty1;
+                tile_rect(r.a.x, r.a.y, radius, GX, GY, tx0, tx1, ty0, ty1);
+                const int tx = tile % GX, ty = tile / GX;
+                const long long sl =
+                    (long long)__float_as_int(r.c.w) + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
+                if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && sl >= 0 && sl < n_slots) slot = (int)sl;
+            }
+            if (threadIdx.x < kDSlots) S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
+        }
+        // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
+        // exponent never exceeds log2 o, so alpha_raw never exceeds
+        // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
+        // 0.99 never clamps. Most batches have none, and their walk skips the
+        // clamp's three instructions per step.
+        const bool may_clamp = keep && id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
+        int len[kHalves];
+        const bool clamp_batch = build_store_lists<kDSlots, kDListLen>(hit, may_clamp, S, list, list_cnt, len);
+        int base[kHalves];  // first partial record of each half
+        base[0] = 0;
+#pragma unroll
+        for (int q = 1; q < kHalves; ++q) base[q] = base[q - 1] + len[q - 1];
+        const int next_hi = lo + cut;
+        // the wave's two list lengths and first records (wave-uniform selects
+        // over the unrolled halves: no indexing of the register arrays by the
+        // wave number), then this lane's half
+        const int wvu = __builtin_amdgcn_readfirstlane(wv);
+        int len_a = 0, len_b = 0, base_a = 0, base_b = 0;
+#pragma unroll
+        for (int q = 0; q < kHalves; q += 2) {
+            len_a = q == 2 * wvu ? len[q] : len_a;
+            len_b = q == 2 * wvu ? len[q + 1] : len_b;
+            base_a = q == 2 * wvu ? base[q] : base_a;
+            base_b = q == 2 * wvu ? base[q + 1] : base_b;
+        }
+        const int my_len = half ? len_b : len_a, len_other = half ? len_a : len_b;
+        // the bases wait in LDS for the flush (past the barrier after the walk)
+        // rather than in registers through the walk
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int q = 0; q < kHalves; ++q) half_base[q] = base[q];
+        }
+        // the same for both halves: wave-uniform, so the loop runs on scalar control
+        const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
+        // the shorter half takes the dummy entry once its list is exhausted
+        // (and both read up to four entries past the end, ahead of use)
+        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDDummyOff;
+        // batch slots below this pixel's walk end, as a byte offset bound
+        const int ncb_off = (nc - lo) * (int)sizeof(StoreSlot);
+        const unsigned short* L = list[hq];
+        const char* Sb = reinterpret_cast<const char*>(S);
+        // phase 2: this lane's record (half ph of the wave) and its first record
+        const int ph_len = ph ? len_b : len_a, ph_base = ph ? base_b : base_a;
+        const unsigned short* Lp = list[2 * wvu + ph];
+        float2* const my_pad = &pad[wv][0][lane];
+
+        auto rec_at = [&](int o) -> const StoreSlot& { return *reinterpret_cast<const StoreSlot*>(Sb + o); };
+        auto list_at = [&](int i) -> int {
+            int o = L[i];
+            asm("" : "+v"(o));
+            return o;
+        };
+        // Phase 1, one lockstep step: alpha, the contributing lanes, T and the
+        // colour behind recovered; the lane's w = alpha T and s = dL/dsigma go
+        // to the pad (zeros where it does not contribute).
+        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur, int j, auto clamp_tag) {
+            constexpr bool kClamp = decltype(clamp_tag)::value;
+            const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
+            float dx, dy;
+            const float ar = alpha_raw(kf, px, py, dx, dy);
+            const float al = kClamp ? fminf(kAlphaMax, ar) : ar;
+            const unsigned long long bal = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) &
+                                           __builtin_amdgcn_sicmp(cur, ncb_off, 40 /* signed < */);
+            const bool contrib = __builtin_amdgcn_inverse_ballot_w64(bal);
+            const float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
+            // no branch on "no lane contributes" (a few percent of the steps):
+            // those lanes' updates are exact no-ops (alpha 0: T, the colour
+            // behind and w, s unchanged or zero)
+            const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
+            const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
+            const float eg = cg - Bg;
+            Bg = __builtin_fmaf(ae, eg, Bg);
+            T = Ti;
+            const float w = ae * Ti;
+            const float s = (!kClamp || ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
+            my_pad[j * kWave] = make_float2(w, s);
+        };
+        // Phase 2, after each chunk of steps: lane (j, h, u) sums row u of
+        // half h at step c + j in registers: the moments of s over the row's
+        // column offsets kx = 0..7 (dx = dx0 + kx, dy constant along the row)
+        // and w g; four lanes (the rows of the half) then add their totals,
+        // and the first stores the (half, position) record.
+        auto phase2 = [&](int c) {
+            const int jr = lane / (2 * kLPR);   // this lane's record: step c + jr of half ph
+            const int p = c + jr;
+            const bool valid = p < ph_len;
+            const int off = valid ? (int)Lp[min(p, NB)] : (int)kDDummyOff;
+            const float2 mu = *reinterpret_cast<const float2*>(Sb + off);
+            const float4* pp = reinterpret_cast<const float4*>(&pad[wv][jr][32 * ph + 8 * pu + pkx0]);
+            float w_[kPPL], s_[kPPL];
+#pragma unroll
+            for (int i = 0; i < kPPL / 2; ++i) {
+                const float4 q = pp[i];
+                w_[2 * i] = q.x;
+                s_[2 * i] = q.y;
+                w_[2 * i + 1] = q.z;
+                s_[2 * i + 1] = q.w;
+            }
+            // moments of s over the lane's column offsets k (dx = dx0 + k)
+            float S0 = s_[0] + s_[1], Sx = s_[1], Sxx = s_[1];
+            float Wr = w_[0] * gr[0], Wg = w_[0] * gg[0], Wb = w_[0] * gb[0], Wt = w_[0];
+#pragma unroll
+            for (int kx = 1; kx < kPPL; ++kx) {
+                if (kx >= 2) {
+                    S0 += s_[kx];
+                    Sx = __builtin_fmaf((float)kx, s_[kx], Sx);
+                    Sxx = __builtin_fmaf((float)(kx * kx), s_[kx], Sxx);
+                }
+                Wr = __builtin_fmaf(w_[kx], gr[kx], Wr);
+                Wg = __builtin_fmaf(w_[kx], gg[kx], Wg);
+                Wb = __builtin_fmaf(w_[kx], gb[kx], Wb);
+                if (AW) Wt += w_[kx];
+            }
+            const float dx0 = row_x0 - mu.x, dyr = row_y - mu.y;
+            float f[kRaw];
+            f[0] = Wr;
+            f[1] = Wg;
+            f[2] = Wb;
+            f[3] = S0;
+            f[4] = __builtin_fmaf(dx0, S0, Sx);                                  // sum s dx
+            f[5] = dyr * S0;                                                      // sum s dy
+            f[6] = __builtin_fmaf(dx0, __builtin_fmaf(dx0, S0, Sx + Sx), Sxx);   // sum s dx^2
+            f[7] = dyr * f[4];                                                    // sum s dx dy
+            f[8] = dyr * f[5];                                                    // sum s dy^2
+            f[9] = AW ? Wt : 0.0f;
+            // the record's kLPR lanes add their totals: inside each quad, then
+            // (eight lanes) between the two quads of each 8-lane half-row
+#pragma unroll
+            for (int q = 0; q < kF; ++q) {
+                f[q] = dpp_add_quad_xor1(dpp_add_quad_xor2(f[q]));
+                if (kLPR == 8) f[q] = dpp_add_half_mirror(f[q]);
+                asm volatile("" : "+v"(f[q]));  // fused DPP adds, outside the store's lane mask
+            }
+            if (pv == 0 && valid) {
+                float* rec = parts + (ph_base + p) * kF;
+#pragma unroll
+                for (int q = 0; q < kF; ++q) rec[q] = f[q];
+            }
+        };
+        auto walk = [&](auto clamp_tag) {
+            int o_cur = list_at(0), o_nxt = list_at(1);
+            float4 A = rec_at(o_cur).a, B = rec_at(o_cur).b;
+            float C = rec_at(o_cur).c;
+            for (int c = 0; c < steps; c += KC) {
+#pragma unroll
+                for (int j = 0; j < KC; ++j) {
+                    const int it = c + j;
+                    if (it >= steps) break;   // wave-uniform
+                    // the next entry's record one step ahead, its list entry two
+                    const float4 An = rec_at(o_nxt).a, Bn = rec_at(o_nxt).b;
+                    const float Cn = rec_at(o_nxt).c;
+                    const int o_nn = list_at(it + 2);
+                    step(A, B, C, o_cur, j, clamp_tag);
+                    A = An;
+                    B = Bn;
+                    C = Cn;
+                    o_cur = o_nxt;
+                    o_nxt = o_nn;
+                }
+                // the pad's rows go from the lanes that wrote them to the lanes
+                // that sum them: LDS accesses of one wave are served in order, so
+                // keeping the compiler from reordering them is enough
+                asm volatile("" ::: "memory");
+                phase2(c);
+                asm volatile("" ::: "memory");
+            }
+        };
+        if (clamp_batch)
+            walk(std::true_type{});
+        else
+            walk(std::false_type{});
+        __syncthreads();
+
+        // Flush: thread t owns the entry it staged; its sums are those of the
+        // records of the halves that listed it.
+        const int slot = threadIdx.x < kDSlots ? S[threadIdx.x].slot : -1;
         if (slot >= 0) {
             const uint2 pw = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
             float u[kRaw] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -1304,7 +1707,17 @@ __device__ __forceinline__ void gather_write(int i, const float (&u)[10], const 
 // opacity and writes every output (zeros for a splat no pixel took).
 constexpr int kGatherWin = 16 * kWave;  // flag bytes scanned per step
 constexpr int kGatherRegMaxPairs = 32;  // mean pairs per splat up to which gather_kernel runs
-constexpr int kWalkStoreMinPairs = 16;  // mean pairs per splat above which the stored-partials walk runs
+constexpr int kWalkManyPairs = 16;  // mean pairs per splat above which the deferred walk takes smaller batches
+// Shapes of the deferred walk (entries per batch, steps per chunk, workgroups
+// per CU), measured on the 2M-splat and the high-overlap scenes: 255-entry
+// batches where splats cover few tiles; 191 where they cover many (more
+// half-list records per entry: the smaller batch leaves room for 552 records
+// against 438, and fewer batches are cut). Four-step chunks keep the per-wave
+// pads at 2 KB, so four workgroups per CU fit; eight-step chunks (cheaper
+// phase 2) need 4 KB pads and ran slower at three workgroups per CU or with
+// 127-entry batches.
+constexpr int kDeferChunk = 4, kDeferWG = 4;
+constexpr int kDeferBatchFew = 255, kDeferBatchMany = 191;
 
 template <bool AW>
 __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
@@ -1598,15 +2011,19 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
                  (long long)n_isect);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
                  "gs_rasterize_bwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
-    GS_CHECK_ARG((flags & ~(uint32_t)(GS_FLAG_ACCUM_WEIGHT | GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE)) == 0,
+    constexpr uint32_t kWalkFlags = GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE | GS_FLAG_WALK_DEFER;
+    GS_CHECK_ARG((flags & ~(uint32_t)(GS_FLAG_ACCUM_WEIGHT | kWalkFlags)) == 0,
                  "gs_rasterize_bwd: unknown flags 0x%x", flags);
-    GS_CHECK_ARG((flags & (GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE)) != (GS_FLAG_WALK_ADD | GS_FLAG_WALK_STORE),
-                 "gs_rasterize_bwd: GS_FLAG_WALK_ADD and GS_FLAG_WALK_STORE both set");
+    GS_CHECK_ARG(__builtin_popcount(flags & kWalkFlags) <= 1,
+                 "gs_rasterize_bwd: more than one walk flag set (GS_FLAG_WALK_ADD, _STORE, _DEFER)");
     const bool aw = (flags & GS_FLAG_ACCUM_WEIGHT) != 0;
     // the stored-partials walk pays off where splats cover many tiles (more
     // contributing lanes per step, more LDS adds per entry)
-    const bool store_walk = (flags & GS_FLAG_WALK_STORE) != 0 ||
-                            ((flags & GS_FLAG_WALK_ADD) == 0 && n_isect > (long long)kWalkStoreMinPairs * n);
+    // the deferred walk unless another is forced; its batch size by the mean
+    // tiles per splat
+    const bool store_walk = (flags & GS_FLAG_WALK_STORE) != 0;
+    const bool add_walk = (flags & GS_FLAG_WALK_ADD) != 0;
+    const bool many_tiles = n_isect > (long long)kWalkManyPairs * n;
     GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities && radii && splat_offsets),
                  "gs_rasterize_bwd: NULL splat array");
     GS_CHECK_ARG(n == 0 || (dL_dmeans2d && dL_dconics && dL_dcolors && dL_dopacities),
@@ -1651,8 +2068,14 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         };
         if (store_walk)
             aw ? launch(bwd_store_kernel<true>) : launch(bwd_store_kernel<false>);
-        else
+        else if (add_walk)
             aw ? launch(bwd_kernel<true>) : launch(bwd_kernel<false>);
+        else if (many_tiles)
+            aw ? launch(bwd_defer_kernel<true, kDeferBatchMany, kDeferChunk, kDeferWG>)
+               : launch(bwd_defer_kernel<false, kDeferBatchMany, kDeferChunk, kDeferWG>);
+        else
+            aw ? launch(bwd_defer_kernel<true, kDeferBatchFew, kDeferChunk, kDeferWG>)
+               : launch(bwd_defer_kernel<false, kDeferBatchFew, kDeferChunk, kDeferWG>);
         GS_HIP(hipGetLastError());
         GS_HIP(mark(2));
     } else {

@@ -27,9 +27,9 @@ import sys
 
 COPY_BYTES = 1 << 30          # the copy kernel moves 1 GiB in and 1 GiB out per launch
 COPY_NAME = "copy_kernel"
-CALL_KERNELS = ["bwd_setup_kernel", "band_order_kernel", "bwd_kernel", "bwd_store_kernel", "gather_kernel",
-                "gather_staged_kernel"]
-DOMINANT = ("bwd_kernel<", "bwd_store_kernel<")  # the reverse walk (either form): the roofline's kernel
+CALL_KERNELS = ["bwd_setup_kernel", "band_order_kernel", "bwd_defer_kernel", "bwd_kernel", "bwd_store_kernel",
+                "gather_kernel", "gather_staged_kernel"]
+DOMINANT = ("bwd_defer_kernel<", "bwd_kernel<", "bwd_store_kernel<")  # the reverse walk (any form): the roofline's kernel
 
 
 def _short(name: str) -> str:

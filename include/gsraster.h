@@ -97,20 +97,30 @@ enum {
      * kernels: without the flag no instruction, register or global store is
      * spent on it. The LDS-add walk keeps an 80-byte LDS slot per staged
      * entry in both instances (16-byte aligned records at an odd multiple of
-     * 16 bytes); the stored-partials walk's records are 36 bytes without the
-     * weight and 40 with it. */
+     * 16 bytes); the records of the deferred and stored-partials walks are 36
+     * bytes without the weight and 40 with it. */
     GS_FLAG_ACCUM_WEIGHT = 1u << 0,
-    /* Force one of the two reverse walks (same results up to the order of
-     * float additions). Without either, the call takes the stored-partials
-     * walk when the splats average more than 16 tiles each, else the LDS-add
-     * walk. Setting both is an invalid argument.
-     *   WALK_ADD:   each wave adds its per-step totals into the entry's LDS
-     *               partial sums (float LDS adds; 255-entry batches);
-     *   WALK_STORE: each (half-list, position) step stores its totals into a
-     *               record of its own (no adds; batches of at most 127
-     *               entries, cut further if their records would not fit). */
+    /* Force one of the three reverse walks (same results up to the order of
+     * float additions); setting more than one is an invalid argument.
+     * Without any, the call takes the deferred walk.
+     *   WALK_DEFER: each lockstep step only recovers alpha, T and the colour
+     *               behind and parks each lane's (w = alpha T, s = dL/dsigma)
+     *               in a per-wave buffer; every four steps the lanes sum the
+     *               (half-list, position) records of those steps in registers
+     *               (moments of s and w over their pixels) and store them;
+     *               each entry's records are summed once per batch (no LDS
+     *               float adds). Batches of 255 entries, or 191 when the
+     *               splats average more than 16 tiles each.
+     *   WALK_ADD:   each step reduces its ten sums across the half-wave and
+     *               adds them into the entry's LDS partial sums (float LDS
+     *               adds; 255-entry batches);
+     *   WALK_STORE: each (half-list, position) step reduces and stores its
+     *               totals into a record of its own (no adds; batches of at
+     *               most 127 entries, cut further if their records would not
+     *               fit). */
     GS_FLAG_WALK_ADD = 1u << 1,
-    GS_FLAG_WALK_STORE = 1u << 2
+    GS_FLAG_WALK_STORE = 1u << 2,
+    GS_FLAG_WALK_DEFER = 1u << 3
 };
 
 /* Thread-local description of the last non-OK status returned on this thread. */

@@ -81,8 +81,11 @@ def test_bwd_rejects_bad_arguments():
     assert call(n=-5) == _lib.GS_ERR_INVALID_ARG
     assert call(flags=0x80) == _lib.GS_ERR_INVALID_ARG
     assert b"unknown flags" in lib.gs_last_error()
-    assert call(flags=_lib.GS_FLAG_WALK_ADD | _lib.GS_FLAG_WALK_STORE) == _lib.GS_ERR_INVALID_ARG
-    assert b"both set" in lib.gs_last_error()
+    for two in (_lib.GS_FLAG_WALK_ADD | _lib.GS_FLAG_WALK_STORE, _lib.GS_FLAG_WALK_ADD | _lib.GS_FLAG_WALK_DEFER,
+                _lib.GS_FLAG_WALK_STORE | _lib.GS_FLAG_WALK_DEFER):
+        assert call(flags=two) == _lib.GS_ERR_INVALID_ARG
+        assert b"more than one walk flag" in lib.gs_last_error()
+    assert call(flags=0x10) == _lib.GS_ERR_INVALID_ARG
     assert call(flags=_lib.GS_FLAG_ACCUM_WEIGHT, aw=None) == _lib.GS_ERR_INVALID_ARG
     assert b"accum_weight" in lib.gs_last_error()
     assert call(grad=ctypes.c_void_p(0)) == _lib.GS_ERR_INVALID_ARG

@@ -137,9 +137,9 @@ def check_bins(sc, bins):
     return ids_o, rng_o
 
 
-def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store")):
+def check_scene(sc, accum_weight=None, runs=1, walks=("add", "store", "defer")):
     """Full parity of one scene: bins, forward, backward (with each of the
-    two reverse walks by default)."""
+    three reverse walks by default)."""
     if accum_weight is None:
         accum_weight = sc.accum_weight
     _say(f"scene {sc.name} seed {sc.seed} {sc.width}x{sc.height} n={sc.n}: binning")
@@ -295,7 +295,7 @@ def test_no_splats_and_no_intersections():
     assert np.all(bins.tile_ranges.cpu().numpy() == 0)
     img, T, nc = gpu_fwd(sc, bins)
     assert np.all(T.cpu().numpy() == 1.0) and np.all(nc.cpu().numpy() == 0)
-    for walk in ("add", "store"):
+    for walk in ("add", "store", "defer"):
         out = gpu_bwd(sc, bins, T, nc, sc.dL_dimage, walk=walk)
         for v in out.values():
             assert torch.all(v == 0)
@@ -431,7 +431,7 @@ def test_out_of_range_ids_and_ranges():
     g[fo["ambiguous"]] = 0.0
     bo = oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
                               rng_o, ids_o, g)
-    for walk in ("add", "store"):
+    for walk in ("add", "store", "defer"):
         out = gpu_bwd(sc, gb, T, nc, g, walk=walk)
         check_fields({k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}, bo, label=walk)
     # ranges: one past the end of the pair list, one inverted, one starting below 0
@@ -453,7 +453,7 @@ def test_out_of_range_ids_and_ranges():
     assert np.abs(img2.cpu().numpy() - fo2["image"])[ok2].max() <= IMG_TOL
     assert np.abs(T2.cpu().numpy() - fo2["final_T"])[ok2].max() <= T_TOL
     np.testing.assert_array_equal(nc2.cpu().numpy()[ok2], fo2["n_contrib"][ok2])
-    for walk in ("add", "store"):
+    for walk in ("add", "store", "defer"):
         out = gpu_bwd(sc, gb2, T0, nc0, sc.dL_dimage, walk=walk)
         torch.cuda.synchronize()
         for k, v in out.items():
