@@ -19,7 +19,12 @@ formulas; see gs_oracle.c for the compositing reading):
 * :func:`rasterize_fwd` / :func:`rasterize_bwd` -- per-pixel front-to-back
   composite and the exact gradient of L = sum <dL/dImage, image> (C core,
   float64, OpenMP over tiles).
-* :func:`composite_bruteforce` -- the same composite with no tiles at all:
+* :func:`rasterize_fwd_depth` / :func:`rasterize_bwd_depth` -- the
+  distortion and median-depth terms (the optional features of
+  rasterize_bwd_2d on the Spirula Studio page, section 机制拆解, which gives
+  no formula; the reading is stated there) and their exact gradients.
+* :func:`composite_bruteforce` / :func:`depth_terms_bruteforce` -- the same
+  composite (and depth terms, as a full double sum) with no tiles at all:
   every pixel walks every splat in (depth, id) order. Used to pin the tiled
   oracle.
 
@@ -63,6 +68,10 @@ def _load():
         lib.gso_max_weight.restype = i32
         lib.gso_pixel_outcomes.argtypes = [i32, i32, P, P, P, P, P, P, P, i32, P, P, i32, P, P, P, P]
         lib.gso_pixel_outcomes.restype = i32
+        lib.gso_forward_depth.argtypes = [i32, i32, P, P, P, P, P, P, P, P, P, i32, P, P, P, P]
+        lib.gso_forward_depth.restype = i32
+        lib.gso_backward_depth.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, i32, P, P]
+        lib.gso_backward_depth.restype = i32
         lib.gso_threads.argtypes = []
         lib.gso_threads.restype = i32
         lib.gso_set_threads.argtypes = [i32]
@@ -254,6 +263,72 @@ def max_weight(means2d, conics, colors, opacities, background, width: int, heigh
     return mw, unc
 
 
+def _tiles_arg(tiles):
+    if tiles is None:
+        return None, 0, None
+    tarr = np.ascontiguousarray(tiles, dtype=np.int32)
+    return _ptr(tarr), len(tarr), tarr
+
+
+def rasterize_fwd_depth(means2d, conics, colors, opacities, background, width: int, height: int,
+                        tile_ranges, sorted_ids, depths, tiles=None):
+    """Depth terms of the forward: the distortion and median-depth options
+    that the Spirula Studio page lists for rasterize_bwd_2d (section 机制拆解:
+    a per-pixel float4 of distortion totals, and a median output) without a
+    formula. Read as
+
+      distortion  D = sum over composited pairs i < j of w_i w_j (z_i - z_j)^2
+                  (w = alpha T, z = the splat's depth)
+      median      the depth of the last composited splat whose transmittance
+                  before it is still > 1/2 (0 when nothing composites), and
+                  its list position + 1 (0: none)
+
+    Returns dict: totals [H,W,4] = (A, B, C, D) with A = sum w,
+    B = sum w (z - median), C = sum w (z - median)^2; distortion [H,W] (= D);
+    median_depth [H,W]; median_pos [H,W] int32; median_ambiguous [H,W] bool
+    (the T > 1/2 decision lies inside its float32 error band)."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    z = np.ascontiguousarray(depths, dtype=np.float64)
+    tot = np.zeros((height, width, 4), dtype=np.float64)
+    med = np.zeros((height, width), dtype=np.float64)
+    pos = np.zeros((height, width), dtype=np.int32)
+    amb = np.zeros((height, width), dtype=np.uint8)
+    tl, ntl, _keep = _tiles_arg(tiles)
+    lib.gso_forward_depth(width, height, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o), _ptr(bg),
+                          _ptr(z), tl, ntl, _ptr(tot), _ptr(med), _ptr(pos), _ptr(amb))
+    return {"totals": tot, "distortion": tot[..., 3].copy(), "median_depth": med, "median_pos": pos,
+            "median_ambiguous": amb.astype(bool)}
+
+
+def rasterize_bwd_depth(means2d, conics, colors, opacities, background, width: int, height: int,
+                        tile_ranges, sorted_ids, depths, dL_ddist=None, dL_dmedian=None, tiles=None):
+    """Exact gradients of L = sum_p dL_ddist_p D_p + dL_dmedian_p median_p
+    (terms of :func:`rasterize_fwd_depth`; either upstream may be None), every
+    discrete decision held fixed. Returns dict of float64 arrays: dmeans2d
+    [n,2], dconics [n,3], dcolors [n,3] (zeros), dopacities [n], ddepths [n]."""
+    lib = _load()
+    m, q, c, o = _arrs(means2d, conics, colors, opacities)
+    n = m.shape[0]
+    bg = np.ascontiguousarray(np.zeros(3) if background is None else background, dtype=np.float64)
+    rng_ = np.ascontiguousarray(tile_ranges, dtype=np.int32)
+    ids = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    z = np.ascontiguousarray(depths, dtype=np.float64)
+    gd = None if dL_ddist is None else np.ascontiguousarray(dL_ddist, dtype=np.float64)
+    gm = None if dL_dmedian is None else np.ascontiguousarray(dL_dmedian, dtype=np.float64)
+    grads = np.zeros((n, 9), dtype=np.float64)
+    dz = np.zeros(n, dtype=np.float64)
+    tl, ntl, _keep = _tiles_arg(tiles)
+    lib.gso_backward_depth(width, height, n, _ptr(rng_), _ptr(ids), _ptr(m), _ptr(q), _ptr(c), _ptr(o),
+                           _ptr(bg), _ptr(z), None if gd is None else _ptr(gd), None if gm is None else _ptr(gm),
+                           tl, ntl, _ptr(grads), _ptr(dz))
+    return {"dmeans2d": grads[:, 0:2].copy(), "dconics": grads[:, 2:5].copy(),
+            "dcolors": grads[:, 5:8].copy(), "dopacities": grads[:, 8].copy(), "ddepths": dz}
+
+
 def pixel_outcomes(means2d, conics, colors, opacities, background, width: int, height: int,
                    tile_ranges, sorted_ids, xs, ys, cap: int = 64):
     """Every admissible (image, final_T, n_contrib) of the pixels (xs, ys):
@@ -356,6 +431,57 @@ def composite_bruteforce(means2d, conics, colors, opacities, depths, radii, back
     if return_max_weight:
         res = res + (maxw,)
     return res
+
+
+def depth_terms_bruteforce(means2d, conics, opacities, depths, radii, width: int, height: int):
+    """Distortion and median with no tiles and no running sums: every pixel
+    walks every live splat in (float32 depth bits, id) order with the skip /
+    clamp / stop rules, recording each splat's weight w = alpha T and the
+    transmittance before it; then
+
+      D_p      = 1/2 sum_i sum_j w_i w_j (z_i - z_j)^2   (the full double sum)
+      median_p = z of the last splat with w > 0 and T before it > 1/2
+
+    Float64 numpy, vectorised over pixels; O(pixels x splats^2) memory-light
+    (one splat pair row at a time). Returns (D [H,W], median_depth [H,W],
+    weights [H*W, K], T_before [H*W, K], order [K])."""
+    m = np.asarray(means2d, dtype=np.float64)
+    q = np.asarray(conics, dtype=np.float64)
+    op = np.asarray(opacities, dtype=np.float64)
+    d32 = np.asarray(depths, dtype=np.float32)
+    z = np.asarray(depths, dtype=np.float64)
+    live = (np.asarray(radii) > 0) & (d32 > 0) & np.isfinite(m).all(axis=1)
+    ids = np.nonzero(live)[0]
+    order = ids[np.lexsort((ids, d32.view(np.uint32)[ids]))]
+    ys, xs = np.mgrid[0:height, 0:width]
+    px = xs.ravel() + 0.5
+    py = ys.ravel() + 0.5
+    P, K = px.size, len(order)
+    Wm = np.zeros((P, K))
+    Tb = np.zeros((P, K))
+    T = np.ones(P)
+    done = np.zeros(P, dtype=bool)
+    for k, i in enumerate(order):
+        dx = px - m[i, 0]
+        dy = py - m[i, 1]
+        alpha = np.minimum(ALPHA_MAX, op[i] * np.exp(-0.5 * (q[i, 0] * dx * dx + q[i, 2] * dy * dy) - q[i, 1] * dx * dy))
+        use = (~done) & (alpha >= ALPHA_MIN)
+        nxt = T * (1.0 - alpha)
+        stop = use & (nxt < T_MIN)
+        done |= stop
+        use &= ~stop
+        Wm[use, k] = alpha[use] * T[use]
+        Tb[:, k] = T
+        T = np.where(use, nxt, T)
+    zo = z[order]
+    D = np.zeros(P)
+    for a in range(K):
+        D += 0.5 * Wm[:, a] * (Wm * (zo[a] - zo[None, :]) ** 2).sum(axis=1)
+    med = np.zeros(P)
+    for k in range(K):
+        sel = (Wm[:, k] > 0) & (Tb[:, k] > 0.5)
+        med[sel] = zo[k]
+    return D.reshape(height, width), med.reshape(height, width), Wm, Tb, order
 
 
 # ----------------------------------------------------------------------------

@@ -43,6 +43,12 @@
  *   compositing weight a splat receives):
  *     max_weight_i = max_p alpha_i T_i over composited pairs (0 if none)
  *
+ *   Depth terms (gso_forward_depth / gso_backward_depth, below): the
+ *   distortion and median-depth options of rasterize_bwd_2d that the Spirula
+ *   Studio page names (section 机制拆解) without formulas; read as the squared
+ *   distortion over a pixel's composited pairs and the depth where its
+ *   transmittance falls to 1/2.
+ *
  *   Unlike the kernels this evaluates T forwards (products) and S as a suffix
  *   sum, in float64, with no division recurrence.
  *
@@ -82,6 +88,7 @@ typedef struct {
     int32_t k;       /* position in the tile list */
     double alpha, T, G, dx, dy;
     int clamped;
+    double errT;     /* float32 error bound of T (relative), before this entry */
 } contrib_t;
 
 /* Relative error bound of a float32 evaluation of alpha at this pair. */
@@ -163,6 +170,7 @@ static int walk_pixel(const splats_t* s, const int32_t* ids, int32_t start, int3
             contrib_t* e = &out[cnt];
             e->k = k; e->alpha = alpha; e->T = T; e->G = q.G; e->dx = q.dx; e->dy = q.dy;
             e->clamped = !(ah < ALPHA_MAX);
+            e->errT = errT;
         }
         ++cnt;
         T = test;
@@ -243,6 +251,21 @@ int gso_forward(int W, int H, const int32_t* ranges, const int32_t* ids,
  * dr, dg, db_colour, dopacity), accum_w [n]; both are ADDED to (caller zeroes).
  * dimg [H][W][3] is the upstream gradient g.
  */
+/* dL/dalpha of one walked entry carried on to the mean (o[0..1]), the conic
+ * (o[2..4]) and the opacity (o[8]); a clamped alpha passes nothing on. */
+static void add_alpha_grad(double* o, const contrib_t* q, const double* conic, double dal)
+{
+    if (q->clamped) return;
+    double a_ = conic[0], b_ = conic[1], c_ = conic[2];
+    double ds = q->alpha * dal;  /* dL/dsigma */
+    o[0] += (a_ * q->dx + b_ * q->dy) * ds;
+    o[1] += (b_ * q->dx + c_ * q->dy) * ds;
+    o[2] += -0.5 * q->dx * q->dx * ds;
+    o[3] += -q->dx * q->dy * ds;
+    o[4] += -0.5 * q->dy * q->dy * ds;
+    o[8] += q->G * dal;
+}
+
 int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
                  const double* means, const double* conics, const double* colors, const double* opac,
                  const double* bg, const double* dimg, const int32_t* tiles, int ntiles,
@@ -295,16 +318,7 @@ int gso_backward(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
                         o[5] += w * g[0];
                         o[6] += w * g[1];
                         o[7] += w * g[2];
-                        if (!q->clamped) {
-                            double a_ = s.conics[3 * i], b_ = s.conics[3 * i + 1], c_ = s.conics[3 * i + 2];
-                            double ds = al * dal;
-                            o[0] += (a_ * q->dx + b_ * q->dy) * ds;
-                            o[1] += (b_ * q->dx + c_ * q->dy) * ds;
-                            o[2] += -0.5 * q->dx * q->dx * ds;
-                            o[3] += -q->dx * q->dy * ds;
-                            o[4] += -0.5 * q->dy * q->dy * ds;
-                            o[8] += q->G * dal;
-                        }
+                        add_alpha_grad(o, q, s.conics + 3 * i, dal);
                         o[9] += w;
                         S[0] += col[0] * w;
                         S[1] += col[1] * w;
@@ -517,6 +531,193 @@ int gso_max_weight(int W, int H, int n, const int32_t* ranges, const int32_t* id
         free(part);
         free(pamb);
         free(pcert);
+    }
+    return threads_used();
+}
+
+/*
+ * Depth terms (the distortion and median-depth options that the Spirula Studio
+ * page names in section 机制拆解 -- a per-pixel float4 of "distortion totals"
+ * and a median-depth output -- without defining them). Read as:
+ *
+ *   distortion  D(p) = sum over composited pairs i < j of w_i w_j (z_i - z_j)^2,
+ *               w = alpha T, z = the splat's view depth (the squared form of the
+ *               mip-NeRF 360 distortion loss over the pixel's composited splats)
+ *   median      the depth z_m of the last composited splat m whose transmittance
+ *               before it is still > 1/2 (0 when the pixel composites nothing);
+ *               m + 1 is reported as the median's list position (0: none)
+ *
+ * Because D does not change when every depth is shifted, the totals the
+ * backward needs are taken about the median depth:
+ *   totals = (A, B, C, D),  A = sum w,  B = sum w (z - z_m),  C = sum w (z - z_m)^2
+ *
+ * median_amb marks a pixel whose median decision (T > 1/2) lies inside the
+ * float32 error band of T.
+ */
+/* The median entry of a walked pixel: the last composited entry whose
+ * transmittance before it is > 1/2 (-1 if none). *amb (if given) is set when
+ * some entry's T lies inside the float32 error band of 1/2. */
+static int median_entry(const contrib_t* buf, int cnt, int* amb)
+{
+    int m = -1;
+    for (int e = 0; e < cnt; ++e) {
+        const contrib_t* q = &buf[e];
+        if (amb && fabs(q->T - 0.5) <= K_T * (q->errT + 4.0 * U32) * 0.5 + 1e-6 * 0.5) *amb = 1;
+        if (q->T > 0.5) m = e;
+    }
+    return m;
+}
+
+/* Totals of a walked pixel about the reference depth zm: A = sum w,
+ * B = sum w u, C = sum w u^2 (u = z - zm), and the distortion in list order,
+ * D = sum_j w_j (sum_{i<j} w_i (z_i - z_j)^2), the inner sum expanded about zm. */
+static void depth_totals(const contrib_t* buf, int cnt, const int32_t* ids, const double* depths, double zm,
+                         double* A_, double* B_, double* C_, double* D_)
+{
+    double A = 0.0, B = 0.0, Cs = 0.0, D = 0.0;
+    for (int e = 0; e < cnt; ++e) {
+        const contrib_t* q = &buf[e];
+        double w = q->alpha * q->T, u = depths[ids[q->k]] - zm;
+        D += w * (u * u * A - 2.0 * u * B + Cs);
+        A += w;
+        B += w * u;
+        Cs += w * u * u;
+    }
+    *A_ = A;
+    *B_ = B;
+    *C_ = Cs;
+    *D_ = D;
+}
+
+int gso_forward_depth(int W, int H, const int32_t* ranges, const int32_t* ids,
+                      const double* means, const double* conics, const double* colors, const double* opac,
+                      const double* bg, const double* depths, const int32_t* tiles, int ntiles,
+                      double* totals, double* median, int32_t* median_pos, uint8_t* median_amb)
+{
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE, GY = (H + TILE - 1) / TILE;
+    int nt = tiles ? ntiles : GX * GY;
+#pragma omp parallel
+    {
+        int cap = 0;
+        contrib_t* buf = NULL;
+#pragma omp for schedule(dynamic, 1)
+        for (int ti = 0; ti < nt; ++ti) {
+            int t = tiles ? tiles[ti] : ti;
+            int tx = t % GX, ty = t / GX;
+            int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+            int L = end - start;
+            if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
+            for (int ly = 0; ly < TILE; ++ly) {
+                int y = ty * TILE + ly;
+                if (y >= H) break;
+                for (int lx = 0; lx < TILE; ++lx) {
+                    int x = tx * TILE + lx;
+                    if (x >= W) break;
+                    double T, C[3];
+                    int32_t nc;
+                    int a;
+                    int cnt = L > 0 ? walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, buf, cap, &T, &nc, C, &a, NULL)
+                                    : 0;
+                    size_t p = (size_t)y * W + x;
+                    int amb = 0;
+                    int m = median_entry(buf, cnt, &amb);
+                    double zm = m >= 0 ? depths[ids[buf[m].k]] : 0.0;
+                    double A, B, Cs, D;
+                    depth_totals(buf, cnt, ids, depths, zm, &A, &B, &Cs, &D);
+                    totals[4 * p + 0] = A;
+                    totals[4 * p + 1] = B;
+                    totals[4 * p + 2] = Cs;
+                    totals[4 * p + 3] = D;
+                    median[p] = zm;
+                    median_pos[p] = m >= 0 ? buf[m].k - start + 1 : 0;
+                    median_amb[p] = (uint8_t)amb;
+                }
+            }
+        }
+        free(buf);
+    }
+    return threads_used();
+}
+
+/*
+ * Gradients of L_depth = sum_p gD_p D_p + gM_p median_p (upstream g_dist [H][W],
+ * g_median [H][W]), every discrete decision held fixed, ADDED into grads [n][9]
+ * (the same fields as gso_backward) and ddepth [n]:
+ *   dD/dw_k     = sum_i w_i (z_i - z_k)^2 = u_k^2 A - 2 u_k B + C   (u = z - z_m)
+ *   dD/dalpha_k = T_k dD/dw_k - (sum_{j>k} w_j dD/dw_j) / (1 - alpha_k)
+ *   dD/dz_k     = 2 w_k (u_k A - B)
+ *   dmedian/dz_m = 1
+ * and dL/dalpha continues to opacity, conic and mean as in gso_backward (no
+ * alpha path for a clamped alpha).
+ */
+int gso_backward_depth(int W, int H, int n, const int32_t* ranges, const int32_t* ids,
+                       const double* means, const double* conics, const double* colors, const double* opac,
+                       const double* bg, const double* depths, const double* g_dist, const double* g_median,
+                       const int32_t* tiles, int ntiles, double* grads, double* ddepth)
+{
+    (void)n;
+    splats_t s = {means, conics, colors, opac, {bg[0], bg[1], bg[2]}};
+    int GX = (W + TILE - 1) / TILE, GY = (H + TILE - 1) / TILE;
+    int nt = tiles ? ntiles : GX * GY;
+#pragma omp parallel
+    {
+        int cap = 0;
+        contrib_t* buf = NULL;
+        double* part = NULL;  /* per tile-list entry: 9 grads + ddepth */
+        int part_cap = 0;
+#pragma omp for schedule(dynamic, 1)
+        for (int ti = 0; ti < nt; ++ti) {
+            int t = tiles ? tiles[ti] : ti;
+            int tx = t % GX, ty = t / GX;
+            int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+            int L = end - start;
+            if (L <= 0) continue;
+            if (L > cap) { free(buf); cap = L; buf = (contrib_t*)malloc(sizeof(contrib_t) * cap); }
+            if (L > part_cap) { free(part); part_cap = L; part = (double*)malloc(sizeof(double) * 10 * part_cap); }
+            memset(part, 0, sizeof(double) * 10 * L);
+            for (int ly = 0; ly < TILE; ++ly) {
+                int y = ty * TILE + ly;
+                if (y >= H) break;
+                for (int lx = 0; lx < TILE; ++lx) {
+                    int x = tx * TILE + lx;
+                    if (x >= W) break;
+                    double T, C[3];
+                    int32_t nc;
+                    int a;
+                    int cnt = walk_pixel(&s, ids, start, end, x + 0.5, y + 0.5, buf, cap, &T, &nc, C, &a, NULL);
+                    size_t p = (size_t)y * W + x;
+                    double gD = g_dist ? g_dist[p] : 0.0, gM = g_median ? g_median[p] : 0.0;
+                    int m = median_entry(buf, cnt, NULL);
+                    double zm = m >= 0 ? depths[ids[buf[m].k]] : 0.0;
+                    double A, B, Cs, D;
+                    depth_totals(buf, cnt, ids, depths, zm, &A, &B, &Cs, &D);
+                    double S = 0.0;  /* sum over the composited entries behind: w_j dD/dw_j */
+                    for (int e = cnt - 1; e >= 0; --e) {
+                        const contrib_t* q = &buf[e];
+                        int32_t i = ids[q->k];
+                        double al = q->alpha, Ti = q->T, w = al * Ti, u = depths[i] - zm;
+                        double dw = u * u * A - 2.0 * u * B + Cs;
+                        double dal = gD * (Ti * dw - S / (1.0 - al));
+                        double* o = part + 10 * (q->k - start);
+                        o[9] += gD * 2.0 * w * (u * A - B) + (e == m ? gM : 0.0);
+                        add_alpha_grad(o, q, s.conics + 3 * i, dal);
+                        S += w * dw;
+                    }
+                }
+            }
+#pragma omp critical(gso_merge_depth)
+            {
+                for (int k = 0; k < L; ++k) {
+                    const double* o = part + 10 * k;
+                    int32_t i = ids[start + k];
+                    for (int f = 0; f < 9; ++f) grads[9 * (size_t)i + f] += o[f];
+                    ddepth[i] += o[9];
+                }
+            }
+        }
+        free(buf);
+        free(part);
     }
     return threads_used();
 }

@@ -3,8 +3,9 @@
 Each case below plants one mistake in a copy of the oracle's C core (a sign,
 a factor, an index, a threshold or a dropped term that a careful reader could
 still miss), builds it with the same flags as the real one into a temporary
-directory and runs the pins (`test_oracle_pins.py`) against it in a fresh
-process: every mutant must fail at least one pin. An unmutated copy built the
+directory and runs the pins (`test_oracle_pins.py`, or `test_oracle_depth_pins.py`
+for the depth terms) against it in a fresh process: every mutant must fail at
+least one pin. An unmutated copy built the
 same way must pass them all. The binning, which the oracle writes in numpy,
 gets the same treatment: a mutated copy of the oracle package is imported in
 place of the real one. Everything runs on the CPU.
@@ -32,10 +33,10 @@ MUTANTS = [
     ("behind_not_divided", "S[ch] / (1.0 - al)", "S[ch]"),
     ("dmean_index", "(a_ * q->dx + b_ * q->dy) * ds", "(a_ * q->dx + b_ * q->dx) * ds"),
     ("dconic_b_halved", "o[3] += -q->dx * q->dy * ds;", "o[3] += -0.5 * q->dx * q->dy * ds;"),
-    ("dopacity_alpha_for_G", "o[8] += q->G * dal;", "o[8] += al * dal;"),
+    ("dopacity_alpha_for_G", "o[8] += q->G * dal;", "o[8] += q->alpha * dal;"),
     ("dcolour_channel", "o[6] += w * g[1];", "o[6] += w * g[0];"),
     ("behind_accumulates_alpha", "S[1] += col[1] * w;", "S[1] += col[1] * al;"),
-    ("clamped_alpha_keeps_sigma_path", "if (!q->clamped) {", "if (1) {"),
+    ("clamped_alpha_keeps_sigma_path", "if (q->clamped) return;", ""),
     ("n_contrib_off_by_one", "last = k - start + 1;", "last = k - start;"),
     ("image_without_background", "image[3 * p + 0] = C[0] + T * s.bg[0];", "image[3 * p + 0] = C[0];"),
     ("accum_weight_alpha", "o[9] += w;", "o[9] += al;"),
@@ -54,7 +55,29 @@ MUTANTS = [
 ]
 
 
-def _run(name, text, repl, tmp):
+# mistakes in the depth terms (distortion and median), against the depth pins
+DEPTH_MUTANTS = [
+    ("dist_pair_cross_sign", "D += w * (u * u * A - 2.0 * u * B + Cs);", "D += w * (u * u * A + 2.0 * u * B + Cs);"),
+    ("median_first_not_last", "if (q->T > 0.5) m = e;", "if (q->T > 0.5 && m < 0) m = e;"),
+    ("median_pos_off_by_one", "median_pos[p] = m >= 0 ? buf[m].k - start + 1 : 0;",
+     "median_pos[p] = m >= 0 ? buf[m].k - start : 0;"),
+    ("totals_B_unweighted", "B += w * u;", "B += u;"),
+    ("totals_about_zero", "double w = q->alpha * q->T, u = depths[ids[q->k]] - zm;",
+     "double w = q->alpha * q->T, u = depths[ids[q->k]];"),
+    ("median_band_dropped", "if (amb && fabs(q->T - 0.5) <= K_T * (q->errT + 4.0 * U32) * 0.5 + 1e-6 * 0.5) *amb = 1;",
+     ""),
+    ("bwd_dist_behind_not_divided", "double dal = gD * (Ti * dw - S / (1.0 - al));",
+     "double dal = gD * (Ti * dw - S);"),
+    ("bwd_dz_missing_two", "o[9] += gD * 2.0 * w * (u * A - B) + (e == m ? gM : 0.0);",
+     "o[9] += gD * w * (u * A - B) + (e == m ? gM : 0.0);"),
+    ("bwd_median_to_last_entry", "+ (e == m ? gM : 0.0);", "+ (e == cnt - 1 ? gM : 0.0);"),
+    ("bwd_dw_cross_sign", "double dw = u * u * A - 2.0 * u * B + Cs;", "double dw = u * u * A + 2.0 * u * B + Cs;"),
+    ("bwd_behind_sum_unweighted", "S += w * dw;", "S += dw;"),
+    ("bwd_median_depth_of_first", "int m = median_entry(buf, cnt, NULL);", "int m = cnt > 0 ? 0 : -1;"),
+]
+
+
+def _run(name, text, repl, tmp, pins="test_oracle_pins.py"):
     src = open(SRC).read()
     if text is not None:
         assert src.count(text) == 1, (name, src.count(text))
@@ -67,7 +90,7 @@ def _run(name, text, repl, tmp):
     subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
                     "-o", so, c, "-lm"], check=True, capture_output=True)
     env = dict(os.environ, GS_ORACLE_LIB=so, OMP_NUM_THREADS="2")
-    p = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-x", "-q",
+    p = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", pins), "-x", "-q",
                         "-p", "no:cacheprovider", "-m", "not gpu"], cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=600)
     return p.returncode, p.stdout[-400:]
@@ -117,18 +140,20 @@ def outcomes(tmp_path_factory):
     cases = [("unmutated", None, None)] + MUTANTS
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         futs = {name: ex.submit(_run, name, t, r, tmp) for name, t, r in cases}
+        futs.update({name: ex.submit(_run, name, t, r, tmp, "test_oracle_depth_pins.py")
+                     for name, t, r in [("depth_unmutated", None, None)] + DEPTH_MUTANTS})
         futs.update({name: ex.submit(_run_py, name, t, r, tmp, lib)
                      for name, t, r in [("py_unmutated", None, None)] + PY_MUTANTS})
         return {name: f.result() for name, f in futs.items()}
 
 
-@pytest.mark.parametrize("name", ["unmutated", "py_unmutated"])
+@pytest.mark.parametrize("name", ["unmutated", "py_unmutated", "depth_unmutated"])
 def test_unmutated_copy_passes(outcomes, name):
     rc, tail = outcomes[name]
     assert rc == 0, tail
 
 
-@pytest.mark.parametrize("name", [m[0] for m in MUTANTS + PY_MUTANTS])
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS + PY_MUTANTS + DEPTH_MUTANTS])
 def test_pins_catch_mutant(outcomes, name):
     rc, tail = outcomes[name]
     assert rc == 1, f"pins did not fail on mutant {name} (exit {rc}): {tail}"  # 1: tests ran and failed
