@@ -15,9 +15,10 @@ import torch
 from . import _lib
 from ._lib import GS_FLAG_ACCUM_WEIGHT, GsError
 
-__all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_rasterize_bwd_workspace_size",
-           "gs_rasterize_fwd_workspace_size", "gs_rasterize_bwd_noalloc", "gs_rasterize_bwd_noalloc_capacity",
-           "gs_version", "GsError", "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid", "Bins"]
+__all__ = ["gs_bin_tiles", "gs_rasterize_fwd", "gs_rasterize_fwd_depth", "gs_rasterize_bwd",
+           "gs_rasterize_bwd_depth", "gs_rasterize_bwd_workspace_size", "gs_rasterize_fwd_workspace_size",
+           "gs_rasterize_bwd_noalloc", "gs_rasterize_bwd_noalloc_capacity", "gs_version", "GsError",
+           "GS_FLAG_ACCUM_WEIGHT", "TILE", "tile_grid", "Bins"]
 
 TILE = 16
 
@@ -190,6 +191,57 @@ def gs_rasterize_fwd(means2d, conics, colors, opacities, background, width: int,
     return image, final_T, n_contrib
 
 
+def gs_rasterize_fwd_depth(means2d, conics, colors, opacities, depths, background, width: int, height: int,
+                           tile_ranges, sorted_ids, distortion: bool = True, median: bool = True,
+                           max_weight: bool = False, workspace=None, stream=None, n_isect: int | None = None):
+    """gs_rasterize_fwd with the depth outputs. Returns a dict: image, final_T,
+    n_contrib, [max_weight]; with ``distortion`` dist_totals [H,W,4] = (A, B,
+    C, D): A = sum alpha T, B and C the first two moments of depth about the
+    median, D = sum over composited pairs i < j of w_i w_j (z_i - z_j)^2; with
+    ``median`` median_depth [H,W] (depth of the last composited splat whose
+    transmittance before it is > 1/2, 0 if none); median_pos [H,W] int32
+    (that splat's list position + 1, 0 if none) with either, since the
+    backward's depth terms need it."""
+    n = int(means2d.shape[0])
+    _need(means2d, "means2d", torch.float32, (n, 2))
+    _need(conics, "conics", torch.float32, (n, 3))
+    _need(colors, "colors", torch.float32, (n, 3))
+    _need(opacities, "opacities", torch.float32, (n,))
+    _need(depths, "depths", torch.float32, (n,))
+    if background is not None:
+        _need(background, "background", torch.float32, (3,))
+    GX, GY = tile_grid(width, height)
+    _need(tile_ranges, "tile_ranges", torch.int32, (GX * GY, 2))
+    _need(sorted_ids, "sorted_ids", torch.int32)
+    n_pairs = _pair_count(sorted_ids, n_isect)
+    dev = means2d.device
+    _same_device(dev, conics=conics, colors=colors, opacities=opacities, depths=depths, background=background,
+                 tile_ranges=tile_ranges, sorted_ids=sorted_ids, workspace=workspace)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"image": torch.empty((height, width, 3), **f32), "final_T": torch.empty((height, width), **f32),
+           "n_contrib": torch.empty((height, width), dtype=torch.int32, device=dev)}
+    if max_weight:
+        out["max_weight"] = torch.empty((n,), **f32)
+    if distortion:
+        out["dist_totals"] = torch.empty((height, width, 4), **f32)
+    if median:
+        out["median_depth"] = torch.empty((height, width), **f32)
+    if distortion or median:
+        out["median_pos"] = torch.empty((height, width), dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    ws_bytes = int(lib.gs_rasterize_fwd_workspace_size(n))
+    workspace, wsp = _workspace(workspace, ws_bytes, dev)
+    st = _stream(stream, dev)
+    g = out.get
+    with torch.cuda.device(dev):
+        _lib.check(lib.gs_rasterize_fwd_depth(
+            n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(depths), _ptr(background), width,
+            height, _ptr(tile_ranges), _ptr(sorted_ids), n_pairs, _ptr(out["image"]), _ptr(out["final_T"]),
+            _ptr(out["n_contrib"]), _ptr(g("max_weight")), _ptr(g("dist_totals")), _ptr(g("median_depth")),
+            _ptr(g("median_pos")), wsp, ws_bytes, st))
+    return out
+
+
 def _check_bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
                     n_contrib, dL_dimage, workspace):
     n = int(means2d.shape[0])
@@ -283,6 +335,53 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
         else:
             handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
             _lib.check(lib.gs_rasterize_bwd_timed(*args, handles))
+    return out
+
+
+def gs_rasterize_bwd_depth(means2d, conics, colors, opacities, depths, radii, background, width: int,
+                           height: int, bins: Bins, final_T, n_contrib, median_pos, dL_dimage, dist_totals=None,
+                           dL_ddist=None, dL_dmedian=None, accum_weight: bool = False, out=None, workspace=None,
+                           stream=None, walk=None):
+    """gs_rasterize_bwd with the depth terms: also the gradients of
+    sum dL_ddist * D + dL_dmedian * median_depth (either upstream may be
+    None; dist_totals and median_pos as gs_rasterize_fwd_depth returned
+    them). Returns gs_rasterize_bwd's dict plus dL_ddepths [n]."""
+    n = int(means2d.shape[0])
+    dev = means2d.device
+    _check_bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                    n_contrib, dL_dimage, workspace)
+    _need(depths, "depths", torch.float32, (n,))
+    _need(median_pos, "median_pos", torch.int32, (height, width))
+    if dL_ddist is not None:
+        _need(dL_ddist, "dL_ddist", torch.float32, (height, width))
+        if dist_totals is None:
+            raise ValueError("dL_ddist needs dist_totals (from gs_rasterize_fwd_depth)")
+    if dist_totals is not None:
+        _need(dist_totals, "dist_totals", torch.float32, (height, width, 4))
+    if dL_dmedian is not None:
+        _need(dL_dmedian, "dL_dmedian", torch.float32, (height, width))
+    _same_device(dev, depths=depths, median_pos=median_pos, dist_totals=dist_totals, dL_ddist=dL_ddist,
+                 dL_dmedian=dL_dmedian)
+    lib = _lib.load()
+    shapes = dict(_output_shapes(n, accum_weight), dL_ddepths=(n,))
+    if out is None:
+        out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+    else:
+        for k, v in shapes.items():
+            if k not in out:
+                raise ValueError(f"out lacks {k!r}")
+            _need(out[k], k, torch.float32, v)
+            _same_device(dev, **{k: out[k]})
+    a = _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
+                  n_contrib, dL_dimage, out, accum_weight, walk)
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
+    workspace, wsp = _workspace(workspace, ws_bytes, dev)
+    # gs_rasterize_bwd's arguments with the depth inputs and output spliced in
+    args = (a[:5] + (_ptr(depths),) + a[5:15] + (_ptr(dist_totals), _ptr(median_pos), a[15], _ptr(dL_ddist),
+                                                 _ptr(dL_dmedian)) + a[16:20] + (_ptr(out["dL_ddepths"]),) + a[20:]
+            + (wsp, ws_bytes, _stream(stream, dev)))
+    with torch.cuda.device(dev):
+        _lib.check(lib.gs_rasterize_bwd_depth(*args))
     return out
 
 

@@ -27,9 +27,9 @@ STATUS_NAMES = {0: "GS_OK", 1: "GS_ERR_INVALID_ARG", 2: "GS_ERR_CAPACITY", 3: "G
 
 # Every symbol include/gsraster.h declares.
 EXPORTS = ["gs_last_error", "gs_version", "gs_bin_tiles_workspace_size", "gs_bin_tiles",
-           "gs_rasterize_fwd_workspace_size", "gs_rasterize_fwd", "gs_rasterize_bwd_workspace_size",
-           "gs_rasterize_bwd", "gs_rasterize_bwd_timed", "gs_rasterize_bwd_noalloc_capacity",
-           "gs_rasterize_bwd_noalloc"]
+           "gs_rasterize_fwd_workspace_size", "gs_rasterize_fwd", "gs_rasterize_fwd_depth",
+           "gs_rasterize_bwd_workspace_size", "gs_rasterize_bwd", "gs_rasterize_bwd_depth",
+           "gs_rasterize_bwd_timed", "gs_rasterize_bwd_noalloc_capacity", "gs_rasterize_bwd_noalloc"]
 
 _lib = None
 
@@ -60,11 +60,17 @@ def load() -> ctypes.CDLL:
     lib.gs_rasterize_fwd_workspace_size.restype = sz
     lib.gs_rasterize_fwd.argtypes = [i32, P, P, P, P, P, i32, i32, P, P, i64, P, P, P, P, P, sz, P]
     lib.gs_rasterize_fwd.restype = ctypes.c_int
+    lib.gs_rasterize_fwd_depth.argtypes = [i32, P, P, P, P, P, P, i32, i32, P, P, i64, P, P, P, P, P, P, P,
+                                           P, sz, P]
+    lib.gs_rasterize_fwd_depth.restype = ctypes.c_int
     lib.gs_rasterize_bwd_workspace_size.argtypes = [i32, i64, i32, i32]
     lib.gs_rasterize_bwd_workspace_size.restype = sz
     lib.gs_rasterize_bwd.argtypes = [i32, P, P, P, P, P, P, i32, i32, P, P, P, i64, P, P, P,
                                      P, P, P, P, P, u32, P, sz, P]
     lib.gs_rasterize_bwd.restype = ctypes.c_int
+    lib.gs_rasterize_bwd_depth.argtypes = [i32, P, P, P, P, P, P, P, i32, i32, P, P, P, i64, P, P, P, P,
+                                           P, P, P, P, P, P, P, P, P, u32, P, sz, P]
+    lib.gs_rasterize_bwd_depth.restype = ctypes.c_int
     lib.gs_rasterize_bwd_timed.argtypes = lib.gs_rasterize_bwd.argtypes + [ctypes.POINTER(P)]
     lib.gs_rasterize_bwd_timed.restype = ctypes.c_int
     lib.gs_rasterize_bwd_noalloc_capacity.argtypes = []

@@ -72,14 +72,17 @@ __device__ __forceinline__ SplatRec make_rec(int i, const float2* __restrict__ m
     return r;
 }
 
+// depths may be NULL; when given (the forward's depth outputs) the depth takes
+// the record's last word, which only the backward uses otherwise.
 __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
                                                    const float* __restrict__ conics, const float* __restrict__ colors,
                                                    const float* __restrict__ opac, const int* __restrict__ radii,
-                                                   SplatRec* __restrict__ recs)
+                                                   const float* __restrict__ depths, SplatRec* __restrict__ recs)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const SplatRec r = make_rec(i, means, conics, colors, opac, radii);
+    SplatRec r = make_rec(i, means, conics, colors, opac, radii);
+    if (depths) r.c.w = depths[i];
     recs[i] = r;
 }
 
@@ -198,7 +201,18 @@ struct StoreSlot {
     float4 b;                      // l22, log2(opacity), red, green
     float c;                       // blue
     unsigned char pos[kHalves];    // list position in each half, 0xff: not in that list
-    int slot;                      // the entry's (splat, tile) pair slot, -1: nothing to flush
+    int slot;                      // the entry's (splat, tile) pair slot, -1: nothing to flush; in the
+                                   // deferred walk with depth terms, the splat's depth (float bits), the
+                                   // pair slot then staying in the staging thread's register
+};
+
+// Per-pixel inputs of the backward's depth terms (distortion, median depth).
+struct DepthIn {
+    const float* depths;      // [n]
+    const float4* totals;     // [H][W]: A, B, C about the median depth, D (distortion)
+    const int* median_pos;    // [H][W]: median list position + 1, 0: none
+    const float* g_dist;      // [H][W]: dL/dD
+    const float* g_med;       // [H][W]: dL/dmedian
 };
 static_assert(sizeof(StoreSlot) == 48 && offsetof(StoreSlot, pos) == 36, "StoreSlot layout");
 
@@ -224,13 +238,16 @@ template <bool AW> struct BwdParts {
 // steps between two deferred reductions; WG: workgroups per CU the LDS is
 // sized for. The partial records take what the slots, lists and per-wave
 // pads leave of 160 KB / WG.
-template <bool AW, int NB, int KC, int WG> struct DeferShape {
-    static constexpr int kF = AW ? kRaw : kRaw - 1;
+// DEP: the depth terms (bit 0 distortion, bit 1 median), one more record
+// field (the depth gradient) and a per-wave pad of one float per lane and step.
+template <bool AW, int NB, int KC, int WG, int DEP = 0> struct DeferShape {
+    static constexpr int kF = (AW ? kRaw : kRaw - 1) + (DEP ? 1 : 0);
+    static constexpr int kZ = AW ? kRaw : kRaw - 1;  // the depth gradient's field (DEP)
     static constexpr int kSlots = NB + 1;
     static constexpr int kListLen = NB + 5;  // up to NB entries, then dummies read ahead of use
     static constexpr unsigned short kDummyOff = (unsigned short)(NB * sizeof(StoreSlot));
     static constexpr int kFixed = kSlots * (int)sizeof(StoreSlot) + kHalves * kListLen * 2 + 4 * KC * 64 * 8 +
-                                  4 * (kHalves + 1) * 4 + 2 * kHalves * 4 + 4 * 4 + 4;
+                                  (DEP ? 4 * KC * 64 * 4 : 4) + 4 * (kHalves + 1) * 4 + 2 * kHalves * 4 + 4 * 4 + 4;
     static constexpr int kCap = ((160 * 1024) / WG - kFixed - 256) / (kF * 4);
     static_assert(kCap >= 2 * kHalves * KC, "the partial records must hold at least one chunk");
 };
@@ -640,16 +657,17 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 // The pads (KC x 64 float2 per wave) are written and read by the same wave,
 // whose LDS accesses are served in order: no barrier is needed around them.
 // ---------------------------------------------------------------------------
-template <bool AW, int NB, int KC, int WG>
+template <bool AW, int NB, int KC, int WG, int DEP>
 __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
     const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
-    unsigned char* __restrict__ slot_used)
+    unsigned char* __restrict__ slot_used, DepthIn dz)
 {
-    using PP = DeferShape<AW, NB, KC, WG>;
+    using PP = DeferShape<AW, NB, KC, WG, DEP>;
     constexpr int kF = PP::kF, kCap = PP::kCap, kDSlots = PP::kSlots, kDListLen = PP::kListLen;
+    constexpr int kZ = PP::kZ;
     constexpr unsigned short kDDummyOff = PP::kDummyOff;
     constexpr int kLPR = 32 / KC;   // phase 2: lanes per (half, position) record
     constexpr int kPPL = KC;        // phase 2: pixels per lane (a row or part of one)
@@ -663,6 +681,8 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     __shared__ int cut;                                // lowest kept candidate of the batch
     // per wave: each lane's (w, s) at each step of the current chunk
     __shared__ __align__(16) float2 pad[4][KC][kWave];
+    // DEP: each lane's depth gradient at each step of the chunk
+    __shared__ __align__(16) float padz[DEP ? 4 : 1][DEP ? KC : 1][DEP ? kWave : 1];
 
     const int tile = order ? order[blockIdx.x] : xcd_tile(blockIdx.x, tiles);
     if (tile < 0 || tile >= tiles) return;
@@ -677,6 +697,12 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
+    // DEP: the median depth zm and list position mp; the distortion totals
+    // about zm (A, -2B, C) and its upstream gD, with 2 gD A and -2 gD B; the
+    // median's upstream gM; E, the distortion behind the current entry
+    // (normalised by the transmittance after it, like the colour behind)
+    float zm = 0.0f, dA = 0.0f, nB2 = 0.0f, dC = 0.0f, gD = 0.0f, A2g = 0.0f, mB2g = 0.0f, gM = 0.0f, E = 0.0f;
+    int mp = 0;
     if (inside) {
         const int p = y * W + x;
         T = final_T[p];
@@ -685,6 +711,23 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         g0 = dimg[3 * p + 0];
         g1 = dimg[3 * p + 1];
         g2 = dimg[3 * p + 2];
+        if (DEP) {
+            mp = min(max(dz.median_pos[p], 0), nc);  // the median is a composited entry
+            if (mp > 0) {
+                const int mid = ids[rg.x + mp - 1];
+                zm = (unsigned)mid < (unsigned)n ? dz.depths[mid] : 0.0f;
+            }
+            if (DEP & 1) {
+                const float4 t = dz.totals[p];
+                gD = dz.g_dist[p];
+                dA = t.x;
+                nB2 = -2.0f * t.y;
+                dC = t.z;
+                A2g = 2.0f * gD * t.x;
+                mB2g = -2.0f * gD * t.y;
+            }
+            if (DEP & 2) gM = dz.g_med[p];
+        }
     }
     // Colour "behind" the current splat (normalised by the transmittance after
     // it; the background at the start), carried only as its dot product with
@@ -745,6 +788,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     // records are cleared only after the next barrier.
     int hi = tmax;  // the batches cover [0, tmax) from the top down
     while (hi > 0) {
+        int my_slot = -1;  // this thread's staged entry's pair slot
         const int lo = max(0, hi - NB);  // candidates [lo, hi): entry lo + t in slot t
         const int k = lo + (int)threadIdx.x;
         const bool cand = (int)threadIdx.x < NB && k < hi;
@@ -754,8 +798,10 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         r.c = make_float4(0.0f, -1.0f, 0.0f, 0.0f);  // no entry: reaches nothing
         if (cand) id = ids[rg.x + k];
         if ((unsigned)id >= (unsigned)n) id = -1;  // an id outside [0, n) is no entry
+        float zent = 0.0f;  // DEP: the entry's depth (0 for no entry and the dummy)
         if (id >= 0) {
             r = recs[id];
+            if (DEP) zent = dz.depths[id];
             radius = __float_as_int(r.c.z);
             S[threadIdx.x].a = r.a;
             S[threadIdx.x].b = r.b;
@@ -799,7 +845,10 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                     (long long)__float_as_int(r.c.w) + (long long)(ty - ty0) * (tx1 - tx0) + (tx - tx0);
                 if (tx >= tx0 && tx < tx1 && ty >= ty0 && ty < ty1 && sl >= 0 && sl < n_slots) slot = (int)sl;
             }
-            if (threadIdx.x < kDSlots) S[threadIdx.x].slot = slot;  // thread t's own slot; the walk does not read it
+            // thread t's own slot; the walk does not read it (with depth terms
+            // the slot word carries the depth, which the walk reads)
+            if (threadIdx.x < kDSlots) S[threadIdx.x].slot = DEP ? __float_as_int(zent) : slot;
+            my_slot = slot;
         }
         // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
         // exponent never exceeds log2 o, so alpha_raw never exceeds
@@ -814,6 +863,10 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
 #pragma unroll
         for (int q = 1; q < kHalves; ++q) base[q] = base[q - 1] + len[q - 1];
         const int next_hi = lo + cut;
+        // DEP: the slot offset of this pixel's median entry when this batch
+        // walks it (the kept candidates [next_hi, hi)), else -1
+        const int med_off = (DEP & 2) && mp - 1 >= next_hi && mp - 1 < hi
+                                ? (mp - 1 - lo) * (int)sizeof(StoreSlot) : -1;
         // the wave's two list lengths and first records (wave-uniform selects
         // over the unrolled halves: no indexing of the register arrays by the
         // wave number), then this lane's half
@@ -846,8 +899,10 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         const int ph_len = ph ? len_b : len_a, ph_base = ph ? base_b : base_a;
         const unsigned short* Lp = list[2 * wvu + ph];
         float2* const my_pad = &pad[wv][0][lane];
+        float* const my_padz = &padz[DEP ? wv : 0][0][DEP ? lane : 0];
 
         auto rec_at = [&](int o) -> const StoreSlot& { return *reinterpret_cast<const StoreSlot*>(Sb + o); };
+        auto z_at = [&](int o) -> float { return DEP ? __int_as_float(rec_at(o).slot) : 0.0f; };
         auto list_at = [&](int i) -> int {
             int o = L[i];
             asm("" : "+v"(o));
@@ -856,7 +911,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         // Phase 1, one lockstep step: alpha, the contributing lanes, T and the
         // colour behind recovered; the lane's w = alpha T and s = dL/dsigma go
         // to the pad (zeros where it does not contribute).
-        auto step = [&](const float4& A, const float4& Bq, float Cb, int cur, int j, auto clamp_tag) {
+        auto step = [&](const float4& A, const float4& Bq, float Cb, float Zc, int cur, int j, auto clamp_tag) {
             constexpr bool kClamp = decltype(clamp_tag)::value;
             const AlphaCoef kf{A.x, A.y, A.z, A.w, Bq.x, Bq.y};
             float dx, dy;
@@ -875,7 +930,21 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             Bg = __builtin_fmaf(ae, eg, Bg);
             T = Ti;
             const float w = ae * Ti;
-            const float s = (!kClamp || ar < kAlphaMax) ? w * eg : 0.0f;  // clamped alpha: no sigma path
+            float egt = eg;  // dL/dalpha / T
+            if (DEP) {
+                const float u = Zc - zm;
+                float vz = 0.0f;
+                if (DEP & 1) {
+                    // dD/dw = u^2 A - 2 u B + C, less the distortion behind
+                    const float ed = __builtin_fmaf(u, __builtin_fmaf(u, dA, nB2), dC) - E;
+                    E = __builtin_fmaf(ae, ed, E);
+                    egt = __builtin_fmaf(gD, ed, eg);
+                    vz = w * __builtin_fmaf(u, A2g, mB2g);  // gD dD/dz = 2 gD w (u A - B)
+                }
+                if (DEP & 2) vz += cur == med_off ? gM : 0.0f;
+                my_padz[j * kWave] = vz;
+            }
+            const float s = (!kClamp || ar < kAlphaMax) ? w * egt : 0.0f;  // clamped alpha: no sigma path
             my_pad[j * kWave] = make_float2(w, s);
         };
         // Phase 2, after each chunk of steps: lane (j, h, u) sums row u of
@@ -914,8 +983,18 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                 Wb = __builtin_fmaf(w_[kx], gb[kx], Wb);
                 if (AW) Wt += w_[kx];
             }
+            float Vz = 0.0f;  // DEP: the depth gradients of the lane's pixels
+            if (DEP) {
+                static_assert(DEP == 0 || kPPL % 4 == 0, "depth pad read as float4");
+                const float4* pz = reinterpret_cast<const float4*>(&padz[wv][jr][32 * ph + 8 * pu + pkx0]);
+#pragma unroll
+                for (int i = 0; i < kPPL / 4; ++i) {
+                    const float4 q = pz[i];
+                    Vz += (q.x + q.y) + (q.z + q.w);
+                }
+            }
             const float dx0 = row_x0 - mu.x, dyr = row_y - mu.y;
-            float f[kRaw];
+            float f[kRaw + 1];
             f[0] = Wr;
             f[1] = Wg;
             f[2] = Wb;
@@ -925,7 +1004,8 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             f[6] = __builtin_fmaf(dx0, __builtin_fmaf(dx0, S0, Sx + Sx), Sxx);   // sum s dx^2
             f[7] = dyr * f[4];                                                    // sum s dx dy
             f[8] = dyr * f[5];                                                    // sum s dy^2
-            f[9] = AW ? Wt : 0.0f;
+            f[9] = AW ? Wt : Vz;
+            f[10] = Vz;  // field kZ: 9 or 10
             // the record's kLPR lanes add their totals: inside each quad, then
             // (eight lanes) between the two quads of each 8-lane half-row
 #pragma unroll
@@ -944,6 +1024,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             int o_cur = list_at(0), o_nxt = list_at(1);
             float4 A = rec_at(o_cur).a, B = rec_at(o_cur).b;
             float C = rec_at(o_cur).c;
+            float Z = z_at(o_cur);
             for (int c = 0; c < steps; c += KC) {
 #pragma unroll
                 for (int j = 0; j < KC; ++j) {
@@ -952,11 +1033,13 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                     // the next entry's record one step ahead, its list entry two
                     const float4 An = rec_at(o_nxt).a, Bn = rec_at(o_nxt).b;
                     const float Cn = rec_at(o_nxt).c;
+                    const float Zn = z_at(o_nxt);
                     const int o_nn = list_at(it + 2);
-                    step(A, B, C, o_cur, j, clamp_tag);
+                    step(A, B, C, Z, o_cur, j, clamp_tag);
                     A = An;
                     B = Bn;
                     C = Cn;
+                    Z = Zn;
                     o_cur = o_nxt;
                     o_nxt = o_nn;
                 }
@@ -976,10 +1059,10 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
 
         // Flush: thread t owns the entry it staged; its sums are those of the
         // records of the halves that listed it.
-        const int slot = threadIdx.x < kDSlots ? S[threadIdx.x].slot : -1;
+        const int slot = threadIdx.x < kDSlots ? (DEP ? my_slot : S[threadIdx.x].slot) : -1;
         if (slot >= 0) {
             const uint2 pw = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
-            float u[kRaw] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+            float u[kRaw + 1] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int q = 0; q < kHalves; ++q) {
                 const unsigned at = ((q < 4 ? pw.x : pw.y) >> (8 * (q & 3))) & 0xffu;
@@ -989,14 +1072,17 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                     for (int f = 0; f < kF; ++f) u[f] += pr[f];
                 }
             }
-            const bool any = (u[0] != 0.0f) | (u[1] != 0.0f) | (u[2] != 0.0f) | (u[3] != 0.0f) |
-                             (u[4] != 0.0f) | (u[5] != 0.0f) | (u[6] != 0.0f) | (u[7] != 0.0f) |
-                             (u[8] != 0.0f) | (AW && u[9] != 0.0f);
+            bool any = false;
+#pragma unroll
+            for (int f = 0; f < kF; ++f) any |= u[f] != 0.0f;
             if (any) {
                 rec_out[3 * (long long)slot + 0] = make_float4(u[0], u[1], u[2], u[3]);
                 rec_out[3 * (long long)slot + 1] = make_float4(u[4], u[5], u[6], u[7]);
-                // the third part's last 8 bytes are padding, never read
-                *reinterpret_cast<float2*>(rec_out + 3 * (long long)slot + 2) = make_float2(u[8], AW ? u[9] : 0.0f);
+                const float uw = AW ? u[9] : 0.0f;
+                if (DEP)  // the depth gradient in the third part's third word
+                    rec_out[3 * (long long)slot + 2] = make_float4(u[8], uw, u[kZ], 0.0f);
+                else      // the third part's last 8 bytes are padding, never read
+                    *reinterpret_cast<float2*>(rec_out + 3 * (long long)slot + 2) = make_float2(u[8], uw);
                 slot_used[slot] = 1;
             }
         }
@@ -1357,24 +1443,38 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* __restrict__ p,
 // integer atomic max. Weights are >= 0, so the order of their float32 bit
 // patterns is the order of their values, and a max is the same in any order:
 // the result does not depend on scheduling.
+//
+// Optional depth outputs (DEP: 0 none, 1 the median, 2 the median and the
+// distortion totals). The median entry of a pixel is the last composited
+// entry whose transmittance before it is > 1/2; since T only falls, a lane
+// keeps the latest such entry and its depth. The totals A = sum w, B = sum w u,
+// C = sum w u^2 (u = z - reference) are summed about the depth of the current
+// median candidate: each new candidate moves them to its own depth (B' = B -
+// d A, C' = C - d (B + B'), d = new - old reference), which happens only while
+// T > 1/2, i.e. over a pixel's first few composited entries, while the sums
+// are still small; every later entry is summed about the final median, so
+// the rounding error stays relative to the moments about the median rather
+// than about a distant depth. The distortion is D = A C - B^2: half the double
+// sum of w_i w_j (z_i - z_j)^2 over all pairs, i.e. the sum over pairs i < j.
 // ---------------------------------------------------------------------------
 struct FwdSlot {
     float4 a;       // mean x, mean y, l11, l21 (scaled factor)
     float4 b;       // l22, log2(opacity), red, green
     float c;        // blue
+    float z;        // depth (depth outputs only)
     unsigned char pos[kHalves];  // list position in each half, 0xff: not listed (MW only)
-    float pad;
 };
-static_assert(sizeof(FwdSlot) == 48, "FwdSlot layout");
+static_assert(sizeof(FwdSlot) == 48 && offsetof(FwdSlot, pos) == 40, "FwdSlot layout");
 
-template <bool MW>
+template <bool MW, int DEP>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX, int tiles,
                                                      const int2* __restrict__ ranges, long long n_pairs,
                                                      const int* __restrict__ ids,
                                                      const SplatRec* __restrict__ recs,
                                                      const float* __restrict__ bg, float* __restrict__ image,
                                                      float* __restrict__ final_T, int* __restrict__ n_contrib,
-                                                     unsigned* __restrict__ max_weight)
+                                                     unsigned* __restrict__ max_weight, float4* __restrict__ dist_totals,
+                                                     float* __restrict__ median_depth, int* __restrict__ median_pos)
 {
     __shared__ FwdSlot S[kBlock];
     __shared__ unsigned short list[kHalves][kListLen];  // per half: slots that may touch it, then dummies
@@ -1396,6 +1496,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         S[kDummy].a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         S[kDummy].b = make_float4(0.0f, -__builtin_inff(), 0.0f, 0.0f);
         S[kDummy].c = 0.0f;
+        S[kDummy].z = 0.0f;  // every lane reads it (weight 0 times a finite depth)
     }
     constexpr unsigned short kDummyFwd = (unsigned short)(kDummy * sizeof(FwdSlot));
     const char* Sb = reinterpret_cast<const char*>(S);
@@ -1403,6 +1504,9 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f;
     int last_n = 0;  // list position of the last composited entry, plus one
+    // DEP: the median entry's list position plus one, and depth; the totals
+    float zmed = 0.0f, zmed_ref = 0.0f, Aw = 0.0f, Bw = 0.0f, Cw = 0.0f;
+    int med_n = 0;
     // the wave's stopped pixels (and those outside the image), as a lane mask:
     // the walk's tests then build their masks with compare instructions alone
     unsigned long long done_m = __ballot(!inside);
@@ -1427,6 +1531,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             S[threadIdx.x].a = r.a;
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
+            if (DEP) S[threadIdx.x].z = r.c.w;
         }
         if (MW) {  // this batch's records start cleared
             uint4* z = reinterpret_cast<uint4*>(&mw_rec[0][0]) + 2 * threadIdx.x;
@@ -1472,11 +1577,12 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         const unsigned short* L = list[hq];
 
         int bl_cur = -1;  // slot offset of this batch's last composited entry (-1: none)
+        int med_cur = -1; // DEP: slot offset of this batch's last median candidate (-1: none)
         // One entry against the lane's pixel. Lanes whose alpha reaches 1/255
         // are walked; of those, the ones whose T stays >= 1e-4 composite and
         // the others stop here.
         unsigned long long any_c = 0;  // MW: lanes that composited in the current pair of steps
-        auto step = [&](const float4& A, const float4& B, float Cb, int cur) -> float {
+        auto step = [&](const float4& A, const float4& B, float2 Cz, int cur) -> float {
             const AlphaCoef k{A.x, A.y, A.z, A.w, B.x, B.y};
             float dx, dy;
             const float al = fminf(kAlphaMax, alpha_raw(k, px, py, dx, dy));
@@ -1489,7 +1595,27 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             const float wgt = comp ? al * T : 0.0f;  // other lanes add exact zeros
             C0 = __builtin_fmaf(B.z, wgt, C0);
             C1 = __builtin_fmaf(B.w, wgt, C1);
-            C2 = __builtin_fmaf(Cb, wgt, C2);
+            C2 = __builtin_fmaf(Cz.x, wgt, C2);
+            if (DEP) {  // a median candidate: composited with T before it > 1/2
+                const bool mh = comp && T > 0.5f;
+                med_cur = mh ? cur : med_cur;
+                zmed = mh ? Cz.y : zmed;
+                // DEP 2: a new candidate moves the sums' reference to its depth
+                // (only while T > 1/2: a few steps per pixel)
+                if (DEP == 2 && __builtin_amdgcn_ballot_w64(mh) != 0) {
+                    const float d = mh ? Cz.y - zmed_ref : 0.0f;
+                    const float Bn = __builtin_fmaf(-d, Aw, Bw);
+                    Cw = __builtin_fmaf(-d, Bw + Bn, Cw);
+                    Bw = Bn;
+                    zmed_ref = mh ? Cz.y : zmed_ref;
+                }
+            }
+            if (DEP == 2) {  // the totals about the current median candidate's depth
+                const float u = Cz.y - zmed_ref, wu = wgt * u;
+                Aw += wgt;
+                Bw += wu;
+                Cw = __builtin_fmaf(wu, u, Cw);
+            }
             T = comp ? test : T;
             bl_cur = comp ? cur : bl_cur;
             if (MW) any_c |= c_m;
@@ -1507,14 +1633,16 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         };
         // Two entries per iteration with two record buffers, each refilled
         // one entry ahead of its use (the lists hold dummies past their end).
+        // blue, and the depth where it is used
+        auto cz_at = [&](int o) -> float2 { return make_float2(rec_at(o).c, DEP ? rec_at(o).z : 0.0f); };
         int o0 = L[0], o1 = L[1];
         float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
-        float K0 = rec_at(o0).c;
+        float2 K0 = cz_at(o0);
         float w_tail = 0.0f;  // MW: the weights of an odd count's last step, stored after the loop
         for (int it = 0; it < steps; it += 2) {
             if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
             const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
-            const float K1 = rec_at(o1).c;
+            const float2 K1 = cz_at(o1);
             const int n0 = L[it + 2];
             const float w0 = step(A0, B0, K0, o0);
             if (it + 1 >= steps) {
@@ -1523,7 +1651,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             }
             A0 = rec_at(n0).a;
             B0 = rec_at(n0).b;
-            K0 = rec_at(n0).c;
+            K0 = cz_at(n0);
             const int n1 = L[it + 3];
             const float w1 = step(A1, B1, K1, o1);
             if (MW) store_max(w0, w1, it);
@@ -1532,6 +1660,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         }
         if (MW && (steps & 1)) store_max(w_tail, 0.0f, steps - 1);  // any_c is 0 if it was not walked
         if (bl_cur >= 0) last_n = bs - rg.x + bl_cur / (int)sizeof(FwdSlot) + 1;
+        if (DEP && med_cur >= 0) med_n = bs - rg.x + med_cur / (int)sizeof(FwdSlot) + 1;
         __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
         if (MW && id >= 0 && id < n) {  // thread t owns slot t until it restages it
             const uint2 pp = *reinterpret_cast<const uint2*>(S[threadIdx.x].pos);
@@ -1553,6 +1682,15 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
         final_T[p] = T;
         n_contrib[p] = last_n;
+        if (DEP) {
+            // the first composited entry is always a median candidate (T = 1
+            // before it), so med_n == 0 exactly when nothing composited
+            const float zm = med_n > 0 ? zmed : 0.0f;
+            if (median_depth) median_depth[p] = zm;
+            if (median_pos) median_pos[p] = med_n;
+            if (DEP == 2)  // already about the median (zmed_ref == zm); 0 when nothing composited
+                dist_totals[p] = make_float4(Aw, Bw, Cw, fmaxf(__builtin_fmaf(Aw, Cw, -Bw * Bw), 0.0f));
+        }
     }
 }
 
@@ -1673,11 +1811,13 @@ __device__ __forceinline__ SplatConsts load_consts(int i, int n, const float* __
     return SplatConsts{conics[3 * i + 0], conics[3 * i + 1], conics[3 * i + 2], opac[i]};
 }
 
-template <bool AW>
-__device__ __forceinline__ void gather_write(int i, const float (&u)[10], const SplatConsts& k,
+// Per splat: u[0..8] the nine sums, u[9] the weight (AW), u[10] the depth
+// gradient (DZ).
+template <bool AW, bool DZ>
+__device__ __forceinline__ void gather_write(int i, const float (&u)[11], const SplatConsts& k,
                                              float2* __restrict__ d_means, float* __restrict__ d_conics,
                                              float* __restrict__ d_colors, float* __restrict__ d_opac,
-                                             float* __restrict__ accum_w)
+                                             float* __restrict__ accum_w, float* __restrict__ d_depths)
 {
     d_means[i] = make_float2(__builtin_fmaf(k.a, u[4], k.b * u[5]), __builtin_fmaf(k.b, u[4], k.c * u[5]));
     d_conics[3 * i + 0] = -0.5f * u[6];
@@ -1688,6 +1828,7 @@ __device__ __forceinline__ void gather_write(int i, const float (&u)[10], const 
     d_colors[3 * i + 2] = u[2];
     d_opac[i] = u[3] != 0.0f ? u[3] / k.o : 0.0f;
     if (AW) accum_w[i] = u[9];
+    if (DZ) d_depths[i] = u[10];
 }
 
 // Gathers: one wave per 64 consecutive splats. Their pairs are contiguous,
@@ -1719,14 +1860,14 @@ constexpr int kWalkManyPairs = 16;  // mean pairs per splat above which the defe
 constexpr int kDeferChunk = 4, kDeferWG = 4;
 constexpr int kDeferBatchFew = 255, kDeferBatchMany = 191;
 
-template <bool AW>
+template <bool AW, bool DZ>
 __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,
                                                        const float4* __restrict__ rec,
                                                        const uint4* __restrict__ flags16,
                                                        const float* __restrict__ conics, const float* __restrict__ opac,
                                                        float2* __restrict__ d_means, float* __restrict__ d_conics,
                                                        float* __restrict__ d_colors, float* __restrict__ d_opac,
-                                                       float* __restrict__ accum_w)
+                                                       float* __restrict__ accum_w, float* __restrict__ d_depths)
 {
     __shared__ int used_list[kGatherWin];  // used pairs of the current window, relative to its start
     const int lane = threadIdx.x;
@@ -1736,14 +1877,21 @@ __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restr
     const SplatConsts sc = load_consts(i, n, conics, opac);
     const long long p0 = __shfl(my_off, 0, kWave);
     const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
-    float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float u[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     auto add_rec = [&](long long P) {
         const float4 a = rec[3 * P + 0], b = rec[3 * P + 1];
-        const float2 c = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
+        float4 c;
+        if (DZ) {
+            c = rec[3 * P + 2];
+        } else {  // the last 8 bytes are padding
+            const float2 c2 = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
+            c = make_float4(c2.x, c2.y, 0.0f, 0.0f);
+        }
         u[0] += a.x; u[1] += a.y; u[2] += a.z; u[3] += a.w;
         u[4] += b.x; u[5] += b.y; u[6] += b.z; u[7] += b.w;
         u[8] += c.x;
         if (AW) u[9] += c.y;
+        if (DZ) u[10] += c.z;
     };
     const long long w0 = p0 & ~15ll;  // windows start on 16-byte flag boundaries
     auto window = [&](long long wb) -> uint4 {
@@ -1805,11 +1953,10 @@ __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restr
         __syncthreads();  // used_list is rewritten by the next window
     }
     if (i >= n) return;
-    if (!AW) u[9] = 0.0f;
-    gather_write<AW>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w);
+    gather_write<AW, DZ>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w, d_depths);
 }
 
-template <bool AW>
+template <bool AW, bool DZ>
 __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* __restrict__ splat_offsets,
                                                               long long n_slots, const float4* __restrict__ rec,
                                                               const uint4* __restrict__ flags16,
@@ -1818,7 +1965,8 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
                                                               float2* __restrict__ d_means,
                                                               float* __restrict__ d_conics,
                                                               float* __restrict__ d_colors,
-                                                              float* __restrict__ d_opac, float* __restrict__ accum_w)
+                                                              float* __restrict__ d_opac, float* __restrict__ accum_w,
+                                                              float* __restrict__ d_depths)
 {
     __shared__ int used_list[kGatherWin];  // used pairs of the current window, relative to its start
     __shared__ float4 stage[kWave][3];     // records of up to 64 listed pairs
@@ -1829,7 +1977,7 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
     const SplatConsts sc = load_consts(i, n, conics, opac);
     const long long p0 = __shfl(my_off, 0, kWave);
     const long long p1 = min(max((long long)splat_offsets[min(i0 + kWave, n)], 0ll), n_slots);
-    float u[10] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float u[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     const long long w0 = p0 & ~15ll;  // windows start on 16-byte flag boundaries
     auto window = [&](long long wb) -> uint4 {
         const long long q = wb + 16 * lane;
@@ -1889,8 +2037,12 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
                 const long long P = wb + used_list[r];
                 stage[lane][0] = rec[3 * P + 0];
                 stage[lane][1] = rec[3 * P + 1];
-                const float2 c2 = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
-                stage[lane][2] = make_float4(c2.x, c2.y, 0.0f, 0.0f);
+                if (DZ) {
+                    stage[lane][2] = rec[3 * P + 2];
+                } else {  // the last 8 bytes are padding
+                    const float2 c2 = *reinterpret_cast<const float2*>(rec + 3 * P + 2);
+                    stage[lane][2] = make_float4(c2.x, c2.y, 0.0f, 0.0f);
+                }
             }
             __syncthreads();
             const int k1 = min(end, r0 + kWave);
@@ -1900,14 +2052,14 @@ __global__ __launch_bounds__(kWave) void gather_staged_kernel(int n, const int* 
                 u[4] += b.x; u[5] += b.y; u[6] += b.z; u[7] += b.w;
                 u[8] += c.x;
                 if (AW) u[9] += c.y;
+                if (DZ) u[10] += c.z;
             }
             __syncthreads();  // stage is rewritten by the next round
         }
         __syncthreads();  // used_list is rewritten by the next window
     }
     if (i >= n) return;
-    if (!AW) u[9] = 0.0f;
-    gather_write<AW>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w);
+    gather_write<AW, DZ>(i, u, sc, d_means, d_conics, d_colors, d_opac, accum_w, d_depths);
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1942,48 +2094,83 @@ extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
     return layout(n > 0 ? n : 1, 0, 0).bytes;
 }
 
+namespace {
+gs_status fwd_impl(const char* name, int32_t n, const float* means2d, const float* conics, const float* colors,
+                   const float* opacities, const float* depths, const float* background, int32_t width,
+                   int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids, int64_t n_isect,
+                   float* image, float* final_T, int32_t* n_contrib, float* max_weight, float* dist_totals,
+                   float* median_depth, int32_t* median_pos, void* workspace, size_t workspace_bytes,
+                   hipStream_t st)
+{
+    GS_CHECK_ARG(n >= 0, "%s: n = %d < 0", name, n);
+    GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "%s: n_isect = %lld out of range", name,
+                 (long long)n_isect);
+    GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
+                 "%s: image size %d x %d outside 1..%d", name, width, height, kMaxDim);
+    GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "%s: NULL splat array", name);
+    GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "%s: NULL image-side array", name);
+    GS_CHECK_ARG(n_isect == 0 || sorted_ids, "%s: sorted_ids is NULL", name);
+    const int dep = dist_totals ? 2 : (median_depth || median_pos) ? 1 : 0;
+    GS_CHECK_ARG(dep == 0 || n == 0 || depths, "%s: depth outputs requested with depths NULL", name);
+    const Layout L = layout(n > 0 ? n : 1, 0, 0);
+    GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes), "%s: workspace %zu bytes, need %zu", name,
+                 workspace_bytes, L.bytes);
+    GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "%s: workspace not 256-byte aligned", name);
+    SplatRec* recs = n ? (SplatRec*)((char*)workspace + L.recs) : nullptr;
+    if (n > 0) {
+        prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, nullptr,
+                                                     dep ? depths : nullptr, recs);
+        GS_HIP(hipGetLastError());
+    }
+    const int GX = grid_x(width), tiles = GX * grid_y(height);
+    if (max_weight && n > 0) {
+        zero_u32_kernel<<<(n + 255) / 256, 256, 0, st>>>((unsigned*)max_weight, n);
+        GS_HIP(hipGetLastError());
+    }
+    auto launch = [&](auto kernel) {
+        kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges, n_isect,
+                                                   sorted_ids, recs, background, image, final_T, n_contrib,
+                                                   (unsigned*)max_weight, (float4*)dist_totals, median_depth,
+                                                   median_pos);
+    };
+    // every combination of the optional outputs is its own instance
+    if (max_weight) {
+        if (dep == 2) launch(fwd_kernel<true, 2>);
+        else if (dep == 1) launch(fwd_kernel<true, 1>);
+        else launch(fwd_kernel<true, 0>);
+    } else {
+        if (dep == 2) launch(fwd_kernel<false, 2>);
+        else if (dep == 1) launch(fwd_kernel<false, 1>);
+        else launch(fwd_kernel<false, 0>);
+    }
+    GS_HIP(hipGetLastError());
+    return GS_OK;
+}
+}  // namespace
+
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                                       const float* opacities, const float* background, int32_t width,
                                       int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
                                       int64_t n_isect, float* image, float* final_T, int32_t* n_contrib,
                                       float* max_weight, void* workspace, size_t workspace_bytes,
-                                      gs_stream_t stream_)
+                                      gs_stream_t stream)
 {
-    hipStream_t st = (hipStream_t)stream_;
-    GS_CHECK_ARG(n >= 0, "gs_rasterize_fwd: n = %d < 0", n);
-    GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "gs_rasterize_fwd: n_isect = %lld out of range",
-                 (long long)n_isect);
-    GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
-                 "gs_rasterize_fwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
-    GS_CHECK_ARG(n == 0 || (means2d && conics && colors && opacities), "gs_rasterize_fwd: NULL splat array");
-    GS_CHECK_ARG(tile_ranges && image && final_T && n_contrib, "gs_rasterize_fwd: NULL image-side array");
-    GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_fwd: sorted_ids is NULL");
-    const Layout L = layout(n > 0 ? n : 1, 0, 0);
-    GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
-                 "gs_rasterize_fwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
-    GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_fwd: workspace not 256-byte aligned");
-    SplatRec* recs = n ? (SplatRec*)((char*)workspace + L.recs) : nullptr;
-    if (n > 0) {
-        prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, colors, opacities, nullptr,
-                                                     recs);
-        GS_HIP(hipGetLastError());
-    }
-    const int GX = grid_x(width), tiles = GX * grid_y(height);
-    if (max_weight) {
-        if (n > 0) {
-            zero_u32_kernel<<<(n + 255) / 256, 256, 0, st>>>((unsigned*)max_weight, n);
-            GS_HIP(hipGetLastError());
-        }
-        fwd_kernel<true><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
-                                                             n_isect, sorted_ids, recs, background, image, final_T,
-                                                             n_contrib, (unsigned*)max_weight);
-    } else {
-        fwd_kernel<false><<<xcd_grid(tiles), kBlock, 0, st>>>(n, width, height, GX, tiles, (const int2*)tile_ranges,
-                                                              n_isect, sorted_ids, recs, background, image, final_T,
-                                                              n_contrib, nullptr);
-    }
-    GS_HIP(hipGetLastError());
-    return GS_OK;
+    return fwd_impl("gs_rasterize_fwd", n, means2d, conics, colors, opacities, nullptr, background, width, height,
+                    tile_ranges, sorted_ids, n_isect, image, final_T, n_contrib, max_weight, nullptr, nullptr,
+                    nullptr, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* conics,
+                                            const float* colors, const float* opacities, const float* depths,
+                                            const float* background, int32_t width, int32_t height,
+                                            const int32_t* tile_ranges, const int32_t* sorted_ids, int64_t n_isect,
+                                            float* image, float* final_T, int32_t* n_contrib, float* max_weight,
+                                            float* dist_totals, float* median_depth, int32_t* median_pos,
+                                            void* workspace, size_t workspace_bytes, gs_stream_t stream)
+{
+    return fwd_impl("gs_rasterize_fwd_depth", n, means2d, conics, colors, opacities, depths, background, width,
+                    height, tile_ranges, sorted_ids, n_isect, image, final_T, n_contrib, max_weight, dist_totals,
+                    median_depth, median_pos, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height)
@@ -1993,13 +2180,16 @@ extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, in
 }
 
 namespace {
+// dep: the depth terms taken (bit 0 distortion, bit 1 median; dz holds their
+// inputs, dL_ddepths their output), 0 for none.
 gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const float* colors,
                    const float* opacities, const int32_t* radii, const float* background, int32_t width,
                    int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
                    const int32_t* splat_offsets, int64_t n_isect, const float* final_T, const int32_t* n_contrib,
                    const float* dL_dimage, float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                    float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
-                   size_t workspace_bytes, gs_stream_t stream_, const gs_event_t* events)
+                   size_t workspace_bytes, gs_stream_t stream_, const gs_event_t* events, int dep = 0,
+                   DepthIn dz = DepthIn{}, float* dL_ddepths = nullptr)
 {
     hipStream_t st = (hipStream_t)stream_;
     // stage-boundary events of gs_rasterize_bwd_timed (none for gs_rasterize_bwd)
@@ -2031,6 +2221,16 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
     GS_CHECK_ARG(!aw || n == 0 || accum_weight, "gs_rasterize_bwd: GS_FLAG_ACCUM_WEIGHT with accum_weight NULL");
     GS_CHECK_ARG(tile_ranges && final_T && n_contrib && dL_dimage, "gs_rasterize_bwd: NULL image-side array");
     GS_CHECK_ARG(n_isect == 0 || sorted_ids, "gs_rasterize_bwd: sorted_ids is NULL");
+    if (dep) {
+        GS_CHECK_ARG(n == 0 || (dz.depths && dL_ddepths), "gs_rasterize_bwd_depth: depths or dL_ddepths NULL");
+        GS_CHECK_ARG(dz.median_pos, "gs_rasterize_bwd_depth: median_pos is NULL");
+        GS_CHECK_ARG(!(dep & 1) || dz.totals, "gs_rasterize_bwd_depth: dL_ddist given with dist_totals NULL");
+        if (store_walk || add_walk) {
+            set_error("gs_rasterize_bwd_depth: the depth terms run on the deferred walk only "
+                      "(GS_FLAG_WALK_ADD / GS_FLAG_WALK_STORE set)");
+            return GS_ERR_UNSUPPORTED;
+        }
+    }
     const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
     const Layout L = layout(n, n_isect, tiles);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
@@ -2061,21 +2261,33 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         GS_HIP(hipGetLastError());
         GS_HIP(mark(1));
         const int* ord = order;
-        auto launch = [&](auto kernel) {
+        auto launch = [&](auto kernel, auto... extra) {
             kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, GY, tiles, n, (const int2*)tile_ranges,
                                                        sorted_ids, recs, splat_offsets, n_isect, background,
-                                                       final_T, n_contrib, dL_dimage, ord, slots, used);
+                                                       final_T, n_contrib, dL_dimage, ord, slots, used, extra...);
+        };
+        // the deferred walk: one instance per (weight, batch size, depth terms)
+        auto defer = [&](auto nb_tag) {
+            constexpr int NB = decltype(nb_tag)::value;
+            using std::integral_constant;
+            auto go = [&](auto dep_tag) {
+                constexpr int D = decltype(dep_tag)::value;
+                aw ? launch(bwd_defer_kernel<true, NB, kDeferChunk, kDeferWG, D>, dz)
+                   : launch(bwd_defer_kernel<false, NB, kDeferChunk, kDeferWG, D>, dz);
+            };
+            if (dep == 3) go(integral_constant<int, 3>{});
+            else if (dep == 2) go(integral_constant<int, 2>{});
+            else if (dep == 1) go(integral_constant<int, 1>{});
+            else go(integral_constant<int, 0>{});
         };
         if (store_walk)
             aw ? launch(bwd_store_kernel<true>) : launch(bwd_store_kernel<false>);
         else if (add_walk)
             aw ? launch(bwd_kernel<true>) : launch(bwd_kernel<false>);
         else if (many_tiles)
-            aw ? launch(bwd_defer_kernel<true, kDeferBatchMany, kDeferChunk, kDeferWG>)
-               : launch(bwd_defer_kernel<false, kDeferBatchMany, kDeferChunk, kDeferWG>);
+            defer(std::integral_constant<int, kDeferBatchMany>{});
         else
-            aw ? launch(bwd_defer_kernel<true, kDeferBatchFew, kDeferChunk, kDeferWG>)
-               : launch(bwd_defer_kernel<false, kDeferBatchFew, kDeferChunk, kDeferWG>);
+            defer(std::integral_constant<int, kDeferBatchFew>{});
         GS_HIP(hipGetLastError());
         GS_HIP(mark(2));
     } else {
@@ -2084,15 +2296,20 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
     }
     const uint4* flags16 = reinterpret_cast<const uint4*>(used);  // padded to whole 16-byte units
     const unsigned gb = (unsigned)((n + kWave - 1) / kWave);
-#define GS_GATHER(K, AWV, ACC)                                                                                    \
-    K<AWV><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities, (float2*)dL_dmeans2d, \
-                                 dL_dconics, dL_dcolors, dL_dopacities, ACC)
+#define GS_GATHER(K, AWV, ACC, DZV, DD)                                                                            \
+    K<AWV, DZV><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities,                   \
+                                      (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities, ACC, DD)
+    const bool dzo = dep != 0;
     if (n_isect <= (long long)kGatherRegMaxPairs * n) {
-        if (aw) GS_GATHER(gather_kernel, true, accum_weight);
-        else GS_GATHER(gather_kernel, false, nullptr);
+        if (aw) dzo ? GS_GATHER(gather_kernel, true, accum_weight, true, dL_ddepths)
+                    : GS_GATHER(gather_kernel, true, accum_weight, false, nullptr);
+        else dzo ? GS_GATHER(gather_kernel, false, nullptr, true, dL_ddepths)
+                 : GS_GATHER(gather_kernel, false, nullptr, false, nullptr);
     } else {
-        if (aw) GS_GATHER(gather_staged_kernel, true, accum_weight);
-        else GS_GATHER(gather_staged_kernel, false, nullptr);
+        if (aw) dzo ? GS_GATHER(gather_staged_kernel, true, accum_weight, true, dL_ddepths)
+                    : GS_GATHER(gather_staged_kernel, true, accum_weight, false, nullptr);
+        else dzo ? GS_GATHER(gather_staged_kernel, false, nullptr, true, dL_ddepths)
+                 : GS_GATHER(gather_staged_kernel, false, nullptr, false, nullptr);
     }
 #undef GS_GATHER
     GS_HIP(hipGetLastError());
@@ -2113,6 +2330,36 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const flo
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
                     sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, const float* conics,
+                                            const float* colors, const float* opacities, const float* depths,
+                                            const int32_t* radii, const float* background, int32_t width,
+                                            int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                            const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                            const int32_t* n_contrib, const float* dist_totals,
+                                            const int32_t* median_pos, const float* dL_dimage,
+                                            const float* dL_ddist, const float* dL_dmedian, float* dL_dmeans2d,
+                                            float* dL_dconics, float* dL_dcolors, float* dL_dopacities,
+                                            float* dL_ddepths, float* accum_weight, uint32_t flags,
+                                            void* workspace, size_t workspace_bytes, gs_stream_t stream)
+{
+    const int dep = (dL_ddist ? 1 : 0) | (dL_dmedian ? 2 : 0);
+    if (dep == 0) {  // no depth term: the plain backward, and zero depth gradients if asked for
+        const gs_status r = bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height,
+                                     tile_ranges, sorted_ids, splat_offsets, n_isect, final_T, n_contrib,
+                                     dL_dimage, dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities, accum_weight,
+                                     flags, workspace, workspace_bytes, stream, nullptr);
+        if (r != GS_OK || !dL_ddepths || n <= 0) return r;
+        zero_u32_kernel<<<(n + 255) / 256, 256, 0, (hipStream_t)stream>>>((unsigned*)dL_ddepths, n);
+        GS_HIP(hipGetLastError());
+        return GS_OK;
+    }
+    const DepthIn dz{depths, (const float4*)dist_totals, median_pos, dL_ddist, dL_dmedian};
+    return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
+                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, nullptr,
+                    dep, dz, dL_ddepths);
 }
 
 extern "C" gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* conics,

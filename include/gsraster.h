@@ -223,6 +223,37 @@ gs_status gs_rasterize_fwd(int32_t n, const float* means2d, const float* conics,
                            void* workspace, size_t workspace_bytes, gs_stream_t stream);
 
 /*
+ * gs_rasterize_fwd with the depth outputs: the distortion and median-depth
+ * options of rasterize_bwd_2d that the Spirula Studio page lists (section
+ * 机制拆解: a per-pixel float4 of "distortion totals" and a median output)
+ * without defining them. Read as
+ *
+ *   median      the depth of the last composited splat whose transmittance
+ *               before it is still > 1/2, 0 when nothing composites; and its
+ *               list position (within the tile's list) plus one, 0 for none
+ *   distortion  D = sum over composited pairs i < j of w_i w_j (z_i - z_j)^2,
+ *               w = alpha T, z = the splat's depth
+ *   totals      (A, B, C, D): A = sum w, B = sum w (z - median),
+ *               C = sum w (z - median)^2, and D (which equals A C - B^2)
+ *
+ * Same arguments, outputs and errors as gs_rasterize_fwd, and:
+ *   depths        device float [n], the depths given to gs_bin_tiles; required
+ *                 when any depth output is asked for
+ *   dist_totals   device float [height][width][4] (out), or NULL
+ *   median_depth  device float [height][width] (out), or NULL
+ *   median_pos    device int32 [height][width] (out), or NULL
+ * With all three NULL the call is gs_rasterize_fwd. Each combination of the
+ * optional outputs runs its own kernel instance; without dist_totals no
+ * instruction or register is spent on the sums.
+ */
+gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                 const float* opacities, const float* depths, const float* background,
+                                 int32_t width, int32_t height, const int32_t* tile_ranges,
+                                 const int32_t* sorted_ids, int64_t n_isect, float* image, float* final_T,
+                                 int32_t* n_contrib, float* max_weight, float* dist_totals, float* median_depth,
+                                 int32_t* median_pos, void* workspace, size_t workspace_bytes, gs_stream_t stream);
+
+/*
  * Backward (rasterize_backwards in "Phase 5 step 30b — kernel-by-kernel
  * timing", sections 計測結果 and ホットスポット ranking; rasterize_bwd_2d on the
  * Spirula Studio page). One workgroup (4 wave64) per tile walks the tile's
@@ -270,6 +301,42 @@ gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                            float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                            size_t workspace_bytes, gs_stream_t stream);
+
+/*
+ * gs_rasterize_bwd with the depth terms of gs_rasterize_fwd_depth: the
+ * gradients of L = sum_p <dL_dimage_p, image_p> + dL_ddist_p D_p +
+ * dL_dmedian_p median_p, every discrete decision (skip, stop, clamp, the
+ * median's splat) held as the forward took it. The distortion reaches each
+ * composited splat through its alpha (hence mean, conic and opacity) and its
+ * depth, dD/dz_k = 2 w_k (A (z_k - median) - B); the median reaches only the
+ * depth of its splat (dmedian/dz = 1).
+ *
+ * Same arguments, outputs and errors as gs_rasterize_bwd, and:
+ *   depths        device float [n]; required with a depth term
+ *   dist_totals   device float [height][width][4], as gs_rasterize_fwd_depth
+ *                 wrote it; required with dL_ddist
+ *   median_pos    device int32 [height][width], as gs_rasterize_fwd_depth
+ *                 wrote it (clamped to [0, n_contrib]); required with a depth
+ *                 term (the totals are taken about the median's depth)
+ *   dL_ddist      device float [height][width], or NULL: no distortion term
+ *   dL_dmedian    device float [height][width], or NULL: no median term
+ *   dL_ddepths    device float [n] (out): required with a depth term; with
+ *                 neither term it may be NULL, else it is zero-filled
+ * The depth terms run on the deferred walk: with GS_FLAG_WALK_ADD or
+ * GS_FLAG_WALK_STORE and a depth term the call returns GS_ERR_UNSUPPORTED.
+ * Each combination of the terms is its own kernel instance (one more partial
+ * sum per record and a per-wave LDS pad of one float per lane and step).
+ */
+gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, const float* conics, const float* colors,
+                                 const float* opacities, const float* depths, const int32_t* radii,
+                                 const float* background, int32_t width, int32_t height,
+                                 const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                 const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                 const int32_t* n_contrib, const float* dist_totals, const int32_t* median_pos,
+                                 const float* dL_dimage, const float* dL_ddist, const float* dL_dmedian,
+                                 float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors, float* dL_dopacities,
+                                 float* dL_ddepths, float* accum_weight, uint32_t flags, void* workspace,
+                                 size_t workspace_bytes, gs_stream_t stream);
 
 /*
  * gs_rasterize_bwd with its stages timed: the same work, arguments and errors,

@@ -207,3 +207,13 @@ def custom_scene(width: int, height: int, means2d, sigmas, thetas, opacities, co
         background=np.ascontiguousarray(background, dtype=np.float32),
         accum_weight=accum_weight,
     )
+
+
+def depth_upstream(sc: Scene, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Upstream gradients of the per-pixel depth outputs (distortion, median
+    depth) for a scene: two [H, W] float32 fields of standard normals, drawn
+    with ``numpy.random.default_rng(10000 + seed)``."""
+    rng = np.random.default_rng(10000 + seed)
+    g_dist = rng.standard_normal((sc.height, sc.width), dtype=np.float32)
+    g_median = rng.standard_normal((sc.height, sc.width), dtype=np.float32)
+    return g_dist, g_median

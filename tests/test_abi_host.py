@@ -181,3 +181,37 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_call():
     assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(w=0) == _lib.GS_ERR_INVALID_ARG
     assert lib.gs_rasterize_bwd_workspace_size(1000, 1_000_000, 64, 64) <= cap
+
+
+def test_depth_entry_points_reject_bad_arguments():
+    """The depth variants check their extra arguments on the host, before any
+    device work, and refuse the depth terms on the walks that lack them."""
+    lib = _lib.load()
+    p = ctypes.c_void_p(1)
+    ws = ctypes.c_void_p(256)
+
+    def fwd(depths=p, totals=p, med=None, pos=None):
+        return lib.gs_rasterize_fwd_depth(4, p, p, p, p, depths, None, 64, 64, p, p, 0, p, p, p, None, totals, med,
+                                          pos, ws, 1 << 20, None)
+    assert fwd(depths=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"depths" in lib.gs_last_error()
+    assert fwd(depths=None, totals=None, pos=p) == _lib.GS_ERR_INVALID_ARG
+
+    def bwd(depths=p, totals=p, pos=p, gd=p, gm=None, dz=p, flags=0):
+        return lib.gs_rasterize_bwd_depth(1, p, p, p, p, depths, p, None, 8, 8, p, p, p, 0, p, p, totals, pos, p, gd,
+                                          gm, p, p, p, p, dz, None, flags, None, 0, None)
+    assert bwd(depths=None) == _lib.GS_ERR_INVALID_ARG
+    assert bwd(dz=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"dL_ddepths" in lib.gs_last_error()
+    assert bwd(pos=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"median_pos" in lib.gs_last_error()
+    assert bwd(totals=None) == _lib.GS_ERR_INVALID_ARG
+    assert b"dist_totals" in lib.gs_last_error()
+    # the median term needs no totals: the call gets as far as the workspace check
+    assert bwd(totals=None, gd=None, gm=p) == _lib.GS_ERR_INVALID_ARG
+    assert b"workspace" in lib.gs_last_error()
+    for walk in (_lib.GS_FLAG_WALK_ADD, _lib.GS_FLAG_WALK_STORE):
+        assert bwd(flags=walk) == _lib.GS_ERR_UNSUPPORTED
+        assert b"deferred walk" in lib.gs_last_error()
+        assert bwd(gd=None, gm=p, flags=walk) == _lib.GS_ERR_UNSUPPORTED
+    assert bwd(flags=0x80) == _lib.GS_ERR_INVALID_ARG

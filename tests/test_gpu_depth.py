@@ -1,0 +1,257 @@
+"""GPU parity of the depth terms (distortion and median depth): the forward's
+depth outputs and the backward's depth gradients, through the C ABI, against
+the CPU float64 oracle.
+
+Bars:
+  * forward: the image, final_T and n_contrib bit-identical with and without
+    the depth outputs; on pixels the oracle flags neither for the walk nor for
+    the median decision: median_pos exact, median_depth bit-exact (a copy of a
+    float32 depth), A within 1e-5 absolute (it is 1 - final_T), and B, C, D
+    within the float32 bound of a running sum over the pixel's n composited
+    entries, (4 n + 16) u times the sum of the magnitudes of its terms
+    (u = 2^-24; the weights carry the running product's error, about 2 n u,
+    and the sum its own, about n u): sum w |u| <= sqrt(A C) for B, C itself
+    for C, and A C + B^2 for D = A C - B^2; on pixels flagged for the median
+    only, median_pos may be another composited entry: its depth must match
+    it, A and D the oracle's, and B, C the oracle's moments moved to the
+    GPU's median;
+  * backward: each of the nine scalar gradient fields and the depth gradient
+    within 1e-4 * max|oracle field|, with every upstream zeroed at the pixels
+    flagged for the walk and dL/dmedian also at those flagged for the median
+    (the colour, distortion and median terms checked together, and alone).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scenes
+import differentiable_tile_rasterization_amd as gsr
+from test_gpu_parity import (FIELDS, GRAD_REL, IMG_TOL, T_TOL, _custom, _dev, _say, check_bins, gpu_bins,
+                             gpu_fwd)
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+DEPTH_ABS = 1e-9   # absolute floor of the totals' bars (pixels with nothing composited)
+DEPTH_FIELD = ("dL_ddepths", "ddepths", None, "ddepth")
+
+
+def _list_depths(sc, rng_o, ids_o, pos):
+    """Depth of list entry pos - 1 of each pixel's tile (nan where pos == 0)."""
+    GX, _ = oracle.grid(sc.width, sc.height)
+    ys, xs = np.mgrid[0:sc.height, 0:sc.width]
+    start = rng_o[(ys // 16) * GX + xs // 16, 0]
+    z = np.full(pos.shape, np.nan)
+    has = pos > 0
+    z[has] = sc.depths[ids_o[start[has] + pos[has] - 1]]
+    return z
+
+
+def check_depth_forward(sc, bins, ids_o, rng_o):
+    """The forward's depth outputs. Returns (GPU outputs, oracle forward,
+    walk-flagged, median-flagged)."""
+    img, T, nc = gpu_fwd(sc, bins)
+    d = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                   _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                   bins.sorted_ids)
+    torch.cuda.synchronize()
+    assert torch.equal(d["image"], img) and torch.equal(d["final_T"], T) and torch.equal(d["n_contrib"], nc)
+    # the instances with one of the outputs only give the same values
+    d_med = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                       _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                       bins.sorted_ids, distortion=False)
+    d_dis = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                       _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                       bins.sorted_ids, median=False, max_weight=True)
+    torch.cuda.synchronize()
+    assert torch.equal(d_med["median_depth"], d["median_depth"]) and torch.equal(d_med["median_pos"], d["median_pos"])
+    assert torch.equal(d_dis["dist_totals"], d["dist_totals"]) and torch.equal(d_dis["median_pos"], d["median_pos"])
+    assert "dist_totals" not in d_med and "median_depth" not in d_dis
+
+    fo = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
+                              rng_o, ids_o)
+    fd = oracle.rasterize_fwd_depth(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
+                                    sc.height, rng_o, ids_o, sc.depths)
+    amb, mamb = fo["ambiguous"], fd["median_ambiguous"] & ~fo["ambiguous"]
+    ok = ~amb & ~mamb
+    pos = d["median_pos"].cpu().numpy()
+    zmed = d["median_depth"].cpu().numpy().astype(np.float64)
+    tot = d["dist_totals"].cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(pos[ok], fd["median_pos"][ok])
+    np.testing.assert_array_equal(zmed[ok], fd["median_depth"][ok])
+    A, B, C, D = np.moveaxis(fd["totals"], -1, 0)
+    k_n = (4 * fo["n_contrib"] + 16) * U32
+    mag = {1: np.sqrt(A * C), 2: C, 3: A * C + B * B}
+    err_A = np.abs(tot[..., 0] - A)[~amb].max(initial=0.0)
+    assert err_A <= T_TOL, err_A
+    rel = {}
+    for k, ref in ((1, B), (2, C), (3, D)):
+        bar = k_n * mag[k] + DEPTH_ABS
+        e = np.abs(tot[..., k] - ref)
+        bad = ok & (e > bar)
+        assert not bad.any(), ("BCD"[k - 1], int(bad.sum()), e[bad][:5], bar[bad][:5], fo["n_contrib"][bad][:5])
+        rel["BCD"[k - 1]] = float((e[ok] / bar[ok]).max(initial=0.0))
+    # median-flagged pixels: a composited entry, with its own depth; the
+    # distortion does not depend on the choice, B and C move with it
+    if mamb.any():
+        p, z = pos[mamb], zmed[mamb]
+        nc_h = nc.cpu().numpy()[mamb]
+        assert np.all((p >= 1) & (p <= nc_h))
+        np.testing.assert_array_equal(z, _list_depths(sc, rng_o, ids_o, pos)[mamb])
+        dl = z - fd["median_depth"][mamb]
+        Am, Bo, Co = A[mamb], B[mamb], C[mamb]
+        Bm = Bo - dl * Am
+        Cm = Co - 2 * dl * Bo + dl * dl * Am
+        km = k_n[mamb]
+        assert np.all(np.abs(tot[..., 3][mamb] - D[mamb]) <= km * mag[3][mamb] + DEPTH_ABS)
+        assert np.all(np.abs(tot[..., 1][mamb] - Bm) <= km * (np.sqrt(Am * Cm) + np.abs(dl) * Am) + DEPTH_ABS)
+        assert np.all(np.abs(tot[..., 2][mamb] - Cm) <= km * (Cm + dl * dl * Am) + DEPTH_ABS)
+    _say(f"depth forward: median-flagged px {int(mamb.sum())}, walk-flagged {int(amb.sum())}, "
+         f"A err {err_A:.1e}, B/C/D largest err / bar {rel}")
+    return d, T, nc, amb, mamb
+
+
+def check_depth_backward(sc, bins, ids_o, rng_o, d, T, nc, amb, mamb, accum_weight=False,
+                         terms=("all", "dist", "median")):
+    gD, gM = scenes.depth_upstream(sc, 0)
+    gD, gM = gD.copy(), gM.copy()
+    gD[amb] = 0.0
+    gM[amb | mamb] = 0.0
+    g = sc.dL_dimage.copy()
+    g[amb] = 0.0
+    zero_img = np.zeros_like(g)
+    bo_col = None
+    for term in terms:
+        gi = g if term == "all" else zero_img
+        gd = gD if term in ("all", "dist") else None
+        gm = gM if term in ("all", "median") else None
+        out = gsr.gs_rasterize_bwd_depth(
+            _dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.depths), _dev(sc.radii),
+            _dev(sc.background), sc.width, sc.height, bins, T, nc, d["median_pos"], _dev(gi),
+            dist_totals=d["dist_totals"] if gd is not None else None, dL_ddist=None if gd is None else _dev(gd),
+            dL_dmedian=None if gm is None else _dev(gm), accum_weight=accum_weight)
+        torch.cuda.synchronize()
+        res = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+        bd = oracle.rasterize_bwd_depth(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width,
+                                        sc.height, rng_o, ids_o, sc.depths, gd, gm)
+        ref = dict(bd)
+        if term == "all":
+            if bo_col is None:
+                bo_col = oracle.rasterize_bwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
+                                              sc.width, sc.height, rng_o, ids_o, g)
+            for k in ("dmeans2d", "dconics", "dcolors", "dopacities"):
+                ref[k] = bd[k] + bo_col[k]
+            ref["accum_weight"] = bo_col["accum_weight"]
+        errs = {}
+        for gk, ok_, col, name in FIELDS + [DEPTH_FIELD]:
+            r = ref[ok_] if col is None else ref[ok_][:, col]
+            v = res[gk] if col is None else res[gk][:, col]
+            e, s = float(np.abs(v - r).max(initial=0.0)), float(np.abs(r).max(initial=0.0))
+            assert e <= GRAD_REL * max(s, 1e-30), (term, name, e, s)
+            errs[name] = e / s if s > 0 else e
+        if term == "median":  # the median reaches nothing but depths
+            for gk in ("dL_dmeans2d", "dL_dconics", "dL_dcolors", "dL_dopacities"):
+                assert not res[gk].any(), gk
+        if accum_weight and term == "all":
+            e = np.abs(res["accum_weight"] - ref["accum_weight"]).max()
+            assert e <= GRAD_REL * np.abs(ref["accum_weight"]).max()
+        _say(f"depth backward [{term}]: err / max|field|", {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+def check_depth_scene(sc, accum_weight=False, terms=("all", "dist", "median")):
+    _say(f"depth terms: scene {sc.name} seed {sc.seed} {sc.width}x{sc.height} n={sc.n}")
+    bins = gpu_bins(sc)
+    ids_o, rng_o = check_bins(sc, bins)
+    d, T, nc, amb, mamb = check_depth_forward(sc, bins, ids_o, rng_o)
+    check_depth_backward(sc, bins, ids_o, rng_o, d, T, nc, amb, mamb, accum_weight, terms)
+    return bins
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_depth_tiny(seed):
+    check_depth_scene(scenes.make_scene("tiny", seed))
+
+
+def test_depth_tiny_with_accum_weight():
+    check_depth_scene(scenes.make_scene("tiny", 3), accum_weight=True)
+
+
+def test_depth_early():
+    check_depth_scene(scenes.make_scene("early", 0))
+
+
+def test_depth_mid():
+    check_depth_scene(scenes.make_scene("mid", 0), terms=("all", "dist"))
+
+
+def test_depth_bench_full_size():
+    check_depth_scene(scenes.make_scene("bench", 0), terms=("all",))
+
+
+def test_depth_stress_full_size_with_accum_weight():
+    """Splats over many tiles: the 191-entry batches and the staged gather."""
+    check_depth_scene(scenes.make_scene("stress", 0), accum_weight=True, terms=("all",))
+
+
+def test_depth_ragged_image_with_background():
+    check_depth_scene(_custom(1, 50, 37, 120, bg=[0.2, 0.5, 0.7]))
+
+
+def test_depth_long_lists_many_batches():
+    """Hundreds of splats on one tile: the median entry falls in various batches."""
+    bins = check_depth_scene(_custom(6, 16, 16, 900, sig=(2.0, 6.0), op=(0.01, 0.2)))
+    assert bins.n_isect > 512
+
+
+def test_depth_clamped_opacity():
+    check_depth_scene(_custom(2, 48, 48, 60, op=(0.991, 1.0)))
+
+
+def test_depth_image_covering_splats():
+    check_depth_scene(_custom(12, 300, 200, 6, sig=(40.0, 90.0), op=(0.2, 0.6), pad=0))
+
+
+def test_depth_no_intersections():
+    sc = _custom(9, 32, 32, 4, pad=0)
+    sc.radii[:] = 0
+    bins = gpu_bins(sc)
+    d = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                   _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                   bins.sorted_ids)
+    for k in ("dist_totals", "median_depth", "median_pos"):
+        assert torch.all(d[k] == 0), k
+    gD, gM = scenes.depth_upstream(sc, 0)
+    out = gsr.gs_rasterize_bwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                     _dev(sc.depths), _dev(sc.radii), _dev(sc.background), sc.width, sc.height,
+                                     bins, d["final_T"], d["n_contrib"], d["median_pos"], _dev(sc.dL_dimage),
+                                     dist_totals=d["dist_totals"], dL_ddist=_dev(gD), dL_dmedian=_dev(gM))
+    for v in out.values():
+        assert torch.all(v == 0)
+
+
+def test_depth_terms_refused_on_other_walks():
+    sc = scenes.make_scene("tiny", 0)
+    bins = gpu_bins(sc)
+    d = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                   _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                   bins.sorted_ids)
+    gD, _ = scenes.depth_upstream(sc, 0)
+    for walk in ("add", "store"):
+        with pytest.raises(gsr.GsError, match="GS_ERR_UNSUPPORTED"):
+            gsr.gs_rasterize_bwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                       _dev(sc.depths), _dev(sc.radii), _dev(sc.background), sc.width, sc.height,
+                                       bins, d["final_T"], d["n_contrib"], d["median_pos"], _dev(sc.dL_dimage),
+                                       dist_totals=d["dist_totals"], dL_ddist=_dev(gD), walk=walk)
+    # without a depth term the call is the plain backward, with zero depth gradients
+    plain = gsr.gs_rasterize_bwd(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                 _dev(sc.radii), _dev(sc.background), sc.width, sc.height, bins, d["final_T"],
+                                 d["n_contrib"], _dev(sc.dL_dimage))
+    none = gsr.gs_rasterize_bwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                      _dev(sc.depths), _dev(sc.radii), _dev(sc.background), sc.width, sc.height,
+                                      bins, d["final_T"], d["n_contrib"], d["median_pos"], _dev(sc.dL_dimage))
+    torch.cuda.synchronize()
+    assert torch.all(none["dL_ddepths"] == 0)
+    for k, v in plain.items():
+        ref = v.cpu().numpy()
+        np.testing.assert_allclose(none[k].cpu().numpy(), ref, rtol=0, atol=1e-6 * max(np.abs(ref).max(), 1e-30))
