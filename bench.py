@@ -267,6 +267,16 @@ def main():
     log("stages (ms, mean of %d calls): " % args.steps + ", ".join(f"{k} {v:.4f}" for k, v in stage_mean.items()))
     t_fwd = per_call(fwd, 10, 2)
     t_mw = per_call(fwd_max_weight, 10, 2)
+    # the depth variants (distortion and median together), outside the timed region
+    fwd_d = gsr.gs_rasterize_fwd_depth(m, q, c, o, d, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
+    gD, gM = (t(a) for a in scenes.depth_upstream(sc, args.seed))
+    out_d = dict(out, dL_ddepths=torch.empty((sc.n,), dtype=torch.float32, device=dev))
+    t_fwd_depth = per_call(lambda: gsr.gs_rasterize_fwd_depth(m, q, c, o, d, bg, sc.width, sc.height,
+                                                              bins.tile_ranges, bins.sorted_ids), 10, 2)
+    t_bwd_depth = per_call(lambda: gsr.gs_rasterize_bwd_depth(
+        m, q, c, o, d, r, bg, sc.width, sc.height, bins, T, nc, fwd_d["median_pos"], g,
+        dist_totals=fwd_d["dist_totals"], dL_ddist=gD, dL_dmedian=gM, accum_weight=aw, out=out_d, workspace=ws),
+        10, 2)
     t0 = time.perf_counter()
     for _ in range(3):
         gsr.gs_bin_tiles(m, r, d, sc.width, sc.height, capacity=bins.n_isect)
@@ -359,7 +369,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages_ms": {"tile_isect": t_bin, "raster_fwd": float(np.median(t_fwd)),
-                      "raster_fwd_max_wt": float(np.median(t_mw)), "raster_bwd": ms,
+                      "raster_fwd_max_wt": float(np.median(t_mw)),
+                      "raster_fwd_depth": float(np.median(t_fwd_depth)),
+                      "raster_bwd_depth": float(np.median(t_bwd_depth)), "raster_bwd": ms,
                       "raster_bwd_median": float(np.median(t_calls)), "raster_bwd_min": float(np.min(t_calls))},
         "counts": {"p_walk": p_walk, "p_composited": p_contrib, "walked_entries": entries,
                    "splat_tile_groups": groups_tile, "splat_quadrant_groups": groups_wave,

@@ -2,12 +2,12 @@
 
     python -m differentiable_tile_rasterization_amd.profsum stats <kernel_stats.csv> <out.md> "<command>"
     python -m differentiable_tile_rasterization_amd.profsum pmc <fetch_dir> <write_dir> <out.json> <out.md> \\
-        "<fetch command>" "<write command>" [config]
-    python -m differentiable_tile_rasterization_amd.profsum counters <out.md> <kernel prefix> \\
+        "<fetch command>" "<write command>" <config> "<call kernels, ';'-separated, the walk first>"
+    python -m differentiable_tile_rasterization_amd.profsum counters <out.md> <kernel instance> \\
         <dir> "<command>" [<dir> "<command>" ...]
 
-`counters` lists, for the last dispatch of the named kernel in each --pmc run
-directory, every counter summed over the device, with the LDS and VALU
+`counters` lists, for the last dispatch of the named kernel instance (its full
+name up to the argument list) in each --pmc run directory, every counter summed over the device, with the LDS and VALU
 utilisations they give. `stats` lists every kernel of a --kernel-trace --stats run (calls, average and
 total time). `pmc` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) into bytes per launch, scaled by what the same counters read for the
@@ -27,8 +27,6 @@ import sys
 
 COPY_BYTES = 1 << 30          # the copy kernel moves 1 GiB in and 1 GiB out per launch
 COPY_NAME = "copy_kernel"
-CALL_KERNELS = ["bwd_setup_kernel", "band_order_kernel", "bwd_defer_kernel", "bwd_kernel", "bwd_store_kernel",
-                "gather_kernel", "gather_staged_kernel"]
 DOMINANT = ("bwd_defer_kernel<", "bwd_kernel<", "bwd_store_kernel<")  # the reverse walk (any form): the roofline's kernel
 
 
@@ -89,7 +87,7 @@ def _per_kernel(dir_path: str) -> dict[str, list[float]]:
 
 
 def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: str, cmd_write: str,
-        config: str = "bench") -> None:
+        config: str, call_kernels: str) -> None:
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     from bench import kernel_source_hash  # the hash the benchmark compares against
     fe, wr = _per_kernel(fetch_dir), _per_kernel(write_dir)
@@ -101,9 +99,14 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
         fb = avg(fe[k]) * 1024.0 * f_scale if k in fe else 0.0
         wb = avg(wr[k]) * 1024.0 * w_scale if k in wr else 0.0
         per[k] = {"fetch_bytes": fb, "write_bytes": wb}
-    call = [k for k in per if any(k.startswith(c) for c in CALL_KERNELS)]
+    # the call's kernel instances, named exactly (the benchmark also runs other
+    # instances of the same kernels: the optional variants)
+    call = [k.strip() for k in call_kernels.split(";") if k.strip()]
+    missing = [k for k in call if k not in per]
+    if missing:
+        raise SystemExit(f"not in the counter output: {missing}")
     total = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in call)
-    dom = [k for k in per if k.startswith(DOMINANT)]
+    dom = [k for k in call if k.startswith(DOMINANT)][:1]
     dom_bytes = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in dom)
     rec = {"config": config, "source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
            "dominant_kernel": dom, "hbm_bytes_per_launch": dom_bytes, "call_kernels": call,
@@ -123,20 +126,22 @@ def pmc(fetch_dir: str, write_dir: str, out_json: str, out_md: str, cmd_fetch: s
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def counters(out_md: str, prefix: str, *runs: str) -> None:
+def counters(out_md: str, kernel: str, *runs: str) -> None:
     vals: dict[str, float] = {}
     cmds = []
     for d, cmd in zip(runs[0::2], runs[1::2]):
         path = [os.path.join(d, f) for f in os.listdir(d) if f.endswith("counter_collection.csv")][0]
         per: dict[int, dict[str, float]] = collections.defaultdict(lambda: collections.defaultdict(float))
         for r in csv.DictReader(open(path)):
-            if _short(r["Kernel_Name"]).startswith(prefix):
+            if _short(r["Kernel_Name"]) == kernel:
                 per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"{kernel} not in {path}")
         last = per[max(per)]
         for k, v in last.items():
             vals[k if k != "GRBM_GUI_ACTIVE" else f"GRBM_GUI_ACTIVE ({os.path.basename(d)})"] = v
         cmds.append(cmd)
-    lines = [f"# Counters of {prefix} (last dispatch of each run, summed over the device)", "",
+    lines = [f"# Counters of {kernel} (its last dispatch in each run, summed over the device)", "",
              "Commands (repo root, on the MI355X host):", ""] + ["    " + c for c in cmds] + [
              "", "| counter | value |", "|---|---:|"]
     lines += [f"| {k} | {v:.4g} |" for k, v in sorted(vals.items())]
