@@ -810,25 +810,36 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         bool hit[kHalves] = {false, false, false, false, false, false, false, false};
         if (threadIdx.x < kDSlots) half_hits(r, ox, oy, k, hend, hit);  // the candidates' waves
         // Keep the top candidates whose half-list entries fit the partial
-        // records: suffix sums of the hit counts over the slots, from the top.
-        int hc = 0;
+        // records. Usually all of them do (the wave totals, from ballots, say
+        // so); otherwise suffix sums of the hit counts over the slots, from
+        // the top, pick the candidates that fit.
+        {
+            int wtot = 0;  // this wave's half-list entries (wave-uniform)
 #pragma unroll
-        for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
-        int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int u = __shfl_down(suf, off, kWave);
-            if (lane + off < kWave) suf += u;
+            for (int q = 0; q < kHalves; ++q) wtot += __popcll(__ballot(hit[q]));
+            if (lane == 0) wave_hits[wv] = wtot;
+            if (threadIdx.x == 0) cut = NB;
         }
-        if (lane == 0) wave_hits[wv] = suf;
-        if (threadIdx.x == 0) cut = NB;
         __syncthreads();
-        for (int w2 = wv + 1; w2 < 4; ++w2) suf += wave_hits[w2];
-        const bool keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
-        const unsigned long long kb = __ballot(keep);
-        if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));
-        if (!keep) {
+        const int total = wave_hits[0] + wave_hits[1] + wave_hits[2] + wave_hits[3];
+        bool keep = cand;
+        if (total > kCap) {  // workgroup-uniform
+            int hc = 0;
 #pragma unroll
-            for (int q = 0; q < kHalves; ++q) hit[q] = false;
+            for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
+            int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int u = __shfl_down(suf, off, kWave);
+                if (lane + off < kWave) suf += u;
+            }
+            for (int w2 = wv + 1; w2 < 4; ++w2) suf += wave_hits[w2];
+            keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
+            const unsigned long long kb = __ballot(keep);
+            if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));  // lowest kept
+            if (!keep) {
+#pragma unroll
+                for (int q = 0; q < kHalves; ++q) hit[q] = false;
+            }
         }
         // The entry's pair slot: the splat's first slot (from its record) plus
         // the tile's row-major index inside the splat's tile rectangle
@@ -862,7 +873,9 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         base[0] = 0;
 #pragma unroll
         for (int q = 1; q < kHalves; ++q) base[q] = base[q - 1] + len[q - 1];
-        const int next_hi = lo + cut;
+        // the candidates below the lowest kept one go to the next batch (all
+        // were kept when the records fit)
+        const int next_hi = total > kCap ? lo + cut : lo;
         // DEP: the slot offset of this pixel's median entry when this batch
         // walks it (the kept candidates [next_hi, hi)), else -1
         const int med_off = (DEP & 2) && mp - 1 >= next_hi && mp - 1 < hi
@@ -888,9 +901,11 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         }
         // the same for both halves: wave-uniform, so the loop runs on scalar control
         const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
-        // the shorter half takes the dummy entry once its list is exhausted
-        // (and both read up to four entries past the end, ahead of use)
-        for (int p = my_len + (lane & 31); p < steps + 4; p += 32) list[hq][p] = kDDummyOff;
+        // the shorter half takes the dummy entry once its list is exhausted;
+        // both run a whole number of chunks (steps rounded up to KC) and read
+        // two entries past that, ahead of use
+        const int steps_kc = (steps + KC - 1) & ~(KC - 1);
+        for (int p = my_len + (lane & 31); p < steps_kc + 2; p += 32) list[hq][p] = kDDummyOff;
         // batch slots below this pixel's walk end, as a byte offset bound
         const int ncb_off = (nc - lo) * (int)sizeof(StoreSlot);
         const unsigned short* L = list[hq];
@@ -994,23 +1009,28 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                 }
             }
             const float dx0 = row_x0 - mu.x, dyr = row_y - mu.y;
+            // The two lanes of each pixel row (lanes 2u, 2u + 1 of the record)
+            // add their sums first; the row's dy then turns the row totals of
+            // s and s dx into those of s dy, s dx dy and s dy^2, with no cross-
+            // lane adds of their own.
+            static_assert(kPPL == 4, "two lanes per pixel row");
             float f[kRaw + 1];
-            f[0] = Wr;
-            f[1] = Wg;
-            f[2] = Wb;
-            f[3] = S0;
-            f[4] = __builtin_fmaf(dx0, S0, Sx);                                  // sum s dx
-            f[5] = dyr * S0;                                                      // sum s dy
-            f[6] = __builtin_fmaf(dx0, __builtin_fmaf(dx0, S0, Sx + Sx), Sxx);   // sum s dx^2
-            f[7] = dyr * f[4];                                                    // sum s dx dy
-            f[8] = dyr * f[5];                                                    // sum s dy^2
-            f[9] = AW ? Wt : Vz;
-            f[10] = Vz;  // field kZ: 9 or 10
-            // the record's kLPR lanes add their totals: inside each quad, then
-            // (eight lanes) between the two quads of each 8-lane half-row
+            f[0] = dpp_add_quad_xor1(Wr);
+            f[1] = dpp_add_quad_xor1(Wg);
+            f[2] = dpp_add_quad_xor1(Wb);
+            f[3] = dpp_add_quad_xor1(S0);                                                      // sum s
+            f[4] = dpp_add_quad_xor1(__builtin_fmaf(dx0, S0, Sx));                             // sum s dx
+            f[6] = dpp_add_quad_xor1(__builtin_fmaf(dx0, __builtin_fmaf(dx0, S0, Sx + Sx), Sxx));  // sum s dx^2
+            f[5] = dyr * f[3];                                                                   // sum s dy
+            f[7] = dyr * f[4];                                                                   // sum s dx dy
+            f[8] = dyr * f[5];                                                                   // sum s dy^2
+            f[9] = dpp_add_quad_xor1(AW ? Wt : Vz);
+            f[10] = dpp_add_quad_xor1(Vz);  // field kZ: 9 or 10
+            // then the rows: the two pairs of each quad, and (eight lanes) the
+            // two quads of each 8-lane half-row
 #pragma unroll
             for (int q = 0; q < kF; ++q) {
-                f[q] = dpp_add_quad_xor1(dpp_add_quad_xor2(f[q]));
+                f[q] = dpp_add_quad_xor2(f[q]);
                 if (kLPR == 8) f[q] = dpp_add_half_mirror(f[q]);
                 asm volatile("" : "+v"(f[q]));  // fused DPP adds, outside the store's lane mask
             }
@@ -1020,28 +1040,31 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                 for (int q = 0; q < kF; ++q) rec[q] = f[q];
             }
         };
+        // Every chunk runs all KC steps (the lists hold dummies up to a whole
+        // number of chunks), in pairs over two record buffers, each refilled
+        // one entry ahead of its use: the loads land where the next step reads
+        // them, with no register copies.
+        static_assert(KC % 2 == 0, "steps run in pairs");
         auto walk = [&](auto clamp_tag) {
-            int o_cur = list_at(0), o_nxt = list_at(1);
-            float4 A = rec_at(o_cur).a, B = rec_at(o_cur).b;
-            float C = rec_at(o_cur).c;
-            float Z = z_at(o_cur);
-            for (int c = 0; c < steps; c += KC) {
+            int o0 = list_at(0), o1 = list_at(1);
+            float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+            float C0 = rec_at(o0).c, Z0 = z_at(o0);
+            for (int c = 0; c < steps_kc; c += KC) {
 #pragma unroll
-                for (int j = 0; j < KC; ++j) {
+                for (int j = 0; j < KC; j += 2) {
                     const int it = c + j;
-                    if (it >= steps) break;   // wave-uniform
-                    // the next entry's record one step ahead, its list entry two
-                    const float4 An = rec_at(o_nxt).a, Bn = rec_at(o_nxt).b;
-                    const float Cn = rec_at(o_nxt).c;
-                    const float Zn = z_at(o_nxt);
-                    const int o_nn = list_at(it + 2);
-                    step(A, B, C, Z, o_cur, j, clamp_tag);
-                    A = An;
-                    B = Bn;
-                    C = Cn;
-                    Z = Zn;
-                    o_cur = o_nxt;
-                    o_nxt = o_nn;
+                    const float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+                    const float C1 = rec_at(o1).c, Z1 = z_at(o1);
+                    const int n0 = list_at(it + 2);
+                    step(A0, B0, C0, Z0, o0, j, clamp_tag);
+                    A0 = rec_at(n0).a;
+                    B0 = rec_at(n0).b;
+                    C0 = rec_at(n0).c;
+                    Z0 = z_at(n0);
+                    const int n1 = list_at(it + 3);
+                    step(A1, B1, C1, Z1, o1, j + 1, clamp_tag);
+                    o0 = n0;
+                    o1 = n1;
                 }
                 // the pad's rows go from the lanes that wrote them to the lanes
                 // that sum them: LDS accesses of one wave are served in order, so
@@ -1072,10 +1095,12 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                     for (int f = 0; f < kF; ++f) u[f] += pr[f];
                 }
             }
-            bool any = false;
+            // some sum != 0 (as a float compare: -0 counts as zero, NaN not):
+            // the OR of the bit patterns without their sign bits
+            unsigned bits = 0;
 #pragma unroll
-            for (int f = 0; f < kF; ++f) any |= u[f] != 0.0f;
-            if (any) {
+            for (int f = 0; f < kF; ++f) bits |= __float_as_uint(u[f]);
+            if ((bits << 1) != 0u) {
                 rec_out[3 * (long long)slot + 0] = make_float4(u[0], u[1], u[2], u[3]);
                 rec_out[3 * (long long)slot + 1] = make_float4(u[4], u[5], u[6], u[7]);
                 const float uw = AW ? u[9] : 0.0f;
