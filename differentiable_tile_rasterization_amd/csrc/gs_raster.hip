@@ -1720,16 +1720,15 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
 }
 
 // ---------------------------------------------------------------------------
-// Launch order of the backward's tiles: longest first inside each XCD's band.
+// Launch order of the backward's tiles inside each XCD's band.
 //
 // The backward runs about 2.6 rounds of resident workgroups per CU, and tile
 // costs vary (on the 2M-splat scene the costliest tile takes 1.5x the mean):
 // in plain tile order the last workgroups start late and leave CUs idle at
-// the end. Dispatching each band's tiles in decreasing order of their largest
-// n_contrib (the walk length; correlation 0.9 with the walk's cost) is the
-// longest-processing-time rule, which keeps that tail short. Workgroup w still
-// runs a tile of band w % 8 (the band of tile rows that XCD w % 8 works on),
-// as in the plain mapping.
+// the end. The cost of a tile is its largest n_contrib (the walk length;
+// correlation 0.9 with the walk's cost). Workgroup w still runs a tile of band
+// w % 8 (the band of tile rows that XCD w % 8 works on), as in the plain
+// mapping.
 // ---------------------------------------------------------------------------
 
 // Setup of a backward call, one launch. Blocks [0, cost_blocks) give one
@@ -1775,15 +1774,21 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, in
     if (i < n16) flags16[i] = make_uint4(0, 0, 0, 0);
 }
 
-// One workgroup per band: counting sort of the band's tiles into 256 cost
-// buckets, costliest bucket first, then order[r * 8 + band] = the band's r-th
-// tile (-1 for padding). Ties within a bucket take any order; no result
-// depends on the launch order, only the time does.
+// One workgroup per band. The band's cheapest tiles (a quarter of them, by a
+// 256-bucket cost histogram) go last, costliest first (the longest-processing-
+// time rule for the end of the launch, where late long tiles would leave CUs
+// idle); the others go first in tile-id order, so that workgroups running at
+// the same time on the band's XCD work on neighbouring tiles, whose lists
+// share splats: their records are then re-read from that XCD's L2 rather than
+// from HBM. order[r * 8 + band] = the band's r-th tile (-1 for padding).
+// No result depends on the launch order, only the time and traffic do.
 __global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* __restrict__ cost,
                                                           int* __restrict__ order)
 {
     __shared__ int hist[256];
     __shared__ int cmax;
+    __shared__ int cut_key;               // keys above it (the cheapest tiles) form the tail
+    __shared__ int wsum[1024 / 64];       // head tiles per wave's chunk range, then its prefix
     const int per = (tiles + kXcds - 1) / kXcds;
     const int band = blockIdx.x, t0 = band * per;
     const int n = max(0, min(per, tiles - t0));
@@ -1812,11 +1817,51 @@ __global__ __launch_bounds__(1024) void band_order_kernel(int tiles, const int* 
         hist[4 * l + 1] = ex + h0;
         hist[4 * l + 2] = ex + h0 + h1;
         hist[4 * l + 3] = ex + h0 + h1 + h2;
+        // the tail: the buckets whose tiles all start at or after 3/4 of the
+        // band (bucket k starts at hist[k]); the smallest such key
+        int first = 256;
+        for (int j = 3; j >= 0; --j)
+            if (hist[4 * l + j] * 4 >= 3 * n) first = 4 * l + j;
+        first = -wave_max_i32(-first);
+        if (l == 0) cut_key = first;
     }
     __syncthreads();
+    const int ck = cut_key;
+    // head: tiles with key < ck, in tile-id order. Each thread takes a
+    // contiguous range of the band's tiles; a block scan of the per-thread
+    // counts gives each head tile its position.
+    const int chunk = (n + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int i0 = (int)threadIdx.x * chunk, i1 = min(n, i0 + chunk);
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) cnt += key(cost[t0 + i]) < ck ? 1 : 0;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = cnt;  // inclusive scan inside the wave
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += u;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int w = 0; w < (int)blockDim.x / 64; ++w) {
+            const int c = wsum[w];
+            wsum[w] = acc;
+            acc += c;
+        }
+    }
+    __syncthreads();
+    int pos = wsum[wv] + incl - cnt;
+    for (int i = i0; i < i1; ++i)
+        if (key(cost[t0 + i]) < ck) order[(pos++) * kXcds + band] = t0 + i;
+    // tail: after the head, by bucket (costliest first); the head's tiles are
+    // exactly those of the buckets before ck, so the bucket offsets carry over
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int r = atomicAdd(&hist[key(cost[t0 + i])], 1);
-        order[r * kXcds + band] = t0 + i;
+        const int k = key(cost[t0 + i]);
+        if (k >= ck) {
+            const int r = atomicAdd(&hist[k], 1);
+            order[r * kXcds + band] = t0 + i;
+        }
     }
     for (int r = n + threadIdx.x; r < per; r += blockDim.x) order[r * kXcds + band] = -1;
 }
