@@ -420,7 +420,7 @@ def cpu_baseline(oracle, sc, bins, nc, args, log):
     oracle.set_threads(1)
     for name in ("tiny", "early", "mid"):
         s2 = scenes.make_scene(name, 0)
-        ids2, rng2 = oracle.bin_tiles(s2.means2d, s2.radii, s2.depths, s2.width, s2.height)
+        ids2, rng2 = oracle.bin_tiles(s2.means2d, s2.conics, s2.opacities, s2.radii, s2.depths, s2.width, s2.height)
         c0 = time.perf_counter()
         fo = oracle.rasterize_fwd(s2.means2d, s2.conics, s2.colors, s2.opacities, s2.background, s2.width,
                                   s2.height, rng2, ids2)

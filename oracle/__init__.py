@@ -129,28 +129,144 @@ def tile_rects(means2d: np.ndarray, radii: np.ndarray, depths: np.ndarray, width
     return tx0, tx1, ty0, ty1
 
 
-def bin_tiles(means2d, radii, depths, width: int, height: int):
-    """Tile lists, as (sorted_ids int32 [I], tile_ranges int32 [GX*GY, 2]).
+def cull_ellipses(means2d, conics, opacities):
+    """Per-splat constants of the binning's culling ellipse, float32.
 
-    Each tile's list holds the splats whose rectangle covers it, ordered by
-    the float32 bit pattern of depth (positive floats order like their bit
-    patterns), ties broken by ascending splat id. Tile ids are row-major,
-    ``ty * GX + tx``; the lists are concatenated in tile-id order.
+    A splat can reach alpha >= 1/255 only where its quadratic form
+    Q(d) = a dx^2 + 2 b dx dy + c dy^2 <= 2 ln(255 o). The binning keeps a
+    tile only if the ellipse {Q <= T} meets the tile's pixel-centre rectangle,
+    with T an upper bound on 2 ln(255 o) taken with basic float32 operations
+    only (each rounded once, in a fixed order, so that any IEEE float32
+    implementation decides every tile identically): with 255 o = m2 * 2^e2,
+    m2 in [1, 2), ln(255 o) <= e2 ln 2 + (m2 - 1) / sqrt(m2) (the bound
+    ln x <= (x - 1)/sqrt(x) for x >= 1), then T = 2 lnb (1 + 2^-10) + 2^-10.
+    Q is taken through the Cholesky factors of the conic: Q = (l11 u + l21 v)^2
+    + (l22 v)^2 with u = x - mean_x, v = y - mean_y.
 
-    Written as the definition: every (splat, tile) pair is listed, then one
-    library sort orders the pairs by (tile id, depth bits, splat id)."""
-    GX, GY = grid(width, height)
+    Returns a dict of float32 arrays: mx, my, l11, l21, l22, T, vmax (the
+    ellipse's half height), vL (v of its leftmost point; -vL is that of the
+    rightmost), and boolean ``cull`` (False where the constants are not usable:
+    such a splat keeps its whole rectangle) and ``dead`` (the float32 product
+    255 o is below 1, so alpha <= o < 1/255 everywhere)."""
+    f = np.float32
+    m = np.asarray(means2d, dtype=f)
+    q = np.asarray(conics, dtype=f)
+    o = np.asarray(opacities, dtype=f)
+    with np.errstate(all="ignore"):
+        y = f(255.0) * o
+        mant, ex = np.frexp(y)                       # y = mant * 2^ex, mant in [0.5, 1)
+        m2 = mant * f(2.0)                           # in [1, 2)
+        e2 = (ex - 1).astype(f)
+        lnb = e2 * LN2_F32 + (m2 - f(1.0)) / np.sqrt(m2)
+        T = f(2.0) * lnb
+        T = (T + T * f(1.0 / 1024.0)) + f(1.0 / 1024.0)
+        l11 = np.sqrt(q[:, 0])
+        l21 = q[:, 1] / l11
+        l22 = np.sqrt(np.maximum(q[:, 2] - l21 * l21, f(0.0)))
+        sT = np.sqrt(T)
+        vmax = sT / l22
+        nrm = np.sqrt(l21 * l21 + l22 * l22)
+        vL = (sT * l21) / (l22 * nrm)
+        dead = ~(y >= f(1.0))           # 255 o < 1: alpha <= o < 1/255 everywhere
+        usable = np.isfinite(T) & np.isfinite(l11) & np.isfinite(l21) & np.isfinite(l22) & \
+            np.isfinite(vmax) & np.isfinite(vL) & (l11 > 0) & (l22 > 0) & np.isfinite(m).all(axis=1)
+    return {"mx": m[:, 0], "my": m[:, 1], "l11": l11, "l21": l21, "l22": l22, "T": T, "vmax": vmax, "vL": vL,
+            "cull": usable & ~dead, "dead": dead}
+
+
+LN2_F32 = np.float32(0.6931471805599453)  # rounds up: float32(ln 2) > ln 2
+
+
+def row_columns(ce, idx, ty, tx0, tx1):
+    """For splat idx[k] and tile row ty[k]: the range [c_lo, c_hi] of tile
+    columns of [tx0[k], tx1[k]) whose pixel-centre rectangle meets the
+    culling ellipse (empty when c_lo > c_hi). Float32, every operation rounded
+    once in the order written.
+
+    Over the row's band of pixel centres y in [Y0, Y0 + 15], v = y - mean_y,
+    the ellipse's points have u = (-l21 v +- sqrt(T - (l22 v)^2)) / l11; the
+    left end is convex in v and least at the leftmost point's v (clamped to
+    the band and to |v| <= vmax), the right end concave and largest at the
+    rightmost's. A column c (pixel centres x in [16 c + 0.5, 16 c + 15.5])
+    meets the ellipse's part in the band iff 16 c + 15.5 >= xl and
+    16 c + 0.5 <= xr."""
+    f = np.float32
+    mx, my, l11, l21, l22 = (ce[k][idx] for k in ("mx", "my", "l11", "l21", "l22"))
+    T, vmax, vL = ce["T"][idx], ce["vmax"][idx], ce["vL"][idx]
+    with np.errstate(all="ignore"):
+        Y0 = ty.astype(f) * f(16.0) + f(0.5)
+        v0 = Y0 - my
+        v1 = v0 + f(15.0)
+        lo = np.maximum(v0, -vmax)
+        hi = np.minimum(v1, vmax)
+        row_ok = lo <= hi
+        vl = np.minimum(np.maximum(vL, lo), hi)
+        vr = np.minimum(np.maximum(-vL, lo), hi)
+        tl = l22 * vl
+        sl = np.sqrt(np.maximum(T - tl * tl, f(0.0)))
+        xl = mx + (-(l21 * vl) - sl) / l11
+        tr = l22 * vr
+        sr = np.sqrt(np.maximum(T - tr * tr, f(0.0)))
+        xr = mx + (-(l21 * vr) + sr) / l11
+        txf0, txf1 = tx0.astype(f), tx1.astype(f)
+        # smallest c with 16 c + 15.5 >= xl, largest with 16 c + 0.5 <= xr
+        # (estimates clamped near the rectangle, then corrected by one)
+        cl = np.minimum(np.maximum(np.ceil((xl - f(15.5)) * f(0.0625)), txf0 - f(1.0)), txf1 + f(1.0))
+        cl = np.where((cl - f(1.0)) * f(16.0) + f(15.5) >= xl, cl - f(1.0), cl)
+        cl = np.where(cl * f(16.0) + f(15.5) < xl, cl + f(1.0), cl)
+        ch = np.minimum(np.maximum(np.floor((xr - f(0.5)) * f(0.0625)), txf0 - f(2.0)), txf1)
+        ch = np.where((ch + f(1.0)) * f(16.0) + f(0.5) <= xr, ch + f(1.0), ch)
+        ch = np.where(ch * f(16.0) + f(0.5) > xr, ch - f(1.0), ch)
+    c_lo = np.maximum(cl.astype(np.int64), tx0)
+    c_hi = np.minimum(ch.astype(np.int64), tx1 - 1)
+    empty = ~row_ok
+    c_lo = np.where(empty, tx1, c_lo)
+    c_hi = np.where(empty, tx1 - 1, c_hi)
+    return c_lo, c_hi
+
+
+def kept_pairs(means2d, conics, opacities, radii, depths, width: int, height: int):
+    """Every (splat, tile) pair of the splats' tile rectangles, splat by splat,
+    each splat's tiles row-major (the pair numbering the backward's slots use),
+    with whether the binning keeps it. Returns (ids, tx, ty, kept)."""
     tx0, tx1, ty0, ty1 = tile_rects(means2d, radii, depths, width, height)
     nx = tx1 - tx0
     cnt = nx * (ty1 - ty0)
     total = int(cnt.sum())
-    # every (splat, tile) pair: splat by splat, each splat's tiles row-major
     ids = np.repeat(np.arange(len(cnt), dtype=np.int32), cnt)
     local = np.arange(total, dtype=np.int64) - np.repeat(np.cumsum(cnt) - cnt, cnt)
     nxr = np.maximum(np.repeat(nx, cnt), 1)
     tx = np.repeat(tx0, cnt) + local % nxr
     ty = np.repeat(ty0, cnt) + local // nxr
     del local, nxr
+    ce = cull_ellipses(means2d, conics, opacities)
+    # the column range of each (splat, row), taken once per row
+    rows = (ty1 - ty0)
+    r_ids = np.repeat(np.arange(len(cnt), dtype=np.int64), rows)
+    r_ty = np.repeat(ty0, rows) + (np.arange(int(rows.sum()), dtype=np.int64) - np.repeat(np.cumsum(rows) - rows, rows))
+    c_lo, c_hi = row_columns(ce, r_ids, r_ty, tx0[r_ids], tx1[r_ids])
+    row_first = np.cumsum(rows) - rows                 # first row task of each splat
+    rt = row_first[ids] + (ty - ty0[ids])              # row task of each pair
+    kept = (tx >= c_lo[rt]) & (tx <= c_hi[rt])
+    # splats whose constants are unusable keep their whole rectangle; dead ones none
+    kept = np.where(ce["cull"][ids], kept, ~ce["dead"][ids])
+    return ids, tx, ty, kept
+
+
+def bin_tiles(means2d, conics, opacities, radii, depths, width: int, height: int):
+    """Tile lists, as (sorted_ids int32 [I], tile_ranges int32 [GX*GY, 2]).
+
+    Each tile's list holds the splats whose rectangle covers it and whose
+    culling ellipse (:func:`cull_ellipses`) meets its pixel-centre rectangle,
+    ordered by the float32 bit pattern of depth (positive floats order like
+    their bit patterns), ties broken by ascending splat id. Tile ids are
+    row-major, ``ty * GX + tx``; the lists are concatenated in tile-id order.
+
+    Written as the definition: every kept (splat, tile) pair is listed, then
+    one library sort orders the pairs by (tile id, depth bits, splat id)."""
+    GX, GY = grid(width, height)
+    ids, tx, ty, kept = kept_pairs(means2d, conics, opacities, radii, depths, width, height)
+    ids, tx, ty = ids[kept], tx[kept], ty[kept]
     tile = ty * GX + tx
     del tx, ty
     dbits = np.asarray(depths, dtype=np.float32).view(np.uint32)
@@ -490,7 +606,7 @@ def depth_terms_bruteforce(means2d, conics, opacities, depths, radii, width: int
 
 def run_scene(sc, tiles=None, backward=True, dL_dimage=None):
     """Bin, forward and (optionally) backward a scene. Returns a dict."""
-    ids, rng_ = bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    ids, rng_ = bin_tiles(sc.means2d, sc.conics, sc.opacities, sc.radii, sc.depths, sc.width, sc.height)
     out = {"sorted_ids": ids, "tile_ranges": rng_}
     out.update(rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background,
                              sc.width, sc.height, rng_, ids, tiles=tiles))

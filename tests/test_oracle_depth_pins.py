@@ -48,7 +48,7 @@ def _bwd(sc, ids, rng_, gd, gm, depths=None):
 
 
 def _bins(sc):
-    return oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    return oracle.bin_tiles(sc.means2d, sc.conics, sc.opacities, sc.radii, sc.depths, sc.width, sc.height)
 
 
 # ---------------------------------------------------------------- closed forms

@@ -106,6 +106,16 @@ PY_MUTANTS = [
      "perm = np.lexsort((ids, tile, dbits[ids]))"),
     ("negative_depth_not_culled", "live = (np.asarray(radii) > 0) & (d > 0) &", "live = (np.asarray(radii) > 0) &"),
     ("tile_ids_column_major", "tile = ty * GX + tx", "tile = tx * GY + ty"),
+    # the culling ellipse
+    ("cull_threshold_not_doubled", "T = f(2.0) * lnb", "T = lnb"),
+    ("cull_log_bound_mantissa_dropped", "lnb = e2 * LN2_F32 + (m2 - f(1.0)) / np.sqrt(m2)", "lnb = e2 * LN2_F32"),
+    ("cull_leftmost_v_sign", "vL = (sT * l21) / (l22 * nrm)", "vL = -(sT * l21) / (l22 * nrm)"),
+    ("cull_left_end_shear_sign", "xl = mx + (-(l21 * vl) - sl) / l11", "xl = mx + ((l21 * vl) - sl) / l11"),
+    ("cull_band_without_half_pixel", "Y0 = ty.astype(f) * f(16.0) + f(0.5)", "Y0 = ty.astype(f) * f(16.0)"),
+    ("cull_row_band_one_pixel_short", "v1 = v0 + f(15.0)", "v1 = v0 + f(14.0)"),
+    ("cull_not_applied", "kept = np.where(ce[\"cull\"][ids], kept, ~ce[\"dead\"][ids])", "kept = ~ce[\"dead\"][ids]"),
+    ("cull_dead_splats_kept", "kept = np.where(ce[\"cull\"][ids], kept, ~ce[\"dead\"][ids])",
+     "kept = np.where(ce[\"cull\"][ids], kept, True)"),
 ]
 
 
