@@ -132,9 +132,9 @@ def main():
     r, d, g = t(sc.radii), t(sc.depths), t(sc.dL_dimage)
     aw = sc.accum_weight
     log(f"workload {args.config}: {sc.width}x{sc.height}, {sc.n} splats, accum_weight={aw}")
-    bins = gsr.gs_bin_tiles(m, r, d, sc.width, sc.height)
+    bins = gsr.gs_bin_tiles(m, q, o, r, d, sc.width, sc.height)
     img, T, nc = gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
-    ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_isect, sc.width, sc.height) + 256, dtype=torch.uint8,
+    ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_slots, sc.width, sc.height) + 256, dtype=torch.uint8,
                      device=dev)
     out = gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw,
                                workspace=ws, walk=args.walk)
@@ -279,7 +279,7 @@ def main():
         10, 2)
     t0 = time.perf_counter()
     for _ in range(3):
-        gsr.gs_bin_tiles(m, r, d, sc.width, sc.height, capacity=bins.n_isect)
+        gsr.gs_bin_tiles(m, q, o, r, d, sc.width, sc.height, capacity=bins.n_isect)
     torch.cuda.synchronize()
     t_bin = (time.perf_counter() - t0) / 3 * 1e3
 
@@ -376,6 +376,7 @@ def main():
         "counts": {"p_walk": p_walk, "p_composited": p_contrib, "walked_entries": entries,
                    "splat_tile_groups": groups_tile, "splat_quadrant_groups": groups_wave,
                    "entry_quadrant_walk": ew_walk, "entry_quadrant_kept": ew_kept, "n_isect": bins.n_isect,
+                   "n_slots": bins.n_slots,
                    "splat_half_groups": groups_half, "splat_block4_groups": groups_blk,
                    "lockstep_half_iters": iters_half, "lockstep_block4_iters": iters_blk},
         "kernel_source_hash": kernel_source_hash(),
@@ -420,7 +421,8 @@ def cpu_baseline(oracle, sc, bins, nc, args, log):
     oracle.set_threads(1)
     for name in ("tiny", "early", "mid"):
         s2 = scenes.make_scene(name, 0)
-        ids2, rng2 = oracle.bin_tiles(s2.means2d, s2.conics, s2.opacities, s2.radii, s2.depths, s2.width, s2.height)
+        ids2, rng2 = oracle.bin_tiles(s2.means2d, s2.conics, s2.opacities, s2.radii, s2.depths, s2.width,
+                                      s2.height)
         c0 = time.perf_counter()
         fo = oracle.rasterize_fwd(s2.means2d, s2.conics, s2.colors, s2.opacities, s2.background, s2.width,
                                   s2.height, rng2, ids2)

@@ -85,16 +85,21 @@ def _pair_count(sorted_ids, n_isect) -> int:
 
 class Bins:
     """Result of gs_bin_tiles: sorted_ids [n_isect] int32, tile_ranges
-    [GX*GY, 2] int32, splat_offsets [n+1] int32 (the numbering of each splat's
-    (splat, tile) pairs that the backward uses for its accumulation slots)."""
+    [GX*GY, 2] int32, splat_offsets [n+1] int32 (the numbering of the tiles of
+    each splat's rectangle that the backward uses for its accumulation slots)
+    and n_slots, the number of those slots (splat_offsets[n]; when not given,
+    the larger of that and n_isect, read from the device)."""
 
-    def __init__(self, sorted_ids, tile_ranges, splat_offsets, n_isect, width, height):
+    def __init__(self, sorted_ids, tile_ranges, splat_offsets, n_isect, width, height, n_slots=None):
         self.sorted_ids = sorted_ids
         self.tile_ranges = tile_ranges
         self.splat_offsets = splat_offsets
         self.n_isect = n_isect
         self.width = width
         self.height = height
+        if n_slots is None:
+            n_slots = max(int(n_isect), int(splat_offsets[-1].item()) if splat_offsets.numel() else 0)
+        self.n_slots = int(n_slots)
 
 
 def _aligned_workspace(nbytes, dev):
@@ -113,19 +118,22 @@ def _workspace(ws, nbytes, dev):
     return ws, ctypes.c_void_p((ws.data_ptr() + 255) & ~255)
 
 
-def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int | None = None,
+def gs_bin_tiles(means2d, conics, opacities, radii, depths, width: int, height: int, capacity: int | None = None,
                  stream=None) -> Bins:
-    """Bin splats into 16x16 tiles and sort each tile's list by depth.
+    """Bin splats into 16x16 tiles (each splat only where its alpha >= 1/255
+    ellipse can reach) and sort each tile's list by depth.
 
-    Allocates sorted_ids with ``capacity`` slots (default: 4 per splat) and,
+    Allocates sorted_ids with ``capacity`` entries (default: 4 per splat) and,
     if the count read back exceeds it, reallocates and calls again."""
     n = int(means2d.shape[0])
     _need(means2d, "means2d", torch.float32, (n, 2))
+    _need(conics, "conics", torch.float32, (n, 3))
+    _need(opacities, "opacities", torch.float32, (n,))
     _need(radii, "radii", torch.int32, (n,))
     _need(depths, "depths", torch.float32, (n,))
     lib = _lib.load()
     dev = means2d.device
-    _same_device(dev, radii=radii, depths=depths)
+    _same_device(dev, conics=conics, opacities=opacities, radii=radii, depths=depths)
     GX, GY = tile_grid(width, height)
     cap = int(capacity) if capacity is not None else max(4 * n, 1)
     ranges = torch.empty((GX * GY, 2), dtype=torch.int32, device=dev)
@@ -135,17 +143,17 @@ def gs_bin_tiles(means2d, radii, depths, width: int, height: int, capacity: int 
         ids = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
         ws_bytes = int(lib.gs_bin_tiles_workspace_size(n, cap, width, height))
         ws, wsp = _aligned_workspace(ws_bytes, dev)
-        n_isect = ctypes.c_int64(0)
+        n_isect, n_slots = ctypes.c_int64(0), ctypes.c_int64(0)
         with torch.cuda.device(dev):
-            status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(radii), _ptr(depths), width, height, cap,
-                                      _ptr(ids), _ptr(ranges), _ptr(offsets), ctypes.byref(n_isect), wsp, ws_bytes,
-                                      st)
+            status = lib.gs_bin_tiles(n, _ptr(means2d), _ptr(conics), _ptr(opacities), _ptr(radii), _ptr(depths),
+                                      width, height, cap, _ptr(ids), _ptr(ranges), _ptr(offsets),
+                                      ctypes.byref(n_isect), ctypes.byref(n_slots), wsp, ws_bytes, st)
         if status == _lib.GS_ERR_CAPACITY:
             cap = int(n_isect.value)
             continue
         _lib.check(status)
         I = int(n_isect.value)
-        return Bins(ids[:I], ranges, offsets, I, width, height)
+        return Bins(ids[:I], ranges, offsets, I, width, height, n_slots=int(n_slots.value))
     raise GsError(_lib.GS_ERR_CAPACITY, "binning capacity still too small after reallocation")
 
 
@@ -296,7 +304,7 @@ def _bwd_args(means2d, conics, colors, opacities, radii, background, width, heig
         flags |= walks[walk]
     return (n, _ptr(means2d), _ptr(conics), _ptr(colors), _ptr(opacities), _ptr(radii), _ptr(background), width,
             height, _ptr(bins.tile_ranges), _ptr(bins.sorted_ids), _ptr(bins.splat_offsets), bins.n_isect,
-            _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
+            bins.n_slots, _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(out["dL_dmeans2d"]), _ptr(out["dL_dconics"]),
             _ptr(out["dL_dcolors"]), _ptr(out["dL_dopacities"]),
             _ptr(out.get("accum_weight") if accum_weight else None), flags)
 
@@ -310,7 +318,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
     the deferred walk), "defer", "add" or "store" (GS_FLAG_WALK_DEFER /
     GS_FLAG_WALK_ADD / GS_FLAG_WALK_STORE). ``out`` may pass preallocated outputs
     (same dict keys) and ``workspace`` a uint8 device buffer of at least
-    gs_rasterize_bwd_workspace_size(n, n_isect, width, height) + 256 bytes, to keep
+    gs_rasterize_bwd_workspace_size(n, bins.n_slots, width, height) + 256 bytes, to keep
     allocation out of timed loops. ``events``: four torch.cuda.Event objects
     (timing enabled, already recorded once) to be recorded at the call's
     stage boundaries (gs_rasterize_bwd_timed)."""
@@ -323,7 +331,7 @@ def gs_rasterize_bwd(means2d, conics, colors, opacities, radii, background, widt
         out = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in _output_shapes(n, accum_weight).items()}
     else:
         _check_outputs(out, n, accum_weight, dev)
-    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_slots, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     args = _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
                      n_contrib, dL_dimage, out, accum_weight, walk) + (wsp, ws_bytes, _stream(stream, dev))
@@ -374,11 +382,11 @@ def gs_rasterize_bwd_depth(means2d, conics, colors, opacities, depths, radii, ba
             _same_device(dev, **{k: out[k]})
     a = _bwd_args(means2d, conics, colors, opacities, radii, background, width, height, bins, final_T,
                   n_contrib, dL_dimage, out, accum_weight, walk)
-    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_isect, width, height))
+    ws_bytes = int(lib.gs_rasterize_bwd_workspace_size(n, bins.n_slots, width, height))
     workspace, wsp = _workspace(workspace, ws_bytes, dev)
     # gs_rasterize_bwd's arguments with the depth inputs and output spliced in
-    args = (a[:5] + (_ptr(depths),) + a[5:15] + (_ptr(dist_totals), _ptr(median_pos), a[15], _ptr(dL_ddist),
-                                                 _ptr(dL_dmedian)) + a[16:20] + (_ptr(out["dL_ddepths"]),) + a[20:]
+    args = (a[:5] + (_ptr(depths),) + a[5:16] + (_ptr(dist_totals), _ptr(median_pos), a[16], _ptr(dL_ddist),
+                                                 _ptr(dL_dmedian)) + a[17:21] + (_ptr(out["dL_ddepths"]),) + a[21:]
             + (wsp, ws_bytes, _stream(stream, dev)))
     with torch.cuda.device(dev):
         _lib.check(lib.gs_rasterize_bwd_depth(*args))
@@ -411,8 +419,8 @@ def gs_rasterize_bwd_noalloc_capacity() -> int:
     return int(_lib.load().gs_rasterize_bwd_noalloc_capacity())
 
 
-def gs_rasterize_bwd_workspace_size(n: int, n_isect: int, width: int, height: int) -> int:
-    return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_isect, width, height))
+def gs_rasterize_bwd_workspace_size(n: int, n_slots: int, width: int, height: int) -> int:
+    return int(_lib.load().gs_rasterize_bwd_workspace_size(n, n_slots, width, height))
 
 
 def gs_rasterize_fwd_workspace_size(n: int) -> int:

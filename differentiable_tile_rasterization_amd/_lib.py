@@ -54,7 +54,8 @@ def load() -> ctypes.CDLL:
     lib.gs_version.restype = ctypes.c_int
     lib.gs_bin_tiles_workspace_size.argtypes = [i32, i64, i32, i32]
     lib.gs_bin_tiles_workspace_size.restype = sz
-    lib.gs_bin_tiles.argtypes = [i32, P, P, P, i32, i32, i64, P, P, P, ctypes.POINTER(i64), P, sz, P]
+    lib.gs_bin_tiles.argtypes = [i32, P, P, P, P, P, i32, i32, i64, P, P, P, ctypes.POINTER(i64),
+                                 ctypes.POINTER(i64), P, sz, P]
     lib.gs_bin_tiles.restype = ctypes.c_int
     lib.gs_rasterize_fwd_workspace_size.argtypes = [i32]
     lib.gs_rasterize_fwd_workspace_size.restype = sz
@@ -65,17 +66,17 @@ def load() -> ctypes.CDLL:
     lib.gs_rasterize_fwd_depth.restype = ctypes.c_int
     lib.gs_rasterize_bwd_workspace_size.argtypes = [i32, i64, i32, i32]
     lib.gs_rasterize_bwd_workspace_size.restype = sz
-    lib.gs_rasterize_bwd.argtypes = [i32, P, P, P, P, P, P, i32, i32, P, P, P, i64, P, P, P,
+    lib.gs_rasterize_bwd.argtypes = [i32, P, P, P, P, P, P, i32, i32, P, P, P, i64, i64, P, P, P,
                                      P, P, P, P, P, u32, P, sz, P]
     lib.gs_rasterize_bwd.restype = ctypes.c_int
-    lib.gs_rasterize_bwd_depth.argtypes = [i32, P, P, P, P, P, P, P, i32, i32, P, P, P, i64, P, P, P, P,
+    lib.gs_rasterize_bwd_depth.argtypes = [i32, P, P, P, P, P, P, P, i32, i32, P, P, P, i64, i64, P, P, P, P,
                                            P, P, P, P, P, P, P, P, P, u32, P, sz, P]
     lib.gs_rasterize_bwd_depth.restype = ctypes.c_int
     lib.gs_rasterize_bwd_timed.argtypes = lib.gs_rasterize_bwd.argtypes + [ctypes.POINTER(P)]
     lib.gs_rasterize_bwd_timed.restype = ctypes.c_int
     lib.gs_rasterize_bwd_noalloc_capacity.argtypes = []
     lib.gs_rasterize_bwd_noalloc_capacity.restype = sz
-    lib.gs_rasterize_bwd_noalloc.argtypes = lib.gs_rasterize_bwd.argtypes[:22] + [P]
+    lib.gs_rasterize_bwd_noalloc.argtypes = lib.gs_rasterize_bwd.argtypes[:23] + [P]
     lib.gs_rasterize_bwd_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -3,18 +3,21 @@
 // Stages (the binning / sort / range kernels of the 3dgs-rs pipeline listed in
 // the timing table of "Phase 5 step 30b — kernel-by-kernel timing", section
 // 計測結果: emit_pairs, radix_hist, radix_scatter, extract_offsets):
-//   1. count   one thread per splat: float32 tile rectangle, number of tiles
-//   2. scan    exclusive prefix sum of the counts in splat order (device-wide,
-//              32-bit items and offsets, sums and the total in 64 bits): each
-//              splat's first pair slot, splat_offsets
-//   3. host    read the total back (the call's only synchronisation; the
+//   1. count   one thread per splat: float32 tile rectangle and its number
+//              of tiles; the number of them the splat's culling ellipse
+//              (alpha >= 1/255) keeps, row by row
+//   2. scan    exclusive prefix sum of the rectangle counts in splat order
+//              (device-wide, 32-bit items and offsets, sums and the total in
+//              64 bits): each splat's first pair slot, splat_offsets; and the
+//              total of the kept counts
+//   3. host    read both totals back (the call's only synchronisation; the
 //              depth sort is already queued behind the copy)
 //   4. depth   stable LSD radix sort of the splats by the bit pattern of their
 //              depth (32 bits, 8-bit digits), splat ids starting in id order
-//   5. emit    the splats' tile rectangles (stored by the count pass) and
+//   5. emit    the splats' tile rectangles (stored by the count pass) and kept
 //              counts gathered into depth order and scanned; the splat of
-//              depth rank k writes its tiles, row-major, at that offset, as
-//              (tile id, splat id), tile ids 16-bit up to 65536 tiles
+//              depth rank k writes its kept tiles, row-major, at that offset,
+//              as (tile id, splat id), tile ids 16-bit up to 65536 tiles
 //   6. tiles   stable LSD radix sort of the pairs by tile id over only the
 //              ceil(log2(tiles)) bits it can have, split as evenly as possible
 //              over as few passes as 8-bit digits allow, narrower digits first
@@ -58,13 +61,115 @@ __device__ __forceinline__ bool splat_rect(float mx, float my, int r, float dept
     return live && tx1 > tx0 && ty1 > ty0;
 }
 
-// counts[i] = number of tiles of splat i; rects[i] = its tile rectangle
-// (tx0, ty0, tx1, ty1), empty for a culled splat. A grid has at most 2048
-// tiles per side, so 16 bits per bound suffice.
+// ---------------------------------------------------------------------------
+// The culling ellipse. A splat reaches alpha >= 1/255 only where its quadratic
+// form Q = a dx^2 + 2 b dx dy + c dy^2 is at most 2 ln(255 o); a tile of the
+// rectangle is kept only if the ellipse {Q <= T} meets the tile's pixel-centre
+// rectangle, T an upper bound on 2 ln(255 o). Everything here is float32 with
+// each operation rounded once, in the order written (no fused multiply-adds;
+// division and square root correctly rounded), so the decisions are those of
+// any IEEE float32 evaluation of the same expressions:
+//   255 o = m2 2^e2, m2 in [1, 2):  ln(255 o) <= e2 ln 2 + (m2 - 1) / sqrt(m2)
+//   (ln x <= (x - 1) / sqrt(x) for x >= 1; ln 2 taken as float32 ln 2, which
+//   rounds up), T = 2 lnb (1 + 2^-10) + 2^-10 (a margin for the rounding of Q
+//   in the compositing);
+//   Q = (l11 u + l21 v)^2 + (l22 v)^2 with the conic's Cholesky factors
+//   l11 = sqrt(a), l21 = b / l11, l22 = sqrt(max(c - l21^2, 0)), u = x - mean_x,
+//   v = y - mean_y;
+//   per tile row, over its band of pixel centres v in [v0, v0 + 15]: the
+//   ellipse's left end u = (-l21 v - sqrt(T - (l22 v)^2)) / l11 is convex in v,
+//   least at the leftmost point's v = vL = sqrt(T) l21 / (l22 sqrt(l21^2 +
+//   l22^2)), so it is taken at vL clamped to the band (and to |v| <= vmax =
+//   sqrt(T) / l22); the right end likewise at -vL. Column c (pixel centres
+//   16 c + 0.5 .. 16 c + 15.5) is kept iff 16 c + 15.5 >= x_left and
+//   16 c + 0.5 <= x_right.
+// A splat whose float32 product 255 o is below 1 is kept nowhere (alpha <= o <
+// 1/255); one whose factors are not finite and positive keeps its whole
+// rectangle.
+// ---------------------------------------------------------------------------
+enum : int { kCullNone = 0, kCullRect = 1, kCullRows = 2 };
+
+struct CullEllipse {
+    float mx, my, l11, l21, l22, T, vmax, vL;
+    int mode;
+};
+
+__device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
+
+__device__ __attribute__((noinline)) CullEllipse cull_ellipse(float2 m, float a, float b, float c, float o)
+{
+#pragma clang fp contract(off)
+    CullEllipse E{};
+    E.mx = m.x;
+    E.my = m.y;
+    const float y = 255.0f * o;
+    if (!(y >= 1.0f)) {  // also NaN
+        E.mode = kCullNone;
+        return E;
+    }
+    // y = m2 2^e2 from its bit pattern (y >= 1 is normal; an infinite y gives
+    // an unusable ellipse below)
+    const unsigned yb = __float_as_uint(y);
+    const float e2 = (float)((int)(yb >> 23) - 127);
+    const float m2 = __uint_as_float((yb & 0x7fffffu) | 0x3f800000u);
+    const float ln2_up = 0x1.62e430p-1f;  // float32 nearest ln 2, above it
+    const float lnb = e2 * ln2_up + (m2 - 1.0f) / __builtin_sqrtf(m2);
+    float T = 2.0f * lnb;
+    T = (T + T * 0x1p-10f) + 0x1p-10f;
+    E.T = T;
+    E.l11 = __builtin_sqrtf(a);
+    E.l21 = b / E.l11;
+    E.l22 = __builtin_sqrtf(fmaxf(c - E.l21 * E.l21, 0.0f));
+    const float sT = __builtin_sqrtf(T);
+    E.vmax = sT / E.l22;
+    const float nrm = __builtin_sqrtf(E.l21 * E.l21 + E.l22 * E.l22);
+    E.vL = (sT * E.l21) / (E.l22 * nrm);
+    const bool usable = finite_f(y) && finite_f(T) && finite_f(E.l11) && finite_f(E.l21) && finite_f(E.l22) &&
+                        finite_f(E.vmax) && finite_f(E.vL) && E.l11 > 0.0f && E.l22 > 0.0f && finite_f(m.x) &&
+                        finite_f(m.y);
+    E.mode = usable ? kCullRows : kCullRect;
+    return E;
+}
+
+// The kept columns [x, y] of tile row ty within [tx0, tx1) (x > y: none).
+__device__ __attribute__((noinline)) int2 cull_row(const CullEllipse& E, int ty, int tx0, int tx1)
+{
+#pragma clang fp contract(off)
+    if (E.mode != kCullRows) return E.mode == kCullRect ? make_int2(tx0, tx1 - 1) : make_int2(tx1, tx1 - 1);
+    const float v0 = ((float)ty * 16.0f + 0.5f) - E.my;
+    const float v1 = v0 + 15.0f;
+    const float lo = fmaxf(v0, -E.vmax), hi = fminf(v1, E.vmax);
+    if (!(lo <= hi)) return make_int2(tx1, tx1 - 1);
+    const float vl = fminf(fmaxf(E.vL, lo), hi);
+    const float vr = fminf(fmaxf(-E.vL, lo), hi);
+    const float tl = E.l22 * vl;
+    const float sl = __builtin_sqrtf(fmaxf(E.T - tl * tl, 0.0f));
+    const float xl = E.mx + (-(E.l21 * vl) - sl) / E.l11;
+    const float tr = E.l22 * vr;
+    const float sr = __builtin_sqrtf(fmaxf(E.T - tr * tr, 0.0f));
+    const float xr = E.mx + (-(E.l21 * vr) + sr) / E.l11;
+    const float f0 = (float)tx0, f1 = (float)tx1;
+    // smallest c with 16 c + 15.5 >= xl, largest with 16 c + 0.5 <= xr: an
+    // estimate clamped near the rectangle, then corrected by one either way
+    float cl = fminf(fmaxf(ceilf((xl - 15.5f) * 0.0625f), f0 - 1.0f), f1 + 1.0f);
+    if ((cl - 1.0f) * 16.0f + 15.5f >= xl) cl = cl - 1.0f;
+    if (cl * 16.0f + 15.5f < xl) cl = cl + 1.0f;
+    float ch = fminf(fmaxf(floorf((xr - 0.5f) * 0.0625f), f0 - 2.0f), f1);
+    if ((ch + 1.0f) * 16.0f + 0.5f <= xr) ch = ch + 1.0f;
+    if (ch * 16.0f + 0.5f > xr) ch = ch - 1.0f;
+    return make_int2(max((int)cl, tx0), min((int)ch, tx1 - 1));
+}
+
+// counts[i] = number of tiles of splat i's rectangle, kept[i] = the number of
+// them its culling ellipse keeps; rects[i] = the rectangle (tx0, ty0, tx1,
+// ty1), empty for a culled splat. A grid has at most 2048 tiles per side, so
+// 16 bits per bound suffice.
 __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
+                                                    const float* __restrict__ conics,
+                                                    const float* __restrict__ opacities,
                                                     const int* __restrict__ radii,
                                                     const float* __restrict__ depths, int GX, int GY,
-                                                    unsigned* __restrict__ counts,
+                                                    unsigned* __restrict__ counts, unsigned* __restrict__ kept,
                                                     ushort4* __restrict__ rects)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -72,7 +177,16 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
     const float2 m = means[i];
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
+    unsigned k = 0;
+    if (live) {
+        const CullEllipse E = cull_ellipse(m, conics[3 * i], conics[3 * i + 1], conics[3 * i + 2], opacities[i]);
+        for (int ty = ty0; ty < ty1; ++ty) {
+            const int2 cr = cull_row(E, ty, tx0, tx1);
+            k += cr.y >= cr.x ? (unsigned)(cr.y - cr.x + 1) : 0u;
+        }
+    }
     counts[i] = live ? (unsigned)((tx1 - tx0) * (ty1 - ty0)) : 0u;  // at most 2048 x 2048
+    kept[i] = k;
     rects[i] = live ? make_ushort4((unsigned short)tx0, (unsigned short)ty0, (unsigned short)tx1,
                                    (unsigned short)ty1)
                     : make_ushort4(0, 0, 0, 0);
@@ -174,85 +288,44 @@ hipError_t exclusive_scan(const unsigned* in, unsigned* out, long long n, unsign
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __restrict__ by_depth,
                                                            const ushort4* __restrict__ rects,
+                                                           const unsigned* __restrict__ kept,
                                                            ushort4* __restrict__ rect_sorted,
                                                            unsigned* __restrict__ cnt_sorted)
 {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
-    const ushort4 rc = rects[by_depth[k]];
-    rect_sorted[k] = rc;
-    cnt_sorted[k] = (unsigned)(rc.z - rc.x) * (unsigned)(rc.w - rc.y);
+    const int i = by_depth[k];
+    rect_sorted[k] = rects[i];
+    cnt_sorted[k] = kept[i];
 }
 
-// Emission: one wave per 64 consecutive depth ranks. Their pairs are
-// contiguous, [emit_off[k0], emit_off[k0 + 64]), and the wave writes them
-// together, one pair per lane per step (coalesced): the splat of depth rank k
-// writes its tiles, row-major, from emit_off[k], as (tile id, splat id). At
-// each step of 64 pairs, every splat whose first pair falls in the step marks
-// that position with its lane (non-empty splats start at distinct positions),
-// and an inclusive max-scan over the lanes, seeded with the previous step's
-// last owner, gives each position its splat. The row inside the splat's
-// rectangle comes from a float quotient corrected by one (rel < 2^22 and the
-// width <= 2048, so the estimate is within one of the quotient).
-__device__ __forceinline__ int wave_max_scan(int x)  // inclusive, ascending lanes, x >= 0
-{
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));  // row_shr:4
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));  // row_shr:8
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15 into rows 1, 3
-    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31 into rows 2, 3
-    return x;
-}
-
+// Emission: one thread per depth rank k. The splat of rank k writes its kept
+// tiles, row by row and left to right, from emit_off[k], as (tile id, splat
+// id); the kept count taken by the count pass (the same ellipse function on
+// the same inputs) bounds the writes.
 template <typename K>
-__global__ __launch_bounds__(kWave) void emit_kernel(int n, long long n_pairs, const int* __restrict__ by_depth,
-                                                     const ushort4* __restrict__ rect_sorted,
-                                                     const unsigned* __restrict__ emit_off, int GX,
-                                                     K* __restrict__ keys, int* __restrict__ vals)
+__global__ __launch_bounds__(256) void emit_kernel(int n, const int* __restrict__ by_depth,
+                                                   const ushort4* __restrict__ rect_sorted,
+                                                   const unsigned* __restrict__ cnt_sorted,
+                                                   const unsigned* __restrict__ emit_off,
+                                                   const float2* __restrict__ means, const float* __restrict__ conics,
+                                                   const float* __restrict__ opacities, int GX,
+                                                   K* __restrict__ keys, int* __restrict__ vals)
 {
-    __shared__ ushort4 rc[kWave];
-    __shared__ unsigned rstart[kWave];  // first pair of the lane's splat, relative to the wave's first
-    __shared__ int sid[kWave];
-    __shared__ int mark[kWave];         // per step: 1 + lane of the splat starting at the position, or 0
-    const int lane = threadIdx.x;
-    const int k0 = blockIdx.x * kWave, k = k0 + lane;
-    // the pair count is below 2^31 here (checked before emission)
-    const unsigned my_off = k < n ? emit_off[k] : (unsigned)n_pairs;
-    const unsigned p0 = emit_off[k0];
-    const unsigned p1 = k0 + kWave < n ? emit_off[k0 + kWave] : (unsigned)n_pairs;
-    const ushort4 b = k < n ? rect_sorted[k] : make_ushort4(0, 0, 0, 0);
-    const unsigned my_cnt = (unsigned)(b.z - b.x) * (unsigned)(b.w - b.y);
-    const unsigned my_rel = my_off - p0;
-    rc[lane] = b;
-    rstart[lane] = my_rel;
-    sid[lane] = k < n ? by_depth[k] : 0;
-    const unsigned total = p1 - p0;
-    int carry = 0;
-    for (unsigned q = 0; q < total; q += kWave) {
-        mark[lane] = 0;
-        __syncthreads();
-        if (my_cnt > 0 && my_rel >= q && my_rel - q < (unsigned)kWave) mark[my_rel - q] = lane + 1;
-        __syncthreads();
-        const int o = max(wave_max_scan(mark[lane]), carry);
-        carry = __builtin_amdgcn_readlane(o, kWave - 1);
-        const unsigned rel_p = q + (unsigned)lane;
-        if (rel_p < total) {
-            const int s = o - 1;
-            const ushort4 bs = rc[s];
-            const unsigned rel = rel_p - rstart[s], wdt = (unsigned)(bs.z - bs.x);
-            int row = (int)((float)rel * __builtin_amdgcn_rcpf((float)wdt));
-            int col = (int)rel - row * (int)wdt;
-            if (col < 0) {
-                --row;
-                col += (int)wdt;
-            } else if (col >= (int)wdt) {
-                ++row;
-                col -= (int)wdt;
-            }
-            const unsigned p = p0 + rel_p;
-            keys[p] = (K)((bs.y + row) * GX + bs.x + col);
-            vals[p] = sid[s];
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const unsigned cnt = cnt_sorted[k];
+    if (cnt == 0) return;
+    const int i = by_depth[k];
+    const ushort4 b = rect_sorted[k];
+    unsigned p = emit_off[k];  // the pair count is below 2^31 here (checked before emission)
+    const unsigned pend = p + cnt;
+    const CullEllipse E = cull_ellipse(means[i], conics[3 * i], conics[3 * i + 1], conics[3 * i + 2], opacities[i]);
+    for (int ty = b.y; ty < (int)b.w && p < pend; ++ty) {
+        const int2 cr = cull_row(E, ty, b.x, b.z);
+        for (int c = cr.x; c <= cr.y && p < pend; ++c, ++p) {
+            keys[p] = (K)(ty * GX + c);
+            vals[p] = i;
         }
     }
 }
@@ -433,7 +506,7 @@ struct alignas(4 * sizeof(K)) Keys4 {
 };
 
 template <typename K>
-__global__ __launch_bounds__(256) void ranges_kernel(const K* __restrict__ keys, long long n,
+__global__ __launch_bounds__(256) void ranges_kernel(const K* __restrict__ keys, long long n, int tiles,
                                                      int2* __restrict__ ranges)
 {
     const long long i0 = 4 * ((long long)blockIdx.x * blockDim.x + threadIdx.x);
@@ -454,9 +527,10 @@ __global__ __launch_bounds__(256) void ranges_kernel(const K* __restrict__ keys,
         const long long i = i0 + j;
         if (i >= n) break;
         const int t = k[j];
-        if (t != prev) ranges[t].x = (int)i;
+        const bool in = (unsigned)t < (unsigned)tiles;  // every emitted key is; bounds the writes regardless
+        if (t != prev && in) ranges[t].x = (int)i;
         const int nx = j < 3 && i + 1 < n ? k[j + 1] : (j < 3 ? -1 : next);
-        if (nx != t) ranges[t].y = (int)(i + 1);
+        if (nx != t && in) ranges[t].y = (int)(i + 1);
         prev = t;
     }
 }
@@ -477,7 +551,7 @@ __global__ __launch_bounds__(256) void outputs_kernel(int n, int tiles, const un
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BinLayout {
-    size_t counts, rects, offsets, part, total, pairs, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted,
+    size_t counts, kept, rects, offsets, part, total, pairs, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted,
         cnt_sorted, emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
 };
 
@@ -491,11 +565,12 @@ BinLayout bin_layout(long long n, long long cap)
     const long long nparts = (scan_items + kScanTile - 1) / kScanTile + 1;
     const size_t n1 = (size_t)(n > 0 ? n : 1), c1 = (size_t)(cap > 0 ? cap : 1);
     L.counts = o;     o += align256(sizeof(unsigned) * n1);
+    L.kept = o;       o += align256(sizeof(unsigned) * n1);
     L.rects = o;      o += align256(sizeof(ushort4) * n1);
     L.offsets = o;    o += align256(sizeof(unsigned) * n1);
     L.part = o;       o += align256(sizeof(unsigned long long) * (size_t)nparts);
     L.total = o;      o += align256(sizeof(unsigned long long));
-    L.pairs = o;      o += align256(sizeof(unsigned long long));  // the pair count, kept apart from the scans' totals
+    L.pairs = o;      o += align256(2 * sizeof(unsigned long long));  // rectangle and kept pair counts, apart from the scans' totals
     L.dkeys_a = o;    o += align256(sizeof(unsigned) * n1);
     L.dkeys_b = o;    o += align256(sizeof(unsigned) * n1);
     L.dvals_a = o;    o += align256(sizeof(int) * n1);
@@ -544,16 +619,18 @@ hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long lon
 // Emission, the tile passes (ping-ponged so that the last one writes its
 // values into sorted_ids) and the ranges, with keys of type K.
 template <typename K>
-hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rect_sorted,
-                     const unsigned* emit_off, int GX, int np, int tb, K* keys_a, K* keys_b, int* vals_t,
-                     int* sorted_ids, unsigned* hist, unsigned long long* part, unsigned long long* total,
-                     int2* tile_ranges, hipStream_t st)
+hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rect_sorted, const unsigned* cnt_sorted,
+                     const unsigned* emit_off, const float2* means, const float* conics, const float* opacities,
+                     int GX, int tiles, int np, int tb, K* keys_a, K* keys_b, int* vals_t, int* sorted_ids,
+                     unsigned* hist, unsigned long long* part, unsigned long long* total, int2* tile_ranges,
+                     hipStream_t st)
 {
     K* kin = keys_a;
     K* kout = keys_b;
     int* vin = (np % 2 == 0) ? sorted_ids : vals_t;
     int* vout = (np % 2 == 0) ? vals_t : sorted_ids;
-    emit_kernel<K><<<(n + kWave - 1) / kWave, kWave, 0, st>>>(n, I, by_depth, rect_sorted, emit_off, GX, kin, vin);
+    emit_kernel<K><<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rect_sorted, cnt_sorted, emit_off, means, conics,
+                                                    opacities, GX, kin, vin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int shift = 0;
@@ -567,7 +644,7 @@ hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rec
         K* tk = kin; kin = kout; kout = tk;
         int* tv = vin; vin = vout; vout = tv;
     }
-    ranges_kernel<K><<<(unsigned)((I + 1023) / 1024), 256, 0, st>>>(kin, I, tile_ranges);
+    ranges_kernel<K><<<(unsigned)((I + 1023) / 1024), 256, 0, st>>>(kin, I, tiles, tile_ranges);
     return hipGetLastError();
 }
 
@@ -624,10 +701,11 @@ struct CountEvent {  // destroyed on every return path
 
 using namespace gs;
 
-extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
-                                  int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
-                                  int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect,
-                                  void* workspace, size_t workspace_bytes, gs_stream_t stream_)
+extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* conics, const float* opacities,
+                                  const int32_t* radii, const float* depths, int32_t width, int32_t height,
+                                  int64_t capacity, int32_t* sorted_ids, int32_t* tile_ranges,
+                                  int32_t* splat_offsets, int64_t* n_isect, int64_t* n_slots, void* workspace,
+                                  size_t workspace_bytes, gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
     GS_CHECK_ARG(n >= 0, "gs_bin_tiles: n = %d < 0", n);
@@ -637,7 +715,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     GS_CHECK_ARG(n_isect != nullptr, "gs_bin_tiles: n_isect is NULL");
     GS_CHECK_ARG(tile_ranges != nullptr, "gs_bin_tiles: tile_ranges is NULL");
     GS_CHECK_ARG(splat_offsets != nullptr, "gs_bin_tiles: splat_offsets is NULL");
-    GS_CHECK_ARG(n == 0 || (means2d && radii && depths), "gs_bin_tiles: NULL splat array");
+    GS_CHECK_ARG(n == 0 || (means2d && conics && opacities && radii && depths), "gs_bin_tiles: NULL splat array");
     GS_CHECK_ARG(capacity == 0 || sorted_ids != nullptr, "gs_bin_tiles: sorted_ids is NULL");
     const BinLayout L = bin_layout(n, capacity);
     GS_CHECK_ARG(workspace != nullptr && workspace_bytes >= L.bytes,
@@ -648,12 +726,13 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     const int tiles = GX * GY;
     char* ws = (char*)workspace;
     auto* counts = (unsigned*)(ws + L.counts);
+    auto* kept = (unsigned*)(ws + L.kept);
     auto* offsets = (unsigned*)(ws + L.offsets);
     auto* part = (unsigned long long*)(ws + L.part);
     auto* total = (unsigned long long*)(ws + L.total);
     auto* rects = (ushort4*)(ws + L.rects);
 
-    auto* pairs = (unsigned long long*)(ws + L.pairs);
+    auto* pairs = (unsigned long long*)(ws + L.pairs);  // [0] rectangle pairs, [1] kept pairs
     auto* dka = (unsigned*)(ws + L.dkeys_a);
     auto* dkb = (unsigned*)(ws + L.dkeys_b);
     auto* dva = (int*)(ws + L.dvals_a);
@@ -664,25 +743,28 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     auto* emit_off = (unsigned*)(ws + L.emit_off);
     const int* by_depth = dva;
 
-    // The pair count is read back with an asynchronous copy into pinned host
-    // memory, and everything that does not need it (the splats' depth sort
-    // and their rectangles in depth order; workspace only) is enqueued before
-    // the host waits for that copy: the GPU stays busy while the host waits
-    // and then enqueues the pair stages behind the depth sort.
-    unsigned long long h_total = 0;
+    // Both pair counts are read back with one asynchronous copy into pinned
+    // host memory, and everything that does not need them (the splats' depth
+    // sort and their rectangles and kept counts in depth order; workspace
+    // only) is enqueued before the host waits for that copy: the GPU stays
+    // busy while the host waits and then enqueues the pair stages behind the
+    // depth sort.
+    unsigned long long h_tot[2] = {0, 0};
     if (n > 0) {
-        count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, radii, depths, GX, GY, counts,
-                                                      rects);
+        count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, opacities, radii, depths,
+                                                      GX, GY, counts, kept, rects);
         GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(counts, offsets, n, part, pairs, st));
+        // the kept total (the scan's output goes to emit_off, rewritten below)
+        GS_HIP(exclusive_scan(kept, emit_off, n, part, pairs + 1, st));
         unsigned long long* pin = pinned_count();
         CountEvent ev;
         if (pin) {
-            GS_HIP(hipMemcpyAsync(pin, pairs, sizeof(*pin), hipMemcpyDeviceToHost, st));
+            GS_HIP(hipMemcpyAsync(pin, pairs, 2 * sizeof(*pin), hipMemcpyDeviceToHost, st));
             GS_HIP(hipEventCreateWithFlags(&ev.e, hipEventDisableTiming));
             GS_HIP(hipEventRecord(ev.e, st));
         } else {  // no pinned buffer: a plain synchronous read
-            GS_HIP(hipMemcpyAsync(&h_total, pairs, sizeof(h_total), hipMemcpyDeviceToHost, st));
+            GS_HIP(hipMemcpyAsync(h_tot, pairs, sizeof(h_tot), hipMemcpyDeviceToHost, st));
             GS_HIP(hipStreamSynchronize(st));
         }
         // Splats in depth order: stable sort of (depth bits, id). The first
@@ -701,24 +783,26 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
         }
         by_depth = dv_in;
         // Emission offsets in depth order.
-        gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, rect_sorted, cnt_sorted);
+        gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, kept, rect_sorted, cnt_sorted);
         GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(cnt_sorted, emit_off, n, part, total, st));
         if (pin) {
             GS_HIP(hipEventSynchronize(ev.e));
-            h_total = *pin;
+            h_tot[0] = pin[0];
+            h_tot[1] = pin[1];
         }
     }
-    *n_isect = (int64_t)h_total;
-    if (h_total > 0x7fffffffull) {
-        set_error("gs_bin_tiles: %llu intersections exceed the int32 index range", h_total);
+    *n_isect = (int64_t)h_tot[1];
+    if (n_slots) *n_slots = (int64_t)h_tot[0];
+    if (h_tot[0] > 0x7fffffffull) {  // the kept pairs are among them
+        set_error("gs_bin_tiles: %llu rectangle pairs exceed the int32 index range", h_tot[0]);
         return GS_ERR_UNSUPPORTED;
     }
-    if ((long long)h_total > capacity) {
-        set_error("gs_bin_tiles: capacity %lld < %llu intersections", (long long)capacity, h_total);
+    if ((long long)h_tot[1] > capacity) {
+        set_error("gs_bin_tiles: capacity %lld < %llu intersections", (long long)capacity, h_tot[1]);
         return GS_ERR_CAPACITY;
     }
-    const long long I = (long long)h_total;
+    const long long I = (long long)h_tot[1];
     {
         const long long cover = (long long)n + 1 > 2ll * tiles ? (long long)n + 1 : 2ll * tiles;
         outputs_kernel<<<(unsigned)((cover + 255) / 256), 256, 0, st>>>(n, tiles, offsets, n > 0 ? pairs : nullptr,
@@ -736,14 +820,16 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t
     const int np = (tb + kRadixBits - 1) / kRadixBits;
 
     int* vals_t = (int*)(ws + L.vals_tmp);
+    const float2* m2 = (const float2*)means2d;
     // 16-bit tile keys up to 65536 tiles (a quarter less traffic per pass)
     if (tiles <= 65536)
-        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, rect_sorted, emit_off, GX, np, tb,
-                                         (unsigned short*)(ws + L.keys_a), (unsigned short*)(ws + L.keys_b), vals_t,
-                                         sorted_ids, hist, part, total, (int2*)tile_ranges, st));
+        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, rect_sorted, cnt_sorted, emit_off, m2, conics, opacities, GX,
+                                         tiles, np, tb, (unsigned short*)(ws + L.keys_a),
+                                         (unsigned short*)(ws + L.keys_b), vals_t, sorted_ids, hist, part, total,
+                                         (int2*)tile_ranges, st));
     else
-        GS_HIP(tile_sort<unsigned>(n, I, by_depth, rect_sorted, emit_off, GX, np, tb, (unsigned*)(ws + L.keys_a),
-                                   (unsigned*)(ws + L.keys_b), vals_t, sorted_ids, hist, part, total,
-                                   (int2*)tile_ranges, st));
+        GS_HIP(tile_sort<unsigned>(n, I, by_depth, rect_sorted, cnt_sorted, emit_off, m2, conics, opacities, GX, tiles,
+                                   np, tb, (unsigned*)(ws + L.keys_a), (unsigned*)(ws + L.keys_b), vals_t,
+                                   sorted_ids, hist, part, total, (int2*)tile_ranges, st));
     return GS_OK;
 }

@@ -316,7 +316,7 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
 template <bool AW>
 __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
-    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_isect, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
     unsigned char* __restrict__ slot_used)
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
+    const int2 rg = clamp_range(ranges[tile], n_isect);  // a range past the pair list reads nothing wild
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 template <bool AW, int NB, int KC, int WG, int DEP>
 __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
-    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_isect, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
     unsigned char* __restrict__ slot_used, DepthIn dz)
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
+    const int2 rg = clamp_range(ranges[tile], n_isect);  // a range past the pair list reads nothing wild
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
@@ -1182,7 +1182,7 @@ __device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool
 template <bool AW>
 __global__ __launch_bounds__(kBlock) void bwd_kernel(
     int W, int H, int GX, int GY, int tiles, int n, const int2* __restrict__ ranges, const int* __restrict__ ids,
-    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_slots,
+    const SplatRec* __restrict__ recs, const int* __restrict__ splat_offsets, long long n_isect, long long n_slots,
     const float* __restrict__ bg, const float* __restrict__ final_T, const int* __restrict__ n_contrib,
     const float* __restrict__ dimg, const int* __restrict__ order, float4* __restrict__ rec_out,
     unsigned char* __restrict__ slot_used)
@@ -1201,7 +1201,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     const bool inside = x < W && y < H;
     const float px = (float)x + 0.5f, py = (float)y + 0.5f;
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
-    const int2 rg = clamp_range(ranges[tile], n_slots);  // a range past the pair list reads nothing wild
+    const int2 rg = clamp_range(ranges[tile], n_isect);  // a range past the pair list reads nothing wild
 
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
@@ -2243,10 +2243,10 @@ extern "C" gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, con
                     median_depth, median_pos, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
-extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height)
+extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_slots, int32_t width, int32_t height)
 {
-    if (n < 0 || n_isect < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
-    return layout(n > 0 ? n : 1, n_isect, (long long)grid_x(width) * grid_y(height)).bytes;
+    if (n < 0 || n_slots < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
+    return layout(n > 0 ? n : 1, n_slots, (long long)grid_x(width) * grid_y(height)).bytes;
 }
 
 namespace {
@@ -2255,8 +2255,8 @@ namespace {
 gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const float* colors,
                    const float* opacities, const int32_t* radii, const float* background, int32_t width,
                    int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                   const int32_t* splat_offsets, int64_t n_isect, const float* final_T, const int32_t* n_contrib,
-                   const float* dL_dimage, float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                   const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots, const float* final_T,
+                   const int32_t* n_contrib, const float* dL_dimage, float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                    float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                    size_t workspace_bytes, gs_stream_t stream_, const gs_event_t* events, int dep = 0,
                    DepthIn dz = DepthIn{}, float* dL_ddepths = nullptr)
@@ -2268,6 +2268,9 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
     };
     GS_CHECK_ARG(n >= 0, "gs_rasterize_bwd: n = %d < 0", n);
     GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "gs_rasterize_bwd: n_isect = %lld out of range",
+                 (long long)n_isect);
+    GS_CHECK_ARG(n_slots >= n_isect && n_slots <= 0x7fffffffll,
+                 "gs_rasterize_bwd: n_slots = %lld outside n_isect .. 2^31 - 1 (n_isect = %lld)", (long long)n_slots,
                  (long long)n_isect);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
                  "gs_rasterize_bwd: image size %d x %d outside 1..%d", width, height, kMaxDim);
@@ -2302,7 +2305,7 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         }
     }
     const int GX = grid_x(width), GY = grid_y(height), tiles = GX * GY;
-    const Layout L = layout(n, n_isect, tiles);
+    const Layout L = layout(n, n_slots, tiles);
     GS_CHECK_ARG(n == 0 || (workspace && workspace_bytes >= L.bytes),
                  "gs_rasterize_bwd: workspace %zu bytes, need %zu", workspace_bytes, L.bytes);
     GS_CHECK_ARG(n == 0 || ((uintptr_t)workspace & 255) == 0, "gs_rasterize_bwd: workspace not 256-byte aligned");
@@ -2314,13 +2317,16 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         return GS_OK;
     }
     SplatRec* recs = (SplatRec*)((char*)workspace + L.recs);
-    float4* slots = n_isect ? (float4*)((char*)workspace + L.slots) : nullptr;
-    unsigned char* used = n_isect ? (unsigned char*)workspace + L.used : nullptr;
+    // without pairs no slot is written (nor its flag cleared): the gather then
+    // sees no slots at all
+    const long long n_slots_live = n_isect > 0 ? n_slots : 0;
+    float4* slots = n_slots_live ? (float4*)((char*)workspace + L.slots) : nullptr;
+    unsigned char* used = n_slots_live ? (unsigned char*)workspace + L.used : nullptr;
     int* cost = (int*)((char*)workspace + L.cost);
     int* order = (int*)((char*)workspace + L.order);
     if (n_isect > 0) {
         // flags cleared in whole 16-byte units (the region is padded)
-        const long long n16 = (n_isect + 15) >> 4;
+        const long long n16 = (n_slots + 15) >> 4;
         const int cost_blocks = (tiles + 3) / 4, rec_blocks = (n + 255) / 256;
         const long long blocks = (long long)cost_blocks + rec_blocks + (n16 + 255) / 256;
         bwd_setup_kernel<<<(unsigned)blocks, 256, 0, st>>>(
@@ -2333,7 +2339,8 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
         const int* ord = order;
         auto launch = [&](auto kernel, auto... extra) {
             kernel<<<xcd_grid(tiles), kBlock, 0, st>>>(width, height, GX, GY, tiles, n, (const int2*)tile_ranges,
-                                                       sorted_ids, recs, splat_offsets, n_isect, background,
+                                                       sorted_ids, recs, splat_offsets, n_isect, n_slots,
+                                                       background,
                                                        final_T, n_contrib, dL_dimage, ord, slots, used, extra...);
         };
         // the deferred walk: one instance per (weight, batch size, depth terms)
@@ -2367,10 +2374,10 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
     const uint4* flags16 = reinterpret_cast<const uint4*>(used);  // padded to whole 16-byte units
     const unsigned gb = (unsigned)((n + kWave - 1) / kWave);
 #define GS_GATHER(K, AWV, ACC, DZV, DD)                                                                            \
-    K<AWV, DZV><<<gb, kWave, 0, st>>>(n, splat_offsets, n_isect, slots, flags16, conics, opacities,                   \
+    K<AWV, DZV><<<gb, kWave, 0, st>>>(n, splat_offsets, n_slots_live, slots, flags16, conics, opacities,              \
                                       (float2*)dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities, ACC, DD)
     const bool dzo = dep != 0;
-    if (n_isect <= (long long)kGatherRegMaxPairs * n) {
+    if (n_slots_live <= (long long)kGatherRegMaxPairs * n) {
         if (aw) dzo ? GS_GATHER(gather_kernel, true, accum_weight, true, dL_ddepths)
                     : GS_GATHER(gather_kernel, true, accum_weight, false, nullptr);
         else dzo ? GS_GATHER(gather_kernel, false, nullptr, true, dL_ddepths)
@@ -2391,14 +2398,14 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
 extern "C" gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                                       const float* opacities, const int32_t* radii, const float* background,
                                       int32_t width, int32_t height, const int32_t* tile_ranges,
-                                      const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
+                                      const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots,
                                       const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
                                       float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                                       float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                                       size_t workspace_bytes, gs_stream_t stream)
 {
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
-                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    sorted_ids, splat_offsets, n_isect, n_slots, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -2406,7 +2413,7 @@ extern "C" gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, con
                                             const float* colors, const float* opacities, const float* depths,
                                             const int32_t* radii, const float* background, int32_t width,
                                             int32_t height, const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                            const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                            const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots, const float* final_T,
                                             const int32_t* n_contrib, const float* dist_totals,
                                             const int32_t* median_pos, const float* dL_dimage,
                                             const float* dL_ddist, const float* dL_dmedian, float* dL_dmeans2d,
@@ -2417,7 +2424,7 @@ extern "C" gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, con
     const int dep = (dL_ddist ? 1 : 0) | (dL_dmedian ? 2 : 0);
     if (dep == 0) {  // no depth term: the plain backward, and zero depth gradients if asked for
         const gs_status r = bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height,
-                                     tile_ranges, sorted_ids, splat_offsets, n_isect, final_T, n_contrib,
+                                     tile_ranges, sorted_ids, splat_offsets, n_isect, n_slots, final_T, n_contrib,
                                      dL_dimage, dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities, accum_weight,
                                      flags, workspace, workspace_bytes, stream, nullptr);
         if (r != GS_OK || !dL_ddepths || n <= 0) return r;
@@ -2427,7 +2434,7 @@ extern "C" gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, con
     }
     const DepthIn dz{depths, (const float4*)dist_totals, median_pos, dL_ddist, dL_dmedian};
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
-                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    sorted_ids, splat_offsets, n_isect, n_slots, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, nullptr,
                     dep, dz, dL_ddepths);
 }
@@ -2436,7 +2443,7 @@ extern "C" gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, con
                                             const float* colors, const float* opacities, const int32_t* radii,
                                             const float* background, int32_t width, int32_t height,
                                             const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                            const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                            const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots, const float* final_T,
                                             const int32_t* n_contrib, const float* dL_dimage, float* dL_dmeans2d,
                                             float* dL_dconics, float* dL_dcolors, float* dL_dopacities,
                                             float* accum_weight, uint32_t flags, void* workspace,
@@ -2444,7 +2451,7 @@ extern "C" gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, con
 {
     GS_CHECK_ARG(events, "gs_rasterize_bwd_timed: events is NULL");
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
-                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    sorted_ids, splat_offsets, n_isect, n_slots, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, workspace, workspace_bytes, stream, events);
 }
 
@@ -2496,26 +2503,26 @@ extern "C" gs_status gs_rasterize_bwd_noalloc(int32_t n, const float* means2d, c
                                               const float* colors, const float* opacities, const int32_t* radii,
                                               const float* background, int32_t width, int32_t height,
                                               const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                              const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
+                                              const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots, const float* final_T,
                                               const int32_t* n_contrib, const float* dL_dimage,
                                               float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                                               float* dL_dopacities, float* accum_weight, uint32_t flags,
                                               gs_stream_t stream)
 {
     // sizes first, on the host: a call that would not fit touches no device
-    const size_t need = gs_rasterize_bwd_workspace_size(n, n_isect, width, height);
-    GS_CHECK_ARG(need > 0, "gs_rasterize_bwd_noalloc: n = %d, n_isect = %lld or image %d x %d out of range", n,
-                 (long long)n_isect, width, height);
+    const size_t need = gs_rasterize_bwd_workspace_size(n, n_slots, width, height);
+    GS_CHECK_ARG(need > 0, "gs_rasterize_bwd_noalloc: n = %d, n_slots = %lld or image %d x %d out of range", n,
+                 (long long)n_slots, width, height);
     if (need > kScratchBytes) {
-        set_error("gs_rasterize_bwd_noalloc: %d splats, %lld pairs and %d x %d pixels need %zu bytes of scratch; "
+        set_error("gs_rasterize_bwd_noalloc: %d splats, %lld pair slots and %d x %d pixels need %zu bytes of scratch; "
                   "the fixed scratch holds %zu (use gs_rasterize_bwd with a workspace)",
-                  n, (long long)n_isect, width, height, need, kScratchBytes);
+                  n, (long long)n_slots, width, height, need, kScratchBytes);
         return GS_ERR_CAPACITY;
     }
     void* ws = nullptr;
     const gs_status st = scratch_address(&ws);
     if (st != GS_OK) return st;
     return bwd_impl(n, means2d, conics, colors, opacities, radii, background, width, height, tile_ranges,
-                    sorted_ids, splat_offsets, n_isect, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
+                    sorted_ids, splat_offsets, n_isect, n_slots, final_T, n_contrib, dL_dimage, dL_dmeans2d, dL_dconics,
                     dL_dcolors, dL_dopacities, accum_weight, flags, ws, kScratchBytes, stream, nullptr);
 }

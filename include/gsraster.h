@@ -58,10 +58,10 @@
  *  - Binning outputs passed on: tile_ranges, sorted_ids and splat_offsets
  *    should come from one gs_bin_tiles call on the same splats and image
  *    size. The kernels still bound what they read: a sorted_ids entry
- *    outside [0, n) is no entry, and both rasterizers clamp every tile
- *    range (the backward also every splat offset) to [0, n_isect], the pair
- *    count the caller passes with sorted_ids (which must hold at least
- *    n_isect entries).
+ *    outside [0, n) is no entry, both rasterizers clamp every tile range to
+ *    [0, n_isect], the pair count the caller passes with sorted_ids (which
+ *    must hold at least n_isect entries), and the backward clamps every
+ *    splat offset to [0, n_slots].
  *  - Calls are re-entrant; there is no global mutable state other than the
  *    thread-local error string.
  */
@@ -140,43 +140,57 @@ int gs_version(void);
  * in float32 as
  *     tx0 = clamp(floor((mean_x - r) * 0.0625),       0, GX)
  *     tx1 = clamp(floor((mean_x + r) * 0.0625) + 1,   0, GX)
- * (and likewise in y), r = (float)radii[i]. Each tile's list holds the splats
- * covering it, ordered by the float32 bit pattern of depth, ties broken by
- * ascending splat id (so the result is unique). Lists are concatenated in
+ * (and likewise in y), r = (float)radii[i]. Within its rectangle a splat is
+ * listed only in the tiles that its alpha >= 1/255 ellipse can reach: the
+ * compositing skips alpha < 1/255, so a tile whose pixel centres all lie
+ * outside {Q <= 2 ln(255 o)} (Q the splat's quadratic form) gets nothing from
+ * it. The test takes, in float32 with every operation rounded once in a fixed
+ * order, an upper bound T on 2 ln(255 o) (with a small margin) and, per tile
+ * row, the ellipse {Q <= T}'s x-extent over the row's band of pixel centres;
+ * a splat with 255 o < 1 is listed nowhere, one with a conic that is not
+ * positive definite keeps its whole rectangle. Each tile's list holds the
+ * splats kept there, ordered by the float32 bit pattern of depth, ties broken
+ * by ascending splat id (so the result is unique). Lists are concatenated in
  * tile-id order into sorted_ids; tile_ranges[t] = [start, end) into it
  * ({0, 0} for an empty tile).
  *
  *   n            number of splats (>= 0)
  *   means2d      device float [n][2], pixels
+ *   conics       device float [n][3] = (a, b, c) of the inverse covariance
+ *   opacities    device float [n]
  *   radii        device int32 [n], screen radius in pixels (<= 0: culled)
  *   depths       device float [n] (not > 0: culled)
  *   width,height image size in pixels, 1 .. 32768 each
  *   capacity     number of int32 slots in sorted_ids
  *   sorted_ids   device int32 [capacity] (out)
  *   tile_ranges  device int32 [GX*GY][2] (out)
- *   splat_offsets device int32 [n + 1] (out): splat i's (splat, tile) pairs
- *                are numbered splat_offsets[i] .. splat_offsets[i+1]-1, tiles
- *                of its rectangle in row-major order; [n] = n_isect. The
- *                backward uses this numbering to give each pair its own
- *                accumulation slot.
- *   n_isect      host int64 (out): total number of (splat, tile) pairs
+ *   splat_offsets device int32 [n + 1] (out): the tiles of splat i's whole
+ *                rectangle (kept or not), in row-major order, are numbered
+ *                splat_offsets[i] .. splat_offsets[i+1]-1; [n] = n_slots. The
+ *                backward uses this numbering to give each (splat, tile) pair
+ *                its own accumulation slot.
+ *   n_isect      host int64 (out): number of listed (splat, tile) pairs, the
+ *                length of sorted_ids
+ *   n_slots      host int64 (out), or NULL: number of rectangle pairs
+ *                (>= n_isect), the backward's slot count
  *   workspace    device scratch of at least gs_bin_tiles_workspace_size(...)
  *                bytes, 256-byte aligned
  *
- * Waits once on the host for the pair count (an asynchronous copy into a
- * small pinned host buffer that each calling thread keeps from its first
- * call; the stages that do not need the count are enqueued before the wait,
- * so the GPU does not idle meanwhile). If capacity < *n_isect it returns
- * GS_ERR_CAPACITY with *n_isect set and sorted_ids / tile_ranges /
- * splat_offsets untouched: allocate *n_isect slots (and the matching
- * workspace) and call again. Totals above 2^31 - 1 return GS_ERR_UNSUPPORTED.
+ * Waits once on the host for both counts (an asynchronous copy into a small
+ * pinned host buffer that each calling thread keeps from its first call; the
+ * stages that do not need the counts are enqueued before the wait, so the GPU
+ * does not idle meanwhile). If capacity < *n_isect it returns GS_ERR_CAPACITY
+ * with *n_isect (and *n_slots) set and sorted_ids / tile_ranges /
+ * splat_offsets untouched: allocate *n_isect entries (and the matching
+ * workspace) and call again. A rectangle total above 2^31 - 1 returns
+ * GS_ERR_UNSUPPORTED.
  */
 size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32_t width, int32_t height);
 
-gs_status gs_bin_tiles(int32_t n, const float* means2d, const int32_t* radii, const float* depths,
-                       int32_t width, int32_t height, int64_t capacity, int32_t* sorted_ids,
-                       int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect, void* workspace,
-                       size_t workspace_bytes, gs_stream_t stream);
+gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* conics, const float* opacities,
+                       const int32_t* radii, const float* depths, int32_t width, int32_t height, int64_t capacity,
+                       int32_t* sorted_ids, int32_t* tile_ranges, int32_t* splat_offsets, int64_t* n_isect,
+                       int64_t* n_slots, void* workspace, size_t workspace_bytes, gs_stream_t stream);
 
 /*
  * Forward composite (rasterize_f32 in the timing table of "Phase 5 step 30b —
@@ -267,8 +281,10 @@ gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* c
  *   n .. opacities       as gs_rasterize_fwd
  *   radii                device int32 [n], the radii given to gs_bin_tiles
  *   background           device float [3] or NULL (black)
- *   tile_ranges, sorted_ids, splat_offsets, n_isect
- *                        as returned by gs_bin_tiles for the same splats
+ *   tile_ranges, sorted_ids, splat_offsets, n_isect, n_slots
+ *                        as returned by gs_bin_tiles for the same splats;
+ *                        n_isect <= n_slots <= 2^31 - 1, else
+ *                        GS_ERR_INVALID_ARG
  *   final_T, n_contrib   device, as written by gs_rasterize_fwd for the same
  *                        scene; n_contrib is clamped to each tile's list length
  *   dL_dimage            device float [height][width][3]
@@ -281,8 +297,8 @@ gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* c
  *                        GS_FLAG_ACCUM_WEIGHT, else ignored (may be NULL)
  *   flags                bitwise OR of GS_FLAG_*
  *   workspace            device scratch of at least
- *                        gs_rasterize_bwd_workspace_size(n, n_isect, width,
- *                        height) bytes (48 per splat + 49 per pair + 8 per
+ *                        gs_rasterize_bwd_workspace_size(n, n_slots, width,
+ *                        height) bytes (48 per splat + 49 per slot + 8 per
  *                        tile), 256-byte aligned; contents on entry do not
  *                        matter
  *
@@ -290,14 +306,14 @@ gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* c
  * zeros. Inputs that do not come from one binning of the same splats are
  * not detected; the kernels never write outside the outputs and workspace.
  */
-/* 0 for n < 0, n_isect < 0 or a width / height outside 1..32768 */
-size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_isect, int32_t width, int32_t height);
+/* 0 for n < 0, n_slots < 0 or a width / height outside 1..32768 */
+size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_slots, int32_t width, int32_t height);
 
 gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,
                            const float* opacities, const int32_t* radii, const float* background,
                            int32_t width, int32_t height, const int32_t* tile_ranges,
                            const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
-                           const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                           int64_t n_slots, const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                            float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                            size_t workspace_bytes, gs_stream_t stream);
@@ -331,8 +347,8 @@ gs_status gs_rasterize_bwd_depth(int32_t n, const float* means2d, const float* c
                                  const float* opacities, const float* depths, const int32_t* radii,
                                  const float* background, int32_t width, int32_t height,
                                  const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                 const int32_t* splat_offsets, int64_t n_isect, const float* final_T,
-                                 const int32_t* n_contrib, const float* dist_totals, const int32_t* median_pos,
+                                 const int32_t* splat_offsets, int64_t n_isect, int64_t n_slots,
+                                 const float* final_T, const int32_t* n_contrib, const float* dist_totals, const int32_t* median_pos,
                                  const float* dL_dimage, const float* dL_ddist, const float* dL_dmedian,
                                  float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors, float* dL_dopacities,
                                  float* dL_ddepths, float* accum_weight, uint32_t flags, void* workspace,
@@ -354,8 +370,8 @@ gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* c
                                  const float* opacities, const int32_t* radii, const float* background,
                                  int32_t width, int32_t height, const int32_t* tile_ranges,
                                  const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
-                                 const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
-                                 float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
+                                 int64_t n_slots, const float* final_T, const int32_t* n_contrib,
+                                 const float* dL_dimage, float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                                  float* dL_dopacities, float* accum_weight, uint32_t flags, void* workspace,
                                  size_t workspace_bytes, gs_stream_t stream, const gs_event_t events[4]);
 
@@ -369,7 +385,7 @@ gs_status gs_rasterize_bwd_timed(int32_t n, const float* means2d, const float* c
  * The workspace gs_rasterize_bwd would take lives in a fixed device array of
  * the library, gs_rasterize_bwd_noalloc_capacity() bytes (64 MiB), which each
  * GPU the library runs on holds from its first call until the process ends
- * (enough for about a million (splat, tile) pairs: gs_rasterize_bwd_workspace_size
+ * (enough for about a million (splat, tile) slots: gs_rasterize_bwd_workspace_size
  * tells what a scene needs). A scene that needs more returns GS_ERR_CAPACITY
  * before anything is enqueued. The call allocates nothing: no hipMalloc, no
  * hipFree, no allocating library routine; its first call on a device looks up
@@ -385,7 +401,7 @@ gs_status gs_rasterize_bwd_noalloc(int32_t n, const float* means2d, const float*
                                    const float* opacities, const int32_t* radii, const float* background,
                                    int32_t width, int32_t height, const int32_t* tile_ranges,
                                    const int32_t* sorted_ids, const int32_t* splat_offsets, int64_t n_isect,
-                                   const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                                   int64_t n_slots, const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
                                    float* dL_dmeans2d, float* dL_dconics, float* dL_dcolors,
                                    float* dL_dopacities, float* accum_weight, uint32_t flags,
                                    gs_stream_t stream);

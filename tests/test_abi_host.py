@@ -75,9 +75,10 @@ def test_bwd_rejects_bad_arguments():
     lib = _lib.load()
     p = ctypes.c_void_p(1)
 
-    def call(n=1, w=8, h=8, flags=0, aw=None, grad=p, n_isect=0, ws=None, wsb=0):
-        return lib.gs_rasterize_bwd(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, p, p, p, grad, grad, grad,
-                                    grad, aw, flags, ws, wsb, None)
+    def call(n=1, w=8, h=8, flags=0, aw=None, grad=p, n_isect=0, n_slots=None, ws=None, wsb=0):
+        n_slots = n_isect if n_slots is None else n_slots
+        return lib.gs_rasterize_bwd(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, n_slots, p, p, p, grad, grad,
+                                    grad, grad, aw, flags, ws, wsb, None)
     assert call(n=-5) == _lib.GS_ERR_INVALID_ARG
     assert call(flags=0x80) == _lib.GS_ERR_INVALID_ARG
     assert b"unknown flags" in lib.gs_last_error()
@@ -92,6 +93,11 @@ def test_bwd_rejects_bad_arguments():
     assert call(w=-3) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=1 << 31) == _lib.GS_ERR_INVALID_ARG
+    # the slot count: at least the pair count, at most 2^31 - 1
+    assert call(n_isect=10, n_slots=9) == _lib.GS_ERR_INVALID_ARG
+    assert b"n_slots" in lib.gs_last_error()
+    assert call(n_isect=10, n_slots=1 << 31) == _lib.GS_ERR_INVALID_ARG
+    assert b"n_slots" in lib.gs_last_error()
     need = lib.gs_rasterize_bwd_workspace_size(1, 100, 8, 8)
     assert need >= 100 * 49 + 64
     assert call(n_isect=100, ws=None, wsb=need) == _lib.GS_ERR_INVALID_ARG
@@ -99,6 +105,10 @@ def test_bwd_rejects_bad_arguments():
     assert call(n_isect=100, ws=ctypes.c_void_p(256), wsb=need - 1) == _lib.GS_ERR_INVALID_ARG
     assert call(n_isect=100, ws=ctypes.c_void_p(300), wsb=need) == _lib.GS_ERR_INVALID_ARG
     assert b"aligned" in lib.gs_last_error()
+    # the workspace is sized by the slots, not the pairs
+    assert call(n_isect=10, n_slots=100, ws=ctypes.c_void_p(256),
+                wsb=lib.gs_rasterize_bwd_workspace_size(1, 10, 8, 8)) == _lib.GS_ERR_INVALID_ARG
+    assert b"workspace" in lib.gs_last_error()
 
 
 def test_bwd_timed_rejects_bad_arguments():
@@ -106,8 +116,8 @@ def test_bwd_timed_rejects_bad_arguments():
     p = ctypes.c_void_p(1)
 
     def call(events, n=-5):
-        return lib.gs_rasterize_bwd_timed(n, p, p, p, p, p, None, 8, 8, p, p, p, 0, p, p, p, p, p, p, p, None, 0,
-                                          None, 0, None, events)
+        return lib.gs_rasterize_bwd_timed(n, p, p, p, p, p, None, 8, 8, p, p, p, 0, 0, p, p, p, p, p, p, p, None,
+                                          0, None, 0, None, events)
     assert call(None) == _lib.GS_ERR_INVALID_ARG
     assert b"events" in lib.gs_last_error()
     # the plain argument checks come first, before any event is recorded
@@ -119,15 +129,18 @@ def test_bin_rejects_bad_arguments():
     lib = _lib.load()
     p = ctypes.c_void_p(256)
     cnt = ctypes.c_int64(0)
-    def call(n=4, w=64, h=64, cap=16, ws=p, wsb=1 << 20, ncnt=True, offs=p):
-        return lib.gs_bin_tiles(n, p, p, p, w, h, cap, p, p, offs, ctypes.byref(cnt) if ncnt else None, ws, wsb,
-                                None)
+    def call(n=4, w=64, h=64, cap=16, ws=p, wsb=1 << 20, ncnt=True, offs=p, conics=p, opac=p):
+        return lib.gs_bin_tiles(n, p, conics, opac, p, p, w, h, cap, p, p, offs, ctypes.byref(cnt) if ncnt else None,
+                                None, ws, wsb, None)
     assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(w=0) == _lib.GS_ERR_INVALID_ARG
     assert call(cap=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(ncnt=False) == _lib.GS_ERR_INVALID_ARG
     assert call(offs=None) == _lib.GS_ERR_INVALID_ARG
     assert b"splat_offsets" in lib.gs_last_error()
+    for kw in ({"conics": None}, {"opac": None}):   # the culling ellipse's inputs
+        assert call(**kw) == _lib.GS_ERR_INVALID_ARG
+        assert b"NULL splat array" in lib.gs_last_error()
     assert call(wsb=16) == _lib.GS_ERR_INVALID_ARG
     assert b"workspace" in lib.gs_last_error()
     assert call(ws=ctypes.c_void_p(257)) == _lib.GS_ERR_INVALID_ARG
@@ -173,11 +186,13 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_call():
     assert cap == 64 << 20
     p = ctypes.c_void_p(1)
 
-    def call(n=1000, n_isect=0, w=64, h=64):
-        return lib.gs_rasterize_bwd_noalloc(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, p, p, p, p, p, p, p,
-                                            None, 0, None)
+    def call(n=1000, n_isect=0, n_slots=None, w=64, h=64):
+        n_slots = n_isect if n_slots is None else n_slots
+        return lib.gs_rasterize_bwd_noalloc(n, p, p, p, p, p, None, w, h, p, p, p, n_isect, n_slots, p, p, p, p, p,
+                                            p, p, None, 0, None)
     assert call(n_isect=2_000_000) == _lib.GS_ERR_CAPACITY
     assert b"scratch" in lib.gs_last_error()
+    assert call(n_isect=1000, n_slots=2_000_000) == _lib.GS_ERR_CAPACITY   # sized by the slots
     assert call(n=-1) == _lib.GS_ERR_INVALID_ARG
     assert call(w=0) == _lib.GS_ERR_INVALID_ARG
     assert lib.gs_rasterize_bwd_workspace_size(1000, 1_000_000, 64, 64) <= cap
@@ -198,8 +213,8 @@ def test_depth_entry_points_reject_bad_arguments():
     assert fwd(depths=None, totals=None, pos=p) == _lib.GS_ERR_INVALID_ARG
 
     def bwd(depths=p, totals=p, pos=p, gd=p, gm=None, dz=p, flags=0):
-        return lib.gs_rasterize_bwd_depth(1, p, p, p, p, depths, p, None, 8, 8, p, p, p, 0, p, p, totals, pos, p, gd,
-                                          gm, p, p, p, p, dz, None, flags, None, 0, None)
+        return lib.gs_rasterize_bwd_depth(1, p, p, p, p, depths, p, None, 8, 8, p, p, p, 0, 0, p, p, totals, pos, p,
+                                          gd, gm, p, p, p, p, dz, None, flags, None, 0, None)
     assert bwd(depths=None) == _lib.GS_ERR_INVALID_ARG
     assert bwd(dz=None) == _lib.GS_ERR_INVALID_ARG
     assert b"dL_ddepths" in lib.gs_last_error()

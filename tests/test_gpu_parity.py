@@ -91,8 +91,9 @@ def _dev(a, dtype=None):
     return t.to("cuda:0")
 
 
-def gpu_bins(sc):
-    return gsr.gs_bin_tiles(_dev(sc.means2d), _dev(sc.radii), _dev(sc.depths), sc.width, sc.height)
+def gpu_bins(sc, capacity=None):
+    return gsr.gs_bin_tiles(_dev(sc.means2d), _dev(sc.conics), _dev(sc.opacities), _dev(sc.radii), _dev(sc.depths),
+                            sc.width, sc.height, capacity=capacity)
 
 
 def gpu_fwd(sc, bins, bg=True, max_weight=False):
@@ -127,13 +128,16 @@ def gpu_bwd(sc, bins, final_T, n_contrib, g, accum_weight=False, walk=None):
 
 
 def check_bins(sc, bins):
-    ids_o, rng_o = oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    """The lists (culled by the alpha >= 1/255 ellipse) bit for bit, and the
+    rectangle numbering of the backward's slots."""
+    ids_o, rng_o = oracle.bin_tiles(sc.means2d, sc.conics, sc.opacities, sc.radii, sc.depths, sc.width, sc.height)
     assert bins.n_isect == len(ids_o)
     np.testing.assert_array_equal(bins.tile_ranges.cpu().numpy(), rng_o)
     np.testing.assert_array_equal(bins.sorted_ids.cpu().numpy(), ids_o)
     tx0, tx1, ty0, ty1 = oracle.tile_rects(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
     offs = np.concatenate([[0], np.cumsum((tx1 - tx0) * (ty1 - ty0))])
     np.testing.assert_array_equal(bins.splat_offsets.cpu().numpy(), offs)
+    assert bins.n_slots == offs[-1] >= bins.n_isect
     return ids_o, rng_o
 
 
@@ -328,8 +332,7 @@ def test_large_grid_forward_backward():
 
 def test_binning_capacity_retry():
     sc = scenes.make_scene("tiny", 0)
-    bins = gsr.gs_bin_tiles(_dev(sc.means2d), _dev(sc.radii), _dev(sc.depths), sc.width, sc.height,
-                            capacity=3)
+    bins = gpu_bins(sc, capacity=3)
     check_bins(sc, bins)
 
 
@@ -420,7 +423,7 @@ def test_out_of_range_ids_and_ranges():
     rng_o = np.stack([new_pos[rng[:, 0]], new_pos[rng[:, 1]]], 1).astype(np.int32)
     ids_o = ids[keep].astype(np.int32)
     gb = gsr.Bins(torch.from_numpy(ids_bad).cuda(), bins.tile_ranges, bins.splat_offsets, bins.n_isect,
-                  sc.width, sc.height)
+                  sc.width, sc.height, n_slots=bins.n_slots)
     img, T, nc = gpu_fwd(sc, gb)
     fo = oracle.rasterize_fwd(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.background, sc.width, sc.height,
                               rng_o, ids_o)
@@ -441,7 +444,7 @@ def test_out_of_range_ids_and_ranges():
     r2[1] = [rng[1, 1], rng[1, 0]]
     r2[2] = [-50, rng[2, 1]]
     gb2 = gsr.Bins(bins.sorted_ids, torch.from_numpy(r2).cuda(), bins.splat_offsets, bins.n_isect, sc.width,
-                   sc.height)
+                   sc.height, n_slots=bins.n_slots)
     # the forward walks each range clamped to [0, n_isect] (an inverted one is
     # empty): the oracle on the clamped ranges gives the same image
     r2c = np.clip(r2, 0, len(ids))

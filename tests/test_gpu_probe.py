@@ -44,7 +44,7 @@ def test_walk_counts_match_oracle():
     dev = "cuda:0"
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     m, q, c, o = t(sc.means2d), t(sc.conics), t(sc.colors), t(sc.opacities)
-    bins = gsr.gs_bin_tiles(m, t(sc.radii), t(sc.depths), sc.width, sc.height)
+    bins = gsr.gs_bin_tiles(m, q, o, t(sc.radii), t(sc.depths), sc.width, sc.height)
     _, _, nc = gsr.gs_rasterize_fwd(m, q, c, o, t(sc.background), sc.width, sc.height, bins.tile_ranges,
                                     bins.sorted_ids)
     cnt = torch.zeros(12, dtype=torch.int64, device=dev)
@@ -55,7 +55,7 @@ def test_walk_counts_match_oracle():
     cnt = cnt.cpu().numpy()
     assert cnt[0] == int(nc.sum().item())
     # composited pairs = sum of alpha*T weights' support: count them with the oracle
-    ids_o, rng_o = oracle.bin_tiles(sc.means2d, sc.radii, sc.depths, sc.width, sc.height)
+    ids_o, rng_o = oracle.bin_tiles(sc.means2d, sc.conics, sc.opacities, sc.radii, sc.depths, sc.width, sc.height)
     ys, xs = np.mgrid[0:sc.height, 0:sc.width]
     img, T, nstep = oracle.composite_bruteforce(sc.means2d, sc.conics, sc.colors, sc.opacities, sc.depths,
                                                 sc.radii, sc.background, sc.width, sc.height)

@@ -20,14 +20,14 @@ def _dev(a):
 def _inputs(sc):
     m, q, c, o, r = _dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.radii)
     bg = _dev(sc.background)
-    bins = gsr.gs_bin_tiles(m, r, _dev(sc.depths), sc.width, sc.height)
+    bins = gsr.gs_bin_tiles(m, q, o, r, _dev(sc.depths), sc.width, sc.height)
     _, T, nc = gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
     return (m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, _dev(sc.dL_dimage))
 
 
 def _compare(sc, accum_weight, walk=None):
     args = _inputs(sc)
-    need = gsr.gs_rasterize_bwd_workspace_size(sc.n, args[8].n_isect, sc.width, sc.height)
+    need = gsr.gs_rasterize_bwd_workspace_size(sc.n, args[8].n_slots, sc.width, sc.height)
     assert need <= gsr.gs_rasterize_bwd_noalloc_capacity()
     ref = gsr.gs_rasterize_bwd(*args, accum_weight=accum_weight, walk=walk)
     out = {k: torch.full_like(v, float("nan")) for k, v in ref.items()}   # every element must be written
