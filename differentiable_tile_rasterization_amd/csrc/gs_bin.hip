@@ -14,10 +14,11 @@
 //              depth sort is already queued behind the copy)
 //   4. depth   stable LSD radix sort of the splats by the bit pattern of their
 //              depth (32 bits, 8-bit digits), splat ids starting in id order
-//   5. emit    the splats' tile rectangles (stored by the count pass) and kept
-//              counts gathered into depth order and scanned; the splat of
-//              depth rank k writes its kept tiles, row-major, at that offset,
-//              as (tile id, splat id), tile ids 16-bit up to 65536 tiles
+//   5. emit    the kept counts gathered into depth order and scanned; the
+//              splat of depth rank k reads its rectangle and ellipse factors
+//              (stored by the count pass) and writes its kept tiles,
+//              row-major, at that offset, as (tile id, splat id), tile ids
+//              16-bit up to 65536 tiles
 //   6. tiles   stable LSD radix sort of the pairs by tile id over only the
 //              ceil(log2(tiles)) bits it can have, split as evenly as possible
 //              over as few passes as 8-bit digits allow, narrower digits first
@@ -94,9 +95,43 @@ struct CullEllipse {
     int mode;
 };
 
+// What the emission needs of a splat, written by the count pass in splat
+// order and read once per splat in depth order (32 bytes, one aligned load
+// pair): the mean, the factors (l11 = 0 marks a splat that keeps its whole
+// rectangle) and T, and the rectangle. vmax and vL are recomputed from these
+// by the same operations.
+struct alignas(16) CullRec {
+    float mx, my, l11, l21, l22, T;
+    ushort4 rect;  // tx0, ty0, tx1, ty1
+};
+
 __device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
 
-__device__ __attribute__((noinline)) CullEllipse cull_ellipse(float2 m, float a, float b, float c, float o)
+// vmax and vL from l21, l22 and T.
+__device__ __forceinline__ void ellipse_extents(CullEllipse& E)
+{
+#pragma clang fp contract(off)
+    const float sT = __builtin_sqrtf(E.T);
+    E.vmax = sT / E.l22;
+    const float nrm = __builtin_sqrtf(E.l21 * E.l21 + E.l22 * E.l22);
+    E.vL = (sT * E.l21) / (E.l22 * nrm);
+}
+
+__device__ __forceinline__ CullEllipse ellipse_of(const CullRec& r)
+{
+    CullEllipse E{};
+    E.mx = r.mx;
+    E.my = r.my;
+    E.l11 = r.l11;
+    E.l21 = r.l21;
+    E.l22 = r.l22;
+    E.T = r.T;
+    E.mode = r.l11 > 0.0f ? kCullRows : kCullRect;
+    if (E.mode == kCullRows) ellipse_extents(E);
+    return E;
+}
+
+__device__ __forceinline__ CullEllipse cull_ellipse(float2 m, float a, float b, float c, float o)
 {
 #pragma clang fp contract(off)
     CullEllipse E{};
@@ -120,10 +155,7 @@ __device__ __attribute__((noinline)) CullEllipse cull_ellipse(float2 m, float a,
     E.l11 = __builtin_sqrtf(a);
     E.l21 = b / E.l11;
     E.l22 = __builtin_sqrtf(fmaxf(c - E.l21 * E.l21, 0.0f));
-    const float sT = __builtin_sqrtf(T);
-    E.vmax = sT / E.l22;
-    const float nrm = __builtin_sqrtf(E.l21 * E.l21 + E.l22 * E.l22);
-    E.vL = (sT * E.l21) / (E.l22 * nrm);
+    ellipse_extents(E);
     const bool usable = finite_f(y) && finite_f(T) && finite_f(E.l11) && finite_f(E.l21) && finite_f(E.l22) &&
                         finite_f(E.vmax) && finite_f(E.vL) && E.l11 > 0.0f && E.l22 > 0.0f && finite_f(m.x) &&
                         finite_f(m.y);
@@ -132,7 +164,7 @@ __device__ __attribute__((noinline)) CullEllipse cull_ellipse(float2 m, float a,
 }
 
 // The kept columns [x, y] of tile row ty within [tx0, tx1) (x > y: none).
-__device__ __attribute__((noinline)) int2 cull_row(const CullEllipse& E, int ty, int tx0, int tx1)
+__device__ __forceinline__ int2 cull_row(const CullEllipse E, int ty, int tx0, int tx1)
 {
 #pragma clang fp contract(off)
     if (E.mode != kCullRows) return E.mode == kCullRect ? make_int2(tx0, tx1 - 1) : make_int2(tx1, tx1 - 1);
@@ -161,16 +193,16 @@ __device__ __attribute__((noinline)) int2 cull_row(const CullEllipse& E, int ty,
 }
 
 // counts[i] = number of tiles of splat i's rectangle, kept[i] = the number of
-// them its culling ellipse keeps; rects[i] = the rectangle (tx0, ty0, tx1,
-// ty1), empty for a culled splat. A grid has at most 2048 tiles per side, so
-// 16 bits per bound suffice.
+// them its culling ellipse keeps; recs[i] = what the emission needs (the
+// rectangle (tx0, ty0, tx1, ty1), empty for a culled splat: a grid has at
+// most 2048 tiles per side, so 16 bits per bound suffice).
 __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
                                                     const float* __restrict__ conics,
                                                     const float* __restrict__ opacities,
                                                     const int* __restrict__ radii,
                                                     const float* __restrict__ depths, int GX, int GY,
                                                     unsigned* __restrict__ counts, unsigned* __restrict__ kept,
-                                                    ushort4* __restrict__ rects)
+                                                    CullRec* __restrict__ recs)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -178,18 +210,24 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
     unsigned k = 0;
+    CullRec r{};
     if (live) {
         const CullEllipse E = cull_ellipse(m, conics[3 * i], conics[3 * i + 1], conics[3 * i + 2], opacities[i]);
         for (int ty = ty0; ty < ty1; ++ty) {
             const int2 cr = cull_row(E, ty, tx0, tx1);
             k += cr.y >= cr.x ? (unsigned)(cr.y - cr.x + 1) : 0u;
         }
+        r.mx = E.mx;
+        r.my = E.my;
+        r.l11 = E.mode == kCullRows ? E.l11 : 0.0f;
+        r.l21 = E.l21;
+        r.l22 = E.l22;
+        r.T = E.T;
+        r.rect = make_ushort4((unsigned short)tx0, (unsigned short)ty0, (unsigned short)tx1, (unsigned short)ty1);
     }
     counts[i] = live ? (unsigned)((tx1 - tx0) * (ty1 - ty0)) : 0u;  // at most 2048 x 2048
     kept[i] = k;
-    rects[i] = live ? make_ushort4((unsigned short)tx0, (unsigned short)ty0, (unsigned short)tx1,
-                                   (unsigned short)ty1)
-                    : make_ushort4(0, 0, 0, 0);
+    recs[i] = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -286,30 +324,24 @@ hipError_t exclusive_scan(const unsigned* in, unsigned* out, long long n, unsign
 // ---------------------------------------------------------------------------
 // Depth order and emission.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gather_rects_kernel(int n, const int* __restrict__ by_depth,
-                                                           const ushort4* __restrict__ rects,
-                                                           const unsigned* __restrict__ kept,
-                                                           ushort4* __restrict__ rect_sorted,
-                                                           unsigned* __restrict__ cnt_sorted)
+__global__ __launch_bounds__(256) void gather_kept_kernel(int n, const int* __restrict__ by_depth,
+                                                          const unsigned* __restrict__ kept,
+                                                          unsigned* __restrict__ cnt_sorted)
 {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
-    const int i = by_depth[k];
-    rect_sorted[k] = rects[i];
-    cnt_sorted[k] = kept[i];
+    cnt_sorted[k] = kept[by_depth[k]];
 }
 
 // Emission: one thread per depth rank k. The splat of rank k writes its kept
 // tiles, row by row and left to right, from emit_off[k], as (tile id, splat
-// id); the kept count taken by the count pass (the same ellipse function on
-// the same inputs) bounds the writes.
+// id): the rows' columns by the same operations on the same values as in the
+// count pass, whose kept count also bounds the writes.
 template <typename K>
 __global__ __launch_bounds__(256) void emit_kernel(int n, const int* __restrict__ by_depth,
-                                                   const ushort4* __restrict__ rect_sorted,
                                                    const unsigned* __restrict__ cnt_sorted,
                                                    const unsigned* __restrict__ emit_off,
-                                                   const float2* __restrict__ means, const float* __restrict__ conics,
-                                                   const float* __restrict__ opacities, int GX,
+                                                   const CullRec* __restrict__ recs, int GX,
                                                    K* __restrict__ keys, int* __restrict__ vals)
 {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
@@ -317,10 +349,11 @@ __global__ __launch_bounds__(256) void emit_kernel(int n, const int* __restrict_
     const unsigned cnt = cnt_sorted[k];
     if (cnt == 0) return;
     const int i = by_depth[k];
-    const ushort4 b = rect_sorted[k];
+    const CullRec r = recs[i];
+    const ushort4 b = r.rect;
     unsigned p = emit_off[k];  // the pair count is below 2^31 here (checked before emission)
     const unsigned pend = p + cnt;
-    const CullEllipse E = cull_ellipse(means[i], conics[3 * i], conics[3 * i + 1], conics[3 * i + 2], opacities[i]);
+    const CullEllipse E = ellipse_of(r);
     for (int ty = b.y; ty < (int)b.w && p < pend; ++ty) {
         const int2 cr = cull_row(E, ty, b.x, b.z);
         for (int c = cr.x; c <= cr.y && p < pend; ++c, ++p) {
@@ -551,8 +584,8 @@ __global__ __launch_bounds__(256) void outputs_kernel(int n, int tiles, const un
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BinLayout {
-    size_t counts, kept, rects, offsets, part, total, pairs, dkeys_a, dkeys_b, dvals_a, dvals_b, rect_sorted,
-        cnt_sorted, emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
+    size_t counts, kept, recs, offsets, part, total, pairs, dkeys_a, dkeys_b, dvals_a, dvals_b, cnt_sorted,
+        emit_off, keys_a, keys_b, vals_tmp, hist, bytes;
 };
 
 BinLayout bin_layout(long long n, long long cap)
@@ -566,7 +599,7 @@ BinLayout bin_layout(long long n, long long cap)
     const size_t n1 = (size_t)(n > 0 ? n : 1), c1 = (size_t)(cap > 0 ? cap : 1);
     L.counts = o;     o += align256(sizeof(unsigned) * n1);
     L.kept = o;       o += align256(sizeof(unsigned) * n1);
-    L.rects = o;      o += align256(sizeof(ushort4) * n1);
+    L.recs = o;       o += align256(sizeof(CullRec) * n1);
     L.offsets = o;    o += align256(sizeof(unsigned) * n1);
     L.part = o;       o += align256(sizeof(unsigned long long) * (size_t)nparts);
     L.total = o;      o += align256(sizeof(unsigned long long));
@@ -575,7 +608,6 @@ BinLayout bin_layout(long long n, long long cap)
     L.dkeys_b = o;    o += align256(sizeof(unsigned) * n1);
     L.dvals_a = o;    o += align256(sizeof(int) * n1);
     L.dvals_b = o;    o += align256(sizeof(int) * n1);
-    L.rect_sorted = o; o += align256(sizeof(ushort4) * n1);
     L.cnt_sorted = o; o += align256(sizeof(unsigned) * n1);
     L.emit_off = o;   o += align256(sizeof(unsigned) * n1);
     L.keys_a = o;     o += align256(sizeof(unsigned) * c1);
@@ -619,18 +651,16 @@ hipError_t radix_pass(const K* kin, const int* vin, K* kout, int* vout, long lon
 // Emission, the tile passes (ping-ponged so that the last one writes its
 // values into sorted_ids) and the ranges, with keys of type K.
 template <typename K>
-hipError_t tile_sort(int n, long long I, const int* by_depth, const ushort4* rect_sorted, const unsigned* cnt_sorted,
-                     const unsigned* emit_off, const float2* means, const float* conics, const float* opacities,
-                     int GX, int tiles, int np, int tb, K* keys_a, K* keys_b, int* vals_t, int* sorted_ids,
-                     unsigned* hist, unsigned long long* part, unsigned long long* total, int2* tile_ranges,
-                     hipStream_t st)
+hipError_t tile_sort(int n, long long I, const int* by_depth, const unsigned* cnt_sorted, const unsigned* emit_off,
+                     const CullRec* recs, int GX, int tiles, int np, int tb, K* keys_a, K* keys_b, int* vals_t,
+                     int* sorted_ids, unsigned* hist, unsigned long long* part, unsigned long long* total,
+                     int2* tile_ranges, hipStream_t st)
 {
     K* kin = keys_a;
     K* kout = keys_b;
     int* vin = (np % 2 == 0) ? sorted_ids : vals_t;
     int* vout = (np % 2 == 0) ? vals_t : sorted_ids;
-    emit_kernel<K><<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rect_sorted, cnt_sorted, emit_off, means, conics,
-                                                    opacities, GX, kin, vin);
+    emit_kernel<K><<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, cnt_sorted, emit_off, recs, GX, kin, vin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int shift = 0;
@@ -730,7 +760,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
     auto* offsets = (unsigned*)(ws + L.offsets);
     auto* part = (unsigned long long*)(ws + L.part);
     auto* total = (unsigned long long*)(ws + L.total);
-    auto* rects = (ushort4*)(ws + L.rects);
+    auto* recs = (CullRec*)(ws + L.recs);
 
     auto* pairs = (unsigned long long*)(ws + L.pairs);  // [0] rectangle pairs, [1] kept pairs
     auto* dka = (unsigned*)(ws + L.dkeys_a);
@@ -738,21 +768,19 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
     auto* dva = (int*)(ws + L.dvals_a);
     auto* dvb = (int*)(ws + L.dvals_b);
     auto* hist = (unsigned*)(ws + L.hist);
-    auto* rect_sorted = (ushort4*)(ws + L.rect_sorted);
     auto* cnt_sorted = (unsigned*)(ws + L.cnt_sorted);
     auto* emit_off = (unsigned*)(ws + L.emit_off);
     const int* by_depth = dva;
 
     // Both pair counts are read back with one asynchronous copy into pinned
     // host memory, and everything that does not need them (the splats' depth
-    // sort and their rectangles and kept counts in depth order; workspace
-    // only) is enqueued before the host waits for that copy: the GPU stays
+    // sort and their kept counts in depth order; workspace only) is enqueued before the host waits for that copy: the GPU stays
     // busy while the host waits and then enqueues the pair stages behind the
     // depth sort.
     unsigned long long h_tot[2] = {0, 0};
     if (n > 0) {
         count_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, (const float2*)means2d, conics, opacities, radii, depths,
-                                                      GX, GY, counts, kept, rects);
+                                                      GX, GY, counts, kept, recs);
         GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(counts, offsets, n, part, pairs, st));
         // the kept total (the scan's output goes to emit_off, rewritten below)
@@ -783,7 +811,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
         }
         by_depth = dv_in;
         // Emission offsets in depth order.
-        gather_rects_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, rects, kept, rect_sorted, cnt_sorted);
+        gather_kept_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, kept, cnt_sorted);
         GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(cnt_sorted, emit_off, n, part, total, st));
         if (pin) {
@@ -820,16 +848,14 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
     const int np = (tb + kRadixBits - 1) / kRadixBits;
 
     int* vals_t = (int*)(ws + L.vals_tmp);
-    const float2* m2 = (const float2*)means2d;
     // 16-bit tile keys up to 65536 tiles (a quarter less traffic per pass)
     if (tiles <= 65536)
-        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, rect_sorted, cnt_sorted, emit_off, m2, conics, opacities, GX,
-                                         tiles, np, tb, (unsigned short*)(ws + L.keys_a),
-                                         (unsigned short*)(ws + L.keys_b), vals_t, sorted_ids, hist, part, total,
-                                         (int2*)tile_ranges, st));
+        GS_HIP(tile_sort<unsigned short>(n, I, by_depth, cnt_sorted, emit_off, recs, GX, tiles, np, tb,
+                                         (unsigned short*)(ws + L.keys_a), (unsigned short*)(ws + L.keys_b), vals_t,
+                                         sorted_ids, hist, part, total, (int2*)tile_ranges, st));
     else
-        GS_HIP(tile_sort<unsigned>(n, I, by_depth, rect_sorted, cnt_sorted, emit_off, m2, conics, opacities, GX, tiles,
-                                   np, tb, (unsigned*)(ws + L.keys_a), (unsigned*)(ws + L.keys_b), vals_t,
-                                   sorted_ids, hist, part, total, (int2*)tile_ranges, st));
+        GS_HIP(tile_sort<unsigned>(n, I, by_depth, cnt_sorted, emit_off, recs, GX, tiles, np, tb,
+                                   (unsigned*)(ws + L.keys_a), (unsigned*)(ws + L.keys_b), vals_t, sorted_ids, hist,
+                                   part, total, (int2*)tile_ranges, st));
     return GS_OK;
 }

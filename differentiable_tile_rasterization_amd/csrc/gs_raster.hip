@@ -651,9 +651,10 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 //     dx = dx0 + k and dy is constant along the row), turning them into the
 //     record's ten sums about the entry's mean, and the record's lanes add
 //     theirs with fused DPP adds; the first lane stores the record.
-// A step then costs about 21 VALU instructions instead of about 50 (the
+// A step then costs 19 VALU instructions instead of about 50 (the
 // cross-lane tree of the other walks: ~21 per step, and the LDS float adds
-// of the first walk, ~25 LDS cycles each), and phase 2 about 15 per step.
+// of the first walk, ~25 LDS cycles each), and phase 2 about 15 per step
+// (136 VALU per four-step chunk in all).
 // The pads (KC x 64 float2 per wave) are written and read by the same wave,
 // whose LDS accesses are served in order: no barrier is needed around them.
 // ---------------------------------------------------------------------------
@@ -695,7 +696,11 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     const float ox = (float)((tile % GX) * kTile) + 0.5f, oy = (float)((tile / GX) * kTile) + 0.5f;
     const int2 rg = clamp_range(ranges[tile], n_isect);  // a range past the pair list reads nothing wild
 
-    float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    // the reciprocal of the transmittance after the current entry (1 / final_T
+    // at the start): the walk multiplies it by (1 - alpha) and takes T before
+    // the entry as its reciprocal, so rounding does not accumulate through
+    // the reciprocals
+    float IT = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
     // DEP: the median depth zm and list position mp; the distortion totals
     // about zm (A, -2B, C) and its upstream gD, with 2 gD A and -2 gD B; the
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     int mp = 0;
     if (inside) {
         const int p = y * W + x;
-        T = final_T[p];
+        IT = 1.0f / final_T[p];
         // never walk past the tile's list, whatever n_contrib holds
         nc = min(max(n_contrib[p], 0), rg.y - rg.x);
         g0 = dimg[3 * p + 0];
@@ -935,15 +940,15 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             const unsigned long long bal = __builtin_amdgcn_fcmpf(al, kAlphaMin, 3 /* ordered >= */) &
                                            __builtin_amdgcn_sicmp(cur, ncb_off, 40 /* signed < */);
             const bool contrib = __builtin_amdgcn_inverse_ballot_w64(bal);
-            const float cg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, Cb * g2));
+            // (colour - colour behind) . dL/dC
+            const float eg = __builtin_fmaf(Bq.z, g0, __builtin_fmaf(Bq.w, g1, __builtin_fmaf(Cb, g2, -Bg)));
             // no branch on "no lane contributes" (a few percent of the steps):
-            // those lanes' updates are exact no-ops (alpha 0: T, the colour
+            // those lanes' updates are exact no-ops (alpha 0: 1 / T, the colour
             // behind and w, s unchanged or zero)
             const float ae = contrib ? al : 0.0f;   // non-contributing lanes: no-op update
-            const float Ti = T * __builtin_amdgcn_rcpf(1.0f - ae);
-            const float eg = cg - Bg;
+            IT = __builtin_fmaf(-ae, IT, IT);       // 1 / T before the entry
+            const float Ti = __builtin_amdgcn_rcpf(IT);
             Bg = __builtin_fmaf(ae, eg, Bg);
-            T = Ti;
             const float w = ae * Ti;
             float egt = eg;  // dL/dalpha / T
             if (DEP) {
@@ -1024,6 +1029,9 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             f[5] = dyr * f[3];                                                                   // sum s dy
             f[7] = dyr * f[4];                                                                   // sum s dx dy
             f[8] = dyr * f[5];                                                                   // sum s dy^2
+            // plain products: folded into the next DPP add they would cost a
+            // DPP move, a zeroing move and a fused multiply-add each
+            asm volatile("" : "+v"(f[5]), "+v"(f[7]), "+v"(f[8]));
             f[9] = dpp_add_quad_xor1(AW ? Wt : Vz);
             f[10] = dpp_add_quad_xor1(Vz);  // field kZ: 9 or 10
             // then the rows: the two pairs of each quad, and (eight lanes) the
@@ -1920,15 +1928,14 @@ constexpr int kGatherWin = 16 * kWave;  // flag bytes scanned per step
 constexpr int kGatherRegMaxPairs = 32;  // mean pairs per splat up to which gather_kernel runs
 constexpr int kWalkManyPairs = 16;  // mean pairs per splat above which the deferred walk takes smaller batches
 // Shapes of the deferred walk (entries per batch, steps per chunk, workgroups
-// per CU), measured on the 2M-splat and the high-overlap scenes: 255-entry
-// batches where splats cover few tiles; 191 where they cover many (more
-// half-list records per entry: the smaller batch leaves room for 552 records
-// against 438, and fewer batches are cut). Four-step chunks keep the per-wave
-// pads at 2 KB, so four workgroups per CU fit; eight-step chunks (cheaper
-// phase 2) need 4 KB pads and ran slower at three workgroups per CU or with
-// 127-entry batches.
+// per CU), measured on the 2M-splat and the high-overlap scenes with the
+// culled tile lists: 191-entry batches where splats cover few tiles; 127
+// where they cover many (more half-list records per entry: a smaller batch
+// leaves room for more records, and fewer batches are cut). Four-step chunks
+// keep the per-wave pads at 2 KB, so four workgroups per CU fit; three per CU
+// (more records) ran 40% slower, five (fewer) no faster.
 constexpr int kDeferChunk = 4, kDeferWG = 4;
-constexpr int kDeferBatchFew = 255, kDeferBatchMany = 191;
+constexpr int kDeferBatchFew = 191, kDeferBatchMany = 127;
 
 template <bool AW, bool DZ>
 __global__ __launch_bounds__(kWave) void gather_kernel(int n, const int* __restrict__ splat_offsets, long long n_slots,

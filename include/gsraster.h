@@ -109,8 +109,8 @@ enum {
      *               (half-list, position) records of those steps in registers
      *               (moments of s and w over their pixels) and store them;
      *               each entry's records are summed once per batch (no LDS
-     *               float adds). Batches of 255 entries, or 191 when the
-     *               splats average more than 16 tiles each.
+     *               float adds). Batches of 191 entries, or 127 when the
+     *               splats average more than 16 listed tiles each.
      *   WALK_ADD:   each step reduces its ten sums across the half-wave and
      *               adds them into the entry's LDS partial sums (float LDS
      *               adds; 255-entry batches);
