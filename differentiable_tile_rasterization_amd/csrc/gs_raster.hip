@@ -137,8 +137,9 @@ __device__ __forceinline__ void quadrant_pixel(int tile, int GX, int& x, int& y)
 constexpr int kRaw = 10;   // w g_r, w g_g, w g_b, s, s dx, s dy, s dx^2, s dx dy, s dy^2, w
 constexpr int kHalves = 8; // 4 waves x 2 halves
 
-// Staging test of the half-wave walk: hit[hq] says whether the splat can
-// reach half h of quadrant q (hq = 2 q + h; the 8x4 pixels of rows 4 h ..
+// Staging test of the half-wave walk: bit `lane` of hits[hq] (a wave ballot,
+// so that the lists are built from wave masks with no per-lane flags to pack
+// and unpack) says whether the lane's splat can reach half h of quadrant q (hq = 2 q + h; the 8x4 pixels of rows 4 h ..
 // 4 h + 3 of the quadrant), i.e. column q & 1 of 8-pixel columns and row
 // 2 (q >> 1) + h of 4-pixel rows. Over a rectangle of pixel centres, the
 // minimum of the convex form q' is 0 if the mean lies inside; otherwise it
@@ -153,7 +154,7 @@ constexpr int kHalves = 8; // 4 waves x 2 halves
 // nothing to cancellation for elongated splats. Halves whose walk ends at or
 // before entry k (`hend`, wave-uniform) drop the entry.
 __device__ __forceinline__ void half_hits(const SplatRec& r, float ox, float oy, int k, const int (&hend)[kHalves],
-                                          bool (&hit)[kHalves])
+                                          unsigned long long (&hits)[kHalves])
 {
     const float l11 = r.a.z, l21 = r.a.w, l22 = r.b.x, tau = r.c.y;
     // the minimiser along x = u is y = kv u; along y = v it is x = kh v
@@ -189,7 +190,7 @@ __device__ __forceinline__ void half_hits(const SplatRec& r, float ox, float oy,
         const float xs = __builtin_amdgcn_fmed3f(xv[rw], u0[c], u1[c]);
         const float a2 = __builtin_fmaf(l11, xs, pv[rw]);
         const float qh = __builtin_fmaf(a2, a2, sv[rw]);
-        hit[hq] = (fminf(qv, qh) <= tau) & (k < hend[hq]);
+        hits[hq] = __ballot((fminf(qv, qh) <= tau) & (k < hend[hq]));
     }
 }
 
@@ -267,7 +268,7 @@ constexpr unsigned short kSDummyOff = (unsigned short)(kSBatch * sizeof(StoreSlo
 // per-wave counts also ORs `flag` over the workgroup, which is returned, and
 // gives every half's list length (len, wave-uniform). Ends with a barrier.
 template <int NSlots = kSSlots, int ListLen = kSListLen>
-__device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bool flag, StoreSlot* S,
+__device__ __forceinline__ bool build_store_lists(const unsigned long long (&hits)[kHalves], bool flag, StoreSlot* S,
                                                  unsigned short (*list)[ListLen], int (*cnt)[kHalves + 1],
                                                  int (&len)[kHalves])
 {
@@ -276,7 +277,7 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
     int mine = __ballot(flag) != 0 ? 1 : 0;  // lane kHalves: the wave's flag
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
-        const int c = __popcll(__ballot(hit[q]));  // whole-wave ballot, outside any lane branch
+        const int c = __popcll(hits[q]);
         mine = lane == q ? c : mine;
     }
     if (lane <= kHalves) cnt[wv][lane] = mine;
@@ -298,8 +299,8 @@ __device__ __forceinline__ bool build_store_lists(const bool (&hit)[kHalves], bo
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
         len[q] = __builtin_amdgcn_readlane(tot, q);
-        const unsigned long long bal = __ballot(hit[q]);
-        if (hit[q]) {
+        const unsigned long long bal = hits[q];
+        if (__builtin_amdgcn_inverse_ballot_w64(bal)) {
             const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
             const int at = __builtin_amdgcn_readlane(top, q) - rank;
@@ -414,13 +415,13 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
         }
-        bool hit[kHalves] = {false, false, false, false, false, false, false, false};
-        if (threadIdx.x < kSSlots) half_hits(r, ox, oy, k, hend, hit);  // waves 0, 1: the candidates' waves
+        unsigned long long hits[kHalves] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (threadIdx.x < kSSlots) half_hits(r, ox, oy, k, hend, hits);  // waves 0, 1: the candidates' waves
         // Keep the top candidates whose half-list entries fit the partial
         // records: suffix sums of the hit counts over the slots, from the top.
         int hc = 0;
 #pragma unroll
-        for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
+        for (int q = 0; q < kHalves; ++q) hc += __builtin_amdgcn_inverse_ballot_w64(hits[q]) ? 1 : 0;
         int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
         for (int off = 1; off < kWave; off <<= 1) {
             const int u = __shfl_down(suf, off, kWave);
@@ -433,10 +434,8 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         const bool keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
         const unsigned long long kb = __ballot(keep);
         if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));
-        if (!keep) {
 #pragma unroll
-            for (int q = 0; q < kHalves; ++q) hit[q] = false;
-        }
+        for (int q = 0; q < kHalves; ++q) hits[q] &= kb;
         // The entry's pair slot: the splat's first slot (from its record) plus
         // the tile's row-major index inside the splat's tile rectangle
         // (recomputed from mean and radius with the binning's float32 rule).
@@ -461,7 +460,7 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
         // clamp's three instructions per step.
         const bool may_clamp = keep && id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
         int len[kHalves];
-        const bool clamp_batch = build_store_lists(hit, may_clamp, S, list, list_cnt, len);
+        const bool clamp_batch = build_store_lists(hits, may_clamp, S, list, list_cnt, len);
         int base[kHalves];  // first partial record of each half
         base[0] = 0;
 #pragma unroll
@@ -617,7 +616,8 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
             for (int q = 0; q < kHalves; ++q) {
                 const unsigned at = ((q < 4 ? pw.x : pw.y) >> (8 * (q & 3))) & 0xffu;
                 if (at != 0xffu) {
-                    const float* pr = parts + (half_base[q] + (int)at) * kF;
+                    // 24-bit multiply (full rate; the record index is below 2^24)
+                    const float* pr = parts + __mul24(half_base[q] + (int)at, kF);
 #pragma unroll
                     for (int f = 0; f < kF; ++f) u[f] += pr[f];
                 }
@@ -812,8 +812,8 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             S[threadIdx.x].b = r.b;
             S[threadIdx.x].c = r.c.x;
         }
-        bool hit[kHalves] = {false, false, false, false, false, false, false, false};
-        if (threadIdx.x < kDSlots) half_hits(r, ox, oy, k, hend, hit);  // the candidates' waves
+        unsigned long long hits[kHalves] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (threadIdx.x < kDSlots) half_hits(r, ox, oy, k, hend, hits);  // the candidates' waves
         // Keep the top candidates whose half-list entries fit the partial
         // records. Usually all of them do (the wave totals, from ballots, say
         // so); otherwise suffix sums of the hit counts over the slots, from
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         {
             int wtot = 0;  // this wave's half-list entries (wave-uniform)
 #pragma unroll
-            for (int q = 0; q < kHalves; ++q) wtot += __popcll(__ballot(hit[q]));
+            for (int q = 0; q < kHalves; ++q) wtot += __popcll(hits[q]);
             if (lane == 0) wave_hits[wv] = wtot;
             if (threadIdx.x == 0) cut = NB;
         }
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         if (total > kCap) {  // workgroup-uniform
             int hc = 0;
 #pragma unroll
-            for (int q = 0; q < kHalves; ++q) hc += hit[q] ? 1 : 0;
+            for (int q = 0; q < kHalves; ++q) hc += __builtin_amdgcn_inverse_ballot_w64(hits[q]) ? 1 : 0;
             int suf = hc;  // inclusive suffix sum inside the wave (higher lanes)
             for (int off = 1; off < kWave; off <<= 1) {
                 const int u = __shfl_down(suf, off, kWave);
@@ -841,10 +841,8 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             keep = cand && suf <= kCap;  // monotone: every slot above a kept one is kept
             const unsigned long long kb = __ballot(keep);
             if (kb != 0 && lane == 0) atomicMin(&cut, (int)threadIdx.x + __builtin_ctzll(kb));  // lowest kept
-            if (!keep) {
 #pragma unroll
-                for (int q = 0; q < kHalves; ++q) hit[q] = false;
-            }
+            for (int q = 0; q < kHalves; ++q) hits[q] &= kb;
         }
         // The entry's pair slot: the splat's first slot (from its record) plus
         // the tile's row-major index inside the splat's tile rectangle
@@ -873,7 +871,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         // clamp's three instructions per step.
         const bool may_clamp = keep && id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
         int len[kHalves];
-        const bool clamp_batch = build_store_lists<kDSlots, kDListLen>(hit, may_clamp, S, list, list_cnt, len);
+        const bool clamp_batch = build_store_lists<kDSlots, kDListLen>(hits, may_clamp, S, list, list_cnt, len);
         int base[kHalves];  // first partial record of each half
         base[0] = 0;
 #pragma unroll
@@ -1098,7 +1096,8 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             for (int q = 0; q < kHalves; ++q) {
                 const unsigned at = ((q < 4 ? pw.x : pw.y) >> (8 * (q & 3))) & 0xffu;
                 if (at != 0xffu) {
-                    const float* pr = parts + (half_base[q] + (int)at) * kF;
+                    // 24-bit multiply (full rate; the record index is below 2^24)
+                    const float* pr = parts + __mul24(half_base[q] + (int)at, kF);
 #pragma unroll
                     for (int f = 0; f < kF; ++f) u[f] += pr[f];
                 }
@@ -1147,7 +1146,7 @@ constexpr unsigned short kAddDummyOff = (unsigned short)(kDummy * sizeof(AddSlot
 // offsets in descending slot order (the walk's order). The same exchange of
 // per-wave counts also ORs `flag` over the workgroup, which is returned.
 // Ends with a workgroup barrier.
-__device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool flag,
+__device__ __forceinline__ bool build_add_lists(const unsigned long long (&hits)[kHalves], bool flag,
                                                  unsigned short (*list)[kListLen], int (*cnt)[kHalves + 1])
 {
     const int lane = threadIdx.x & 63;
@@ -1155,7 +1154,7 @@ __device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool
     int mine = __ballot(flag) != 0 ? 1 : 0;  // lane kHalves: the wave's flag
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
-        const int c = __popcll(__ballot(hit[q]));  // whole-wave ballot, outside any lane branch
+        const int c = __popcll(hits[q]);
         mine = lane == q ? c : mine;
     }
     if (lane <= kHalves) cnt[wv][lane] = mine;
@@ -1175,8 +1174,8 @@ __device__ __forceinline__ bool build_add_lists(const bool (&hit)[kHalves], bool
     }
 #pragma unroll
     for (int q = 0; q < kHalves; ++q) {
-        const unsigned long long bal = __ballot(hit[q]);
-        if (hit[q]) {
+        const unsigned long long bal = hits[q];
+        if (__builtin_amdgcn_inverse_ballot_w64(bal)) {
             const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
             list[q][__builtin_amdgcn_readlane(top, q) - rank] =
@@ -1281,15 +1280,15 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
         *add_part4(S[threadIdx.x], 0) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         *add_part4(S[threadIdx.x], 1) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         *reinterpret_cast<float2*>(S[threadIdx.x].part + 8) = make_float2(0.0f, 0.0f);
-        bool hit[kHalves];
-        half_hits(r, ox, oy, k, hend, hit);
+        unsigned long long hits[kHalves];
+        half_hits(r, ox, oy, k, hend, hits);
         // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
         // exponent never exceeds log2 o, so alpha_raw never exceeds
         // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
         // 0.99 never clamps. Most batches have none, and their walk skips the
         // clamp's three instructions per step.
         const bool may_clamp = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
-        const bool clamp_batch = build_add_lists(hit, may_clamp, list, list_cnt);
+        const bool clamp_batch = build_add_lists(hits, may_clamp, list, list_cnt);
         // this half's list length, and the wave's step count (longer half)
         const int my_len = list_cnt[0][hq] + list_cnt[1][hq] + list_cnt[2][hq] + list_cnt[3][hq];
         const int other = hq ^ 1;
@@ -1570,13 +1569,13 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             uint4* z = reinterpret_cast<uint4*>(&mw_rec[0][0]) + 2 * threadIdx.x;
             z[0] = z[1] = make_uint4(0u, 0u, 0u, 0u);
         }
-        bool hit[kHalves];
-        half_hits(r, ox, oy, 0, hend, hit);
+        unsigned long long hits[kHalves];
+        half_hits(r, ox, oy, 0, hend, hits);
         // ascending slot order: list position = (hits in lower waves and lanes)
         int mine = 0;
 #pragma unroll
         for (int q = 0; q < kHalves; ++q) {
-            const int c = __popcll(__ballot(hit[q]));
+            const int c = __popcll(hits[q]);
             mine = lane == q ? c : mine;
         }
         if (lane < kHalves) list_cnt[wv][lane] = mine;
@@ -1587,8 +1586,8 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         unsigned pos_lo = ~0u, pos_hi = ~0u;  // MW: the entry's list positions, a byte per half
 #pragma unroll
         for (int q = 0; q < kHalves; ++q) {
-            const unsigned long long bal = __ballot(hit[q]);
-            if (hit[q]) {
+            const unsigned long long bal = hits[q];
+            if (__builtin_amdgcn_inverse_ballot_w64(bal)) {
                 const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
                 const int at = __builtin_amdgcn_readlane(below, q) + rank;
