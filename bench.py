@@ -7,7 +7,11 @@ workload: the fixed raster_bench load of the Spirula Studio page (section
 亲手验证): 2,000,000 splats at 1237x822, 20 timed iterations.
 
 Prints one JSON line with the metric (pairs/s; pairs = sum over pixels of
-n_contrib, the list entries the backward must revisit), ms/call, a roofline
+n_contrib under the tile-rectangle lists, i.e. the list entries a backward
+must revisit when each splat is listed in every tile of its rectangle: the
+scene's count, which does not depend on how tightly the binning culls; the
+library's own lists skip the tiles a splat's alpha >= 1/255 ellipse cannot
+reach, and their smaller sum is reported beside it), ms/call, a roofline
 object for the call's dominant kernel, the reverse walk, and a CPU baseline
 (the float64 oracle on the same scene, on the host's threads, plus one-thread
 times of the three small workloads).
@@ -78,6 +82,49 @@ def kernel_source_hash() -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def rect_walk_pairs(torch, m, r, d, width, height, n_contrib, sorted_ids, tile_ranges):
+    """Per pixel, n_contrib under the tile-rectangle lists: the number of
+    splats of the pixel's tile rectangle list (every splat whose rectangle
+    covers the tile, in (depth bits, id) order) up to and including the last
+    one the pixel composites. The last composited splat comes from the
+    culled lists the forward walked (a culled list keeps the rectangle
+    list's order and drops only splats that cannot composite there). All on
+    the device; int64 [height, width]."""
+    dev = m.device
+    f32 = torch.float32
+    GX, GY = (width + 15) // 16, (height + 15) // 16
+    rf = r.to(f32)
+    # the binning's float32 tile rectangle
+    tx0 = torch.floor((m[:, 0] - rf) * 0.0625).clamp(0, GX)
+    tx1 = (torch.floor((m[:, 0] + rf) * 0.0625) + 1.0).clamp(0, GX)
+    ty0 = torch.floor((m[:, 1] - rf) * 0.0625).clamp(0, GY)
+    ty1 = (torch.floor((m[:, 1] + rf) * 0.0625) + 1.0).clamp(0, GY)
+    live = (r > 0) & (d > 0) & torch.isfinite(m[:, 0]) & torch.isfinite(m[:, 1])
+    tx0, tx1, ty0, ty1 = (v.nan_to_num(0.0).to(torch.int64) for v in (tx0, tx1, ty0, ty1))
+    nx, ny = (tx1 - tx0).clamp(min=0), (ty1 - ty0).clamp(min=0)
+    cnt = torch.where(live, nx * ny, torch.zeros_like(nx))
+    n = m.shape[0]
+    # each splat's rank in (depth bits, id) order
+    order = torch.sort(d.view(torch.int32).to(torch.int64) * (1 << 32) + torch.arange(n, device=dev)).indices
+    drank = torch.empty(n, dtype=torch.int64, device=dev)
+    drank[order] = torch.arange(n, device=dev)
+    sid = torch.repeat_interleave(torch.arange(n, device=dev), cnt)
+    local = torch.arange(sid.numel(), device=dev) - torch.repeat_interleave(torch.cumsum(cnt, 0) - cnt, cnt)
+    nxs = nx[sid]
+    tile = (ty0[sid] + local // nxs) * GX + tx0[sid] + local % nxs
+    sh = 1 << max(1, (n - 1).bit_length())  # above every depth rank
+    keys = torch.sort(tile * sh + drank[sid]).values
+    del sid, local, nxs, tile
+    ys, xs = torch.meshgrid(torch.arange(height, device=dev), torch.arange(width, device=dev), indexing="ij")
+    tp = (ys // 16) * GX + xs // 16
+    nc = n_contrib.to(torch.int64)
+    start = tile_ranges[:, 0].to(torch.int64)[tp]
+    last = sorted_ids.to(torch.int64)[(start + nc - 1).clamp(min=0)]
+    kp = tp * sh + drank[last]
+    upto = torch.searchsorted(keys, kp, right=True) - torch.searchsorted(keys, tp * sh)
+    return torch.where(nc > 0, upto, torch.zeros_like(upto))
 
 
 def load_probe():
@@ -182,6 +229,9 @@ def main():
     groups_half, groups_blk, iters_half, iters_blk = cnt[7:11]
     p_walk_check = int(nc.to(torch.int64).sum().item())
     assert p_walk == p_walk_check, (p_walk, p_walk_check)
+    nrect = rect_walk_pairs(torch, m, r, d, sc.width, sc.height, nc, bins.sorted_ids, bins.tile_ranges)
+    p_rect = int(nrect.sum().item())
+    assert p_rect >= p_walk, (p_rect, p_walk)
 
     # ---- measured ceilings
     def gpu_time(fn, reps=5):
@@ -277,11 +327,10 @@ def main():
         m, q, c, o, d, r, bg, sc.width, sc.height, bins, T, nc, fwd_d["median_pos"], g,
         dist_totals=fwd_d["dist_totals"], dL_ddist=gD, dL_dmedian=gM, accum_weight=aw, out=out_d, workspace=ws),
         10, 2)
-    t0 = time.perf_counter()
-    for _ in range(3):
-        gsr.gs_bin_tiles(m, q, o, r, d, sc.width, sc.height, capacity=bins.n_isect)
-    torch.cuda.synchronize()
-    t_bin = (time.perf_counter() - t0) / 3 * 1e3
+    # the binning: events around each call (it waits once on the host for its
+    # pair counts, so a call's span includes that wait), median of 10
+    t_bin = float(np.median(per_call(lambda: gsr.gs_bin_tiles(m, q, o, r, d, sc.width, sc.height,
+                                                              capacity=bins.n_isect), 10, 3)))
 
     # ---- roofline of the reverse walk (the call's dominant kernel)
     ms = float(ms_region)
@@ -356,9 +405,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        cpu = cpu_baseline(oracle, sc, bins, nc, args, log)
+        cpu = cpu_baseline(oracle, sc, bins, nc, nrect, args, log)
 
-    value = p_walk / t_s
+    value = p_rect / t_s
     rec = {
         "metric": "rasterize_bwd ms/call + (splat,pixel) pairs/s", "value": value, "unit": "pairs/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -373,7 +422,9 @@ def main():
                       "raster_fwd_depth": float(np.median(t_fwd_depth)),
                       "raster_bwd_depth": float(np.median(t_bwd_depth)), "raster_bwd": ms,
                       "raster_bwd_median": float(np.median(t_calls)), "raster_bwd_min": float(np.min(t_calls))},
-        "counts": {"p_walk": p_walk, "p_composited": p_contrib, "walked_entries": entries,
+        "pairs": {"value_counts": "p_walk_rect (sum of n_contrib under the tile-rectangle lists)",
+                  "p_walk_rect": p_rect, "pairs_per_s_own_lists": p_walk / t_s},
+        "counts": {"p_walk": p_walk, "p_walk_rect": p_rect, "p_composited": p_contrib, "walked_entries": entries,
                    "splat_tile_groups": groups_tile, "splat_quadrant_groups": groups_wave,
                    "entry_quadrant_walk": ew_walk, "entry_quadrant_kept": ew_kept, "n_isect": bins.n_isect,
                    "n_slots": bins.n_slots,
@@ -384,7 +435,7 @@ def main():
     print(json.dumps(rec))
 
 
-def cpu_baseline(oracle, sc, bins, nc, args, log):
+def cpu_baseline(oracle, sc, bins, nc, nrect, args, log):
     """The float64 oracle on the host: forward and backward of the timed
     scene over a sample of its tiles (all tiles by default) on every host
     thread, and both on one thread for the three small workloads (tiny, early,
@@ -402,7 +453,8 @@ def cpu_baseline(oracle, sc, bins, nc, args, log):
     nc_h = nc.cpu().numpy()
     ys, xs = np.mgrid[0:sc.height, 0:sc.width]
     sel = np.isin((ys // 16) * GX + xs // 16, tiles)
-    pw_sample = int(nc_h[sel].astype(np.int64).sum())
+    # the sample's pairs counted like the GPU's value (tile-rectangle lists)
+    pw_sample = int(nrect.cpu().numpy()[sel].sum())
     # the host threads OpenMP is given (OMP_NUM_THREADS: the CPU share of this
     # job, which may be fewer than the host's cores)
     threads = oracle.threads()
@@ -439,8 +491,8 @@ def cpu_baseline(oracle, sc, bins, nc, args, log):
             "host_cpu_count": os.cpu_count(), "forward_s": f_s, "backward_s": b_s,
             "forward_pairs_per_s": pw_sample / f_s,
             "sample": f"float64 oracle rasterize_fwd and rasterize_bwd over {k} of {ntiles} tiles (random, "
-                      f"seed 0) of the same scene, {pw_sample} walked pairs, on {used} threads; binning excluded; "
-                      "value = walked pairs / backward seconds",
+                      f"seed 0) of the same scene, {pw_sample} walked pairs (tile-rectangle lists, as the GPU "
+                      f"value), on {used} threads; binning excluded; value = those pairs / backward seconds",
             "single_thread": single}
 
 
