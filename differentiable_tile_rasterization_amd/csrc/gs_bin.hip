@@ -13,8 +13,9 @@
 //   3. host    read both totals back (the call's only synchronisation; the
 //              depth sort is already queued behind the copy)
 //   4. depth   stable LSD radix sort of the splats by the bit pattern of their
-//              depth (32 bits, 8-bit digits), splat ids starting in id order
-//   5. emit    the kept counts gathered into depth order and scanned; the
+//              depth (32 bits, 8-bit digits), splat ids starting in id order;
+//              the last pass also gathers the kept counts into depth order
+//   5. emit    the kept counts in depth order scanned; the
 //              splat of depth rank k reads its rectangle and ellipse factors
 //              (stored by the count pass) and writes its kept tiles,
 //              row-major, at that offset, as (tile id, splat id), tile ids
@@ -192,20 +193,15 @@ __device__ __forceinline__ int2 cull_row(const CullEllipse E, int ty, int tx0, i
     return make_int2(max((int)cl, tx0), min((int)ch, tx1 - 1));
 }
 
-// counts[i] = number of tiles of splat i's rectangle, kept[i] = the number of
-// them its culling ellipse keeps; recs[i] = what the emission needs (the
-// rectangle (tx0, ty0, tx1, ty1), empty for a culled splat: a grid has at
-// most 2048 tiles per side, so 16 bits per bound suffice).
-__global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
-                                                    const float* __restrict__ conics,
-                                                    const float* __restrict__ opacities,
-                                                    const int* __restrict__ radii,
-                                                    const float* __restrict__ depths, int GX, int GY,
-                                                    unsigned* __restrict__ counts, unsigned* __restrict__ kept,
-                                                    CullRec* __restrict__ recs)
+// One splat's counts and emission record (count_kernel below); returns its
+// kept count.
+__device__ __forceinline__ unsigned count_splat(int i, const float2* __restrict__ means,
+                                                const float* __restrict__ conics,
+                                                const float* __restrict__ opacities, const int* __restrict__ radii,
+                                                const float* __restrict__ depths, int GX, int GY,
+                                                unsigned* __restrict__ counts, unsigned* __restrict__ kept,
+                                                CullRec* __restrict__ recs)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
     const float2 m = means[i];
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
@@ -228,6 +224,23 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
     counts[i] = live ? (unsigned)((tx1 - tx0) * (ty1 - ty0)) : 0u;  // at most 2048 x 2048
     kept[i] = k;
     recs[i] = r;
+    return k;
+}
+
+// counts[i] = number of tiles of splat i's rectangle, kept[i] = the number of
+// them its culling ellipse keeps; recs[i] = what the emission needs (the
+// rectangle (tx0, ty0, tx1, ty1), empty for a culled splat: a grid has at
+// most 2048 tiles per side, so 16 bits per bound suffice).
+__global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restrict__ means,
+                                                    const float* __restrict__ conics,
+                                                    const float* __restrict__ opacities,
+                                                    const int* __restrict__ radii,
+                                                    const float* __restrict__ depths, int GX, int GY,
+                                                    unsigned* __restrict__ counts, unsigned* __restrict__ kept,
+                                                    CullRec* __restrict__ recs)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) count_splat(i, means, conics, opacities, radii, depths, GX, GY, counts, kept, recs);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,14 +337,6 @@ hipError_t exclusive_scan(const unsigned* in, unsigned* out, long long n, unsign
 // ---------------------------------------------------------------------------
 // Depth order and emission.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gather_kept_kernel(int n, const int* __restrict__ by_depth,
-                                                          const unsigned* __restrict__ kept,
-                                                          unsigned* __restrict__ cnt_sorted)
-{
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n) return;
-    cnt_sorted[k] = kept[by_depth[k]];
-}
 
 // Emission: one thread per depth rank k. The splat of rank k writes its kept
 // tiles, row by row and left to right, from emit_off[k], as (tile id, splat
@@ -422,7 +427,9 @@ __global__ __launch_bounds__(SortTiling<W>::kThreads) void radix_scatter_kernel(
                                                                                 long long n, int shift, int nwg,
                                                                                 const unsigned* __restrict__ offs,
                                                                                 K* __restrict__ keys_out,
-                                                                                int* __restrict__ vals_out)
+                                                                                int* __restrict__ vals_out,
+                                                                                const unsigned* __restrict__ gat_in,
+                                                                                unsigned* __restrict__ gat_out)
 {
     constexpr int R = 1 << BITS;
     constexpr int kSortWaves = W, kSortThreads = SortTiling<W>::kThreads, kSortTile = SortTiling<W>::kTile;
@@ -526,7 +533,9 @@ __global__ __launch_bounds__(SortTiling<W>::kThreads) void radix_scatter_kernel(
             const unsigned d = (unsigned)(k >> shift) & (R - 1);
             const unsigned pos = global_off[d] + ((unsigned)lp - local_start[d]);
             keys_out[pos] = k;
-            vals_out[pos] = lval[lp];
+            const int v = lval[lp];
+            vals_out[pos] = v;
+            if (gat_out) gat_out[pos] = gat_in[v];  // a word of the value's, into the output order
         }
     }
 }
@@ -621,7 +630,8 @@ BinLayout bin_layout(long long n, long long cap)
 // One stable LSD pass over the BITS-bit digit at `shift` of keys_in -> keys_out.
 template <typename K, int BITS, int W>
 hipError_t radix_pass_b(const K* kin, const int* vin, K* kout, int* vout, long long cnt, int shift, unsigned* hist,
-                        unsigned long long* part, unsigned long long* total, hipStream_t st)
+                        unsigned long long* part, unsigned long long* total, hipStream_t st,
+                        const unsigned* gat_in = nullptr, unsigned* gat_out = nullptr)
 {
     constexpr int kSortThreads = SortTiling<W>::kThreads, kSortTile = SortTiling<W>::kTile;
     const int nwg = (int)((cnt + kSortTile - 1) / kSortTile);
@@ -630,7 +640,8 @@ hipError_t radix_pass_b(const K* kin, const int* vin, K* kout, int* vout, long l
     if (e != hipSuccess) return e;
     e = exclusive_scan(hist, hist, (long long)(1 << BITS) * nwg, part, total, st);
     if (e != hipSuccess) return e;
-    radix_scatter_kernel<K, BITS, W><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout);
+    radix_scatter_kernel<K, BITS, W><<<nwg, kSortThreads, 0, st>>>(kin, vin, cnt, shift, nwg, hist, kout, vout,
+                                                                   gat_in, gat_out);
     return hipGetLastError();
 }
 
@@ -783,7 +794,9 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
                                                       GX, GY, counts, kept, recs);
         GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(counts, offsets, n, part, pairs, st));
-        // the kept total (the scan's output goes to emit_off, rewritten below)
+        // the kept total (one atomic per wave into a single word serialised at
+        // the L2 and doubled the binning's time); the scan's output goes to
+        // emit_off, rewritten below
         GS_HIP(exclusive_scan(kept, emit_off, n, part, pairs + 1, st));
         unsigned long long* pin = pinned_count();
         CountEvent ev;
@@ -802,8 +815,11 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
         unsigned* dk_out = dkb;
         int* dv_out = dvb;
         for (int shift = 0; shift < 32; shift += kRadixBits) {
+            // the last pass also gathers the kept counts into depth order
+            const bool last = shift + kRadixBits >= 32;
             GS_HIP((radix_pass_b<unsigned, kRadixBits, kDepthWaves>(dk_in, dv_in, dk_out, dv_out, n, shift, hist, part,
-                                                                     total, st)));
+                                                                     total, st, last ? kept : nullptr,
+                                                                     last ? cnt_sorted : nullptr)));
             dk_in = dk_out;
             dv_in = dv_out;
             dk_out = dk_out == dkb ? dka : dkb;
@@ -811,8 +827,6 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
         }
         by_depth = dv_in;
         // Emission offsets in depth order.
-        gather_kept_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, by_depth, kept, cnt_sorted);
-        GS_HIP(hipGetLastError());
         GS_HIP(exclusive_scan(cnt_sorted, emit_off, n, part, total, st));
         if (pin) {
             GS_HIP(hipEventSynchronize(ev.e));
