@@ -217,8 +217,10 @@ def row_columns(ce, idx, ty, tx0, tx1):
         ch = np.minimum(np.maximum(np.floor((xr - f(0.5)) * f(0.0625)), txf0 - f(2.0)), txf1)
         ch = np.where((ch + f(1.0)) * f(16.0) + f(0.5) <= xr, ch + f(1.0), ch)
         ch = np.where(ch * f(16.0) + f(0.5) > xr, ch - f(1.0), ch)
-    c_lo = np.maximum(cl.astype(np.int64), tx0)
-    c_hi = np.minimum(ch.astype(np.int64), tx1 - 1)
+    # (rows of splats whose constants are not usable compute NaN here; their
+    # pairs take the whole rectangle or nothing, see kept_pairs)
+    c_lo = np.maximum(np.nan_to_num(cl).astype(np.int64), tx0)
+    c_hi = np.minimum(np.nan_to_num(ch).astype(np.int64), tx1 - 1)
     empty = ~row_ok
     c_lo = np.where(empty, tx1, c_lo)
     c_hi = np.where(empty, tx1 - 1, c_hi)

@@ -291,6 +291,15 @@ def test_culled_and_offscreen_splats():
             assert np.all(r[k][:18] == 0.0)
 
 
+def test_binning_degenerate_culling_constants():
+    """The culling's degenerate modes (factors not finite or not positive:
+    the whole rectangle; 255 o below 1 or NaN: nowhere; 255 o rounding to 1:
+    a speck) list the same pairs as the oracle."""
+    from test_oracle_pins import degenerate_cull_scene
+    sc = degenerate_cull_scene()
+    check_bins(sc, gpu_bins(sc))
+
+
 def test_no_splats_and_no_intersections():
     sc = _custom(9, 32, 32, 4, pad=0)
     sc.radii[:] = 0

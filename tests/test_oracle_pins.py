@@ -287,6 +287,45 @@ def test_culled_splats_never_binned():
     assert not np.isin([0, 1, 2, 3], ids).any()
 
 
+def degenerate_cull_scene():
+    """Splats whose culling constants are degenerate, each with a non-empty
+    rectangle: the binning keeps the whole rectangle where the factors are not
+    finite and positive, and nothing where 255 o < 1 (float32) or o is NaN.
+    Shared with the GPU binning test."""
+    sc = _ragged_scene(21, n=40)
+    f = np.float32
+    sc.radii[:12] = np.maximum(sc.radii[:12], 20)
+    sc.depths[:12] = np.abs(sc.depths[:12]) + f(1.0)
+    q = sc.conics
+    q[0] = (0.0, 0.0, 0.5)                 # a = 0: l11 = 0
+    q[1] = (-0.2, 0.0, 0.5)                # a < 0: l11 NaN
+    q[2] = (0.25, 0.5, 1.0)                # c = b^2 / a: l22 = 0
+    q[3] = (np.inf, 0.0, 0.5)              # l11 infinite
+    q[4] = (0.3, 0.0, np.nan)              # l22 NaN
+    sc.opacities[5] = f(0.5 / 255.0)       # 255 o < 1: nowhere
+    sc.opacities[6] = f(np.nan)            # nowhere
+    sc.opacities[7] = f(np.inf)            # T infinite: whole rectangle
+    sc.opacities[8] = f(1.0) / f(255.0)    # 255 o rounds to 1: T = 2^-10, a speck
+    sc.opacities[9] = np.nextafter(f(1.0) / f(255.0), f(0.0))
+    return sc
+
+
+def test_culling_degenerate_inputs():
+    sc = degenerate_cull_scene()
+    ids, tx, ty, kept = oracle.kept_pairs(sc.means2d, sc.conics, sc.opacities, sc.radii, sc.depths, sc.width,
+                                          sc.height)
+    for i in range(5):
+        assert (ids == i).sum() > 0 and kept[ids == i].all(), i      # whole rectangle
+    for i in (5, 6):
+        assert (ids == i).sum() > 0 and not kept[ids == i].any(), i  # nowhere
+    assert kept[ids == 7].all()
+    # 255 o rounded to 1: the threshold is 2^-10, the ellipse a speck around
+    # the mean: at most the tiles holding pixel centres within ~0.1 px of it
+    assert 0 < kept[ids == 8].sum() <= 4
+    y9 = np.float32(255.0) * sc.opacities[9]
+    assert kept[ids == 9].any() == bool(y9 >= 1.0)
+
+
 # ---------------------------------------------------------------- gradients
 
 def _fd_scene(seed, n=6, bg=None, clamp=False):
