@@ -200,13 +200,13 @@ __device__ __forceinline__ unsigned count_splat(int i, const float2* __restrict_
                                                 const float* __restrict__ opacities, const int* __restrict__ radii,
                                                 const float* __restrict__ depths, int GX, int GY,
                                                 unsigned* __restrict__ counts, unsigned* __restrict__ kept,
-                                                CullRec* __restrict__ recs)
+                                                CullRec& r)
 {
     const float2 m = means[i];
     int tx0, tx1, ty0, ty1;
     const bool live = splat_rect(m.x, m.y, radii[i], depths[i], GX, GY, tx0, tx1, ty0, ty1);
     unsigned k = 0;
-    CullRec r{};
+    r = CullRec{};
     if (live) {
         const CullEllipse E = cull_ellipse(m, conics[3 * i], conics[3 * i + 1], conics[3 * i + 2], opacities[i]);
         for (int ty = ty0; ty < ty1; ++ty) {
@@ -223,7 +223,6 @@ __device__ __forceinline__ unsigned count_splat(int i, const float2* __restrict_
     }
     counts[i] = live ? (unsigned)((tx1 - tx0) * (ty1 - ty0)) : 0u;  // at most 2048 x 2048
     kept[i] = k;
-    recs[i] = r;
     return k;
 }
 
@@ -239,8 +238,20 @@ __global__ __launch_bounds__(256) void count_kernel(int n, const float2* __restr
                                                     unsigned* __restrict__ counts, unsigned* __restrict__ kept,
                                                     CullRec* __restrict__ recs)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) count_splat(i, means, conics, opacities, radii, depths, GX, GY, counts, kept, recs);
+    // the block's records go out through LDS as consecutive 16-byte stores by
+    // consecutive threads (not two per thread at a 32-byte stride)
+    __shared__ float4 buf[2 * 256];
+    const int i0 = blockIdx.x * 256, i = i0 + threadIdx.x;
+    CullRec r{};
+    if (i < n) count_splat(i, means, conics, opacities, radii, depths, GX, GY, counts, kept, r);
+    static_assert(sizeof(CullRec) == 2 * sizeof(float4), "two float4 per record");
+    const float4* rv = reinterpret_cast<const float4*>(&r);
+    buf[2 * threadIdx.x + 0] = rv[0];
+    buf[2 * threadIdx.x + 1] = rv[1];
+    __syncthreads();
+    const int cnt = 2 * min(256, n - i0);
+    float4* const out = reinterpret_cast<float4*>(recs + i0);
+    for (int k = threadIdx.x; k < cnt; k += 256) out[k] = buf[k];
 }
 
 // ---------------------------------------------------------------------------

@@ -72,6 +72,23 @@ __device__ __forceinline__ SplatRec make_rec(int i, const float2* __restrict__ m
     return r;
 }
 
+// Stores the records of a 256-thread block (thread t: record i0 + t, those
+// below n) through LDS, as consecutive 16-byte stores by consecutive threads
+// rather than three 16-byte stores per thread at a 48-byte stride. Every
+// thread of the block must call it.
+__device__ __forceinline__ void store_recs_block(SplatRec* __restrict__ recs, const SplatRec& r, int i0, int n)
+{
+    __shared__ float4 buf[3 * 256];
+    const int t = threadIdx.x;
+    buf[3 * t + 0] = r.a;
+    buf[3 * t + 1] = r.b;
+    buf[3 * t + 2] = r.c;
+    __syncthreads();
+    const int cnt = 3 * min(256, n - i0);
+    float4* const out = reinterpret_cast<float4*>(recs + i0);
+    for (int k = t; k < cnt; k += 256) out[k] = buf[k];
+}
+
 // depths may be NULL; when given (the forward's depth outputs) the depth takes
 // the record's last word, which only the backward uses otherwise.
 __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restrict__ means,
@@ -79,11 +96,13 @@ __global__ __launch_bounds__(256) void prep_kernel(int n, const float2* __restri
                                                    const float* __restrict__ opac, const int* __restrict__ radii,
                                                    const float* __restrict__ depths, SplatRec* __restrict__ recs)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    SplatRec r = make_rec(i, means, conics, colors, opac, radii);
-    if (depths) r.c.w = depths[i];
-    recs[i] = r;
+    const int i0 = blockIdx.x * 256, i = i0 + threadIdx.x;
+    SplatRec r{};
+    if (i < n) {
+        r = make_rec(i, means, conics, colors, opac, radii);
+        if (depths) r.c.w = depths[i];
+    }
+    store_recs_block(recs, r, i0, n);
 }
 
 // Pixel of thread threadIdx.x in the walks: wave w owns the 8x8 quadrant
@@ -1779,9 +1798,11 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(int W, int H, int GX, in
         if (lane == 0) cost[tile] = v;
         return;
     }
-    if (b < cost_blocks + rec_blocks) {
-        const int i = (b - cost_blocks) * 256 + threadIdx.x;
-        if (i < n) recs[i] = make_rec(i, means, conics, colors, opac, radii, splat_offsets);
+    if (b < cost_blocks + rec_blocks) {  // block-uniform
+        const int i0 = (b - cost_blocks) * 256, i = i0 + threadIdx.x;
+        SplatRec r{};
+        if (i < n) r = make_rec(i, means, conics, colors, opac, radii, splat_offsets);
+        store_recs_block(recs, r, i0, n);
         return;
     }
     const long long i = (long long)(b - cost_blocks - rec_blocks) * 256 + threadIdx.x;
