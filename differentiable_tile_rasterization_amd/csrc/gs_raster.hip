@@ -694,6 +694,9 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     constexpr int kF = PP::kF, kCap = PP::kCap, kDSlots = PP::kSlots, kDListLen = PP::kListLen;
     constexpr int kZ = PP::kZ;
     constexpr unsigned short kDDummyOff = PP::kDummyOff;
+    // list entries read ahead of the step that uses them (four record buffers
+    // where the registers allow, two with the depth terms)
+    constexpr int kAhead = DEP ? 2 : 4;
     constexpr int kLPR = 32 / KC;   // phase 2: lanes per (half, position) record
     constexpr int kPPL = KC;        // phase 2: pixels per lane (a row or part of one)
     __shared__ StoreSlot S[kDSlots];
@@ -932,7 +935,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         // both run a whole number of chunks (steps rounded up to KC) and read
         // two entries past that, ahead of use
         const int steps_kc = (steps + KC - 1) & ~(KC - 1);
-        for (int p = my_len + (lane & 31); p < steps_kc + 2; p += 32) list[hq][p] = kDDummyOff;
+        for (int p = my_len + (lane & 31); p < steps_kc + kAhead; p += 32) list[hq][p] = kDDummyOff;
         // batch slots below this pixel's walk end, as a byte offset bound
         const int ncb_off = (nc - lo) * (int)sizeof(StoreSlot);
         const unsigned short* L = list[hq];
@@ -994,14 +997,16 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         // column offsets kx = 0..7 (dx = dx0 + kx, dy constant along the row)
         // and w g; four lanes (the rows of the half) then add their totals,
         // and the first stores the (half, position) record.
-        auto phase2 = [&](int c) {
-            const int jr = lane / (2 * kLPR);   // this lane's record: step c + jr of half ph
+        const int jr = lane / (2 * kLPR);   // phase 2: this lane's record is step c + jr of half ph
+        // the mean of that record's entry (both halves' lists hold entries or
+        // dummies up to the padded step count, which c + jr stays below)
+        auto rec_mean = [&](int c) -> float2 {
+            const int off = (int)Lp[c + jr];
+            return *reinterpret_cast<const float2*>(Sb + off);
+        };
+        auto phase2 = [&](int c, float2 mu) {
             const int p = c + jr;
             const bool valid = p < ph_len;
-            // both halves' lists hold entries or dummies up to the padded
-            // step count, which p stays below
-            const int off = (int)Lp[p];
-            const float2 mu = *reinterpret_cast<const float2*>(Sb + off);
             const float4* pp = reinterpret_cast<const float4*>(&pad[wv][jr][32 * ph + 8 * pu + pkx0]);
             float w_[kPPL], s_[kPPL];
 #pragma unroll
@@ -1073,11 +1078,53 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             }
         };
         // Every chunk runs all KC steps (the lists hold dummies up to a whole
-        // number of chunks), in pairs over two record buffers, each refilled
-        // one entry ahead of its use: the loads land where the next step reads
+        // number of chunks) over kAhead record buffers, each refilled kAhead - 1
+        // entries ahead of its use: the loads land where a later step reads
         // them, with no register copies.
         static_assert(KC % 2 == 0, "steps run in pairs");
         auto walk = [&](auto clamp_tag) {
+            if constexpr (kAhead == 4) {
+                // four record buffers: each entry's coefficients are requested
+                // three steps before its use
+                static_assert(KC == 4, "one rotation of the four buffers per chunk");
+                int o0 = list_at(0), o1 = list_at(1), o2 = list_at(2), o3 = list_at(3);
+                float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+                float C0 = rec_at(o0).c;
+                float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+                float C1 = rec_at(o1).c;
+                float4 A2 = rec_at(o2).a, B2 = rec_at(o2).b;
+                float C2 = rec_at(o2).c;
+                for (int c = 0; c < steps_kc; c += KC) {
+                    const float2 mu = rec_mean(c);  // phase 2's, requested before the steps
+                    const float4 A3 = rec_at(o3).a, B3 = rec_at(o3).b;
+                    const float C3 = rec_at(o3).c;
+                    const int n0 = list_at(c + 4);
+                    step(A0, B0, C0, 0.0f, o0, 0, clamp_tag);
+                    A0 = rec_at(n0).a;
+                    B0 = rec_at(n0).b;
+                    C0 = rec_at(n0).c;
+                    const int n1 = list_at(c + 5);
+                    step(A1, B1, C1, 0.0f, o1, 1, clamp_tag);
+                    A1 = rec_at(n1).a;
+                    B1 = rec_at(n1).b;
+                    C1 = rec_at(n1).c;
+                    const int n2 = list_at(c + 6);
+                    step(A2, B2, C2, 0.0f, o2, 2, clamp_tag);
+                    A2 = rec_at(n2).a;
+                    B2 = rec_at(n2).b;
+                    C2 = rec_at(n2).c;
+                    const int n3 = list_at(c + 7);
+                    step(A3, B3, C3, 0.0f, o3, 3, clamp_tag);
+                    o0 = n0;
+                    o1 = n1;
+                    o2 = n2;
+                    o3 = n3;
+                    asm volatile("" ::: "memory");
+                    phase2(c, mu);
+                    asm volatile("" ::: "memory");
+                }
+                return;
+            }
             int o0 = list_at(0), o1 = list_at(1);
             float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
             float C0 = rec_at(o0).c, Z0 = z_at(o0);
@@ -1102,7 +1149,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                 // that sum them: LDS accesses of one wave are served in order, so
                 // keeping the compiler from reordering them is enough
                 asm volatile("" ::: "memory");
-                phase2(c);
+                phase2(c, rec_mean(c));
                 asm volatile("" ::: "memory");
             }
         };
