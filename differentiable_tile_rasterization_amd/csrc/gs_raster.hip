@@ -1678,7 +1678,11 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         const int len_other = list_cnt[0][other] + list_cnt[1][other] + list_cnt[2][other] + list_cnt[3][other];
         // the same for both halves: wave-uniform, so the loop runs on scalar control
         const int steps = __builtin_amdgcn_readfirstlane(max(my_len, len_other));
-        for (int p = my_len + (lane & 31); p < steps + 3; p += 32) list[hq][p] = kDummyFwd;
+        // dummies past the end: up to a whole number of four-step groups and
+        // the four entries read ahead of them (two entries read ahead with
+        // the depth outputs)
+        const int pad_end = DEP == 0 ? ((steps + 3) & ~3) + 4 : steps + 3;
+        for (int p = my_len + (lane & 31); p < pad_end; p += 32) list[hq][p] = kDummyFwd;
         const unsigned short* L = list[hq];
 
         int bl_cur = -1;  // slot offset of this batch's last composited entry (-1: none)
@@ -1736,10 +1740,50 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             if (__builtin_amdgcn_inverse_ballot_w64(0x0001000100010001ull))
                 mw_rec[hq][it + ((lane >> 4) & 1)] = m;
         };
-        // Two entries per iteration with two record buffers, each refilled
-        // one entry ahead of its use (the lists hold dummies past their end).
         // blue, and the depth where it is used
         auto cz_at = [&](int o) -> float2 { return make_float2(rec_at(o).c, DEP ? rec_at(o).z : 0.0f); };
+        if constexpr (DEP == 0) {
+        // Four record buffers, each refilled three entries ahead of its use;
+        // the steps past the end of a half's list take dummies (weight 0).
+        static_assert(kListLen >= ((kBatch + 3) & ~3) + 4, "list rows hold the four-step read-ahead");
+        int o0 = L[0], o1 = L[1], o2 = L[2], o3 = L[3];
+        float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
+        float2 K0 = cz_at(o0);
+        float4 A1 = rec_at(o1).a, B1 = rec_at(o1).b;
+        float2 K1 = cz_at(o1);
+        float4 A2 = rec_at(o2).a, B2 = rec_at(o2).b;
+        float2 K2 = cz_at(o2);
+        for (int it = 0; it < steps; it += 4) {
+            if (done_m == ~0ull) break;  // the wave's 64 pixels have stopped
+            const float4 A3 = rec_at(o3).a, B3 = rec_at(o3).b;
+            const float2 K3 = cz_at(o3);
+            const int n0 = L[it + 4];
+            const float w0 = step(A0, B0, K0, o0);
+            A0 = rec_at(n0).a;
+            B0 = rec_at(n0).b;
+            K0 = cz_at(n0);
+            const int n1 = L[it + 5];
+            const float w1 = step(A1, B1, K1, o1);
+            if (MW) store_max(w0, w1, it);
+            A1 = rec_at(n1).a;
+            B1 = rec_at(n1).b;
+            K1 = cz_at(n1);
+            const int n2 = L[it + 6];
+            const float w2 = step(A2, B2, K2, o2);
+            A2 = rec_at(n2).a;
+            B2 = rec_at(n2).b;
+            K2 = cz_at(n2);
+            const int n3 = L[it + 7];
+            const float w3 = step(A3, B3, K3, o3);
+            if (MW) store_max(w2, w3, it + 2);
+            o0 = n0;
+            o1 = n1;
+            o2 = n2;
+            o3 = n3;
+        }
+        } else {
+        // With the depth outputs (whose sums take the registers): two record
+        // buffers, each refilled one entry ahead of its use.
         int o0 = L[0], o1 = L[1];
         float4 A0 = rec_at(o0).a, B0 = rec_at(o0).b;
         float2 K0 = cz_at(o0);
@@ -1764,6 +1808,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
             o1 = n1;
         }
         if (MW && (steps & 1)) store_max(w_tail, 0.0f, steps - 1);  // any_c is 0 if it was not walked
+        }
         if (bl_cur >= 0) last_n = bs - rg.x + bl_cur / (int)sizeof(FwdSlot) + 1;
         if (DEP && med_cur >= 0) med_n = bs - rg.x + med_cur / (int)sizeof(FwdSlot) + 1;
         __syncthreads();  // the walk's reads of the slots and lists precede their rewriting
