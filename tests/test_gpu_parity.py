@@ -339,6 +339,16 @@ def test_large_grid_forward_backward():
     assert bins.tile_ranges.shape[0] == 66049 and bins.n_isect > 100000
 
 
+@pytest.mark.parametrize("W,H", [(32768, 20), (20, 32768)])
+def test_maximum_image_dimensions(W, H):
+    """A width or height at the largest the library takes (32768 pixels, 2048
+    tiles along that axis), with a ragged tile row or column across the
+    other: binning, forward and the three reverse walks against the oracle."""
+    sc = _custom(14, W, H, 2500, sig=(1.0, 12.0), pad=20)
+    bins, _ = check_scene(sc)
+    assert bins.tile_ranges.shape[0] == 2048 * 2 and bins.n_isect > 2500
+
+
 def test_binning_capacity_retry():
     sc = scenes.make_scene("tiny", 0)
     bins = gpu_bins(sc, capacity=3)
