@@ -820,6 +820,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     // records are cleared only after the next barrier.
     int hi = tmax;  // the batches cover [0, tmax) from the top down
     while (hi > 0) {
+        __builtin_amdgcn_s_setprio(2);  // staging and flush: their loads and stores issue first
         int my_slot = -1;  // this thread's staged entry's pair slot
         const int lo = max(0, hi - NB);  // candidates [lo, hi): entry lo + t in slot t
         const int k = lo + (int)threadIdx.x;
@@ -1153,10 +1154,12 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
                 asm volatile("" ::: "memory");
             }
         };
+        __builtin_amdgcn_s_setprio(0);
         if (clamp_batch)
             walk(std::true_type{});
         else
             walk(std::false_type{});
+        __builtin_amdgcn_s_setprio(2);
         __syncthreads();
 
         // Flush: thread t owns the entry it staged; its sums are those of the
@@ -1616,6 +1619,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
     // the walk's tests then build their masks with compare instructions alone
     unsigned long long done_m = __ballot(!inside);
     for (int bs = rg.x; bs < rg.y; bs += kBatch) {
+        __builtin_amdgcn_s_setprio(2);  // staging: its loads issue first
         // halves with a pixel still compositing; the tile stops when none is left
         const bool half_alive = ~done_m & (half ? 0xffffffff00000000ull : 0xffffffffull);
         if ((lane & 31) == 0) half_live[hq] = half_alive ? 1 : 0;
@@ -1742,6 +1746,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         };
         // blue, and the depth where it is used
         auto cz_at = [&](int o) -> float2 { return make_float2(rec_at(o).c, DEP ? rec_at(o).z : 0.0f); };
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (DEP == 0) {
         // Four record buffers, each refilled three entries ahead of its use;
         // the steps past the end of a half's list take dummies (weight 0).
