@@ -272,7 +272,7 @@ template <bool AW, int NB, int KC, int WG, int DEP = 0> struct DeferShape {
     static constexpr int kListLen = NB + 5;  // up to NB entries, then dummies read ahead of use
     static constexpr unsigned short kDummyOff = (unsigned short)(NB * sizeof(StoreSlot));
     static constexpr int kFixed = kSlots * (int)sizeof(StoreSlot) + kHalves * kListLen * 2 + 4 * KC * 64 * 8 +
-                                  (DEP ? 4 * KC * 64 * 4 : 4) + 4 * (kHalves + 1) * 4 + 2 * kHalves * 4 + 4 * 4 + 4;
+                                  (DEP ? 4 * KC * 64 * 4 : 4) + 2 * 4 * (kHalves + 1) * 4 + 2 * kHalves * 4 + 4 * 4 + 4;
     static constexpr int kCap = ((160 * 1024) / WG - kFixed - 256) / (kF * 4);
     static_assert(kCap >= 2 * kHalves * KC, "the partial records must hold at least one chunk");
 };
@@ -291,10 +291,11 @@ constexpr unsigned short kSDummyOff = (unsigned short)(kSBatch * sizeof(StoreSlo
 // position is also written into its own slot's pos bytes. The same exchange of
 // per-wave counts also ORs `flag` over the workgroup, which is returned, and
 // gives every half's list length (len, wave-uniform). Ends with a barrier.
-template <int NSlots = kSSlots, int ListLen = kSListLen>
-__device__ __forceinline__ bool build_store_lists(const unsigned long long (&hits)[kHalves], bool flag, StoreSlot* S,
-                                                 unsigned short (*list)[ListLen], int (*cnt)[kHalves + 1],
-                                                 int (&len)[kHalves])
+// The exchange is split in two: publish_counts (each wave's per-half counts
+// and flag, before a workgroup barrier) and place_lists (after it);
+// build_store_lists does both.
+__device__ __forceinline__ void publish_counts(const unsigned long long (&hits)[kHalves], bool flag,
+                                               int (*cnt)[kHalves + 1])
 {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,7 +306,15 @@ __device__ __forceinline__ bool build_store_lists(const unsigned long long (&hit
         mine = lane == q ? c : mine;
     }
     if (lane <= kHalves) cnt[wv][lane] = mine;
-    __syncthreads();
+}
+
+template <int NSlots = kSSlots, int ListLen = kSListLen>
+__device__ __forceinline__ bool place_lists(const unsigned long long (&hits)[kHalves], StoreSlot* S,
+                                           unsigned short (*list)[ListLen], int (*cnt)[kHalves + 1],
+                                           int (&len)[kHalves])
+{
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool any_flag = (cnt[0][kHalves] | cnt[1][kHalves] | cnt[2][kHalves] | cnt[3][kHalves]) != 0;
     // lane q: list position of this wave's lowest hit of half q, counted from
     // the front (slots of higher waves come first)
@@ -334,6 +343,16 @@ __device__ __forceinline__ bool build_store_lists(const unsigned long long (&hit
     }
     __syncthreads();
     return any_flag;
+}
+
+template <int NSlots = kSSlots, int ListLen = kSListLen>
+__device__ __forceinline__ bool build_store_lists(const unsigned long long (&hits)[kHalves], bool flag, StoreSlot* S,
+                                                 unsigned short (*list)[ListLen], int (*cnt)[kHalves + 1],
+                                                 int (&len)[kHalves])
+{
+    publish_counts(hits, flag, cnt);
+    __syncthreads();
+    return place_lists<NSlots, ListLen>(hits, S, list, cnt, len);
 }
 
 // Six waves per SIMD: the LDS allows six workgroups per CU, and the walk's
@@ -703,6 +722,7 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     __shared__ float parts[kCap * kF];
     __shared__ unsigned short list[kHalves][kDListLen];  // per half: slots that may touch it, then dummies
     __shared__ int list_cnt[4][kHalves + 1];           // [staging wave][half], then the wave's clamp flag
+    __shared__ int pre_cnt[4][kHalves + 1];            // the same before any cut
     __shared__ int half_end[kHalves];
     __shared__ int half_base[kHalves];                 // first partial record of each half, for the flush
     __shared__ int wave_hits[4];                       // half-list entries of each wave's candidates
@@ -845,13 +865,22 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
         // Keep the top candidates whose half-list entries fit the partial
         // records. Usually all of them do (the wave totals, from ballots, say
         // so); otherwise suffix sums of the hit counts over the slots, from
-        // the top, pick the candidates that fit.
+        // the top, pick the candidates that fit. The per-half counts and the
+        // clamp flag as they stand when all fit go out with the wave totals,
+        // so that the usual batch builds its lists after this one barrier.
+        // Can an entry reach the 0.99 clamp? alpha_raw's exponent never
+        // exceeds log2 o, so alpha_raw never exceeds exp2(log2 o) (the same
+        // monotone v_exp_f32): an entry with exp2(log2 o) clearly below 0.99
+        // never clamps. Most batches have none, and their walk skips the
+        // clamp's three instructions per step.
+        const bool clamps = id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
         {
             int wtot = 0;  // this wave's half-list entries (wave-uniform)
 #pragma unroll
             for (int q = 0; q < kHalves; ++q) wtot += __popcll(hits[q]);
             if (lane == 0) wave_hits[wv] = wtot;
             if (threadIdx.x == 0) cut = NB;
+            publish_counts(hits, cand && clamps, pre_cnt);
         }
         __syncthreads();
         const int total = wave_hits[0] + wave_hits[1] + wave_hits[2] + wave_hits[3];
@@ -892,14 +921,11 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
             if (threadIdx.x < kDSlots) S[threadIdx.x].slot = DEP ? __float_as_int(zent) : slot;
             my_slot = slot;
         }
-        // Can any entry of the batch reach the 0.99 clamp? alpha_raw's
-        // exponent never exceeds log2 o, so alpha_raw never exceeds
-        // exp2(log2 o) (the same monotone v_exp_f32): an entry with exp2(log2 o) clearly below
-        // 0.99 never clamps. Most batches have none, and their walk skips the
-        // clamp's three instructions per step.
-        const bool may_clamp = keep && id >= 0 && !(__builtin_amdgcn_exp2f(r.b.y) < kAlphaMax * (1.0f - 0x1p-20f));
         int len[kHalves];
-        const bool clamp_batch = build_store_lists<kDSlots, kDListLen>(hits, may_clamp, S, list, list_cnt, len);
+        const bool clamp_batch = total > kCap  // workgroup-uniform: a cut batch exchanges its counts again
+                                     ? build_store_lists<kDSlots, kDListLen>(hits, keep && clamps, S, list, list_cnt,
+                                                                             len)
+                                     : place_lists<kDSlots, kDListLen>(hits, S, list, pre_cnt, len);
         int base[kHalves];  // first partial record of each half
         base[0] = 0;
 #pragma unroll
