@@ -696,8 +696,8 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
 //     theirs with fused DPP adds; the first lane stores the record.
 // A step then costs 19 VALU instructions instead of about 50 (the
 // cross-lane tree of the other walks: ~21 per step, and the LDS float adds
-// of the first walk, ~25 LDS cycles each), and phase 2 about 15 per step
-// (136 VALU per four-step chunk in all).
+// of the first walk, ~25 LDS cycles each), and phase 2 about 14 per step
+// (about 130 VALU per four-step chunk in all).
 // The pads (KC x 64 float2 per wave) are written and read by the same wave,
 // whose LDS accesses are served in order: no barrier is needed around them.
 // ---------------------------------------------------------------------------
