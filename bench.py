@@ -157,6 +157,9 @@ def main():
     ap.add_argument("--walk", default=None, choices=["add", "store", "defer"],
                     help="force one reverse walk (default: the library's choice)")
     ap.add_argument("--cpu-sample", type=float, default=1.0, help="fraction of tiles the oracle baseline runs")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the backward on the other workloads (profiler runs: their launches of the same "
+                         "kernels would mix into the per-kernel figures)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
@@ -402,6 +405,9 @@ def main():
                                  "atomic_replay_per_s": n_atomics / t_atomic}
 
     # ---- CPU baseline: the oracle beside the GPU, on the host's cores
+    others = None
+    if not args.no_other_workloads:
+        others = other_workloads(torch, np, gsr, scenes, args, log)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -430,9 +436,68 @@ def main():
                    "n_slots": bins.n_slots,
                    "splat_half_groups": groups_half, "splat_block4_groups": groups_blk,
                    "lockstep_half_iters": iters_half, "lockstep_block4_iters": iters_blk},
+        "other_workloads": others,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec))
+
+
+def other_workloads(torch, np, gsr, scenes, args, log):
+    """The backward on the other four workloads, in the same run (not the
+    headline: no roofline or CPU baseline here): per workload 20 calls back to
+    back between two HIP events on the call's stream, after 10 warm-up calls
+    (ms/call, as the headline), then the mean walk span over 10 calls from the
+    library's stage events, and pairs/s counted as for the headline value
+    (tile-rectangle lists)."""
+    dev = "cuda:0"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("tiny", "early", "mid", "bench", "stress"):
+        if name == args.config:
+            continue
+        sc = scenes.make_scene(name, args.seed)
+        m, q, c, o, bg = t(sc.means2d), t(sc.conics), t(sc.colors), t(sc.opacities), t(sc.background)
+        r, d, g = t(sc.radii), t(sc.depths), t(sc.dL_dimage)
+        aw = sc.accum_weight
+        bins = gsr.gs_bin_tiles(m, q, o, r, d, sc.width, sc.height)
+        _, T, nc = gsr.gs_rasterize_fwd(m, q, c, o, bg, sc.width, sc.height, bins.tile_ranges, bins.sorted_ids)
+        ws = torch.empty(gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_slots, sc.width, sc.height) + 256,
+                         dtype=torch.uint8, device=dev)
+        res = gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw,
+                                   workspace=ws)
+        def bwd(events=None):
+            gsr.gs_rasterize_bwd(m, q, c, o, r, bg, sc.width, sc.height, bins, T, nc, g, accum_weight=aw,
+                                 out=res, workspace=ws, events=events)
+        for _ in range(10):
+            bwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        walks = []
+        for _ in range(10):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for e in evs:
+                e.record(stream)   # creates the HIP events the library records again
+            bwd(evs)
+            torch.cuda.synchronize()
+            walks.append(evs[1].elapsed_time(evs[2]))
+        nrect = rect_walk_pairs(torch, m, r, d, sc.width, sc.height, nc, bins.sorted_ids, bins.tile_ranges)
+        p_rect = int(nrect.sum().item())
+        out[name] = {"workload": f"{name}: {sc.width}x{sc.height} RGB, {sc.n} splats"
+                                 + (", accum weight" if aw else ""),
+                     "ms_per_call": ms, "walk_ms": float(np.mean(walks)), "p_walk_rect": p_rect,
+                     "pairs_per_s": p_rect / (ms * 1e-3)}
+        log(f"other workload {name}: {ms:.4f} ms/call, walk {np.mean(walks):.4f} ms, "
+            f"{p_rect / (ms * 1e-3):.3e} pairs/s")
+        del m, q, c, o, bg, r, d, g, bins, T, nc, ws, res, nrect
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(oracle, sc, bins, nc, nrect, args, log):
