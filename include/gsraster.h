@@ -275,8 +275,11 @@ gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* c
  * division, and accumulates the nine gradient fields per splat. Partial sums
  * are reduced inside each wave and across the workgroup, stored once per
  * (splat, tile) pair into that pair's own workspace slot, and summed per
- * splat by a second kernel in a fixed order: the result does not depend on
- * scheduling (no floating-point atomics).
+ * splat by a second kernel in a fixed order. With the deferred walk (the
+ * default) and the stored-partials walk every sum runs in a fixed order, so
+ * a call gives the same bits on every run; the LDS-add walk adds inside a
+ * workgroup with LDS float atomics, whose order (and so the last bits) may
+ * vary from run to run. No walk uses global floating-point atomics.
  *
  *   n .. opacities       as gs_rasterize_fwd
  *   radii                device int32 [n], the radii given to gs_bin_tiles
