@@ -27,7 +27,7 @@ def test_alu_peak_from_unit_counts():
     # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: VALU lane-operations without packed forms
     assert bench.PEAK_VALU_TOPS == pytest.approx(39.3216, rel=1e-12)
     assert bench.PEAK_HBM_GBS == 8000.0
-    # the survey's minimum model: 60 VALU lane-ops + 2 transcendentals per composited pair
+    # the minimum model: 60 VALU lane-ops + 2 transcendentals per composited pair
     assert (bench.VALU_MIN_PER_PAIR, bench.TRANS_PER_PAIR) == (60, 2)
     assert (bench.LDS_RECORD_BYTES, bench.LDS_READS_PER_ENTRY) == (40, 4)
 
