@@ -402,6 +402,56 @@ def test_timed_entry_point_matches_and_orders_its_events():
     assert all(x >= 0 for x in spans) and spans[1] > 0
 
 
+@pytest.mark.parametrize("name", ["bench", "stress"])
+def test_dirty_outputs_and_workspace(name):
+    """Outputs are overwritten, never accumulated, and every workspace byte a
+    call reads it writes first: outputs prefilled with NaN and a workspace
+    filled with 0xff give the same bits as fresh zeroed buffers (the fixed-order
+    walks; the LDS-add walk to ~ulp). With dL/dImage = 0 every gradient is 0
+    and the accumulated weight, which does not depend on it, is unchanged.
+    Full-size workloads: the batch sizes and gathers of both splat regimes."""
+    sc = scenes.make_scene(name, 0)
+    aw = sc.accum_weight
+    bins = gpu_bins(sc)
+    _, T, nc = gpu_fwd(sc, bins)
+    n = sc.n
+    ws_bytes = gsr.gs_rasterize_bwd_workspace_size(n, bins.n_slots, sc.width, sc.height) + 256
+    args = (_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.radii),
+            _dev(sc.background), sc.width, sc.height, bins, T, nc)
+    g = _dev(sc.dL_dimage)
+    shapes = {"dL_dmeans2d": (n, 2), "dL_dconics": (n, 3), "dL_dcolors": (n, 3), "dL_dopacities": (n,)}
+    if aw:
+        shapes["accum_weight"] = (n,)
+
+    def call(walk, dirty, grad):
+        fill = float("nan") if dirty else 0.0
+        out = {k: torch.full(v, fill, device="cuda") for k, v in shapes.items()}
+        ws = torch.full((ws_bytes,), 0xFF if dirty else 0, dtype=torch.uint8, device="cuda")
+        res = gsr.gs_rasterize_bwd(*args, grad, accum_weight=aw, out=out, workspace=ws, walk=walk)
+        torch.cuda.synchronize()
+        return res
+
+    for walk in ("defer", "store", "add"):
+        _say(f"{name}: walk {walk}, clean and dirty buffers")
+        clean, dirty = call(walk, False, g), call(walk, True, g)
+        for k in shapes:
+            assert torch.isfinite(dirty[k]).all(), (walk, k)
+            if walk == "add":
+                ref = clean[k]
+                tol = 1e-6 * max(float(ref.abs().max()), 1e-30)
+                assert float((dirty[k] - ref).abs().max()) <= tol, (walk, k)
+            else:
+                assert torch.equal(dirty[k], clean[k]), (walk, k)
+        if walk == "add":
+            continue
+        zero = call(walk, True, torch.zeros_like(g))
+        for k in shapes:
+            if k == "accum_weight":
+                assert torch.equal(zero[k], clean[k]), walk
+            else:
+                assert bool((zero[k] == 0).all()), (walk, k)
+
+
 def test_binding_rejects_bad_outputs_before_launch():
     """Caller-supplied outputs are checked like inputs (the kernels write every
     element): a wrong shape, dtype or a missing entry raises, nothing runs."""
