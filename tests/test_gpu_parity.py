@@ -452,6 +452,28 @@ def test_dirty_outputs_and_workspace(name):
                 assert bool((zero[k] == 0).all()), (walk, k)
 
 
+def test_forward_dirty_workspace():
+    """The forward (with the max weight, and with the depth outputs) gives the
+    same bits with a workspace filled with 0xff as with a zeroed one."""
+    sc = scenes.make_scene("bench", 0)
+    bins = gpu_bins(sc)
+    ws_bytes = gsr.gs_rasterize_fwd_workspace_size(sc.n) + 256
+    base = (_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities))
+    for fill in (0, 0xFF):
+        ws = torch.full((ws_bytes,), fill, dtype=torch.uint8, device="cuda")
+        plain = gsr.gs_rasterize_fwd(*base, _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                     bins.sorted_ids, max_weight=True, workspace=ws)
+        ws.fill_(fill)
+        depth = gsr.gs_rasterize_fwd_depth(*base, _dev(sc.depths), _dev(sc.background), sc.width, sc.height,
+                                           bins.tile_ranges, bins.sorted_ids, workspace=ws)
+        torch.cuda.synchronize()
+        got = list(plain) + [depth[k] for k in sorted(depth)]
+        if fill == 0:
+            ref = got
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(got, ref))
+
+
 def test_binding_rejects_bad_outputs_before_launch():
     """Caller-supplied outputs are checked like inputs (the kernels write every
     element): a wrong shape, dtype or a missing entry raises, nothing runs."""
