@@ -452,6 +452,38 @@ def test_dirty_outputs_and_workspace(name):
                 assert bool((zero[k] == 0).all()), (walk, k)
 
 
+@pytest.mark.parametrize("name", ["bench", "stress"])
+def test_binning_dirty_workspace(name):
+    """gs_bin_tiles through the C ABI with its workspace filled with 0xff and
+    every output prefilled with 0xff bytes: the same lists, ranges, pair
+    numbering and counts as the binding's call."""
+    import ctypes
+    sc = scenes.make_scene(name, 0)
+    ref = gpu_bins(sc)
+    lib = gsr._lib.load()
+    n, W, H = sc.n, sc.width, sc.height
+    GX, GY = gsr.tile_grid(W, H)
+    cap = ref.n_isect
+    ws_bytes = int(lib.gs_bin_tiles_workspace_size(n, cap, W, H))
+    ws = torch.full((ws_bytes + 256,), 0xFF, dtype=torch.uint8, device="cuda")
+    ids = torch.full((cap,), -1, dtype=torch.int32, device="cuda")
+    ranges = torch.full((GX * GY, 2), -1, dtype=torch.int32, device="cuda")
+    offs = torch.full((n + 1,), -1, dtype=torch.int32, device="cuda")
+    d = [_dev(sc.means2d), _dev(sc.conics), _dev(sc.opacities), _dev(sc.radii), _dev(sc.depths)]
+    n_isect, n_slots = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    status = lib.gs_bin_tiles(n, *[ctypes.c_void_p(t.data_ptr()) for t in d], W, H, cap,
+                              ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(ranges.data_ptr()),
+                              ctypes.c_void_p(offs.data_ptr()), ctypes.byref(n_isect), ctypes.byref(n_slots),
+                              ctypes.c_void_p((ws.data_ptr() + 255) & ~255), ws_bytes, st)
+    torch.cuda.synchronize()
+    assert status == 0, gsr._lib.load().gs_last_error()
+    assert n_isect.value == ref.n_isect and n_slots.value == ref.n_slots
+    assert torch.equal(ids, ref.sorted_ids)
+    assert torch.equal(ranges, ref.tile_ranges)
+    assert torch.equal(offs, ref.splat_offsets)
+
+
 def test_forward_dirty_workspace():
     """The forward (with the max weight, and with the depth outputs) gives the
     same bits with a workspace filled with 0xff as with a zeroed one."""
