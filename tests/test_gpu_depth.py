@@ -255,3 +255,36 @@ def test_depth_terms_refused_on_other_walks():
     for k, v in plain.items():
         ref = v.cpu().numpy()
         np.testing.assert_allclose(none[k].cpu().numpy(), ref, rtol=0, atol=1e-6 * max(np.abs(ref).max(), 1e-30))
+
+
+@pytest.mark.parametrize("name", ["bench", "stress"])
+def test_depth_backward_dirty_buffers_and_repeats(name):
+    """The depth backward (both terms, with the weight where the workload has
+    it) on outputs prefilled with NaN and a workspace filled with 0xff gives
+    the same bits as on zeroed buffers, and as a second call."""
+    sc = scenes.make_scene(name, 0)
+    bins = gpu_bins(sc)
+    d = gsr.gs_rasterize_fwd_depth(_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities),
+                                   _dev(sc.depths), _dev(sc.background), sc.width, sc.height, bins.tile_ranges,
+                                   bins.sorted_ids)
+    gD, gM = scenes.depth_upstream(sc, 0)
+    ws_bytes = gsr.gs_rasterize_bwd_workspace_size(sc.n, bins.n_slots, sc.width, sc.height) + 256
+
+    def call(dirty, out=None):
+        ws = torch.full((ws_bytes,), 0xFF if dirty else 0, dtype=torch.uint8, device="cuda")
+        res = gsr.gs_rasterize_bwd_depth(
+            _dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.depths), _dev(sc.radii),
+            _dev(sc.background), sc.width, sc.height, bins, d["final_T"], d["n_contrib"], d["median_pos"],
+            _dev(sc.dL_dimage), dist_totals=d["dist_totals"], dL_ddist=_dev(gD), dL_dmedian=_dev(gM),
+            accum_weight=sc.accum_weight, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        return res
+
+    clean = call(False)
+    again = call(False)
+    dirty = call(True, {k: torch.full_like(v, float("nan")) for k, v in clean.items()})
+    for k in clean:
+        assert torch.isfinite(dirty[k]).all(), k
+        assert torch.equal(again[k], clean[k]), k
+        assert torch.equal(dirty[k], clean[k]), k
+    _say(f"depth backward {name}: dirty buffers and a repeat give the same bits ({sorted(clean)})")
