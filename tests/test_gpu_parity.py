@@ -506,6 +506,30 @@ def test_forward_dirty_workspace():
             assert all(torch.equal(a, b) for a, b in zip(got, ref))
 
 
+def test_calls_on_a_side_stream():
+    """Binning, forward and backward enqueued on a non-default stream that is
+    kept busy first (so that work ordered against another stream, or a count
+    read back before the stream's earlier work, would see unfinished inputs)
+    give the default stream's bits."""
+    sc = scenes.make_scene("early", 0)
+    bins0 = gpu_bins(sc)
+    img0, T0, nc0 = gpu_fwd(sc, bins0)
+    g0 = gpu_bwd(sc, bins0, T0, nc0, sc.dL_dimage)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)  # a bounded spin, ~10 ms
+        bins = gpu_bins(sc)
+        img, T, nc = gpu_fwd(sc, bins)
+        g = gpu_bwd(sc, bins, T, nc, sc.dL_dimage)
+    side.synchronize()
+    assert bins.n_isect == bins0.n_isect and bins.n_slots == bins0.n_slots
+    assert torch.equal(bins.sorted_ids, bins0.sorted_ids) and torch.equal(bins.tile_ranges, bins0.tile_ranges)
+    assert torch.equal(img, img0) and torch.equal(T, T0) and torch.equal(nc, nc0)
+    for k in g0:
+        assert torch.equal(g[k], g0[k]), k
+
+
 def test_binding_rejects_bad_outputs_before_launch():
     """Caller-supplied outputs are checked like inputs (the kernels write every
     element): a wrong shape, dtype or a missing entry raises, nothing runs."""
