@@ -40,7 +40,10 @@
  *    allocates or frees device memory; scratch comes in as `workspace`.
  *  - All work is enqueued on `stream` (0 = the null stream) in stream order;
  *    calls return before the work finishes, except gs_bin_tiles, which waits
- *    once to read the intersection count back to the host.
+ *    once to read the intersection count back to the host. The backward
+ *    calls enqueue kernel launches only (no allocation, copy, memset or
+ *    synchronisation), so a caller may capture them in a HIP graph; the
+ *    binning cannot be captured (its read-back).
  *  - Outputs are overwritten, never accumulated into.
  *  - Tiles are 16x16 pixels; tile ids are row-major: ty * GX + tx with
  *    GX = ceil(width / 16), GY = ceil(height / 16).
@@ -62,8 +65,9 @@
  *    [0, n_isect], the pair count the caller passes with sorted_ids (which
  *    must hold at least n_isect entries), and the backward clamps every
  *    splat offset to [0, n_slots].
- *  - Calls are re-entrant; there is no global mutable state other than the
- *    thread-local error string.
+ *  - Calls are re-entrant; the only global mutable state is the thread-local
+ *    error string and the fixed per-device scratch of
+ *    gs_rasterize_bwd_noalloc (calls of it that overlap on one GPU race).
  */
 #ifndef GSRASTER_H
 #define GSRASTER_H

@@ -530,6 +530,60 @@ def test_calls_on_a_side_stream():
         assert torch.equal(g[k], g0[k]), k
 
 
+@pytest.mark.parametrize("entry", ["workspace", "noalloc"])
+def test_backward_captured_in_a_hip_graph(entry):
+    """The backward enqueues kernels only (no allocation, copy, memset or
+    synchronisation), so it can be captured in a HIP graph: the caller's
+    workspace or the library's fixed scratch, preallocated outputs. Every
+    replay, with eager work between them (outputs and workspace dirtied, the
+    image gradient changed in place), gives the eager call's bits."""
+    sc = scenes.make_scene("early", 0)
+    bins = gpu_bins(sc)
+    _, T, nc = gpu_fwd(sc, bins)
+    n = sc.n
+    args = (_dev(sc.means2d), _dev(sc.conics), _dev(sc.colors), _dev(sc.opacities), _dev(sc.radii),
+            _dev(sc.background), sc.width, sc.height, bins, T, nc)
+    g = _dev(sc.dL_dimage)
+    g_alt = torch.flip(g, dims=[0]).contiguous()
+    shapes = {"dL_dmeans2d": (n, 2), "dL_dconics": (n, 3), "dL_dcolors": (n, 3), "dL_dopacities": (n,)}
+    ws_bytes = gsr.gs_rasterize_bwd_workspace_size(n, bins.n_slots, sc.width, sc.height) + 256
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device="cuda")
+    out = {k: torch.zeros(v, device="cuda") for k, v in shapes.items()}
+    grad = g.clone()
+
+    def run(o, gi):
+        if entry == "workspace":
+            return gsr.gs_rasterize_bwd(*args, gi, out=o, workspace=ws)
+        return gsr.gs_rasterize_bwd_noalloc(*args, gi, out=o)
+
+    eager = {}
+    for name, gi in (("g", g), ("alt", g_alt)):
+        eager[name] = run({k: torch.zeros(v, device="cuda") for k, v in shapes.items()}, gi)
+        torch.cuda.synchronize()
+        eager[name] = {k: v.clone() for k, v in eager[name].items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(out, grad)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(out, grad)
+    torch.cuda.synchronize()
+    for r, name in enumerate(("g", "alt", "g", "alt")):
+        for v in out.values():
+            v.fill_(float("nan"))
+        ws.fill_(0xFF)
+        grad.copy_(g if name == "g" else g_alt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in shapes:
+            assert torch.equal(out[k], eager[name][k]), (entry, r, k)
+    _say(f"graph ({entry}): four replays equal to the eager calls")
+
+
 def test_binding_rejects_bad_outputs_before_launch():
     """Caller-supplied outputs are checked like inputs (the kernels write every
     element): a wrong shape, dtype or a missing entry raises, nothing runs."""
