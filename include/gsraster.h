@@ -40,10 +40,11 @@
  *    allocates or frees device memory; scratch comes in as `workspace`.
  *  - All work is enqueued on `stream` (0 = the null stream) in stream order;
  *    calls return before the work finishes, except gs_bin_tiles, which waits
- *    once to read the intersection count back to the host. The backward
- *    calls enqueue kernel launches only (no allocation, copy, memset or
- *    synchronisation), so a caller may capture them in a HIP graph; the
- *    binning cannot be captured (its read-back).
+ *    once to read the intersection count back to the host.
+ *    gs_rasterize_bwd and gs_rasterize_bwd_noalloc enqueue kernel launches
+ *    only (no allocation, copy, memset or synchronisation), so a caller may
+ *    capture them in a HIP graph; the binning cannot be captured (its
+ *    read-back).
  *  - Outputs are overwritten, never accumulated into.
  *  - Tiles are 16x16 pixels; tile ids are row-major: ty * GX + tx with
  *    GX = ceil(width / 16), GY = ceil(height / 16).
