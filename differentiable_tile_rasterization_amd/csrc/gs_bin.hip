@@ -716,7 +716,7 @@ extern "C" size_t gs_bin_tiles_workspace_size(int32_t n, int64_t capacity, int32
 {
     (void)width;
     (void)height;
-    if (n < 0 || capacity < 0) return 0;
+    if (n < 0 || n > kMaxSplats || capacity < 0) return 0;
     return bin_layout(n, capacity).bytes;
 }
 
@@ -760,7 +760,7 @@ extern "C" gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* 
                                   size_t workspace_bytes, gs_stream_t stream_)
 {
     hipStream_t st = (hipStream_t)stream_;
-    GS_CHECK_ARG(n >= 0, "gs_bin_tiles: n = %d < 0", n);
+    GS_CHECK_ARG(n >= 0 && n <= kMaxSplats, "gs_bin_tiles: n = %d outside 0..%d", n, kMaxSplats);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
                  "gs_bin_tiles: image size %d x %d outside 1..%d", width, height, kMaxDim);
     GS_CHECK_ARG(capacity >= 0, "gs_bin_tiles: capacity %lld < 0", (long long)capacity);

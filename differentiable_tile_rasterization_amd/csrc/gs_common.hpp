@@ -15,6 +15,9 @@ constexpr int kTile = 16;            // tile edge in pixels
 constexpr int kBlock = 256;          // threads per raster workgroup = pixels per tile
 constexpr int kWave = 64;            // gfx950 wavefront
 constexpr int kMaxDim = 32768;       // largest accepted width / height
+// largest accepted splat count: per-splat offsets such as 3 i (colour, conic)
+// and block counts such as (n + 255) / 256 stay within int32
+constexpr int kMaxSplats = 1 << 29;
 
 // Compositing constants of the rule documented in gsraster.h.
 constexpr float kAlphaMax = 0.99f;

@@ -2317,7 +2317,7 @@ using namespace gs;
 
 extern "C" size_t gs_rasterize_fwd_workspace_size(int32_t n)
 {
-    if (n < 0) return 0;
+    if (n < 0 || n > kMaxSplats) return 0;
     return layout(n > 0 ? n : 1, 0, 0).bytes;
 }
 
@@ -2329,7 +2329,7 @@ gs_status fwd_impl(const char* name, int32_t n, const float* means2d, const floa
                    float* median_depth, int32_t* median_pos, void* workspace, size_t workspace_bytes,
                    hipStream_t st)
 {
-    GS_CHECK_ARG(n >= 0, "%s: n = %d < 0", name, n);
+    GS_CHECK_ARG(n >= 0 && n <= kMaxSplats, "%s: n = %d outside 0..%d", name, n, kMaxSplats);
     GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "%s: n_isect = %lld out of range", name,
                  (long long)n_isect);
     GS_CHECK_ARG(width > 0 && height > 0 && width <= kMaxDim && height <= kMaxDim,
@@ -2402,7 +2402,7 @@ extern "C" gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, con
 
 extern "C" size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_slots, int32_t width, int32_t height)
 {
-    if (n < 0 || n_slots < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
+    if (n < 0 || n > kMaxSplats || n_slots < 0 || width <= 0 || height <= 0 || width > kMaxDim || height > kMaxDim) return 0;
     return layout(n > 0 ? n : 1, n_slots, (long long)grid_x(width) * grid_y(height)).bytes;
 }
 
@@ -2423,7 +2423,7 @@ gs_status bwd_impl(int32_t n, const float* means2d, const float* conics, const f
     auto mark = [&](int k) -> hipError_t {
         return (events && events[k]) ? hipEventRecord((hipEvent_t)events[k], st) : hipSuccess;
     };
-    GS_CHECK_ARG(n >= 0, "gs_rasterize_bwd: n = %d < 0", n);
+    GS_CHECK_ARG(n >= 0 && n <= kMaxSplats, "gs_rasterize_bwd: n = %d outside 0..%d", n, kMaxSplats);
     GS_CHECK_ARG(n_isect >= 0 && n_isect <= 0x7fffffffll, "gs_rasterize_bwd: n_isect = %lld out of range",
                  (long long)n_isect);
     GS_CHECK_ARG(n_slots >= n_isect && n_slots <= 0x7fffffffll,

@@ -50,7 +50,7 @@
  *    GX = ceil(width / 16), GY = ceil(height / 16).
  *  - Images are HWC, row-major, y pointing down: image[(y * width + x) * 3 + ch].
  *  - Errors: arguments the host can check (NULL where a pointer is required,
- *    n < 0, width or height <= 0 or too large, unknown flags) return
+ *    n outside 0 .. 2^29, width or height <= 0 or too large, unknown flags) return
  *    GS_ERR_INVALID_ARG before any work is enqueued. A failing HIP call
  *    returns GS_ERR_HIP. gs_last_error() then describes the failure (a
  *    thread-local string, valid until the thread's next call). Faults inside
@@ -159,7 +159,8 @@ int gs_version(void);
  * tile-id order into sorted_ids; tile_ranges[t] = [start, end) into it
  * ({0, 0} for an empty tile).
  *
- *   n            number of splats (>= 0)
+ *   n            number of splats, 0 .. 2^29 (536,870,912), else
+ *                GS_ERR_INVALID_ARG
  *   means2d      device float [n][2], pixels
  *   conics       device float [n][3] = (a, b, c) of the inverse covariance
  *   opacities    device float [n]
@@ -212,7 +213,7 @@ gs_status gs_bin_tiles(int32_t n, const float* means2d, const float* conics, con
  * splat receives over the pixels that composite it, 0 if none). The result
  * does not depend on scheduling.
  *
- *   n                 number of splats
+ *   n                 number of splats, 0 .. 2^29, else GS_ERR_INVALID_ARG
  *   means2d           device float [n][2]
  *   conics            device float [n][3] = (a, b, c) of the inverse covariance
  *   colors            device float [n][3]
@@ -314,7 +315,7 @@ gs_status gs_rasterize_fwd_depth(int32_t n, const float* means2d, const float* c
  * zeros. Inputs that do not come from one binning of the same splats are
  * not detected; the kernels never write outside the outputs and workspace.
  */
-/* 0 for n < 0, n_slots < 0 or a width / height outside 1..32768 */
+/* 0 for n outside 0 .. 2^29, n_slots < 0 or a width / height outside 1..32768 */
 size_t gs_rasterize_bwd_workspace_size(int32_t n, int64_t n_slots, int32_t width, int32_t height);
 
 gs_status gs_rasterize_bwd(int32_t n, const float* means2d, const float* conics, const float* colors,

@@ -230,3 +230,28 @@ def test_depth_entry_points_reject_bad_arguments():
         assert b"deferred walk" in lib.gs_last_error()
         assert bwd(gd=None, gm=p, flags=walk) == _lib.GS_ERR_UNSUPPORTED
     assert bwd(flags=0x80) == _lib.GS_ERR_INVALID_ARG
+
+
+def test_splat_count_limit_is_checked_everywhere():
+    """n up to 2^29 (per-splat int32 offsets such as 3 n stay in range); one
+    more is refused by every entry point before any device work, and the
+    workspace queries return 0 for it."""
+    lib = _lib.load()
+    big = (1 << 29) + 1
+    p = ctypes.c_void_p(256)
+    cnt = ctypes.c_int64(0)
+    assert lib.gs_bin_tiles_workspace_size(big, 0, 64, 64) == 0
+    assert lib.gs_rasterize_fwd_workspace_size(big) == 0
+    assert lib.gs_rasterize_bwd_workspace_size(big, 0, 64, 64) == 0
+    assert lib.gs_rasterize_fwd_workspace_size(1 << 29) >= 48 * (1 << 29)
+    assert lib.gs_bin_tiles(big, p, p, p, p, p, 64, 64, 16, p, p, p, ctypes.byref(cnt), None, p, 1 << 20,
+                            None) == _lib.GS_ERR_INVALID_ARG
+    assert b"outside 0..536870912" in lib.gs_last_error()
+    assert _fwd(lib, n=big) == _lib.GS_ERR_INVALID_ARG
+    assert b"outside 0..536870912" in lib.gs_last_error()
+    q = ctypes.c_void_p(1)
+    assert lib.gs_rasterize_bwd(big, q, q, q, q, q, None, 8, 8, q, q, q, 0, 0, q, q, q, q, q, q, q, None, 0,
+                                None, 0, None) == _lib.GS_ERR_INVALID_ARG
+    assert b"outside 0..536870912" in lib.gs_last_error()
+    assert lib.gs_rasterize_bwd_noalloc(big, q, q, q, q, q, None, 8, 8, q, q, q, 0, 0, q, q, q, q, q, q, q,
+                                        None, 0, None) == _lib.GS_ERR_INVALID_ARG
