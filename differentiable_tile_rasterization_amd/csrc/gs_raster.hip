@@ -390,13 +390,13 @@ __global__ __launch_bounds__(kBlock, 6) void bwd_store_kernel(
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
     if (inside) {
-        const int p = y * W + x;
+        const int p = y * W + x;  // < 2^30: the HWC offset 3 p fits 32 unsigned bits
         T = final_T[p];
         // never walk past the tile's list, whatever n_contrib holds
         nc = min(max(n_contrib[p], 0), rg.y - rg.x);
-        g0 = dimg[3 * p + 0];
-        g1 = dimg[3 * p + 1];
-        g2 = dimg[3 * p + 2];
+        g0 = dimg[3u * (unsigned)p + 0];
+        g1 = dimg[3u * (unsigned)p + 1];
+        g2 = dimg[3u * (unsigned)p + 2];
     }
     // Colour "behind" the current splat (normalised by the transmittance after
     // it; the background at the start), carried only as its dot product with
@@ -756,13 +756,13 @@ __global__ __launch_bounds__(kBlock, WG) void bwd_defer_kernel(
     float zm = 0.0f, dA = 0.0f, nB2 = 0.0f, dC = 0.0f, gD = 0.0f, A2g = 0.0f, mB2g = 0.0f, gM = 0.0f, E = 0.0f;
     int mp = 0;
     if (inside) {
-        const int p = y * W + x;
+        const int p = y * W + x;  // < 2^30: the HWC offset 3 p fits 32 unsigned bits
         IT = 1.0f / final_T[p];
         // never walk past the tile's list, whatever n_contrib holds
         nc = min(max(n_contrib[p], 0), rg.y - rg.x);
-        g0 = dimg[3 * p + 0];
-        g1 = dimg[3 * p + 1];
-        g2 = dimg[3 * p + 2];
+        g0 = dimg[3u * (unsigned)p + 0];
+        g1 = dimg[3u * (unsigned)p + 1];
+        g2 = dimg[3u * (unsigned)p + 2];
         if (DEP) {
             mp = min(max(dz.median_pos[p], 0), nc);  // the median is a composited entry
             if (mp > 0) {
@@ -1315,13 +1315,13 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(
     float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
     int nc = 0;
     if (inside) {
-        const int p = y * W + x;
+        const int p = y * W + x;  // < 2^30: the HWC offset 3 p fits 32 unsigned bits
         T = final_T[p];
         // never walk past the tile's list, whatever n_contrib holds
         nc = min(max(n_contrib[p], 0), rg.y - rg.x);
-        g0 = dimg[3 * p + 0];
-        g1 = dimg[3 * p + 1];
-        g2 = dimg[3 * p + 2];
+        g0 = dimg[3u * (unsigned)p + 0];
+        g1 = dimg[3u * (unsigned)p + 1];
+        g2 = dimg[3u * (unsigned)p + 2];
     }
     // Colour "behind" the current splat (normalised by the transmittance after
     // it; the background at the start), carried only as its dot product with
@@ -1855,12 +1855,12 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(int n, int W, int H, int GX
         }
     }
     if (inside) {
-        const int p = y * W + x;
+        const int p = y * W + x;  // < 2^30: the HWC offset 3 p fits 32 unsigned bits
         float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
         if (bg) { b0 = bg[0]; b1 = bg[1]; b2 = bg[2]; }
-        image[3 * p + 0] = __builtin_fmaf(T, b0, C0);
-        image[3 * p + 1] = __builtin_fmaf(T, b1, C1);
-        image[3 * p + 2] = __builtin_fmaf(T, b2, C2);
+        image[3u * (unsigned)p + 0] = __builtin_fmaf(T, b0, C0);
+        image[3u * (unsigned)p + 1] = __builtin_fmaf(T, b1, C1);
+        image[3u * (unsigned)p + 2] = __builtin_fmaf(T, b2, C2);
         final_T[p] = T;
         n_contrib[p] = last_n;
         if (DEP) {

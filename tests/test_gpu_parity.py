@@ -353,6 +353,52 @@ def test_maximum_image_dimensions(W, H):
     assert bins.tile_ranges.shape[0] == 2048 * 2 and bins.n_isect > 2500
 
 
+def test_hwc_offsets_beyond_int32_on_a_32768_square_image():
+    """A 32768 x 32768 image has 2^30 pixels, so the HWC offsets 3 p of its last
+    rows pass 2^31. Splats only in its last 64 x 64 block, with dL/dImage zero
+    elsewhere, give that block's image, final_T and n_contrib and the
+    gradients of the same splats moved by (-32704, -32704) into a 64 x 64
+    image, which the oracle checks. The means are multiples of 2^-9, so every
+    pixel-minus-mean difference is exact at both positions."""
+    import dataclasses
+    rng = np.random.default_rng(21)
+    n = 150
+    m = np.round(np.stack([rng.uniform(0.5, 63.5, n), rng.uniform(0.5, 63.5, n)], 1) * 512) / 512
+    small = scenes.custom_scene(64, 64, means2d=m, sigmas=rng.uniform(0.7, 5.0, (n, 2)),
+                                thetas=rng.uniform(0, math.pi, n), opacities=rng.uniform(0.05, 1.0, n),
+                                colors=rng.uniform(0, 1, (n, 3)), depths=rng.uniform(0.1, 10, n), seed=21)
+    check_scene(small)  # the small scene against the oracle
+    S, off = 32768, 32704
+    big_means = (small.means2d.astype(np.float64) + off).astype(np.float32)
+    assert np.array_equal(big_means.astype(np.float64) - off, small.means2d.astype(np.float64))
+    big = dataclasses.replace(small, width=S, height=S, means2d=big_means)
+    bins_s = gpu_bins(small)
+    img_s, T_s, nc_s = gpu_fwd(small, bins_s)
+    g_s = _dev(small.dL_dimage)
+    out_s = gpu_bwd(small, bins_s, T_s, nc_s, small.dL_dimage)
+    torch.cuda.synchronize()
+    _say("32768 x 32768: binning")
+    bins = gpu_bins(big)
+    assert bins.tile_ranges.shape[0] == 2048 * 2048
+    _say("32768 x 32768: forward")
+    img, T, nc = gpu_fwd(big, bins)
+    torch.cuda.synchronize()
+    assert float((img[off:, off:] - img_s).abs().max()) <= 1e-6
+    assert float((T[off:, off:] - T_s).abs().max()) <= 1e-6
+    assert torch.equal(nc[off:, off:], nc_s)
+    g = torch.zeros((S, S, 3), dtype=torch.float32, device="cuda")
+    g[off:, off:] = g_s
+    _say("32768 x 32768: backward")
+    out = gsr.gs_rasterize_bwd(_dev(big.means2d), _dev(big.conics), _dev(big.colors), _dev(big.opacities),
+                               _dev(big.radii), _dev(big.background), S, S, bins, T, nc, g)
+    torch.cuda.synchronize()
+    for k in out_s:
+        tol = 1e-6 * max(float(out_s[k].abs().max()), 1e-30)
+        assert float((out[k] - out_s[k]).abs().max()) <= tol, k
+    del img, T, nc, g, out
+    torch.cuda.empty_cache()
+
+
 def test_binning_capacity_retry():
     sc = scenes.make_scene("tiny", 0)
     bins = gpu_bins(sc, capacity=3)
